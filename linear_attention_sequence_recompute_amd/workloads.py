@@ -1,0 +1,202 @@
+"""Seeded synthetic inputs for the chunked gated delta rule and its decode step.
+
+This module draws random inputs and nothing else: it holds none of the method's
+arithmetic, so the GPU path and the CPU oracle can both be fed from it without
+sharing any computation.
+
+Recipe (shapes and distributions of the workloads the WarpDrive page and the
+vLLM KdaSplit page describe; neither page measures on a public dataset):
+
+* q, k ~ N(0, 1), each per-(token, head) vector scaled to unit L2 norm, then
+  rounded to the input dtype (round-to-nearest-even);
+* v ~ N(0, 1), rounded to the input dtype;
+* beta = sigmoid(N(0, 1)), float32;
+* raw per-token log-gate a = -softplus(N(0, 1) + shift), float32, shift = 2 for the
+  standard "short memory" gate (mean per-token decay about 0.16) and -4 for the
+  "long memory" gate that stresses the carry across chunks;
+* initial states and pools ~ N(0, 0.1^2), float32, in [.., H, V, K] layout.
+
+All values are returned as float64 numpy arrays that are exactly representable in
+the stated storage dtype, plus the storage dtype itself, so the oracle consumes
+exactly the values the kernels read.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "round_to_bf16",
+    "round_to_f32",
+    "ChunkInputs",
+    "DecodeInputs",
+    "chunk_inputs",
+    "varlen_lengths",
+    "decode_inputs",
+]
+
+
+def round_to_f32(x: np.ndarray) -> np.ndarray:
+    """Round to float32 (RNE) and return as float64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to bfloat16 (round-to-nearest-even via float32) and return as float64."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = (u.astype(np.uint32) << 16).view(np.float32)
+    return out.astype(np.float64)
+
+
+def _round(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype == "f32":
+        return round_to_f32(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
+    x = rng.standard_normal(shape)
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+@dataclass
+class ChunkInputs:
+    """Inputs of one chunked forward call. Token-major packed layout.
+
+    q, k: [Ttot, H, K]; v: [Ttot, H, V]; a, beta: [Ttot, H]; cu_seqlens: [N+1]
+    (int64, host); h0: [N, H, V, K] or None; pool/slots: optional state pool
+    [P, H, V, K] with per-sequence slot ids [N] (slot <= 0: zero initial state,
+    final state not stored).
+    """
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    a: np.ndarray
+    beta: np.ndarray
+    cu_seqlens: np.ndarray
+    dtype: str
+    h0: np.ndarray | None = None
+    pool: np.ndarray | None = None
+    slots: np.ndarray | None = None
+    equal_length: bool = True
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def n_seqs(self) -> int:
+        return len(self.cu_seqlens) - 1
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+
+def varlen_lengths(n: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Sequence lengths uniform on [lo, hi] (inclusive), seeded."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, hi + 1, n)
+
+
+def chunk_inputs(
+    lengths,
+    H: int,
+    K: int,
+    V: int,
+    dtype: str = "bf16",
+    seed: int = 0,
+    gate_shift: float = 2.0,
+    h0_std: float | None = None,
+    pool_slots: int | None = None,
+    slot_ids=None,
+) -> ChunkInputs:
+    """Draw inputs for sequences of the given lengths packed into one token stream.
+
+    ``lengths`` may be an int list; all-equal lengths mark the call as equal-length
+    (no cu_seqlens needed by the kernels). ``h0_std`` draws a dense initial state;
+    ``pool_slots`` draws a state pool of that many slots (slot 0 reserved) and uses
+    ``slot_ids`` (default 1..N) as the per-sequence slots.
+    """
+    lengths = np.asarray(lengths, dtype=np.int64)
+    n = len(lengths)
+    rng = np.random.default_rng(seed)
+    cu = np.zeros(n + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    T = int(cu[-1])
+    q = _round(_unit_rows(rng, (T, H, K)), dtype)
+    k = _round(_unit_rows(rng, (T, H, K)), dtype)
+    v = _round(rng.standard_normal((T, H, V)), dtype)
+    beta = round_to_f32(_sigmoid(rng.standard_normal((T, H))))
+    a = round_to_f32(-_softplus(rng.standard_normal((T, H)) + gate_shift))
+    h0 = None
+    if h0_std is not None:
+        h0 = round_to_f32(rng.normal(0.0, h0_std, (n, H, V, K)))
+    pool = slots = None
+    if pool_slots is not None:
+        pool = round_to_f32(rng.normal(0.0, 0.1, (pool_slots, H, V, K)))
+        slots = (np.arange(1, n + 1) if slot_ids is None else np.asarray(slot_ids)).astype(np.int32)
+    equal = bool(n > 0 and np.all(lengths == lengths[0]))
+    return ChunkInputs(q, k, v, a, beta, cu, dtype, h0=h0, pool=pool, slots=slots,
+                       equal_length=equal, meta=dict(seed=seed, gate_shift=gate_shift))
+
+
+@dataclass
+class DecodeInputs:
+    """Inputs of one decode step: q, k [N, H, K]; v [N, H, V]; a, beta [N, H];
+    pool [P, H, V, K]; slots [N] (int32; <= 0 marks a padding row)."""
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    a: np.ndarray
+    beta: np.ndarray
+    pool: np.ndarray
+    slots: np.ndarray
+    dtype: str
+
+
+def decode_inputs(
+    N: int,
+    H: int,
+    K: int,
+    V: int,
+    pool_slots: int,
+    dtype: str = "bf16",
+    seed: int = 0,
+    n_padding: int = 0,
+    gate_shift: float = 2.0,
+) -> DecodeInputs:
+    """Draw one decode step over a slot pool. Active rows get distinct slots drawn
+    without replacement from 1..pool_slots-1; ``n_padding`` rows at random positions
+    get slot 0 or -1."""
+    rng = np.random.default_rng(seed)
+    q = _round(_unit_rows(rng, (N, H, K)), dtype)
+    k = _round(_unit_rows(rng, (N, H, K)), dtype)
+    v = _round(rng.standard_normal((N, H, V)), dtype)
+    beta = round_to_f32(_sigmoid(rng.standard_normal((N, H))))
+    a = round_to_f32(-_softplus(rng.standard_normal((N, H)) + gate_shift))
+    pool = round_to_f32(rng.normal(0.0, 0.1, (pool_slots, H, V, K)))
+    n_active = N - n_padding
+    if n_active > pool_slots - 1:
+        raise ValueError("more active rows than usable pool slots")
+    active = rng.choice(np.arange(1, pool_slots), n_active, replace=False)
+    slots = np.zeros(N, dtype=np.int32)
+    pad_pos = rng.choice(N, n_padding, replace=False) if n_padding else np.zeros(0, np.int64)
+    mask = np.ones(N, bool)
+    mask[pad_pos] = False
+    slots[mask] = active
+    slots[pad_pos] = rng.choice(np.array([0, -1]), len(pad_pos))
+    return DecodeInputs(q, k, v, a, beta, pool, slots, dtype)

@@ -1,0 +1,30 @@
+"""fp64 CPU oracle for the chunked gated delta rule forward pass and its decode step.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or execute
+anything in this package: only the tests, the smoke check of the graft entry point
+and the CPU-baseline leg of the benchmark use it. It shares no code with the HIP
+library (no kernels, headers, helpers, tables or pre/post-processing); both sides
+are fed from the seeded generators in ``workloads.py``, which hold none of the
+method's arithmetic.
+
+Functions (all float64 numpy):
+
+* ``recurrent_fwd``  - the definition: the per-token gated delta rule.
+* ``chunked_fwd``    - the chunked WY algorithm (recompute_w_u, chunk_fwd_h,
+  chunk_fwd_o with chunk size 64), exposing its intermediates.
+* ``*_varlen``       - the same over a packed token stream with sequence offsets.
+* ``decode_step``    - one recurrent step over a slot-indexed state pool.
+
+Every function is pinned by tests in ``tests/test_oracle_pins.py`` against closed
+forms, invariants and a hand-derived golden example; no function is "parity
+unpinned".
+"""
+
+from .gdn import (  # noqa: F401
+    recurrent_fwd,
+    chunked_fwd,
+    recurrent_fwd_varlen,
+    chunked_fwd_varlen,
+    decode_step,
+    unit_lower_inverse,
+)

@@ -1,0 +1,385 @@
+"""Pins of the fp64 oracle against facts the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: every check is a closed form, an
+invariant, a hand-derived example (tests/golden/hand_derived.json) or the agreement
+of the two independent formulations (the per-token definition and the chunked WY
+algorithm). A second group plants plausible mistakes in copies of the algorithm
+and checks that some pin catches each of them.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from oracle import (chunked_fwd, chunked_fwd_varlen, decode_step, recurrent_fwd,
+                    recurrent_fwd_varlen, unit_lower_inverse)
+from linear_attention_sequence_recompute_amd.workloads import chunk_inputs, decode_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_derived.json")
+
+
+def rel(x, ref):
+    ref = np.asarray(ref)
+    scale = np.sqrt(np.mean(ref ** 2)) if ref.size else 1.0
+    return float(np.max(np.abs(np.asarray(x) - ref)) / max(scale, 1e-300)) if ref.size else 0.0
+
+
+def _inputs(T, H=2, K=16, V=12, seed=0, shift=2.0, h0=True):
+    ci = chunk_inputs([T], H, K, V, dtype="f32", seed=seed, gate_shift=shift,
+                      h0_std=0.1 if h0 else None)
+    S0 = ci.h0[0] if h0 else None
+    return ci.q, ci.k, ci.v, ci.a, ci.beta, S0
+
+
+def _orthonormal(K, seed):
+    rng = np.random.default_rng(seed)
+    Qm, _ = np.linalg.qr(rng.standard_normal((K, K)))
+    return Qm.T  # rows are orthonormal
+
+
+# ---------------------------------------------------------------- golden example
+
+@pytest.mark.parametrize("fn", [recurrent_fwd, chunked_fwd], ids=["recurrent", "chunked"])
+def test_golden_hand_derived(fn):
+    cases = json.load(open(GOLDEN))["cases"]
+    for c in cases:
+        q = np.array(c["q"], float)[:, None, :]
+        k = np.array(c["k"], float)[:, None, :]
+        v = np.array(c["v"], float)[:, None, :]
+        a = np.log(np.array(c["decay"], float))[:, None]
+        b = np.array(c["beta"], float)[:, None]
+        S0 = np.array(c["S0"], float)[None]
+        o, S = fn(q, k, v, a, b, scale=c["scale"], S0=S0)
+        np.testing.assert_allclose(o[:, 0], np.array(c["o"]), rtol=0, atol=1e-14, err_msg=c["name"])
+        np.testing.assert_allclose(S[0], np.array(c["S_T"]), rtol=0, atol=1e-14, err_msg=c["name"])
+
+
+# ------------------------------------------------------ the two formulations agree
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 128, 293])
+@pytest.mark.parametrize("shift", [2.0, -4.0])
+@pytest.mark.parametrize("scale", [1.0, 0.25])
+def test_recurrent_equals_chunked(T, shift, scale):
+    q, k, v, a, b, S0 = _inputs(T, seed=T, shift=shift)
+    o1, S1 = recurrent_fwd(q, k, v, a, b, scale=scale, S0=S0)
+    o2, S2 = chunked_fwd(q, k, v, a, b, scale=scale, S0=S0)
+    assert rel(o2, o1) < 1e-12
+    assert rel(S2, S1) < 1e-12
+
+
+@settings(max_examples=40, deadline=None)
+@given(T=st.integers(1, 200), K=st.sampled_from([4, 8]), V=st.sampled_from([4, 8]),
+       shift=st.floats(-5.0, 3.0), seed=st.integers(0, 2 ** 31 - 1))
+def test_recurrent_equals_chunked_property(T, K, V, shift, seed):
+    q, k, v, a, b, S0 = _inputs(T, H=1, K=K, V=V, seed=seed, shift=shift)
+    o1, S1 = recurrent_fwd(q, k, v, a, b, S0=S0)
+    o2, S2 = chunked_fwd(q, k, v, a, b, S0=S0)
+    assert rel(o2, o1) < 1e-10
+    assert rel(S2, S1) < 1e-10
+
+
+# --------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("fn", [recurrent_fwd, chunked_fwd], ids=["recurrent", "chunked"])
+def test_beta_zero_is_pure_decay(fn):
+    """With beta = 0 the rule never writes: S_t = exp(G_t) S0 (G the running sum of
+    a) and o_t = exp(G_t) S0 (s q_t)."""
+    T, s = 150, 0.5
+    q, k, v, a, b, S0 = _inputs(T, shift=-4.0)
+    b = np.zeros_like(b)
+    G = np.cumsum(a, axis=0)  # [T, H]
+    o_ref = np.exp(G)[:, :, None] * np.einsum("hvk,thk->thv", S0, s * q)
+    o, S = fn(q, k, v, a, b, scale=s, S0=S0)
+    assert rel(o, o_ref) < 1e-13
+    assert rel(S, np.exp(G[-1])[:, None, None] * S0) < 1e-13
+
+
+@pytest.mark.parametrize("fn", [recurrent_fwd, chunked_fwd], ids=["recurrent", "chunked"])
+def test_small_beta_limit_is_decayed_linear_attention(fn):
+    """As beta = eps -> 0 with S0 = 0, o / eps tends to decayed linear attention
+    s sum_{tau <= t} exp(G_t - G_tau) (q_t . k_tau) v_tau, with O(eps) error. The
+    diagonal tau = t is included."""
+    T, s, eps = 140, 0.75, 1e-7
+    q, k, v, a, b, _ = _inputs(T, shift=-4.0, h0=False)
+    G = np.cumsum(a, axis=0)
+    decay = np.exp(G[:, None, :] - G[None, :, :])  # [t, tau, H]
+    causal = np.tril(np.ones((T, T)))[:, :, None]
+    scores = np.einsum("thk,uhk->tuh", s * q, k) * decay * causal
+    o_ref = np.einsum("tuh,uhv->thv", scores, v)
+    o, _ = fn(q, k, v, a, np.full_like(b, eps), scale=s, S0=None)
+    assert rel(o / eps, o_ref) < 1e-5
+
+
+@pytest.mark.parametrize("fn", [recurrent_fwd, chunked_fwd], ids=["recurrent", "chunked"])
+def test_exact_overwrite(fn):
+    """g = 0, beta = 1, keys drawn with repeats from an orthonormal basis, S0 = 0:
+    each write replaces what was stored under its key, so o_t is s times the value
+    last written under q_t (at or before t), or 0 if none was."""
+    T, K, V, s = 200, 16, 8, 1.5
+    rng = np.random.default_rng(7)
+    basis = _orthonormal(K, 8)
+    kidx = rng.integers(0, K, T)
+    qidx = rng.integers(0, K, T)
+    k = basis[kidx][:, None, :]
+    q = basis[qidx][:, None, :]
+    v = rng.standard_normal((T, 1, V))
+    a = np.zeros((T, 1))
+    b = np.ones((T, 1))
+    o_ref = np.zeros((T, 1, V))
+    last = {}
+    for t in range(T):
+        last[kidx[t]] = v[t, 0]
+        if qidx[t] in last:
+            o_ref[t, 0] = s * last[qidx[t]]
+    o, _ = fn(q, k, v, a, b, scale=s, S0=None)
+    assert np.max(np.abs(o - o_ref)) < 1e-12
+
+
+@pytest.mark.parametrize("fn", [recurrent_fwd, chunked_fwd], ids=["recurrent", "chunked"])
+@pytest.mark.parametrize("shift", [2.0, -4.0])
+def test_orthonormal_key_ema(fn, shift):
+    """With keys and queries from a full orthonormal basis {e_i}, S = sum_i m_i e_i^T
+    and each token does: m_i <- exp(a_t) m_i for all i, then
+    m_j <- (1 - beta_t) m_j + beta_t v_t for the key index j; o_t = s m_{q index}.
+    Pins the gate, beta, the initial state and the carry across chunks exactly."""
+    T, K, V, s = 300, 8, 6, 0.8
+    rng = np.random.default_rng(11)
+    basis = _orthonormal(K, 12)
+    kidx = rng.integers(0, K, T)
+    qidx = rng.integers(0, K, T)
+    k = basis[kidx][:, None, :]
+    q = basis[qidx][:, None, :]
+    v = rng.standard_normal((T, 1, V))
+    a = -np.logaddexp(0, rng.standard_normal((T, 1)) + shift)
+    b = 1 / (1 + np.exp(-rng.standard_normal((T, 1))))
+    S0 = rng.normal(0, 0.1, (1, V, K))
+    m = S0[0] @ basis.T  # column i = S0 e_i
+    o_ref = np.zeros((T, 1, V))
+    for t in range(T):
+        m *= np.exp(a[t, 0])
+        j = kidx[t]
+        m[:, j] = (1 - b[t, 0]) * m[:, j] + b[t, 0] * v[t, 0]
+        o_ref[t, 0] = s * m[:, qidx[t]]
+    S_ref = m @ basis  # sum_i m_i e_i^T
+    o, S = fn(q, k, v, a, b, scale=s, S0=S0)
+    assert np.max(np.abs(o - o_ref)) < 1e-12
+    assert np.max(np.abs(S[0] - S_ref)) < 1e-12
+
+
+# ----------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("t1", [1, 64, 100, 191])
+def test_split_invariance(t1):
+    """Running [0, t1) and then [t1, T) from the state at t1 equals one pass."""
+    T = 256
+    q, k, v, a, b, S0 = _inputs(T, seed=3, shift=-4.0)
+    o, S = chunked_fwd(q, k, v, a, b, S0=S0)
+    oa, Sa = chunked_fwd(q[:t1], k[:t1], v[:t1], a[:t1], b[:t1], S0=S0)
+    ob, Sb = chunked_fwd(q[t1:], k[t1:], v[t1:], a[t1:], b[t1:], S0=Sa)
+    assert rel(np.concatenate([oa, ob]), o) < 1e-12
+    assert rel(Sb, S) < 1e-12
+
+
+def test_varlen_equals_separate():
+    ci = chunk_inputs([70, 1, 0, 130, 64], 2, 8, 8, dtype="f32", seed=5, h0_std=0.1)
+    o, S = chunked_fwd_varlen(ci.q, ci.k, ci.v, ci.a, ci.beta, ci.cu_seqlens, scale=0.5, S0=ci.h0)
+    o_r, S_r = recurrent_fwd_varlen(ci.q, ci.k, ci.v, ci.a, ci.beta, ci.cu_seqlens, scale=0.5, S0=ci.h0)
+    assert rel(o, o_r) < 1e-12 and rel(S, S_r) < 1e-12
+    cu = ci.cu_seqlens
+    for s_ in range(ci.n_seqs):
+        r = slice(cu[s_], cu[s_ + 1])
+        if cu[s_ + 1] == cu[s_]:
+            np.testing.assert_array_equal(S[s_], ci.h0[s_])  # empty sequence: state passes through
+            continue
+        o1, S1 = chunked_fwd(ci.q[r], ci.k[r], ci.v[r], ci.a[r], ci.beta[r], scale=0.5, S0=ci.h0[s_])
+        np.testing.assert_array_equal(o[r], o1)
+        np.testing.assert_array_equal(S[s_], S1)
+
+
+def test_linearity_in_values_and_state():
+    """For fixed q, k, beta, g the map (v, S0) -> (o, S_T) is linear."""
+    T = 150
+    q, k, v, a, b, S0 = _inputs(T, seed=9, shift=-4.0)
+    rng = np.random.default_rng(10)
+    v2 = rng.standard_normal(v.shape)
+    S02 = rng.standard_normal(S0.shape)
+    al, be = 0.7, -1.3
+    o1, S1 = chunked_fwd(q, k, v, a, b, S0=S0)
+    o2, S2 = chunked_fwd(q, k, v2, a, b, S0=S02)
+    o3, S3 = chunked_fwd(q, k, al * v + be * v2, a, b, S0=al * S0 + be * S02)
+    assert rel(o3, al * o1 + be * o2) < 1e-12
+    assert rel(S3, al * S1 + be * S2) < 1e-12
+
+
+def test_wy_matrix_inverse():
+    """A = (I + L)^-1 is unit lower-triangular, (I + L) A = I, and it matches the
+    library inverse."""
+    rng = np.random.default_rng(4)
+    L = np.tril(rng.standard_normal((3, 64, 64)) * 0.2, -1)
+    A = unit_lower_inverse(L)
+    I = np.eye(64)
+    assert np.max(np.abs((I + L) @ A - I)) < 1e-12
+    assert np.all(np.triu(A, 1) == 0) and np.all(np.diagonal(A, axis1=1, axis2=2) == 1)
+    assert np.max(np.abs(A - np.linalg.inv(I + L))) < 1e-10
+
+
+def test_chunk_stages_consistent():
+    """The exposed chunk intermediates satisfy their defining equations."""
+    q, k, v, a, b, S0 = _inputs(100, seed=2)
+    _, _, stages = chunked_fwd(q, k, v, a, b, S0=S0, return_stages=True)
+    assert len(stages) == 2 and stages[1]["A"].shape[-1] == 36
+    st0 = stages[0]
+    n = 64
+    Kc = k[:n].transpose(1, 0, 2)
+    L = np.tril(b[:n].T[:, :, None] * (Kc @ Kc.transpose(0, 2, 1))
+                * np.exp(st0["g"][:, :, None] - st0["g"][:, None, :]), -1)
+    assert np.max(np.abs((np.eye(n) + L) @ st0["A"] - np.eye(n))) < 1e-12
+    np.testing.assert_allclose(st0["g"], np.cumsum(a[:n].T, axis=1), rtol=0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------- decode
+
+def test_decode_equals_recurrence_and_padding():
+    di = decode_inputs(N=12, H=2, K=8, V=8, pool_slots=20, dtype="f32", seed=1, n_padding=4)
+    o, pool = decode_step(di.q, di.k, di.v, di.a, di.beta, di.pool, di.slots, scale=0.3)
+    used = set()
+    for b in range(12):
+        s = int(di.slots[b])
+        if s <= 0:
+            assert np.all(o[b] == 0)
+            continue
+        used.add(s)
+        ob, S = recurrent_fwd(di.q[b:b + 1], di.k[b:b + 1], di.v[b:b + 1], di.a[b:b + 1],
+                              di.beta[b:b + 1], scale=0.3, S0=di.pool[s])
+        np.testing.assert_array_equal(o[b], ob[0])
+        np.testing.assert_array_equal(pool[s], S)
+    for s in range(20):
+        if s not in used:
+            np.testing.assert_array_equal(pool[s], di.pool[s])  # untouched, bit for bit
+
+
+def test_decode_steps_equal_prefill():
+    """T successive decode steps on one slot equal the chunked forward over the
+    same T tokens (outputs and final state)."""
+    T, H, K, V = 70, 2, 8, 8
+    ci = chunk_inputs([T], H, K, V, dtype="f32", seed=6, h0_std=0.1)
+    pool = np.zeros((3, H, V, K))
+    pool[2] = ci.h0[0]
+    outs = []
+    for t in range(T):
+        ot, pool = decode_step(ci.q[t:t + 1], ci.k[t:t + 1], ci.v[t:t + 1], ci.a[t:t + 1],
+                               ci.beta[t:t + 1], pool, np.array([2]), scale=0.4)
+        outs.append(ot[0])
+    o, S = chunked_fwd(ci.q, ci.k, ci.v, ci.a, ci.beta, scale=0.4, S0=ci.h0[0])
+    assert rel(np.stack(outs), o) < 1e-12
+    assert rel(pool[2], S) < 1e-12
+
+
+# ------------------------------------------------- planted mistakes are caught
+
+def _recurrent_mutant(q, k, v, a, beta, scale=1.0, S0=None, mutation=None):
+    T, H, K = q.shape
+    V = v.shape[-1]
+    S = np.zeros((H, V, K)) if S0 is None else S0.copy()
+    o = np.zeros((T, H, V))
+    for t in range(T):
+        if mutation == "output_before_update":
+            S *= np.exp(a[t])[:, None, None]
+            o[t] = np.einsum("hvk,hk->hv", S, scale * q[t])
+        elif mutation != "decay_after_update":
+            S *= np.exp(a[t])[:, None, None]
+        Sx = S.transpose(0, 2, 1) if mutation == "transposed_state" else S
+        dot = np.einsum("hvk,hk->hv", Sx, k[t])
+        bt = np.ones_like(beta[t]) if mutation == "no_beta" else beta[t]
+        delta = bt[:, None] * (v[t] - dot)
+        if mutation == "sign":
+            delta = bt[:, None] * (v[t] + dot)
+        S += delta[:, :, None] * k[t][:, None, :]
+        if mutation == "decay_after_update":
+            S *= np.exp(a[t])[:, None, None]
+        if mutation == "scale_on_state":
+            S *= scale
+        if mutation != "output_before_update":
+            o[t] = np.einsum("hvk,hk->hv", S, scale * q[t])
+    return o, S
+
+
+def _chunked_mutant(q, k, v, a, beta, scale=1.0, S0=None, mutation=None, chunk=64):
+    T, H, K = q.shape
+    V = v.shape[-1]
+    h = np.zeros((H, K, V)) if S0 is None else S0.transpose(0, 2, 1).copy()
+    o = np.zeros((T, H, V))
+    for c0 in range(0, T, chunk):
+        n = min(chunk, T - c0)
+        r = slice(c0, c0 + n)
+        Q, Kc, Vc = (x[r].transpose(1, 0, 2) for x in (q, k, v))
+        b = beta[r].T
+        g = np.cumsum(a[r].T, axis=1)
+        if mutation == "global_cumsum":
+            g = np.cumsum(a[:c0 + n].T, axis=1)[:, c0:]
+        gL = g[:, -1] if mutation != "gL_first_row" else g[:, 0]
+        diff = g[:, :, None] - g[:, None, :]
+        strict = np.tril(np.ones((n, n), bool), -1)
+        incl = np.tril(np.ones((n, n), bool), -1 if mutation == "strict_output_mask" else 0)
+        Es = np.where(strict, np.exp(np.where(strict, diff, 0)), 0)
+        Ei = np.where(incl, np.exp(np.where(incl, diff, 0)), 0)
+        L = b[:, :, None] * (Kc @ Kc.transpose(0, 2, 1)) * Es
+        if mutation == "L_transposed":
+            L = L.transpose(0, 2, 1)
+            A = np.linalg.inv(np.eye(n) + L)
+        else:
+            A = unit_lower_inverse(L)
+        u = A @ (b[:, :, None] * Vc)
+        wg = b if mutation == "w_missing_exp_g" else b * np.exp(g)
+        w = A @ (wg[:, :, None] * Kc)
+        v_new = u - w @ h
+        P = scale * (Q @ Kc.transpose(0, 2, 1)) * Ei
+        inter_gate = np.ones_like(g) if mutation == "inter_missing_exp_g" else np.exp(g)
+        o[r] = (scale * inter_gate[:, :, None] * (Q @ h) + P @ v_new).transpose(1, 0, 2)
+        h = np.exp(gL)[:, None, None] * h + Kc.transpose(0, 2, 1) @ (np.exp(gL[:, None] - g)[:, :, None] * v_new)
+    return o, h.transpose(0, 2, 1)
+
+
+def _pins_fail(fn):
+    """Run the pins on ``fn``; return the list of pins it fails."""
+    failed = []
+    for name, test in [("golden", test_golden_hand_derived),
+                       ("beta0", test_beta_zero_is_pure_decay),
+                       ("small_beta", test_small_beta_limit_is_decayed_linear_attention),
+                       ("overwrite", test_exact_overwrite)]:
+        try:
+            test(fn)
+        except (AssertionError, ValueError, IndexError):
+            failed.append(name)
+    try:
+        test_orthonormal_key_ema(fn, -4.0)
+    except (AssertionError, ValueError, IndexError):
+        failed.append("ema")
+    return failed
+
+
+@pytest.mark.parametrize("mutation", ["output_before_update", "decay_after_update", "transposed_state",
+                                      "no_beta", "sign", "scale_on_state"])
+def test_pins_catch_recurrence_mistakes(mutation):
+    def fn(*args, **kw):
+        return _recurrent_mutant(*args, **kw, mutation=mutation)
+    assert _pins_fail(fn), f"no pin caught the planted mistake {mutation!r}"
+
+
+@pytest.mark.parametrize("mutation", ["global_cumsum", "gL_first_row", "strict_output_mask", "L_transposed",
+                                      "w_missing_exp_g", "inter_missing_exp_g"])
+def test_pins_catch_chunk_mistakes(mutation):
+    def fn(*args, **kw):
+        return _chunked_mutant(*args, **kw, mutation=mutation)
+    # the unmutated copy passes every pin, so a failure is the mistake's doing
+    assert not _pins_fail(lambda *a_, **k_: _chunked_mutant(*a_, **k_, mutation=None))
+    caught = _pins_fail(fn)
+    q, k, v, a, b, S0 = _inputs(293, seed=1, shift=-4.0)
+    o1, S1 = recurrent_fwd(q, k, v, a, b, scale=0.5, S0=S0)
+    o2, S2 = fn(q, k, v, a, b, scale=0.5, S0=S0)
+    if rel(o2, o1) > 1e-8 or rel(S2, S1) > 1e-8:
+        caught.append("recurrent_equals_chunked")
+    assert caught, f"no pin caught the planted mistake {mutation!r}"
