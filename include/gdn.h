@@ -1,0 +1,139 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) gated delta rule library.
+ *
+ * Two operations:
+ *
+ *  gdn_chunk_fwd       the chunked forward pass of the gated delta rule
+ *                      (GatedDeltaNet): recompute_w_u, then chunk_fwd_h, then
+ *                      chunk_fwd_o over chunks of 64 tokens, as the WarpDrive
+ *                      page describes them (kernels 5, 3, 4 and its "Pipeline"
+ *                      paragraph);
+ *  gdn_recurrent_step  one token of the same rule per request over a
+ *                      slot-indexed state pool, as the vLLM KdaSplit page's
+ *                      decode kernel runs it (class docstring and method
+ *                      update), with one scalar decay per token and head.
+ *
+ * Per sequence and head, with q_t, k_t in R^K, v_t in R^V, beta_t in (0,1), the
+ * raw log-gate a_t <= 0 and the query scale s, both compute
+ *
+ *      S <- exp(a_t) S;  S <- S + beta_t (v_t - S k_t) k_t^T;  o_t = S (s q_t)
+ *
+ * where S is the V x K state (rows = value channels, columns = key channels).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are device pointers owned by the caller unless stated otherwise.
+ *    The library allocates nothing and keeps no state between calls.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *    Calls return without waiting for the GPU.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is launched and the status says why. GDN_EHIP reports a
+ *    launch failure from the HIP runtime.
+ *  - Layouts are dense row-major with the last index contiguous. Tensors of the
+ *    input dtype (q, k, v) and the output o must be 16-byte aligned; float
+ *    arrays 4-byte aligned.
+ *  - Supported head sizes: K in {64, 128}, V in {64, 128}.
+ *  - States (h0, ht, pools) are float32 [.., H, V, K].
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_EINVAL = -1,       /* bad pointer, size, alignment, or inconsistent lengths */
+  GDN_EUNSUPPORTED = -2, /* K or V not in {64, 128}, or an unknown dtype */
+  GDN_EWORKSPACE = -3,   /* workspace NULL or smaller than required */
+  GDN_EHIP = -4          /* the HIP runtime reported an error at launch */
+} gdn_status;
+
+typedef enum gdn_dtype {
+  GDN_BF16 = 0, /* bfloat16 */
+  GDN_F32 = 1   /* float32 */
+} gdn_dtype;
+
+/*
+ * Bytes of device workspace gdn_chunk_fwd needs for a call with these sizes
+ * (an upper bound valid for every split of total_tokens into n_seqs
+ * sequences). Returns 0 for invalid sizes. The workspace holds the chunk
+ * intermediates of recompute_w_u (the WY-transformed keys w and values u, the
+ * masked intra-chunk scores, the chunk-local gate sums) and the chunk schedule.
+ */
+size_t gdn_chunk_fwd_workspace_bytes(int n_seqs, int64_t total_tokens, int H, int K, int V,
+                                     gdn_dtype in_dtype);
+
+/*
+ * Chunked forward pass over n_seqs sequences packed into one token stream.
+ *
+ *  q, k        [total_tokens, H, K] in_dtype   queries, keys (the library does
+ *                                              not normalise them)
+ *  v           [total_tokens, H, V] in_dtype   values
+ *  g           [total_tokens, H] float32       raw per-token log-gate a_t (<= 0),
+ *                                              NOT cumulated: the library takes the
+ *                                              inclusive sum within each chunk
+ *  beta        [total_tokens, H] float32       write strengths
+ *  o           [total_tokens, H, V] out_dtype  output (written; rows are tokens)
+ *  scale       multiplies q only
+ *  cu_seqlens  device int32 [n_seqs + 1] sequence offsets, or NULL: then the
+ *              n_seqs sequences have equal length total_tokens / n_seqs
+ *  cu_seqlens_host  host copy of cu_seqlens (sizes the launch grid); NULL iff
+ *              cu_seqlens is NULL. Must start at 0, never decrease and end at
+ *              total_tokens.
+ *  h0, ht      float32 [n_seqs, H, V, K]: initial state (NULL = zeros) and final
+ *              state (NULL = not stored). They may alias (in-place update).
+ *  state_pool, pool_slots, state_slots
+ *              alternative to h0/ht: float32 pool [pool_slots, H, V, K] and
+ *              device int32 state_slots[n_seqs]. Sequence i reads its initial
+ *              state from and writes its final state to pool[state_slots[i]] in
+ *              place; a slot <= 0 means a zero initial state and no write, and a
+ *              slot >= pool_slots is treated the same way. Active slots must be
+ *              distinct. When state_pool is given, h0 and ht must be NULL.
+ *  workspace   device scratch of at least gdn_chunk_fwd_workspace_bytes(...)
+ *              bytes, 256-byte aligned; contents on entry are ignored.
+ *
+ * Chunks of 64 tokens start at every sequence start; a sequence's last chunk
+ * may be shorter. An empty sequence passes its initial state to ht unchanged.
+ * The result is deterministic: identical calls give identical bits, and o in
+ * bfloat16 equals round-to-nearest-even of the float32 result of the same call.
+ */
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, void* o, int n_seqs, int64_t total_tokens, int H,
+                         int K, int V, float scale, gdn_dtype in_dtype, gdn_dtype out_dtype,
+                         const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                         const float* h0, float* ht, float* state_pool, int64_t pool_slots,
+                         const int32_t* state_slots, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * One decode step for N requests over a slot-indexed state pool (the vLLM
+ * KdaSplit page: state [slot, head, value, key], slots <= 0 are padding).
+ *
+ *  q, k        [N, H, K] in_dtype;  v [N, H, V] in_dtype
+ *  g, beta     [N, H] float32 raw log-gate a (<= 0) and write strength
+ *  state_pool  float32 [pool_slots, H, V, K], updated in place for active rows
+ *  slots       device int32 [N]; slot <= 0 marks padding: its o rows are +0 and
+ *              the pool is not touched. A slot >= pool_slots is treated as
+ *              padding. Active slots must be distinct.
+ *  o           [N, H, V] out_dtype
+ *
+ * Per active row b and head h: S = pool[slots[b], h]; S <- exp(a) S;
+ * S <- S + beta (v - S k) k^T; o = S (scale q); the updated S is stored back.
+ */
+gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, float* state_pool, int64_t pool_slots,
+                              const int32_t* slots, void* o, int N, int H, int K, int V,
+                              float scale, gdn_dtype in_dtype, gdn_dtype out_dtype, void* stream);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* gdn_status_string(gdn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

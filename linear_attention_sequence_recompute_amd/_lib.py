@@ -1,0 +1,66 @@
+"""ctypes loader for libgdn.so: symbol signatures and status codes.
+
+The library is built in-tree by ``build.build_library()``. Loading fails loudly
+when it is missing: there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libgdn.so")
+
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
+GDN_BF16, GDN_F32 = 0, 1
+
+# (name, restype, argtypes) for every entry point declared in include/gdn.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "gdn_chunk_fwd_workspace_bytes": (_SZ, [_I, _I64, _I, _I, _I, _I]),
+    "gdn_chunk_fwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I,
+                           _P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "gdn_recurrent_step": (_I, [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "gdn_status_string": (ctypes.c_char_p, [_I]),
+}
+
+
+class GdnError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m linear_attention_sequence_recompute_amd.build` (there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().gdn_status_string(status).decode()
+
+
+def check(status: int, where: str) -> None:
+    if status != GDN_OK:
+        raise GdnError(status, where)

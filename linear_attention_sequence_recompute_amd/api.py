@@ -1,0 +1,154 @@
+"""Thin torch-facing wrappers over the C ABI (argument marshalling only).
+
+Torch supplies device memory and the current stream; every step of the
+computation runs in the HIP kernels of libgdn.so.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+
+__all__ = ["chunk_fwd", "recurrent_step", "workspace_bytes", "GdnError"]
+
+GdnError = _lib.GdnError
+
+_DTYPES = {torch.bfloat16: _lib.GDN_BF16, torch.float32: _lib.GDN_F32}
+
+
+def _dt(t: torch.dtype) -> int:
+    if t not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t}; use torch.bfloat16 or torch.float32")
+    return _DTYPES[t]
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _need(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def workspace_bytes(n_seqs: int, total_tokens: int, H: int, K: int, V: int, in_dtype=torch.bfloat16) -> int:
+    """Device workspace bytes ``chunk_fwd`` needs (see gdn_chunk_fwd_workspace_bytes)."""
+    return int(_lib.lib().gdn_chunk_fwd_workspace_bytes(n_seqs, total_tokens, H, K, V, _dt(in_dtype)))
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
+              scale: Optional[float] = None, cu_seqlens: Optional[Sequence[int]] = None,
+              cu_seqlens_dev: Optional[torch.Tensor] = None, h0: Optional[torch.Tensor] = None,
+              output_final_state: bool = True, ht: Optional[torch.Tensor] = None,
+              state_pool: Optional[torch.Tensor] = None, state_slots: Optional[torch.Tensor] = None,
+              out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, stream=None):
+    """Chunked gated delta rule forward (gdn_chunk_fwd).
+
+    q, k: [B, T, H, K] (B equal-length sequences) or [Ttot, H, K] with
+    ``cu_seqlens`` (host sequence offsets, length N + 1); v: [..., H, V];
+    g, beta: [..., H] float32 (g is the raw per-token log-gate). ``h0``:
+    [N, H, V, K] float32. Returns (o, ht): o shaped like v in ``out_dtype``
+    (default: q's dtype); ht [N, H, V, K] float32 or None. With ``state_pool``
+    ([P, H, V, K]) and ``state_slots`` ([N] int32) the initial and final states
+    live in the pool (updated in place) and ht is None.
+    """
+    H, K = q.shape[-2], q.shape[-1]
+    V = v.shape[-1]
+    if q.dim() == 4:
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens needs packed [Ttot, H, K] inputs")
+        n_seqs, total = q.shape[0], q.shape[0] * q.shape[1]
+    elif q.dim() == 3:
+        total = q.shape[0]
+        n_seqs = 1 if cu_seqlens is None else len(cu_seqlens) - 1
+    else:
+        raise ValueError("q must be [B, T, H, K] or [Ttot, H, K]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    for name, t in (("g", g), ("beta", beta)):
+        _need(t, name, torch.float32)
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or g.shape != q.shape[:-1] or beta.shape != g.shape:
+        raise ValueError("inconsistent shapes of q, k, v, g, beta")
+    in_dt = q.dtype
+    out_dtype = out_dtype or in_dt
+    if out is None:
+        out = torch.empty(v.shape, dtype=out_dtype, device=v.device)
+    _need(out, "out", out_dtype)
+
+    cu_host = cu_dev = None
+    if cu_seqlens is not None:
+        host = torch.as_tensor(list(cu_seqlens) if not torch.is_tensor(cu_seqlens) else cu_seqlens,
+                               dtype=torch.int32).cpu().contiguous()
+        cu_host = host
+        cu_dev = cu_seqlens_dev if cu_seqlens_dev is not None else host.to(q.device)
+        _need(cu_dev, "cu_seqlens_dev", torch.int32)
+
+    if state_pool is not None:
+        _need(state_pool, "state_pool", torch.float32)
+        _need(state_slots, "state_slots", torch.int32)
+        ht = None
+        pool_slots = state_pool.shape[0]
+    else:
+        pool_slots = 0
+        if h0 is not None:
+            _need(h0, "h0", torch.float32)
+        if output_final_state and ht is None:
+            ht = torch.empty((n_seqs, H, V, K), dtype=torch.float32, device=q.device)
+        if ht is not None:
+            _need(ht, "ht", torch.float32)
+
+    need = workspace_bytes(n_seqs, total, H, K, V, in_dt)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = _lib.lib().gdn_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(out), n_seqs, total, H, K, V,
+        float(K ** -0.5 if scale is None else scale), _dt(in_dt), _dt(out_dtype),
+        _ptr(cu_dev), None if cu_host is None else cu_host.data_ptr(),
+        _ptr(h0), _ptr(ht), _ptr(state_pool), pool_slots, _ptr(state_slots),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check(st, "gdn_chunk_fwd")
+    return out, ht
+
+
+def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                   state_pool: torch.Tensor, slots: torch.Tensor, *, scale: Optional[float] = None,
+                   out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None, stream=None):
+    """One decode step (gdn_recurrent_step): q, k [N, H, K]; v [N, H, V]; g, beta
+    [N, H] float32; state_pool [P, H, V, K] float32 updated in place; slots [N]
+    int32 (<= 0: padding). Returns o [N, H, V]."""
+    N, H, K = q.shape
+    V = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    for name, t in (("g", g), ("beta", beta), ("state_pool", state_pool)):
+        _need(t, name, torch.float32)
+    _need(slots, "slots", torch.int32)
+    if k.shape != q.shape or v.shape[:2] != (N, H) or g.shape != (N, H) or beta.shape != (N, H):
+        raise ValueError("inconsistent shapes of q, k, v, g, beta")
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, V, K) or slots.shape != (N,):
+        raise ValueError("state_pool must be [P, H, V, K] and slots [N]")
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((N, H, V), dtype=out_dtype, device=q.device)
+    _need(out, "out", out_dtype)
+    st = _lib.lib().gdn_recurrent_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), state_pool.shape[0], _ptr(slots),
+        _ptr(out), N, H, K, V, float(K ** -0.5 if scale is None else scale), _dt(q.dtype), _dt(out_dtype),
+        _stream(stream))
+    _lib.check(st, "gdn_recurrent_step")
+    return out
+

@@ -1,0 +1,168 @@
+// C ABI of the gated delta rule library: host-side argument validation,
+// workspace carving and the launch sequence. Declarations and contracts are in
+// include/gdn.h.
+#include <limits.h>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+constexpr int64_t kChunkTokens = 64;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_dim(int d) { return d == 64 || d == 128; }
+
+bool valid_dtype(gdn_dtype t) { return t == GDN_BF16 || t == GDN_F32; }
+
+size_t dtype_bytes(gdn_dtype t) { return t == GDN_F32 ? 4 : 2; }
+
+// Upper bound on the number of chunks of any split of total_tokens into n_seqs
+// sequences: sum ceil(len / 64) <= total / 64 + n_seqs.
+int64_t max_chunks(int n_seqs, int64_t total_tokens) { return total_tokens / kChunkTokens + n_seqs; }
+
+gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK:
+      return "GDN_OK";
+    case GDN_EINVAL:
+      return "GDN_EINVAL: invalid argument";
+    case GDN_EUNSUPPORTED:
+      return "GDN_EUNSUPPORTED: unsupported head size or dtype";
+    case GDN_EWORKSPACE:
+      return "GDN_EWORKSPACE: workspace missing or too small";
+    case GDN_EHIP:
+      return "GDN_EHIP: HIP runtime error at launch";
+  }
+  return "GDN_UNKNOWN_STATUS";
+}
+
+size_t gdn_chunk_fwd_workspace_bytes(int n_seqs, int64_t total_tokens, int H, int K, int V,
+                                     gdn_dtype in_dtype) {
+  if (n_seqs < 0 || total_tokens < 0 || H <= 0 || !supported_dim(K) || !supported_dim(V) ||
+      !valid_dtype(in_dtype))
+    return 0;
+  return gdn::workspace_layout(max_chunks(n_seqs, total_tokens), n_seqs, H, K, V, in_dtype == GDN_F32)
+      .total;
+}
+
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         void* o, int n_seqs, int64_t total_tokens, int H, int K, int V, float scale,
+                         gdn_dtype in_dtype, gdn_dtype out_dtype, const int32_t* cu_seqlens,
+                         const int32_t* cu_seqlens_host, const float* h0, float* ht, float* state_pool,
+                         int64_t pool_slots, const int32_t* state_slots, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !supported_dim(K) || !supported_dim(V))
+    return GDN_EUNSUPPORTED;
+  if (n_seqs < 0 || total_tokens < 0 || H <= 0 || H > 65535) return GDN_EINVAL;
+  if (total_tokens > INT_MAX - 2 * kChunkTokens) return GDN_EINVAL;
+  if (n_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_EINVAL;
+  if ((cu_seqlens == nullptr) != (cu_seqlens_host == nullptr)) return GDN_EINVAL;
+  if (static_cast<int64_t>(n_seqs) * H > INT_MAX / 8) return GDN_EINVAL;
+
+  // Chunk count and sequence lengths.
+  int64_t n_chunks = 0;
+  int T_eq = 0;
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] != 0 || cu_seqlens_host[n_seqs] != total_tokens) return GDN_EINVAL;
+    for (int s = 0; s < n_seqs; ++s) {
+      const int64_t len = static_cast<int64_t>(cu_seqlens_host[s + 1]) - cu_seqlens_host[s];
+      if (len < 0) return GDN_EINVAL;
+      n_chunks += (len + kChunkTokens - 1) / kChunkTokens;
+    }
+  } else {
+    if (total_tokens % n_seqs != 0) return GDN_EINVAL;
+    T_eq = static_cast<int>(total_tokens / n_seqs);
+    n_chunks = static_cast<int64_t>(n_seqs) * ((T_eq + kChunkTokens - 1) / kChunkTokens);
+  }
+  if (n_chunks > INT_MAX) return GDN_EINVAL;
+
+  // Tensors.
+  if (total_tokens > 0) {
+    if (!q || !k || !v || !g || !beta || !o) return GDN_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return GDN_EINVAL;
+    if (!aligned(g, 4) || !aligned(beta, 4)) return GDN_EINVAL;
+  }
+
+  // State source and destination.
+  if (state_pool) {
+    if (h0 || ht || !state_slots || pool_slots <= 0 || !aligned(state_pool, 16)) return GDN_EINVAL;
+  } else {
+    if (state_slots) return GDN_EINVAL;
+    if ((h0 && !aligned(h0, 16)) || (ht && !aligned(ht, 16))) return GDN_EINVAL;
+  }
+
+  // Workspace.
+  const gdn::WsLayout layout =
+      gdn::workspace_layout(max_chunks(n_seqs, total_tokens), n_seqs, H, K, V, in_dtype == GDN_F32);
+  if (!workspace || workspace_bytes < layout.total || !aligned(workspace, 256)) return GDN_EWORKSPACE;
+
+  gdn::ChunkArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.o = o;
+  a.n_seqs = n_seqs;
+  a.total_tokens = total_tokens;
+  a.H = H;
+  a.K = K;
+  a.V = V;
+  a.scale = scale;
+  a.in_f32 = in_dtype == GDN_F32;
+  a.out_f32 = out_dtype == GDN_F32;
+  a.cu_seqlens = cu_seqlens;
+  a.n_chunks = n_chunks;
+  a.T_eq = T_eq;
+  a.h0 = h0;
+  a.ht = ht;
+  a.pool = state_pool;
+  a.pool_slots = pool_slots;
+  a.slots = state_slots;
+  a.ws = gdn::carve_workspace(layout, workspace);
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_chunk_fwd(a));
+}
+
+gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                              float* state_pool, int64_t pool_slots, const int32_t* slots, void* o, int N, int H,
+                              int K, int V, float scale, gdn_dtype in_dtype, gdn_dtype out_dtype, void* stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !supported_dim(K) || !supported_dim(V))
+    return GDN_EUNSUPPORTED;
+  if (N < 0 || H <= 0 || H > 65535) return GDN_EINVAL;
+  if (N == 0) return GDN_OK;
+  if (!q || !k || !v || !g || !beta || !state_pool || !slots || !o || pool_slots <= 0) return GDN_EINVAL;
+  if (!aligned(state_pool, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(slots, 4)) return GDN_EINVAL;
+  const size_t in_b = dtype_bytes(in_dtype), out_b = dtype_bytes(out_dtype);
+  if (!aligned(q, in_b) || !aligned(k, in_b) || !aligned(v, in_b) || !aligned(o, out_b)) return GDN_EINVAL;
+
+  gdn::DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.pool = state_pool;
+  a.pool_slots = pool_slots;
+  a.slots = slots;
+  a.o = o;
+  a.N = N;
+  a.H = H;
+  a.K = K;
+  a.V = V;
+  a.scale = scale;
+  a.in_f32 = in_dtype == GDN_F32;
+  a.out_f32 = out_dtype == GDN_F32;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_decode(a));
+}
+
+}  // extern "C"

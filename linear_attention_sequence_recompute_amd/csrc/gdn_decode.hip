@@ -1,0 +1,121 @@
+// Recurrent decode step of the gated delta rule over a slot-indexed state pool.
+//
+// The vLLM KdaSplit page (method update) streams each value row of the state,
+// decays it, dots it with k, forms v_new = (v - dot) beta, adds k v_new to the
+// row and dots the result with q; rows are independent, so the state is split
+// by value rows across lanes and workgroups. Here one scalar decay per token and
+// head replaces that page's per-key-channel decays.
+//
+// Layout on gfx950: a state row of K floats is covered by K/4 lanes holding one
+// float4 each (32 lanes for K = 128), so a wave64 updates 2 (K = 128) or 4
+// (K = 64) rows at once and reduces its dot products with xor-shuffles inside
+// each row's lane group. A workgroup of 256 threads owns 64 rows of one
+// (request, head) state page and issues all of its loads before any arithmetic
+// so that 32 KiB per workgroup are in flight. The page is read and written
+// exactly once, with non-temporal hints: it is not reused by this launch.
+#include "gdn_common.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+constexpr int kDecodeRows = 64;  // state rows per workgroup
+
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+template <int K, int V, typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void recurrent_step_kernel(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ pool,
+    int64_t pool_slots, const int32_t* __restrict__ slots, Tout* __restrict__ o, int H,
+    float scale) {
+  constexpr int LPR = K / 4;                     // lanes per state row
+  constexpr int RPP = 256 / LPR;                 // rows per pass of the workgroup
+  constexpr int PASSES = kDecodeRows / RPP;      // passes per workgroup
+  const int b = blockIdx.x, h = blockIdx.y, part = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int col = (tid % LPR) * 4;
+  const int rsub = tid / LPR;
+  const int row0 = part * kDecodeRows;
+  const int64_t tok = static_cast<int64_t>(b) * H + h;
+  Tout* orow = o + tok * V + row0;
+  const int slot = slots[b];
+  if (slot <= 0 || slot >= pool_slots) {  // padding: zero output, state untouched
+    if (tid < kDecodeRows) store_out(orow + tid, 0.f);
+    return;
+  }
+  float* S = pool + (static_cast<int64_t>(slot) * H + h) * (static_cast<int64_t>(V) * K) +
+             static_cast<int64_t>(row0) * K;
+
+  f32x4 s[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p)
+    s[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (p * RPP + rsub) * K + col));
+
+  float kk[4], qq[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    kk[e] = In<Tin>::ld(k + tok * K + col + e);
+    qq[e] = scale * In<Tin>::ld(q + tok * K + col + e);
+  }
+  float vv[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) vv[p] = In<Tin>::ld(v + tok * V + row0 + p * RPP + rsub);
+  const float decay = expf(g[tok]);
+  const float bt = beta[tok];
+
+  float dk[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    s[p] *= decay;
+    dk[p] = s[p][0] * kk[0] + s[p][1] * kk[1] + s[p][2] * kk[2] + s[p][3] * kk[3];
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) dk[p] = group_sum<LPR>(dk[p]);
+  float dq[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const float vn = bt * (vv[p] - dk[p]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[p][e] = fmaf(kk[e], vn, s[p][e]);
+    dq[p] = s[p][0] * qq[0] + s[p][1] * qq[1] + s[p][2] * qq[2] + s[p][3] * qq[3];
+    __builtin_nontemporal_store(s[p], reinterpret_cast<f32x4*>(S + (p * RPP + rsub) * K + col));
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) dq[p] = group_sum<LPR>(dq[p]);
+  if (tid % LPR == 0) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) store_out(orow + p * RPP + rsub, dq[p]);
+  }
+}
+
+template <int K, int V, typename Tin, typename Tout>
+static hipError_t launch_decode_t(const DecodeArgs& a) {
+  dim3 grid(a.N, a.H, V / kDecodeRows);
+  hipLaunchKernelGGL((recurrent_step_kernel<K, V, Tin, Tout>), grid, dim3(256), 0, a.stream,
+                     static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
+                     static_cast<const Tin*>(a.v), a.g, a.beta, a.pool, a.pool_slots, a.slots,
+                     static_cast<Tout*>(a.o), a.H, a.scale);
+  return hipGetLastError();
+}
+
+template <int K, int V>
+static hipError_t launch_decode_kv(const DecodeArgs& a) {
+  if (a.in_f32) {
+    return a.out_f32 ? launch_decode_t<K, V, float, float>(a) : launch_decode_t<K, V, float, __bf16>(a);
+  }
+  return a.out_f32 ? launch_decode_t<K, V, __bf16, float>(a) : launch_decode_t<K, V, __bf16, __bf16>(a);
+}
+
+hipError_t launch_decode(const DecodeArgs& a) {
+  if (a.K == 128 && a.V == 128) return launch_decode_kv<128, 128>(a);
+  if (a.K == 128 && a.V == 64) return launch_decode_kv<128, 64>(a);
+  if (a.K == 64 && a.V == 128) return launch_decode_kv<64, 128>(a);
+  return launch_decode_kv<64, 64>(a);
+}
+
+}  // namespace gdn

@@ -1,0 +1,79 @@
+// Host-side interface between the C ABI (argument validation, workspace
+// carving) and the kernel launchers. Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  float* pool;
+  int64_t pool_slots;
+  const int32_t* slots;
+  void* o;
+  int N, H, K, V;
+  float scale;
+  bool in_f32, out_f32;
+  hipStream_t stream;
+};
+
+// Chunk intermediates written by the prep kernel and read by the scan kernel,
+// stored in the MFMA fragment order the reader consumes (one 16-byte load per
+// lane and fragment). "ch" = chunk * H + head.
+//   wf  [ch][K/32 kb][4 rt][2 hi|lo][64 lane][8]  bf16: w = A diag(beta e^g) K as
+//        A operands over key block kb for output row tile rt
+//   ktf [ch][K/16 kt][2 ks][parts][64 lane][8]    bf16: K^T as A operands
+//   uf  [ch][V/16 vt][4 rt][64 lane][4]           f32 : u = A diag(beta) V as
+//        accumulator tiles
+//   pf  [ch][4 rt][2 ks][2 hi|lo][64 lane][8]     bf16: P = s (Q K^T) * E * M as
+//        A operands
+//   gc  [ch][64]                                   f32 : chunk-local inclusive
+//        cumulative sum of the log-gate (rows past the chunk end repeat g_last)
+//   info [chunk] int4 {seq, first token, rows, 0} and seq_chunk0 [n_seqs + 1]:
+//        the chunk schedule of a packed (varlen) call
+struct ChunkWs {
+  __bf16* wf;
+  __bf16* ktf;
+  float* uf;
+  __bf16* pf;
+  float* gc;
+  int4* info;
+  int* seq_chunk0;
+};
+
+struct ChunkArgs {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  void* o;
+  int n_seqs;
+  int64_t total_tokens;
+  int H, K, V;
+  float scale;
+  bool in_f32, out_f32;
+  const int32_t* cu_seqlens;  // device, or null for equal lengths
+  int64_t n_chunks;           // total chunks over all sequences
+  int T_eq;                   // equal-length mode: tokens per sequence
+  const float* h0;
+  float* ht;
+  float* pool;
+  int64_t pool_slots;
+  const int32_t* slots;
+  ChunkWs ws;
+  hipStream_t stream;
+};
+
+// Workspace layout for a call with at most max_chunks chunks.
+struct WsLayout {
+  size_t wf, ktf, uf, pf, gc, info, seq_chunk0, total;
+};
+WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, bool in_f32);
+ChunkWs carve_workspace(const WsLayout& l, void* base);
+
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_chunk_fwd(const ChunkArgs& a);
+
+}  // namespace gdn

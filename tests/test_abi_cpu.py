@@ -1,0 +1,129 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol include/gdn.h
+declares, and its host-side validation rejects bad arguments before launching
+anything (no call here reaches a kernel launch, so no GPU is needed)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from linear_attention_sequence_recompute_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libgdn.so not built")
+
+BF16, F32 = _lib.GDN_BF16, _lib.GDN_F32
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced by the failing calls below
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^\S[^()#]*?\b(gdn_\w+)\s*\(", text, re.M)
+
+
+def test_header_declares_the_boundary():
+    assert set(declared_functions()) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
+                                         "gdn_recurrent_step", "gdn_status_string"}
+
+
+def test_library_exports_every_declared_symbol():
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert set(_lib.SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4):
+        assert _lib.status_string(st).startswith("GDN_")
+    assert _lib.status_string(-99) == "GDN_UNKNOWN_STATUS"
+
+
+def test_workspace_bytes():
+    L = _lib.lib()
+    assert L.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 96, 128, BF16) == 0
+    assert L.gdn_chunk_fwd_workspace_bytes(1, 4096, 0, 128, 128, BF16) == 0
+    assert L.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 128, 7) == 0
+    b1 = L.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 128, BF16)
+    b2 = L.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 128, F32)
+    b3 = L.gdn_chunk_fwd_workspace_bytes(16, 60217, 16, 128, 128, BF16)
+    assert 0 < b1 < b2 and b3 > b1
+    # about 96 KiB of intermediates per (chunk, head) at K = V = 128
+    per = b1 / ((4096 // 64 + 1) * 16)
+    assert 90e3 < per < 110e3
+
+
+def _chunk(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE, n_seqs=1, total=256, H=2, K=64, V=64,
+                scale=1.0, in_dt=BF16, out_dt=BF16, cu=None, cu_host=None, h0=None, ht=None, pool=None,
+                pool_slots=0, slots=None, ws=FAKE, ws_bytes=0, stream=None)
+    args.update(kw)
+    a = args
+    return _lib.lib().gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["o"], a["n_seqs"], a["total"],
+                                    a["H"], a["K"], a["V"], a["scale"], a["in_dt"], a["out_dt"], a["cu"],
+                                    a["cu_host"], a["h0"], a["ht"], a["pool"], a["pool_slots"], a["slots"],
+                                    a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_chunk_fwd_validation():
+    E = _lib
+    assert _chunk(K=96) == E.GDN_EUNSUPPORTED
+    assert _chunk(V=32) == E.GDN_EUNSUPPORTED
+    assert _chunk(in_dt=5) == E.GDN_EUNSUPPORTED
+    assert _chunk(H=0) == E.GDN_EINVAL
+    assert _chunk(total=-1) == E.GDN_EINVAL
+    assert _chunk(n_seqs=3, total=256) == E.GDN_EINVAL  # not divisible into equal lengths
+    assert _chunk(q=None) == E.GDN_EINVAL
+    assert _chunk(q=FAKE + 2) == E.GDN_EINVAL  # misaligned
+    assert _chunk(h0=FAKE + 4) == E.GDN_EINVAL
+    assert _chunk(pool=FAKE, pool_slots=4, slots=None) == E.GDN_EINVAL
+    assert _chunk(pool=FAKE, pool_slots=4, slots=FAKE, h0=FAKE) == E.GDN_EINVAL
+    assert _chunk(slots=FAKE) == E.GDN_EINVAL
+    assert _chunk(ws_bytes=10) == E.GDN_EWORKSPACE
+    assert _chunk(ws=None, ws_bytes=1 << 40) == E.GDN_EWORKSPACE
+    assert _chunk(ws=FAKE + 16, ws_bytes=1 << 40) == E.GDN_EWORKSPACE
+    # empty call is a no-op success
+    assert _chunk(n_seqs=0, total=0) == E.GDN_OK
+
+
+def test_chunk_fwd_cu_seqlens_validation():
+    E = _lib
+    good = np.array([0, 100, 100, 256], dtype=np.int32)
+    ptr = good.ctypes.data
+    assert _chunk(n_seqs=3, cu=FAKE, cu_host=None) == E.GDN_EINVAL
+    assert _chunk(n_seqs=3, cu=None, cu_host=ptr) == E.GDN_EINVAL
+    bad_end = np.array([0, 100, 100, 255], dtype=np.int32)
+    assert _chunk(n_seqs=3, cu=FAKE, cu_host=bad_end.ctypes.data) == E.GDN_EINVAL
+    bad_start = np.array([1, 100, 100, 256], dtype=np.int32)
+    assert _chunk(n_seqs=3, cu=FAKE, cu_host=bad_start.ctypes.data) == E.GDN_EINVAL
+    decreasing = np.array([0, 100, 90, 256], dtype=np.int32)
+    assert _chunk(n_seqs=3, cu=FAKE, cu_host=decreasing.ctypes.data) == E.GDN_EINVAL
+    # a consistent schedule gets as far as the workspace check
+    assert _chunk(n_seqs=3, cu=FAKE, cu_host=ptr, ws_bytes=0) == E.GDN_EWORKSPACE
+
+
+def _step(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, pool=FAKE, pool_slots=8, slots=FAKE, o=FAKE, N=4, H=2,
+             K=128, V=128, scale=1.0, in_dt=BF16, out_dt=BF16, stream=None)
+    a.update(kw)
+    return _lib.lib().gdn_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["pool_slots"],
+                                         a["slots"], a["o"], a["N"], a["H"], a["K"], a["V"], a["scale"],
+                                         a["in_dt"], a["out_dt"], a["stream"])
+
+
+def test_recurrent_step_validation():
+    E = _lib
+    assert _step(K=32) == E.GDN_EUNSUPPORTED
+    assert _step(out_dt=3) == E.GDN_EUNSUPPORTED
+    assert _step(H=0) == E.GDN_EINVAL
+    assert _step(N=-1) == E.GDN_EINVAL
+    assert _step(N=0) == E.GDN_OK
+    assert _step(pool=None) == E.GDN_EINVAL
+    assert _step(slots=None) == E.GDN_EINVAL
+    assert _step(pool_slots=0) == E.GDN_EINVAL
+    assert _step(pool=FAKE + 4) == E.GDN_EINVAL
+    assert _step(q=FAKE + 1) == E.GDN_EINVAL

@@ -1,0 +1,292 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances (stated per the target): float32 outputs and final states within
+max|err| <= 2e-3 * RMS(reference) for bf16 inputs and <= 1e-4 * RMS(reference)
+for float32 inputs; bf16 outputs equal round-to-nearest-even of the float32
+output of the same call, bit for bit. Integer work (schedules, slots, padding,
+untouched pool pages) is checked exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_sequence_recompute_amd import api
+from linear_attention_sequence_recompute_amd.workloads import chunk_inputs, decode_inputs, varlen_lengths
+from tests.gpu_util import TORCH_DT, bf16_rne, dev, host, max_err_over_rms
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-3, "f32": 1e-4}
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    yield
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# --------------------------------------------------------------------- chunk
+
+def run_chunk(ci, scale, out_dtype, use_pool=False, pool_dev=None):
+    dt = TORCH_DT[ci.dtype]
+    q, k, v = dev(ci.q, dt), dev(ci.k, dt), dev(ci.v, dt)
+    g, b = dev(ci.a), dev(ci.beta)
+    kw = {}
+    if not ci.equal_length:
+        kw["cu_seqlens"] = ci.cu_seqlens.tolist()
+    elif ci.n_seqs > 1:
+        T = ci.total_tokens // ci.n_seqs
+        q, k, v = (x.view(ci.n_seqs, T, *x.shape[1:]) for x in (q, k, v))
+        g, b = (x.view(ci.n_seqs, T, -1) for x in (g, b))
+    if use_pool:
+        kw["state_pool"] = pool_dev
+        kw["state_slots"] = dev(ci.slots, torch.int32)
+    elif ci.h0 is not None:
+        kw["h0"] = dev(ci.h0)
+    o, ht = api.chunk_fwd(q, k, v, g, b, scale=scale, out_dtype=TORCH_DT[out_dtype], **kw)
+    torch.cuda.synchronize()
+    return o.reshape(ci.total_tokens, *o.shape[-2:]), ht
+
+
+def oracle_chunk(ci, scale, heads=None, seqs=None):
+    """Oracle outputs for the chosen heads of the chosen sequences (all by default)."""
+    heads = slice(None) if heads is None else heads
+    cu = ci.cu_seqlens
+    seqs = range(ci.n_seqs) if seqs is None else seqs
+    res = {}
+    for s in seqs:
+        r = slice(int(cu[s]), int(cu[s + 1]))
+        if ci.h0 is not None:
+            S0 = ci.h0[s][heads]
+        elif ci.pool is not None and ci.slots[s] > 0:
+            S0 = ci.pool[ci.slots[s]][heads]
+        else:
+            S0 = None
+        if cu[s + 1] == cu[s]:
+            res[s] = (np.zeros((0,)), S0)
+            continue
+        o, S = oracle.chunked_fwd(ci.q[r][:, heads], ci.k[r][:, heads], ci.v[r][:, heads], ci.a[r][:, heads],
+                                  ci.beta[r][:, heads], scale=scale, S0=S0)
+        res[s] = (o, S)
+    return res
+
+
+def check_chunk(ci, scale, heads=None, seqs=None, label=""):
+    """f32 output vs oracle; bf16 output == RNE(f32 output); final states."""
+    tol = TOL[ci.dtype]
+    o32, ht = run_chunk(ci, scale, "f32")
+    o16, ht2 = run_chunk(ci, scale, "bf16")
+    assert torch.equal(o16, bf16_rne(o32)), f"{label}: bf16 output is not RNE of the f32 output"
+    if ht is not None:
+        assert torch.equal(ht, ht2), f"{label}: final state depends on the output dtype"
+    ref = oracle_chunk(ci, scale, heads, seqs)
+    o32h = host(o32)
+    hsel = slice(None) if heads is None else heads
+    worst_o = worst_s = 0.0
+    for s, (o_ref, S_ref) in ref.items():
+        r = slice(int(ci.cu_seqlens[s]), int(ci.cu_seqlens[s + 1]))
+        if o_ref.size:
+            e = max_err_over_rms(o32h[r][:, hsel], o_ref)
+            worst_o = max(worst_o, e)
+        if ht is not None:
+            S_gpu = host(ht[s])[hsel]
+            S_exp = np.zeros_like(S_gpu) if S_ref is None else S_ref
+            e = max_err_over_rms(S_gpu, S_exp) if np.any(S_exp) else float(np.max(np.abs(S_gpu)))
+            worst_s = max(worst_s, e)
+    _print(f"[chunk {label}] max|do|/rms={worst_o:.3e} max|dS|/rms={worst_s:.3e} tol={tol}")
+    assert worst_o <= tol, f"{label}: output error {worst_o:.3e} > {tol}"
+    assert worst_s <= tol, f"{label}: state error {worst_s:.3e} > {tol}"
+    return o32, ht
+
+
+def test_tiny_fp32_mode():
+    """B=1, H=1, T=256 (4 chunks), K=V=64, float32 inputs and outputs, h0 = 0."""
+    ci = chunk_inputs([256], 1, 64, 64, dtype="f32", seed=1)
+    for scale in (1.0, 0.125):
+        check_chunk(ci, scale, label=f"tiny-f32 s={scale}")
+
+
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("T", [293, 64, 1])
+def test_ragged_small(K, V, T):
+    """Several chunks plus a ragged tail; all head sizes; nonzero initial state."""
+    ci = chunk_inputs([T], 3, K, V, dtype="bf16", seed=T + K + V, h0_std=0.1)
+    check_chunk(ci, K ** -0.5, label=f"ragged K={K} V={V} T={T}")
+
+
+@pytest.mark.parametrize("shift", [2.0, -4.0])
+def test_gates(shift):
+    """Short-memory (config) and long-memory gates, which stress the carry."""
+    ci = chunk_inputs([640], 4, 128, 128, dtype="bf16", seed=10, gate_shift=shift, h0_std=0.1)
+    check_chunk(ci, 128 ** -0.5, label=f"gate shift={shift}")
+
+
+def test_fp32_mode_long_memory():
+    ci = chunk_inputs([300], 2, 128, 128, dtype="f32", seed=12, gate_shift=-4.0, h0_std=0.1)
+    check_chunk(ci, 0.3, label="f32 long memory")
+
+
+def test_config_h16_t4096_full():
+    """B=1, H=16, T=4096, K=V=128, bf16: every output and the final state."""
+    ci = chunk_inputs([4096], 16, 128, 128, dtype="bf16", seed=2)
+    check_chunk(ci, 128 ** -0.5, label="H16 T4096")
+
+
+def test_config_batched_long_sampled():
+    """B=4, H=32, T=8192, K=V=128, bf16, h0 ~ N(0, 0.1^2): the launch the long
+    configuration times; the oracle checks sampled (sequence, head) pairs."""
+    ci = chunk_inputs([8192] * 4, 32, 128, 128, dtype="bf16", seed=3, h0_std=0.1)
+    check_chunk(ci, 128 ** -0.5, heads=[0, 17, 31], seqs=[0, 3], label="B4 H32 T8192 sampled")
+
+
+def test_varlen_pool_sampled():
+    """16 packed sequences, lengths uniform in [100, 6000] (not chunk-aligned),
+    initial states read from and final states written back to a state pool."""
+    lengths = varlen_lengths(16, 100, 6000, seed=4)
+    ci = chunk_inputs(lengths, 16, 128, 128, dtype="bf16", seed=4, pool_slots=17)
+    pool0 = dev(ci.pool)
+    scale = 128 ** -0.5
+    pool32 = pool0.clone()
+    o32, _ = run_chunk(ci, scale, "f32", use_pool=True, pool_dev=pool32)
+    pool16 = pool0.clone()
+    o16, _ = run_chunk(ci, scale, "bf16", use_pool=True, pool_dev=pool16)
+    assert torch.equal(o16, bf16_rne(o32))
+    assert torch.equal(pool16, pool32)
+    # slot 0 is reserved and untouched
+    assert torch.equal(pool32[0], pool0[0])
+    seqs = [int(np.argmin(lengths)), int(np.argmax(lengths)), 5]
+    heads = [0, 9]
+    ref = oracle_chunk(ci, scale, heads=heads, seqs=seqs)
+    o_h = host(o32)
+    for s in seqs:
+        r = slice(int(ci.cu_seqlens[s]), int(ci.cu_seqlens[s + 1]))
+        o_ref, S_ref = ref[s]
+        eo = max_err_over_rms(o_h[r][:, heads], o_ref)
+        es = max_err_over_rms(host(pool32[ci.slots[s]])[heads], S_ref)
+        _print(f"[varlen seq {s} len {lengths[s]}] max|do|/rms={eo:.3e} max|dS|/rms={es:.3e}")
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_varlen_edge_lengths_dense_states():
+    """Empty sequences, single tokens, exact chunk multiples and ragged tails in
+    one packed call, with dense h0/ht; every sequence checked."""
+    lengths = [0, 1, 64, 65, 0, 130, 127, 3]
+    ci = chunk_inputs(lengths, 3, 128, 128, dtype="bf16", seed=21, h0_std=0.1)
+    check_chunk(ci, 0.2, label="varlen edges")
+
+
+def test_pool_padding_slots():
+    """Sequences whose slot is <= 0 start from zero and write nothing back."""
+    lengths = [100, 70, 200]
+    ci = chunk_inputs(lengths, 2, 64, 64, dtype="bf16", seed=22, pool_slots=6, slot_ids=[3, 0, -1])
+    pool0 = dev(ci.pool)
+    pool = pool0.clone()
+    o, _ = run_chunk(ci, 0.5, "f32", use_pool=True, pool_dev=pool)
+    for s in range(6):
+        if s != 3:
+            assert torch.equal(pool[s], pool0[s]), f"slot {s} was written"
+    ref = oracle_chunk(ci, 0.5)
+    o_h = host(o)
+    for s in range(3):
+        r = slice(int(ci.cu_seqlens[s]), int(ci.cu_seqlens[s + 1]))
+        assert max_err_over_rms(o_h[r], ref[s][0]) <= TOL["bf16"]
+    assert max_err_over_rms(host(pool[3]), ref[0][1]) <= TOL["bf16"]
+
+
+def test_in_place_state_alias_and_determinism():
+    ci = chunk_inputs([200, 200], 2, 128, 128, dtype="bf16", seed=23, h0_std=0.1)
+    dt = torch.bfloat16
+    q, k, v = (dev(x, dt).view(2, 200, 2, -1) for x in (ci.q, ci.k, ci.v))
+    g, b = dev(ci.a).view(2, 200, 2), dev(ci.beta).view(2, 200, 2)
+    h0 = dev(ci.h0)
+    o1, ht1 = api.chunk_fwd(q, k, v, g, b, scale=0.1, h0=h0, out_dtype=torch.float32)
+    o2, ht2 = api.chunk_fwd(q, k, v, g, b, scale=0.1, h0=h0, out_dtype=torch.float32)
+    assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
+    state = h0.clone()
+    o3, _ = api.chunk_fwd(q, k, v, g, b, scale=0.1, h0=state, ht=state, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o1) and torch.equal(state, ht1)
+
+
+def test_decode_steps_match_chunked_prefill_on_gpu():
+    """T decode steps on one slot and one chunked call over the same tokens agree
+    (both against each other and the oracle)."""
+    T, H, K, V = 70, 2, 128, 128
+    ci = chunk_inputs([T], H, K, V, dtype="bf16", seed=24, h0_std=0.1)
+    o_c, ht = run_chunk(ci, 0.25, "f32")
+    pool = torch.zeros(3, H, V, K, device="cuda")
+    pool[1] = dev(ci.h0[0])
+    slots = torch.tensor([1], dtype=torch.int32, device="cuda")
+    outs = []
+    for t in range(T):
+        sl = slice(t, t + 1)
+        outs.append(api.recurrent_step(dev(ci.q[sl], torch.bfloat16), dev(ci.k[sl], torch.bfloat16),
+                                       dev(ci.v[sl], torch.bfloat16), dev(ci.a[sl]), dev(ci.beta[sl]), pool,
+                                       slots, scale=0.25, out_dtype=torch.float32))
+    o_d = torch.cat(outs)
+    torch.cuda.synchronize()
+    assert max_err_over_rms(host(o_d), host(o_c)) <= TOL["bf16"]
+    assert max_err_over_rms(host(pool[1]), host(ht[0])) <= TOL["bf16"]
+
+
+# -------------------------------------------------------------------- decode
+
+def run_decode(di, scale, out_dtype, pool_dev):
+    dt = TORCH_DT[di.dtype]
+    o = api.recurrent_step(dev(di.q, dt), dev(di.k, dt), dev(di.v, dt), dev(di.a), dev(di.beta), pool_dev,
+                           dev(di.slots, torch.int32), scale=scale, out_dtype=TORCH_DT[out_dtype])
+    torch.cuda.synchronize()
+    return o
+
+
+def check_decode(di, scale, label):
+    tol = TOL[di.dtype]
+    pool0 = dev(di.pool)
+    p32 = pool0.clone()
+    o32 = run_decode(di, scale, "f32", p32)
+    p16 = pool0.clone()
+    o16 = run_decode(di, scale, "bf16", p16)
+    assert torch.equal(o16, bf16_rne(o32)), f"{label}: bf16 output is not RNE of the f32 output"
+    assert torch.equal(p16, p32)
+    o_ref, pool_ref = oracle.decode_step(di.q, di.k, di.v, di.a, di.beta, di.pool, di.slots, scale=scale)
+    pad = di.slots <= 0
+    o_h = host(o32)
+    assert np.all(o_h[pad] == 0) and not np.any(np.signbit(o_h[pad])), f"{label}: padding rows not +0"
+    active = di.slots[~pad]
+    eo = max_err_over_rms(o_h[~pad], o_ref[~pad])
+    es = max_err_over_rms(host(p32[active.tolist()]), pool_ref[active])
+    untouched = np.setdiff1d(np.arange(di.pool.shape[0]), active)
+    assert torch.equal(p32[untouched.tolist()], pool0[untouched.tolist()]), f"{label}: untouched slots changed"
+    _print(f"[decode {label}] max|do|/rms={eo:.3e} max|dS|/rms={es:.3e} tol={tol}")
+    assert eo <= tol and es <= tol
+
+
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_small(K, V, dtype):
+    di = decode_inputs(N=40, H=3, K=K, V=V, pool_slots=64, dtype=dtype, seed=K + V, n_padding=6)
+    check_decode(di, K ** -0.5, f"K={K} V={V} {dtype}")
+
+
+def test_decode_config_full():
+    """N=256 requests, H=32, K=V=128, pool of 512 slots (1 GiB), 32 padding rows."""
+    di = decode_inputs(N=256, H=32, K=128, V=128, pool_slots=512, dtype="bf16", seed=5, n_padding=32)
+    check_decode(di, 128 ** -0.5, "N256 H32 pool512")
+
+
+def test_decode_out_of_range_slot_is_padding():
+    di = decode_inputs(N=8, H=2, K=64, V=64, pool_slots=16, dtype="bf16", seed=31)
+    di.slots[3] = 16  # == pool_slots: out of range
+    di.slots[5] = 10 ** 6
+    pool0 = dev(di.pool)
+    pool = pool0.clone()
+    o = run_decode(di, 0.5, "f32", pool)
+    assert torch.all(o[3] == 0) and torch.all(o[5] == 0)
+    keep = [s for s in range(16) if s not in set(di.slots[[0, 1, 2, 4, 6, 7]].tolist())]
+    assert torch.equal(pool[keep], pool0[keep])
