@@ -110,6 +110,25 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          void* stream);
 
 /*
+ * Diagnostic variant of gdn_chunk_fwd for measurement: same arguments, same
+ * results, and in addition it records three caller-created HIP events
+ * (hipEvent_t, passed as void*) on `stream`: events[0] before the first kernel,
+ * events[1] after the prep kernel (recompute_w_u: gate sums, K K^T, triangular
+ * solve, u, w and the masked intra-chunk scores), events[2] after the scan
+ * kernel (chunk_fwd_h fused with chunk_fwd_o). hipEventElapsedTime of
+ * consecutive events then gives each kernel's duration on that stream.
+ * `events` must point to three valid events; GDN_EINVAL otherwise.
+ */
+gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, void* o, int n_seqs, int64_t total_tokens,
+                                  int H, int K, int V, float scale, gdn_dtype in_dtype,
+                                  gdn_dtype out_dtype, const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_host, const float* h0, float* ht,
+                                  float* state_pool, int64_t pool_slots,
+                                  const int32_t* state_slots, void* workspace,
+                                  size_t workspace_bytes, void* stream, void* const* events);
+
+/*
  * One decode step for N requests over a slot-indexed state pool (the vLLM
  * KdaSplit page: state [slot, head, value, key], slots <= 0 are padding).
  *

@@ -6,6 +6,7 @@ computation runs in the HIP kernels of libgdn.so.
 
 from __future__ import annotations
 
+import ctypes
 from typing import Optional, Sequence
 
 import torch
@@ -55,7 +56,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               output_final_state: bool = True, ht: Optional[torch.Tensor] = None,
               state_pool: Optional[torch.Tensor] = None, state_slots: Optional[torch.Tensor] = None,
               out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None, stream=None):
+              workspace: Optional[torch.Tensor] = None, stream=None, events: Optional[Sequence[int]] = None):
     """Chunked gated delta rule forward (gdn_chunk_fwd).
 
     q, k: [B, T, H, K] (B equal-length sequences) or [Ttot, H, K] with
@@ -64,7 +65,9 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     [N, H, V, K] float32. Returns (o, ht): o shaped like v in ``out_dtype``
     (default: q's dtype); ht [N, H, V, K] float32 or None. With ``state_pool``
     ([P, H, V, K]) and ``state_slots`` ([N] int32) the initial and final states
-    live in the pool (updated in place) and ht is None.
+    live in the pool (updated in place) and ht is None. ``events``: three
+    hipEvent_t handles recorded around the prep and scan kernels
+    (gdn_chunk_fwd_profiled).
     """
     H, K = q.shape[-2], q.shape[-1]
     V = v.shape[-1]
@@ -114,12 +117,15 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     need = workspace_bytes(n_seqs, total, H, K, V, in_dt)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    st = _lib.lib().gdn_chunk_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(out), n_seqs, total, H, K, V,
-        float(K ** -0.5 if scale is None else scale), _dt(in_dt), _dt(out_dtype),
-        _ptr(cu_dev), None if cu_host is None else cu_host.data_ptr(),
-        _ptr(h0), _ptr(ht), _ptr(state_pool), pool_slots, _ptr(state_slots),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(out), n_seqs, total, H, K, V,
+            float(K ** -0.5 if scale is None else scale), _dt(in_dt), _dt(out_dtype),
+            _ptr(cu_dev), None if cu_host is None else cu_host.data_ptr(),
+            _ptr(h0), _ptr(ht), _ptr(state_pool), pool_slots, _ptr(state_slots),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if events is None:
+        st = _lib.lib().gdn_chunk_fwd(*args)
+    else:
+        st = _lib.lib().gdn_chunk_fwd_profiled(*args, (ctypes.c_void_p * 3)(*events))
     _lib.check(st, "gdn_chunk_fwd")
     return out, ht
 

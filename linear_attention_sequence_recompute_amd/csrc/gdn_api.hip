@@ -53,12 +53,16 @@ size_t gdn_chunk_fwd_workspace_bytes(int n_seqs, int64_t total_tokens, int H, in
       .total;
 }
 
-gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                         void* o, int n_seqs, int64_t total_tokens, int H, int K, int V, float scale,
-                         gdn_dtype in_dtype, gdn_dtype out_dtype, const int32_t* cu_seqlens,
-                         const int32_t* cu_seqlens_host, const float* h0, float* ht, float* state_pool,
-                         int64_t pool_slots, const int32_t* state_slots, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          void* o, int n_seqs, int64_t total_tokens, int H, int K, int V, float scale,
+                          gdn_dtype in_dtype, gdn_dtype out_dtype, const int32_t* cu_seqlens,
+                          const int32_t* cu_seqlens_host, const float* h0, float* ht, float* state_pool,
+                          int64_t pool_slots, const int32_t* state_slots, void* workspace,
+                          size_t workspace_bytes, void* stream, void* const* events) {
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !supported_dim(K) || !supported_dim(V))
     return GDN_EUNSUPPORTED;
   if (n_seqs < 0 || total_tokens < 0 || H <= 0 || H > 65535) return GDN_EINVAL;
@@ -129,7 +133,35 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
   a.slots = state_slots;
   a.ws = gdn::carve_workspace(layout, workspace);
   a.stream = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < 3; ++i) a.events[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
   return hip_status(gdn::launch_chunk_fwd(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         void* o, int n_seqs, int64_t total_tokens, int H, int K, int V, float scale,
+                         gdn_dtype in_dtype, gdn_dtype out_dtype, const int32_t* cu_seqlens,
+                         const int32_t* cu_seqlens_host, const float* h0, float* ht, float* state_pool,
+                         int64_t pool_slots, const int32_t* state_slots, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl(q, k, v, g, beta, o, n_seqs, total_tokens, H, K, V, scale, in_dtype, out_dtype,
+                        cu_seqlens, cu_seqlens_host, h0, ht, state_pool, pool_slots, state_slots, workspace,
+                        workspace_bytes, stream, nullptr);
+}
+
+gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, void* o, int n_seqs, int64_t total_tokens, int H, int K,
+                                  int V, float scale, gdn_dtype in_dtype, gdn_dtype out_dtype,
+                                  const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, const float* h0,
+                                  float* ht, float* state_pool, int64_t pool_slots, const int32_t* state_slots,
+                                  void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  if (!events || !events[0] || !events[1] || !events[2]) return GDN_EINVAL;
+  return chunk_fwd_impl(q, k, v, g, beta, o, n_seqs, total_tokens, H, K, V, scale, in_dtype, out_dtype,
+                        cu_seqlens, cu_seqlens_host, h0, ht, state_pool, pool_slots, state_slots, workspace,
+                        workspace_bytes, stream, events);
 }
 
 gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta,

@@ -27,23 +27,9 @@
 
 namespace gdn {
 
+
 constexpr int kLdt = 68;  // padded row length (elements) of the transposed LDS tiles
-
-__device__ __forceinline__ bf16x8 ld_frag(const __bf16* p) {
-  return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ void st_frag(__bf16* p, bf16x8 x) {
-  *reinterpret_cast<u32x4*>(p) = as_u32x4(x);
-}
-
-// Reads the kappa-ordered 8 elements of row `row` of a transposed LDS tile,
-// contraction block starting at column c0.
-__device__ __forceinline__ bf16x8 lds_frag(const __bf16* tile, int row, int c0, int g) {
-  const __bf16* p = tile + row * kLdt + c0;
-  u32x2 a = *reinterpret_cast<const u32x2*>(p + 4 * g);
-  u32x2 b = *reinterpret_cast<const u32x2*>(p + 16 + 4 * g);
-  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
-}
+constexpr int kPlane = 1024;  // bytes of one fragment plane (64 lanes x 16 bytes)
 
 // ---------------------------------------------------------------------------
 // Chunk schedule of a packed call: chunk c of sequence s gets global index
@@ -95,7 +81,8 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// recompute_w_u (+ the pieces of chunk_fwd_o that do not depend on the state).
+// recompute_w_u, plus the parts of chunk_fwd_o that do not depend on the state.
+// One workgroup (4 waves) per (chunk, head).
 // ---------------------------------------------------------------------------
 template <int K, int V, typename Tin>
 __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
@@ -103,9 +90,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
                                                    const float* __restrict__ beta, int H, float scale,
                                                    int T_eq, int ncs_eq, int total_tokens,
                                                    const int4* __restrict__ info, ChunkWs ws) {
-  constexpr int NP = In<Tin>::kParts;
-  __shared__ __attribute__((aligned(16))) __bf16 sKt[NP][K][kLdt];  // K^T: [key][token]
-  __shared__ __attribute__((aligned(16))) __bf16 sVt[NP][V][kLdt];  // V^T: [value][token]
+  using P = Prec<Tin>;
+  using In = typename P::In;
+  using Cmp = typename P::Cmp;
+  using Stage = typename P::Stage;
+  __shared__ __attribute__((aligned(16))) Stage sKt[K][kLdt];  // K^T: [key][token]
+  __shared__ __attribute__((aligned(16))) Stage sVt[V][kLdt];  // V^T: [value][token]
   __shared__ float sL[64][65];
   __shared__ float sA[64][65];
   __shared__ float sg[64], sb[64], sbeg[64];
@@ -139,60 +129,28 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   }
   // (2) transposed copies of the chunk's K and V (rows past the end are zero).
   {
-    const int per_row = K / 8;
-    for (int id = tid; id < kChunk * per_row; id += 256) {
-      const int t = id / per_row, c8 = (id % per_row) * 8;
-      float x[8];
-      if (t < n) {
-        const Tin* p = k + (static_cast<int64_t>(t0 + t) * H + h) * K + c8;
+    constexpr int PR = K / 8;
+    for (int id = tid; id < kChunk * PR; id += 256) {
+      const int t = id / PR, c8 = (id % PR) * 8;
+      const Tin* p = k + (static_cast<int64_t>(t0 + t) * H + h) * K + c8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = In<Tin>::ld(p + e);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        __bf16 hi, lo;
-        split1(x[e], hi, lo);
-        sKt[0][c8 + e][t] = hi;
-        if constexpr (NP == 2) sKt[NP - 1][c8 + e][t] = lo;
-      }
+      for (int e = 0; e < 8; ++e) sKt[c8 + e][t] = P::to_stage(t < n ? ld_in(p + e) : 0.f);
     }
   }
   {
-    const int per_row = V / 8;
-    for (int id = tid; id < kChunk * per_row; id += 256) {
-      const int t = id / per_row, c8 = (id % per_row) * 8;
-      float x[8];
-      if (t < n) {
-        const Tin* p = v + (static_cast<int64_t>(t0 + t) * H + h) * V + c8;
+    constexpr int PR = V / 8;
+    for (int id = tid; id < kChunk * PR; id += 256) {
+      const int t = id / PR, c8 = (id % PR) * 8;
+      const Tin* p = v + (static_cast<int64_t>(t0 + t) * H + h) * V + c8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = In<Tin>::ld(p + e);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        __bf16 hi, lo;
-        split1(x[e], hi, lo);
-        sVt[0][c8 + e][t] = hi;
-        if constexpr (NP == 2) sVt[NP - 1][c8 + e][t] = lo;
-      }
+      for (int e = 0; e < 8; ++e) sVt[c8 + e][t] = P::to_stage(t < n ? ld_in(p + e) : 0.f);
     }
   }
-  // identity init of A
   for (int idx = tid; idx < 64 * 64; idx += 256) sA[idx >> 6][idx & 63] = (idx >> 6) == (idx & 63) ? 1.f : 0.f;
   __syncthreads();
 
-  auto krow_frag = [&](const Tin* base, int D, int row, int kb, bf16x8& hi, bf16x8& lo) {
-    if (row < n) {
-      In<Tin>::row_frag(base + (static_cast<int64_t>(t0 + row) * H + h) * D + 32 * kb, lg, hi, lo);
-    } else {
-      hi = zero_bf16x8();
-      lo = zero_bf16x8();
-    }
+  auto row_in = [&](const Tin* base, int row, int kb) -> In {
+    return row < n ? P::in_row(base + (static_cast<int64_t>(t0 + row) * H + h) * K + 32 * kb, lg) : P::in_zero();
   };
 
   // (3) L = StrictLower(diag(beta) K K^T * E): the 10 lower 16x16 tiles.
@@ -201,12 +159,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
     const int bj = tix - (bi * (bi + 1)) / 2;
     f32x4 acc = zero4();
 #pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) {
-      bf16x8 ahi, alo, bhi, blo;
-      krow_frag(k, K, 16 * bi + lc, kb, ahi, alo);
-      krow_frag(k, K, 16 * bj + lc, kb, bhi, blo);
-      acc = mma_split<NP, NP>(ahi, alo, bhi, blo, acc);
-    }
+    for (int kb = 0; kb < K / 32; ++kb) acc = mma(row_in(k, 16 * bi + lc, kb), row_in(k, 16 * bj + lc, kb), acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * bi + 4 * lg + r, j = 16 * bj + lc;
@@ -214,38 +167,27 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
     }
   }
 
-  // (4) P = s (Q K^T) * E * M, computed transposed so that accumulator tiles are
-  // directly the A operands of P: wave w owns output row tile w.
+  // (4) P = s (Q K^T) * E * M, computed transposed so that pairs of accumulator
+  // tiles are directly the A operands of P; wave w owns output row tile w.
   {
     const int bi = w;
-    const int nks = bi >= 2 ? 2 : 1;
     for (int ks = 0; ks < 2; ++ks) {
       f32x4 d[2] = {zero4(), zero4()};
-      if (ks < nks) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int bt = 2 * ks + half;
-          if (bt > bi) continue;
+      for (int half = 0; half < 2; ++half) {
+        const int bt = 2 * ks + half;
+        if (bt > bi) continue;
 #pragma unroll
-          for (int kb = 0; kb < K / 32; ++kb) {
-            bf16x8 ahi, alo, bhi, blo;
-            krow_frag(k, K, 16 * bt + lc, kb, ahi, alo);
-            krow_frag(q, K, 16 * bi + lc, kb, bhi, blo);
-            d[half] = mma_split<NP, NP>(ahi, alo, bhi, blo, d[half]);
-          }
-          const int i = 16 * bi + lc;
+        for (int kb = 0; kb < K / 32; ++kb)
+          d[half] = mma(row_in(k, 16 * bt + lc, kb), row_in(q, 16 * bi + lc, kb), d[half]);
+        const int i = 16 * bi + lc;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int tp = 16 * bt + 4 * lg + r;
-            d[half][r] = tp <= i ? scale * d[half][r] * __expf(sg[i] - sg[tp]) : 0.f;
-          }
+        for (int r = 0; r < 4; ++r) {
+          const int tp = 16 * bt + 4 * lg + r;
+          d[half][r] = tp <= i ? scale * d[half][r] * __expf(sg[i] - sg[tp]) : 0.f;
         }
       }
-      bf16x8 phi, plo;
-      split_tiles(d[0], d[1], phi, plo);
-      __bf16* dst = ws.pf + ch * 8192 + ((bi * 2 + ks) * 2) * 512 + lane * 8;
-      st_frag(dst, phi);
-      st_frag(dst + 512, plo);
+      P::st_cmp(ws.pf + ch * (8 * 2 * kPlane) + (bi * 2 + ks) * 2 * kPlane, lane, P::cmp_tiles(d[0], d[1]));
     }
   }
   __syncthreads();
@@ -265,13 +207,13 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
     }
   }
 
-  // (6) u = A diag(beta) V, wave w owns output row tile w (all value tiles).
+  // (6) u = A diag(beta) V; wave w owns output row tile w (all value tiles).
   {
     constexpr int NVT = V / 16;
     f32x4 acc[NVT];
 #pragma unroll
     for (int vt = 0; vt < NVT; ++vt) acc[vt] = zero4();
-    const int nks = w >= 2 ? 2 : 1;
+    const int nks = w >= 2 ? 2 : 1;  // A is lower triangular
     for (int ks = 0; ks < nks; ++ks) {
       float x[8];
 #pragma unroll
@@ -279,14 +221,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
         const int m = 32 * ks + kappa(lg, e);
         x[e] = sA[16 * w + lc][m] * sb[m];
       }
-      bf16x8 ahi, alo;
-      split8(x, ahi, alo);
+      const Cmp a = P::cmp8(x);
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) {
-        const bf16x8 bhi = lds_frag(&sVt[0][0][0], 16 * vt + lc, 32 * ks, lg);
-        const bf16x8 blo = NP == 2 ? lds_frag(&sVt[NP - 1][0][0], 16 * vt + lc, 32 * ks, lg) : zero_bf16x8();
-        acc[vt] = mma_split<2, NP>(ahi, alo, bhi, blo, acc[vt]);
-      }
+      for (int vt = 0; vt < NVT; ++vt) acc[vt] = mma(a, P::in_lds(&sVt[16 * vt + lc][32 * ks], lg), acc[vt]);
     }
 #pragma unroll
     for (int vt = 0; vt < NVT; ++vt)
@@ -308,33 +245,20 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
         const int m = 32 * ks + kappa(lg, e);
         x[e] = sA[16 * w + lc][m] * sbeg[m];
       }
-      bf16x8 bhi, blo;
-      split8(x, bhi, blo);
+      const Cmp b = P::cmp8(x);
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-        const bf16x8 ahi = lds_frag(&sKt[0][0][0], 16 * kt + lc, 32 * ks, lg);
-        const bf16x8 alo = NP == 2 ? lds_frag(&sKt[NP - 1][0][0], 16 * kt + lc, 32 * ks, lg) : zero_bf16x8();
-        acc[kt] = mma_split<NP, 2>(ahi, alo, bhi, blo, acc[kt]);
-      }
+      for (int kt = 0; kt < NKT; ++kt) acc[kt] = mma(P::in_lds(&sKt[16 * kt + lc][32 * ks], lg), b, acc[kt]);
     }
 #pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) {
-      bf16x8 hi, lo;
-      split_tiles(acc[2 * kb], acc[2 * kb + 1], hi, lo);
-      __bf16* dst = ws.wf + ch * (K * 128) + ((kb * 4 + w) * 2) * 512 + lane * 8;
-      st_frag(dst, hi);
-      st_frag(dst + 512, lo);
-    }
+    for (int kb = 0; kb < K / 32; ++kb)
+      P::st_cmp(ws.wf + ch * (K * 256) + (kb * 4 + w) * 2 * kPlane, lane, P::cmp_tiles(acc[2 * kb], acc[2 * kb + 1]));
   }
 
   // (8) K^T as A operands for the state update of the scan kernel.
   for (int idx = w; idx < (K / 16) * 2; idx += 4) {
     const int kt = idx >> 1, ks = idx & 1;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const bf16x8 f = lds_frag(&sKt[p][0][0], 16 * kt + lc, 32 * ks, lg);
-      st_frag(ws.ktf + ch * (K * 64 * NP) + ((kt * 2 + ks) * NP + p) * 512 + lane * 8, f);
-    }
+    P::st_in(ws.ktf + ch * (K * 128 * P::kInPlanes) + (kt * 2 + ks) * P::kInPlanes * kPlane, lane,
+             P::in_lds(&sKt[16 * kt + lc][32 * ks], lg));
   }
 }
 
@@ -345,15 +269,19 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
 template <int K, int V, int NSUB, typename Tin, typename Tout>
 __global__ __launch_bounds__(K / 32 * 64) void scan_kernel(
     const Tin* __restrict__ q, Tout* __restrict__ o, int H, float scale, int n_seqs, int T_eq,
-    int ncs_eq, int total_tokens, int n_chunks, const int32_t* __restrict__ cu, const float* __restrict__ h0, float* __restrict__ ht,
-    float* __restrict__ pool, int64_t pool_slots, const int32_t* __restrict__ slots, ChunkWs ws) {
-  constexpr int NW = K / 32;          // waves; wave w owns key rows [32w, 32w + 32)
-  constexpr int NP = In<Tin>::kParts;
-  constexpr int RT = 4 / NW;          // output row tiles each wave finishes
+    int ncs_eq, int total_tokens, int n_chunks, const int32_t* __restrict__ cu, const float* __restrict__ h0,
+    float* __restrict__ ht, float* __restrict__ pool, int64_t pool_slots, const int32_t* __restrict__ slots,
+    ChunkWs ws) {
+  using P = Prec<Tin>;
+  using In = typename P::In;
+  using Cmp = typename P::Cmp;
+  using Tile = typename P::Tile;
+  constexpr int NW = K / 32;  // waves; wave w owns key rows [32w, 32w + 32)
+  constexpr int RT = 4 / NW;  // output row tiles each wave finishes
   constexpr int NSL = V / (16 * NSUB);
-  __shared__ f32x4 sX[NW][4][NSUB][64];  // partial w h over this wave's key rows
-  __shared__ f32x4 sY[NW][4][NSUB][64];  // partial q h
-  __shared__ u32x2 sVn[4][NSUB][4][64];  // v_new hi, lo and gated v_new hi, lo (4 bf16 each)
+  __shared__ f32x4 sX[NW][4][NSUB][64];   // partial w h over this wave's key rows
+  __shared__ f32x4 sY[NW][4][NSUB][64];   // partial q h
+  __shared__ Tile sVn[4][NSUB][2][64];    // v_new and gated v_new, B-operand ready
 
   // Workgroups of one (sequence, head) share an XCD (blockIdx % 8) and its L2.
   const int bid = blockIdx.x;
@@ -412,29 +340,22 @@ __global__ __launch_bounds__(K / 32 * 64) void scan_kernel(
     const float* gch = ws.gc + ch * kChunk;
     const float gL = gch[kChunk - 1];
 
-    // (1) the state as hi/lo B operands of this wave's 32-key block
-    bf16x8 hhi[NSUB], hlo[NSUB];
+    // (1) the state as the B operand of this wave's 32-key block
+    Cmp hb[NSUB];
 #pragma unroll
-    for (int ns = 0; ns < NSUB; ++ns) split_tiles(hs[ns][0], hs[ns][1], hhi[ns], hlo[ns]);
+    for (int ns = 0; ns < NSUB; ++ns) hb[ns] = P::cmp_tiles(hs[ns][0], hs[ns][1]);
 
     // (2) partial w h and q h over this wave's key rows, all 64 chunk rows
-    const __bf16* wf = ws.wf + ch * (K * 128) + (w * 4 * 2) * 512 + lane * 8;
+    const uint8_t* wf = ws.wf + ch * (K * 256) + (w * 4) * 2 * kPlane;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const bf16x8 whi = ld_frag(wf + (rt * 2) * 512);
-      const bf16x8 wlo = ld_frag(wf + (rt * 2 + 1) * 512);
-      bf16x8 qhi, qlo;
+      const Cmp wfr = P::ld_cmp(wf + rt * 2 * kPlane, lane);
       const int row = 16 * rt + lc;
-      if (row < n) {
-        In<Tin>::row_frag(q + (static_cast<int64_t>(t0 + row) * H + h) * K + 32 * w, lg, qhi, qlo);
-      } else {
-        qhi = zero_bf16x8();
-        qlo = zero_bf16x8();
-      }
+      const In qf = row < n ? P::in_row(q + (static_cast<int64_t>(t0 + row) * H + h) * K + 32 * w, lg) : P::in_zero();
 #pragma unroll
       for (int ns = 0; ns < NSUB; ++ns) {
-        sX[w][rt][ns][lane] = mma_split<2, 2>(whi, wlo, hhi[ns], hlo[ns], zero4());
-        sY[w][rt][ns][lane] = mma_split<NP, 2>(qhi, qlo, hhi[ns], hlo[ns], zero4());
+        sX[w][rt][ns][lane] = mma(wfr, hb[ns], zero4());
+        sY[w][rt][ns][lane] = mma(qf, hb[ns], zero4());
       }
     }
     __syncthreads();
@@ -457,52 +378,35 @@ __global__ __launch_bounds__(K / 32 * 64) void scan_kernel(
         }
         const f32x4 u =
             *reinterpret_cast<const f32x4*>(ws.uf + ch * (V * 64) + (((slice * NSUB + ns) * 4 + rt) * 64 + lane) * 4);
-        bf16x4 vnh, vnl, vgh, vgl;
+        f32x4 vn, vg;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float vn = u[r] - x[r];
-          const float vg = vn * __expf(gL - gr[r]);
+          vn[r] = u[r] - x[r];
+          vg[r] = vn[r] * __expf(gL - gr[r]);
           acc_o[rho][ns][r] = scale * __expf(gr[r]) * y[r];
-          __bf16 a, b;
-          split1(vn, a, b);
-          vnh[r] = a;
-          vnl[r] = b;
-          split1(vg, a, b);
-          vgh[r] = a;
-          vgl[r] = b;
         }
-        sVn[rt][ns][0][lane] = __builtin_bit_cast(u32x2, vnh);
-        sVn[rt][ns][1][lane] = __builtin_bit_cast(u32x2, vnl);
-        sVn[rt][ns][2][lane] = __builtin_bit_cast(u32x2, vgh);
-        sVn[rt][ns][3][lane] = __builtin_bit_cast(u32x2, vgl);
+        sVn[rt][ns][0][lane] = P::tile(vn);
+        sVn[rt][ns][1][lane] = P::tile(vg);
       }
     }
     __syncthreads();
 
-    auto vfrag = [&](int ks, int ns, int part) {
-      const u32x2 a = sVn[2 * ks][ns][part][lane];
-      const u32x2 b = sVn[2 * ks + 1][ns][part][lane];
-      return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
-    };
-
-    // (4) state update: h <- e^{g_last} h + K^T v_gated, decay folded into the
-    // accumulator before the products are added.
+    // (4) state update: h <- e^{g_last} h + K^T v_gated, the decay folded into
+    // the accumulator before the products are added.
     const float dL = __expf(gL);
-    const __bf16* ktf = ws.ktf + ch * (K * 64 * NP) + lane * 8;
+    const uint8_t* ktf = ws.ktf + ch * (K * 128 * P::kInPlanes);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int kt = 2 * w + tt;
-      bf16x8 khi[2], klo[2];
+      In kf[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        khi[ks] = ld_frag(ktf + ((kt * 2 + ks) * NP) * 512);
-        klo[ks] = NP == 2 ? ld_frag(ktf + ((kt * 2 + ks) * NP + NP - 1) * 512) : zero_bf16x8();
-      }
+      for (int ks = 0; ks < 2; ++ks) kf[ks] = P::ld_in_frag(ktf + (kt * 2 + ks) * P::kInPlanes * kPlane, lane);
 #pragma unroll
       for (int ns = 0; ns < NSUB; ++ns) {
         f32x4 acc = hs[ns][tt] * dL;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) acc = mma_split<NP, 2>(khi[ks], klo[ks], vfrag(ks, ns, 2), vfrag(ks, ns, 3), acc);
+        for (int ks = 0; ks < 2; ++ks)
+          acc = mma(kf[ks], P::cmp_from(sVn[2 * ks][ns][1][lane], sVn[2 * ks + 1][ns][1][lane]), acc);
         hs[ns][tt] = acc;
       }
     }
@@ -511,15 +415,14 @@ __global__ __launch_bounds__(K / 32 * 64) void scan_kernel(
 #pragma unroll
     for (int rho = 0; rho < RT; ++rho) {
       const int rt = w * RT + rho;
-      const __bf16* pf = ws.pf + ch * 8192 + (rt * 2 * 2) * 512 + lane * 8;
+      const uint8_t* pf = ws.pf + ch * (8 * 2 * kPlane) + rt * 2 * 2 * kPlane;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         if (ks == 1 && rt < 2) continue;  // P is causal: columns >= 32 vanish for rows < 32
-        const bf16x8 phi = ld_frag(pf + (ks * 2) * 512);
-        const bf16x8 plo = ld_frag(pf + (ks * 2 + 1) * 512);
+        const Cmp pfr = P::ld_cmp(pf + ks * 2 * kPlane, lane);
 #pragma unroll
         for (int ns = 0; ns < NSUB; ++ns)
-          acc_o[rho][ns] = mma_split<2, 2>(phi, plo, vfrag(ks, ns, 0), vfrag(ks, ns, 1), acc_o[rho][ns]);
+          acc_o[rho][ns] = mma(pfr, P::cmp_from(sVn[2 * ks][ns][0][lane], sVn[2 * ks + 1][ns][0][lane]), acc_o[rho][ns]);
       }
 #pragma unroll
       for (int ns = 0; ns < NSUB; ++ns) {
@@ -577,10 +480,10 @@ WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, b
 ChunkWs carve_workspace(const WsLayout& l, void* base) {
   char* b = static_cast<char*>(base);
   ChunkWs ws;
-  ws.wf = reinterpret_cast<__bf16*>(b + l.wf);
-  ws.ktf = reinterpret_cast<__bf16*>(b + l.ktf);
+  ws.wf = reinterpret_cast<uint8_t*>(b + l.wf);
+  ws.ktf = reinterpret_cast<uint8_t*>(b + l.ktf);
   ws.uf = reinterpret_cast<float*>(b + l.uf);
-  ws.pf = reinterpret_cast<__bf16*>(b + l.pf);
+  ws.pf = reinterpret_cast<uint8_t*>(b + l.pf);
   ws.gc = reinterpret_cast<float*>(b + l.gc);
   ws.info = reinterpret_cast<int4*>(b + l.info);
   ws.seq_chunk0 = reinterpret_cast<int*>(b + l.seq_chunk0);
@@ -593,6 +496,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
   constexpr int NSL = V / (16 * NSUB);
   const bool varlen = a.cu_seqlens != nullptr;
   const int ncs_eq = varlen ? 0 : (a.T_eq + kChunk - 1) / kChunk;
+  if (a.events[0]) (void)hipEventRecord(a.events[0], a.stream);
   if (varlen) {
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(256), 0, a.stream, a.cu_seqlens, a.n_seqs,
                        static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.ws.seq_chunk0,
@@ -604,12 +508,16 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
                        static_cast<const Tin*>(a.v), a.g, a.beta, a.H, a.scale, a.T_eq, ncs_eq,
                        static_cast<int>(a.total_tokens), varlen ? a.ws.info : nullptr, a.ws);
   }
+  if (a.events[1]) (void)hipEventRecord(a.events[1], a.stream);
   const int64_t pairs = static_cast<int64_t>(a.n_seqs) * a.H;
   const int64_t blocks = 8 * NSL * ((pairs + 7) / 8);
   hipLaunchKernelGGL((scan_kernel<K, V, NSUB, Tin, Tout>), dim3(static_cast<unsigned>(blocks)), dim3(K / 32 * 64),
                      0, a.stream, static_cast<const Tin*>(a.q), static_cast<Tout*>(a.o), a.H, a.scale, a.n_seqs,
-                     a.T_eq, ncs_eq, static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0, a.ht, a.pool, a.pool_slots, a.slots, a.ws);
-  return hipGetLastError();
+                     a.T_eq, ncs_eq, static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks),
+                     a.cu_seqlens, a.h0, a.ht, a.pool, a.pool_slots, a.slots, a.ws);
+  const hipError_t err = hipGetLastError();
+  if (a.events[2]) (void)hipEventRecord(a.events[2], a.stream);
+  return err;
 }
 
 template <int K, int V>

@@ -1,6 +1,7 @@
 // Device-side building blocks shared by the gfx950 kernels of the gated delta
-// rule library: vector types, the 16x16x32 bf16 MFMA, fp32 -> bf16 hi/lo
-// operand splitting, and the fragment index map all kernels agree on.
+// rule library: vector types, the MFMA instructions used, the fragment index map
+// all kernels agree on, and the precision policies (how inputs and computed
+// operands enter the matrix cores).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,7 +18,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kChunk = 64;  // tokens per chunk (WarpDrive page, "Pipeline": C = 64)
 
 // ---------------------------------------------------------------------------
-// MFMA fragment conventions (v_mfma_f32_16x16x32_bf16, wave64).
+// MFMA fragment conventions (wave64, 16 x 16 output tiles).
 //
 // Lane l is split as g = l >> 4 (0..3) and c = l & 15.
 //  * Accumulator D (16 x 16 fp32): lane (g, c) holds D[4g + r][c], r = 0..3.
@@ -27,20 +28,30 @@ constexpr int kChunk = 64;  // tokens per chunk (WarpDrive page, "Pipeline": C =
 //    kappa(g, e).
 // kappa(g, e) = 4g + e for e < 4 and 16 + 4g + (e - 4) for e >= 4. Any bijection
 // of the 32 contraction indices gives the same product as long as A and B use
-// the same one; this one makes the two accumulator tiles covering rows
-// [0, 16) and [16, 32) of a 32-row block exactly the B operand of that block
+// the same one; this one makes the two accumulator tiles covering rows [0, 16)
+// and [16, 32) of a 32-row block exactly the B operand of that block
 // ({tile0[0..3], tile1[0..3]} per lane), so a state held as accumulators feeds
 // the next product with no data movement.
+//
+// With v_mfma_f32_16x16x32_bf16 a lane's 8 values go in one instruction. With
+// v_mfma_f32_16x16x4f32 (lane (g, c) supplies contraction index g of row/column
+// c) the same 32-deep product takes 8 instructions, the j-th feeding each lane's
+// element j: together they cover every (g, e) pair once.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int kappa(int g, int e) { return e < 4 ? 4 * g + e : 12 + 4 * g + e; }
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
 __device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 b) { return __builtin_bit_cast(u32x4, b); }
+__device__ __forceinline__ bf16x8 zero_bf16x8() { return as_bf16x8(u32x4{0u, 0u, 0u, 0u}); }
 
 // x ~= hi + lo with hi = RNE_bf16(x), lo = RNE_bf16(x - hi); |x - hi - lo| <= 2^-17 |x|.
 __device__ __forceinline__ void split1(float x, __bf16& hi, __bf16& lo) {
@@ -48,81 +59,45 @@ __device__ __forceinline__ void split1(float x, __bf16& hi, __bf16& lo) {
   lo = to_bf16(x - static_cast<float>(hi));
 }
 
-// Pack two accumulator tiles (rows [0,16) and [16,32) of a 32-row block) into the
-// hi/lo B operand of that block.
-__device__ __forceinline__ void split_tiles(const f32x4& t0, const f32x4& t1, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    __bf16 h, l;
-    split1(t0[e], h, l);
-    hi[e] = h;
-    lo[e] = l;
-    split1(t1[e], h, l);
-    hi[4 + e] = h;
-    lo[4 + e] = l;
-  }
-}
-
-__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    __bf16 h, l;
-    split1(x[e], h, l);
-    hi[e] = h;
-    lo[e] = l;
-  }
-}
-
-// Products of split operands. A "part" count of 1 means the operand is exact
-// in bf16 (lo == 0 and skipped); 2 means hi + lo. The lo x lo term is dropped.
-template <int PA, int PB>
-__device__ __forceinline__ f32x4 mma_split(bf16x8 ahi, bf16x8 alo, bf16x8 bhi, bf16x8 blo, f32x4 acc) {
-  if constexpr (PB == 2) acc = mfma(ahi, blo, acc);
-  if constexpr (PA == 2) acc = mfma(alo, bhi, acc);
-  return mfma(ahi, bhi, acc);
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
-__device__ __forceinline__ u32x4 as_u32x4(bf16x8 b) { return __builtin_bit_cast(u32x4, b); }
-
-__device__ __forceinline__ bf16x8 zero_bf16x8() { return as_bf16x8(u32x4{0u, 0u, 0u, 0u}); }
-
-// Load the 8 contraction-ordered elements kappa(g, 0..7) of a row whose
-// 32-element block starts at p (element type bf16): two 8-byte loads.
-__device__ __forceinline__ bf16x8 load_row_frag_bf16(const __bf16* p, int g) {
-  u32x2 a = *reinterpret_cast<const u32x2*>(p + 4 * g);
-  u32x2 b = *reinterpret_cast<const u32x2*>(p + 16 + 4 * g);
-  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
-}
-
-// Same for a float32 row, split into hi/lo parts.
-__device__ __forceinline__ void load_row_frag_f32(const float* p, int g, bf16x8& hi, bf16x8& lo) {
-  f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * g);
-  f32x4 b = *reinterpret_cast<const f32x4*>(p + 16 + 4 * g);
-  float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  split8(x, hi, lo);
-}
-
-// Input element loading, for bf16 or float32 tensors.
-template <typename T>
-struct In;
-template <>
-struct In<__bf16> {
-  static constexpr int kParts = 1;
-  __device__ static __forceinline__ float ld(const __bf16* p) { return static_cast<float>(*p); }
-  __device__ static __forceinline__ void row_frag(const __bf16* p, int g, bf16x8& hi, bf16x8& lo) {
-    hi = load_row_frag_bf16(p, g);
-    lo = zero_bf16x8();
-  }
+// ---------------------------------------------------------------------------
+// Operand fragments: the 8 kappa-ordered values a lane contributes.
+// ---------------------------------------------------------------------------
+struct FragB {  // values exact in bf16 (bf16 inputs)
+  bf16x8 x;
 };
-template <>
-struct In<float> {
-  static constexpr int kParts = 2;
-  __device__ static __forceinline__ float ld(const float* p) { return *p; }
-  __device__ static __forceinline__ void row_frag(const float* p, int g, bf16x8& hi, bf16x8& lo) {
-    load_row_frag_f32(p, g, hi, lo);
-  }
+struct FragS {  // fp32 values carried as bf16 hi + lo (about 16 significant bits)
+  bf16x8 hi, lo;
 };
+struct FragF {  // fp32 values (elements 0..3 in a, 4..7 in b)
+  f32x4 a, b;
+};
+
+// Products accumulated in fp32. The lo x lo term of two split operands is dropped.
+__device__ __forceinline__ f32x4 mma(const FragB& a, const FragB& b, f32x4 acc) { return mfma(a.x, b.x, acc); }
+__device__ __forceinline__ f32x4 mma(const FragB& a, const FragS& b, f32x4 acc) {
+  acc = mfma(a.x, b.lo, acc);
+  return mfma(a.x, b.hi, acc);
+}
+__device__ __forceinline__ f32x4 mma(const FragS& a, const FragB& b, f32x4 acc) {
+  acc = mfma(a.lo, b.x, acc);
+  return mfma(a.hi, b.x, acc);
+}
+__device__ __forceinline__ f32x4 mma(const FragS& a, const FragS& b, f32x4 acc) {
+  acc = mfma(a.hi, b.lo, acc);
+  acc = mfma(a.lo, b.hi, acc);
+  return mfma(a.hi, b.hi, acc);
+}
+__device__ __forceinline__ f32x4 mma(const FragF& a, const FragF& b, f32x4 acc) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = mfma_f32(a.a[e], b.a[e], acc);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = mfma_f32(a.b[e], b.b[e], acc);
+  return acc;
+}
+
+// Scalar element loads of an input tensor.
+__device__ __forceinline__ float ld_in(const __bf16* p) { return static_cast<float>(*p); }
+__device__ __forceinline__ float ld_in(const float* p) { return *p; }
 
 template <typename T>
 __device__ __forceinline__ void store_out(T* p, float x);
@@ -130,6 +105,116 @@ template <>
 __device__ __forceinline__ void store_out<float>(float* p, float x) { *p = x; }
 template <>
 __device__ __forceinline__ void store_out<__bf16>(__bf16* p, float x) { *p = to_bf16(x); }
+
+// ---------------------------------------------------------------------------
+// Precision policies. Prec<Tin> names the fragment types and conversions for
+// inputs of type Tin:
+//   In    fragments of q, k, v (exact: bf16 -> FragB, float -> FragF);
+//   Cmp   fragments of computed operands (bf16 mode: FragS; float mode: FragF);
+//   Stage element type of transposed input tiles staged in LDS;
+//   Tile  an accumulator slice (4 rows of one column) in the form two of them
+//         make a Cmp B operand (exchanged through LDS).
+// A fragment is stored in memory as planes of 64 lanes x 16 bytes: FragB uses
+// one plane, FragS (hi, lo) and FragF (a, b) two, so one lane's 16-byte load of
+// a plane is fully coalesced across the wave.
+// ---------------------------------------------------------------------------
+template <typename Tin>
+struct Prec;
+
+template <>
+struct Prec<__bf16> {
+  using In = FragB;
+  using Cmp = FragS;
+  using Stage = __bf16;
+  using Tile = u32x4;  // {hi bf16x4, lo bf16x4}
+  static constexpr int kInPlanes = 1;
+
+  __device__ static __forceinline__ In in_row(const __bf16* p, int g) {
+    const u32x2 a = *reinterpret_cast<const u32x2*>(p + 4 * g);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(p + 16 + 4 * g);
+    return In{as_bf16x8(u32x4{a[0], a[1], b[0], b[1]})};
+  }
+  __device__ static __forceinline__ In in_zero() { return In{zero_bf16x8()}; }
+  __device__ static __forceinline__ In in_lds(const __bf16* row, int g) { return in_row(row, g); }
+  __device__ static __forceinline__ Stage to_stage(float x) { return to_bf16(x); }
+  __device__ static __forceinline__ void st_in(void* base, int lane, const In& f) {
+    reinterpret_cast<u32x4*>(base)[lane] = as_u32x4(f.x);
+  }
+  __device__ static __forceinline__ In ld_in_frag(const void* base, int lane) {
+    return In{as_bf16x8(reinterpret_cast<const u32x4*>(base)[lane])};
+  }
+
+  __device__ static __forceinline__ Cmp cmp8(const float (&x)[8]) {
+    Cmp f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 h, l;
+      split1(x[e], h, l);
+      f.hi[e] = h;
+      f.lo[e] = l;
+    }
+    return f;
+  }
+  __device__ static __forceinline__ Cmp cmp_tiles(const f32x4& t0, const f32x4& t1) {
+    const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+    return cmp8(x);
+  }
+  __device__ static __forceinline__ void st_cmp(void* base, int lane, const Cmp& f) {
+    reinterpret_cast<u32x4*>(base)[lane] = as_u32x4(f.hi);
+    reinterpret_cast<u32x4*>(base)[64 + lane] = as_u32x4(f.lo);
+  }
+  __device__ static __forceinline__ Cmp ld_cmp(const void* base, int lane) {
+    return Cmp{as_bf16x8(reinterpret_cast<const u32x4*>(base)[lane]),
+               as_bf16x8(reinterpret_cast<const u32x4*>(base)[64 + lane])};
+  }
+  __device__ static __forceinline__ Tile tile(const f32x4& t) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      __bf16 a, b;
+      split1(t[r], a, b);
+      h[r] = a;
+      l[r] = b;
+    }
+    const u32x2 hu = __builtin_bit_cast(u32x2, h), lu = __builtin_bit_cast(u32x2, l);
+    return Tile{hu[0], hu[1], lu[0], lu[1]};
+  }
+  __device__ static __forceinline__ Cmp cmp_from(const Tile& t0, const Tile& t1) {
+    return Cmp{as_bf16x8(u32x4{t0[0], t0[1], t1[0], t1[1]}), as_bf16x8(u32x4{t0[2], t0[3], t1[2], t1[3]})};
+  }
+};
+
+template <>
+struct Prec<float> {
+  using In = FragF;
+  using Cmp = FragF;
+  using Stage = float;
+  using Tile = f32x4;
+  static constexpr int kInPlanes = 2;
+
+  __device__ static __forceinline__ In in_row(const float* p, int g) {
+    return In{*reinterpret_cast<const f32x4*>(p + 4 * g), *reinterpret_cast<const f32x4*>(p + 16 + 4 * g)};
+  }
+  __device__ static __forceinline__ In in_zero() { return In{zero4(), zero4()}; }
+  __device__ static __forceinline__ In in_lds(const float* row, int g) { return in_row(row, g); }
+  __device__ static __forceinline__ Stage to_stage(float x) { return x; }
+  __device__ static __forceinline__ void st_in(void* base, int lane, const In& f) { st_cmp(base, lane, f); }
+  __device__ static __forceinline__ In ld_in_frag(const void* base, int lane) { return ld_cmp(base, lane); }
+
+  __device__ static __forceinline__ Cmp cmp8(const float (&x)[8]) {
+    return Cmp{f32x4{x[0], x[1], x[2], x[3]}, f32x4{x[4], x[5], x[6], x[7]}};
+  }
+  __device__ static __forceinline__ Cmp cmp_tiles(const f32x4& t0, const f32x4& t1) { return Cmp{t0, t1}; }
+  __device__ static __forceinline__ void st_cmp(void* base, int lane, const Cmp& f) {
+    reinterpret_cast<f32x4*>(base)[lane] = f.a;
+    reinterpret_cast<f32x4*>(base)[64 + lane] = f.b;
+  }
+  __device__ static __forceinline__ Cmp ld_cmp(const void* base, int lane) {
+    return Cmp{reinterpret_cast<const f32x4*>(base)[lane], reinterpret_cast<const f32x4*>(base)[64 + lane]};
+  }
+  __device__ static __forceinline__ Tile tile(const f32x4& t) { return t; }
+  __device__ static __forceinline__ Cmp cmp_from(const Tile& t0, const Tile& t1) { return Cmp{t0, t1}; }
+};
 
 // Wave-wide inclusive prefix sum over 64 lanes.
 __device__ __forceinline__ float wave_inclusive_scan(float x) {

@@ -59,12 +59,12 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
   float kk[4], qq[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    kk[e] = In<Tin>::ld(k + tok * K + col + e);
-    qq[e] = scale * In<Tin>::ld(q + tok * K + col + e);
+    kk[e] = ld_in(k + tok * K + col + e);
+    qq[e] = scale * ld_in(q + tok * K + col + e);
   }
   float vv[PASSES];
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) vv[p] = In<Tin>::ld(v + tok * V + row0 + p * RPP + rsub);
+  for (int p = 0; p < PASSES; ++p) vv[p] = ld_in(v + tok * V + row0 + p * RPP + rsub);
   const float decay = expf(g[tok]);
   const float bt = beta[tok];
 

@@ -22,24 +22,24 @@ struct DecodeArgs {
 };
 
 // Chunk intermediates written by the prep kernel and read by the scan kernel,
-// stored in the MFMA fragment order the reader consumes (one 16-byte load per
-// lane and fragment). "ch" = chunk * H + head.
-//   wf  [ch][K/32 kb][4 rt][2 hi|lo][64 lane][8]  bf16: w = A diag(beta e^g) K as
-//        A operands over key block kb for output row tile rt
-//   ktf [ch][K/16 kt][2 ks][parts][64 lane][8]    bf16: K^T as A operands
-//   uf  [ch][V/16 vt][4 rt][64 lane][4]           f32 : u = A diag(beta) V as
-//        accumulator tiles
-//   pf  [ch][4 rt][2 ks][2 hi|lo][64 lane][8]     bf16: P = s (Q K^T) * E * M as
-//        A operands
-//   gc  [ch][64]                                   f32 : chunk-local inclusive
+// stored in the MFMA fragment order the reader consumes. A fragment is stored as
+// planes of [64 lanes][16 bytes] (see Prec in gdn_common.h: two planes for a
+// computed operand, one or two for an input). "ch" = chunk * H + head.
+//   wf  [ch][K/32 kb][4 rt][2 planes]      w = A diag(beta e^g) K as A operands
+//        over key block kb for output row tile rt
+//   ktf [ch][K/16 kt][2 ks][input planes]  K^T as A operands
+//   uf  [ch][V/16 vt][4 rt][64 lane][4]    f32 u = A diag(beta) V as accumulator
+//        tiles
+//   pf  [ch][4 rt][2 ks][2 planes]         P = s (Q K^T) * E * M as A operands
+//   gc  [ch][64]                           f32 chunk-local inclusive
 //        cumulative sum of the log-gate (rows past the chunk end repeat g_last)
 //   info [chunk] int4 {seq, first token, rows, 0} and seq_chunk0 [n_seqs + 1]:
 //        the chunk schedule of a packed (varlen) call
 struct ChunkWs {
-  __bf16* wf;
-  __bf16* ktf;
+  uint8_t* wf;
+  uint8_t* ktf;
   float* uf;
-  __bf16* pf;
+  uint8_t* pf;
   float* gc;
   int4* info;
   int* seq_chunk0;
@@ -64,6 +64,7 @@ struct ChunkArgs {
   const int32_t* slots;
   ChunkWs ws;
   hipStream_t stream;
+  hipEvent_t events[3];  // optional: recorded before prep, after prep, after scan
 };
 
 // Workspace layout for a call with at most max_chunks chunks.

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
-                                         "gdn_recurrent_step", "gdn_status_string"}
+                                         "gdn_chunk_fwd_profiled", "gdn_recurrent_step", "gdn_status_string"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -88,6 +88,14 @@ def test_chunk_fwd_validation():
     assert _chunk(ws=FAKE + 16, ws_bytes=1 << 40) == E.GDN_EWORKSPACE
     # empty call is a no-op success
     assert _chunk(n_seqs=0, total=0) == E.GDN_OK
+
+
+def test_chunk_fwd_profiled_needs_events():
+    L = _lib.lib()
+    args = [FAKE] * 6 + [1, 256, 2, 64, 64, 1.0, BF16, BF16, None, None, None, None, None, 0, None, FAKE, 1 << 40, None]
+    assert L.gdn_chunk_fwd_profiled(*args, None) == _lib.GDN_EINVAL
+    ev = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
+    assert L.gdn_chunk_fwd_profiled(*args, ev) == _lib.GDN_EINVAL
 
 
 def test_chunk_fwd_cu_seqlens_validation():
