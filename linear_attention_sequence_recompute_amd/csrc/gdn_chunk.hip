@@ -22,6 +22,8 @@
 // computed operand (A diag(beta), A diag(beta e^g), w, h, v_new, P) enters as a
 // bf16 hi + lo pair with fp32 accumulation, which keeps about 16 significant bits.
 // Float32 inputs are split the same way.
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
@@ -94,10 +96,10 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   using In = typename P::In;
   using Cmp = typename P::Cmp;
   using Stage = typename P::Stage;
+  constexpr int LDA = 68;  // row stride (floats) of the L / A tile: 16-byte aligned rows
   __shared__ __attribute__((aligned(16))) Stage sKt[K][kLdt];  // K^T: [key][token]
   __shared__ __attribute__((aligned(16))) Stage sVt[V][kLdt];  // V^T: [value][token]
-  __shared__ float sL[64][65];
-  __shared__ float sA[64][65];
+  __shared__ __attribute__((aligned(16))) float sLA[64][LDA];  // L, then A = (I + L)^-1
   __shared__ float sg[64], sb[64], sbeg[64];
 
   const int c = blockIdx.x, h = blockIdx.y;
@@ -116,54 +118,93 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   }
   const int64_t ch = static_cast<int64_t>(c) * H + h;
 
-  // (1) chunk-local inclusive cumsum of the log-gate; beta; beta e^g.
+  // (1) chunk-local inclusive cumsum of the log-gate; beta; beta e^g; the gate
+  // factors e^g and e^{g_last - g} the scan kernel applies.
   if (w == 0) {
     const int64_t gi = static_cast<int64_t>(t0 + lane) * H + h;
     const float a = lane < n ? g[gi] : 0.f;
     const float gl = wave_inclusive_scan(a);
+    const float glast = __shfl(gl, 63, 64);
     const float bl = lane < n ? beta[gi] : 0.f;
     sg[lane] = gl;
     sb[lane] = bl;
     sbeg[lane] = bl * __expf(gl);
-    ws.gc[ch * kChunk + lane] = gl;
+    ws.gx[ch * 128 + lane] = __expf(gl);
+    ws.gx[ch * 128 + 64 + lane] = __expf(glast - gl);
   }
-  // (2) transposed copies of the chunk's K and V (rows past the end are zero).
-  {
-    constexpr int PR = K / 8;
-    for (int id = tid; id < kChunk * PR; id += 256) {
-      const int t = id / PR, c8 = (id % PR) * 8;
-      const Tin* p = k + (static_cast<int64_t>(t0 + t) * H + h) * K + c8;
+  // Row fragments of all of K and of this wave's 16 rows of Q, loaded up front so
+  // their latency overlaps the staging below.
+  In kf[4][K / 32], qf[K / 32];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sKt[c8 + e][t] = P::to_stage(t < n ? ld_in(p + e) : 0.f);
-    }
-  }
-  {
-    constexpr int PR = V / 8;
-    for (int id = tid; id < kChunk * PR; id += 256) {
-      const int t = id / PR, c8 = (id % PR) * 8;
-      const Tin* p = v + (static_cast<int64_t>(t0 + t) * H + h) * V + c8;
+  for (int b = 0; b < 4; ++b) {
+    const int row = 16 * b + lc;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sVt[c8 + e][t] = P::to_stage(t < n ? ld_in(p + e) : 0.f);
-    }
+    for (int kb = 0; kb < K / 32; ++kb)
+      kf[b][kb] = row < n ? P::in_row(k + (static_cast<int64_t>(t0 + row) * H + h) * K + 32 * kb, lg) : P::in_zero();
   }
-  for (int idx = tid; idx < 64 * 64; idx += 256) sA[idx >> 6][idx & 63] = (idx >> 6) == (idx & 63) ? 1.f : 0.f;
+#pragma unroll
+  for (int kb = 0; kb < K / 32; ++kb) {
+    const int row = 16 * w + lc;
+    qf[kb] = row < n ? P::in_row(q + (static_cast<int64_t>(t0 + row) * H + h) * K + 32 * kb, lg) : P::in_zero();
+  }
+
+  // (2) transposed copies of the chunk's K and V (rows past the end are zero),
+  // 16-byte global loads, all issued before the LDS writes.
+  auto stage = [&](const Tin* src, auto dim, Stage* dst) {
+    constexpr int D = decltype(dim)::value;
+    constexpr int PR = D / 8;
+    constexpr int ITERS = kChunk * PR / 256;
+    float x[ITERS][8];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int id = tid + 256 * it;
+      const int t = id / PR, c8 = (id % PR) * 8;
+      if (t < n) {
+        const Tin* p = src + (static_cast<int64_t>(t0 + t) * H + h) * D + c8;
+        if constexpr (sizeof(Tin) == 2) {
+          const bf16x8 r = as_bf16x8(*reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[it][e] = static_cast<float>(r[e]);
+        } else {
+          const f32x4 r0 = *reinterpret_cast<const f32x4*>(p);
+          const f32x4 r1 = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[it][e] = r0[e];
+            x[it][4 + e] = r1[e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[it][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int id = tid + 256 * it;
+      const int t = id / PR, c8 = (id % PR) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[(c8 + e) * kLdt + t] = P::to_stage(x[it][e]);
+    }
+  };
+  stage(k, std::integral_constant<int, K>{}, &sKt[0][0]);
+  stage(v, std::integral_constant<int, V>{}, &sVt[0][0]);
+  for (int idx = tid; idx < 64 * LDA; idx += 256) (&sLA[0][0])[idx] = 0.f;
   __syncthreads();
 
-  auto row_in = [&](const Tin* base, int row, int kb) -> In {
-    return row < n ? P::in_row(base + (static_cast<int64_t>(t0 + row) * H + h) * K + 32 * kb, lg) : P::in_zero();
-  };
-
   // (3) L = StrictLower(diag(beta) K K^T * E): the 10 lower 16x16 tiles.
-  for (int tix = w; tix < 10; tix += 4) {
+#pragma unroll
+  for (int tix = 0; tix < 10; ++tix) {
+    if ((tix & 3) != w) continue;
     const int bi = tix == 0 ? 0 : tix < 3 ? 1 : tix < 6 ? 2 : 3;
     const int bj = tix - (bi * (bi + 1)) / 2;
     f32x4 acc = zero4();
 #pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) acc = mma(row_in(k, 16 * bi + lc, kb), row_in(k, 16 * bj + lc, kb), acc);
+    for (int kb = 0; kb < K / 32; ++kb) acc = mma(kf[bi][kb], kf[bj][kb], acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * bi + 4 * lg + r, j = 16 * bj + lc;
-      sL[i][j] = j < i ? sb[i] * acc[r] * __expf(sg[i] - sg[j]) : 0.f;
+      if (j < i) sLA[i][j] = sb[i] * acc[r] * __expf(sg[i] - sg[j]);
     }
   }
 
@@ -171,6 +212,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   // tiles are directly the A operands of P; wave w owns output row tile w.
   {
     const int bi = w;
+#pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       f32x4 d[2] = {zero4(), zero4()};
 #pragma unroll
@@ -178,8 +220,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
         const int bt = 2 * ks + half;
         if (bt > bi) continue;
 #pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb)
-          d[half] = mma(row_in(k, 16 * bt + lc, kb), row_in(q, 16 * bi + lc, kb), d[half]);
+        for (int kb = 0; kb < K / 32; ++kb) d[half] = mma(kf[bt][kb], qf[kb], d[half]);
         const int i = 16 * bi + lc;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -192,20 +233,39 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   }
   __syncthreads();
 
-  // (5) A = (I + L)^-1 by forward substitution, one row per step: thread
-  // (j, part) sums a quarter of row i's terms for column j.
+  // (5) A = (I + L)^-1 by forward substitution without barriers: the four lanes
+  // (j, part) of column j are adjacent in one wave; lane part keeps rows
+  // [16 part, 16 part + 16) of column j in registers. Row i of (I + L) A = I gives
+  // A[i][j] = -sum_m L[i][m] A[m][j]; each lane sums its 16 rows (L[i][m] = 0 for
+  // m >= i, and A[m][j] not yet known is 0) and the four parts are added with
+  // shuffles.
   {
     const int j = tid >> 2, part = tid & 3;
+    float a[16];
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) a[kk] = (16 * part + kk == j) ? 1.f : 0.f;
+#pragma unroll
     for (int i = 1; i < 64; ++i) {
-      float s = 0.f;
-      if (j < i)
-        for (int m = j + part; m < i; m += 4) s += sL[i][m] * sA[m][j];
+      const f32x4* row = reinterpret_cast<const f32x4*>(&sLA[i][16 * part]);
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const f32x4 l4 = row[qq];
+        s0 = fmaf(l4[0], a[4 * qq + 0], s0);
+        s1 = fmaf(l4[1], a[4 * qq + 1], s1);
+        s2 = fmaf(l4[2], a[4 * qq + 2], s2);
+        s3 = fmaf(l4[3], a[4 * qq + 3], s3);
+      }
+      float s = (s0 + s1) + (s2 + s3);
       s += __shfl_xor(s, 1, 64);
       s += __shfl_xor(s, 2, 64);
-      if (part == 0 && j < i) sA[i][j] = -s;
-      __syncthreads();
+      if (part == (i >> 4) && i > j) a[i & 15] = -s;
     }
+    __syncthreads();  // every lane is done reading L
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) sLA[16 * part + kk][j] = a[kk];
   }
+  __syncthreads();
 
   // (6) u = A diag(beta) V; wave w owns output row tile w (all value tiles).
   {
@@ -219,7 +279,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int m = 32 * ks + kappa(lg, e);
-        x[e] = sA[16 * w + lc][m] * sb[m];
+        x[e] = sLA[16 * w + lc][m] * sb[m];
       }
       const Cmp a = P::cmp8(x);
 #pragma unroll
@@ -232,6 +292,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
 
   // (7) w = A diag(beta e^g) K, computed as w^T = K^T (A diag(beta e^g))^T so that
   // pairs of accumulator tiles are the A operands of w over a 32-key block.
+  // Stored as [row tile][key block] fragments.
   {
     constexpr int NKT = K / 16;
     f32x4 acc[NKT];
@@ -243,7 +304,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int m = 32 * ks + kappa(lg, e);
-        x[e] = sA[16 * w + lc][m] * sbeg[m];
+        x[e] = sLA[16 * w + lc][m] * sbeg[m];
       }
       const Cmp b = P::cmp8(x);
 #pragma unroll
@@ -251,7 +312,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
     }
 #pragma unroll
     for (int kb = 0; kb < K / 32; ++kb)
-      P::st_cmp(ws.wf + ch * (K * 256) + (kb * 4 + w) * 2 * kPlane, lane, P::cmp_tiles(acc[2 * kb], acc[2 * kb + 1]));
+      P::st_cmp(ws.wf + ch * (K * 256) + (w * (K / 32) + kb) * 2 * kPlane, lane,
+                P::cmp_tiles(acc[2 * kb], acc[2 * kb + 1]));
   }
 
   // (8) K^T as A operands for the state update of the scan kernel.
@@ -264,24 +326,59 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
 
 // ---------------------------------------------------------------------------
 // chunk_fwd_h with chunk_fwd_o fused: sequential over the chunks of one
-// sequence, for one head and one slice of 16 * NSUB value columns.
+// sequence, for one head and one slice of 16 value columns.
+//
+// A workgroup has 2 K/32 waves in two roles that meet at two barriers per chunk:
+//  * chain wave w (w < K/32) owns key rows [32w, 32w + 32) of the state slice as
+//    two accumulator tiles and output row tiles [w RT, (w+1) RT). It publishes its
+//    state block in LDS as a B operand; after the first barrier it forms
+//    w h for its row tiles over all key blocks, then v_new = u - w h and the gated
+//    v_new, which it publishes; after the second barrier it updates its state rows
+//    with K^T v_gated, the decay e^{g_last} folded into the accumulator first.
+//  * output wave (w >= K/32) owns the same row tiles: after the first barrier it
+//    forms q h from the published state blocks (the inter-chunk term), after the
+//    second it adds P v_new (the intra-chunk term) and stores its output rows.
+// One chain wave and one output wave share each SIMD, so the output products fill
+// the gaps of the sequential chain. Every accumulation is split over independent
+// accumulators (one per key block) so dependent matrix-core instructions do not
+// serialize, and each wave loads its next chunk's operands one chunk ahead.
 // ---------------------------------------------------------------------------
-template <int K, int V, int NSUB, typename Tin, typename Tout>
-__global__ __launch_bounds__(K / 32 * 64) void scan_kernel(
+template <int K, typename Tin>
+struct ChainOps {
+  using P = Prec<Tin>;
+  static constexpr int NW = K / 32;
+  static constexpr int RT = 4 / NW;
+  typename P::Cmp w[RT][NW];   // w rows of my row tiles, per key block
+  typename P::In kt[2][2];     // K^T for my key rows (two 16-row tiles) x token blocks
+  f32x4 u[RT];                 // u of my row tiles in this slice
+  f32x4 egl[RT];               // e^{g_last - g} at my rows
+  float dL;                    // e^{g_last}
+};
+
+template <int K, typename Tin>
+struct OutOps {
+  using P = Prec<Tin>;
+  static constexpr int NW = K / 32;
+  static constexpr int RT = 4 / NW;
+  typename P::In q[RT][NW];    // q rows of my row tiles, per key block
+  typename P::Cmp p[RT][2];    // P rows of my row tiles, per token block
+  f32x4 eg[RT];                // e^g at my rows
+};
+
+template <int K, int V, typename Tin, typename Tout>
+__global__ __launch_bounds__(K / 32 * 128) void scan_kernel(
     const Tin* __restrict__ q, Tout* __restrict__ o, int H, float scale, int n_seqs, int T_eq,
     int ncs_eq, int total_tokens, int n_chunks, const int32_t* __restrict__ cu, const float* __restrict__ h0,
     float* __restrict__ ht, float* __restrict__ pool, int64_t pool_slots, const int32_t* __restrict__ slots,
     ChunkWs ws) {
   using P = Prec<Tin>;
-  using In = typename P::In;
   using Cmp = typename P::Cmp;
-  using Tile = typename P::Tile;
-  constexpr int NW = K / 32;  // waves; wave w owns key rows [32w, 32w + 32)
-  constexpr int RT = 4 / NW;  // output row tiles each wave finishes
-  constexpr int NSL = V / (16 * NSUB);
-  __shared__ f32x4 sX[NW][4][NSUB][64];   // partial w h over this wave's key rows
-  __shared__ f32x4 sY[NW][4][NSUB][64];   // partial q h
-  __shared__ Tile sVn[4][NSUB][2][64];    // v_new and gated v_new, B-operand ready
+  constexpr int NW = K / 32;
+  constexpr int RT = 4 / NW;
+  constexpr int NSL = V / 16;
+  // State blocks and (gated) v_new, both stored as B-operand fragments (two planes).
+  __shared__ u32x4 sH[NW][2][64];
+  __shared__ u32x4 sV[2][2][2][64];  // [token block][v_new | gated v_new][plane][lane]
 
   // Workgroups of one (sequence, head) share an XCD (blockIdx % 8) and its L2.
   const int bid = blockIdx.x;
@@ -291,8 +388,11 @@ __global__ __launch_bounds__(K / 32 * 64) void scan_kernel(
   if (pair >= n_seqs * H) return;
   const int seq = pair / H, h = pair % H;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool chain = wv < NW;
+  const int w = chain ? wv : wv - NW;  // key block (chain) / row-tile group (output)
   const int lg = lane >> 4, lc = lane & 15;
+  const int vcol = slice * 16 + lc;
   int start, len, chunk0;
   if (cu) {
     start = cu[seq];
@@ -307,144 +407,170 @@ __global__ __launch_bounds__(K / 32 * 64) void scan_kernel(
   }
   const int nc = (len + kChunk - 1) / kChunk;
 
-  const float* s_in = nullptr;
-  float* s_out = nullptr;
-  const int64_t page = static_cast<int64_t>(V) * K;
-  if (pool) {
-    const int s = slots[seq];
-    if (s > 0 && s < pool_slots) {
-      s_in = pool + (static_cast<int64_t>(s) * H + h) * page;
-      s_out = pool + (static_cast<int64_t>(s) * H + h) * page;
+  if (chain) {
+    using Ops = ChainOps<K, Tin>;
+    const float* s_in = nullptr;
+    float* s_out = nullptr;
+    const int64_t page = static_cast<int64_t>(V) * K;
+    if (pool) {
+      const int s = slots[seq];
+      if (s > 0 && s < pool_slots) {
+        s_in = pool + (static_cast<int64_t>(s) * H + h) * page;
+        s_out = pool + (static_cast<int64_t>(s) * H + h) * page;
+      }
+    } else {
+      if (h0) s_in = h0 + (static_cast<int64_t>(seq) * H + h) * page;
+      if (ht) s_out = ht + (static_cast<int64_t>(seq) * H + h) * page;
     }
-  } else {
-    if (h0) s_in = h0 + (static_cast<int64_t>(seq) * H + h) * page;
-    if (ht) s_out = ht + (static_cast<int64_t>(seq) * H + h) * page;
-  }
-
-  // State slice h[key][value] = S[value][key]: two accumulator tiles per 16 columns.
-  f32x4 hs[NSUB][2];
-#pragma unroll
-  for (int ns = 0; ns < NSUB; ++ns) {
-    const int vcol = (slice * NSUB + ns) * 16 + lc;
+    // State slice h[key][value] = S[value][key]: two accumulator tiles.
+    f32x4 hs[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int k0 = 32 * w + 16 * tt + 4 * lg;
-      hs[ns][tt] = s_in ? *reinterpret_cast<const f32x4*>(s_in + static_cast<int64_t>(vcol) * K + k0) : zero4();
+      hs[tt] = s_in ? *reinterpret_cast<const f32x4*>(s_in + static_cast<int64_t>(vcol) * K + k0) : zero4();
     }
-  }
 
-  for (int c = 0; c < nc; ++c) {
-    const int64_t ch = static_cast<int64_t>(chunk0 + c) * H + h;
-    const int t0 = start + kChunk * c;
-    const int n = min(kChunk, len - kChunk * c);
-    const float* gch = ws.gc + ch * kChunk;
-    const float gL = gch[kChunk - 1];
-
-    // (1) the state as the B operand of this wave's 32-key block
-    Cmp hb[NSUB];
+    // Loads are unconditional (a chunk index past the end is clamped to the last
+    // chunk) so that the wait counters can keep the next chunk's loads in flight.
+    auto load = [&](Ops& op, int c_req) {
+      const int c = min(c_req, nc - 1);
+      const int64_t ch = static_cast<int64_t>(chunk0 + c) * H + h;
 #pragma unroll
-    for (int ns = 0; ns < NSUB; ++ns) hb[ns] = P::cmp_tiles(hs[ns][0], hs[ns][1]);
-
-    // (2) partial w h and q h over this wave's key rows, all 64 chunk rows
-    const uint8_t* wf = ws.wf + ch * (K * 256) + (w * 4) * 2 * kPlane;
+      for (int rho = 0; rho < RT; ++rho) {
+        const int rt = w * RT + rho;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const Cmp wfr = P::ld_cmp(wf + rt * 2 * kPlane, lane);
-      const int row = 16 * rt + lc;
-      const In qf = row < n ? P::in_row(q + (static_cast<int64_t>(t0 + row) * H + h) * K + 32 * w, lg) : P::in_zero();
-#pragma unroll
-      for (int ns = 0; ns < NSUB; ++ns) {
-        sX[w][rt][ns][lane] = mma(wfr, hb[ns], zero4());
-        sY[w][rt][ns][lane] = mma(qf, hb[ns], zero4());
+        for (int kb = 0; kb < NW; ++kb)
+          op.w[rho][kb] = P::ld_cmp(ws.wf + ch * (K * 256) + (rt * NW + kb) * 2 * kPlane, lane);
+        op.u[rho] = *reinterpret_cast<const f32x4*>(ws.uf + ch * (V * 64) + ((slice * 4 + rt) * 64 + lane) * 4);
+        op.egl[rho] = *reinterpret_cast<const f32x4*>(ws.gx + ch * 128 + 64 + 16 * rt + 4 * lg);
       }
-    }
-    __syncthreads();
-
-    // (3) this wave's output row tiles: v_new = u - w h, gated v_new, inter part
-    f32x4 acc_o[RT][NSUB];
 #pragma unroll
-    for (int rho = 0; rho < RT; ++rho) {
-      const int rt = w * RT + rho;
-      float gr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) gr[r] = gch[16 * rt + 4 * lg + r];
-#pragma unroll
-      for (int ns = 0; ns < NSUB; ++ns) {
-        f32x4 x = sX[0][rt][ns][lane], y = sY[0][rt][ns][lane];
-#pragma unroll
-        for (int ww = 1; ww < NW; ++ww) {
-          x += sX[ww][rt][ns][lane];
-          y += sY[ww][rt][ns][lane];
-        }
-        const f32x4 u =
-            *reinterpret_cast<const f32x4*>(ws.uf + ch * (V * 64) + (((slice * NSUB + ns) * 4 + rt) * 64 + lane) * 4);
-        f32x4 vn, vg;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          vn[r] = u[r] - x[r];
-          vg[r] = vn[r] * __expf(gL - gr[r]);
-          acc_o[rho][ns][r] = scale * __expf(gr[r]) * y[r];
-        }
-        sVn[rt][ns][0][lane] = P::tile(vn);
-        sVn[rt][ns][1][lane] = P::tile(vg);
-      }
-    }
-    __syncthreads();
-
-    // (4) state update: h <- e^{g_last} h + K^T v_gated, the decay folded into
-    // the accumulator before the products are added.
-    const float dL = __expf(gL);
-    const uint8_t* ktf = ws.ktf + ch * (K * 128 * P::kInPlanes);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int kt = 2 * w + tt;
-      In kf[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) kf[ks] = P::ld_in_frag(ktf + (kt * 2 + ks) * P::kInPlanes * kPlane, lane);
-#pragma unroll
-      for (int ns = 0; ns < NSUB; ++ns) {
-        f32x4 acc = hs[ns][tt] * dL;
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          acc = mma(kf[ks], P::cmp_from(sVn[2 * ks][ns][1][lane], sVn[2 * ks + 1][ns][1][lane]), acc);
-        hs[ns][tt] = acc;
-      }
-    }
+          op.kt[tt][ks] = P::ld_in_frag(
+              ws.ktf + ch * (K * 128 * P::kInPlanes) + ((2 * w + tt) * 2 + ks) * P::kInPlanes * kPlane, lane);
+      op.dL = ws.gx[ch * 128 + 63];
+    };
 
-    // (5) o = inter + P v_new for this wave's row tiles
+    auto step = [&](const Ops& cur) {
+      // (1) publish this wave's state block as a B operand
+      const Cmp hown = P::cmp_tiles(hs[0], hs[1]);
+      P::st_cmp(&sH[w][0][0], lane, hown);
+      __syncthreads();
+      // (2) w h for my row tiles over all key blocks; v_new and gated v_new
+      Cmp hb[NW];
 #pragma unroll
-    for (int rho = 0; rho < RT; ++rho) {
-      const int rt = w * RT + rho;
-      const uint8_t* pf = ws.pf + ch * (8 * 2 * kPlane) + rt * 2 * 2 * kPlane;
+      for (int kb = 0; kb < NW; ++kb) hb[kb] = kb == w ? hown : P::ld_cmp(&sH[kb][0][0], lane);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (ks == 1 && rt < 2) continue;  // P is causal: columns >= 32 vanish for rows < 32
-        const Cmp pfr = P::ld_cmp(pf + ks * 2 * kPlane, lane);
+      for (int rho = 0; rho < RT; ++rho) {
+        const int rt = w * RT + rho;
+        f32x4 xp[NW];
 #pragma unroll
-        for (int ns = 0; ns < NSUB; ++ns)
-          acc_o[rho][ns] = mma(pfr, P::cmp_from(sVn[2 * ks][ns][0][lane], sVn[2 * ks + 1][ns][0][lane]), acc_o[rho][ns]);
+        for (int kb = 0; kb < NW; ++kb) xp[kb] = mma(cur.w[rho][kb], hb[kb], zero4());
+        f32x4 x = xp[0];
+#pragma unroll
+        for (int kb = 1; kb < NW; ++kb) x += xp[kb];
+        const f32x4 vn = cur.u[rho] - x;
+        P::st_tile(&sV[rt >> 1][0][0][0], lane, rt & 1, vn);
+        P::st_tile(&sV[rt >> 1][1][0][0], lane, rt & 1, vn * cur.egl[rho]);
       }
+      __syncthreads();
+      // (3) h <- e^{g_last} h + K^T v_gated
+      const Cmp vg0 = P::ld_cmp(&sV[0][1][0][0], lane);
+      const Cmp vg1 = P::ld_cmp(&sV[1][1][0][0], lane);
 #pragma unroll
-      for (int ns = 0; ns < NSUB; ++ns) {
-        const int vcol = (slice * NSUB + ns) * 16 + lc;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * rt + 4 * lg + r;
-          if (row < n) store_out(o + (static_cast<int64_t>(t0 + row) * H + h) * V + vcol, acc_o[rho][ns][r]);
-        }
+      for (int tt = 0; tt < 2; ++tt) {
+        const f32x4 a0 = mma(cur.kt[tt][0], vg0, hs[tt] * cur.dL);
+        const f32x4 a1 = mma(cur.kt[tt][1], vg1, zero4());
+        hs[tt] = a0 + a1;
       }
-    }
-  }
+    };
 
-  if (s_out) {
-#pragma unroll
-    for (int ns = 0; ns < NSUB; ++ns) {
-      const int vcol = (slice * NSUB + ns) * 16 + lc;
+    Ops bufA, bufB;
+    if (nc > 0) load(bufA, 0);
+    for (int c = 0; c < nc; c += 2) {
+      load(bufB, c + 1);
+      step(bufA);
+      if (c + 1 >= nc) break;
+      load(bufA, c + 2);
+      step(bufB);
+    }
+    if (s_out) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int k0 = 32 * w + 16 * tt + 4 * lg;
-        *reinterpret_cast<f32x4*>(s_out + static_cast<int64_t>(vcol) * K + k0) = hs[ns][tt];
+        *reinterpret_cast<f32x4*>(s_out + static_cast<int64_t>(vcol) * K + k0) = hs[tt];
       }
+    }
+  } else {
+    using Ops = OutOps<K, Tin>;
+    auto load = [&](Ops& op, int c_req) {
+      const int c = min(c_req, nc - 1);
+      const int64_t ch = static_cast<int64_t>(chunk0 + c) * H + h;
+      const int t0 = start + kChunk * c;
+      const int n = min(kChunk, len - kChunk * c);
+#pragma unroll
+      for (int rho = 0; rho < RT; ++rho) {
+        const int rt = w * RT + rho;
+        const int row = 16 * rt + lc;
+        const int rowc = min(row, n - 1);  // rows past the end: load a valid row, then zero
+#pragma unroll
+        for (int kb = 0; kb < NW; ++kb) {
+          op.q[rho][kb] = P::in_row(q + (static_cast<int64_t>(t0 + rowc) * H + h) * K + 32 * kb, lg);
+          if (row >= n) op.q[rho][kb] = P::in_zero();
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          op.p[rho][ks] = P::ld_cmp(ws.pf + ch * (8 * 2 * kPlane) + (rt * 2 + ks) * 2 * kPlane, lane);
+        op.eg[rho] = *reinterpret_cast<const f32x4*>(ws.gx + ch * 128 + 16 * rt + 4 * lg);
+      }
+    };
+
+    auto step = [&](const Ops& cur, int c) {
+      const int t0 = start + kChunk * c;
+      const int n = min(kChunk, len - kChunk * c);
+      __syncthreads();
+      // (1) inter-chunk term s e^g (q h) from the published state blocks
+      Cmp hb[NW];
+#pragma unroll
+      for (int kb = 0; kb < NW; ++kb) hb[kb] = P::ld_cmp(&sH[kb][0][0], lane);
+      f32x4 acc[RT];
+#pragma unroll
+      for (int rho = 0; rho < RT; ++rho) {
+        f32x4 yp[NW];
+#pragma unroll
+        for (int kb = 0; kb < NW; ++kb) yp[kb] = mma(cur.q[rho][kb], hb[kb], zero4());
+        f32x4 y = yp[0];
+#pragma unroll
+        for (int kb = 1; kb < NW; ++kb) y += yp[kb];
+        acc[rho] = (scale * cur.eg[rho]) * y;
+      }
+      __syncthreads();
+      // (2) intra-chunk term P v_new; store
+      const Cmp vn0 = P::ld_cmp(&sV[0][0][0][0], lane);
+#pragma unroll
+      for (int rho = 0; rho < RT; ++rho) {
+        const int rt = w * RT + rho;
+        f32x4 o1 = zero4();
+        if (rt >= 2) o1 = mma(cur.p[rho][1], P::ld_cmp(&sV[1][0][0][0], lane), o1);  // P is causal
+        acc[rho] = mma(cur.p[rho][0], vn0, acc[rho]) + o1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * rt + 4 * lg + r;
+          if (row < n) store_out(o + (static_cast<int64_t>(t0 + row) * H + h) * V + vcol, acc[rho][r]);
+        }
+      }
+    };
+
+    Ops bufA, bufB;
+    if (nc > 0) load(bufA, 0);
+    for (int c = 0; c < nc; c += 2) {
+      load(bufB, c + 1);
+      step(bufA, c);
+      if (c + 1 >= nc) break;
+      load(bufA, c + 2);
+      step(bufB, c + 1);
     }
   }
 }
@@ -467,8 +593,8 @@ WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, b
   off = align256(off + nch * V * 64 * 4);
   l.pf = off;
   off = align256(off + nch * 8192 * 2);
-  l.gc = off;
-  off = align256(off + nch * kChunk * 4);
+  l.gx = off;
+  off = align256(off + nch * 2 * kChunk * 4);
   l.info = off;
   off = align256(off + static_cast<size_t>(max_chunks) * 16);
   l.seq_chunk0 = off;
@@ -484,7 +610,7 @@ ChunkWs carve_workspace(const WsLayout& l, void* base) {
   ws.ktf = reinterpret_cast<uint8_t*>(b + l.ktf);
   ws.uf = reinterpret_cast<float*>(b + l.uf);
   ws.pf = reinterpret_cast<uint8_t*>(b + l.pf);
-  ws.gc = reinterpret_cast<float*>(b + l.gc);
+  ws.gx = reinterpret_cast<float*>(b + l.gx);
   ws.info = reinterpret_cast<int4*>(b + l.info);
   ws.seq_chunk0 = reinterpret_cast<int*>(b + l.seq_chunk0);
   return ws;
@@ -492,8 +618,7 @@ ChunkWs carve_workspace(const WsLayout& l, void* base) {
 
 template <int K, int V, typename Tin, typename Tout>
 static hipError_t launch_chunk_t(const ChunkArgs& a) {
-  constexpr int NSUB = 1;
-  constexpr int NSL = V / (16 * NSUB);
+  constexpr int NSL = V / 16;
   const bool varlen = a.cu_seqlens != nullptr;
   const int ncs_eq = varlen ? 0 : (a.T_eq + kChunk - 1) / kChunk;
   if (a.events[0]) (void)hipEventRecord(a.events[0], a.stream);
@@ -511,7 +636,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
   if (a.events[1]) (void)hipEventRecord(a.events[1], a.stream);
   const int64_t pairs = static_cast<int64_t>(a.n_seqs) * a.H;
   const int64_t blocks = 8 * NSL * ((pairs + 7) / 8);
-  hipLaunchKernelGGL((scan_kernel<K, V, NSUB, Tin, Tout>), dim3(static_cast<unsigned>(blocks)), dim3(K / 32 * 64),
+  hipLaunchKernelGGL((scan_kernel<K, V, Tin, Tout>), dim3(static_cast<unsigned>(blocks)), dim3(K / 32 * 128),
                      0, a.stream, static_cast<const Tin*>(a.q), static_cast<Tout*>(a.o), a.H, a.scale, a.n_seqs,
                      a.T_eq, ncs_eq, static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks),
                      a.cu_seqlens, a.h0, a.ht, a.pool, a.pool_slots, a.slots, a.ws);

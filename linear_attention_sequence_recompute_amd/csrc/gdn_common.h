@@ -182,6 +182,15 @@ struct Prec<__bf16> {
   __device__ static __forceinline__ Cmp cmp_from(const Tile& t0, const Tile& t1) {
     return Cmp{as_bf16x8(u32x4{t0[0], t0[1], t1[0], t1[1]}), as_bf16x8(u32x4{t0[2], t0[3], t1[2], t1[3]})};
   }
+  // Writes accumulator tile t (4 rows of one column per lane) as half `half` of
+  // the stored B-operand fragment at `base` (planes as in st_cmp): rows [0, 16) of
+  // a 32-row block are half 0, rows [16, 32) half 1.
+  __device__ static __forceinline__ void st_tile(void* base, int lane, int half, const f32x4& t) {
+    const Tile v = tile(t);
+    char* b = static_cast<char*>(base) + lane * 16 + half * 8;
+    *reinterpret_cast<u32x2*>(b) = u32x2{v[0], v[1]};
+    *reinterpret_cast<u32x2*>(b + 1024) = u32x2{v[2], v[3]};
+  }
 };
 
 template <>
@@ -214,6 +223,9 @@ struct Prec<float> {
   }
   __device__ static __forceinline__ Tile tile(const f32x4& t) { return t; }
   __device__ static __forceinline__ Cmp cmp_from(const Tile& t0, const Tile& t1) { return Cmp{t0, t1}; }
+  __device__ static __forceinline__ void st_tile(void* base, int lane, int half, const f32x4& t) {
+    reinterpret_cast<f32x4*>(base)[half * 64 + lane] = t;
+  }
 };
 
 // Wave-wide inclusive prefix sum over 64 lanes.

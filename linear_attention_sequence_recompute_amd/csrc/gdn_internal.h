@@ -25,14 +25,15 @@ struct DecodeArgs {
 // stored in the MFMA fragment order the reader consumes. A fragment is stored as
 // planes of [64 lanes][16 bytes] (see Prec in gdn_common.h: two planes for a
 // computed operand, one or two for an input). "ch" = chunk * H + head.
-//   wf  [ch][K/32 kb][4 rt][2 planes]      w = A diag(beta e^g) K as A operands
-//        over key block kb for output row tile rt
+//   wf  [ch][4 rt][K/32 kb][2 planes]      w = A diag(beta e^g) K as A operands
+//        of output row tile rt over key block kb
 //   ktf [ch][K/16 kt][2 ks][input planes]  K^T as A operands
 //   uf  [ch][V/16 vt][4 rt][64 lane][4]    f32 u = A diag(beta) V as accumulator
 //        tiles
 //   pf  [ch][4 rt][2 ks][2 planes]         P = s (Q K^T) * E * M as A operands
-//   gc  [ch][64]                           f32 chunk-local inclusive
-//        cumulative sum of the log-gate (rows past the chunk end repeat g_last)
+//   gx  [ch][2][64]                        f32 gate factors e^{g_i} and
+//        e^{g_last - g_i}, g the chunk-local inclusive cumulative sum of the
+//        log-gate (rows past the chunk end repeat g_last, so e^{g_63} = e^{g_last})
 //   info [chunk] int4 {seq, first token, rows, 0} and seq_chunk0 [n_seqs + 1]:
 //        the chunk schedule of a packed (varlen) call
 struct ChunkWs {
@@ -40,7 +41,7 @@ struct ChunkWs {
   uint8_t* ktf;
   float* uf;
   uint8_t* pf;
-  float* gc;
+  float* gx;
   int4* info;
   int* seq_chunk0;
 };
@@ -69,7 +70,7 @@ struct ChunkArgs {
 
 // Workspace layout for a call with at most max_chunks chunks.
 struct WsLayout {
-  size_t wf, ktf, uf, pf, gc, info, seq_chunk0, total;
+  size_t wf, ktf, uf, pf, gx, info, seq_chunk0, total;
 };
 WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, bool in_f32);
 ChunkWs carve_workspace(const WsLayout& l, void* base);
