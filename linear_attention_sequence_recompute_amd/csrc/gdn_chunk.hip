@@ -4,24 +4,23 @@
 // recompute_w_u (u = A (v beta), w = A (k beta e^g) with the chunk's WY matrix A),
 // chunk_fwd_h (the sequential state recurrence over a [K, V] state) and
 // chunk_fwd_o (inter-chunk q h e^g plus the causally masked intra-chunk term).
-// This file runs them as two launches (plus a schedule launch for packed
-// sequences):
+// Since u - w h = A diag(beta) (V - diag(e^g) K h), the whole chunk step only
+// needs the chunk's inputs, its gate sums and A' = A diag(beta). This file runs:
 //
 //  * prep_kernel, one workgroup per (chunk, head), fully parallel: the
 //    chunk-local gate cumsum, K K^T -> L, the triangular solve A = (I + L)^-1 in
-//    LDS, u and w, the masked score matrix P of chunk_fwd_o and K^T, all written
-//    in the MFMA operand order the scan kernel reads.
-//  * scan_kernel, one workgroup per (sequence, head, slice of V): the sequential
-//    chunk loop of chunk_fwd_h with chunk_fwd_o fused into it, so the per-chunk
-//    states and v_new never leave the chip. The state slice lives in MFMA
-//    accumulator registers for the whole sequence; each wave owns 32 key rows of
-//    it, the decay e^{g_last} is folded into the accumulator before K^T v_gated
-//    is added, and the partial products over key rows are summed through LDS.
+//    LDS, and A' stored in the MFMA operand order the scan kernel reads;
+//  * scan_kernel, one workgroup per (sequence, head, 16-column slice of V): the
+//    sequential chunk loop of chunk_fwd_h with chunk_fwd_o fused into it. Each
+//    chunk's K is staged once in LDS and serves K h, K^T (read transposed) and the
+//    score matrix P = s (Q K^T) * E * M; v_new = A' (V - e^g (K h)); the state
+//    lives in MFMA accumulators, the decay e^{g_last} folded into the accumulator
+//    before K^T v_gated is added. Per-chunk states and v_new never leave the chip.
 //
 // Precision: q, k, v are exact in bf16 and enter the MFMA as one operand; every
-// computed operand (A diag(beta), A diag(beta e^g), w, h, v_new, P) enters as a
-// bf16 hi + lo pair with fp32 accumulation, which keeps about 16 significant bits.
-// Float32 inputs are split the same way.
+// computed operand (A', K h residuals, h, v_new, P) enters as a bf16 hi + lo pair
+// with fp32 accumulation, which keeps about 16 significant bits. Float32 inputs
+// run the same code on the fp32 MFMA.
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -29,8 +28,6 @@
 
 namespace gdn {
 
-
-constexpr int kLdt = 68;  // padded row length (elements) of the transposed LDS tiles
 constexpr int kPlane = 1024;  // bytes of one fragment plane (64 lanes x 16 bytes)
 
 // ---------------------------------------------------------------------------
@@ -83,24 +80,21 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// recompute_w_u, plus the parts of chunk_fwd_o that do not depend on the state.
+// recompute_w_u, reduced to what the fused scan needs: the chunk-local gate
+// sums and A' = A diag(beta), A = (I + StrictLower(diag(beta) K K^T * E))^-1,
+// plus the state-independent score matrix P of chunk_fwd_o.
 // One workgroup (4 waves) per (chunk, head).
 // ---------------------------------------------------------------------------
-template <int K, int V, typename Tin>
+template <int K, typename Tin>
 __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
-                                                   const Tin* __restrict__ v, const float* __restrict__ g,
-                                                   const float* __restrict__ beta, int H, float scale,
-                                                   int T_eq, int ncs_eq, int total_tokens,
+                                                   const float* __restrict__ g, const float* __restrict__ beta,
+                                                   int H, float scale, int T_eq, int ncs_eq, int total_tokens,
                                                    const int4* __restrict__ info, ChunkWs ws) {
   using P = Prec<Tin>;
   using In = typename P::In;
-  using Cmp = typename P::Cmp;
-  using Stage = typename P::Stage;
   constexpr int LDA = 68;  // row stride (floats) of the L / A tile: 16-byte aligned rows
-  __shared__ __attribute__((aligned(16))) Stage sKt[K][kLdt];  // K^T: [key][token]
-  __shared__ __attribute__((aligned(16))) Stage sVt[V][kLdt];  // V^T: [value][token]
-  __shared__ __attribute__((aligned(16))) float sLA[64][LDA];  // L, then A = (I + L)^-1
-  __shared__ float sg[64], sb[64], sbeg[64];
+  __shared__ __attribute__((aligned(16))) float sLA[64][LDA];  // L, then A
+  __shared__ float sg[64], sb[64];
 
   const int c = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -118,81 +112,48 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   }
   const int64_t ch = static_cast<int64_t>(c) * H + h;
 
-  // (1) chunk-local inclusive cumsum of the log-gate; beta; beta e^g; the gate
-  // factors e^g and e^{g_last - g} the scan kernel applies.
+  // Row fragments of the chunk's K (rows past the end are zero).
+  In kf[4][K / 32];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int row = 16 * b + lc;
+    const int rowc = min(row, n - 1);
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) {
+      kf[b][kb] = P::in_row(k + (static_cast<int64_t>(t0 + rowc) * H + h) * K + 32 * kb, lg);
+      if (row >= n) kf[b][kb] = P::in_zero();
+    }
+  }
+
+  // Row fragments of this wave's 16 rows of Q.
+  In qf[K / 32];
+  {
+    const int row = 16 * w + lc;
+    const int rowc = min(row, n - 1);
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) {
+      qf[kb] = P::in_row(q + (static_cast<int64_t>(t0 + rowc) * H + h) * K + 32 * kb, lg);
+      if (row >= n) qf[kb] = P::in_zero();
+    }
+  }
+
+  // (1) chunk-local inclusive cumsum of the log-gate; beta; the gate vectors g,
+  // e^g and e^{g_last - g} the scan kernel applies.
   if (w == 0) {
     const int64_t gi = static_cast<int64_t>(t0 + lane) * H + h;
     const float a = lane < n ? g[gi] : 0.f;
     const float gl = wave_inclusive_scan(a);
     const float glast = __shfl(gl, 63, 64);
-    const float bl = lane < n ? beta[gi] : 0.f;
     sg[lane] = gl;
-    sb[lane] = bl;
-    sbeg[lane] = bl * __expf(gl);
-    ws.gx[ch * 128 + lane] = __expf(gl);
-    ws.gx[ch * 128 + 64 + lane] = __expf(glast - gl);
+    sb[lane] = lane < n ? beta[gi] : 0.f;
+    ws.gx[ch * 192 + lane] = gl;
+    ws.gx[ch * 192 + 64 + lane] = __expf(gl);
+    ws.gx[ch * 192 + 128 + lane] = __expf(glast - gl);
   }
-  // Row fragments of all of K and of this wave's 16 rows of Q, loaded up front so
-  // their latency overlaps the staging below.
-  In kf[4][K / 32], qf[K / 32];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int row = 16 * b + lc;
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb)
-      kf[b][kb] = row < n ? P::in_row(k + (static_cast<int64_t>(t0 + row) * H + h) * K + 32 * kb, lg) : P::in_zero();
-  }
-#pragma unroll
-  for (int kb = 0; kb < K / 32; ++kb) {
-    const int row = 16 * w + lc;
-    qf[kb] = row < n ? P::in_row(q + (static_cast<int64_t>(t0 + row) * H + h) * K + 32 * kb, lg) : P::in_zero();
-  }
-
-  // (2) transposed copies of the chunk's K and V (rows past the end are zero),
-  // 16-byte global loads, all issued before the LDS writes.
-  auto stage = [&](const Tin* src, auto dim, Stage* dst) {
-    constexpr int D = decltype(dim)::value;
-    constexpr int PR = D / 8;
-    constexpr int ITERS = kChunk * PR / 256;
-    float x[ITERS][8];
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int id = tid + 256 * it;
-      const int t = id / PR, c8 = (id % PR) * 8;
-      if (t < n) {
-        const Tin* p = src + (static_cast<int64_t>(t0 + t) * H + h) * D + c8;
-        if constexpr (sizeof(Tin) == 2) {
-          const bf16x8 r = as_bf16x8(*reinterpret_cast<const u32x4*>(p));
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[it][e] = static_cast<float>(r[e]);
-        } else {
-          const f32x4 r0 = *reinterpret_cast<const f32x4*>(p);
-          const f32x4 r1 = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[it][e] = r0[e];
-            x[it][4 + e] = r1[e];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[it][e] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int id = tid + 256 * it;
-      const int t = id / PR, c8 = (id % PR) * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dst[(c8 + e) * kLdt + t] = P::to_stage(x[it][e]);
-    }
-  };
-  stage(k, std::integral_constant<int, K>{}, &sKt[0][0]);
-  stage(v, std::integral_constant<int, V>{}, &sVt[0][0]);
   for (int idx = tid; idx < 64 * LDA; idx += 256) (&sLA[0][0])[idx] = 0.f;
   __syncthreads();
 
-  // (3) L = StrictLower(diag(beta) K K^T * E): the 10 lower 16x16 tiles.
+  // (2) L = StrictLower(diag(beta) K K^T * E): the 10 lower 16x16 tiles.
 #pragma unroll
   for (int tix = 0; tix < 10; ++tix) {
     if ((tix & 3) != w) continue;
@@ -208,32 +169,33 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
     }
   }
 
-  // (4) P = s (Q K^T) * E * M, computed transposed so that pairs of accumulator
-  // tiles are directly the A operands of P; wave w owns output row tile w.
-  {
-    const int bi = w;
+  // (2b) the score matrix of chunk_fwd_o, P = s (Q K^T) * E * M (E_ij = e^{g_i - g_j},
+  // M the inclusive causal mask), computed transposed (P^T = K Q^T) so that pairs
+  // of accumulator tiles are directly its A operands; wave w owns row tile w.
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      f32x4 d[2] = {zero4(), zero4()};
+  for (int ks = 0; ks < 2; ++ks) {
+    f32x4 d[2] = {zero4(), zero4()};
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int bt = 2 * ks + half;
-        if (bt > bi) continue;
+    for (int half = 0; half < 2; ++half) {
+      const int bt = 2 * ks + half;
+      if (bt > w) continue;
+      f32x4 part[K / 32];
 #pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) d[half] = mma(kf[bt][kb], qf[kb], d[half]);
-        const int i = 16 * bi + lc;
+      for (int kb = 0; kb < K / 32; ++kb) part[kb] = mma(kf[bt][kb], qf[kb], zero4());
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tp = 16 * bt + 4 * lg + r;
-          d[half][r] = tp <= i ? scale * d[half][r] * __expf(sg[i] - sg[tp]) : 0.f;
-        }
+      for (int kb = 0; kb < K / 32; ++kb) d[half] += part[kb];
+      const int i = 16 * w + lc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tp = 16 * bt + 4 * lg + r;
+        d[half][r] = tp <= i ? scale * d[half][r] * __expf(sg[i] - sg[tp]) : 0.f;
       }
-      P::st_cmp(ws.pf + ch * (8 * 2 * kPlane) + (bi * 2 + ks) * 2 * kPlane, lane, P::cmp_tiles(d[0], d[1]));
     }
+    P::st_cmp(ws.pf + ch * (8 * 2 * kPlane) + (w * 2 + ks) * 2 * kPlane, lane, P::cmp_tiles(d[0], d[1]));
   }
   __syncthreads();
 
-  // (5) A = (I + L)^-1 by forward substitution without barriers: the four lanes
+  // (3) A = (I + L)^-1 by forward substitution without barriers: the four lanes
   // (j, part) of column j are adjacent in one wave; lane part keeps rows
   // [16 part, 16 part + 16) of column j in registers. Row i of (I + L) A = I gives
   // A[i][j] = -sum_m L[i][m] A[m][j]; each lane sums its 16 rows (L[i][m] = 0 for
@@ -267,60 +229,17 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   }
   __syncthreads();
 
-  // (6) u = A diag(beta) V; wave w owns output row tile w (all value tiles).
-  {
-    constexpr int NVT = V / 16;
-    f32x4 acc[NVT];
+  // (4) A' = A diag(beta) as A operands: wave w stores row tile w, token blocks
+  // 0 and 1 (A' is lower triangular: block 1 of row tiles 0 and 1 is zero).
 #pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) acc[vt] = zero4();
-    const int nks = w >= 2 ? 2 : 1;  // A is lower triangular
-    for (int ks = 0; ks < nks; ++ks) {
-      float x[8];
+  for (int ks = 0; ks < 2; ++ks) {
+    float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int m = 32 * ks + kappa(lg, e);
-        x[e] = sLA[16 * w + lc][m] * sb[m];
-      }
-      const Cmp a = P::cmp8(x);
-#pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) acc[vt] = mma(a, P::in_lds(&sVt[16 * vt + lc][32 * ks], lg), acc[vt]);
+    for (int e = 0; e < 8; ++e) {
+      const int m = 32 * ks + kappa(lg, e);
+      x[e] = sLA[16 * w + lc][m] * sb[m];
     }
-#pragma unroll
-    for (int vt = 0; vt < NVT; ++vt)
-      *reinterpret_cast<f32x4*>(ws.uf + ch * (V * 64) + ((vt * 4 + w) * 64 + lane) * 4) = acc[vt];
-  }
-
-  // (7) w = A diag(beta e^g) K, computed as w^T = K^T (A diag(beta e^g))^T so that
-  // pairs of accumulator tiles are the A operands of w over a 32-key block.
-  // Stored as [row tile][key block] fragments.
-  {
-    constexpr int NKT = K / 16;
-    f32x4 acc[NKT];
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) acc[kt] = zero4();
-    const int nks = w >= 2 ? 2 : 1;
-    for (int ks = 0; ks < nks; ++ks) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int m = 32 * ks + kappa(lg, e);
-        x[e] = sLA[16 * w + lc][m] * sbeg[m];
-      }
-      const Cmp b = P::cmp8(x);
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) acc[kt] = mma(P::in_lds(&sKt[16 * kt + lc][32 * ks], lg), b, acc[kt]);
-    }
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb)
-      P::st_cmp(ws.wf + ch * (K * 256) + (w * (K / 32) + kb) * 2 * kPlane, lane,
-                P::cmp_tiles(acc[2 * kb], acc[2 * kb + 1]));
-  }
-
-  // (8) K^T as A operands for the state update of the scan kernel.
-  for (int idx = w; idx < (K / 16) * 2; idx += 4) {
-    const int kt = idx >> 1, ks = idx & 1;
-    P::st_in(ws.ktf + ch * (K * 128 * P::kInPlanes) + (kt * 2 + ks) * P::kInPlanes * kPlane, lane,
-             P::in_lds(&sKt[16 * kt + lc][32 * ks], lg));
+    P::st_cmp(ws.af + ch * (8 * 2 * kPlane) + (w * 2 + ks) * 2 * kPlane, lane, P::cmp8(x));
   }
 }
 
@@ -328,31 +247,29 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
 // chunk_fwd_h with chunk_fwd_o fused: sequential over the chunks of one
 // sequence, for one head and one slice of 16 value columns.
 //
-// A workgroup has 2 K/32 waves in two roles that meet at two barriers per chunk:
+// 2 K/32 waves in two roles meet at three barriers per chunk:
 //  * chain wave w (w < K/32) owns key rows [32w, 32w + 32) of the state slice as
-//    two accumulator tiles and output row tiles [w RT, (w+1) RT). It publishes its
-//    state block in LDS as a B operand; after the first barrier it forms
-//    w h for its row tiles over all key blocks, then v_new = u - w h and the gated
-//    v_new, which it publishes; after the second barrier it updates its state rows
-//    with K^T v_gated, the decay e^{g_last} folded into the accumulator first.
-//  * output wave (w >= K/32) owns the same row tiles: after the first barrier it
-//    forms q h from the published state blocks (the inter-chunk term), after the
-//    second it adds P v_new (the intra-chunk term) and stores its output rows.
-// One chain wave and one output wave share each SIMD, so the output products fill
-// the gaps of the sequential chain. Every accumulation is split over independent
-// accumulators (one per key block) so dependent matrix-core instructions do not
-// serialize, and each wave loads its next chunk's operands one chunk ahead.
+//    two accumulator tiles, and output row tiles [w RT, (w+1) RT). It publishes
+//    its state block (barrier 1), forms Z = K h for its row tiles over all key
+//    blocks and R = V - e^g Z, publishes R (barrier 2), forms v_new = A' R and the
+//    gated v_new e^{g_last - g}, publishes them (barrier 3), and updates its state
+//    rows with K^T v_gated, the decay e^{g_last} folded into the accumulator.
+//  * output wave (w >= K/32) owns the same row tiles: after barrier 1 it forms
+//    q h (the inter-chunk term); after barrier 3 it adds P v_new (the intra-chunk
+//    term, P from the prep kernel) and stores its rows.
+// One chain wave and one output wave share each SIMD. Each chunk's K is staged
+// once in LDS (double buffered), prefetched one chunk ahead like every other
+// operand; accumulations are split over independent accumulators.
 // ---------------------------------------------------------------------------
 template <int K, typename Tin>
 struct ChainOps {
   using P = Prec<Tin>;
   static constexpr int NW = K / 32;
   static constexpr int RT = 4 / NW;
-  typename P::Cmp w[RT][NW];   // w rows of my row tiles, per key block
-  typename P::In kt[2][2];     // K^T for my key rows (two 16-row tiles) x token blocks
-  f32x4 u[RT];                 // u of my row tiles in this slice
-  f32x4 egl[RT];               // e^{g_last - g} at my rows
-  float dL;                    // e^{g_last}
+  typename P::Cmp a[RT][2];  // A' rows of my row tiles, per token block
+  f32x4 v[RT];               // V at my rows, this slice's columns
+  f32x4 eg[RT], egl[RT];     // e^g and e^{g_last - g} at my rows
+  float dL;                  // e^{g_last}
 };
 
 template <int K, typename Tin>
@@ -360,25 +277,31 @@ struct OutOps {
   using P = Prec<Tin>;
   static constexpr int NW = K / 32;
   static constexpr int RT = 4 / NW;
-  typename P::In q[RT][NW];    // q rows of my row tiles, per key block
-  typename P::Cmp p[RT][2];    // P rows of my row tiles, per token block
-  f32x4 eg[RT];                // e^g at my rows
+  typename P::In q[RT][NW];   // q rows of my row tiles, per key block
+  typename P::Cmp p[RT][2];   // P rows of my row tiles, per token block
+  f32x4 eg[RT];               // e^g at my rows (D layout)
 };
 
 template <int K, int V, typename Tin, typename Tout>
 __global__ __launch_bounds__(K / 32 * 128) void scan_kernel(
-    const Tin* __restrict__ q, Tout* __restrict__ o, int H, float scale, int n_seqs, int T_eq,
-    int ncs_eq, int total_tokens, int n_chunks, const int32_t* __restrict__ cu, const float* __restrict__ h0,
-    float* __restrict__ ht, float* __restrict__ pool, int64_t pool_slots, const int32_t* __restrict__ slots,
-    ChunkWs ws) {
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o, int H,
+    float scale, int n_seqs, int T_eq, int ncs_eq, int total_tokens, int n_chunks, const int32_t* __restrict__ cu,
+    const float* __restrict__ h0, float* __restrict__ ht, float* __restrict__ pool, int64_t pool_slots,
+    const int32_t* __restrict__ slots, ChunkWs ws) {
   using P = Prec<Tin>;
   using Cmp = typename P::Cmp;
+  using Stage = typename P::Stage;
   constexpr int NW = K / 32;
   constexpr int RT = 4 / NW;
   constexpr int NSL = V / 16;
-  // State blocks and (gated) v_new, both stored as B-operand fragments (two planes).
-  __shared__ u32x4 sH[NW][2][64];
-  __shared__ u32x4 sV[2][2][2][64];  // [token block][v_new | gated v_new][plane][lane]
+  constexpr int NT = NW * 128;                              // threads
+  constexpr int SK = K + (sizeof(Stage) == 2 ? 16 : 4);     // LDS row stride of the staged K
+  constexpr int KSEG = 16 / sizeof(Stage);                  // elements per 16-byte segment
+  constexpr int KLD = kChunk * K / KSEG / NT;               // 16-byte segments each thread stages
+  __shared__ __attribute__((aligned(16))) Stage sK[2][kChunk][SK];
+  __shared__ u32x4 sH[NW][2][64];        // state blocks (B operands, two planes)
+  __shared__ u32x4 sR[2][2][64];         // R per token block (B operand)
+  __shared__ u32x4 sV[2][2][2][64];      // [token block][v_new | gated v_new][plane][lane]
 
   // Workgroups of one (sequence, head) share an XCD (blockIdx % 8) and its L2.
   const int bid = blockIdx.x;
@@ -388,9 +311,10 @@ __global__ __launch_bounds__(K / 32 * 128) void scan_kernel(
   if (pair >= n_seqs * H) return;
   const int seq = pair / H, h = pair % H;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const bool chain = wv < NW;
-  const int w = chain ? wv : wv - NW;  // key block (chain) / row-tile group (output)
+  const int w = chain ? wv : wv - NW;
   const int lg = lane >> 4, lc = lane & 15;
   const int vcol = slice * 16 + lc;
   int start, len, chunk0;
@@ -406,6 +330,40 @@ __global__ __launch_bounds__(K / 32 * 128) void scan_kernel(
     chunk0 = seq * ncs_eq;
   }
   const int nc = (len + kChunk - 1) / kChunk;
+
+  // K staging: every thread loads KLD 16-byte segments of the chunk's K rows
+  // (rows past the end are zeroed) and writes them into sK[buffer].
+  struct KStage {
+    u32x4 seg[KLD];
+  };
+  auto load_k = [&](KStage& st, int c_req) {
+    const int c = min(c_req, nc - 1);
+    const int t0 = start + kChunk * c;
+    const int n = min(kChunk, len - kChunk * c);
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int idx = tid + NT * i;
+      const int row = idx / (K / KSEG), col = (idx % (K / KSEG)) * KSEG;
+      const int rowc = min(row, n - 1);
+      st.seg[i] = *reinterpret_cast<const u32x4*>(k + (static_cast<int64_t>(t0 + rowc) * H + h) * K + col);
+      if (row >= n) st.seg[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_k = [&](const KStage& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int idx = tid + NT * i;
+      const int row = idx / (K / KSEG), col = (idx % (K / KSEG)) * KSEG;
+      *reinterpret_cast<u32x4*>(&sK[buf][row][col]) = st.seg[i];
+    }
+  };
+
+  if (nc > 0) {
+    KStage k0;
+    load_k(k0, 0);
+    store_k(k0, 0);
+  }
+  __syncthreads();
 
   if (chain) {
     using Ops = ChainOps<K, Tin>;
@@ -431,70 +389,87 @@ __global__ __launch_bounds__(K / 32 * 128) void scan_kernel(
     }
 
     // Loads are unconditional (a chunk index past the end is clamped to the last
-    // chunk) so that the wait counters can keep the next chunk's loads in flight.
-    auto load = [&](Ops& op, int c_req) {
+    // chunk, rows past a chunk's end to its last row and zeroed after the load)
+    // so the wait counters can keep the next chunk's loads in flight.
+    auto load = [&](Ops& op, KStage& st, int c_req) {
+      load_k(st, c_req + 1);
       const int c = min(c_req, nc - 1);
       const int64_t ch = static_cast<int64_t>(chunk0 + c) * H + h;
+      const int t0 = start + kChunk * c;
+      const int n = min(kChunk, len - kChunk * c);
 #pragma unroll
       for (int rho = 0; rho < RT; ++rho) {
         const int rt = w * RT + rho;
 #pragma unroll
-        for (int kb = 0; kb < NW; ++kb)
-          op.w[rho][kb] = P::ld_cmp(ws.wf + ch * (K * 256) + (rt * NW + kb) * 2 * kPlane, lane);
-        op.u[rho] = *reinterpret_cast<const f32x4*>(ws.uf + ch * (V * 64) + ((slice * 4 + rt) * 64 + lane) * 4);
-        op.egl[rho] = *reinterpret_cast<const f32x4*>(ws.gx + ch * 128 + 64 + 16 * rt + 4 * lg);
-      }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          op.kt[tt][ks] = P::ld_in_frag(
-              ws.ktf + ch * (K * 128 * P::kInPlanes) + ((2 * w + tt) * 2 + ks) * P::kInPlanes * kPlane, lane);
-      op.dL = ws.gx[ch * 128 + 63];
+          op.a[rho][ks] = P::ld_cmp(ws.af + ch * (8 * 2 * kPlane) + (rt * 2 + ks) * 2 * kPlane, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * rt + 4 * lg + r;
+          const float x = ld_in(v + (static_cast<int64_t>(t0 + min(row, n - 1)) * H + h) * V + vcol);
+          op.v[rho][r] = row < n ? x : 0.f;
+        }
+        op.eg[rho] = *reinterpret_cast<const f32x4*>(ws.gx + ch * 192 + 64 + 16 * rt + 4 * lg);
+        op.egl[rho] = *reinterpret_cast<const f32x4*>(ws.gx + ch * 192 + 128 + 16 * rt + 4 * lg);
+      }
+      op.dL = ws.gx[ch * 192 + 64 + 63];
     };
 
-    auto step = [&](const Ops& cur) {
-      // (1) publish this wave's state block as a B operand
+    auto step = [&](const Ops& cur, const KStage& nk, int c) {
+      const int buf = c & 1;
+      // (1) publish this wave's state block
       const Cmp hown = P::cmp_tiles(hs[0], hs[1]);
       P::st_cmp(&sH[w][0][0], lane, hown);
       __syncthreads();
-      // (2) w h for my row tiles over all key blocks; v_new and gated v_new
+      store_k(nk, buf ^ 1);  // next chunk's K: its buffer was last read before this barrier
+      // (2) Z = K h for my row tiles; R = V - e^g Z
       Cmp hb[NW];
 #pragma unroll
-      for (int kb = 0; kb < NW; ++kb) hb[kb] = kb == w ? hown : P::ld_cmp(&sH[kb][0][0], lane);
+      for (int kb = 0; kb < NW; ++kb) hb[kb] = P::ld_cmp(&sH[kb][0][0], lane);
 #pragma unroll
       for (int rho = 0; rho < RT; ++rho) {
         const int rt = w * RT + rho;
-        f32x4 xp[NW];
+        f32x4 zp[NW];
 #pragma unroll
-        for (int kb = 0; kb < NW; ++kb) xp[kb] = mma(cur.w[rho][kb], hb[kb], zero4());
-        f32x4 x = xp[0];
+        for (int kb = 0; kb < NW; ++kb) zp[kb] = mma(P::in_lds(&sK[buf][16 * rt + lc][32 * kb], lg), hb[kb], zero4());
+        f32x4 z = zp[0];
 #pragma unroll
-        for (int kb = 1; kb < NW; ++kb) x += xp[kb];
-        const f32x4 vn = cur.u[rho] - x;
+        for (int kb = 1; kb < NW; ++kb) z += zp[kb];
+        P::st_tile(&sR[rt >> 1][0][0], lane, rt & 1, cur.v[rho] - cur.eg[rho] * z);
+      }
+      __syncthreads();
+      // (3) v_new = A' R (A' is lower triangular: token block 1 only for row tiles 2, 3)
+      const Cmp r0 = P::ld_cmp(&sR[0][0][0], lane);
+#pragma unroll
+      for (int rho = 0; rho < RT; ++rho) {
+        const int rt = w * RT + rho;
+        f32x4 vn = mma(cur.a[rho][0], r0, zero4());
+        if (rt >= 2) vn += mma(cur.a[rho][1], P::ld_cmp(&sR[1][0][0], lane), zero4());
         P::st_tile(&sV[rt >> 1][0][0][0], lane, rt & 1, vn);
         P::st_tile(&sV[rt >> 1][1][0][0], lane, rt & 1, vn * cur.egl[rho]);
       }
       __syncthreads();
-      // (3) h <- e^{g_last} h + K^T v_gated
+      // (4) h <- e^{g_last} h + K^T v_gated
       const Cmp vg0 = P::ld_cmp(&sV[0][1][0][0], lane);
       const Cmp vg1 = P::ld_cmp(&sV[1][1][0][0], lane);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const f32x4 a0 = mma(cur.kt[tt][0], vg0, hs[tt] * cur.dL);
-        const f32x4 a1 = mma(cur.kt[tt][1], vg1, zero4());
+        const int kt = 2 * w + tt;
+        const f32x4 a0 = mma(P::in_lds_tr(&sK[buf][0][0], SK, 0, 16 * kt, lane), vg0, hs[tt] * cur.dL);
+        const f32x4 a1 = mma(P::in_lds_tr(&sK[buf][0][0], SK, 32, 16 * kt, lane), vg1, zero4());
         hs[tt] = a0 + a1;
       }
     };
 
     Ops bufA, bufB;
-    if (nc > 0) load(bufA, 0);
+    KStage kA, kB;
+    if (nc > 0) load(bufA, kA, 0);
     for (int c = 0; c < nc; c += 2) {
-      load(bufB, c + 1);
-      step(bufA);
+      load(bufB, kB, c + 1);
+      step(bufA, kA, c);
       if (c + 1 >= nc) break;
-      load(bufA, c + 2);
-      step(bufB);
+      load(bufA, kA, c + 2);
+      step(bufB, kB, c + 1);
     }
     if (s_out) {
 #pragma unroll
@@ -505,7 +480,8 @@ __global__ __launch_bounds__(K / 32 * 128) void scan_kernel(
     }
   } else {
     using Ops = OutOps<K, Tin>;
-    auto load = [&](Ops& op, int c_req) {
+    auto load = [&](Ops& op, KStage& st, int c_req) {
+      load_k(st, c_req + 1);
       const int c = min(c_req, nc - 1);
       const int64_t ch = static_cast<int64_t>(chunk0 + c) * H + h;
       const int t0 = start + kChunk * c;
@@ -514,7 +490,7 @@ __global__ __launch_bounds__(K / 32 * 128) void scan_kernel(
       for (int rho = 0; rho < RT; ++rho) {
         const int rt = w * RT + rho;
         const int row = 16 * rt + lc;
-        const int rowc = min(row, n - 1);  // rows past the end: load a valid row, then zero
+        const int rowc = min(row, n - 1);
 #pragma unroll
         for (int kb = 0; kb < NW; ++kb) {
           op.q[rho][kb] = P::in_row(q + (static_cast<int64_t>(t0 + rowc) * H + h) * K + 32 * kb, lg);
@@ -523,15 +499,17 @@ __global__ __launch_bounds__(K / 32 * 128) void scan_kernel(
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
           op.p[rho][ks] = P::ld_cmp(ws.pf + ch * (8 * 2 * kPlane) + (rt * 2 + ks) * 2 * kPlane, lane);
-        op.eg[rho] = *reinterpret_cast<const f32x4*>(ws.gx + ch * 128 + 16 * rt + 4 * lg);
+        op.eg[rho] = *reinterpret_cast<const f32x4*>(ws.gx + ch * 192 + 64 + 16 * rt + 4 * lg);
       }
     };
 
-    auto step = [&](const Ops& cur, int c) {
+    auto step = [&](const Ops& cur, const KStage& nk, int c) {
+      const int buf = c & 1;
       const int t0 = start + kChunk * c;
       const int n = min(kChunk, len - kChunk * c);
       __syncthreads();
-      // (1) inter-chunk term s e^g (q h) from the published state blocks
+      store_k(nk, buf ^ 1);
+      // (1) inter-chunk term s e^g (q h)
       Cmp hb[NW];
 #pragma unroll
       for (int kb = 0; kb < NW; ++kb) hb[kb] = P::ld_cmp(&sH[kb][0][0], lane);
@@ -546,6 +524,7 @@ __global__ __launch_bounds__(K / 32 * 128) void scan_kernel(
         for (int kb = 1; kb < NW; ++kb) y += yp[kb];
         acc[rho] = (scale * cur.eg[rho]) * y;
       }
+      __syncthreads();
       __syncthreads();
       // (2) intra-chunk term P v_new; store
       const Cmp vn0 = P::ld_cmp(&sV[0][0][0][0], lane);
@@ -564,13 +543,14 @@ __global__ __launch_bounds__(K / 32 * 128) void scan_kernel(
     };
 
     Ops bufA, bufB;
-    if (nc > 0) load(bufA, 0);
+    KStage kA, kB;
+    if (nc > 0) load(bufA, kA, 0);
     for (int c = 0; c < nc; c += 2) {
-      load(bufB, c + 1);
-      step(bufA, c);
+      load(bufB, kB, c + 1);
+      step(bufA, kA, c);
       if (c + 1 >= nc) break;
-      load(bufA, c + 2);
-      step(bufB, c + 1);
+      load(bufA, kA, c + 2);
+      step(bufB, kB, c + 1);
     }
   }
 }
@@ -581,20 +561,18 @@ __global__ __launch_bounds__(K / 32 * 128) void scan_kernel(
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, bool in_f32) {
+  (void)K;
+  (void)V;
+  (void)in_f32;
   const size_t nch = static_cast<size_t>(max_chunks) * H;
-  const size_t np = in_f32 ? 2 : 1;
   WsLayout l{};
   size_t off = 0;
-  l.wf = off;
-  off = align256(off + nch * K * 128 * 2);
-  l.ktf = off;
-  off = align256(off + nch * K * 64 * np * 2);
-  l.uf = off;
-  off = align256(off + nch * V * 64 * 4);
+  l.af = off;
+  off = align256(off + nch * 8 * 2 * kPlane);
   l.pf = off;
-  off = align256(off + nch * 8192 * 2);
+  off = align256(off + nch * 8 * 2 * kPlane);
   l.gx = off;
-  off = align256(off + nch * 2 * kChunk * 4);
+  off = align256(off + nch * 3 * kChunk * 4);
   l.info = off;
   off = align256(off + static_cast<size_t>(max_chunks) * 16);
   l.seq_chunk0 = off;
@@ -606,9 +584,7 @@ WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, b
 ChunkWs carve_workspace(const WsLayout& l, void* base) {
   char* b = static_cast<char*>(base);
   ChunkWs ws;
-  ws.wf = reinterpret_cast<uint8_t*>(b + l.wf);
-  ws.ktf = reinterpret_cast<uint8_t*>(b + l.ktf);
-  ws.uf = reinterpret_cast<float*>(b + l.uf);
+  ws.af = reinterpret_cast<uint8_t*>(b + l.af);
   ws.pf = reinterpret_cast<uint8_t*>(b + l.pf);
   ws.gx = reinterpret_cast<float*>(b + l.gx);
   ws.info = reinterpret_cast<int4*>(b + l.info);
@@ -628,18 +604,19 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
                        a.ws.info);
   }
   if (a.n_chunks > 0) {
-    hipLaunchKernelGGL((prep_kernel<K, V, Tin>), dim3(static_cast<unsigned>(a.n_chunks), a.H), dim3(256), 0,
-                       a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
-                       static_cast<const Tin*>(a.v), a.g, a.beta, a.H, a.scale, a.T_eq, ncs_eq,
-                       static_cast<int>(a.total_tokens), varlen ? a.ws.info : nullptr, a.ws);
+    hipLaunchKernelGGL((prep_kernel<K, Tin>), dim3(static_cast<unsigned>(a.n_chunks), a.H), dim3(256), 0,
+                       a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), a.g, a.beta, a.H,
+                       a.scale, a.T_eq, ncs_eq, static_cast<int>(a.total_tokens), varlen ? a.ws.info : nullptr,
+                       a.ws);
   }
   if (a.events[1]) (void)hipEventRecord(a.events[1], a.stream);
   const int64_t pairs = static_cast<int64_t>(a.n_seqs) * a.H;
   const int64_t blocks = 8 * NSL * ((pairs + 7) / 8);
-  hipLaunchKernelGGL((scan_kernel<K, V, Tin, Tout>), dim3(static_cast<unsigned>(blocks)), dim3(K / 32 * 128),
-                     0, a.stream, static_cast<const Tin*>(a.q), static_cast<Tout*>(a.o), a.H, a.scale, a.n_seqs,
-                     a.T_eq, ncs_eq, static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks),
-                     a.cu_seqlens, a.h0, a.ht, a.pool, a.pool_slots, a.slots, a.ws);
+  hipLaunchKernelGGL((scan_kernel<K, V, Tin, Tout>), dim3(static_cast<unsigned>(blocks)), dim3(K / 32 * 128), 0,
+                     a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
+                     static_cast<const Tin*>(a.v), static_cast<Tout*>(a.o), a.H, a.scale, a.n_seqs, a.T_eq, ncs_eq,
+                     static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0, a.ht, a.pool,
+                     a.pool_slots, a.slots, a.ws);
   const hipError_t err = hipGetLastError();
   if (a.events[2]) (void)hipEventRecord(a.events[2], a.stream);
   return err;

@@ -182,6 +182,22 @@ struct Prec<__bf16> {
   __device__ static __forceinline__ Cmp cmp_from(const Tile& t0, const Tile& t1) {
     return Cmp{as_bf16x8(u32x4{t0[0], t0[1], t1[0], t1[1]}), as_bf16x8(u32x4{t0[2], t0[3], t1[2], t1[3]})};
   }
+  // A-operand fragment of the transpose of a row-major LDS tile: rows of the
+  // fragment are tile columns [col0, col0 + 16), its contraction runs over tile
+  // rows [row0, row0 + 32). Uses ds_read_b64_tr_b16: within a group of 16 lanes,
+  // output lane j receives element j & 3 of the 4 loaded by lane 4e + (j >> 2) as
+  // its element e, so lane l' of group g loads 4 consecutive columns of tile row
+  // row0 + 4g + (l' >> 2) (+ 16 for the second half of the fragment).
+  __device__ static __forceinline__ In in_lds_tr(const Stage* tile, int stride, int row0, int col0, int lane) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const int g = lane >> 4, l = lane & 15;
+    const Stage* p0 = tile + (row0 + 4 * g + (l >> 2)) * stride + col0 + 4 * (l & 3);
+    const Stage* p1 = p0 + 16 * stride;
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
+    const u32x2 au = __builtin_bit_cast(u32x2, a), bu = __builtin_bit_cast(u32x2, b);
+    return In{as_bf16x8(u32x4{au[0], au[1], bu[0], bu[1]})};
+  }
   // Writes accumulator tile t (4 rows of one column per lane) as half `half` of
   // the stored B-operand fragment at `base` (planes as in st_cmp): rows [0, 16) of
   // a 32-row block are half 0, rows [16, 32) half 1.
@@ -223,6 +239,16 @@ struct Prec<float> {
   }
   __device__ static __forceinline__ Tile tile(const f32x4& t) { return t; }
   __device__ static __forceinline__ Cmp cmp_from(const Tile& t0, const Tile& t1) { return Cmp{t0, t1}; }
+  __device__ static __forceinline__ In in_lds_tr(const Stage* tile, int stride, int row0, int col0, int lane) {
+    const int g = lane >> 4, c = lane & 15;
+    In f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f.a[e] = tile[(row0 + 4 * g + e) * stride + col0 + c];
+      f.b[e] = tile[(row0 + 16 + 4 * g + e) * stride + col0 + c];
+    }
+    return f;
+  }
   __device__ static __forceinline__ void st_tile(void* base, int lane, int half, const f32x4& t) {
     reinterpret_cast<f32x4*>(base)[half * 64 + lane] = t;
   }

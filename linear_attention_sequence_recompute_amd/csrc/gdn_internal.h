@@ -21,25 +21,18 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
-// Chunk intermediates written by the prep kernel and read by the scan kernel,
-// stored in the MFMA fragment order the reader consumes. A fragment is stored as
-// planes of [64 lanes][16 bytes] (see Prec in gdn_common.h: two planes for a
-// computed operand, one or two for an input). "ch" = chunk * H + head.
-//   wf  [ch][4 rt][K/32 kb][2 planes]      w = A diag(beta e^g) K as A operands
-//        of output row tile rt over key block kb
-//   ktf [ch][K/16 kt][2 ks][input planes]  K^T as A operands
-//   uf  [ch][V/16 vt][4 rt][64 lane][4]    f32 u = A diag(beta) V as accumulator
-//        tiles
-//   pf  [ch][4 rt][2 ks][2 planes]         P = s (Q K^T) * E * M as A operands
-//   gx  [ch][2][64]                        f32 gate factors e^{g_i} and
-//        e^{g_last - g_i}, g the chunk-local inclusive cumulative sum of the
-//        log-gate (rows past the chunk end repeat g_last, so e^{g_63} = e^{g_last})
+// Chunk intermediates written by the prep kernel and read by the scan kernel.
+// A fragment is stored as planes of [64 lanes][16 bytes] (see Prec in
+// gdn_common.h: two planes for a computed operand). "ch" = chunk * H + head.
+//   af  [ch][4 rt][2 ks][2 planes]   A' = A diag(beta) as A operands of output
+//        row tile rt over token block ks
+//   pf  [ch][4 rt][2 ks][2 planes]   P = s (Q K^T) * E * M, the same way
+//   gx  [ch][3][64] f32              g (chunk-local inclusive cumulative sum of
+//        the log-gate; rows past the chunk end repeat g_last), e^g, e^{g_last - g}
 //   info [chunk] int4 {seq, first token, rows, 0} and seq_chunk0 [n_seqs + 1]:
 //        the chunk schedule of a packed (varlen) call
 struct ChunkWs {
-  uint8_t* wf;
-  uint8_t* ktf;
-  float* uf;
+  uint8_t* af;
   uint8_t* pf;
   float* gx;
   int4* info;
@@ -70,7 +63,7 @@ struct ChunkArgs {
 
 // Workspace layout for a call with at most max_chunks chunks.
 struct WsLayout {
-  size_t wf, ktf, uf, pf, gx, info, seq_chunk0, total;
+  size_t af, pf, gx, info, seq_chunk0, total;
 };
 WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, bool in_f32);
 ChunkWs carve_workspace(const WsLayout& l, void* base);
