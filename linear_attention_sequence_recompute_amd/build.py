@@ -37,6 +37,9 @@ def common_flags() -> list[str]:
         "-fPIC",
         # keep the compiler from forming packed-fp32 VALU ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA results in arch VGPRs: the scan's state and partial products feed
+        # VALU work every step, and accumulator registers would need copies
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         f"-I{INCLUDE}",
         f"-I{CSRC}",
     ]

@@ -245,314 +245,518 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
 
 // ---------------------------------------------------------------------------
 // chunk_fwd_h with chunk_fwd_o fused: sequential over the chunks of one
-// sequence, for one head and one slice of 16 value columns.
+// sequence, for one head and one slice of 16 value columns. Three waves:
 //
-// 2 K/32 waves in two roles meet at three barriers per chunk:
-//  * chain wave w (w < K/32) owns key rows [32w, 32w + 32) of the state slice as
-//    two accumulator tiles, and output row tiles [w RT, (w+1) RT). It publishes
-//    its state block (barrier 1), forms Z = K h for its row tiles over all key
-//    blocks and R = V - e^g Z, publishes R (barrier 2), forms v_new = A' R and the
-//    gated v_new e^{g_last - g}, publishes them (barrier 3), and updates its state
-//    rows with K^T v_gated, the decay e^{g_last} folded into the accumulator.
-//  * output wave (w >= K/32) owns the same row tiles: after barrier 1 it forms
-//    q h (the inter-chunk term); after barrier 3 it adds P v_new (the intra-chunk
-//    term, P from the prep kernel) and stores its rows.
-// One chain wave and one output wave share each SIMD. Each chunk's K is staged
-// once in LDS (double buffered), prefetched one chunk ahead like every other
-// operand; accumulations are split over independent accumulators.
+//  * the chain wave (wave 0) holds the slice's whole [K x 16] state in MFMA
+//    accumulators and runs the recurrence with no barrier inside a step and no
+//    global memory access: per chunk it publishes the state (as the B operands
+//    of K h), forms Z = K h, R = V - e^g Z, v_new = A' R (publishing v_new), and
+//    h <- e^{g_last} h + K^T (v_new e^{g_last - g}), the decay folded into the
+//    accumulator;
+//  * two output waves (waves 1 and 2, row tiles {0, 1} and {2, 3}) run one
+//    chunk behind: o = s e^g (q h) + P v_new from the published state and v_new,
+//    with q, P and e^g loaded a chunk ahead into registers. They also stage the
+//    chain's inputs for the chunk after the current one (K, A', the V slice and
+//    the gate vectors) into LDS with direct global-to-LDS loads.
+// All three meet at one barrier per chunk; every LDS buffer is double buffered.
+//
+// The state's key channels are held in a permuted order: within key block kb
+// (32 keys), accumulator row 4 g + r of tile 2 kb + odd is key 32 kb + 8 g +
+// 4 odd + r. Then the 8 contraction values a lane contributes to K h (and q h)
+// are 8 consecutive keys, one 16-byte load, and a lane's two tiles of a block
+// are 8 consecutive keys of the state in memory.
 // ---------------------------------------------------------------------------
-template <int K, typename Tin>
-struct ChainOps {
-  using P = Prec<Tin>;
-  static constexpr int NW = K / 32;
-  static constexpr int RT = 4 / NW;
-  typename P::Cmp a[RT][2];  // A' rows of my row tiles, per token block
-  f32x4 v[RT];               // V at my rows, this slice's columns
-  f32x4 eg[RT], egl[RT];     // e^g and e^{g_last - g} at my rows
-  float dL;                  // e^{g_last}
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
+// lds_block + 16 i (the block address must be the same for all lanes). The low
+// 32 bits of a generic pointer into LDS are its LDS offset.
+__device__ __forceinline__ void dma16(const void* src, void* lds_block) {
+  const uint32_t off = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_block));
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(static_cast<uintptr_t>(off)), 16, 0, 0);
+}
+
+// Waits for this wave's outstanding vector-memory operations (including the
+// direct-to-LDS copies) and nothing else: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// A chunk's K tile in LDS: 64 rows of K elements in 16-byte segments; segment
+// s of row r is stored at position s ^ (r & kMask) of the row, so that 16
+// consecutive rows read at one logical segment hit 16 different bank groups.
+template <int K, typename T>
+struct KTile {
+  static constexpr int kRowBytes = K * static_cast<int>(sizeof(T));
+  static constexpr int kSegs = kRowBytes / 16;
+  static constexpr int kMask = (kSegs < 16 ? kSegs : 16) - 1;
+  static constexpr int kBytes = kChunk * kRowBytes;
+  static constexpr int kDmaOps = kBytes / 1024;
+  static constexpr int kRowsPerOp = 1024 / kRowBytes;
+  __device__ static __forceinline__ int at(int row, int seg) { return row * kRowBytes + ((seg ^ (row & kMask)) << 4); }
 };
 
+// A operand of K h (or q h) in the permuted key order: row `row`, key block kb;
+// lane group g contributes keys [32 kb + 8 g, 32 kb + 8 g + 8).
 template <int K, typename Tin>
-struct OutOps {
-  using P = Prec<Tin>;
-  static constexpr int NW = K / 32;
-  static constexpr int RT = 4 / NW;
-  typename P::In q[RT][NW];   // q rows of my row tiles, per key block
-  typename P::Cmp p[RT][2];   // P rows of my row tiles, per token block
-  f32x4 eg[RT];               // e^g at my rows (D layout)
+struct KFrag;
+
+template <int K>
+struct KFrag<K, __bf16> {
+  using T = KTile<K, __bf16>;
+  __device__ static __forceinline__ FragB row(const char* tile, int row, int kb, int g) {
+    return FragB{as_bf16x8(*reinterpret_cast<const u32x4*>(tile + T::at(row, 4 * kb + g)))};
+  }
+  __device__ static __forceinline__ FragB global_row(const __bf16* p, int kb, int g) {
+    return FragB{as_bf16x8(*reinterpret_cast<const u32x4*>(p + 32 * kb + 8 * g))};
+  }
+  // A operand of K^T v: rows are the 16 keys of state tile 2 kb + odd, the
+  // contraction runs over tokens [32 tb, 32 tb + 32). ds_read_b64_tr_b16 gives
+  // output lane j of a 16-lane group element j & 3 of source lane 4 e + (j >> 2)
+  // as its element e, so source lane l of group g reads the 4 keys
+  // 32 kb + 8 (l & 3) + 4 odd .. + 3 of token 32 tb + 4 g + (l >> 2) (+ 16).
+  __device__ static __forceinline__ FragB tr(const char* tile, int tb, int kb, int odd, int lane) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const int g = lane >> 4, l = lane & 15;
+    const int r0 = 32 * tb + 4 * g + (l >> 2), seg = 4 * kb + (l & 3);
+    const char* p0 = tile + T::at(r0, seg) + 8 * odd;
+    const char* p1 = tile + T::at(r0 + 16, seg) + 8 * odd;
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
+    const u32x2 au = __builtin_bit_cast(u32x2, a), bu = __builtin_bit_cast(u32x2, b);
+    return FragB{as_bf16x8(u32x4{au[0], au[1], bu[0], bu[1]})};
+  }
 };
+
+template <int K>
+struct KFrag<K, float> {
+  using T = KTile<K, float>;
+  __device__ static __forceinline__ FragF row(const char* tile, int row, int kb, int g) {
+    const int s = 8 * kb + 2 * g;
+    return FragF{*reinterpret_cast<const f32x4*>(tile + T::at(row, s)),
+                 *reinterpret_cast<const f32x4*>(tile + T::at(row, s + 1))};
+  }
+  __device__ static __forceinline__ FragF global_row(const float* p, int kb, int g) {
+    return FragF{*reinterpret_cast<const f32x4*>(p + 32 * kb + 8 * g),
+                 *reinterpret_cast<const f32x4*>(p + 32 * kb + 8 * g + 4)};
+  }
+  __device__ static __forceinline__ FragF tr(const char* tile, int tb, int kb, int odd, int lane) {
+    const int g = lane >> 4, c = lane & 15;
+    const int key = 32 * kb + 8 * (c >> 2) + 4 * odd + (c & 3);
+    const int seg = key >> 2, off = 4 * (key & 3);
+    FragF f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f.a[e] = *reinterpret_cast<const float*>(tile + T::at(32 * tb + 4 * g + e, seg) + off);
+      f.b[e] = *reinterpret_cast<const float*>(tile + T::at(32 * tb + 16 + 4 * g + e, seg) + off);
+    }
+    return f;
+  }
+};
+
+// Copies rows [t0, t0 + 64) of K (row r at k + r * row_stride) into a KTile in
+// LDS, rows past n repeating row n - 1. Lane i of copy j fills position
+// i % kSegs of tile row j * kRowsPerOp + i / kSegs.
+template <int K, typename Tin>
+__device__ __forceinline__ void dma_k_tile(const Tin* k, int64_t row_stride, int t0, int n, char* tile) {
+  using KT = KTile<K, Tin>;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < KT::kDmaOps; ++j) {
+    const int row = j * KT::kRowsPerOp + lane / KT::kSegs;
+    const int seg = (lane % KT::kSegs) ^ (row & KT::kMask);
+    dma16(k + static_cast<int64_t>(t0 + min(row, n - 1)) * row_stride + seg * (16 / sizeof(Tin)), tile + 1024 * j);
+  }
+}
+
+// Copies a [64][16] slice (columns [col0, col0 + 16) of rows [t0, t0 + 64), rows
+// past n repeating row n - 1) into LDS in row-major order.
+template <typename Tin>
+__device__ __forceinline__ void dma_v_slice(const Tin* v, int64_t row_stride, int col0, int t0, int n, Tin* tile) {
+  constexpr int kOps = kChunk * 16 * sizeof(Tin) / 1024;
+  constexpr int kPerRow = 16 * sizeof(Tin) / 16;  // 16-byte pieces per row
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < kOps; ++j) {
+    const int tok = j * (64 / kPerRow) + lane / kPerRow;
+    dma16(v + static_cast<int64_t>(t0 + min(tok, n - 1)) * row_stride + col0 + (lane % kPerRow) * (16 / sizeof(Tin)),
+          reinterpret_cast<char*>(tile) + 1024 * j);
+  }
+}
+
+// Index of A' tile (row tile rt, token block ks) among the 6 nonzero ones.
+__device__ __forceinline__ constexpr int a_tile(int rt, int ks) { return rt < 2 ? rt : 2 + 2 * (rt - 2) + ks; }
+
+// V at rows 16 rt + 4 g + i (i < 4), column c of a [64][16] LDS tile, for lane
+// (g, c): the accumulator layout. For bf16 one transposed read serves the four
+// rows: source lane l of group g reads columns 4 (l & 3) .. + 3 of row
+// 16 rt + 4 g + (l >> 2), and output lane c receives element c & 3 of source
+// lane 4 i + (c >> 2) as its element i.
+__device__ __forceinline__ f32x4 v_rows(const __bf16* tile, int rt, int lane) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const int g = lane >> 4, l = lane & 15;
+  const __bf16* p = tile + (16 * rt + 4 * g + (l >> 2)) * 16 + 4 * (l & 3);
+  const u32x2 u = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p)));
+  return f32x4{__builtin_bit_cast(float, u[0] << 16), __builtin_bit_cast(float, u[0] & 0xffff0000u),
+               __builtin_bit_cast(float, u[1] << 16), __builtin_bit_cast(float, u[1] & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x4 v_rows(const float* tile, int rt, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  const float* p = tile + (16 * rt + 4 * g) * 16 + c;
+  return f32x4{p[0], p[16], p[32], p[48]};
+}
+
+// LDS of one scan workgroup, each buffer a separate __shared__ array so that
+// the compiler can tell the direct-to-LDS copies from the exchange buffers
+// (and does not make LDS reads wait for unrelated copies).
+template <int K, typename Tin>
+struct ScanSmem {
+  static constexpr int NKB = K / 32;
+  char (*k)[KTile<K, Tin>::kBytes];  // [2] K tiles (swizzled)
+  char (*a)[6][2 * kPlane];          // [2] A' tiles, two planes each
+  Tin (*v)[kChunk * 16];             // [2] V slice [token][16]
+  float (*gx)[3 * kChunk];           // [2] g, e^g, e^{g_last - g}
+  char (*h)[NKB][2 * kPlane];        // [2] published state (B operands)
+  f32x4 (*vn)[4][64];                // [2] published v_new tiles
+};
+
+struct ScanSeq {
+  int seq, h, slice, start, len, chunk0, nc;
+};
+
+template <int K, int V, typename Tin>
+__device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const ScanSeq& sq, const float* __restrict__ h0,
+                                           float* __restrict__ ht, float* __restrict__ pool, int64_t pool_slots,
+                                           const int32_t* __restrict__ slots, int H) {
+  using P = Prec<Tin>;
+  using In = typename P::In;
+  using Cmp = typename P::Cmp;
+  using KF = KFrag<K, Tin>;
+  constexpr int NKB = K / 32;
+  const int lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
+  const int vcol = sq.slice * 16 + lc;
+
+  const float* s_in = nullptr;
+  float* s_out = nullptr;
+  const int64_t page = static_cast<int64_t>(V) * K;
+  if (pool) {
+    const int s = slots[sq.seq];
+    if (s > 0 && s < pool_slots) {
+      s_in = pool + (static_cast<int64_t>(s) * H + sq.h) * page;
+      s_out = pool + (static_cast<int64_t>(s) * H + sq.h) * page;
+    }
+  } else {
+    if (h0) s_in = h0 + (static_cast<int64_t>(sq.seq) * H + sq.h) * page;
+    if (ht) s_out = ht + (static_cast<int64_t>(sq.seq) * H + sq.h) * page;
+  }
+  // State slice: tile 2 kb + odd, lane (g, c) holds keys 32 kb + 8 g + 4 odd + r
+  // of value column vcol (S[vcol][key] in memory: 8 consecutive floats per block).
+  f32x4 hs[2 * NKB];
+#pragma unroll
+  for (int t = 0; t < 2 * NKB; ++t) {
+    const int key0 = 32 * (t >> 1) + 8 * lg + 4 * (t & 1);
+    hs[t] = s_in ? *reinterpret_cast<const f32x4*>(s_in + static_cast<int64_t>(vcol) * K + key0) : zero4();
+  }
+  // The step is ordered so that each batch of VALU work (operand splits,
+  // gating) has independent MFMAs to run under; the split of the state for the
+  // next step is formed under the last MFMAs of the update.
+  constexpr int NZ = Terms<In, Cmp>::n;   // MFMA terms of K h and K^T v
+  constexpr int NA = Terms<Cmp, Cmp>::n;  // MFMA terms of A' R
+  Cmp hb[NKB];  // the state as B operands of K h
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) hb[kb] = P::cmp_tiles(hs[2 * kb], hs[2 * kb + 1]);
+  __syncthreads();  // the first chunk's inputs are staged
+
+  for (int c = 0; c < sq.nc; ++c) {
+    const int b = c & 1;
+    const char* kt = sm.k[b];
+    // This chunk's operands: K row fragments, A', V and the gate vectors.
+    In kf[4][NKB];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) kf[rt][kb] = KF::row(kt, 16 * rt + lc, kb, lg);
+    Cmp af[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) af[i] = P::ld_cmp(sm.a[b][i], lane);
+    f32x4 vv[4], eg[4], egl[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      eg[rt] = *reinterpret_cast<const f32x4*>(&sm.gx[b][64 + 16 * rt + 4 * lg]);
+      egl[rt] = *reinterpret_cast<const f32x4*>(&sm.gx[b][128 + 16 * rt + 4 * lg]);
+      vv[rt] = v_rows(sm.v[b], rt, lane);
+    }
+    const float dL = sm.gx[b][64 + 63];
+    __builtin_amdgcn_sched_barrier(0);  // issue the reads before any arithmetic
+
+    // (1) publish the state for the output waves
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) P::st_cmp(sm.h[b][kb], lane, hb[kb]);
+
+    // (2) Z = K h, row tiles 0 and 1 first (accumulators split by key-block
+    // parity for independent chains); the decayed state e^{g_last} h, the
+    // accumulator of the update, under them
+    f32x4 z[4][2];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) z[rt][0] = z[rt][1] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < NZ; ++t)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) z[rt][kb & 1] = term(kf[rt][kb], hb[kb], z[rt][kb & 1], t);
+    f32x4 hd[2 * NKB];
+#pragma unroll
+    for (int t = 0; t < 2 * NKB; ++t) hd[t] = hs[t] * dL;
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (3) row tiles 2 and 3 of Z; R = V - e^g Z of row tiles 0, 1 under them
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < NZ; ++t)
+#pragma unroll
+        for (int rt = 2; rt < 4; ++rt) z[rt][kb & 1] = term(kf[rt][kb], hb[kb], z[rt][kb & 1], t);
+    const Cmp rb0 = P::cmp_tiles(vv[0] - eg[0] * (z[0][0] + z[0][1]), vv[1] - eg[1] * (z[1][0] + z[1][1]));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (4) v_new = A' R. Token block 0 of all row tiles, with R of row tiles
+    // 2, 3 split under it; then token block 1 of row tiles 2, 3 (A' is lower
+    // triangular), with the gated v_new of row tiles 0, 1 under it.
+    In ktf[2 * NKB][2];  // K^T fragments of the update, read early
+#pragma unroll
+    for (int t = 0; t < 2 * NKB; ++t)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) ktf[t][tb] = KF::tr(kt, tb, t >> 1, t & 1, lane);
+    f32x4 acc[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) acc[i] = zero4();
+#pragma unroll
+    for (int t = 0; t < NA; ++t)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = term(af[a_tile(rt, 0)], rb0, acc[rt], t);
+    const Cmp rb1 = P::cmp_tiles(vv[2] - eg[2] * (z[2][0] + z[2][1]), vv[3] - eg[3] * (z[3][0] + z[3][1]));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < NA; ++t) {
+      acc[4] = term(af[a_tile(2, 1)], rb1, acc[4], t);
+      acc[5] = term(af[a_tile(3, 1)], rb1, acc[5], t);
+    }
+    sm.vn[b][0][lane] = acc[0];
+    sm.vn[b][1][lane] = acc[1];
+    const Cmp gb0 = P::cmp_tiles(acc[0] * egl[0], acc[1] * egl[1]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (5) h <- e^{g_last} h + K^T (v_new e^{g_last - g}): token block 0, with the
+    // rest of v_new under it; then token block 1 one pair of state tiles at a
+    // time, with the next step's split of each pair under the following ones
+#pragma unroll
+    for (int t = 0; t < NZ; ++t)
+#pragma unroll
+      for (int i = 0; i < 2 * NKB; ++i) hd[i] = term(ktf[i][0], gb0, hd[i], t);
+    const f32x4 vn2 = acc[2] + acc[4], vn3 = acc[3] + acc[5];
+    sm.vn[b][2][lane] = vn2;
+    sm.vn[b][3][lane] = vn3;
+    const Cmp gb1 = P::cmp_tiles(vn2 * egl[2], vn3 * egl[3]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int t = 0; t < NZ; ++t)
+#pragma unroll
+        for (int i = 2 * kb; i < 2 * kb + 2; ++i) hd[i] = term(ktf[i][1], gb1, hd[i], t);
+      if (kb > 0) hb[kb - 1] = P::cmp_tiles(hd[2 * kb - 2], hd[2 * kb - 1]);
+    }
+    hb[NKB - 1] = P::cmp_tiles(hd[2 * NKB - 2], hd[2 * NKB - 1]);
+#pragma unroll
+    for (int i = 0; i < 2 * NKB; ++i) hs[i] = hd[i];
+    __syncthreads();
+  }
+  if (s_out) {
+#pragma unroll
+    for (int t = 0; t < 2 * NKB; ++t) {
+      const int key0 = 32 * (t >> 1) + 8 * lg + 4 * (t & 1);
+      *reinterpret_cast<f32x4*>(s_out + static_cast<int64_t>(vcol) * K + key0) = hs[t];
+    }
+  }
+}
+
+// Output wave OW (row tiles 2 OW and 2 OW + 1). Wave 1 stages K, wave 2 stages
+// A', the V slice and the gate vectors of the chain's next chunk.
+template <int OW, int K, int V, typename Tin, typename Tout>
+__device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const ScanSeq& sq, const Tin* __restrict__ q,
+                                            const Tin* __restrict__ k, const Tin* __restrict__ v,
+                                            Tout* __restrict__ o, int H, float scale, const ChunkWs& ws) {
+  using P = Prec<Tin>;
+  using In = typename P::In;
+  using Cmp = typename P::Cmp;
+  using KF = KFrag<K, Tin>;
+  constexpr int NKB = K / 32;
+  constexpr int NTB = OW + 1;  // token blocks of P v_new for these row tiles
+  const int lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
+  const int h = sq.h, vcol = sq.slice * 16 + lc;
+
+  // Stage the chain's inputs of chunk c into buffer b. Rows past the end of a
+  // chunk repeat its last row: they meet zero columns of A' and zero rows of
+  // v_new, so only their finiteness matters.
+  auto stage = [&](int c, int b) {
+    const int t0 = sq.start + kChunk * c;
+    const int n = min(kChunk, sq.len - kChunk * c);
+    if (OW == 0) {
+      dma_k_tile<K, Tin>(k + static_cast<int64_t>(h) * K, static_cast<int64_t>(H) * K, t0, n, sm.k[b]);
+    } else {
+      const int64_t ch = static_cast<int64_t>(sq.chunk0 + c) * H + h;
+      const uint8_t* af = ws.af + ch * (8 * 2 * kPlane);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks > 0 && rt < 2) continue;
+#pragma unroll
+          for (int pl = 0; pl < 2; ++pl)
+            dma16(af + ((rt * 2 + ks) * 2 + pl) * kPlane + 16 * lane, sm.a[b][a_tile(rt, ks)] + pl * kPlane);
+        }
+      dma_v_slice<Tin>(v + static_cast<int64_t>(h) * V, static_cast<int64_t>(H) * V, sq.slice * 16, t0, n, sm.v[b]);
+      if (lane < 3 * kChunk / 4) dma16(ws.gx + ch * 192 + 4 * lane, sm.gx[b]);
+    }
+  };
+
+  struct Regs {
+    In q[2][NKB];
+    Cmp p[2][NTB];
+    f32x4 eg[2];
+  };
+  auto load = [&](Regs& rg, int c) {
+    const int64_t ch = static_cast<int64_t>(sq.chunk0 + c) * H + h;
+    const int t0 = sq.start + kChunk * c;
+    const int n = min(kChunk, sq.len - kChunk * c);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rt = 2 * OW + i;
+      const Tin* qrow = q + (static_cast<int64_t>(t0 + min(16 * rt + lc, n - 1)) * H + h) * K;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) rg.q[i][kb] = KF::global_row(qrow, kb, lg);
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+        rg.p[i][tb] = P::ld_cmp(ws.pf + ch * (8 * 2 * kPlane) + (rt * 2 + tb) * 2 * kPlane, lane);
+      rg.eg[i] = *reinterpret_cast<const f32x4*>(ws.gx + ch * 192 + 64 + 16 * rt + 4 * lg);
+    }
+  };
+  auto emit = [&](const Regs& rg, int c) {
+    const int b = c & 1;
+    const int t0 = sq.start + kChunk * c;
+    const int n = min(kChunk, sq.len - kChunk * c);
+    Cmp hb[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) hb[kb] = P::ld_cmp(sm.h[b][kb], lane);
+    Cmp vb[NTB];
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) vb[tb] = P::cmp_tiles(sm.vn[b][2 * tb][lane], sm.vn[b][2 * tb + 1][lane]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rt = 2 * OW + i;
+      f32x4 y = mma(rg.q[i][0], hb[0], zero4());
+#pragma unroll
+      for (int kb = 1; kb < NKB; ++kb) y = mma(rg.q[i][kb], hb[kb], y);
+      f32x4 acc = (scale * rg.eg[i]) * y;
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) acc = mma(rg.p[i][tb], vb[tb], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * rt + 4 * lg + r;
+        if (row < n) store_out(o + (static_cast<int64_t>(t0 + row) * H + h) * V + vcol, acc[r]);
+      }
+    }
+  };
+
+  // Interval c (0 <= c <= nc) runs between the barriers that close chain steps
+  // c - 1 and c (the last one has no closing barrier): it stages the chain's
+  // chunk c + 1, loads this wave's operands of chunk c and emits the output rows
+  // of chunk c - 1. Every staged copy has landed before the closing barrier.
+  // Inside the loop staging and loads are unconditional (chunk indices clamped;
+  // an extra copy lands in the buffer the chain is not reading), so that the
+  // wait counters can keep them in flight across the output work.
+  const int nc = sq.nc;
+  if (nc > 0) stage(0, 0);
+  wait_vmem();
+  __syncthreads();
+  if (nc > 0) {
+    Regs ra, rb;
+    if (nc > 1) stage(1, 1);
+    load(ra, 0);
+    wait_vmem();
+    __syncthreads();
+    int c = 1;
+    for (; c + 1 < nc; c += 2) {  // c odd
+      stage(c + 1, 0);
+      load(rb, c);
+      emit(ra, c - 1);
+      wait_vmem();
+      __syncthreads();
+      stage(min(c + 2, nc - 1), 1);
+      load(ra, c + 1);
+      emit(rb, c);
+      wait_vmem();
+      __syncthreads();
+    }
+    if (c < nc) {  // c == nc - 1: intervals nc - 1 and nc remain
+      load(rb, c);
+      emit(ra, c - 1);
+      wait_vmem();
+      __syncthreads();
+      emit(rb, c);
+    } else {  // c == nc: the last interval remains
+      emit(ra, c - 1);
+    }
+  }
+  wait_vmem();
+}
 
 template <int K, int V, typename Tin, typename Tout>
-__global__ __launch_bounds__(K / 32 * 128) void scan_kernel(
+__global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o, int H,
     float scale, int n_seqs, int T_eq, int ncs_eq, int total_tokens, int n_chunks, const int32_t* __restrict__ cu,
     const float* __restrict__ h0, float* __restrict__ ht, float* __restrict__ pool, int64_t pool_slots,
     const int32_t* __restrict__ slots, ChunkWs ws) {
-  using P = Prec<Tin>;
-  using Cmp = typename P::Cmp;
-  using Stage = typename P::Stage;
-  constexpr int NW = K / 32;
-  constexpr int RT = 4 / NW;
   constexpr int NSL = V / 16;
-  constexpr int NT = NW * 128;                              // threads
-  constexpr int SK = K + (sizeof(Stage) == 2 ? 16 : 4);     // LDS row stride of the staged K
-  constexpr int KSEG = 16 / sizeof(Stage);                  // elements per 16-byte segment
-  constexpr int KLD = kChunk * K / KSEG / NT;               // 16-byte segments each thread stages
-  __shared__ __attribute__((aligned(16))) Stage sK[2][kChunk][SK];
-  __shared__ u32x4 sH[NW][2][64];        // state blocks (B operands, two planes)
-  __shared__ u32x4 sR[2][2][64];         // R per token block (B operand)
-  __shared__ u32x4 sV[2][2][2][64];      // [token block][v_new | gated v_new][plane][lane]
+  constexpr int NKB = K / 32;
+  __shared__ __attribute__((aligned(1024))) char lds_k[2][KTile<K, Tin>::kBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_a[2][6][2 * kPlane];
+  __shared__ __attribute__((aligned(1024))) Tin lds_v[2][kChunk * 16];
+  __shared__ __attribute__((aligned(16))) float lds_gx[2][3 * kChunk];
+  __shared__ __attribute__((aligned(16))) char lds_h[2][NKB][2 * kPlane];
+  __shared__ __attribute__((aligned(16))) f32x4 lds_vn[2][4][64];
+  const ScanSmem<K, Tin> sm{lds_k, lds_a, lds_v, lds_gx, lds_h, lds_vn};
 
   // Workgroups of one (sequence, head) share an XCD (blockIdx % 8) and its L2.
   const int bid = blockIdx.x;
   const int xcd = bid & 7, rest = bid >> 3;
-  const int slice = rest % NSL;
+  ScanSeq sq;
+  sq.slice = rest % NSL;
   const int pair = (rest / NSL) * 8 + xcd;
   if (pair >= n_seqs * H) return;
-  const int seq = pair / H, h = pair % H;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-  const bool chain = wv < NW;
-  const int w = chain ? wv : wv - NW;
-  const int lg = lane >> 4, lc = lane & 15;
-  const int vcol = slice * 16 + lc;
-  int start, len, chunk0;
+  sq.seq = pair / H;
+  sq.h = pair % H;
   if (cu) {
-    start = cu[seq];
-    len = cu[seq + 1] - start;
-    chunk0 = ws.seq_chunk0[seq];
-    const int nc_want = (len + kChunk - 1) / kChunk;
-    if (start < 0 || len < 0 || start > total_tokens - len || chunk0 < 0 || chunk0 > n_chunks - nc_want) len = 0;
+    sq.start = cu[sq.seq];
+    sq.len = cu[sq.seq + 1] - sq.start;
+    sq.chunk0 = ws.seq_chunk0[sq.seq];
+    const int nc_want = (sq.len + kChunk - 1) / kChunk;
+    if (sq.start < 0 || sq.len < 0 || sq.start > total_tokens - sq.len || sq.chunk0 < 0 ||
+        sq.chunk0 > n_chunks - nc_want)
+      sq.len = 0;
   } else {
-    start = seq * T_eq;
-    len = T_eq;
-    chunk0 = seq * ncs_eq;
+    sq.start = sq.seq * T_eq;
+    sq.len = T_eq;
+    sq.chunk0 = sq.seq * ncs_eq;
   }
-  const int nc = (len + kChunk - 1) / kChunk;
+  sq.nc = (sq.len + kChunk - 1) / kChunk;
 
-  // K staging: every thread loads KLD 16-byte segments of the chunk's K rows
-  // (rows past the end are zeroed) and writes them into sK[buffer].
-  struct KStage {
-    u32x4 seg[KLD];
-  };
-  auto load_k = [&](KStage& st, int c_req) {
-    const int c = min(c_req, nc - 1);
-    const int t0 = start + kChunk * c;
-    const int n = min(kChunk, len - kChunk * c);
-#pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int idx = tid + NT * i;
-      const int row = idx / (K / KSEG), col = (idx % (K / KSEG)) * KSEG;
-      const int rowc = min(row, n - 1);
-      st.seg[i] = *reinterpret_cast<const u32x4*>(k + (static_cast<int64_t>(t0 + rowc) * H + h) * K + col);
-      if (row >= n) st.seg[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_k = [&](const KStage& st, int buf) {
-#pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int idx = tid + NT * i;
-      const int row = idx / (K / KSEG), col = (idx % (K / KSEG)) * KSEG;
-      *reinterpret_cast<u32x4*>(&sK[buf][row][col]) = st.seg[i];
-    }
-  };
-
-  if (nc > 0) {
-    KStage k0;
-    load_k(k0, 0);
-    store_k(k0, 0);
-  }
-  __syncthreads();
-
-  if (chain) {
-    using Ops = ChainOps<K, Tin>;
-    const float* s_in = nullptr;
-    float* s_out = nullptr;
-    const int64_t page = static_cast<int64_t>(V) * K;
-    if (pool) {
-      const int s = slots[seq];
-      if (s > 0 && s < pool_slots) {
-        s_in = pool + (static_cast<int64_t>(s) * H + h) * page;
-        s_out = pool + (static_cast<int64_t>(s) * H + h) * page;
-      }
-    } else {
-      if (h0) s_in = h0 + (static_cast<int64_t>(seq) * H + h) * page;
-      if (ht) s_out = ht + (static_cast<int64_t>(seq) * H + h) * page;
-    }
-    // State slice h[key][value] = S[value][key]: two accumulator tiles.
-    f32x4 hs[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int k0 = 32 * w + 16 * tt + 4 * lg;
-      hs[tt] = s_in ? *reinterpret_cast<const f32x4*>(s_in + static_cast<int64_t>(vcol) * K + k0) : zero4();
-    }
-
-    // Loads are unconditional (a chunk index past the end is clamped to the last
-    // chunk, rows past a chunk's end to its last row and zeroed after the load)
-    // so the wait counters can keep the next chunk's loads in flight.
-    auto load = [&](Ops& op, KStage& st, int c_req) {
-      load_k(st, c_req + 1);
-      const int c = min(c_req, nc - 1);
-      const int64_t ch = static_cast<int64_t>(chunk0 + c) * H + h;
-      const int t0 = start + kChunk * c;
-      const int n = min(kChunk, len - kChunk * c);
-#pragma unroll
-      for (int rho = 0; rho < RT; ++rho) {
-        const int rt = w * RT + rho;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          op.a[rho][ks] = P::ld_cmp(ws.af + ch * (8 * 2 * kPlane) + (rt * 2 + ks) * 2 * kPlane, lane);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * rt + 4 * lg + r;
-          const float x = ld_in(v + (static_cast<int64_t>(t0 + min(row, n - 1)) * H + h) * V + vcol);
-          op.v[rho][r] = row < n ? x : 0.f;
-        }
-        op.eg[rho] = *reinterpret_cast<const f32x4*>(ws.gx + ch * 192 + 64 + 16 * rt + 4 * lg);
-        op.egl[rho] = *reinterpret_cast<const f32x4*>(ws.gx + ch * 192 + 128 + 16 * rt + 4 * lg);
-      }
-      op.dL = ws.gx[ch * 192 + 64 + 63];
-    };
-
-    auto step = [&](const Ops& cur, const KStage& nk, int c) {
-      const int buf = c & 1;
-      // (1) publish this wave's state block
-      const Cmp hown = P::cmp_tiles(hs[0], hs[1]);
-      P::st_cmp(&sH[w][0][0], lane, hown);
-      __syncthreads();
-      store_k(nk, buf ^ 1);  // next chunk's K: its buffer was last read before this barrier
-      // (2) Z = K h for my row tiles; R = V - e^g Z
-      Cmp hb[NW];
-#pragma unroll
-      for (int kb = 0; kb < NW; ++kb) hb[kb] = P::ld_cmp(&sH[kb][0][0], lane);
-#pragma unroll
-      for (int rho = 0; rho < RT; ++rho) {
-        const int rt = w * RT + rho;
-        f32x4 zp[NW];
-#pragma unroll
-        for (int kb = 0; kb < NW; ++kb) zp[kb] = mma(P::in_lds(&sK[buf][16 * rt + lc][32 * kb], lg), hb[kb], zero4());
-        f32x4 z = zp[0];
-#pragma unroll
-        for (int kb = 1; kb < NW; ++kb) z += zp[kb];
-        P::st_tile(&sR[rt >> 1][0][0], lane, rt & 1, cur.v[rho] - cur.eg[rho] * z);
-      }
-      __syncthreads();
-      // (3) v_new = A' R (A' is lower triangular: token block 1 only for row tiles 2, 3)
-      const Cmp r0 = P::ld_cmp(&sR[0][0][0], lane);
-#pragma unroll
-      for (int rho = 0; rho < RT; ++rho) {
-        const int rt = w * RT + rho;
-        f32x4 vn = mma(cur.a[rho][0], r0, zero4());
-        if (rt >= 2) vn += mma(cur.a[rho][1], P::ld_cmp(&sR[1][0][0], lane), zero4());
-        P::st_tile(&sV[rt >> 1][0][0][0], lane, rt & 1, vn);
-        P::st_tile(&sV[rt >> 1][1][0][0], lane, rt & 1, vn * cur.egl[rho]);
-      }
-      __syncthreads();
-      // (4) h <- e^{g_last} h + K^T v_gated
-      const Cmp vg0 = P::ld_cmp(&sV[0][1][0][0], lane);
-      const Cmp vg1 = P::ld_cmp(&sV[1][1][0][0], lane);
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int kt = 2 * w + tt;
-        const f32x4 a0 = mma(P::in_lds_tr(&sK[buf][0][0], SK, 0, 16 * kt, lane), vg0, hs[tt] * cur.dL);
-        const f32x4 a1 = mma(P::in_lds_tr(&sK[buf][0][0], SK, 32, 16 * kt, lane), vg1, zero4());
-        hs[tt] = a0 + a1;
-      }
-    };
-
-    Ops bufA, bufB;
-    KStage kA, kB;
-    if (nc > 0) load(bufA, kA, 0);
-    for (int c = 0; c < nc; c += 2) {
-      load(bufB, kB, c + 1);
-      step(bufA, kA, c);
-      if (c + 1 >= nc) break;
-      load(bufA, kA, c + 2);
-      step(bufB, kB, c + 1);
-    }
-    if (s_out) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int k0 = 32 * w + 16 * tt + 4 * lg;
-        *reinterpret_cast<f32x4*>(s_out + static_cast<int64_t>(vcol) * K + k0) = hs[tt];
-      }
-    }
-  } else {
-    using Ops = OutOps<K, Tin>;
-    auto load = [&](Ops& op, KStage& st, int c_req) {
-      load_k(st, c_req + 1);
-      const int c = min(c_req, nc - 1);
-      const int64_t ch = static_cast<int64_t>(chunk0 + c) * H + h;
-      const int t0 = start + kChunk * c;
-      const int n = min(kChunk, len - kChunk * c);
-#pragma unroll
-      for (int rho = 0; rho < RT; ++rho) {
-        const int rt = w * RT + rho;
-        const int row = 16 * rt + lc;
-        const int rowc = min(row, n - 1);
-#pragma unroll
-        for (int kb = 0; kb < NW; ++kb) {
-          op.q[rho][kb] = P::in_row(q + (static_cast<int64_t>(t0 + rowc) * H + h) * K + 32 * kb, lg);
-          if (row >= n) op.q[rho][kb] = P::in_zero();
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          op.p[rho][ks] = P::ld_cmp(ws.pf + ch * (8 * 2 * kPlane) + (rt * 2 + ks) * 2 * kPlane, lane);
-        op.eg[rho] = *reinterpret_cast<const f32x4*>(ws.gx + ch * 192 + 64 + 16 * rt + 4 * lg);
-      }
-    };
-
-    auto step = [&](const Ops& cur, const KStage& nk, int c) {
-      const int buf = c & 1;
-      const int t0 = start + kChunk * c;
-      const int n = min(kChunk, len - kChunk * c);
-      __syncthreads();
-      store_k(nk, buf ^ 1);
-      // (1) inter-chunk term s e^g (q h)
-      Cmp hb[NW];
-#pragma unroll
-      for (int kb = 0; kb < NW; ++kb) hb[kb] = P::ld_cmp(&sH[kb][0][0], lane);
-      f32x4 acc[RT];
-#pragma unroll
-      for (int rho = 0; rho < RT; ++rho) {
-        f32x4 yp[NW];
-#pragma unroll
-        for (int kb = 0; kb < NW; ++kb) yp[kb] = mma(cur.q[rho][kb], hb[kb], zero4());
-        f32x4 y = yp[0];
-#pragma unroll
-        for (int kb = 1; kb < NW; ++kb) y += yp[kb];
-        acc[rho] = (scale * cur.eg[rho]) * y;
-      }
-      __syncthreads();
-      __syncthreads();
-      // (2) intra-chunk term P v_new; store
-      const Cmp vn0 = P::ld_cmp(&sV[0][0][0][0], lane);
-#pragma unroll
-      for (int rho = 0; rho < RT; ++rho) {
-        const int rt = w * RT + rho;
-        f32x4 o1 = zero4();
-        if (rt >= 2) o1 = mma(cur.p[rho][1], P::ld_cmp(&sV[1][0][0][0], lane), o1);  // P is causal
-        acc[rho] = mma(cur.p[rho][0], vn0, acc[rho]) + o1;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * rt + 4 * lg + r;
-          if (row < n) store_out(o + (static_cast<int64_t>(t0 + row) * H + h) * V + vcol, acc[rho][r]);
-        }
-      }
-    };
-
-    Ops bufA, bufB;
-    KStage kA, kB;
-    if (nc > 0) load(bufA, kA, 0);
-    for (int c = 0; c < nc; c += 2) {
-      load(bufB, kB, c + 1);
-      step(bufA, kA, c);
-      if (c + 1 >= nc) break;
-      load(bufA, kA, c + 2);
-      step(bufB, kB, c + 1);
-    }
-  }
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wv == 0)
+    scan_chain<K, V, Tin>(sm, sq, h0, ht, pool, pool_slots, slots, H);
+  else if (wv == 1)
+    scan_output<0, K, V, Tin, Tout>(sm, sq, q, k, v, o, H, scale, ws);
+  else
+    scan_output<1, K, V, Tin, Tout>(sm, sq, q, k, v, o, H, scale, ws);
 }
 
 // ---------------------------------------------------------------------------
@@ -612,7 +816,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
   if (a.events[1]) (void)hipEventRecord(a.events[1], a.stream);
   const int64_t pairs = static_cast<int64_t>(a.n_seqs) * a.H;
   const int64_t blocks = 8 * NSL * ((pairs + 7) / 8);
-  hipLaunchKernelGGL((scan_kernel<K, V, Tin, Tout>), dim3(static_cast<unsigned>(blocks)), dim3(K / 32 * 128), 0,
+  hipLaunchKernelGGL((scan_kernel<K, V, Tin, Tout>), dim3(static_cast<unsigned>(blocks)), dim3(192), 0,
                      a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
                      static_cast<const Tin*>(a.v), static_cast<Tout*>(a.o), a.H, a.scale, a.n_seqs, a.T_eq, ncs_eq,
                      static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0, a.ht, a.pool,

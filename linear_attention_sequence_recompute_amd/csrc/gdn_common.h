@@ -11,6 +11,8 @@ namespace gdn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -53,10 +55,24 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast
 __device__ __forceinline__ u32x4 as_u32x4(bf16x8 b) { return __builtin_bit_cast(u32x4, b); }
 __device__ __forceinline__ bf16x8 zero_bf16x8() { return as_bf16x8(u32x4{0u, 0u, 0u, 0u}); }
 
-// x ~= hi + lo with hi = RNE_bf16(x), lo = RNE_bf16(x - hi); |x - hi - lo| <= 2^-17 |x|.
-__device__ __forceinline__ void split1(float x, __bf16& hi, __bf16& lo) {
-  hi = to_bf16(x);
-  lo = to_bf16(x - static_cast<float>(hi));
+// x ~= hi + lo with hi = RNE_bf16(x), lo = RNE_bf16(x - hi), |x - hi - lo| <= 2^-17 |x|,
+// for a pair, packed: {hi(a), hi(b)} and {lo(a), lo(b)}. The residual x - hi is
+// exact in fp32, so it is formed by a bf16 dot product of the packed hi pair
+// with (-1, 0) or (0, -1) accumulated onto x, one instruction each.
+// The two multiplier pairs are kept in registers (the empty asm hides their
+// value): encoded as an inline constant, the pair (-1, 0) is not read back as
+// that pair by v_dot2c_f32_bf16 on gfx950.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  uint32_t m0u = 0x0000bf80u, m1u = 0xbf800000u;  // {-1, 0}, {0, -1} (low half first)
+  asm("" : "+v"(m0u));
+  asm("" : "+v"(m1u));
+  const bf16x2 m0 = __builtin_bit_cast(bf16x2, m0u);
+  const bf16x2 m1 = __builtin_bit_cast(bf16x2, m1u);
+  const float ra = __builtin_amdgcn_fdot2_f32_bf16(h, m0, a, false);
+  const float rb = __builtin_amdgcn_fdot2_f32_bf16(h, m1, b, false);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{ra, rb}, bf16x2));
 }
 
 // ---------------------------------------------------------------------------
@@ -72,26 +88,51 @@ struct FragF {  // fp32 values (elements 0..3 in a, 4..7 in b)
   f32x4 a, b;
 };
 
-// Products accumulated in fp32. The lo x lo term of two split operands is dropped.
-__device__ __forceinline__ f32x4 mma(const FragB& a, const FragB& b, f32x4 acc) { return mfma(a.x, b.x, acc); }
-__device__ __forceinline__ f32x4 mma(const FragB& a, const FragS& b, f32x4 acc) {
-  acc = mfma(a.x, b.lo, acc);
-  return mfma(a.x, b.hi, acc);
+// Products accumulated in fp32, as a fixed sequence of MFMA instructions
+// ("terms"): term(a, b, acc, t) issues the t-th, t < Terms<A, B>::n, so that
+// code can interleave the terms of independent products. The lo x lo term of
+// two split operands is dropped.
+template <class A, class B>
+struct Terms;
+template <>
+struct Terms<FragB, FragB> {
+  static constexpr int n = 1;
+};
+template <>
+struct Terms<FragB, FragS> {
+  static constexpr int n = 2;
+};
+template <>
+struct Terms<FragS, FragB> {
+  static constexpr int n = 2;
+};
+template <>
+struct Terms<FragS, FragS> {
+  static constexpr int n = 3;
+};
+template <>
+struct Terms<FragF, FragF> {
+  static constexpr int n = 8;
+};
+
+__device__ __forceinline__ f32x4 term(const FragB& a, const FragB& b, f32x4 acc, int) { return mfma(a.x, b.x, acc); }
+__device__ __forceinline__ f32x4 term(const FragB& a, const FragS& b, f32x4 acc, int t) {
+  return mfma(a.x, t == 0 ? b.lo : b.hi, acc);
 }
-__device__ __forceinline__ f32x4 mma(const FragS& a, const FragB& b, f32x4 acc) {
-  acc = mfma(a.lo, b.x, acc);
-  return mfma(a.hi, b.x, acc);
+__device__ __forceinline__ f32x4 term(const FragS& a, const FragB& b, f32x4 acc, int t) {
+  return mfma(t == 0 ? a.lo : a.hi, b.x, acc);
 }
-__device__ __forceinline__ f32x4 mma(const FragS& a, const FragS& b, f32x4 acc) {
-  acc = mfma(a.hi, b.lo, acc);
-  acc = mfma(a.lo, b.hi, acc);
-  return mfma(a.hi, b.hi, acc);
+__device__ __forceinline__ f32x4 term(const FragS& a, const FragS& b, f32x4 acc, int t) {
+  return t == 0 ? mfma(a.hi, b.lo, acc) : t == 1 ? mfma(a.lo, b.hi, acc) : mfma(a.hi, b.hi, acc);
 }
-__device__ __forceinline__ f32x4 mma(const FragF& a, const FragF& b, f32x4 acc) {
+__device__ __forceinline__ f32x4 term(const FragF& a, const FragF& b, f32x4 acc, int t) {
+  return t < 4 ? mfma_f32(a.a[t], b.a[t], acc) : mfma_f32(a.b[t - 4], b.b[t - 4], acc);
+}
+
+template <class A, class B>
+__device__ __forceinline__ f32x4 mma(const A& a, const B& b, f32x4 acc) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) acc = mfma_f32(a.a[e], b.a[e], acc);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc = mfma_f32(a.b[e], b.b[e], acc);
+  for (int t = 0; t < Terms<A, B>::n; ++t) acc = term(a, b, acc, t);
   return acc;
 }
 
@@ -145,15 +186,10 @@ struct Prec<__bf16> {
   }
 
   __device__ static __forceinline__ Cmp cmp8(const float (&x)[8]) {
-    Cmp f;
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      __bf16 h, l;
-      split1(x[e], h, l);
-      f.hi[e] = h;
-      f.lo[e] = l;
-    }
-    return f;
+    for (int e = 0; e < 4; ++e) split2(x[2 * e], x[2 * e + 1], h[e], l[e]);
+    return Cmp{as_bf16x8(u32x4{h[0], h[1], h[2], h[3]}), as_bf16x8(u32x4{l[0], l[1], l[2], l[3]})};
   }
   __device__ static __forceinline__ Cmp cmp_tiles(const f32x4& t0, const f32x4& t1) {
     const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
@@ -168,16 +204,10 @@ struct Prec<__bf16> {
                as_bf16x8(reinterpret_cast<const u32x4*>(base)[64 + lane])};
   }
   __device__ static __forceinline__ Tile tile(const f32x4& t) {
-    bf16x4 h, l;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      __bf16 a, b;
-      split1(t[r], a, b);
-      h[r] = a;
-      l[r] = b;
-    }
-    const u32x2 hu = __builtin_bit_cast(u32x2, h), lu = __builtin_bit_cast(u32x2, l);
-    return Tile{hu[0], hu[1], lu[0], lu[1]};
+    uint32_t h0, h1, l0, l1;
+    split2(t[0], t[1], h0, l0);
+    split2(t[2], t[3], h1, l1);
+    return Tile{h0, h1, l0, l1};
   }
   __device__ static __forceinline__ Cmp cmp_from(const Tile& t0, const Tile& t1) {
     return Cmp{as_bf16x8(u32x4{t0[0], t0[1], t1[0], t1[1]}), as_bf16x8(u32x4{t0[2], t0[3], t1[2], t1[3]})};
