@@ -266,16 +266,6 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
 // are 8 consecutive keys, one 16-byte load, and a lane's two tiles of a block
 // are 8 consecutive keys of the state in memory.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
-// lds_block + 16 i (the block address must be the same for all lanes). The low
-// 32 bits of a generic pointer into LDS are its LDS offset.
-__device__ __forceinline__ void dma16(const void* src, void* lds_block) {
-  const uint32_t off = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_block));
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)(static_cast<uintptr_t>(off)), 16, 0, 0);
-}
-
 // Waits for this wave's outstanding vector-memory operations (including the
 // direct-to-LDS copies) and nothing else: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -352,34 +342,34 @@ struct KFrag<K, float> {
   }
 };
 
-// Copies rows [t0, t0 + 64) of K (row r at k + r * row_stride) into a KTile in
-// LDS, rows past n repeating row n - 1. Lane i of copy j fills position
-// i % kSegs of tile row j * kRowsPerOp + i / kSegs.
+// Copies a chunk's K rows into a KTile in LDS. kd covers the chunk: row r at
+// byte r * row_bytes, rows past the chunk's end outside the descriptor (read
+// as zeros). Copy j, lane i fills position i % kSegs of tile row
+// j * kRowsPerOp + i / kSegs with the segment the swizzle puts there.
 template <int K, typename Tin>
-__device__ __forceinline__ void dma_k_tile(const Tin* k, int64_t row_stride, int t0, int n, char* tile) {
+__device__ __forceinline__ void dma_k_tile(const Buf& kd, uint32_t row_bytes, char* tile) {
   using KT = KTile<K, Tin>;
   const int lane = threadIdx.x & 63;
+  const uint32_t lane_row = static_cast<uint32_t>(lane / KT::kSegs) * row_bytes;
 #pragma unroll
   for (int j = 0; j < KT::kDmaOps; ++j) {
     const int row = j * KT::kRowsPerOp + lane / KT::kSegs;
-    const int seg = (lane % KT::kSegs) ^ (row & KT::kMask);
-    dma16(k + static_cast<int64_t>(t0 + min(row, n - 1)) * row_stride + seg * (16 / sizeof(Tin)), tile + 1024 * j);
+    const uint32_t seg = static_cast<uint32_t>((lane % KT::kSegs) ^ (row & KT::kMask));
+    kd.to_lds16(tile + 1024 * j, lane_row + 16 * seg, static_cast<uint32_t>(j * KT::kRowsPerOp) * row_bytes);
   }
 }
 
-// Copies a [64][16] slice (columns [col0, col0 + 16) of rows [t0, t0 + 64), rows
-// past n repeating row n - 1) into LDS in row-major order.
+// Copies a [64][16] slice (16 consecutive columns of each of a chunk's rows,
+// row r at byte r * row_bytes of vd) into LDS in row-major order.
 template <typename Tin>
-__device__ __forceinline__ void dma_v_slice(const Tin* v, int64_t row_stride, int col0, int t0, int n, Tin* tile) {
+__device__ __forceinline__ void dma_v_slice(const Buf& vd, uint32_t row_bytes, Tin* tile) {
   constexpr int kOps = kChunk * 16 * sizeof(Tin) / 1024;
   constexpr int kPerRow = 16 * sizeof(Tin) / 16;  // 16-byte pieces per row
   const int lane = threadIdx.x & 63;
+  const uint32_t voff = static_cast<uint32_t>(lane / kPerRow) * row_bytes + 16 * (lane % kPerRow);
 #pragma unroll
-  for (int j = 0; j < kOps; ++j) {
-    const int tok = j * (64 / kPerRow) + lane / kPerRow;
-    dma16(v + static_cast<int64_t>(t0 + min(tok, n - 1)) * row_stride + col0 + (lane % kPerRow) * (16 / sizeof(Tin)),
-          reinterpret_cast<char*>(tile) + 1024 * j);
-  }
+  for (int j = 0; j < kOps; ++j)
+    vd.to_lds16(reinterpret_cast<char*>(tile) + 1024 * j, voff, static_cast<uint32_t>(j * (64 / kPerRow)) * row_bytes);
 }
 
 // Index of A' tile (row tile rt, token block ks) among the 6 nonzero ones.
@@ -468,32 +458,37 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
   for (int c = 0; c < sq.nc; ++c) {
     const int b = c & 1;
     const char* kt = sm.k[b];
-    // This chunk's operands: K row fragments, A', V and the gate vectors.
+    // LDS reads are issued one phase ahead of their use; scheduling barriers
+    // keep each phase's reads, MFMAs and VALU work together.
+    // (0) reads for (1) and (3): K rows of row tiles 0, 1, V, e^g, e^{g_last};
+    // publish the state; the decayed state e^{g_last} h, the accumulator of the
+    // update, covers the read latency
+    const float dL = sm.gx[b][64 + 63];  // first: the decay below waits for it alone
+    __builtin_amdgcn_sched_barrier(0);
     In kf[4][NKB];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) kf[rt][kb] = KF::row(kt, 16 * rt + lc, kb, lg);
-    Cmp af[6];
-#pragma unroll
-    for (int i = 0; i < 6; ++i) af[i] = P::ld_cmp(sm.a[b][i], lane);
     f32x4 vv[4], eg[4], egl[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       eg[rt] = *reinterpret_cast<const f32x4*>(&sm.gx[b][64 + 16 * rt + 4 * lg]);
-      egl[rt] = *reinterpret_cast<const f32x4*>(&sm.gx[b][128 + 16 * rt + 4 * lg]);
       vv[rt] = v_rows(sm.v[b], rt, lane);
     }
-    const float dL = sm.gx[b][64 + 63];
-    __builtin_amdgcn_sched_barrier(0);  // issue the reads before any arithmetic
-
-    // (1) publish the state for the output waves
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) P::st_cmp(sm.h[b][kb], lane, hb[kb]);
+    f32x4 hd[2 * NKB];
+#pragma unroll
+    for (int t = 0; t < 2 * NKB; ++t) hd[t] = hs[t] * dL;
+    __builtin_amdgcn_sched_barrier(0);
 
-    // (2) Z = K h, row tiles 0 and 1 first (accumulators split by key-block
-    // parity for independent chains); the decayed state e^{g_last} h, the
-    // accumulator of the update, under them
+    // (1) Z = K h for row tiles 0, 1 (accumulators split by key-block parity
+    // for independent chains); reads for (2): K rows of row tiles 2, 3
+#pragma unroll
+    for (int rt = 2; rt < 4; ++rt)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) kf[rt][kb] = KF::row(kt, 16 * rt + lc, kb, lg);
     f32x4 z[4][2];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) z[rt][0] = z[rt][1] = zero4();
@@ -503,12 +498,15 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
       for (int t = 0; t < NZ; ++t)
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) z[rt][kb & 1] = term(kf[rt][kb], hb[kb], z[rt][kb & 1], t);
-    f32x4 hd[2 * NKB];
-#pragma unroll
-    for (int t = 0; t < 2 * NKB; ++t) hd[t] = hs[t] * dL;
     __builtin_amdgcn_sched_barrier(0);
 
-    // (3) row tiles 2 and 3 of Z; R = V - e^g Z of row tiles 0, 1 under them
+    // (2) Z for row tiles 2, 3, with R = V - e^g Z of row tiles 0, 1 under it;
+    // reads for (3): A', e^{g_last - g}
+    Cmp af[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) af[i] = P::ld_cmp(sm.a[b][i], lane);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) egl[rt] = *reinterpret_cast<const f32x4*>(&sm.gx[b][128 + 16 * rt + 4 * lg]);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -518,14 +516,11 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
     const Cmp rb0 = P::cmp_tiles(vv[0] - eg[0] * (z[0][0] + z[0][1]), vv[1] - eg[1] * (z[1][0] + z[1][1]));
     __builtin_amdgcn_sched_barrier(0);
 
-    // (4) v_new = A' R. Token block 0 of all row tiles, with R of row tiles
-    // 2, 3 split under it; then token block 1 of row tiles 2, 3 (A' is lower
-    // triangular), with the gated v_new of row tiles 0, 1 under it.
-    In ktf[2 * NKB][2];  // K^T fragments of the update, read early
+    // (3) v_new = A' R, token block 0 of all row tiles, with R of row tiles 2, 3
+    // split under it; reads for (5): K^T fragments of token block 0
+    In ktf[2 * NKB][2];
 #pragma unroll
-    for (int t = 0; t < 2 * NKB; ++t)
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) ktf[t][tb] = KF::tr(kt, tb, t >> 1, t & 1, lane);
+    for (int t = 0; t < 2 * NKB; ++t) ktf[t][0] = KF::tr(kt, 0, t >> 1, t & 1, lane);
     f32x4 acc[6];
 #pragma unroll
     for (int i = 0; i < 6; ++i) acc[i] = zero4();
@@ -535,6 +530,11 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
       for (int rt = 0; rt < 4; ++rt) acc[rt] = term(af[a_tile(rt, 0)], rb0, acc[rt], t);
     const Cmp rb1 = P::cmp_tiles(vv[2] - eg[2] * (z[2][0] + z[2][1]), vv[3] - eg[3] * (z[3][0] + z[3][1]));
     __builtin_amdgcn_sched_barrier(0);
+
+    // (4) token block 1 of row tiles 2, 3 (A' is lower triangular), with the
+    // gated v_new of row tiles 0, 1 under it; reads for (6): K^T of token block 1
+#pragma unroll
+    for (int t = 0; t < 2 * NKB; ++t) ktf[t][1] = KF::tr(kt, 1, t >> 1, t & 1, lane);
 #pragma unroll
     for (int t = 0; t < NA; ++t) {
       acc[4] = term(af[a_tile(2, 1)], rb1, acc[4], t);
@@ -545,9 +545,8 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
     const Cmp gb0 = P::cmp_tiles(acc[0] * egl[0], acc[1] * egl[1]);
     __builtin_amdgcn_sched_barrier(0);
 
-    // (5) h <- e^{g_last} h + K^T (v_new e^{g_last - g}): token block 0, with the
-    // rest of v_new under it; then token block 1 one pair of state tiles at a
-    // time, with the next step's split of each pair under the following ones
+    // (5) h <- e^{g_last} h + K^T (v_new e^{g_last - g}), token block 0, with
+    // the rest of v_new under it
 #pragma unroll
     for (int t = 0; t < NZ; ++t)
 #pragma unroll
@@ -557,6 +556,9 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
     sm.vn[b][3][lane] = vn3;
     const Cmp gb1 = P::cmp_tiles(vn2 * egl[2], vn3 * egl[3]);
     __builtin_amdgcn_sched_barrier(0);
+
+    // (6) token block 1, one pair of state tiles at a time, with the next
+    // step's split of each finished pair under the following ones
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -588,23 +590,33 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const Sc
   using P = Prec<Tin>;
   using In = typename P::In;
   using Cmp = typename P::Cmp;
-  using KF = KFrag<K, Tin>;
   constexpr int NKB = K / 32;
   constexpr int NTB = OW + 1;  // token blocks of P v_new for these row tiles
   const int lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
-  const int h = sq.h, vcol = sq.slice * 16 + lc;
+  const int h = sq.h;
 
-  // Stage the chain's inputs of chunk c into buffer b. Rows past the end of a
-  // chunk repeat its last row: they meet zero columns of A' and zero rows of
-  // v_new, so only their finiteness matters.
+  // Every global access goes through a buffer descriptor of the chunk: base at
+  // its first row for this head, size ending at its last row, so rows past the
+  // end read as zeros (loads, copies) or are dropped (stores). Per-lane offsets
+  // are the same for every chunk.
+  constexpr uint32_t ES = sizeof(Tin);
+  const uint32_t row_k = static_cast<uint32_t>(H) * K * ES;  // bytes between tokens of q and k
+  const uint32_t row_v = static_cast<uint32_t>(H) * V * ES;
+  const uint32_t row_o = static_cast<uint32_t>(H) * V * sizeof(Tout);
+  auto rows = [&](int c) { return min(kChunk, sq.len - kChunk * c); };
+  auto token0 = [&](int c) { return static_cast<int64_t>(sq.start + kChunk * c); };
+  auto chunk_head = [&](int c) { return static_cast<int64_t>(sq.chunk0 + c) * H + h; };
+
+  // Stage the chain's inputs of chunk c into buffer b (rows past the chunk's
+  // end are zeros: they meet zero columns of A' and zero rows of v_new).
   auto stage = [&](int c, int b) {
-    const int t0 = sq.start + kChunk * c;
-    const int n = min(kChunk, sq.len - kChunk * c);
+    const int n = rows(c);
     if (OW == 0) {
-      dma_k_tile<K, Tin>(k + static_cast<int64_t>(h) * K, static_cast<int64_t>(H) * K, t0, n, sm.k[b]);
+      const Buf kd(k + (token0(c) * H + h) * K, (n - 1) * row_k + K * ES);
+      dma_k_tile<K, Tin>(kd, row_k, sm.k[b]);
     } else {
-      const int64_t ch = static_cast<int64_t>(sq.chunk0 + c) * H + h;
-      const uint8_t* af = ws.af + ch * (8 * 2 * kPlane);
+      const int64_t ch = chunk_head(c);
+      const Buf ad(ws.af + ch * (8 * 2 * kPlane), 8 * 2 * kPlane);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -612,10 +624,12 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const Sc
           if (ks > 0 && rt < 2) continue;
 #pragma unroll
           for (int pl = 0; pl < 2; ++pl)
-            dma16(af + ((rt * 2 + ks) * 2 + pl) * kPlane + 16 * lane, sm.a[b][a_tile(rt, ks)] + pl * kPlane);
+            ad.to_lds16(sm.a[b][a_tile(rt, ks)] + pl * kPlane, 16 * lane, ((rt * 2 + ks) * 2 + pl) * kPlane);
         }
-      dma_v_slice<Tin>(v + static_cast<int64_t>(h) * V, static_cast<int64_t>(H) * V, sq.slice * 16, t0, n, sm.v[b]);
-      if (lane < 3 * kChunk / 4) dma16(ws.gx + ch * 192 + 4 * lane, sm.gx[b]);
+      const Buf vd(v + (token0(c) * H + h) * V + sq.slice * 16, (n - 1) * row_v + 16 * ES);
+      dma_v_slice<Tin>(vd, row_v, sm.v[b]);
+      const Buf gd(ws.gx + ch * 192, 192 * 4);
+      if (lane < 3 * kChunk / 4) gd.to_lds16(sm.gx[b], 16 * lane, 0);
     }
   };
 
@@ -624,26 +638,42 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const Sc
     Cmp p[2][NTB];
     f32x4 eg[2];
   };
+  const uint32_t q_voff = static_cast<uint32_t>(lc) * row_k + 8 * lg * ES;
   auto load = [&](Regs& rg, int c) {
-    const int64_t ch = static_cast<int64_t>(sq.chunk0 + c) * H + h;
-    const int t0 = sq.start + kChunk * c;
-    const int n = min(kChunk, sq.len - kChunk * c);
+    const int n = rows(c);
+    const int64_t ch = chunk_head(c);
+    const Buf qd(q + (token0(c) * H + h) * K, (n - 1) * row_k + K * ES);
+    const Buf pd(ws.pf + ch * (8 * 2 * kPlane), 8 * 2 * kPlane);
+    const Buf gd(ws.gx + ch * 192, 192 * 4);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int rt = 2 * OW + i;
-      const Tin* qrow = q + (static_cast<int64_t>(t0 + min(16 * rt + lc, n - 1)) * H + h) * K;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) rg.q[i][kb] = KF::global_row(qrow, kb, lg);
+      for (int kb = 0; kb < NKB; ++kb) {
+        const uint32_t so = 16 * rt * row_k + 32 * kb * ES;
+        if constexpr (sizeof(Tin) == 2) {
+          rg.q[i][kb] = In{as_bf16x8(qd.load16(q_voff, so))};
+        } else {
+          rg.q[i][kb] = In{__builtin_bit_cast(f32x4, qd.load16(q_voff, so)),
+                           __builtin_bit_cast(f32x4, qd.load16(q_voff + 16, so))};
+        }
+      }
 #pragma unroll
-      for (int tb = 0; tb < NTB; ++tb)
-        rg.p[i][tb] = P::ld_cmp(ws.pf + ch * (8 * 2 * kPlane) + (rt * 2 + tb) * 2 * kPlane, lane);
-      rg.eg[i] = *reinterpret_cast<const f32x4*>(ws.gx + ch * 192 + 64 + 16 * rt + 4 * lg);
+      for (int tb = 0; tb < NTB; ++tb) {
+        const uint32_t so = (rt * 2 + tb) * 2 * kPlane;
+        const u32x4 p0 = pd.load16(16 * lane, so), p1 = pd.load16(16 * lane, so + kPlane);
+        if constexpr (sizeof(Tin) == 2) {
+          rg.p[i][tb] = Cmp{as_bf16x8(p0), as_bf16x8(p1)};
+        } else {
+          rg.p[i][tb] = Cmp{__builtin_bit_cast(f32x4, p0), __builtin_bit_cast(f32x4, p1)};
+        }
+      }
+      rg.eg[i] = __builtin_bit_cast(f32x4, gd.load16(4 * (64 + 16 * rt + 4 * lg), 0));
     }
   };
   auto emit = [&](const Regs& rg, int c) {
     const int b = c & 1;
-    const int t0 = sq.start + kChunk * c;
-    const int n = min(kChunk, sq.len - kChunk * c);
+    const Buf od(o + (token0(c) * H + h) * V + sq.slice * 16, (rows(c) - 1) * row_o + 16 * sizeof(Tout));
     Cmp hb[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) hb[kb] = P::ld_cmp(sm.h[b][kb], lane);
@@ -660,10 +690,8 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const Sc
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) acc = mma(rg.p[i][tb], vb[tb], acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * rt + 4 * lg + r;
-        if (row < n) store_out(o + (static_cast<int64_t>(t0 + row) * H + h) * V + vcol, acc[r]);
-      }
+      for (int r = 0; r < 4; ++r)
+        od.store(static_cast<Tout>(acc[r]), (4 * lg + r) * row_o + lc * sizeof(Tout), 16 * rt * row_o);
     }
   };
 
@@ -688,17 +716,20 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const Sc
     for (; c + 1 < nc; c += 2) {  // c odd
       stage(c + 1, 0);
       load(rb, c);
+      __builtin_amdgcn_sched_barrier(0);  // loads go out before the output work
       emit(ra, c - 1);
       wait_vmem();
       __syncthreads();
       stage(min(c + 2, nc - 1), 1);
       load(ra, c + 1);
+      __builtin_amdgcn_sched_barrier(0);
       emit(rb, c);
       wait_vmem();
       __syncthreads();
     }
     if (c < nc) {  // c == nc - 1: intervals nc - 1 and nc remain
       load(rb, c);
+      __builtin_amdgcn_sched_barrier(0);  // loads go out before the output work
       emit(ra, c - 1);
       wait_vmem();
       __syncthreads();

@@ -284,6 +284,34 @@ struct Prec<float> {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Buffer addressing: a resource descriptor (base address and size in bytes, in
+// scalar registers) plus a 32-bit per-lane offset and a uniform offset. Loads
+// past the size return zeros and stores past it are dropped, so a descriptor
+// that ends at a chunk's last row masks the rows beyond it without branches.
+// ---------------------------------------------------------------------------
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ Buf(const void* base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000)) {}
+  __device__ __forceinline__ u32x4 load16(uint32_t voff, uint32_t soff) const {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  }
+  // 16 bytes per lane straight into LDS: lane i's bytes land at lds_block + 16 i
+  // (lds_block must be the same for all lanes).
+  __device__ __forceinline__ void to_lds16(void* lds_block, uint32_t voff, uint32_t soff) const {
+    const uint32_t l = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_block));  // LDS offset
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(static_cast<uintptr_t>(l)), 16,
+                                             voff, soff, 0, 0);
+  }
+  __device__ __forceinline__ void store(float x, uint32_t voff, uint32_t soff) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, soff, 0);
+  }
+  __device__ __forceinline__ void store(__bf16 x, uint32_t voff, uint32_t soff) const {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, voff, soff, 0);
+  }
+};
+
 // Wave-wide inclusive prefix sum over 64 lanes.
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
   const int lane = threadIdx.x & 63;
