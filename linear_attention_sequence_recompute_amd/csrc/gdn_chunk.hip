@@ -80,170 +80,6 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// recompute_w_u, reduced to what the fused scan needs: the chunk-local gate
-// sums and A' = A diag(beta), A = (I + StrictLower(diag(beta) K K^T * E))^-1,
-// plus the state-independent score matrix P of chunk_fwd_o.
-// One workgroup (4 waves) per (chunk, head).
-// ---------------------------------------------------------------------------
-template <int K, typename Tin>
-__global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
-                                                   const float* __restrict__ g, const float* __restrict__ beta,
-                                                   int H, float scale, int T_eq, int ncs_eq, int total_tokens,
-                                                   const int4* __restrict__ info, ChunkWs ws) {
-  using P = Prec<Tin>;
-  using In = typename P::In;
-  constexpr int LDA = 68;  // row stride (floats) of the L / A tile: 16-byte aligned rows
-  __shared__ __attribute__((aligned(16))) float sLA[64][LDA];  // L, then A
-  __shared__ float sg[64], sb[64];
-
-  const int c = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int lg = lane >> 4, lc = lane & 15;
-  int t0, n;
-  if (info) {
-    const int4 ci = info[c];
-    t0 = ci.y;
-    n = ci.z;
-    if (ci.x < 0 || n <= 0 || n > kChunk || t0 < 0 || t0 > total_tokens - n) return;
-  } else {
-    const int s = c / ncs_eq, j = c % ncs_eq;
-    t0 = s * T_eq + kChunk * j;
-    n = min(kChunk, T_eq - kChunk * j);
-  }
-  const int64_t ch = static_cast<int64_t>(c) * H + h;
-
-  // Row fragments of the chunk's K (rows past the end are zero).
-  In kf[4][K / 32];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int row = 16 * b + lc;
-    const int rowc = min(row, n - 1);
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) {
-      kf[b][kb] = P::in_row(k + (static_cast<int64_t>(t0 + rowc) * H + h) * K + 32 * kb, lg);
-      if (row >= n) kf[b][kb] = P::in_zero();
-    }
-  }
-
-  // Row fragments of this wave's 16 rows of Q.
-  In qf[K / 32];
-  {
-    const int row = 16 * w + lc;
-    const int rowc = min(row, n - 1);
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) {
-      qf[kb] = P::in_row(q + (static_cast<int64_t>(t0 + rowc) * H + h) * K + 32 * kb, lg);
-      if (row >= n) qf[kb] = P::in_zero();
-    }
-  }
-
-  // (1) chunk-local inclusive cumsum of the log-gate; beta; the gate vectors g,
-  // e^g and e^{g_last - g} the scan kernel applies.
-  if (w == 0) {
-    const int64_t gi = static_cast<int64_t>(t0 + lane) * H + h;
-    const float a = lane < n ? g[gi] : 0.f;
-    const float gl = wave_inclusive_scan(a);
-    const float glast = __shfl(gl, 63, 64);
-    sg[lane] = gl;
-    sb[lane] = lane < n ? beta[gi] : 0.f;
-    ws.gx[ch * 192 + lane] = gl;
-    ws.gx[ch * 192 + 64 + lane] = __expf(gl);
-    ws.gx[ch * 192 + 128 + lane] = __expf(glast - gl);
-  }
-  for (int idx = tid; idx < 64 * LDA; idx += 256) (&sLA[0][0])[idx] = 0.f;
-  __syncthreads();
-
-  // (2) L = StrictLower(diag(beta) K K^T * E): the 10 lower 16x16 tiles.
-#pragma unroll
-  for (int tix = 0; tix < 10; ++tix) {
-    if ((tix & 3) != w) continue;
-    const int bi = tix == 0 ? 0 : tix < 3 ? 1 : tix < 6 ? 2 : 3;
-    const int bj = tix - (bi * (bi + 1)) / 2;
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) acc = mma(kf[bi][kb], kf[bj][kb], acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * bi + 4 * lg + r, j = 16 * bj + lc;
-      if (j < i) sLA[i][j] = sb[i] * acc[r] * __expf(sg[i] - sg[j]);
-    }
-  }
-
-  // (2b) the score matrix of chunk_fwd_o, P = s (Q K^T) * E * M (E_ij = e^{g_i - g_j},
-  // M the inclusive causal mask), computed transposed (P^T = K Q^T) so that pairs
-  // of accumulator tiles are directly its A operands; wave w owns row tile w.
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    f32x4 d[2] = {zero4(), zero4()};
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int bt = 2 * ks + half;
-      if (bt > w) continue;
-      f32x4 part[K / 32];
-#pragma unroll
-      for (int kb = 0; kb < K / 32; ++kb) part[kb] = mma(kf[bt][kb], qf[kb], zero4());
-#pragma unroll
-      for (int kb = 0; kb < K / 32; ++kb) d[half] += part[kb];
-      const int i = 16 * w + lc;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tp = 16 * bt + 4 * lg + r;
-        d[half][r] = tp <= i ? scale * d[half][r] * __expf(sg[i] - sg[tp]) : 0.f;
-      }
-    }
-    P::st_cmp(ws.pf + ch * (8 * 2 * kPlane) + (w * 2 + ks) * 2 * kPlane, lane, P::cmp_tiles(d[0], d[1]));
-  }
-  __syncthreads();
-
-  // (3) A = (I + L)^-1 by forward substitution without barriers: the four lanes
-  // (j, part) of column j are adjacent in one wave; lane part keeps rows
-  // [16 part, 16 part + 16) of column j in registers. Row i of (I + L) A = I gives
-  // A[i][j] = -sum_m L[i][m] A[m][j]; each lane sums its 16 rows (L[i][m] = 0 for
-  // m >= i, and A[m][j] not yet known is 0) and the four parts are added with
-  // shuffles.
-  {
-    const int j = tid >> 2, part = tid & 3;
-    float a[16];
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) a[kk] = (16 * part + kk == j) ? 1.f : 0.f;
-#pragma unroll
-    for (int i = 1; i < 64; ++i) {
-      const f32x4* row = reinterpret_cast<const f32x4*>(&sLA[i][16 * part]);
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const f32x4 l4 = row[qq];
-        s0 = fmaf(l4[0], a[4 * qq + 0], s0);
-        s1 = fmaf(l4[1], a[4 * qq + 1], s1);
-        s2 = fmaf(l4[2], a[4 * qq + 2], s2);
-        s3 = fmaf(l4[3], a[4 * qq + 3], s3);
-      }
-      float s = (s0 + s1) + (s2 + s3);
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
-      if (part == (i >> 4) && i > j) a[i & 15] = -s;
-    }
-    __syncthreads();  // every lane is done reading L
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) sLA[16 * part + kk][j] = a[kk];
-  }
-  __syncthreads();
-
-  // (4) A' = A diag(beta) as A operands: wave w stores row tile w, token blocks
-  // 0 and 1 (A' is lower triangular: block 1 of row tiles 0 and 1 is zero).
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    float x[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int m = 32 * ks + kappa(lg, e);
-      x[e] = sLA[16 * w + lc][m] * sb[m];
-    }
-    P::st_cmp(ws.af + ch * (8 * 2 * kPlane) + (w * 2 + ks) * 2 * kPlane, lane, P::cmp8(x));
-  }
-}
-
-// ---------------------------------------------------------------------------
 // chunk_fwd_h with chunk_fwd_o fused: sequential over the chunks of one
 // sequence, for one head and one slice of 16 value columns. Three waves:
 //
@@ -346,13 +182,15 @@ struct KFrag<K, float> {
 // byte r * row_bytes, rows past the chunk's end outside the descriptor (read
 // as zeros). Copy j, lane i fills position i % kSegs of tile row
 // j * kRowsPerOp + i / kSegs with the segment the swizzle puts there.
-template <int K, typename Tin>
-__device__ __forceinline__ void dma_k_tile(const Buf& kd, uint32_t row_bytes, char* tile) {
+// A wave may issue a share of the copies: j0, j0 + js, ... (js divides kDmaOps).
+template <int K, typename Tin, int js = 1>
+__device__ __forceinline__ void dma_k_tile(const Buf& kd, uint32_t row_bytes, char* tile, int j0 = 0) {
   using KT = KTile<K, Tin>;
   const int lane = threadIdx.x & 63;
   const uint32_t lane_row = static_cast<uint32_t>(lane / KT::kSegs) * row_bytes;
 #pragma unroll
-  for (int j = 0; j < KT::kDmaOps; ++j) {
+  for (int jj = 0; jj < KT::kDmaOps; jj += js) {
+    const int j = jj + j0;
     const int row = j * KT::kRowsPerOp + lane / KT::kSegs;
     const uint32_t seg = static_cast<uint32_t>((lane % KT::kSegs) ^ (row & KT::kMask));
     kd.to_lds16(tile + 1024 * j, lane_row + 16 * seg, static_cast<uint32_t>(j * KT::kRowsPerOp) * row_bytes);
@@ -370,6 +208,16 @@ __device__ __forceinline__ void dma_v_slice(const Buf& vd, uint32_t row_bytes, T
 #pragma unroll
   for (int j = 0; j < kOps; ++j)
     vd.to_lds16(reinterpret_cast<char*>(tile) + 1024 * j, voff, static_cast<uint32_t>(j * (64 / kPerRow)) * row_bytes);
+}
+
+// A operand of q h / q k^T from global memory, permuted key order (keys
+// [32 kb + 8 g, +8) for lane group g): voff addresses the lane's row and key
+// group, soff the row tile and key block.
+__device__ __forceinline__ FragB buf_frag(const Buf& b, uint32_t voff, uint32_t soff, const __bf16*) {
+  return FragB{as_bf16x8(b.load16(voff, soff))};
+}
+__device__ __forceinline__ FragF buf_frag(const Buf& b, uint32_t voff, uint32_t soff, const float*) {
+  return FragF{__builtin_bit_cast(f32x4, b.load16(voff, soff)), __builtin_bit_cast(f32x4, b.load16(voff + 16, soff))};
 }
 
 // Index of A' tile (row tile rt, token block ks) among the 6 nonzero ones.
@@ -392,6 +240,200 @@ __device__ __forceinline__ f32x4 v_rows(const float* tile, int rt, int lane) {
   const int g = lane >> 4, c = lane & 15;
   const float* p = tile + (16 * rt + 4 * g) * 16 + c;
   return f32x4{p[0], p[16], p[32], p[48]};
+}
+
+// ---------------------------------------------------------------------------
+// recompute_w_u, reduced to what the fused scan needs: the chunk-local gate
+// sums and A' = A diag(beta), A = (I + L)^-1 with L = StrictLower(diag(beta)
+// K K^T * E), plus the state-independent score matrix P of chunk_fwd_o.
+// One workgroup (4 waves) per (chunk, head).
+//
+// The inverse is formed by 16 x 16 blocks: each wave inverts one diagonal block
+// D_i = (I + L_ii)^-1 by forward substitution, then the blocks below the
+// diagonal follow by distance d = i - j from it,
+//   A_ij = -D_i (sum_{j <= k < i} L_ik A_kj),   A_jj = D_j,
+// as 16 x 16 x 16 products on the fp32 MFMA.
+// ---------------------------------------------------------------------------
+// 16-deep fp32 product on v_mfma_f32_16x16x4f32: lane (g, c) supplies a =
+// X[c][4 g + e] and b = Y[4 g + e][c] to instruction e.
+__device__ __forceinline__ f32x4 mma16_f32(const f32x4& a, const f32x4& b, f32x4 acc) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], b[e], acc);
+  return acc;
+}
+
+template <int K, typename Tin>
+__global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
+                                                   const float* __restrict__ g, const float* __restrict__ beta,
+                                                   int H, float scale, int T_eq, int ncs_eq, int total_tokens,
+                                                   const int4* __restrict__ info, ChunkWs ws) {
+  using P = Prec<Tin>;
+  using In = typename P::In;
+  using KF = KFrag<K, Tin>;
+  using KT = KTile<K, Tin>;
+  constexpr int NKB = K / 32;
+  constexpr int LDA = 68;  // row stride (floats) of the L / A tile: 16-byte aligned rows
+  __shared__ __attribute__((aligned(1024))) char sK[KT::kBytes];  // the chunk's K (swizzled)
+  __shared__ __attribute__((aligned(16))) float sLA[64][LDA];     // L; diagonal blocks become D_i
+  __shared__ float sOff[6][16][17];                                 // A_ij below the diagonal
+  __shared__ float sg[64], sb[64];
+
+  const int c = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lg = lane >> 4, lc = lane & 15;
+  int t0, n;
+  if (info) {
+    const int4 ci = info[c];
+    t0 = ci.y;
+    n = ci.z;
+    if (ci.x < 0 || n <= 0 || n > kChunk || t0 < 0 || t0 > total_tokens - n) return;
+  } else {
+    const int s = c / ncs_eq, j = c % ncs_eq;
+    t0 = s * T_eq + kChunk * j;
+    n = min(kChunk, T_eq - kChunk * j);
+  }
+  const int64_t ch = static_cast<int64_t>(c) * H + h;
+  auto off_block = [](int i, int j) { return i * (i - 1) / 2 + j; };  // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+
+  // (0) the chunk's K into LDS, a quarter of the copies per wave (rows past
+  // the end read as zeros); this wave's 16 rows of Q
+  constexpr uint32_t ES = sizeof(Tin);
+  const uint32_t row_k = static_cast<uint32_t>(H) * K * ES;
+  const int64_t base = static_cast<int64_t>(t0) * H + h;
+  {
+    const Buf kd(k + base * K, (n - 1) * row_k + K * ES);
+    dma_k_tile<K, Tin, 4>(kd, row_k, sK, w);
+  }
+  In qf[NKB];
+  {
+    const Buf qd(q + base * K, (n - 1) * row_k + K * ES);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      qf[kb] = buf_frag(qd, lc * row_k + 8 * lg * ES, 16 * w * row_k + 32 * kb * ES, q);
+  }
+
+  // (1) chunk-local inclusive cumsum of the log-gate; beta; the gate vectors g,
+  // e^g and e^{g_last - g} the scan kernel applies.
+  if (w == 0) {
+    const int64_t gi = static_cast<int64_t>(t0 + lane) * H + h;
+    const float a = lane < n ? g[gi] : 0.f;
+    const float gl = wave_inclusive_scan(a);
+    const float glast = __shfl(gl, 63, 64);
+    sg[lane] = gl;
+    sb[lane] = lane < n ? beta[gi] : 0.f;
+    ws.gx[ch * 192 + lane] = gl;
+    ws.gx[ch * 192 + 64 + lane] = __expf(gl);
+    ws.gx[ch * 192 + 128 + lane] = __expf(glast - gl);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  // (2) L = StrictLower(diag(beta) K K^T * E): the 10 lower 16x16 tiles,
+  // written whole (zeros on and above the diagonal).
+#pragma unroll
+  for (int tix = 0; tix < 10; ++tix) {
+    if ((tix & 3) != w) continue;
+    const int bi = tix == 0 ? 0 : tix < 3 ? 1 : tix < 6 ? 2 : 3;
+    const int bj = tix - (bi * (bi + 1)) / 2;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      acc = mma(KF::row(sK, 16 * bi + lc, kb, lg), KF::row(sK, 16 * bj + lc, kb, lg), acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * bi + 4 * lg + r, j = 16 * bj + lc;
+      sLA[i][j] = j < i ? sb[i] * acc[r] * __expf(sg[i] - sg[j]) : 0.f;
+    }
+  }
+
+  // (2b) the score matrix of chunk_fwd_o, P = s (Q K^T) * E * M (E_ij = e^{g_i - g_j},
+  // M the inclusive causal mask), computed transposed (P^T = K Q^T) so that pairs
+  // of accumulator tiles are directly its A operands; wave w owns row tile w.
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    f32x4 d[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int bt = 2 * ks + half;
+      if (bt > w) continue;
+      f32x4 part[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) part[kb] = mma(KF::row(sK, 16 * bt + lc, kb, lg), qf[kb], zero4());
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) d[half] += part[kb];
+      const int i = 16 * w + lc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tp = 16 * bt + 4 * lg + r;
+        d[half][r] = tp <= i ? scale * d[half][r] * __expf(sg[i] - sg[tp]) : 0.f;
+      }
+    }
+    P::st_cmp(ws.pf + ch * (8 * 2 * kPlane) + (w * 2 + ks) * 2 * kPlane, lane, P::cmp_tiles(d[0], d[1]));
+  }
+  __syncthreads();
+
+  // (3) D_w = (I + L_ww)^-1 by forward substitution, rows of L_ww from
+  // registers: the four lanes (j, part) of column j are adjacent; lane part
+  // keeps rows [4 part, 4 part + 4) of column j. Row i of (I + L) D = I gives
+  // D[i][j] = -sum_m L[i][m] D[m][j] (L[i][m] = 0 for m >= i, and D[m][j] not
+  // yet known is 0); the four parts are added with shuffles.
+  {
+    const int j = lane >> 2, part = lane & 3;
+    f32x4 lrow[15];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) lrow[i - 1] = *reinterpret_cast<const f32x4*>(&sLA[16 * w + i][16 * w + 4 * part]);
+    f32x4 a;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = (4 * part + r == j) ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      float s = (lrow[i - 1][0] * a[0] + lrow[i - 1][1] * a[1]) + (lrow[i - 1][2] * a[2] + lrow[i - 1][3] * a[3]);
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      if (part == (i >> 2) && i > j) a[i & 3] = -s;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sLA[16 * w + 4 * part + r][16 * w + j] = a[r];
+  }
+  __syncthreads();
+
+  // (4) the blocks below the diagonal, distance 1, 2, 3 (waves 0..3 - d)
+#pragma unroll
+  for (int d = 1; d < 4; ++d) {
+    if (w < 4 - d) {
+      const int jb = w, ib = w + d;
+      f32x4 x = zero4();
+#pragma unroll
+      for (int kb = jb; kb < ib; ++kb) {
+        const f32x4 lik = *reinterpret_cast<const f32x4*>(&sLA[16 * ib + lc][16 * kb + 4 * lg]);
+        f32x4 akj;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          akj[e] = kb == jb ? sLA[16 * jb + 4 * lg + e][16 * jb + lc] : sOff[off_block(kb, jb)][4 * lg + e][lc];
+        x = mma16_f32(lik, akj, x);
+      }
+      const f32x4 di = *reinterpret_cast<const f32x4*>(&sLA[16 * ib + lc][16 * ib + 4 * lg]);
+      const f32x4 y = mma16_f32(di, x, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sOff[off_block(ib, jb)][4 * lg + r][lc] = -y[r];
+    }
+    __syncthreads();
+  }
+
+  // (5) A' = A diag(beta) as A operands: wave w stores row tile w, token blocks
+  // 0 and 1 (blocks above the diagonal are zero).
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int m = 32 * ks + kappa(lg, e);
+      const int mb = m >> 4;
+      const float av = mb == w ? sLA[16 * w + lc][m] : mb < w ? sOff[off_block(w, mb)][lc][m & 15] : 0.f;
+      x[e] = av * sb[m];
+    }
+    P::st_cmp(ws.af + ch * (8 * 2 * kPlane) + (w * 2 + ks) * 2 * kPlane, lane, P::cmp8(x));
+  }
 }
 
 // LDS of one scan workgroup, each buffer a separate __shared__ array so that
