@@ -457,7 +457,7 @@ struct ScanSeq {
 template <int K, int V, typename Tin>
 __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const ScanSeq& sq, const float* __restrict__ h0,
                                            float* __restrict__ ht, float* __restrict__ pool, int64_t pool_slots,
-                                           const int32_t* __restrict__ slots, int H) {
+                                           const int32_t* __restrict__ slots, int H, const ChunkWs& ws) {
   using P = Prec<Tin>;
   using In = typename P::In;
   using Cmp = typename P::Cmp;
@@ -487,25 +487,20 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
     const int key0 = 32 * (t >> 1) + 8 * lg + 4 * (t & 1);
     hs[t] = s_in ? *reinterpret_cast<const f32x4*>(s_in + static_cast<int64_t>(vcol) * K + key0) : zero4();
   }
-  // The step is ordered so that each batch of VALU work (operand splits,
-  // gating) has independent MFMAs to run under; the split of the state for the
-  // next step is formed under the last MFMAs of the update.
+  // One chunk step; the LDS buffer index B is a compile-time constant. The
+  // state hs is split into the B operands of K h in place, after the decayed
+  // state e^{g_last} h (the update's accumulator, hd) has been formed from it.
   constexpr int NZ = Terms<In, Cmp>::n;   // MFMA terms of K h and K^T v
   constexpr int NA = Terms<Cmp, Cmp>::n;  // MFMA terms of A' R
-  Cmp hb[NKB];  // the state as B operands of K h
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) hb[kb] = P::cmp_tiles(hs[2 * kb], hs[2 * kb + 1]);
   __syncthreads();  // the first chunk's inputs are staged
 
-  for (int c = 0; c < sq.nc; ++c) {
-    const int b = c & 1;
+  auto step = [&](auto B) {
+    constexpr int b = decltype(B)::value;
     const char* kt = sm.k[b];
     // LDS reads are issued one phase ahead of their use; scheduling barriers
     // keep each phase's reads, MFMAs and VALU work together.
-    // (0) reads for (1) and (3): K rows of row tiles 0, 1, V, e^g, e^{g_last};
-    // publish the state; the decayed state e^{g_last} h, the accumulator of the
-    // update, covers the read latency
-    const float dL = sm.gx[b][64 + 63];  // first: the decay below waits for it alone
+    // (0) reads for (1) and (3): e^{g_last}, K rows of row tiles 0, 1, V, e^g
+    const float dL = sm.gx[b][64 + 63];
     __builtin_amdgcn_sched_barrier(0);
     In kf[4][NKB];
 #pragma unroll
@@ -518,30 +513,33 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
       eg[rt] = *reinterpret_cast<const f32x4*>(&sm.gx[b][64 + 16 * rt + 4 * lg]);
       vv[rt] = v_rows(sm.v[b], rt, lane);
     }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) P::st_cmp(sm.h[b][kb], lane, hb[kb]);
     f32x4 hd[2 * NKB];
 #pragma unroll
     for (int t = 0; t < 2 * NKB; ++t) hd[t] = hs[t] * dL;
     __builtin_amdgcn_sched_barrier(0);
 
-    // (1) Z = K h for row tiles 0, 1 (accumulators split by key-block parity
-    // for independent chains); reads for (2): K rows of row tiles 2, 3
+    // (1) the state as B operands of K h, one key block at a time, published
+    // for the output waves; Z = K h for row tiles 0, 1 (accumulators split by
+    // key-block parity for independent chains); reads for (2): K rows of row
+    // tiles 2, 3
 #pragma unroll
     for (int rt = 2; rt < 4; ++rt)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) kf[rt][kb] = KF::row(kt, 16 * rt + lc, kb, lg);
+    Cmp hb[NKB];
     f32x4 z[4][2];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) z[rt][0] = z[rt][1] = zero4();
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      hb[kb] = P::cmp_tiles(hs[2 * kb], hs[2 * kb + 1]);
+      P::st_cmp(sm.h[b][kb], lane, hb[kb]);
 #pragma unroll
       for (int t = 0; t < NZ; ++t)
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) z[rt][kb & 1] = term(kf[rt][kb], hb[kb], z[rt][kb & 1], t);
+    }
     __builtin_amdgcn_sched_barrier(0);
-
     // (2) Z for row tiles 2, 3, with R = V - e^g Z of row tiles 0, 1 under it;
     // reads for (3): A', e^{g_last - g}
     Cmp af[6];
@@ -599,21 +597,23 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
     const Cmp gb1 = P::cmp_tiles(vn2 * egl[2], vn3 * egl[3]);
     __builtin_amdgcn_sched_barrier(0);
 
-    // (6) token block 1, one pair of state tiles at a time, with the next
-    // step's split of each finished pair under the following ones
+    // (6) token block 1
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int t = 0; t < NZ; ++t)
 #pragma unroll
-      for (int t = 0; t < NZ; ++t)
-#pragma unroll
-        for (int i = 2 * kb; i < 2 * kb + 2; ++i) hd[i] = term(ktf[i][1], gb1, hd[i], t);
-      if (kb > 0) hb[kb - 1] = P::cmp_tiles(hd[2 * kb - 2], hd[2 * kb - 1]);
-    }
-    hb[NKB - 1] = P::cmp_tiles(hd[2 * NKB - 2], hd[2 * NKB - 1]);
+      for (int i = 0; i < 2 * NKB; ++i) hd[i] = term(ktf[i][1], gb1, hd[i], t);
 #pragma unroll
     for (int i = 0; i < 2 * NKB; ++i) hs[i] = hd[i];
     __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  int c = 0;
+  for (; c + 1 < sq.nc; c += 2) {
+    step(I0{});
+    step(I1{});
   }
+  if (c < sq.nc) step(I0{});
   if (s_out) {
 #pragma unroll
     for (int t = 0; t < 2 * NKB; ++t) {
@@ -825,7 +825,7 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wv == 0)
-    scan_chain<K, V, Tin>(sm, sq, h0, ht, pool, pool_slots, slots, H);
+    scan_chain<K, V, Tin>(sm, sq, h0, ht, pool, pool_slots, slots, H, ws);
   else if (wv == 1)
     scan_output<0, K, V, Tin, Tout>(sm, sq, q, k, v, o, H, scale, ws);
   else
