@@ -442,12 +442,20 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
 template <int K, typename Tin>
 struct ScanSmem {
   static constexpr int NKB = K / 32;
-  char (*k)[KTile<K, Tin>::kBytes];  // [2] K tiles (swizzled)
-  char (*a)[6][2 * kPlane];          // [2] A' tiles, two planes each
-  Tin (*v)[kChunk * 16];             // [2] V slice [token][16]
-  float (*gx)[3 * kChunk];           // [2] g, e^g, e^{g_last - g}
+  // q, P and the gate vectors of the output waves are staged in LDS for bf16
+  // inputs; for fp32 inputs they would not fit and are loaded into registers.
+  static constexpr bool kOutLds = sizeof(Tin) == 2;
+  static constexpr int kQBytes = kOutLds ? KTile<K, Tin>::kBytes : 16;
+  static constexpr int kPTiles = kOutLds ? 6 : 1;
+  char (*k)[KTile<K, Tin>::kBytes];  // [2] K tiles (swizzled), chain
+  char (*a)[6][2 * kPlane];          // [2] A' tiles, two planes each, chain
+  Tin (*v)[kChunk * 16];             // [2] V slice [token][16], chain
+  float (*gx)[3 * kChunk];           // [2] g, e^g, e^{g_last - g}, chain
   char (*h)[NKB][2 * kPlane];        // [2] published state (B operands)
   f32x4 (*vn)[4][64];                // [2] published v_new tiles
+  char (*qt)[kQBytes];               // [2] q tiles (swizzled like K), output waves
+  char (*pt)[kPTiles][2 * kPlane];   // [2] P tiles, output waves
+  float (*go)[3 * kChunk];           // [2] gate vectors, output waves
 };
 
 struct ScanSeq {
@@ -623,99 +631,106 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
   }
 }
 
-// Output wave OW (row tiles 2 OW and 2 OW + 1). Wave 1 stages K, wave 2 stages
-// A', the V slice and the gate vectors of the chain's next chunk.
+// Every global access below goes through a buffer descriptor of one chunk:
+// base at its first row for this head, size ending at its last row, so rows
+// past the end read as zeros (loads, copies) or are dropped (stores).
+// Per-lane offsets are the same for every chunk.
+template <int K, int V, typename Tin>
+struct ScanIo {
+  static constexpr uint32_t ES = sizeof(Tin);
+  const ScanSeq& sq;
+  int H;
+  uint32_t row_k, row_v;  // bytes between tokens of q / k and of v
+  __device__ ScanIo(const ScanSeq& s, int h_count)
+      : sq(s), H(h_count), row_k(static_cast<uint32_t>(h_count) * K * ES), row_v(static_cast<uint32_t>(h_count) * V * ES) {}
+  __device__ int rows(int c) const { return min(kChunk, sq.len - kChunk * c); }
+  __device__ int64_t token0(int c) const { return static_cast<int64_t>(sq.start + kChunk * c); }
+  __device__ int64_t chunk_head(int c) const { return static_cast<int64_t>(sq.chunk0 + c) * H + sq.h; }
+  __device__ Buf qk(const Tin* base, int c) const {  // q or k rows of chunk c, this head
+    return Buf(base + (token0(c) * H + sq.h) * K, (rows(c) - 1) * row_k + K * ES);
+  }
+};
+
+// The producer wave: every direct-to-LDS copy. In the interval that ends with
+// chain step c it stages the chain's inputs of chunk c + 1 (K, A', the V slice,
+// the gate vectors) and, for bf16 inputs, the output waves' inputs of chunk c
+// (q, P, the gate vectors); all copies have landed before the barrier.
+template <int K, int V, typename Tin>
+__device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin>& sm, const ScanSeq& sq, const Tin* __restrict__ q,
+                                              const Tin* __restrict__ k, const Tin* __restrict__ v, int H,
+                                              const ChunkWs& ws) {
+  using S = ScanSmem<K, Tin>;
+  const int lane = threadIdx.x & 63;
+  const ScanIo<K, V, Tin> io(sq, H);
+  // Rows past the chunk's end are zeros: they meet zero columns of A' and
+  // zero rows of v_new (and are never stored).
+  auto stage_chain = [&](int c, int b) {
+    dma_k_tile<K, Tin>(io.qk(k, c), io.row_k, sm.k[b]);
+    const int64_t ch = io.chunk_head(c);
+    const Buf ad(ws.af + ch * (8 * 2 * kPlane), 8 * 2 * kPlane);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (ks > 0 && rt < 2) continue;
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+          ad.to_lds16(sm.a[b][a_tile(rt, ks)] + pl * kPlane, 16 * lane, ((rt * 2 + ks) * 2 + pl) * kPlane);
+      }
+    const Buf vd(v + (io.token0(c) * H + sq.h) * V + sq.slice * 16, (io.rows(c) - 1) * io.row_v + 16 * io.ES);
+    dma_v_slice<Tin>(vd, io.row_v, sm.v[b]);
+    const Buf gd(ws.gx + ch * 192, 192 * 4);
+    if (lane < 3 * kChunk / 4) gd.to_lds16(sm.gx[b], 16 * lane, 0);
+  };
+  auto stage_out = [&](int c, int b) {
+    dma_k_tile<K, Tin>(io.qk(q, c), io.row_k, sm.qt[b]);
+    const int64_t ch = io.chunk_head(c);
+    const Buf pd(ws.pf + ch * (8 * 2 * kPlane), 8 * 2 * kPlane);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        if (tb > 0 && rt < 2) continue;
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+          pd.to_lds16(sm.pt[b][a_tile(rt, tb)] + pl * kPlane, 16 * lane, ((rt * 2 + tb) * 2 + pl) * kPlane);
+      }
+    const Buf gd(ws.gx + ch * 192, 192 * 4);
+    if (lane < 3 * kChunk / 4) gd.to_lds16(sm.go[b], 16 * lane, 0);
+  };
+  const int nc = sq.nc;
+  if (nc > 0) stage_chain(0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int c = 0; c < nc; ++c) {
+    if (c + 1 < nc) stage_chain(c + 1, (c + 1) & 1);
+    if constexpr (S::kOutLds) stage_out(c, c & 1);
+    wait_vmem();
+    __syncthreads();
+  }
+}
+
+// Output wave OW (row tiles 2 OW and 2 OW + 1): in the interval that ends with
+// chain step c it emits the rows of chunk c - 1, o = s e^g (q h) + P v_new,
+// from the published state and v_new.
 template <int OW, int K, int V, typename Tin, typename Tout>
 __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const ScanSeq& sq, const Tin* __restrict__ q,
-                                            const Tin* __restrict__ k, const Tin* __restrict__ v,
                                             Tout* __restrict__ o, int H, float scale, const ChunkWs& ws) {
+  using S = ScanSmem<K, Tin>;
   using P = Prec<Tin>;
   using In = typename P::In;
   using Cmp = typename P::Cmp;
+  using KF = KFrag<K, Tin>;
   constexpr int NKB = K / 32;
   constexpr int NTB = OW + 1;  // token blocks of P v_new for these row tiles
   const int lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
-  const int h = sq.h;
-
-  // Every global access goes through a buffer descriptor of the chunk: base at
-  // its first row for this head, size ending at its last row, so rows past the
-  // end read as zeros (loads, copies) or are dropped (stores). Per-lane offsets
-  // are the same for every chunk.
-  constexpr uint32_t ES = sizeof(Tin);
-  const uint32_t row_k = static_cast<uint32_t>(H) * K * ES;  // bytes between tokens of q and k
-  const uint32_t row_v = static_cast<uint32_t>(H) * V * ES;
+  const ScanIo<K, V, Tin> io(sq, H);
   const uint32_t row_o = static_cast<uint32_t>(H) * V * sizeof(Tout);
-  auto rows = [&](int c) { return min(kChunk, sq.len - kChunk * c); };
-  auto token0 = [&](int c) { return static_cast<int64_t>(sq.start + kChunk * c); };
-  auto chunk_head = [&](int c) { return static_cast<int64_t>(sq.chunk0 + c) * H + h; };
 
-  // Stage the chain's inputs of chunk c into buffer b (rows past the chunk's
-  // end are zeros: they meet zero columns of A' and zero rows of v_new).
-  auto stage = [&](int c, int b) {
-    const int n = rows(c);
-    if (OW == 0) {
-      const Buf kd(k + (token0(c) * H + h) * K, (n - 1) * row_k + K * ES);
-      dma_k_tile<K, Tin>(kd, row_k, sm.k[b]);
-    } else {
-      const int64_t ch = chunk_head(c);
-      const Buf ad(ws.af + ch * (8 * 2 * kPlane), 8 * 2 * kPlane);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if (ks > 0 && rt < 2) continue;
-#pragma unroll
-          for (int pl = 0; pl < 2; ++pl)
-            ad.to_lds16(sm.a[b][a_tile(rt, ks)] + pl * kPlane, 16 * lane, ((rt * 2 + ks) * 2 + pl) * kPlane);
-        }
-      const Buf vd(v + (token0(c) * H + h) * V + sq.slice * 16, (n - 1) * row_v + 16 * ES);
-      dma_v_slice<Tin>(vd, row_v, sm.v[b]);
-      const Buf gd(ws.gx + ch * 192, 192 * 4);
-      if (lane < 3 * kChunk / 4) gd.to_lds16(sm.gx[b], 16 * lane, 0);
-    }
-  };
-
-  struct Regs {
-    In q[2][NKB];
-    Cmp p[2][NTB];
-    f32x4 eg[2];
-  };
-  const uint32_t q_voff = static_cast<uint32_t>(lc) * row_k + 8 * lg * ES;
-  auto load = [&](Regs& rg, int c) {
-    const int n = rows(c);
-    const int64_t ch = chunk_head(c);
-    const Buf qd(q + (token0(c) * H + h) * K, (n - 1) * row_k + K * ES);
-    const Buf pd(ws.pf + ch * (8 * 2 * kPlane), 8 * 2 * kPlane);
-    const Buf gd(ws.gx + ch * 192, 192 * 4);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rt = 2 * OW + i;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const uint32_t so = 16 * rt * row_k + 32 * kb * ES;
-        if constexpr (sizeof(Tin) == 2) {
-          rg.q[i][kb] = In{as_bf16x8(qd.load16(q_voff, so))};
-        } else {
-          rg.q[i][kb] = In{__builtin_bit_cast(f32x4, qd.load16(q_voff, so)),
-                           __builtin_bit_cast(f32x4, qd.load16(q_voff + 16, so))};
-        }
-      }
-#pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) {
-        const uint32_t so = (rt * 2 + tb) * 2 * kPlane;
-        const u32x4 p0 = pd.load16(16 * lane, so), p1 = pd.load16(16 * lane, so + kPlane);
-        if constexpr (sizeof(Tin) == 2) {
-          rg.p[i][tb] = Cmp{as_bf16x8(p0), as_bf16x8(p1)};
-        } else {
-          rg.p[i][tb] = Cmp{__builtin_bit_cast(f32x4, p0), __builtin_bit_cast(f32x4, p1)};
-        }
-      }
-      rg.eg[i] = __builtin_bit_cast(f32x4, gd.load16(4 * (64 + 16 * rt + 4 * lg), 0));
-    }
-  };
-  auto emit = [&](const Regs& rg, int c) {
+  // o rows of chunk c from its q fragments, P fragments and e^g
+  auto emit = [&](int c, const In (&qf)[2][NKB], const Cmp (&pf)[2][NTB], const f32x4 (&eg)[2]) {
     const int b = c & 1;
-    const Buf od(o + (token0(c) * H + h) * V + sq.slice * 16, (rows(c) - 1) * row_o + 16 * sizeof(Tout));
+    const Buf od(o + (io.token0(c) * H + sq.h) * V + sq.slice * 16, (io.rows(c) - 1) * row_o + 16 * sizeof(Tout));
     Cmp hb[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) hb[kb] = P::ld_cmp(sm.h[b][kb], lane);
@@ -725,70 +740,110 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const Sc
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int rt = 2 * OW + i;
-      f32x4 y = mma(rg.q[i][0], hb[0], zero4());
+      f32x4 y = mma(qf[i][0], hb[0], zero4());
 #pragma unroll
-      for (int kb = 1; kb < NKB; ++kb) y = mma(rg.q[i][kb], hb[kb], y);
-      f32x4 acc = (scale * rg.eg[i]) * y;
+      for (int kb = 1; kb < NKB; ++kb) y = mma(qf[i][kb], hb[kb], y);
+      f32x4 acc = (scale * eg[i]) * y;
 #pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) acc = mma(rg.p[i][tb], vb[tb], acc);
+      for (int tb = 0; tb < NTB; ++tb) acc = mma(pf[i][tb], vb[tb], acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         od.store(static_cast<Tout>(acc[r]), (4 * lg + r) * row_o + lc * sizeof(Tout), 16 * rt * row_o);
     }
   };
 
-  // Interval c (0 <= c <= nc) runs between the barriers that close chain steps
-  // c - 1 and c (the last one has no closing barrier): it stages the chain's
-  // chunk c + 1, loads this wave's operands of chunk c and emits the output rows
-  // of chunk c - 1. Every staged copy has landed before the closing barrier.
-  // Inside the loop staging and loads are unconditional (chunk indices clamped;
-  // an extra copy lands in the buffer the chain is not reading), so that the
-  // wait counters can keep them in flight across the output work.
   const int nc = sq.nc;
-  if (nc > 0) stage(0, 0);
-  wait_vmem();
   __syncthreads();
-  if (nc > 0) {
-    Regs ra, rb;
-    if (nc > 1) stage(1, 1);
-    load(ra, 0);
+  if constexpr (S::kOutLds) {
+    // operands staged by the producer into buffer c & 1
+    auto emit_lds = [&](int c) {
+      const int b = c & 1;
+      In qf[2][NKB];
+      Cmp pf[2][NTB];
+      f32x4 eg[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int rt = 2 * OW + i;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) qf[i][kb] = KF::row(sm.qt[b], 16 * rt + lc, kb, lg);
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) pf[i][tb] = P::ld_cmp(sm.pt[b][a_tile(rt, tb)], lane);
+        eg[i] = *reinterpret_cast<const f32x4*>(&sm.go[b][64 + 16 * rt + 4 * lg]);
+      }
+      emit(c, qf, pf, eg);
+    };
+    for (int c = 0; c < nc; ++c) {
+      if (c > 0) emit_lds(c - 1);
+      __syncthreads();
+    }
+    if (nc > 0) emit_lds(nc - 1);
+  } else {
+    // operands loaded into registers one chunk ahead (ping-pong)
+    struct Regs {
+      In q[2][NKB];
+      Cmp p[2][NTB];
+      f32x4 eg[2];
+    };
+    const uint32_t q_voff = static_cast<uint32_t>(lc) * io.row_k + 8 * lg * io.ES;
+    auto load = [&](Regs& rg, int c) {
+      const int64_t ch = io.chunk_head(c);
+      const Buf qd = io.qk(q, c);
+      const Buf pd(ws.pf + ch * (8 * 2 * kPlane), 8 * 2 * kPlane);
+      const Buf gd(ws.gx + ch * 192, 192 * 4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int rt = 2 * OW + i;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) rg.q[i][kb] = buf_frag(qd, q_voff, 16 * rt * io.row_k + 32 * kb * io.ES, q);
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+          const uint32_t so = (rt * 2 + tb) * 2 * kPlane;
+          rg.p[i][tb] = Cmp{__builtin_bit_cast(f32x4, pd.load16(16 * lane, so)),
+                            __builtin_bit_cast(f32x4, pd.load16(16 * lane, so + kPlane))};
+        }
+        rg.eg[i] = __builtin_bit_cast(f32x4, gd.load16(4 * (64 + 16 * rt + 4 * lg), 0));
+      }
+    };
+    if (nc > 0) {
+      Regs ra, rb;
+      load(ra, 0);
+      wait_vmem();
+      __syncthreads();
+      int c = 1;
+      for (; c + 1 < nc; c += 2) {  // c odd
+        load(rb, c);
+        __builtin_amdgcn_sched_barrier(0);  // loads go out before the output work
+        emit(c - 1, ra.q, ra.p, ra.eg);
+        wait_vmem();
+        __syncthreads();
+        load(ra, c + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        emit(c, rb.q, rb.p, rb.eg);
+        wait_vmem();
+        __syncthreads();
+      }
+      if (c < nc) {  // c == nc - 1: intervals nc - 1 and nc remain
+        load(rb, c);
+        __builtin_amdgcn_sched_barrier(0);
+        emit(c - 1, ra.q, ra.p, ra.eg);
+        wait_vmem();
+        __syncthreads();
+        emit(c, rb.q, rb.p, rb.eg);
+      } else {  // c == nc: the last interval remains
+        emit(c - 1, ra.q, ra.p, ra.eg);
+      }
+    }
     wait_vmem();
-    __syncthreads();
-    int c = 1;
-    for (; c + 1 < nc; c += 2) {  // c odd
-      stage(c + 1, 0);
-      load(rb, c);
-      __builtin_amdgcn_sched_barrier(0);  // loads go out before the output work
-      emit(ra, c - 1);
-      wait_vmem();
-      __syncthreads();
-      stage(min(c + 2, nc - 1), 1);
-      load(ra, c + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      emit(rb, c);
-      wait_vmem();
-      __syncthreads();
-    }
-    if (c < nc) {  // c == nc - 1: intervals nc - 1 and nc remain
-      load(rb, c);
-      __builtin_amdgcn_sched_barrier(0);  // loads go out before the output work
-      emit(ra, c - 1);
-      wait_vmem();
-      __syncthreads();
-      emit(rb, c);
-    } else {  // c == nc: the last interval remains
-      emit(ra, c - 1);
-    }
   }
-  wait_vmem();
 }
 
 template <int K, int V, typename Tin, typename Tout>
-__global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o, int H,
     float scale, int n_seqs, int T_eq, int ncs_eq, int total_tokens, int n_chunks, const int32_t* __restrict__ cu,
     const float* __restrict__ h0, float* __restrict__ ht, float* __restrict__ pool, int64_t pool_slots,
     const int32_t* __restrict__ slots, ChunkWs ws) {
+  using S = ScanSmem<K, Tin>;
   constexpr int NSL = V / 16;
   constexpr int NKB = K / 32;
   __shared__ __attribute__((aligned(1024))) char lds_k[2][KTile<K, Tin>::kBytes];
@@ -797,7 +852,10 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __attribute__((aligned(16))) float lds_gx[2][3 * kChunk];
   __shared__ __attribute__((aligned(16))) char lds_h[2][NKB][2 * kPlane];
   __shared__ __attribute__((aligned(16))) f32x4 lds_vn[2][4][64];
-  const ScanSmem<K, Tin> sm{lds_k, lds_a, lds_v, lds_gx, lds_h, lds_vn};
+  __shared__ __attribute__((aligned(1024))) char lds_qt[2][S::kQBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_pt[2][S::kPTiles][2 * kPlane];
+  __shared__ __attribute__((aligned(16))) float lds_go[2][3 * kChunk];
+  const S sm{lds_k, lds_a, lds_v, lds_gx, lds_h, lds_vn, lds_qt, lds_pt, lds_go};
 
   // Workgroups of one (sequence, head) share an XCD (blockIdx % 8) and its L2.
   const int bid = blockIdx.x;
@@ -823,13 +881,16 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   sq.nc = (sq.len + kChunk - 1) / kChunk;
 
+  // Wave roles: 0 the chain, 1 the producer, 2 and 3 the output waves.
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wv == 0)
     scan_chain<K, V, Tin>(sm, sq, h0, ht, pool, pool_slots, slots, H, ws);
   else if (wv == 1)
-    scan_output<0, K, V, Tin, Tout>(sm, sq, q, k, v, o, H, scale, ws);
+    scan_producer<K, V, Tin>(sm, sq, q, k, v, H, ws);
+  else if (wv == 2)
+    scan_output<0, K, V, Tin, Tout>(sm, sq, q, o, H, scale, ws);
   else
-    scan_output<1, K, V, Tin, Tout>(sm, sq, q, k, v, o, H, scale, ws);
+    scan_output<1, K, V, Tin, Tout>(sm, sq, q, o, H, scale, ws);
 }
 
 // ---------------------------------------------------------------------------
@@ -889,7 +950,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
   if (a.events[1]) (void)hipEventRecord(a.events[1], a.stream);
   const int64_t pairs = static_cast<int64_t>(a.n_seqs) * a.H;
   const int64_t blocks = 8 * NSL * ((pairs + 7) / 8);
-  hipLaunchKernelGGL((scan_kernel<K, V, Tin, Tout>), dim3(static_cast<unsigned>(blocks)), dim3(192), 0,
+  hipLaunchKernelGGL((scan_kernel<K, V, Tin, Tout>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
                      static_cast<const Tin*>(a.v), static_cast<Tout*>(a.o), a.H, a.scale, a.n_seqs, a.T_eq, ncs_eq,
                      static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0, a.ht, a.pool,
