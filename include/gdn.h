@@ -142,6 +142,12 @@ gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const void* v, c
  *
  * Per active row b and head h: S = pool[slots[b], h]; S <- exp(a) S;
  * S <- S + beta (v - S k) k^T; o = S (scale q); the updated S is stored back.
+ *
+ * Returns GDN_EUNSUPPORTED for K or V outside {64, 128} or an unknown dtype;
+ * GDN_EINVAL for N < 0, H outside [1, 65535], N * H * V / 16 > INT32_MAX (one
+ * workgroup per 16 state rows), a NULL pointer, pool_slots <= 0 or a misaligned
+ * pointer (pool 16 bytes, g / beta / slots 4 bytes, q / k / v / o their element
+ * size); GDN_OK without launching for N == 0; GDN_EHIP if the launch fails.
  */
 gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g,
                               const float* beta, float* state_pool, int64_t pool_slots,

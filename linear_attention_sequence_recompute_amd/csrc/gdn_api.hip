@@ -170,6 +170,8 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !supported_dim(K) || !supported_dim(V))
     return GDN_EUNSUPPORTED;
   if (N < 0 || H <= 0 || H > 65535) return GDN_EINVAL;
+  // one workgroup per 16 state rows of each (request, head), in a 1-D grid
+  if (static_cast<int64_t>(N) * H * (V / 16) > INT32_MAX) return GDN_EINVAL;
   if (N == 0) return GDN_OK;
   if (!q || !k || !v || !g || !beta || !state_pool || !slots || !o || pool_slots <= 0) return GDN_EINVAL;
   if (!aligned(state_pool, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(slots, 4)) return GDN_EINVAL;

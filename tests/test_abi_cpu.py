@@ -135,3 +135,8 @@ def test_recurrent_step_validation():
     assert _step(pool_slots=0) == E.GDN_EINVAL
     assert _step(pool=FAKE + 4) == E.GDN_EINVAL
     assert _step(q=FAKE + 1) == E.GDN_EINVAL
+
+
+def test_recurrent_step_grid_limit():
+    # one workgroup per 16 state rows of each (request, head) must fit a 1-D grid
+    assert _step(N=1 << 20, H=4096, V=128) == _lib.GDN_EINVAL
