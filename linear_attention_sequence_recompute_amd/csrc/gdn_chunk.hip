@@ -502,7 +502,7 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
   constexpr int NA = Terms<Cmp, Cmp>::n;  // MFMA terms of A' R
   __syncthreads();  // the first chunk's inputs are staged
 
-  auto step = [&](auto B) {
+  auto step = [&](auto B, f32x4 (&hs)[2 * NKB], f32x4 (&hd)[2 * NKB]) {
     constexpr int b = decltype(B)::value;
     const char* kt = sm.k[b];
     // LDS reads are issued one phase ahead of their use; scheduling barriers
@@ -521,7 +521,6 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
       eg[rt] = *reinterpret_cast<const f32x4*>(&sm.gx[b][64 + 16 * rt + 4 * lg]);
       vv[rt] = v_rows(sm.v[b], rt, lane);
     }
-    f32x4 hd[2 * NKB];
 #pragma unroll
     for (int t = 0; t < 2 * NKB; ++t) hd[t] = hs[t] * dL;
     __builtin_amdgcn_sched_barrier(0);
@@ -610,18 +609,23 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
     for (int t = 0; t < NZ; ++t)
 #pragma unroll
       for (int i = 0; i < 2 * NKB; ++i) hd[i] = term(ktf[i][1], gb1, hd[i], t);
-#pragma unroll
-    for (int i = 0; i < 2 * NKB; ++i) hs[i] = hd[i];
     __syncthreads();
   };
+  // The state alternates between two register sets (hs in, hd out), so the
+  // in-place split of the incoming state needs no copy of it.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
+  f32x4 hx[2 * NKB];
   int c = 0;
   for (; c + 1 < sq.nc; c += 2) {
-    step(I0{});
-    step(I1{});
+    step(I0{}, hs, hx);
+    step(I1{}, hx, hs);
   }
-  if (c < sq.nc) step(I0{});
+  if (c < sq.nc) {
+    step(I0{}, hs, hx);
+#pragma unroll
+    for (int i = 0; i < 2 * NKB; ++i) hs[i] = hx[i];
+  }
   if (s_out) {
 #pragma unroll
     for (int t = 0; t < 2 * NKB; ++t) {
