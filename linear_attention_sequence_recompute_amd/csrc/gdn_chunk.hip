@@ -525,10 +525,9 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
     for (int t = 0; t < 2 * NKB; ++t) hd[t] = hs[t] * dL;
     __builtin_amdgcn_sched_barrier(0);
 
-    // (1) the state as B operands of K h, one key block at a time, published
-    // for the output waves; Z = K h for row tiles 0, 1 (accumulators split by
-    // key-block parity for independent chains); reads for (2): K rows of row
-    // tiles 2, 3
+    // (1) the state as B operands of K h, one key block at a time; Z = K h for
+    // row tiles 0, 1 (accumulators split by key-block parity for independent
+    // chains); reads for (2): K rows of row tiles 2, 3
 #pragma unroll
     for (int rt = 2; rt < 4; ++rt)
 #pragma unroll
@@ -540,7 +539,6 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       hb[kb] = P::cmp_tiles(hs[2 * kb], hs[2 * kb + 1]);
-      P::st_cmp(sm.h[b][kb], lane, hb[kb]);
 #pragma unroll
       for (int t = 0; t < NZ; ++t)
 #pragma unroll
@@ -609,6 +607,9 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
     for (int t = 0; t < NZ; ++t)
 #pragma unroll
       for (int i = 0; i < 2 * NKB; ++i) hd[i] = term(ktf[i][1], gb1, hd[i], t);
+    // the state this step started from, for the output waves (read after the barrier)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) P::st_cmp(sm.h[b][kb], lane, hb[kb]);
     __syncthreads();
   };
   // The state alternates between two register sets (hs in, hd out), so the

@@ -91,7 +91,8 @@ struct FragF {  // fp32 values (elements 0..3 in a, 4..7 in b)
 // Products accumulated in fp32, as a fixed sequence of MFMA instructions
 // ("terms"): term(a, b, acc, t) issues the t-th, t < Terms<A, B>::n, so that
 // code can interleave the terms of independent products. The lo x lo term of
-// two split operands is dropped.
+// two split operands is dropped. Terms that use the hi half of a split operand
+// come first: a split forms hi before lo, so the first MFMA can start earlier.
 template <class A, class B>
 struct Terms;
 template <>
@@ -117,13 +118,14 @@ struct Terms<FragF, FragF> {
 
 __device__ __forceinline__ f32x4 term(const FragB& a, const FragB& b, f32x4 acc, int) { return mfma(a.x, b.x, acc); }
 __device__ __forceinline__ f32x4 term(const FragB& a, const FragS& b, f32x4 acc, int t) {
-  return mfma(a.x, t == 0 ? b.lo : b.hi, acc);
+  return mfma(a.x, t == 0 ? b.hi : b.lo, acc);
 }
 __device__ __forceinline__ f32x4 term(const FragS& a, const FragB& b, f32x4 acc, int t) {
-  return mfma(t == 0 ? a.lo : a.hi, b.x, acc);
+  return mfma(t == 0 ? a.hi : a.lo, b.x, acc);
 }
+// (b is the operand split last in the scan: its hi half first)
 __device__ __forceinline__ f32x4 term(const FragS& a, const FragS& b, f32x4 acc, int t) {
-  return t == 0 ? mfma(a.hi, b.lo, acc) : t == 1 ? mfma(a.lo, b.hi, acc) : mfma(a.hi, b.hi, acc);
+  return t == 0 ? mfma(a.hi, b.hi, acc) : t == 1 ? mfma(a.lo, b.hi, acc) : mfma(a.hi, b.lo, acc);
 }
 __device__ __forceinline__ f32x4 term(const FragF& a, const FragF& b, f32x4 acc, int t) {
   return t < 4 ? mfma_f32(a.a[t], b.a[t], acc) : mfma_f32(a.b[t - 4], b.b[t - 4], acc);
