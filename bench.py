@@ -8,10 +8,12 @@ resident in device memory. The decode step (gdn_recurrent_step, N=256 requests,
 H=32, K=V=128, a 512-slot float32 state pool) is timed beside it in the same run
 and reported under "decode".
 
-Prints one JSON line on stdout (everything else goes to stderr). Per-kernel
-durations come from HIP events recorded on the library's stream around each
-launch (gdn_chunk_fwd_profiled); the roofline of the dominant kernel (the scan
-kernel) is its algorithmic FLOPs per launch over that duration.
+Prints one JSON line on stdout (everything else goes to stderr). The K timed
+steps are plain calls. Per-kernel durations come from K further calls of
+gdn_chunk_fwd_profiled, which records HIP events on the library's stream around
+each launch (recording them inside the timed steps would add about 10 us per
+call); the roofline of the dominant kernel (the scan kernel) is its algorithmic
+FLOPs per launch over that duration.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --only chunk|decode|copy --steps K   (profiling runs)
@@ -156,13 +158,21 @@ def bench_chunk(torch, api, hev, steps, warmup, flush_bytes=512 << 20):
         step()
     torch.cuda.synchronize()
 
+    # the timed steps: plain calls (events between the two kernels cost about
+    # 10 us per call, so per-kernel durations come from the next loop)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-kernel durations: as many calls again, with HIP events the library
+    # records on the launch stream before prep, between the kernels and after scan
     evs = [hev.create(3) for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     prep = [hev.ms(e[0], e[1]) for e in evs]
     scan = [hev.ms(e[1], e[2]) for e in evs]
     whole = [hev.ms(e[0], e[2]) for e in evs]
