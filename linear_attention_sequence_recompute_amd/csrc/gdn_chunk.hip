@@ -224,23 +224,27 @@ __device__ __forceinline__ FragF buf_frag(const Buf& b, uint32_t voff, uint32_t 
 __device__ __forceinline__ constexpr int a_tile(int rt, int ks) { return rt < 2 ? rt : 2 + 2 * (rt - 2) + ks; }
 
 // V at rows 16 rt + 4 g + i (i < 4), column c of a [64][16] LDS tile, for lane
-// (g, c): the accumulator layout. For bf16 one transposed read serves the four
-// rows: source lane l of group g reads columns 4 (l & 3) .. + 3 of row
-// 16 rt + 4 g + (l >> 2), and output lane c receives element c & 3 of source
-// lane 4 i + (c >> 2) as its element i.
-__device__ __forceinline__ f32x4 v_rows(const __bf16* tile, int rt, int lane) {
+// (g, c): the accumulator layout. Read (v_raw) and widened to fp32 (v_wide)
+// separately, so that the read can be issued a phase ahead of its use. For bf16
+// one transposed read serves the four rows: source lane l of group g reads
+// columns 4 (l & 3) .. + 3 of row 16 rt + 4 g + (l >> 2), and output lane c
+// receives element c & 3 of source lane 4 i + (c >> 2) as its element i.
+__device__ __forceinline__ u32x2 v_raw(const __bf16* tile, int rt, int lane) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   const int g = lane >> 4, l = lane & 15;
   const __bf16* p = tile + (16 * rt + 4 * g + (l >> 2)) * 16 + 4 * (l & 3);
-  const u32x2 u = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p)));
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p)));
+}
+__device__ __forceinline__ f32x4 v_wide(const u32x2& u) {
   return f32x4{__builtin_bit_cast(float, u[0] << 16), __builtin_bit_cast(float, u[0] & 0xffff0000u),
                __builtin_bit_cast(float, u[1] << 16), __builtin_bit_cast(float, u[1] & 0xffff0000u)};
 }
-__device__ __forceinline__ f32x4 v_rows(const float* tile, int rt, int lane) {
+__device__ __forceinline__ f32x4 v_raw(const float* tile, int rt, int lane) {
   const int g = lane >> 4, c = lane & 15;
   const float* p = tile + (16 * rt + 4 * g) * 16 + c;
   return f32x4{p[0], p[16], p[32], p[48]};
 }
+__device__ __forceinline__ f32x4 v_wide(const f32x4& x) { return x; }
 
 // ---------------------------------------------------------------------------
 // recompute_w_u, reduced to what the fused scan needs: the chunk-local gate
@@ -495,39 +499,33 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
     const int key0 = 32 * (t >> 1) + 8 * lg + 4 * (t & 1);
     hs[t] = s_in ? *reinterpret_cast<const f32x4*>(s_in + static_cast<int64_t>(vcol) * K + key0) : zero4();
   }
-  // One chunk step; the LDS buffer index B is a compile-time constant. The
-  // state hs is split into the B operands of K h in place, after the decayed
-  // state e^{g_last} h (the update's accumulator, hd) has been formed from it.
   constexpr int NZ = Terms<In, Cmp>::n;   // MFMA terms of K h and K^T v
   constexpr int NA = Terms<Cmp, Cmp>::n;  // MFMA terms of A' R
+  using VRaw = decltype(v_raw(sm.v[0], 0, 0));
   __syncthreads();  // the first chunk's inputs are staged
 
+  // One chunk step from state hs to hd; the LDS buffer index B is a
+  // compile-time constant. hs is split into the B operands of K h in place,
+  // after the decayed state e^{g_last} h (the update's accumulator) is formed.
   auto step = [&](auto B, f32x4 (&hs)[2 * NKB], f32x4 (&hd)[2 * NKB]) {
     constexpr int b = decltype(B)::value;
     const char* kt = sm.k[b];
     // LDS reads are issued one phase ahead of their use; scheduling barriers
     // keep each phase's reads, MFMAs and VALU work together.
-    // (0) reads for (1) and (3): e^{g_last}, K rows of row tiles 0, 1, V, e^g
-    const float dL = sm.gx[b][64 + 63];
-    __builtin_amdgcn_sched_barrier(0);
+    // (0) reads for (1): K rows of row tiles 0, 1, and e^{g_last}
     In kf[4][NKB];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) kf[rt][kb] = KF::row(kt, 16 * rt + lc, kb, lg);
-    f32x4 vv[4], eg[4], egl[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      eg[rt] = *reinterpret_cast<const f32x4*>(&sm.gx[b][64 + 16 * rt + 4 * lg]);
-      vv[rt] = v_rows(sm.v[b], rt, lane);
-    }
+    const float dL = sm.gx[b][64 + 63];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 2 * NKB; ++t) hd[t] = hs[t] * dL;
-    __builtin_amdgcn_sched_barrier(0);
 
-    // (1) the state as B operands of K h, one key block at a time; Z = K h for
-    // row tiles 0, 1 (accumulators split by key-block parity for independent
-    // chains); reads for (2): K rows of row tiles 2, 3
+    // (1) the state as the B operands of K h, one key block at a time; Z = K h
+    // for row tiles 0, 1 (accumulators split by key-block parity for
+    // independent chains); reads for (2): K rows of row tiles 2, 3, V, e^g
 #pragma unroll
     for (int rt = 2; rt < 4; ++rt)
 #pragma unroll
@@ -544,7 +542,15 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) z[rt][kb & 1] = term(kf[rt][kb], hb[kb], z[rt][kb & 1], t);
     }
+    VRaw vr[4];
+    f32x4 eg[4], egl[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      vr[rt] = v_raw(sm.v[b], rt, lane);
+      eg[rt] = *reinterpret_cast<const f32x4*>(&sm.gx[b][64 + 16 * rt + 4 * lg]);
+    }
     __builtin_amdgcn_sched_barrier(0);
+
     // (2) Z for row tiles 2, 3, with R = V - e^g Z of row tiles 0, 1 under it;
     // reads for (3): A', e^{g_last - g}
     Cmp af[6];
@@ -558,7 +564,8 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
       for (int t = 0; t < NZ; ++t)
 #pragma unroll
         for (int rt = 2; rt < 4; ++rt) z[rt][kb & 1] = term(kf[rt][kb], hb[kb], z[rt][kb & 1], t);
-    const Cmp rb0 = P::cmp_tiles(vv[0] - eg[0] * (z[0][0] + z[0][1]), vv[1] - eg[1] * (z[1][0] + z[1][1]));
+    const Cmp rb0 = P::cmp_tiles(v_wide(vr[0]) - eg[0] * (z[0][0] + z[0][1]),
+                                 v_wide(vr[1]) - eg[1] * (z[1][0] + z[1][1]));
     __builtin_amdgcn_sched_barrier(0);
 
     // (3) v_new = A' R, token block 0 of all row tiles, with R of row tiles 2, 3
@@ -573,7 +580,8 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
     for (int t = 0; t < NA; ++t)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) acc[rt] = term(af[a_tile(rt, 0)], rb0, acc[rt], t);
-    const Cmp rb1 = P::cmp_tiles(vv[2] - eg[2] * (z[2][0] + z[2][1]), vv[3] - eg[3] * (z[3][0] + z[3][1]));
+    const Cmp rb1 = P::cmp_tiles(v_wide(vr[2]) - eg[2] * (z[2][0] + z[2][1]),
+                                 v_wide(vr[3]) - eg[3] * (z[3][0] + z[3][1]));
     __builtin_amdgcn_sched_barrier(0);
 
     // (4) token block 1 of row tiles 2, 3 (A' is lower triangular), with the
@@ -612,8 +620,8 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const Sca
     for (int kb = 0; kb < NKB; ++kb) P::st_cmp(sm.h[b][kb], lane, hb[kb]);
     __syncthreads();
   };
-  // The state alternates between two register sets (hs in, hd out), so the
-  // in-place split of the incoming state needs no copy of it.
+  // The state alternates between two register sets (hs in, hx out), so no
+  // copy is made between steps.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   f32x4 hx[2 * NKB];
