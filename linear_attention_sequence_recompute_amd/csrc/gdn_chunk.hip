@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   __shared__ float sg[64], sb[64];
 
   const int c = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lc = lane & 15;
   int t0, n;
   if (info) {
@@ -346,7 +346,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * bi + 4 * lg + r, j = 16 * bj + lc;
-      sLA[i][j] = j < i ? sb[i] * acc[r] * __expf(sg[i] - sg[j]) : 0.f;
+      // computed for every element and then selected: no branch per element
+      const float x = sb[i] * acc[r] * __expf(sg[i] - sg[j]);
+      sLA[i][j] = j < i ? x : 0.f;
     }
   }
 
@@ -369,7 +371,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tp = 16 * bt + 4 * lg + r;
-        d[half][r] = tp <= i ? scale * d[half][r] * __expf(sg[i] - sg[tp]) : 0.f;
+        const float x = scale * d[half][r] * __expf(sg[i] - sg[tp]);
+        d[half][r] = tp <= i ? x : 0.f;
       }
     }
     P::st_cmp(ws.pf + ch * (8 * 2 * kPlane) + (w * 2 + ks) * 2 * kPlane, lane, P::cmp_tiles(d[0], d[1]));
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   // registers: the four lanes (j, part) of column j are adjacent; lane part
   // keeps rows [4 part, 4 part + 4) of column j. Row i of (I + L) D = I gives
   // D[i][j] = -sum_m L[i][m] D[m][j] (L[i][m] = 0 for m >= i, and D[m][j] not
-  // yet known is 0); the four parts are added with shuffles.
+  // yet known is 0); the four parts are added by quad permutations.
   {
     const int j = lane >> 2, part = lane & 3;
     f32x4 lrow[15];
@@ -392,8 +395,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
 #pragma unroll
     for (int i = 1; i < 16; ++i) {
       float s = (lrow[i - 1][0] * a[0] + lrow[i - 1][1] * a[1]) + (lrow[i - 1][2] * a[2] + lrow[i - 1][3] * a[3]);
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
+      s += quad_xor1(s);
+      s += quad_xor2(s);
       if (part == (i >> 2) && i > j) a[i & 3] = -s;
     }
 #pragma unroll

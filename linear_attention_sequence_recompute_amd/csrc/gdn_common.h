@@ -315,6 +315,15 @@ struct Buf {
 };
 
 // Wave-wide inclusive prefix sum over 64 lanes.
+// x of lane (lane ^ 1) or (lane ^ 2) within each group of four lanes, by a DPP
+// quad permutation (no LDS round trip, unlike a general shuffle).
+__device__ __forceinline__ float quad_xor1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+}
+
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
