@@ -220,8 +220,11 @@ __device__ __forceinline__ FragF buf_frag(const Buf& b, uint32_t voff, uint32_t 
   return FragF{__builtin_bit_cast(f32x4, b.load16(voff, soff)), __builtin_bit_cast(f32x4, b.load16(voff + 16, soff))};
 }
 
-// Index of A' tile (row tile rt, token block ks) among the 6 nonzero ones.
-__device__ __forceinline__ constexpr int a_tile(int rt, int ks) { return rt < 2 ? rt : 2 + 2 * (rt - 2) + ks; }
+// Index of A' (or P) tile (row tile rt, token block ks) among the 6 nonzero
+// ones: (0, 0) (1, 0) (2, 0) (2, 1) (3, 0) (3, 1). The workspace holds these 6
+// per (chunk, head), each as hi and lo planes.
+__host__ __device__ __forceinline__ constexpr int a_tile(int rt, int ks) { return rt < 2 ? rt : 2 + 2 * (rt - 2) + ks; }
+constexpr int kTileSetBytes = 6 * 2 * kPlane;
 
 // V at rows 16 rt + 4 g + i (i < 4), column c of a [64][16] LDS tile, for lane
 // (g, c): the accumulator layout. Read (v_raw) and widened to fp32 (v_wide)
@@ -308,12 +311,20 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
     const Buf kd(k + base * K, (n - 1) * row_k + K * ES);
     dma_k_tile<K, Tin, 4>(kd, row_k, sK, w);
   }
-  In qf[NKB];
+  // Fragments (row block rb, token block ks) of P, numbered 2 rb + ks, that
+  // this wave computes in (2): three, three, two and two tiles per wave.
+  constexpr int kGrp[4][2] = {{0, 6}, {2, 5}, {4, -1}, {7, -1}};
+  In qg[2][NKB];
   {
     const Buf qd(q + base * K, (n - 1) * row_k + K * ES);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-      qf[kb] = buf_frag(qd, lc * row_k + 8 * lg * ES, 16 * w * row_k + 32 * kb * ES, q);
+    for (int gi = 0; gi < 2; ++gi) {
+      const int grp = kGrp[w][gi];
+      if (grp < 0) continue;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        qg[gi][kb] = buf_frag(qd, lc * row_k + 8 * lg * ES, 16 * (grp >> 1) * row_k + 32 * kb * ES, q);
+    }
   }
 
   // (1) chunk-local inclusive cumsum of the log-gate; beta; the gate vectors g,
@@ -332,50 +343,54 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   wait_vmem();
   __syncthreads();
 
-  // (2) L = StrictLower(diag(beta) K K^T * E): the 10 lower 16x16 tiles,
-  // written whole (zeros on and above the diagonal).
+  // (2) L = StrictLower(diag(beta) K K^T * E) and the score matrix of
+  // chunk_fwd_o, P = s (Q K^T) * E * M (E_ij = e^{g_i - g_j}, M the inclusive
+  // causal mask), by fragment of P: the tiles (rb, bt <= rb), bt = 2 ks + half,
+  // are computed transposed, K_bt K_rb^T and K_bt Q_rb^T, so that a pair of
+  // accumulator tiles is directly the A operand of P and each element's E
+  // serves both. Lane (g, c) then holds 4 consecutive columns j of row
+  // i = 16 rb + c: L is written whole (zeros on and above the diagonal), one
+  // 16-byte store per tile. Elements are computed and then selected (no branch).
 #pragma unroll
-  for (int tix = 0; tix < 10; ++tix) {
-    if ((tix & 3) != w) continue;
-    const int bi = tix == 0 ? 0 : tix < 3 ? 1 : tix < 6 ? 2 : 3;
-    const int bj = tix - (bi * (bi + 1)) / 2;
-    f32x4 acc = zero4();
+  for (int gi = 0; gi < 2; ++gi) {
+    const int grp = kGrp[w][gi];
+    if (grp < 0) continue;
+    const int rb = grp >> 1, ks = grp & 1;
+    const int i = 16 * rb + lc;
+    const float g_i = sg[i], b_i = sb[i];
+    In kr[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-      acc = mma(KF::row(sK, 16 * bi + lc, kb, lg), KF::row(sK, 16 * bj + lc, kb, lg), acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * bi + 4 * lg + r, j = 16 * bj + lc;
-      // computed for every element and then selected: no branch per element
-      const float x = sb[i] * acc[r] * __expf(sg[i] - sg[j]);
-      sLA[i][j] = j < i ? x : 0.f;
-    }
-  }
-
-  // (2b) the score matrix of chunk_fwd_o, P = s (Q K^T) * E * M (E_ij = e^{g_i - g_j},
-  // M the inclusive causal mask), computed transposed (P^T = K Q^T) so that pairs
-  // of accumulator tiles are directly its A operands; wave w owns row tile w.
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    f32x4 d[2] = {zero4(), zero4()};
+    for (int kb = 0; kb < NKB; ++kb) kr[kb] = KF::row(sK, i, kb, lg);
+    f32x4 pt[2] = {zero4(), zero4()};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int bt = 2 * ks + half;
-      if (bt > w) continue;
-      f32x4 part[NKB];
+      if (bt > rb) continue;
+      f32x4 lp[NKB], pp[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) part[kb] = mma(KF::row(sK, 16 * bt + lc, kb, lg), qf[kb], zero4());
+      for (int kb = 0; kb < NKB; ++kb) {
+        const In kt = KF::row(sK, 16 * bt + lc, kb, lg);
+        lp[kb] = mma(kt, kr[kb], zero4());
+        pp[kb] = mma(kt, qg[gi][kb], zero4());
+      }
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) d[half] += part[kb];
-      const int i = 16 * w + lc;
+      for (int kb = 1; kb < NKB; ++kb) {
+        lp[0] += lp[kb];
+        pp[0] += pp[kb];
+      }
+      const f32x4 g_j = *reinterpret_cast<const f32x4*>(&sg[16 * bt + 4 * lg]);
+      f32x4 lv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int tp = 16 * bt + 4 * lg + r;
-        const float x = scale * d[half][r] * __expf(sg[i] - sg[tp]);
-        d[half][r] = tp <= i ? x : 0.f;
+        const int j = 16 * bt + 4 * lg + r;
+        const float e = __expf(g_i - g_j[r]);
+        const float xl = b_i * lp[0][r] * e, xp = scale * pp[0][r] * e;
+        lv[r] = j < i ? xl : 0.f;
+        pt[half][r] = j <= i ? xp : 0.f;
       }
+      *reinterpret_cast<f32x4*>(&sLA[i][16 * bt + 4 * lg]) = lv;
     }
-    P::st_cmp(ws.pf + ch * (8 * 2 * kPlane) + (w * 2 + ks) * 2 * kPlane, lane, P::cmp_tiles(d[0], d[1]));
+    P::st_cmp(ws.pf + ch * kTileSetBytes + a_tile(rb, ks) * 2 * kPlane, lane, P::cmp_tiles(pt[0], pt[1]));
   }
   __syncthreads();
 
@@ -428,9 +443,10 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   }
 
   // (5) A' = A diag(beta) as A operands: wave w stores row tile w, token blocks
-  // 0 and 1 (blocks above the diagonal are zero).
+  // 0 and, for row tiles 2 and 3, 1 (the other blocks are zero).
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
+    if (ks > 0 && w < 2) continue;  // zero, and never read
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -439,7 +455,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
       const float av = mb == w ? sLA[16 * w + lc][m] : mb < w ? sOff[off_block(w, mb)][lc][m & 15] : 0.f;
       x[e] = av * sb[m];
     }
-    P::st_cmp(ws.af + ch * (8 * 2 * kPlane) + (w * 2 + ks) * 2 * kPlane, lane, P::cmp8(x));
+    P::st_cmp(ws.af + ch * kTileSetBytes + a_tile(w, ks) * 2 * kPlane, lane, P::cmp8(x));
   }
 }
 
@@ -683,7 +699,7 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin>& sm, const 
   auto stage_chain = [&](int c, int b) {
     dma_k_tile<K, Tin>(io.qk(k, c), io.row_k, sm.k[b]);
     const int64_t ch = io.chunk_head(c);
-    const Buf ad(ws.af + ch * (8 * 2 * kPlane), 8 * 2 * kPlane);
+    const Buf ad(ws.af + ch * kTileSetBytes, kTileSetBytes);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -691,7 +707,7 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin>& sm, const 
         if (ks > 0 && rt < 2) continue;
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl)
-          ad.to_lds16(sm.a[b][a_tile(rt, ks)] + pl * kPlane, 16 * lane, ((rt * 2 + ks) * 2 + pl) * kPlane);
+          ad.to_lds16(sm.a[b][a_tile(rt, ks)] + pl * kPlane, 16 * lane, (a_tile(rt, ks) * 2 + pl) * kPlane);
       }
     const Buf vd(v + (io.token0(c) * H + sq.h) * V + sq.slice * 16, (io.rows(c) - 1) * io.row_v + 16 * io.ES);
     dma_v_slice<Tin>(vd, io.row_v, sm.v[b]);
@@ -701,7 +717,7 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin>& sm, const 
   auto stage_out = [&](int c, int b) {
     dma_k_tile<K, Tin>(io.qk(q, c), io.row_k, sm.qt[b]);
     const int64_t ch = io.chunk_head(c);
-    const Buf pd(ws.pf + ch * (8 * 2 * kPlane), 8 * 2 * kPlane);
+    const Buf pd(ws.pf + ch * kTileSetBytes, kTileSetBytes);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -709,7 +725,7 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin>& sm, const 
         if (tb > 0 && rt < 2) continue;
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl)
-          pd.to_lds16(sm.pt[b][a_tile(rt, tb)] + pl * kPlane, 16 * lane, ((rt * 2 + tb) * 2 + pl) * kPlane);
+          pd.to_lds16(sm.pt[b][a_tile(rt, tb)] + pl * kPlane, 16 * lane, (a_tile(rt, tb) * 2 + pl) * kPlane);
       }
     const Buf gd(ws.gx + ch * 192, 192 * 4);
     if (lane < 3 * kChunk / 4) gd.to_lds16(sm.go[b], 16 * lane, 0);
@@ -804,7 +820,7 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const Sc
     auto load = [&](Regs& rg, int c) {
       const int64_t ch = io.chunk_head(c);
       const Buf qd = io.qk(q, c);
-      const Buf pd(ws.pf + ch * (8 * 2 * kPlane), 8 * 2 * kPlane);
+      const Buf pd(ws.pf + ch * kTileSetBytes, kTileSetBytes);
       const Buf gd(ws.gx + ch * 192, 192 * 4);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -813,7 +829,7 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const Sc
         for (int kb = 0; kb < NKB; ++kb) rg.q[i][kb] = buf_frag(qd, q_voff, 16 * rt * io.row_k + 32 * kb * io.ES, q);
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
-          const uint32_t so = (rt * 2 + tb) * 2 * kPlane;
+          const uint32_t so = a_tile(rt, tb) * 2 * kPlane;
           rg.p[i][tb] = Cmp{__builtin_bit_cast(f32x4, pd.load16(16 * lane, so)),
                             __builtin_bit_cast(f32x4, pd.load16(16 * lane, so + kPlane))};
         }
@@ -922,9 +938,9 @@ WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, b
   WsLayout l{};
   size_t off = 0;
   l.af = off;
-  off = align256(off + nch * 8 * 2 * kPlane);
+  off = align256(off + nch * kTileSetBytes);
   l.pf = off;
-  off = align256(off + nch * 8 * 2 * kPlane);
+  off = align256(off + nch * kTileSetBytes);
   l.gx = off;
   off = align256(off + nch * 3 * kChunk * 4);
   l.info = off;

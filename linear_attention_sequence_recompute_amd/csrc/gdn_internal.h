@@ -24,9 +24,10 @@ struct DecodeArgs {
 // Chunk intermediates written by the prep kernel and read by the scan kernel.
 // A fragment is stored as planes of [64 lanes][16 bytes] (see Prec in
 // gdn_common.h: two planes for a computed operand). "ch" = chunk * H + head.
-//   af  [ch][4 rt][2 ks][2 planes]   A' = A diag(beta) as A operands of output
-//        row tile rt over token block ks
-//   pf  [ch][4 rt][2 ks][2 planes]   P = s (Q K^T) * E * M, the same way
+//   af  [ch][6 tiles][2 planes]      A' = A diag(beta) as A operands: the
+//        nonzero (output row tile rt, token block ks) tiles (0,0) (1,0) (2,0)
+//        (2,1) (3,0) (3,1) in that order
+//   pf  [ch][6 tiles][2 planes]      P = s (Q K^T) * E * M, the same way
 //   gx  [ch][3][64] f32              g (chunk-local inclusive cumulative sum of
 //        the log-gate; rows past the chunk end repeat g_last), e^g, e^{g_last - g}
 //   info [chunk] int4 {seq, first token, rows, 0} and seq_chunk0 [n_seqs + 1]:

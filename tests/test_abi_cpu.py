@@ -52,9 +52,9 @@ def test_workspace_bytes():
     b2 = L.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 128, F32)
     b3 = L.gdn_chunk_fwd_workspace_bytes(16, 60217, 16, 128, 128, BF16)
     assert 0 < b1 <= b2 and b3 > b1
-    # A' and P (hi/lo fragments, 16 KiB each) plus three 64-float gate vectors per (chunk, head)
+    # A' and P (the 6 nonzero hi/lo fragment tiles, 12 KiB each) plus three 64-float gate vectors per (chunk, head)
     per = b1 / ((4096 // 64 + 1) * 16)
-    assert 32 * 1024 + 768 <= per < 34 * 1024
+    assert 24 * 1024 + 768 <= per < 26 * 1024
 
 
 def _chunk(**kw):
