@@ -220,6 +220,14 @@ __device__ __forceinline__ FragF buf_frag(const Buf& b, uint32_t voff, uint32_t 
   return FragF{__builtin_bit_cast(f32x4, b.load16(voff, soff)), __builtin_bit_cast(f32x4, b.load16(voff + 16, soff))};
 }
 
+// A computed-operand fragment from its two 16-byte planes (hi, lo or a, b).
+__device__ __forceinline__ FragS cmp_planes(const u32x4& x, const u32x4& y, FragS) {
+  return FragS{as_bf16x8(x), as_bf16x8(y)};
+}
+__device__ __forceinline__ FragF cmp_planes(const u32x4& x, const u32x4& y, FragF) {
+  return FragF{__builtin_bit_cast(f32x4, x), __builtin_bit_cast(f32x4, y)};
+}
+
 // Index of A' (or P) tile (row tile rt, token block ks) among the 6 nonzero
 // ones: (0, 0) (1, 0) (2, 0) (2, 1) (3, 0) (3, 1). The workspace holds these 6
 // per (chunk, head), each as hi and lo planes.
@@ -830,8 +838,7 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const Sc
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
           const uint32_t so = a_tile(rt, tb) * 2 * kPlane;
-          rg.p[i][tb] = Cmp{__builtin_bit_cast(f32x4, pd.load16(16 * lane, so)),
-                            __builtin_bit_cast(f32x4, pd.load16(16 * lane, so + kPlane))};
+          rg.p[i][tb] = cmp_planes(pd.load16(16 * lane, so), pd.load16(16 * lane, so + kPlane), Cmp{});
         }
         rg.eg[i] = __builtin_bit_cast(f32x4, gd.load16(4 * (64 + 16 * rt + 4 * lg), 0));
       }
