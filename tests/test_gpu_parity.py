@@ -132,6 +132,20 @@ def test_fp32_mode_long_memory():
     check_chunk(ci, 0.3, label="f32 long memory")
 
 
+@pytest.mark.parametrize("K,V", [(128, 64), (64, 128)])
+def test_fp32_mode_mixed_head_sizes(K, V):
+    """float32 inputs with K != V: several chunks, a ragged tail, long memory."""
+    ci = chunk_inputs([200], 2, K, V, dtype="f32", seed=40 + K + V, gate_shift=-4.0, h0_std=0.1)
+    check_chunk(ci, K ** -0.5, label=f"f32 K={K} V={V}")
+
+
+def test_odd_batch_and_heads():
+    """3 sequences x 5 heads = 15 (sequence, head) pairs: the launch pads the pairs
+    to a multiple of 8 (one per XCD) and the padding workgroups must do nothing."""
+    ci = chunk_inputs([130] * 3, 5, 128, 128, dtype="bf16", seed=41, h0_std=0.1)
+    check_chunk(ci, 128 ** -0.5, label="B=3 H=5")
+
+
 def test_config_h16_t4096_full():
     """B=1, H=16, T=4096, K=V=128, bf16: every output and the final state."""
     ci = chunk_inputs([4096], 16, 128, 128, dtype="bf16", seed=2)
