@@ -738,6 +738,42 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin>& sm, const 
     const Buf gd(ws.gx + ch * 192, 192 * 4);
     if (lane < 3 * kChunk / 4) gd.to_lds16(sm.go[b], 16 * lane, 0);
   };
+  // L2 prefetch of chunk c: one 4-byte read per 128-byte line of its K and q
+  // rows, A', P and this workgroup's V slice, into registers nobody uses (an
+  // empty asm consumes them an interval later, when they have long landed, so
+  // the compiler keeps the loads and waits for them only there). The
+  // workgroups of a (sequence, head) share an XCD and its L2, so each takes
+  // 1 / NSL of the shared lines (rows or lines s, s + NSL, ...); the V lines
+  // are its own. Five loads whatever c is (lanes with nothing to read are out
+  // of range).
+  constexpr int NSL = V / 16;
+  constexpr int kLinesRow = KTile<K, Tin>::kRowBytes / 128;  // lines per K or q row (>= 1)
+  constexpr int kRowsPer = kChunk / NSL;
+  static_assert(kRowsPer * kLinesRow <= 64 && kTileSetBytes / 128 / NSL <= 64, "one load per region");
+  uint32_t sink[5] = {0u, 0u, 0u, 0u, 0u};
+  auto prefetch = [&](int c) {
+    const bool in = c < sq.nc;
+    const int64_t ch = io.chunk_head(in ? c : 0);
+    const uint32_t rows = in ? static_cast<uint32_t>(io.rows(c)) : 0u;
+    const uint32_t kq_bytes = rows ? (rows - 1) * io.row_k + K * io.ES : 0u;
+    const uint32_t kq_off = lane < kRowsPer * kLinesRow
+                                ? static_cast<uint32_t>(sq.slice * kRowsPer + lane / kLinesRow) * io.row_k +
+                                      128u * (lane % kLinesRow)
+                                : 0xFFFFFFF0u;
+    const int64_t row0 = (io.token0(in ? c : 0) * H + sq.h) * K;
+    sink[0] = Buf(k + row0, kq_bytes).load4(kq_off);
+    sink[1] = Buf(q + row0, kq_bytes).load4(kq_off);
+    const uint32_t set_bytes = in ? static_cast<uint32_t>(kTileSetBytes) : 0u;
+    const uint32_t set_off =
+        lane < kTileSetBytes / 128 / NSL ? 128u * static_cast<uint32_t>(sq.slice + NSL * lane) : 0xFFFFFFF0u;
+    sink[2] = Buf(ws.af + ch * kTileSetBytes, set_bytes).load4(set_off);
+    sink[3] = Buf(ws.pf + ch * kTileSetBytes, set_bytes).load4(set_off);
+    const Buf vd(v + (io.token0(in ? c : 0) * H + sq.h) * V + sq.slice * 16,
+                 rows ? (rows - 1) * io.row_v + 16 * io.ES : 0u);
+    sink[4] = vd.load4(static_cast<uint32_t>(lane) * io.row_v);
+  };
+  auto consume = [&] { asm volatile("" ::"v"(sink[0]), "v"(sink[1]), "v"(sink[2]), "v"(sink[3]), "v"(sink[4])); };
+  constexpr int kPrefetchOps = 5;
   const int nc = sq.nc;
   if (nc > 0) stage_chain(0, 0);
   wait_vmem();
@@ -745,9 +781,14 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin>& sm, const 
   for (int c = 0; c < nc; ++c) {
     if (c + 1 < nc) stage_chain(c + 1, (c + 1) & 1);
     if constexpr (S::kOutLds) stage_out(c, c & 1);
-    wait_vmem();
+    consume();  // the previous interval's prefetches (older than these copies)
+    prefetch(c + 2);
+    // the copies have landed; the prefetches, issued last, may still be in
+    // flight (the count drains in issue order)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kPrefetchOps);
     __syncthreads();
   }
+  consume();
 }
 
 // Output wave OW (row tiles 2 OW and 2 OW + 1): in the interval that ends with

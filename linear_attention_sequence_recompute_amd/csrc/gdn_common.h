@@ -306,6 +306,10 @@ struct Buf {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(static_cast<uintptr_t>(l)), 16,
                                              voff, soff, 0, 0);
   }
+  // 4 bytes per lane (0 for lanes with voff >= the descriptor size).
+  __device__ __forceinline__ uint32_t load4(uint32_t voff) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+  }
   __device__ __forceinline__ void store(float x, uint32_t voff, uint32_t soff) const {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, soff, 0);
   }
