@@ -304,3 +304,62 @@ def test_decode_out_of_range_slot_is_padding():
     assert torch.all(o[3] == 0) and torch.all(o[5] == 0)
     keep = [s for s in range(16) if s not in set(di.slots[[0, 1, 2, 4, 6, 7]].tolist())]
     assert torch.equal(pool[keep], pool0[keep])
+
+
+def test_graph_capture_replays_match_eager():
+    """A chunked call and a decode step captured in one HIP graph: three replays,
+    with eager work between them, give the eager results bit for bit (the chunked
+    call is idempotent; the decode step advances the pool like eager steps)."""
+    T, H, K, V = 300, 4, 128, 128
+    ci = chunk_inputs([T], H, K, V, dtype="bf16", seed=42, h0_std=0.1)
+    dt = torch.bfloat16
+    q, k, v = (dev(x, dt).view(1, T, H, -1) for x in (ci.q, ci.k, ci.v))
+    g, b = dev(ci.a).view(1, T, H), dev(ci.beta).view(1, T, H)
+    h0 = dev(ci.h0)
+    o = torch.empty(1, T, H, V, dtype=torch.float32, device="cuda")
+    ht = torch.empty(1, H, V, K, dtype=torch.float32, device="cuda")
+    ws = torch.empty(api.workspace_bytes(1, T, H, K, V), dtype=torch.uint8, device="cuda")
+    di = decode_inputs(N=16, H=H, K=K, V=V, pool_slots=24, dtype="bf16", seed=43, n_padding=3)
+    dq, dk, dv = (dev(x, dt) for x in (di.q, di.k, di.v))
+    dg, dbeta = dev(di.a), dev(di.beta)
+    slots = dev(di.slots, torch.int32)
+    pool0 = dev(di.pool)
+    do = torch.empty(16, H, V, dtype=torch.float32, device="cuda")
+
+    def calls(pool):
+        api.chunk_fwd(q, k, v, g, b, scale=0.2, h0=h0, ht=ht, out=o, out_dtype=torch.float32, workspace=ws)
+        api.recurrent_step(dq, dk, dv, dg, dbeta, pool, slots, scale=0.3, out=do, out_dtype=torch.float32)
+
+    # eager: one chunked call; three decode steps in sequence
+    pool_e = pool0.clone()
+    calls(pool_e)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = o.clone(), ht.clone()
+    do_ref, pool_ref = [do.clone()], [pool_e.clone()]
+    for _ in range(2):
+        calls(pool_e)
+        torch.cuda.synchronize()
+        do_ref.append(do.clone())
+        pool_ref.append(pool_e.clone())
+
+    pool_g = pool0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture, on the capture's stream kind
+        calls(pool0.clone())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls(pool_g)
+    for rep in range(3):
+        o.fill_(float("nan"))
+        ht.fill_(float("nan"))
+        ws.fill_(0xFF)
+        do.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(ht, ht_ref), f"replay {rep}: chunked call differs"
+        assert torch.equal(do, do_ref[rep]) and torch.equal(pool_g, pool_ref[rep]), f"replay {rep}: decode differs"
+    _print("[graph] 3 replays equal to eager")
