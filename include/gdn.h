@@ -61,8 +61,9 @@ typedef enum gdn_dtype {
  * Bytes of device workspace gdn_chunk_fwd needs for a call with these sizes
  * (an upper bound valid for every split of total_tokens into n_seqs
  * sequences). Returns 0 for invalid sizes. The workspace holds the chunk
- * intermediates of recompute_w_u (the WY-transformed keys w and values u, the
- * masked intra-chunk scores, the chunk-local gate sums) and the chunk schedule.
+ * intermediates of recompute_w_u in the form the scan consumes (A' = A diag(beta)
+ * of the WY matrix A, from which u - w h = A'(V - diag(e^g) K h) follows), the
+ * masked intra-chunk scores, the chunk-local gate sums, and the chunk schedule.
  */
 size_t gdn_chunk_fwd_workspace_bytes(int n_seqs, int64_t total_tokens, int H, int K, int V,
                                      gdn_dtype in_dtype);
@@ -114,7 +115,7 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
  * results, and in addition it records three caller-created HIP events
  * (hipEvent_t, passed as void*) on `stream`: events[0] before the first kernel,
  * events[1] after the prep kernel (recompute_w_u: gate sums, K K^T, triangular
- * solve, u, w and the masked intra-chunk scores), events[2] after the scan
+ * solve, A' and the masked intra-chunk scores), events[2] after the scan
  * kernel (chunk_fwd_h fused with chunk_fwd_o). hipEventElapsedTime of
  * consecutive events then gives each kernel's duration on that stream.
  * `events` must point to three valid events; GDN_EINVAL otherwise.
