@@ -139,6 +139,14 @@ def test_fp32_mode_mixed_head_sizes(K, V):
     check_chunk(ci, K ** -0.5, label=f"f32 K={K} V={V}")
 
 
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (128, 64), (64, 128)])
+def test_many_pairs_all_head_sizes(K, V):
+    """80 (sequence, head) pairs: more scan workgroups than compute units (several
+    rounds of workgroups), every head size, nonzero initial states."""
+    ci = chunk_inputs([130] * 5, 16, K, V, dtype="bf16", seed=50 + K + V, h0_std=0.1)
+    check_chunk(ci, K ** -0.5, label=f"80 pairs K={K} V={V}")
+
+
 def test_odd_batch_and_heads():
     """3 sequences x 5 heads = 15 (sequence, head) pairs: the launch pads the pairs
     to a multiple of 8 (one per XCD) and the padding workgroups must do nothing."""
