@@ -24,6 +24,21 @@ int64_t max_chunks(int n_seqs, int64_t total_tokens) { return total_tokens / kCh
 
 gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_EHIP; }
 
+// Compute units of the current device, asked once per device.
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static int cus[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev >= kMaxDevices) dev = kMaxDevices - 1;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -132,6 +147,7 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
   a.pool_slots = pool_slots;
   a.slots = state_slots;
   a.ws = gdn::carve_workspace(layout, workspace);
+  a.n_cus = device_cus();
   a.stream = static_cast<hipStream_t>(stream);
   for (int i = 0; i < 3; ++i) a.events[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
   return hip_status(gdn::launch_chunk_fwd(a));

@@ -467,17 +467,21 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   }
 }
 
-// LDS of one scan workgroup, each buffer a separate __shared__ array so that
-// the compiler can tell the direct-to-LDS copies from the exchange buffers
-// (and does not make LDS reads wait for unrelated copies).
-template <int K, typename Tin>
+// LDS of one scan workgroup as one chain sees it, each buffer a separate
+// __shared__ array so that the compiler can tell the direct-to-LDS copies from
+// the exchange buffers (and does not make LDS reads wait for unrelated copies).
+// K, A' and the gate vectors are shared by the NCH chains of a workgroup; the V
+// slice, the published state and v_new are the chain's own.
+template <int K, typename Tin, int NCH>
 struct ScanSmem {
   static constexpr int NKB = K / 32;
   // q, P and the gate vectors of the output waves are staged in LDS for bf16
-  // inputs; for fp32 inputs they would not fit and are loaded into registers.
-  static constexpr bool kOutLds = sizeof(Tin) == 2;
+  // inputs and one chain per workgroup; otherwise they would not fit and the
+  // output waves load them into registers.
+  static constexpr bool kOutLds = sizeof(Tin) == 2 && NCH == 1;
   static constexpr int kQBytes = kOutLds ? KTile<K, Tin>::kBytes : 16;
   static constexpr int kPTiles = kOutLds ? 6 : 1;
+  static constexpr int kOutBufs = kOutLds ? 2 : 1;
   char (*k)[KTile<K, Tin>::kBytes];  // [2] K tiles (swizzled), chain
   char (*a)[6][2 * kPlane];          // [2] A' tiles, two planes each, chain
   Tin (*v)[kChunk * 16];             // [2] V slice [token][16], chain
@@ -493,8 +497,8 @@ struct ScanSeq {
   int seq, h, slice, start, len, chunk0, nc;
 };
 
-template <int K, int V, typename Tin>
-__device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin>& sm, const ScanSeq& sq, const float* __restrict__ h0,
+template <int K, int V, typename Tin, int NCH>
+__device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, const ScanSeq& sq, const float* __restrict__ h0,
                                            float* __restrict__ ht, float* __restrict__ pool, int64_t pool_slots,
                                            const int32_t* __restrict__ slots, int H, const ChunkWs& ws) {
   using P = Prec<Tin>;
@@ -692,14 +696,16 @@ struct ScanIo {
 };
 
 // The producer wave: every direct-to-LDS copy. In the interval that ends with
-// chain step c it stages the chain's inputs of chunk c + 1 (K, A', the V slice,
-// the gate vectors) and, for bf16 inputs, the output waves' inputs of chunk c
-// (q, P, the gate vectors); all copies have landed before the barrier.
-template <int K, int V, typename Tin>
-__device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin>& sm, const ScanSeq& sq, const Tin* __restrict__ q,
-                                              const Tin* __restrict__ k, const Tin* __restrict__ v, int H,
-                                              const ChunkWs& ws) {
-  using S = ScanSmem<K, Tin>;
+// chain step c it stages the chains' inputs of chunk c + 1 (K, A' and the gate
+// vectors once, each chain's V slice) and, where they are staged in LDS, the
+// output waves' inputs of chunk c (q, P, the gate vectors); all copies have
+// landed before the barrier.
+template <int K, int V, typename Tin, int NCH>
+__device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin, NCH> (&sms)[NCH], const ScanSeq& sq,
+                                              const Tin* __restrict__ q, const Tin* __restrict__ k,
+                                              const Tin* __restrict__ v, int H, const ChunkWs& ws) {
+  using S = ScanSmem<K, Tin, NCH>;
+  const S& sm = sms[0];
   const int lane = threadIdx.x & 63;
   const ScanIo<K, V, Tin> io(sq, H);
   // Rows past the chunk's end are zeros: they meet zero columns of A' and
@@ -717,8 +723,11 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin>& sm, const 
         for (int pl = 0; pl < 2; ++pl)
           ad.to_lds16(sm.a[b][a_tile(rt, ks)] + pl * kPlane, 16 * lane, (a_tile(rt, ks) * 2 + pl) * kPlane);
       }
-    const Buf vd(v + (io.token0(c) * H + sq.h) * V + sq.slice * 16, (io.rows(c) - 1) * io.row_v + 16 * io.ES);
-    dma_v_slice<Tin>(vd, io.row_v, sm.v[b]);
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const Buf vd(v + (io.token0(c) * H + sq.h) * V + (sq.slice + j) * 16, (io.rows(c) - 1) * io.row_v + 16 * io.ES);
+      dma_v_slice<Tin>(vd, io.row_v, sms[j].v[b]);
+    }
     const Buf gd(ws.gx + ch * 192, 192 * 4);
     if (lane < 3 * kChunk / 4) gd.to_lds16(sm.gx[b], 16 * lane, 0);
   };
@@ -739,17 +748,20 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin>& sm, const 
     if (lane < 3 * kChunk / 4) gd.to_lds16(sm.go[b], 16 * lane, 0);
   };
   // L2 prefetch of chunk c: one 4-byte read per 128-byte line of its K and q
-  // rows, A', P and this workgroup's V slice, into registers nobody uses (an
+  // rows, A', P and this workgroup's V slices, into registers nobody uses (an
   // empty asm consumes them an interval later, when they have long landed, so
-  // the compiler keeps the loads and waits for them only there). The
+  // the compiler keeps the loads and waits for them only there). The NG
   // workgroups of a (sequence, head) share an XCD and its L2, so each takes
-  // 1 / NSL of the shared lines (rows or lines s, s + NSL, ...); the V lines
-  // are its own. Five loads whatever c is (lanes with nothing to read are out
-  // of range).
-  constexpr int NSL = V / 16;
+  // 1 / NG of the shared lines (rows or lines s, s + NG, ...); the V lines
+  // are its own (its NCH slices are adjacent, 16 NCH elements of a row, within
+  // one line). Five loads whatever c is (lanes with nothing to read are out of
+  // range).
+  constexpr int NG = V / 16 / NCH;
   constexpr int kLinesRow = KTile<K, Tin>::kRowBytes / 128;  // lines per K or q row (>= 1)
-  constexpr int kRowsPer = kChunk / NSL;
-  static_assert(kRowsPer * kLinesRow <= 64 && kTileSetBytes / 128 / NSL <= 64, "one load per region");
+  constexpr int kRowsPer = kChunk / NG;
+  static_assert(kRowsPer * kLinesRow <= 64 && kTileSetBytes / 128 / NG <= 64, "one load per region");
+  static_assert(16 * NCH * sizeof(Tin) <= 128, "a workgroup's V slices share one line per row");
+  const int grp = sq.slice / NCH;
   uint32_t sink[5] = {0u, 0u, 0u, 0u, 0u};
   auto prefetch = [&](int c) {
     const bool in = c < sq.nc;
@@ -757,7 +769,7 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin>& sm, const 
     const uint32_t rows = in ? static_cast<uint32_t>(io.rows(c)) : 0u;
     const uint32_t kq_bytes = rows ? (rows - 1) * io.row_k + K * io.ES : 0u;
     const uint32_t kq_off = lane < kRowsPer * kLinesRow
-                                ? static_cast<uint32_t>(sq.slice * kRowsPer + lane / kLinesRow) * io.row_k +
+                                ? static_cast<uint32_t>(grp * kRowsPer + lane / kLinesRow) * io.row_k +
                                       128u * (lane % kLinesRow)
                                 : 0xFFFFFFF0u;
     const int64_t row0 = (io.token0(in ? c : 0) * H + sq.h) * K;
@@ -765,7 +777,7 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin>& sm, const 
     sink[1] = Buf(q + row0, kq_bytes).load4(kq_off);
     const uint32_t set_bytes = in ? static_cast<uint32_t>(kTileSetBytes) : 0u;
     const uint32_t set_off =
-        lane < kTileSetBytes / 128 / NSL ? 128u * static_cast<uint32_t>(sq.slice + NSL * lane) : 0xFFFFFFF0u;
+        lane < kTileSetBytes / 128 / NG ? 128u * static_cast<uint32_t>(grp + NG * lane) : 0xFFFFFFF0u;
     sink[2] = Buf(ws.af + ch * kTileSetBytes, set_bytes).load4(set_off);
     sink[3] = Buf(ws.pf + ch * kTileSetBytes, set_bytes).load4(set_off);
     const Buf vd(v + (io.token0(in ? c : 0) * H + sq.h) * V + sq.slice * 16,
@@ -793,11 +805,14 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin>& sm, const 
 
 // Output wave OW (row tiles 2 OW and 2 OW + 1): in the interval that ends with
 // chain step c it emits the rows of chunk c - 1, o = s e^g (q h) + P v_new,
-// from the published state and v_new.
-template <int OW, int K, int V, typename Tin, typename Tout>
-__device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const ScanSeq& sq, const Tin* __restrict__ q,
-                                            Tout* __restrict__ o, int H, float scale, const ChunkWs& ws) {
-  using S = ScanSmem<K, Tin>;
+// from the published state and v_new, for each of the workgroup's NCH slices
+// (the q, P and e^g operands serve all of them).
+template <int OW, int K, int V, typename Tin, typename Tout, int NCH>
+__device__ __forceinline__ void scan_output(const ScanSmem<K, Tin, NCH> (&sms)[NCH], const ScanSeq& sq,
+                                            const Tin* __restrict__ q, Tout* __restrict__ o, int H, float scale,
+                                            const ChunkWs& ws) {
+  using S = ScanSmem<K, Tin, NCH>;
+  const S& sm0 = sms[0];
   using P = Prec<Tin>;
   using In = typename P::In;
   using Cmp = typename P::Cmp;
@@ -811,25 +826,30 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const Sc
   // o rows of chunk c from its q fragments, P fragments and e^g
   auto emit = [&](int c, const In (&qf)[2][NKB], const Cmp (&pf)[2][NTB], const f32x4 (&eg)[2]) {
     const int b = c & 1;
-    const Buf od(o + (io.token0(c) * H + sq.h) * V + sq.slice * 16, (io.rows(c) - 1) * row_o + 16 * sizeof(Tout));
-    Cmp hb[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) hb[kb] = P::ld_cmp(sm.h[b][kb], lane);
-    Cmp vb[NTB];
+    for (int j = 0; j < NCH; ++j) {
+      const S& sm = sms[j];
+      const Buf od(o + (io.token0(c) * H + sq.h) * V + (sq.slice + j) * 16,
+                   (io.rows(c) - 1) * row_o + 16 * sizeof(Tout));
+      Cmp hb[NKB];
 #pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) vb[tb] = P::cmp_tiles(sm.vn[b][2 * tb][lane], sm.vn[b][2 * tb + 1][lane]);
+      for (int kb = 0; kb < NKB; ++kb) hb[kb] = P::ld_cmp(sm.h[b][kb], lane);
+      Cmp vb[NTB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rt = 2 * OW + i;
-      f32x4 y = mma(qf[i][0], hb[0], zero4());
+      for (int tb = 0; tb < NTB; ++tb) vb[tb] = P::cmp_tiles(sm.vn[b][2 * tb][lane], sm.vn[b][2 * tb + 1][lane]);
 #pragma unroll
-      for (int kb = 1; kb < NKB; ++kb) y = mma(qf[i][kb], hb[kb], y);
-      f32x4 acc = (scale * eg[i]) * y;
+      for (int i = 0; i < 2; ++i) {
+        const int rt = 2 * OW + i;
+        f32x4 y = mma(qf[i][0], hb[0], zero4());
 #pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) acc = mma(pf[i][tb], vb[tb], acc);
+        for (int kb = 1; kb < NKB; ++kb) y = mma(qf[i][kb], hb[kb], y);
+        f32x4 acc = (scale * eg[i]) * y;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        od.store(static_cast<Tout>(acc[r]), (4 * lg + r) * row_o + lc * sizeof(Tout), 16 * rt * row_o);
+        for (int tb = 0; tb < NTB; ++tb) acc = mma(pf[i][tb], vb[tb], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          od.store(static_cast<Tout>(acc[r]), (4 * lg + r) * row_o + lc * sizeof(Tout), 16 * rt * row_o);
+      }
     }
   };
 
@@ -846,10 +866,10 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const Sc
       for (int i = 0; i < 2; ++i) {
         const int rt = 2 * OW + i;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) qf[i][kb] = KF::row(sm.qt[b], 16 * rt + lc, kb, lg);
+        for (int kb = 0; kb < NKB; ++kb) qf[i][kb] = KF::row(sm0.qt[b], 16 * rt + lc, kb, lg);
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) pf[i][tb] = P::ld_cmp(sm.pt[b][a_tile(rt, tb)], lane);
-        eg[i] = *reinterpret_cast<const f32x4*>(&sm.go[b][64 + 16 * rt + 4 * lg]);
+        for (int tb = 0; tb < NTB; ++tb) pf[i][tb] = P::ld_cmp(sm0.pt[b][a_tile(rt, tb)], lane);
+        eg[i] = *reinterpret_cast<const f32x4*>(&sm0.go[b][64 + 16 * rt + 4 * lg]);
       }
       emit(c, qf, pf, eg);
     };
@@ -917,32 +937,47 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin>& sm, const Sc
   }
 }
 
-template <int K, int V, typename Tin, typename Tout>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_kernel(
+// Threads of a scan workgroup: one chain wave per slice, two output waves and
+// the producer wave.
+template <int NCH>
+constexpr int scan_threads() {
+  return 64 * (NCH + 3);
+}
+
+// NCH = 1: waves 0 chain, 1 producer, 2 and 3 output. NCH = 2: waves 0 and 1
+// chains, 2 and 3 output, 4 producer. The waves of a workgroup are spread over
+// the four SIMDs of its CU (waves 0..3 on four different ones, wave 4 beside
+// wave 0), so each chain, which is bound by its own instruction issue, has a
+// SIMD to itself or shares it with the producer, the lightest role.
+template <int K, int V, typename Tin, typename Tout, int NCH>
+__global__ __launch_bounds__(scan_threads<NCH>()) __attribute__((amdgpu_waves_per_eu(NCH, NCH))) void scan_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o, int H,
     float scale, int n_seqs, int T_eq, int ncs_eq, int total_tokens, int n_chunks, const int32_t* __restrict__ cu,
     const float* __restrict__ h0, float* __restrict__ ht, float* __restrict__ pool, int64_t pool_slots,
     const int32_t* __restrict__ slots, ChunkWs ws) {
-  using S = ScanSmem<K, Tin>;
-  constexpr int NSL = V / 16;
+  using S = ScanSmem<K, Tin, NCH>;
+  constexpr int NG = V / 16 / NCH;  // workgroups per (sequence, head)
   constexpr int NKB = K / 32;
+  static_assert(NCH == 1 || NCH == 2, "one or two chains per workgroup");
   __shared__ __attribute__((aligned(1024))) char lds_k[2][KTile<K, Tin>::kBytes];
   __shared__ __attribute__((aligned(1024))) char lds_a[2][6][2 * kPlane];
-  __shared__ __attribute__((aligned(1024))) Tin lds_v[2][kChunk * 16];
+  __shared__ __attribute__((aligned(1024))) Tin lds_v[NCH][2][kChunk * 16];
   __shared__ __attribute__((aligned(16))) float lds_gx[2][3 * kChunk];
-  __shared__ __attribute__((aligned(16))) char lds_h[2][NKB][2 * kPlane];
-  __shared__ __attribute__((aligned(16))) f32x4 lds_vn[2][4][64];
-  __shared__ __attribute__((aligned(1024))) char lds_qt[2][S::kQBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_pt[2][S::kPTiles][2 * kPlane];
-  __shared__ __attribute__((aligned(16))) float lds_go[2][3 * kChunk];
-  const S sm{lds_k, lds_a, lds_v, lds_gx, lds_h, lds_vn, lds_qt, lds_pt, lds_go};
+  __shared__ __attribute__((aligned(16))) char lds_h[NCH][2][NKB][2 * kPlane];
+  __shared__ __attribute__((aligned(16))) f32x4 lds_vn[NCH][2][4][64];
+  __shared__ __attribute__((aligned(1024))) char lds_qt[S::kOutBufs][S::kQBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_pt[S::kOutBufs][S::kPTiles][2 * kPlane];
+  __shared__ __attribute__((aligned(16))) float lds_go[S::kOutBufs][3 * kChunk];
+  S sms[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) sms[j] = S{lds_k, lds_a, lds_v[j], lds_gx, lds_h[j], lds_vn[j], lds_qt, lds_pt, lds_go};
 
   // Workgroups of one (sequence, head) share an XCD (blockIdx % 8) and its L2.
   const int bid = blockIdx.x;
   const int xcd = bid & 7, rest = bid >> 3;
   ScanSeq sq;
-  sq.slice = rest % NSL;
-  const int pair = (rest / NSL) * 8 + xcd;
+  sq.slice = (rest % NG) * NCH;  // the workgroup's first slice
+  const int pair = (rest / NG) * 8 + xcd;
   if (pair >= n_seqs * H) return;
   sq.seq = pair / H;
   sq.h = pair % H;
@@ -961,16 +996,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   sq.nc = (sq.len + kChunk - 1) / kChunk;
 
-  // Wave roles: 0 the chain, 1 the producer, 2 and 3 the output waves.
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wv == 0)
-    scan_chain<K, V, Tin>(sm, sq, h0, ht, pool, pool_slots, slots, H, ws);
-  else if (wv == 1)
-    scan_producer<K, V, Tin>(sm, sq, q, k, v, H, ws);
-  else if (wv == 2)
-    scan_output<0, K, V, Tin, Tout>(sm, sq, q, o, H, scale, ws);
-  else
-    scan_output<1, K, V, Tin, Tout>(sm, sq, q, o, H, scale, ws);
+  constexpr int kProducer = NCH == 1 ? 1 : 4;
+  if (wv < NCH) {
+    ScanSeq cs = sq;
+    cs.slice = sq.slice + wv;
+    if (wv == 0)
+      scan_chain<K, V, Tin, NCH>(sms[0], cs, h0, ht, pool, pool_slots, slots, H, ws);
+    else
+      scan_chain<K, V, Tin, NCH>(sms[NCH - 1], cs, h0, ht, pool, pool_slots, slots, H, ws);
+  } else if (wv == kProducer) {
+    scan_producer<K, V, Tin, NCH>(sms, sq, q, k, v, H, ws);
+  } else if (wv == 2) {
+    scan_output<0, K, V, Tin, Tout, NCH>(sms, sq, q, o, H, scale, ws);
+  } else {
+    scan_output<1, K, V, Tin, Tout, NCH>(sms, sq, q, o, H, scale, ws);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1029,12 +1070,23 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
   }
   if (a.events[1]) (void)hipEventRecord(a.events[1], a.stream);
   const int64_t pairs = static_cast<int64_t>(a.n_seqs) * a.H;
-  const int64_t blocks = 8 * NSL * ((pairs + 7) / 8);
-  hipLaunchKernelGGL((scan_kernel<K, V, Tin, Tout>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
-                     static_cast<const Tin*>(a.v), static_cast<Tout*>(a.o), a.H, a.scale, a.n_seqs, a.T_eq, ncs_eq,
-                     static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0, a.ht, a.pool,
-                     a.pool_slots, a.slots, a.ws);
+  // Two chains per workgroup (sharing K, A' and the gates, on two SIMDs of a
+  // CU) once one-chain workgroups would outnumber the compute units; bf16
+  // inputs only (float32 operands would not leave room in LDS for the rest).
+  auto launch = [&](auto kern, int nch) {
+    const int64_t blocks = 8 * (NSL / nch) * ((pairs + 7) / 8);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(64 * (nch + 3)), 0, a.stream,
+                       static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
+                       static_cast<Tout*>(a.o), a.H, a.scale, a.n_seqs, a.T_eq, ncs_eq,
+                       static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0, a.ht,
+                       a.pool, a.pool_slots, a.slots, a.ws);
+  };
+  bool two = false;
+  if constexpr (std::is_same<Tin, __bf16>::value) {
+    two = pairs * NSL > a.n_cus;
+    if (two) launch(scan_kernel<K, V, Tin, Tout, 2>, 2);
+  }
+  if (!two) launch(scan_kernel<K, V, Tin, Tout, 1>, 1);
   const hipError_t err = hipGetLastError();
   if (a.events[2]) (void)hipEventRecord(a.events[2], a.stream);
   return err;

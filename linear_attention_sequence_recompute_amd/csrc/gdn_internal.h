@@ -58,6 +58,7 @@ struct ChunkArgs {
   int64_t pool_slots;
   const int32_t* slots;
   ChunkWs ws;
+  int n_cus;  // compute units of the current device (sizes the scan's workgroups)
   hipStream_t stream;
   hipEvent_t events[3];  // optional: recorded before prep, after prep, after scan
 };

@@ -154,6 +154,23 @@ def test_odd_batch_and_heads():
     check_chunk(ci, 128 ** -0.5, label="B=3 H=5")
 
 
+def test_two_chain_workgroups_odd_pairs():
+    """7 sequences x 5 heads = 35 pairs: 280 single-slice workgroups would exceed
+    the 256 compute units, so the scan runs two slices per workgroup; the pairs
+    are padded to 40 and the padding workgroups must do nothing."""
+    ci = chunk_inputs([130] * 7, 5, 128, 128, dtype="bf16", seed=42, h0_std=0.1)
+    check_chunk(ci, 128 ** -0.5, label="B=7 H=5 (two slices per workgroup)")
+
+
+def test_two_chain_varlen_edges():
+    """Empty, single-token, chunk-multiple and ragged sequences with 40 heads (two
+    slices per scan workgroup), long-memory gates, dense h0/ht; every sequence
+    and head checked."""
+    lengths = [0, 1, 64, 65, 0, 130, 127, 3]
+    ci = chunk_inputs(lengths, 40, 128, 128, dtype="bf16", seed=43, gate_shift=-4.0, h0_std=0.1)
+    check_chunk(ci, 0.2, label="varlen edges, 40 heads")
+
+
 def test_config_h16_t4096_full():
     """B=1, H=16, T=4096, K=V=128, bf16: every output and the final state."""
     ci = chunk_inputs([4096], 16, 128, 128, dtype="bf16", seed=2)
