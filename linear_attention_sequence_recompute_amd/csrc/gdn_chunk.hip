@@ -475,13 +475,16 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
 template <int K, typename Tin, int NCH>
 struct ScanSmem {
   static constexpr int NKB = K / 32;
-  // q, P and the gate vectors of the output waves are staged in LDS for bf16
-  // inputs and one chain per workgroup; otherwise they would not fit and the
-  // output waves load them into registers.
-  static constexpr bool kOutLds = sizeof(Tin) == 2 && NCH == 1;
-  static constexpr int kQBytes = kOutLds ? KTile<K, Tin>::kBytes : 16;
-  static constexpr int kPTiles = kOutLds ? 6 : 1;
-  static constexpr int kOutBufs = kOutLds ? 2 : 1;
+  // The output waves' q tile with the gate vectors (kQLds) and P tiles
+  // (kPLds) are staged in LDS by the producer where they fit: both for bf16
+  // inputs and one chain per workgroup, q alone for two chains; otherwise the
+  // output waves load them into registers a chunk ahead.
+  static constexpr bool kQLds = sizeof(Tin) == 2;
+  static constexpr bool kPLds = sizeof(Tin) == 2 && NCH == 1;
+  static constexpr int kQBytes = kQLds ? KTile<K, Tin>::kBytes : 16;
+  static constexpr int kQBufs = kQLds ? 2 : 1;
+  static constexpr int kPTiles = kPLds ? 6 : 1;
+  static constexpr int kPBufs = kPLds ? 2 : 1;
   char (*k)[KTile<K, Tin>::kBytes];  // [2] K tiles (swizzled), chain
   char (*a)[6][2 * kPlane];          // [2] A' tiles, two planes each, chain
   Tin (*v)[kChunk * 16];             // [2] V slice [token][16], chain
@@ -732,20 +735,24 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin, NCH> (&sms)
     if (lane < 3 * kChunk / 4) gd.to_lds16(sm.gx[b], 16 * lane, 0);
   };
   auto stage_out = [&](int c, int b) {
-    dma_k_tile<K, Tin>(io.qk(q, c), io.row_k, sm.qt[b]);
     const int64_t ch = io.chunk_head(c);
-    const Buf pd(ws.pf + ch * kTileSetBytes, kTileSetBytes);
+    if constexpr (S::kQLds) {
+      dma_k_tile<K, Tin>(io.qk(q, c), io.row_k, sm.qt[b]);
+      const Buf gd(ws.gx + ch * 192, 192 * 4);
+      if (lane < 3 * kChunk / 4) gd.to_lds16(sm.go[b], 16 * lane, 0);
+    }
+    if constexpr (S::kPLds) {
+      const Buf pd(ws.pf + ch * kTileSetBytes, kTileSetBytes);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        if (tb > 0 && rt < 2) continue;
+        for (int tb = 0; tb < 2; ++tb) {
+          if (tb > 0 && rt < 2) continue;
 #pragma unroll
-        for (int pl = 0; pl < 2; ++pl)
-          pd.to_lds16(sm.pt[b][a_tile(rt, tb)] + pl * kPlane, 16 * lane, (a_tile(rt, tb) * 2 + pl) * kPlane);
-      }
-    const Buf gd(ws.gx + ch * 192, 192 * 4);
-    if (lane < 3 * kChunk / 4) gd.to_lds16(sm.go[b], 16 * lane, 0);
+          for (int pl = 0; pl < 2; ++pl)
+            pd.to_lds16(sm.pt[b][a_tile(rt, tb)] + pl * kPlane, 16 * lane, (a_tile(rt, tb) * 2 + pl) * kPlane);
+        }
+    }
   };
   // L2 prefetch of chunk c: one 4-byte read per 128-byte line of its K and q
   // rows, A', P and this workgroup's V slices, into registers nobody uses (an
@@ -792,7 +799,7 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin, NCH> (&sms)
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
     if (c + 1 < nc) stage_chain(c + 1, (c + 1) & 1);
-    if constexpr (S::kOutLds) stage_out(c, c & 1);
+    if constexpr (S::kQLds || S::kPLds) stage_out(c, c & 1);
     consume();  // the previous interval's prefetches (older than these copies)
     prefetch(c + 2);
     // the copies have landed; the prefetches, issued last, may still be in
@@ -823,9 +830,67 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin, NCH> (&sms)[N
   const ScanIo<K, V, Tin> io(sq, H);
   const uint32_t row_o = static_cast<uint32_t>(H) * V * sizeof(Tout);
 
-  // o rows of chunk c from its q fragments, P fragments and e^g
-  auto emit = [&](int c, const In (&qf)[2][NKB], const Cmp (&pf)[2][NTB], const f32x4 (&eg)[2]) {
+  constexpr bool kQ = S::kQLds, kP = S::kPLds;
+  // operands not staged in LDS, loaded into registers one chunk ahead (the
+  // arrays of staged operands have one unused element)
+  struct Regs {
+    In q[kQ ? 1 : 2][kQ ? 1 : NKB];
+    f32x4 eg[kQ ? 1 : 2];
+    Cmp p[kP ? 1 : 2][kP ? 1 : NTB];
+  };
+  const uint32_t q_voff = static_cast<uint32_t>(lc) * io.row_k + 8 * lg * io.ES;
+  auto load = [&](Regs& rg, int c) {
+    const int64_t ch = io.chunk_head(c);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rt = 2 * OW + i;
+      if constexpr (!kQ) {
+        const Buf qd = io.qk(q, c);
+        const Buf gd(ws.gx + ch * 192, 192 * 4);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) rg.q[i][kb] = buf_frag(qd, q_voff, 16 * rt * io.row_k + 32 * kb * io.ES, q);
+        rg.eg[i] = __builtin_bit_cast(f32x4, gd.load16(4 * (64 + 16 * rt + 4 * lg), 0));
+      }
+      if constexpr (!kP) {
+        const Buf pd(ws.pf + ch * kTileSetBytes, kTileSetBytes);
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+          const uint32_t so = a_tile(rt, tb) * 2 * kPlane;
+          rg.p[i][tb] = cmp_planes(pd.load16(16 * lane, so), pd.load16(16 * lane, so + kPlane), Cmp{});
+        }
+      }
+    }
+  };
+
+  // o rows of chunk c, for each slice, from the q fragments, P fragments and
+  // e^g (from LDS buffer c & 1 or from rg) and the published state and v_new
+  auto emit = [&](int c, const Regs& rg) {
     const int b = c & 1;
+    In qf[2][NKB];
+    Cmp pf[2][NTB];
+    f32x4 eg[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rt = 2 * OW + i;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        if constexpr (kQ)
+          qf[i][kb] = KF::row(sm0.qt[b], 16 * rt + lc, kb, lg);
+        else
+          qf[i][kb] = rg.q[i][kb];
+      }
+      if constexpr (kQ)
+        eg[i] = *reinterpret_cast<const f32x4*>(&sm0.go[b][64 + 16 * rt + 4 * lg]);
+      else
+        eg[i] = rg.eg[i];
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        if constexpr (kP)
+          pf[i][tb] = P::ld_cmp(sm0.pt[b][a_tile(rt, tb)], lane);
+        else
+          pf[i][tb] = rg.p[i][tb];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const S& sm = sms[j];
@@ -855,86 +920,45 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin, NCH> (&sms)[N
 
   const int nc = sq.nc;
   __syncthreads();
-  if constexpr (S::kOutLds) {
-    // operands staged by the producer into buffer c & 1
-    auto emit_lds = [&](int c) {
-      const int b = c & 1;
-      In qf[2][NKB];
-      Cmp pf[2][NTB];
-      f32x4 eg[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int rt = 2 * OW + i;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) qf[i][kb] = KF::row(sm0.qt[b], 16 * rt + lc, kb, lg);
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) pf[i][tb] = P::ld_cmp(sm0.pt[b][a_tile(rt, tb)], lane);
-        eg[i] = *reinterpret_cast<const f32x4*>(&sm0.go[b][64 + 16 * rt + 4 * lg]);
-      }
-      emit(c, qf, pf, eg);
-    };
+  if constexpr (kQ && kP) {
+    const Regs none{};
     for (int c = 0; c < nc; ++c) {
-      if (c > 0) emit_lds(c - 1);
+      if (c > 0) emit(c - 1, none);
       __syncthreads();
     }
-    if (nc > 0) emit_lds(nc - 1);
-  } else {
-    // operands loaded into registers one chunk ahead (ping-pong)
-    struct Regs {
-      In q[2][NKB];
-      Cmp p[2][NTB];
-      f32x4 eg[2];
-    };
-    const uint32_t q_voff = static_cast<uint32_t>(lc) * io.row_k + 8 * lg * io.ES;
-    auto load = [&](Regs& rg, int c) {
-      const int64_t ch = io.chunk_head(c);
-      const Buf qd = io.qk(q, c);
-      const Buf pd(ws.pf + ch * kTileSetBytes, kTileSetBytes);
-      const Buf gd(ws.gx + ch * 192, 192 * 4);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int rt = 2 * OW + i;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) rg.q[i][kb] = buf_frag(qd, q_voff, 16 * rt * io.row_k + 32 * kb * io.ES, q);
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-          const uint32_t so = a_tile(rt, tb) * 2 * kPlane;
-          rg.p[i][tb] = cmp_planes(pd.load16(16 * lane, so), pd.load16(16 * lane, so + kPlane), Cmp{});
-        }
-        rg.eg[i] = __builtin_bit_cast(f32x4, gd.load16(4 * (64 + 16 * rt + 4 * lg), 0));
-      }
-    };
-    if (nc > 0) {
-      Regs ra, rb;
-      load(ra, 0);
+    if (nc > 0) emit(nc - 1, none);
+  } else if (nc > 0) {
+    // ping-pong register sets; the loads of chunk c go out at the start of
+    // the interval that emits chunk c - 1
+    Regs ra, rb;
+    load(ra, 0);
+    wait_vmem();
+    __syncthreads();
+    int c = 1;
+    for (; c + 1 < nc; c += 2) {  // c odd
+      load(rb, c);
+      __builtin_amdgcn_sched_barrier(0);  // loads go out before the output work
+      emit(c - 1, ra);
       wait_vmem();
       __syncthreads();
-      int c = 1;
-      for (; c + 1 < nc; c += 2) {  // c odd
-        load(rb, c);
-        __builtin_amdgcn_sched_barrier(0);  // loads go out before the output work
-        emit(c - 1, ra.q, ra.p, ra.eg);
-        wait_vmem();
-        __syncthreads();
-        load(ra, c + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        emit(c, rb.q, rb.p, rb.eg);
-        wait_vmem();
-        __syncthreads();
-      }
-      if (c < nc) {  // c == nc - 1: intervals nc - 1 and nc remain
-        load(rb, c);
-        __builtin_amdgcn_sched_barrier(0);
-        emit(c - 1, ra.q, ra.p, ra.eg);
-        wait_vmem();
-        __syncthreads();
-        emit(c, rb.q, rb.p, rb.eg);
-      } else {  // c == nc: the last interval remains
-        emit(c - 1, ra.q, ra.p, ra.eg);
-      }
+      load(ra, c + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      emit(c, rb);
+      wait_vmem();
+      __syncthreads();
     }
-    wait_vmem();
+    if (c < nc) {  // c == nc - 1: intervals nc - 1 and nc remain
+      load(rb, c);
+      __builtin_amdgcn_sched_barrier(0);
+      emit(c - 1, ra);
+      wait_vmem();
+      __syncthreads();
+      emit(c, rb);
+    } else {  // c == nc: the last interval remains
+      emit(c - 1, ra);
+    }
   }
+  wait_vmem();
 }
 
 // Threads of a scan workgroup: one chain wave per slice, two output waves and
@@ -965,9 +989,9 @@ __global__ __launch_bounds__(scan_threads<NCH>()) __attribute__((amdgpu_waves_pe
   __shared__ __attribute__((aligned(16))) float lds_gx[2][3 * kChunk];
   __shared__ __attribute__((aligned(16))) char lds_h[NCH][2][NKB][2 * kPlane];
   __shared__ __attribute__((aligned(16))) f32x4 lds_vn[NCH][2][4][64];
-  __shared__ __attribute__((aligned(1024))) char lds_qt[S::kOutBufs][S::kQBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_pt[S::kOutBufs][S::kPTiles][2 * kPlane];
-  __shared__ __attribute__((aligned(16))) float lds_go[S::kOutBufs][3 * kChunk];
+  __shared__ __attribute__((aligned(1024))) char lds_qt[S::kQBufs][S::kQBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_pt[S::kPBufs][S::kPTiles][2 * kPlane];
+  __shared__ __attribute__((aligned(16))) float lds_go[S::kQBufs][3 * kChunk];
   S sms[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) sms[j] = S{lds_k, lds_a, lds_v[j], lds_gx, lds_h[j], lds_vn[j], lds_qt, lds_pt, lds_go};
