@@ -87,19 +87,22 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
   if (static_cast<int64_t>(n_seqs) * H > INT_MAX / 8) return GDN_EINVAL;
 
   // Chunk count and sequence lengths.
-  int64_t n_chunks = 0;
+  int64_t n_chunks = 0, max_nc = 0;
   int T_eq = 0;
   if (cu_seqlens_host) {
     if (cu_seqlens_host[0] != 0 || cu_seqlens_host[n_seqs] != total_tokens) return GDN_EINVAL;
     for (int s = 0; s < n_seqs; ++s) {
       const int64_t len = static_cast<int64_t>(cu_seqlens_host[s + 1]) - cu_seqlens_host[s];
       if (len < 0) return GDN_EINVAL;
-      n_chunks += (len + kChunkTokens - 1) / kChunkTokens;
+      const int64_t nc = (len + kChunkTokens - 1) / kChunkTokens;
+      n_chunks += nc;
+      max_nc = nc > max_nc ? nc : max_nc;
     }
   } else {
     if (total_tokens % n_seqs != 0) return GDN_EINVAL;
     T_eq = static_cast<int>(total_tokens / n_seqs);
-    n_chunks = static_cast<int64_t>(n_seqs) * ((T_eq + kChunkTokens - 1) / kChunkTokens);
+    max_nc = (T_eq + kChunkTokens - 1) / kChunkTokens;
+    n_chunks = static_cast<int64_t>(n_seqs) * max_nc;
   }
   if (n_chunks > INT_MAX) return GDN_EINVAL;
 
@@ -140,6 +143,7 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
   a.out_f32 = out_dtype == GDN_F32;
   a.cu_seqlens = cu_seqlens;
   a.n_chunks = n_chunks;
+  a.max_nc = static_cast<int>(max_nc);
   a.T_eq = T_eq;
   a.h0 = h0;
   a.ht = ht;

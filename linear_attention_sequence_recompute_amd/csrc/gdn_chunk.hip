@@ -21,6 +21,7 @@
 // computed operand (A', K h residuals, h, v_new, P) enters as a bf16 hi + lo pair
 // with fp32 accumulation, which keeps about 16 significant bits. Float32 inputs
 // run the same code on the fp32 MFMA.
+#include <algorithm>
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -29,6 +30,7 @@
 namespace gdn {
 
 constexpr int kPlane = 1024;  // bytes of one fragment plane (64 lanes x 16 bytes)
+constexpr int kMaxSegments = 8;  // segments per sequence in the chunk-parallel form
 
 // ---------------------------------------------------------------------------
 // Chunk schedule of a packed call: chunk c of sequence s gets global index
@@ -500,38 +502,40 @@ struct ScanSeq {
   int seq, h, slice, start, len, chunk0, nc;
 };
 
-template <int K, int V, typename Tin, int NCH>
-__device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, const ScanSeq& sq, const float* __restrict__ h0,
-                                           float* __restrict__ ht, float* __restrict__ pool, int64_t pool_slots,
-                                           const int32_t* __restrict__ slots, int H, const ChunkWs& ws) {
+// The chain wave. Its state slice starts from rows [lc][key] of s_in (zeros if
+// null; if ident >= 0, the columns ident .. ident + 15 of the identity, which
+// makes the final state those columns of the chunks' linear map) and ends in
+// s_out (if not null). PUB: publish the state and v_new for output waves.
+template <int K, int V, typename Tin, int NCH, bool PUB = true>
+__device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, const ScanSeq& sq,
+                                           const float* __restrict__ s_in, float* __restrict__ s_out, int ident) {
   using P = Prec<Tin>;
   using In = typename P::In;
   using Cmp = typename P::Cmp;
   using KF = KFrag<K, Tin>;
   constexpr int NKB = K / 32;
   const int lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
-  const int vcol = sq.slice * 16 + lc;
 
-  const float* s_in = nullptr;
-  float* s_out = nullptr;
-  const int64_t page = static_cast<int64_t>(V) * K;
-  if (pool) {
-    const int s = slots[sq.seq];
-    if (s > 0 && s < pool_slots) {
-      s_in = pool + (static_cast<int64_t>(s) * H + sq.h) * page;
-      s_out = pool + (static_cast<int64_t>(s) * H + sq.h) * page;
-    }
-  } else {
-    if (h0) s_in = h0 + (static_cast<int64_t>(sq.seq) * H + sq.h) * page;
-    if (ht) s_out = ht + (static_cast<int64_t>(sq.seq) * H + sq.h) * page;
-  }
   // State slice: tile 2 kb + odd, lane (g, c) holds keys 32 kb + 8 g + 4 odd + r
-  // of value column vcol (S[vcol][key] in memory: 8 consecutive floats per block).
+  // of value column c (S[c][key] in memory: 8 consecutive floats per block).
   f32x4 hs[2 * NKB];
 #pragma unroll
   for (int t = 0; t < 2 * NKB; ++t) {
     const int key0 = 32 * (t >> 1) + 8 * lg + 4 * (t & 1);
-    hs[t] = s_in ? *reinterpret_cast<const f32x4*>(s_in + static_cast<int64_t>(vcol) * K + key0) : zero4();
+    hs[t] = s_in ? *reinterpret_cast<const f32x4*>(s_in + lc * K + key0) : zero4();
+    if (ident >= 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (key0 + r == ident + lc) hs[t][r] = 1.f;
+    }
+  }
+  if (ident >= 0) {
+    // a map column: the chunks' V enters as zeros (the producer leaves this
+    // chain's V buffers alone)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      for (int i = lane; i < kChunk * 16 * static_cast<int>(sizeof(Tin)) / 16; i += 64)
+        reinterpret_cast<u32x4*>(sm.v[b])[i] = u32x4{0u, 0u, 0u, 0u};
   }
   constexpr int NZ = Terms<In, Cmp>::n;   // MFMA terms of K h and K^T v
   constexpr int NA = Terms<Cmp, Cmp>::n;  // MFMA terms of A' R
@@ -627,8 +631,10 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, cons
       acc[4] = term(af[a_tile(2, 1)], rb1, acc[4], t);
       acc[5] = term(af[a_tile(3, 1)], rb1, acc[5], t);
     }
-    sm.vn[b][0][lane] = acc[0];
-    sm.vn[b][1][lane] = acc[1];
+    if constexpr (PUB) {
+      sm.vn[b][0][lane] = acc[0];
+      sm.vn[b][1][lane] = acc[1];
+    }
     const Cmp gb0 = P::cmp_tiles(acc[0] * egl[0], acc[1] * egl[1]);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -639,8 +645,10 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, cons
 #pragma unroll
       for (int i = 0; i < 2 * NKB; ++i) hd[i] = term(ktf[i][0], gb0, hd[i], t);
     const f32x4 vn2 = acc[2] + acc[4], vn3 = acc[3] + acc[5];
-    sm.vn[b][2][lane] = vn2;
-    sm.vn[b][3][lane] = vn3;
+    if constexpr (PUB) {
+      sm.vn[b][2][lane] = vn2;
+      sm.vn[b][3][lane] = vn3;
+    }
     const Cmp gb1 = P::cmp_tiles(vn2 * egl[2], vn3 * egl[3]);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -651,7 +659,8 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, cons
       for (int i = 0; i < 2 * NKB; ++i) hd[i] = term(ktf[i][1], gb1, hd[i], t);
     // the state this step started from, for the output waves (read after the barrier)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) P::st_cmp(sm.h[b][kb], lane, hb[kb]);
+    for (int kb = 0; kb < NKB; ++kb)
+      if constexpr (PUB) P::st_cmp(sm.h[b][kb], lane, hb[kb]);
     __syncthreads();
   };
   // The state alternates between two register sets (hs in, hx out), so no
@@ -673,7 +682,7 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, cons
 #pragma unroll
     for (int t = 0; t < 2 * NKB; ++t) {
       const int key0 = 32 * (t >> 1) + 8 * lg + 4 * (t & 1);
-      *reinterpret_cast<f32x4*>(s_out + static_cast<int64_t>(vcol) * K + key0) = hs[t];
+      *reinterpret_cast<f32x4*>(s_out + lc * K + key0) = hs[t];
     }
   }
 }
@@ -703,10 +712,13 @@ struct ScanIo {
 // vectors once, each chain's V slice) and, where they are staged in LDS, the
 // output waves' inputs of chunk c (q, P, the gate vectors); all copies have
 // landed before the barrier.
-template <int K, int V, typename Tin, int NCH>
+// SUM: for the segment summary kernel (no output waves; the V slices are
+// staged only if has_v, the workgroup's chains being map columns otherwise).
+template <int K, int V, typename Tin, int NCH, bool SUM = false>
 __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin, NCH> (&sms)[NCH], const ScanSeq& sq,
                                               const Tin* __restrict__ q, const Tin* __restrict__ k,
-                                              const Tin* __restrict__ v, int H, const ChunkWs& ws) {
+                                              const Tin* __restrict__ v, int H, const ChunkWs& ws,
+                                              bool has_v = true) {
   using S = ScanSmem<K, Tin, NCH>;
   const S& sm = sms[0];
   const int lane = threadIdx.x & 63;
@@ -726,10 +738,13 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin, NCH> (&sms)
         for (int pl = 0; pl < 2; ++pl)
           ad.to_lds16(sm.a[b][a_tile(rt, ks)] + pl * kPlane, 16 * lane, (a_tile(rt, ks) * 2 + pl) * kPlane);
       }
+    if (!SUM || has_v) {
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const Buf vd(v + (io.token0(c) * H + sq.h) * V + (sq.slice + j) * 16, (io.rows(c) - 1) * io.row_v + 16 * io.ES);
-      dma_v_slice<Tin>(vd, io.row_v, sms[j].v[b]);
+      for (int j = 0; j < NCH; ++j) {
+        const Buf vd(v + (io.token0(c) * H + sq.h) * V + (sq.slice + j) * 16,
+                     (io.rows(c) - 1) * io.row_v + 16 * io.ES);
+        dma_v_slice<Tin>(vd, io.row_v, sms[j].v[b]);
+      }
     }
     const Buf gd(ws.gx + ch * 192, 192 * 4);
     if (lane < 3 * kChunk / 4) gd.to_lds16(sm.gx[b], 16 * lane, 0);
@@ -763,7 +778,7 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin, NCH> (&sms)
   // are its own (its NCH slices are adjacent, 16 NCH elements of a row, within
   // one line). Five loads whatever c is (lanes with nothing to read are out of
   // range).
-  constexpr int NG = V / 16 / NCH;
+  constexpr int NG = SUM ? (V / 16 + K / 16) / NCH : V / 16 / NCH;
   constexpr int kLinesRow = KTile<K, Tin>::kRowBytes / 128;  // lines per K or q row (>= 1)
   constexpr int kRowsPer = kChunk / NG;
   static_assert(kRowsPer * kLinesRow <= 64 && kTileSetBytes / 128 / NG <= 64, "one load per region");
@@ -781,25 +796,25 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin, NCH> (&sms)
                                 : 0xFFFFFFF0u;
     const int64_t row0 = (io.token0(in ? c : 0) * H + sq.h) * K;
     sink[0] = Buf(k + row0, kq_bytes).load4(kq_off);
-    sink[1] = Buf(q + row0, kq_bytes).load4(kq_off);
+    if constexpr (!SUM) sink[1] = Buf(q + row0, kq_bytes).load4(kq_off);
     const uint32_t set_bytes = in ? static_cast<uint32_t>(kTileSetBytes) : 0u;
     const uint32_t set_off =
         lane < kTileSetBytes / 128 / NG ? 128u * static_cast<uint32_t>(grp + NG * lane) : 0xFFFFFFF0u;
     sink[2] = Buf(ws.af + ch * kTileSetBytes, set_bytes).load4(set_off);
-    sink[3] = Buf(ws.pf + ch * kTileSetBytes, set_bytes).load4(set_off);
+    if constexpr (!SUM) sink[3] = Buf(ws.pf + ch * kTileSetBytes, set_bytes).load4(set_off);
     const Buf vd(v + (io.token0(in ? c : 0) * H + sq.h) * V + sq.slice * 16,
                  rows ? (rows - 1) * io.row_v + 16 * io.ES : 0u);
-    sink[4] = vd.load4(static_cast<uint32_t>(lane) * io.row_v);
+    sink[4] = vd.load4((!SUM || has_v) ? static_cast<uint32_t>(lane) * io.row_v : 0xFFFFFFF0u);
   };
   auto consume = [&] { asm volatile("" ::"v"(sink[0]), "v"(sink[1]), "v"(sink[2]), "v"(sink[3]), "v"(sink[4])); };
-  constexpr int kPrefetchOps = 5;
+  constexpr int kPrefetchOps = SUM ? 3 : 5;
   const int nc = sq.nc;
   if (nc > 0) stage_chain(0, 0);
   wait_vmem();
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
     if (c + 1 < nc) stage_chain(c + 1, (c + 1) & 1);
-    if constexpr (S::kQLds || S::kPLds) stage_out(c, c & 1);
+    if constexpr (!SUM && (S::kQLds || S::kPLds)) stage_out(c, c & 1);
     consume();  // the previous interval's prefetches (older than these copies)
     prefetch(c + 2);
     // the copies have landed; the prefetches, issued last, may still be in
@@ -968,19 +983,69 @@ constexpr int scan_threads() {
   return 64 * (NCH + 3);
 }
 
+// The chunks of (sequence, head) pair `pair`: first token, length, global
+// index of its first chunk. A packed call whose offsets do not fit [0,
+// total_tokens] or the chunk count gets an empty sequence (no access can leave
+// the inputs or the workspace).
+__device__ __forceinline__ ScanSeq seq_of(int pair, int H, int T_eq, int ncs_eq, int total_tokens, int n_chunks,
+                                          const int32_t* __restrict__ cu, const ChunkWs& ws) {
+  ScanSeq sq;
+  sq.slice = 0;
+  sq.seq = pair / H;
+  sq.h = pair % H;
+  if (cu) {
+    sq.start = cu[sq.seq];
+    sq.len = cu[sq.seq + 1] - sq.start;
+    sq.chunk0 = ws.seq_chunk0[sq.seq];
+    const int nc_want = (sq.len + kChunk - 1) / kChunk;
+    if (sq.start < 0 || sq.len < 0 || sq.start > total_tokens - sq.len || sq.chunk0 < 0 ||
+        sq.chunk0 > n_chunks - nc_want)
+      sq.len = 0;
+  } else {
+    sq.start = sq.seq * T_eq;
+    sq.len = T_eq;
+    sq.chunk0 = sq.seq * ncs_eq;
+  }
+  sq.nc = (sq.len + kChunk - 1) / kChunk;
+  return sq;
+}
+
+// Segments of seg_len chunks (the last one shorter): a sequence of nc chunks
+// has max(1, ceil(nc / seg_len)) of them, segment 0 existing even for an empty
+// sequence so that its initial state passes to its final state. Never more
+// than n_seg (the grid's and the workspace's count), whatever the device copy
+// of the offsets says.
+__device__ __forceinline__ int seg_count(int nc, int seg_len, int n_seg) {
+  return nc <= seg_len ? 1 : min(n_seg, (nc + seg_len - 1) / seg_len);
+}
+
+// Restricts sq to segment `seg` (which must exist).
+__device__ __forceinline__ void restrict_to_segment(ScanSeq& sq, int seg, int seg_len) {
+  const int c0 = seg * seg_len;
+  sq.start += kChunk * c0;
+  sq.chunk0 += c0;
+  sq.len = min(sq.len - kChunk * c0, kChunk * seg_len);
+  if (sq.len < 0) sq.len = 0;
+  sq.nc = (sq.len + kChunk - 1) / kChunk;
+}
+
 // NCH = 1: waves 0 chain, 1 producer, 2 and 3 output. NCH = 2: waves 0 and 1
 // chains, 2 and 3 output, 4 producer. The waves of a workgroup are spread over
 // the four SIMDs of its CU (waves 0..3 on four different ones, wave 4 beside
 // wave 0), so each chain, which is bound by its own instruction issue, has a
 // SIMD to itself or shares it with the producer, the lightest role.
+//
+// n_seg > 1: the chunk-parallel form. Workgroup (pair, segment, slices) runs
+// its segment from the segment's initial state, which the combine kernel has
+// written to the workspace, and only the last segment stores the final state.
 template <int K, int V, typename Tin, typename Tout, int NCH>
 __global__ __launch_bounds__(scan_threads<NCH>()) __attribute__((amdgpu_waves_per_eu(NCH, NCH))) void scan_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o, int H,
     float scale, int n_seqs, int T_eq, int ncs_eq, int total_tokens, int n_chunks, const int32_t* __restrict__ cu,
     const float* __restrict__ h0, float* __restrict__ ht, float* __restrict__ pool, int64_t pool_slots,
-    const int32_t* __restrict__ slots, ChunkWs ws) {
+    const int32_t* __restrict__ slots, int seg_len, int n_seg, ChunkWs ws) {
   using S = ScanSmem<K, Tin, NCH>;
-  constexpr int NG = V / 16 / NCH;  // workgroups per (sequence, head)
+  constexpr int NG = V / 16 / NCH;  // workgroups per (sequence, head, segment)
   constexpr int NKB = K / 32;
   static_assert(NCH == 1 || NCH == 2, "one or two chains per workgroup");
   __shared__ __attribute__((aligned(1024))) char lds_k[2][KTile<K, Tin>::kBytes];
@@ -999,36 +1064,47 @@ __global__ __launch_bounds__(scan_threads<NCH>()) __attribute__((amdgpu_waves_pe
   // Workgroups of one (sequence, head) share an XCD (blockIdx % 8) and its L2.
   const int bid = blockIdx.x;
   const int xcd = bid & 7, rest = bid >> 3;
-  ScanSeq sq;
-  sq.slice = (rest % NG) * NCH;  // the workgroup's first slice
-  const int pair = (rest / NG) * 8 + xcd;
+  const int grp = rest % NG, r2 = rest / NG;
+  const int seg = r2 % n_seg;
+  const int pair = (r2 / n_seg) * 8 + xcd;
   if (pair >= n_seqs * H) return;
-  sq.seq = pair / H;
-  sq.h = pair % H;
-  if (cu) {
-    sq.start = cu[sq.seq];
-    sq.len = cu[sq.seq + 1] - sq.start;
-    sq.chunk0 = ws.seq_chunk0[sq.seq];
-    const int nc_want = (sq.len + kChunk - 1) / kChunk;
-    if (sq.start < 0 || sq.len < 0 || sq.start > total_tokens - sq.len || sq.chunk0 < 0 ||
-        sq.chunk0 > n_chunks - nc_want)
-      sq.len = 0;
+  ScanSeq sq = seq_of(pair, H, T_eq, ncs_eq, total_tokens, n_chunks, cu, ws);
+  sq.slice = grp * NCH;  // the workgroup's first slice
+
+  // the sequence's initial and final state pages
+  const int64_t page = static_cast<int64_t>(V) * K;
+  const float* st_in = nullptr;
+  float* st_out = nullptr;
+  if (pool) {
+    const int s = slots[sq.seq];
+    if (s > 0 && s < pool_slots) {
+      st_in = pool + (static_cast<int64_t>(s) * H + sq.h) * page;
+      st_out = pool + (static_cast<int64_t>(s) * H + sq.h) * page;
+    }
   } else {
-    sq.start = sq.seq * T_eq;
-    sq.len = T_eq;
-    sq.chunk0 = sq.seq * ncs_eq;
+    if (h0) st_in = h0 + (static_cast<int64_t>(sq.seq) * H + sq.h) * page;
+    if (ht) st_out = ht + (static_cast<int64_t>(sq.seq) * H + sq.h) * page;
   }
-  sq.nc = (sq.len + kChunk - 1) / kChunk;
+  if (n_seg > 1) {
+    const int ns = seg_count(sq.nc, seg_len, n_seg);
+    if (seg >= ns) return;
+    restrict_to_segment(sq, seg, seg_len);
+    st_in = ws.seg_state + (static_cast<int64_t>(pair) * n_seg + seg) * page;
+    if (seg != ns - 1) st_out = nullptr;
+  }
 
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr int kProducer = NCH == 1 ? 1 : 4;
   if (wv < NCH) {
     ScanSeq cs = sq;
     cs.slice = sq.slice + wv;
+    const int64_t rows = static_cast<int64_t>(cs.slice) * 16 * K;
+    const float* s_in = st_in ? st_in + rows : nullptr;
+    float* s_out = st_out ? st_out + rows : nullptr;
     if (wv == 0)
-      scan_chain<K, V, Tin, NCH>(sms[0], cs, h0, ht, pool, pool_slots, slots, H, ws);
+      scan_chain<K, V, Tin, NCH>(sms[0], cs, s_in, s_out, -1);
     else
-      scan_chain<K, V, Tin, NCH>(sms[NCH - 1], cs, h0, ht, pool, pool_slots, slots, H, ws);
+      scan_chain<K, V, Tin, NCH>(sms[NCH - 1], cs, s_in, s_out, -1);
   } else if (wv == kProducer) {
     scan_producer<K, V, Tin, NCH>(sms, sq, q, k, v, H, ws);
   } else if (wv == 2) {
@@ -1038,17 +1114,203 @@ __global__ __launch_bounds__(scan_threads<NCH>()) __attribute__((amdgpu_waves_pe
   }
 }
 
+// Chunk-parallel form, step 1. Over segment j the state map is affine,
+// h_out = M_j h_in + c_j (the chunk step is linear in h). Workgroup (pair,
+// segment j < n_seg - 1, 4 slices) runs the segment's chain with four chain
+// waves (one per SIMD) and a producer: slices of c_j start from zero with the
+// chunks' V, slices of M_j start from identity columns with V = 0. Both land
+// in the workspace in the state layout: page (pair, j) holds rows [v][key] of
+// c_j^T, then rows [m][key] of M_j^T (row m = column m of M_j).
+template <int K, int V>
+__global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(2, 2))) void summary_kernel(
+    const __bf16* __restrict__ k, const __bf16* __restrict__ v, int H, int n_seqs, int T_eq, int ncs_eq,
+    int total_tokens, int n_chunks, const int32_t* __restrict__ cu, int seg_len, int n_seg, ChunkWs ws) {
+  constexpr int NCH = 4;
+  using S = ScanSmem<K, __bf16, NCH>;
+  constexpr int NSL = V / 16, NKS = K / 16;
+  constexpr int NGA = (NSL + NKS) / NCH;
+  static_assert(NSL % NCH == 0 && NKS % NCH == 0, "a workgroup's slices are all of c or all of M");
+  __shared__ __attribute__((aligned(1024))) char lds_k[2][KTile<K, __bf16>::kBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_a[2][6][2 * kPlane];
+  __shared__ __attribute__((aligned(1024))) __bf16 lds_v[NCH][2][kChunk * 16];
+  __shared__ __attribute__((aligned(16))) float lds_gx[2][3 * kChunk];
+  S sms[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) sms[j] = S{lds_k, lds_a, lds_v[j], lds_gx, nullptr, nullptr, nullptr, nullptr, nullptr};
+
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, rest = bid >> 3;
+  const int grp = rest % NGA, r2 = rest / NGA;
+  const int seg = r2 % (n_seg - 1);
+  const int pair = (r2 / (n_seg - 1)) * 8 + xcd;
+  if (pair >= n_seqs * H) return;
+  ScanSeq sq = seq_of(pair, H, T_eq, ncs_eq, total_tokens, n_chunks, cu, ws);
+  if (seg >= seg_count(sq.nc, seg_len, n_seg) - 1) return;  // the last segment's map is never used
+  restrict_to_segment(sq, seg, seg_len);
+  sq.slice = grp * NCH;
+  const bool is_c = sq.slice < NSL;
+  float* page = ws.seg_sum + (static_cast<int64_t>(pair) * (n_seg - 1) + seg) * (V + K) * K;
+
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wv < NCH) {
+    ScanSeq cs = sq;
+    cs.slice = sq.slice + wv;
+    float* s_out = page + static_cast<int64_t>(cs.slice) * 16 * K;  // c rows, then M rows
+    const int ident = is_c ? -1 : (cs.slice - NSL) * 16;
+    if (wv == 0)
+      scan_chain<K, V, __bf16, NCH, false>(sms[0], cs, nullptr, s_out, ident);
+    else if (wv == 1)
+      scan_chain<K, V, __bf16, NCH, false>(sms[1], cs, nullptr, s_out, ident);
+    else if (wv == 2)
+      scan_chain<K, V, __bf16, NCH, false>(sms[2], cs, nullptr, s_out, ident);
+    else
+      scan_chain<K, V, __bf16, NCH, false>(sms[3], cs, nullptr, s_out, ident);
+  } else {
+    scan_producer<K, V, __bf16, NCH, true>(sms, sq, nullptr, k, v, H, ws, is_c);
+  }
+}
+
+// Chunk-parallel form, step 2: the initial state of every segment,
+// S_0 = the sequence's initial state, S_{j+1} = S_j M_j^T + c_j^T (state
+// layout [v][key]), in fp32. Rows are independent: workgroup (pair, 8 rows),
+// thread (p, l) computes rows 2 p, 2 p + 1 at keys 2 l, 2 l + 1. M_j^T is
+// copied into LDS (direct copies, double buffered: the next map lands while
+// the current one is applied); a row's values reach all its threads from LDS.
+template <int K, int V>
+__global__ __launch_bounds__(256) void combine_kernel(int H, int n_seqs, int T_eq, int ncs_eq, int total_tokens,
+                                                     int n_chunks, const int32_t* __restrict__ cu,
+                                                     const float* __restrict__ h0, const float* __restrict__ pool,
+                                                     int64_t pool_slots, const int32_t* __restrict__ slots,
+                                                     int seg_len, int n_seg, ChunkWs ws) {
+  constexpr int RB = V / 8;
+  constexpr int kCopies = K * K * 4 / 1024 / 4;  // 1 KiB copies of one map per wave
+  __shared__ __attribute__((aligned(1024))) float mt_lds[2][K * K];
+  __shared__ __attribute__((aligned(16))) float srow[2][8][K];
+  // a pair's workgroups share an XCD (blockIdx % 8), the one its summaries
+  // were written from, so its maps come into that XCD's L2 once
+  const int xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
+  const int rb = rest % RB, pair = (rest / RB) * 8 + xcd;
+  if (pair >= n_seqs * H) return;
+  const ScanSeq sq = seq_of(pair, H, T_eq, ncs_eq, total_tokens, n_chunks, cu, ws);
+  const int ns = seg_count(sq.nc, seg_len, n_seg);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r0 = 2 * w, key = 2 * lane;
+  const bool on = key < K;
+  const int64_t page = static_cast<int64_t>(V) * K;
+  const int64_t sum_page = static_cast<int64_t>(V + K) * K;
+  const float* sums = ws.seg_sum + static_cast<int64_t>(pair) * (n_seg - 1) * sum_page;
+
+  auto copy_map = [&](int j) {  // M_j^T rows into mt_lds[j & 1]
+    const Buf md(sums + j * sum_page + static_cast<int64_t>(V) * K, K * K * 4);
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+      const int blk = w * kCopies + i;
+      md.to_lds16(reinterpret_cast<char*>(mt_lds[j & 1]) + 1024 * blk, 16 * lane, 1024 * blk);
+    }
+  };
+
+  const float* s0 = nullptr;
+  if (pool) {
+    const int s = slots[sq.seq];
+    if (s > 0 && s < pool_slots) s0 = pool + (static_cast<int64_t>(s) * H + sq.h) * page;
+  } else if (h0) {
+    s0 = h0 + (static_cast<int64_t>(sq.seq) * H + sq.h) * page;
+  }
+  // c_j rows for every step, loaded up front; every state is stored at the end
+  // (so each step waits only for its map's copies)
+  float c[kMaxSegments - 1][2][2], x[kMaxSegments][2][2];
+#pragma unroll
+  for (int j = 0; j + 1 < kMaxSegments; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float* crow = sums + j * sum_page + static_cast<int64_t>(8 * rb + r0 + i) * K + key;
+      const bool ld = on && j + 1 < ns;
+      c[j][i][0] = ld ? crow[0] : 0.f;
+      c[j][i][1] = ld ? crow[1] : 0.f;
+    }
+  if (ns > 1) copy_map(0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t row = 8 * rb + r0 + i;
+    x[0][i][0] = on && s0 ? s0[row * K + key] : 0.f;
+    x[0][i][1] = on && s0 ? s0[row * K + key + 1] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j + 1 < kMaxSegments; ++j) {
+    if (j + 1 >= ns) break;
+    const int b = j & 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (on) *reinterpret_cast<float2*>(&srow[b][r0 + i][key]) = float2{x[j][i][0], x[j][i][1]};
+    wait_vmem();  // this wave's copies of M_j^T
+    __syncthreads();
+    if (j + 2 < ns) copy_map(j + 1);
+    const float* m = mt_lds[b];
+    float acc[2][2] = {{c[j][0][0], c[j][0][1]}, {c[j][1][0], c[j][1][1]}};
+    if (on) {
+      // two partial sums per output (even and odd m) for independent FMA chains
+      float part[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+#pragma unroll 8
+      for (int mm = 0; mm < K; mm += 4) {
+        const f32x4 s_a = *reinterpret_cast<const f32x4*>(&srow[b][r0][mm]);
+        const f32x4 s_b = *reinterpret_cast<const f32x4*>(&srow[b][r0 + 1][mm]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float2 mv = *reinterpret_cast<const float2*>(&m[(mm + e) * K + key]);
+          float(&pa)[2] = (e & 1) ? part[0] : acc[0];
+          float(&pb)[2] = (e & 1) ? part[1] : acc[1];
+          pa[0] += s_a[e] * mv.x;
+          pa[1] += s_a[e] * mv.y;
+          pb[0] += s_b[e] * mv.x;
+          pb[1] += s_b[e] * mv.y;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        acc[i][0] += part[i][0];
+        acc[i][1] += part[i][1];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      x[j + 1][i][0] = acc[i][0];
+      x[j + 1][i][1] = acc[i][1];
+    }
+  }
+  if (on) {
+    float* st = ws.seg_state + static_cast<int64_t>(pair) * n_seg * page;
+#pragma unroll
+    for (int j = 0; j < kMaxSegments; ++j) {
+      if (j >= ns) break;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<float2*>(&st[j * page + static_cast<int64_t>(8 * rb + r0 + i) * K + key]) =
+            float2{x[j][i][0], x[j][i][1]};
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host side: workspace layout and launch sequence.
 // ---------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Segments per sequence for the chunk-parallel form (bf16 inputs): as many as
+// keep two-slice scan workgroups within kSegCUs compute units, at most 8; 1
+// (not used) below 4, where the summaries would cost more than they save.
+constexpr int kSegCUs = 256;
+static int segment_cap(int64_t pairs, int V, bool in_f32) {
+  if (in_f32 || pairs <= 0) return 1;
+  const int64_t wg = pairs * (V / 16) / 2;
+  const int64_t s = std::min<int64_t>(kMaxSegments, kSegCUs / wg);
+  return s >= 4 ? static_cast<int>(s) : 1;
+}
+
 WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, bool in_f32) {
-  (void)K;
-  (void)V;
-  (void)in_f32;
   const size_t nch = static_cast<size_t>(max_chunks) * H;
+  const int64_t pairs = static_cast<int64_t>(n_seqs) * H;
   WsLayout l{};
+  l.max_segments = segment_cap(pairs, V, in_f32);
   size_t off = 0;
   l.af = off;
   off = align256(off + nch * kTileSetBytes);
@@ -1060,6 +1322,11 @@ WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, b
   off = align256(off + static_cast<size_t>(max_chunks) * 16);
   l.seq_chunk0 = off;
   off = align256(off + static_cast<size_t>(n_seqs + 1) * 4);
+  const size_t sm = static_cast<size_t>(l.max_segments);
+  l.seg_sum = off;
+  if (sm > 1) off = align256(off + static_cast<size_t>(pairs) * (sm - 1) * (V + K) * K * 4);
+  l.seg_state = off;
+  if (sm > 1) off = align256(off + static_cast<size_t>(pairs) * sm * V * K * 4);
   l.total = off;
   return l;
 }
@@ -1072,6 +1339,8 @@ ChunkWs carve_workspace(const WsLayout& l, void* base) {
   ws.gx = reinterpret_cast<float*>(b + l.gx);
   ws.info = reinterpret_cast<int4*>(b + l.info);
   ws.seq_chunk0 = reinterpret_cast<int*>(b + l.seq_chunk0);
+  ws.seg_sum = reinterpret_cast<float*>(b + l.seg_sum);
+  ws.seg_state = reinterpret_cast<float*>(b + l.seg_state);
   return ws;
 }
 
@@ -1094,20 +1363,48 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
   }
   if (a.events[1]) (void)hipEventRecord(a.events[1], a.stream);
   const int64_t pairs = static_cast<int64_t>(a.n_seqs) * a.H;
+  const unsigned pair8 = static_cast<unsigned>((pairs + 7) / 8);
+  // Chunk-parallel form where the scan would leave most compute units idle:
+  // n_seg segments per sequence, their maps (summary), the segments' initial
+  // states (combine), then every segment's scan at once.
+  int n_seg = 1, seg_len = 0;
+  const int cap = segment_cap(pairs, V, !std::is_same<Tin, __bf16>::value);
+  if (cap > 1) {
+    const int64_t wg = pairs * NSL / 2;
+    const int s = static_cast<int>(std::min<int64_t>({static_cast<int64_t>(cap), a.n_cus / wg, a.max_nc / 4}));
+    if (s >= 4) {
+      seg_len = (a.max_nc + s - 1) / s;
+      n_seg = (a.max_nc + seg_len - 1) / seg_len;
+    }
+  }
+  if constexpr (std::is_same<Tin, __bf16>::value) {
+    if (n_seg > 1) {
+      constexpr int NGA = (NSL + K / 16) / 4;
+      hipLaunchKernelGGL((summary_kernel<K, V>), dim3(8 * NGA * (n_seg - 1) * pair8), dim3(320), 0, a.stream,
+                         static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v), a.H, a.n_seqs, a.T_eq,
+                         ncs_eq, static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens,
+                         seg_len, n_seg, a.ws);
+      hipLaunchKernelGGL((combine_kernel<K, V>), dim3(8 * (V / 8) * pair8), dim3(256), 0,
+                         a.stream, a.H, a.n_seqs, a.T_eq, ncs_eq, static_cast<int>(a.total_tokens),
+                         static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0, a.pool, a.pool_slots, a.slots, seg_len,
+                         n_seg, a.ws);
+    }
+  }
   // Two chains per workgroup (sharing K, A' and the gates, on two SIMDs of a
-  // CU) once one-chain workgroups would outnumber the compute units; bf16
-  // inputs only (float32 operands would not leave room in LDS for the rest).
+  // CU) once one-chain workgroups would outnumber the compute units, and in
+  // the chunk-parallel form; bf16 inputs only (float32 operands would not
+  // leave room in LDS for the rest).
   auto launch = [&](auto kern, int nch) {
-    const int64_t blocks = 8 * (NSL / nch) * ((pairs + 7) / 8);
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(64 * (nch + 3)), 0, a.stream,
-                       static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
-                       static_cast<Tout*>(a.o), a.H, a.scale, a.n_seqs, a.T_eq, ncs_eq,
-                       static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0, a.ht,
-                       a.pool, a.pool_slots, a.slots, a.ws);
+    const unsigned blocks = 8 * (NSL / nch) * n_seg * pair8;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * (nch + 3)), 0, a.stream, static_cast<const Tin*>(a.q),
+                       static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v), static_cast<Tout*>(a.o), a.H,
+                       a.scale, a.n_seqs, a.T_eq, ncs_eq, static_cast<int>(a.total_tokens),
+                       static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0, a.ht, a.pool, a.pool_slots, a.slots,
+                       seg_len, n_seg, a.ws);
   };
   bool two = false;
   if constexpr (std::is_same<Tin, __bf16>::value) {
-    two = pairs * NSL > a.n_cus;
+    two = pairs * NSL > a.n_cus || n_seg > 1;
     if (two) launch(scan_kernel<K, V, Tin, Tout, 2>, 2);
   }
   if (!two) launch(scan_kernel<K, V, Tin, Tout, 1>, 1);

@@ -32,12 +32,17 @@ struct DecodeArgs {
 //        the log-gate; rows past the chunk end repeat g_last), e^g, e^{g_last - g}
 //   info [chunk] int4 {seq, first token, rows, 0} and seq_chunk0 [n_seqs + 1]:
 //        the chunk schedule of a packed (varlen) call
+//   seg_sum [pair][n_seg - 1][V + K][K] f32   chunk-parallel form: per segment,
+//        the affine map of the state, c^T rows then M^T rows
+//   seg_state [pair][n_seg][V][K] f32          the initial state of each segment
 struct ChunkWs {
   uint8_t* af;
   uint8_t* pf;
   float* gx;
   int4* info;
   int* seq_chunk0;
+  float* seg_sum;
+  float* seg_state;
 };
 
 struct ChunkArgs {
@@ -51,6 +56,7 @@ struct ChunkArgs {
   bool in_f32, out_f32;
   const int32_t* cu_seqlens;  // device, or null for equal lengths
   int64_t n_chunks;           // total chunks over all sequences
+  int max_nc;                 // chunks of the longest sequence
   int T_eq;                   // equal-length mode: tokens per sequence
   const float* h0;
   float* ht;
@@ -65,7 +71,8 @@ struct ChunkArgs {
 
 // Workspace layout for a call with at most max_chunks chunks.
 struct WsLayout {
-  size_t af, pf, gx, info, seq_chunk0, total;
+  size_t af, pf, gx, info, seq_chunk0, seg_sum, seg_state, total;
+  int max_segments;  // segments per sequence the chunk-parallel form may use (1: not used)
 };
 WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, bool in_f32);
 ChunkWs carve_workspace(const WsLayout& l, void* base);

@@ -51,10 +51,16 @@ def test_workspace_bytes():
     b1 = L.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 128, BF16)
     b2 = L.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 128, F32)
     b3 = L.gdn_chunk_fwd_workspace_bytes(16, 60217, 16, 128, 128, BF16)
-    assert 0 < b1 <= b2 and b3 > b1
+    assert 0 < b2 < b1 and b3 > b2
     # A' and P (the 6 nonzero hi/lo fragment tiles, 12 KiB each) plus three 64-float gate vectors per (chunk, head)
-    per = b1 / ((4096 // 64 + 1) * 16)
+    per = b2 / ((4096 // 64 + 1) * 16)
     assert 24 * 1024 + 768 <= per < 26 * 1024
+    # bf16 with 16 (sequence, head) pairs: room for the chunk-parallel form with 4
+    # segments: 3 segment maps ([V + K][K] f32) and 4 initial states ([V][K] f32) per pair
+    assert b1 - b2 == 16 * (3 * 256 * 128 + 4 * 128 * 128) * 4
+    # 256 pairs fill the GPU without segments: no such room
+    per3 = b3 / ((60217 // 64 + 16) * 16)
+    assert 24 * 1024 + 768 <= per3 < 26 * 1024
 
 
 def _chunk(**kw):

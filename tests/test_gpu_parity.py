@@ -171,6 +171,70 @@ def test_two_chain_varlen_edges():
     check_chunk(ci, 0.2, label="varlen edges, 40 heads")
 
 
+# The chunk-parallel form (segments of chunks, their affine state maps, then all
+# segments at once) runs for bf16 inputs when few (sequence, head) pairs would
+# leave most compute units idle: at most 16 pairs at V = 128 and at least 16
+# chunks. Long-memory gates make the segment maps far from zero.
+
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (128, 64), (64, 128)])
+def test_segmented_ragged_long_memory(K, V):
+    """T = 1500 (23 full chunks and a ragged one), 3 heads, h0 != 0."""
+    ci = chunk_inputs([1500], 3, K, V, dtype="bf16", seed=60 + K + V, gate_shift=-4.0, h0_std=0.1)
+    check_chunk(ci, K ** -0.5, label=f"segmented K={K} V={V}")
+
+
+def test_segmented_varlen_pool():
+    """Packed sequences of very different lengths (one segment or several, an
+    empty one) with states in a pool, one slot padding (<= 0)."""
+    lengths = [3000, 100, 0, 1500, 1280, 37]
+    ci = chunk_inputs(lengths, 2, 128, 128, dtype="bf16", seed=61, gate_shift=-4.0, pool_slots=8,
+                      slot_ids=[3, 1, 7, 0, 5, 2])
+    pool0 = dev(ci.pool)
+    scale = 128 ** -0.5
+    pool32 = pool0.clone()
+    o32, _ = run_chunk(ci, scale, "f32", use_pool=True, pool_dev=pool32)
+    pool16 = pool0.clone()
+    o16, _ = run_chunk(ci, scale, "bf16", use_pool=True, pool_dev=pool16)
+    assert torch.equal(o16, bf16_rne(o32))
+    assert torch.equal(pool16, pool32)
+    for s in (0, 4, 6):  # unused slots and the padding sequence's: untouched
+        assert torch.equal(pool32[s], pool0[s]), f"slot {s} was written"
+    ref = oracle_chunk(ci, scale)
+    o_h = host(o32)
+    for s in range(len(lengths)):
+        r = slice(int(ci.cu_seqlens[s]), int(ci.cu_seqlens[s + 1]))
+        o_ref, S_ref = ref[s]
+        if o_ref.size:
+            eo = max_err_over_rms(o_h[r], o_ref)
+            _print(f"[segmented varlen seq {s} len {lengths[s]}] max|do|/rms={eo:.3e}")
+            assert eo <= TOL["bf16"]
+        if ci.slots[s] > 0:
+            got = host(pool32[ci.slots[s]])
+            if S_ref is None:
+                S_ref = np.zeros_like(got)
+            es = max_err_over_rms(got, S_ref) if np.any(S_ref) else float(np.max(np.abs(got)))
+            assert es <= TOL["bf16"], f"seq {s}: state error {es:.3e}"
+
+
+def test_segmented_in_place_state():
+    """ht aliasing h0 in the chunk-parallel form: only the last segment writes
+    the final state, after every segment's initial state was taken."""
+    ci = chunk_inputs([2048, 2048], 2, 128, 128, dtype="bf16", seed=62, gate_shift=-4.0, h0_std=0.1)
+    dt = torch.bfloat16
+    q, k, v = (dev(x, dt).view(2, 2048, 2, -1) for x in (ci.q, ci.k, ci.v))
+    g, b = dev(ci.a).view(2, 2048, 2), dev(ci.beta).view(2, 2048, 2)
+    h0 = dev(ci.h0)
+    o1, ht1 = api.chunk_fwd(q, k, v, g, b, scale=0.1, h0=h0, out_dtype=torch.float32)
+    state = h0.clone()
+    o2, _ = api.chunk_fwd(q, k, v, g, b, scale=0.1, h0=state, ht=state, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o1) and torch.equal(state, ht1)
+    ref = oracle_chunk(ci, 0.1)
+    for s in range(2):
+        assert max_err_over_rms(host(o1[s]), ref[s][0]) <= TOL["bf16"]
+        assert max_err_over_rms(host(ht1[s]), ref[s][1]) <= TOL["bf16"]
+
+
 def test_config_h16_t4096_full():
     """B=1, H=16, T=4096, K=V=128, bf16: every output and the final state."""
     ci = chunk_inputs([4096], 16, 128, 128, dtype="bf16", seed=2)
