@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Throughput of the gated delta rule on one MI355X.
 
-A step is one chunked forward pass (gdn_chunk_fwd: chunk schedule, the prep
-kernel for recompute_w_u, the scan kernel for chunk_fwd_h fused with
-chunk_fwd_o) over one batch of B=1, H=16, T=4096, K=V=128 bf16 inputs, already
-resident in device memory. The decode step (gdn_recurrent_step, N=256 requests,
+A step is one chunked forward pass (gdn_chunk_fwd: the prep kernel for
+recompute_w_u, then chunk_fwd_h fused with chunk_fwd_o, which at this shape runs
+in the chunk-parallel form: summary kernel, combine kernel, scan kernel) over
+one batch of B=1, H=16, T=4096, K=V=128 bf16 inputs, already resident in device
+memory. The decode step (gdn_recurrent_step, N=256 requests,
 H=32, K=V=128, a 512-slot float32 state pool) is timed beside it in the same run
 and reported under "decode".
 
@@ -12,8 +13,9 @@ Prints one JSON line on stdout (everything else goes to stderr). The K timed
 steps are plain calls. Per-kernel durations come from K further calls of
 gdn_chunk_fwd_profiled, which records HIP events on the library's stream around
 each launch (recording them inside the timed steps would add about 10 us per
-call); the roofline of the dominant kernel (the scan kernel) is its algorithmic
-FLOPs per launch over that duration.
+call); the roofline of the dominant part, chunk_fwd_h + chunk_fwd_o (the span of
+the summary, combine and scan kernels), is its algorithmic FLOPs per call over
+that duration.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --only chunk|decode|copy --steps K   (profiling runs)
@@ -120,9 +122,10 @@ def stats(xs):
     return dict(mean=sum(xs) / n, median=xs[n // 2], p10=xs[int(0.1 * (n - 1))], p90=xs[int(0.9 * (n - 1))])
 
 
-def traffic_for(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed PMC counter runs, or
-    None when the kernels changed since the counters were taken."""
+def traffic_for(*kernels: str):
+    """HBM bytes per call of the named kernels (summed) from the committed PMC
+    counter runs, or None when the kernels changed since the counters were
+    taken or one of them was not recorded."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -130,8 +133,13 @@ def traffic_for(kernel: str):
         return None
     if rec.get("source_digest") != source_digest():
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    total = 0
+    for kernel in kernels:
+        k = rec.get("kernels", {}).get(kernel)
+        if k is None or k.get("bytes_per_launch") is None:
+            return None
+        total += k["bytes_per_launch"]
+    return total
 
 
 def bench_chunk(torch, api, hev, steps, warmup, flush_bytes=512 << 20):
@@ -333,14 +341,17 @@ def main():
                                "fp32 beta/g, o bf16 + final state fp32",
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": K, "chunk": C,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "scan_kernel (chunk_fwd_h fused with chunk_fwd_o)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "chunk_fwd_h fused with chunk_fwd_o: summary_kernel + combine_kernel + scan_kernel "
+                               "(chunk-parallel form, 4 segments of 16 chunks)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for("scan_kernel"),
+                     "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_for("summary_kernel", "combine_kernel", "scan_kernel"),
                      "flops_per_launch": flops_ho, "avg_launch_us": scan_s * 1e6},
-        "kernels_us": {"prep": res_c["prep_ms"]["mean"] * 1e3, "scan": res_c["scan_ms"]["mean"] * 1e3,
+        "kernels_us": {"prep": res_c["prep_ms"]["mean"] * 1e3, "h_o": res_c["scan_ms"]["mean"] * 1e3,
                        "call": res_c["call_ms"]["mean"] * 1e3,
                        "cold_prep": res_c["cold_prep_ms"]["mean"] * 1e3,
-                       "cold_scan": res_c["cold_scan_ms"]["mean"] * 1e3},
+                       "cold_h_o": res_c["cold_scan_ms"]["mean"] * 1e3},
         "full_fwd_tflops": flops_full / (ms_per_step / 1e3) / 1e12,
         "decode": {"workload": "recurrent decode step, N=256 requests (all active), H=32, K=V=128, "
                                "pool [512, 32, 128, 128] fp32, bf16 q/k/v/o",
