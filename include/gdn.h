@@ -63,7 +63,9 @@ typedef enum gdn_dtype {
  * sequences). Returns 0 for invalid sizes. The workspace holds the chunk
  * intermediates of recompute_w_u in the form the scan consumes (A' = A diag(beta)
  * of the WY matrix A, from which u - w h = A'(V - diag(e^g) K h) follows), the
- * masked intra-chunk scores, the chunk-local gate sums, and the chunk schedule.
+ * masked intra-chunk scores, the chunk-local gate sums, the chunk schedule
+ * and, for bfloat16 inputs with few (sequence, head) pairs, the chunk-parallel
+ * form's per-segment state maps and initial states.
  */
 size_t gdn_chunk_fwd_workspace_bytes(int n_seqs, int64_t total_tokens, int H, int K, int V,
                                      gdn_dtype in_dtype);
@@ -115,9 +117,10 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const floa
  * results, and in addition it records three caller-created HIP events
  * (hipEvent_t, passed as void*) on `stream`: events[0] before the first kernel,
  * events[1] after the prep kernel (recompute_w_u: gate sums, K K^T, triangular
- * solve, A' and the masked intra-chunk scores), events[2] after the scan
- * kernel (chunk_fwd_h fused with chunk_fwd_o). hipEventElapsedTime of
- * consecutive events then gives each kernel's duration on that stream.
+ * solve, A' and the masked intra-chunk scores), events[2] after chunk_fwd_h
+ * fused with chunk_fwd_o (the scan kernel, preceded in the chunk-parallel form
+ * by the segment summary and combine kernels). hipEventElapsedTime of
+ * consecutive events then gives each part's duration on that stream.
  * `events` must point to three valid events; GDN_EINVAL otherwise.
  */
 gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const void* v, const float* g,
