@@ -504,11 +504,17 @@ struct ScanSeq {
 
 // The chain wave. Its state slice starts from rows [lc][key] of s_in (zeros if
 // null; if ident >= 0, the columns ident .. ident + 15 of the identity, which
-// makes the final state those columns of the chunks' linear map) and ends in
-// s_out (if not null). PUB: publish the state and v_new for output waves.
+// makes the final state those columns of the chunks' linear map), is then
+// carried through n_fold segment maps (h <- M_j h + c_j, M_j rows [key][m] at
+// fm + j fstride, this slice's c_j^T rows [lc][key] at fc + j fstride), and
+// ends in s_out (if not null; rows [lc][key], or with out_t the transpose,
+// s_out[key * K + lc]). PUB: publish the state and v_new for output waves.
 template <int K, int V, typename Tin, int NCH, bool PUB = true>
 __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, const ScanSeq& sq,
-                                           const float* __restrict__ s_in, float* __restrict__ s_out, int ident) {
+                                           const float* __restrict__ s_in, float* __restrict__ s_out, int ident,
+                                           bool out_t = false, const float* __restrict__ fc = nullptr,
+                                           const float* __restrict__ fm = nullptr, int n_fold = 0,
+                                           int64_t fstride = 0) {
   using P = Prec<Tin>;
   using In = typename P::In;
   using Cmp = typename P::Cmp;
@@ -527,6 +533,73 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, cons
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (key0 + r == ident + lc) hs[t][r] = 1.f;
+    }
+  }
+  // the maps of the segments before this one, on the MFMA like K h: A operand
+  // lane (g, c) = 8 consecutive m of row key_row(t, c) of M_j (the state tile's
+  // permuted key order), split hi + lo; B operand = the state split. The map
+  // rows come in batches of two tiles of one key block, kD batches in flight
+  // (a ring of register sets); c_j is added last. From a zero initial state the
+  // first map is not needed: the state after segment 0 is c_0.
+  if (n_fold > 0) {
+    constexpr int NB = NKB * NKB;  // batches per map: NKB key blocks x (2 NKB tiles / 2)
+    constexpr int kD = 4;
+    static_assert(NB % kD == 0, "whole rings per map");
+    f32x4 ring[kD][2][2];
+    auto load_batch = [&](int j, int bt, f32x4 (&buf)[2][2]) {
+      const int kb = bt / NKB, t0 = 2 * (bt % NKB);
+      const float* mj = fm + j * fstride + 32 * kb + 8 * lg;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int t = t0 + i;
+        const int krow = 32 * (t >> 1) + 8 * (lc >> 2) + 4 * (t & 1) + (lc & 3);
+        buf[i][0] = *reinterpret_cast<const f32x4*>(mj + krow * K);
+        buf[i][1] = *reinterpret_cast<const f32x4*>(mj + krow * K + 4);
+      }
+    };
+    const int j0 = s_in ? 0 : 1;  // zero start: h after segment 0 = c_0
+    if (j0 == 1) {
+#pragma unroll
+      for (int t = 0; t < 2 * NKB; ++t) {
+        const int key0 = 32 * (t >> 1) + 8 * lg + 4 * (t & 1);
+        hs[t] = *reinterpret_cast<const f32x4*>(fc + lc * K + key0);
+      }
+    }
+    if (j0 < n_fold) {
+#pragma unroll
+      for (int d = 0; d < kD; ++d) load_batch(j0, d, ring[d]);
+    }
+    for (int j = j0; j < n_fold; ++j) {
+      const float* cj = fc + j * fstride;
+      f32x4 cv[2 * NKB];
+#pragma unroll
+      for (int t = 0; t < 2 * NKB; ++t) {
+        const int key0 = 32 * (t >> 1) + 8 * lg + 4 * (t & 1);
+        cv[t] = *reinterpret_cast<const f32x4*>(cj + lc * K + key0);
+      }
+      Cmp hb[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) hb[kb] = P::cmp_tiles(hs[2 * kb], hs[2 * kb + 1]);
+#pragma unroll
+      for (int t = 0; t < 2 * NKB; ++t) hs[t] = zero4();
+#pragma unroll
+      for (int bt = 0; bt < NB; ++bt) {
+        f32x4(&buf)[2][2] = ring[bt % kD];
+        const int kb = bt / NKB, t0 = 2 * (bt % NKB);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const Cmp am = P::cmp_tiles(buf[i][0], buf[i][1]);
+#pragma unroll
+          for (int u = 0; u < Terms<Cmp, Cmp>::n; ++u) hs[t0 + i] = term(am, hb[kb], hs[t0 + i], u);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (bt + kD < NB)
+          load_batch(j, bt + kD, buf);
+        else if (j + 1 < n_fold)
+          load_batch(j + 1, bt + kD - NB, buf);
+      }
+#pragma unroll
+      for (int t = 0; t < 2 * NKB; ++t) hs[t] += cv[t];
     }
   }
   if (ident >= 0) {
@@ -682,7 +755,12 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, cons
 #pragma unroll
     for (int t = 0; t < 2 * NKB; ++t) {
       const int key0 = 32 * (t >> 1) + 8 * lg + 4 * (t & 1);
-      *reinterpret_cast<f32x4*>(s_out + lc * K + key0) = hs[t];
+      if (out_t) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_out[(key0 + r) * K + lc] = hs[t][r];
+      } else {
+        *reinterpret_cast<f32x4*>(s_out + lc * K + key0) = hs[t];
+      }
     }
   }
 }
@@ -1035,9 +1113,10 @@ __device__ __forceinline__ void restrict_to_segment(ScanSeq& sq, int seg, int se
 // wave 0), so each chain, which is bound by its own instruction issue, has a
 // SIMD to itself or shares it with the producer, the lightest role.
 //
-// n_seg > 1: the chunk-parallel form. Workgroup (pair, segment, slices) runs
-// its segment from the segment's initial state, which the combine kernel has
-// written to the workspace, and only the last segment stores the final state.
+// n_seg > 1: the chunk-parallel form. Workgroup (pair, segment j, slices) runs
+// its segment from the sequence's initial state carried through the maps of
+// segments 0 .. j - 1 (summary kernel), and only the last segment stores the
+// final state.
 template <int K, int V, typename Tin, typename Tout, int NCH>
 __global__ __launch_bounds__(scan_threads<NCH>()) __attribute__((amdgpu_waves_per_eu(NCH, NCH))) void scan_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o, int H,
@@ -1085,11 +1164,20 @@ __global__ __launch_bounds__(scan_threads<NCH>()) __attribute__((amdgpu_waves_pe
     if (h0) st_in = h0 + (static_cast<int64_t>(sq.seq) * H + sq.h) * page;
     if (ht) st_out = ht + (static_cast<int64_t>(sq.seq) * H + sq.h) * page;
   }
+  // chunk-parallel form: a sequence with several segments starts each from the
+  // copy of its initial state the summary kernel made (its final state may be
+  // written in place meanwhile) carried through the maps of the segments before
+  const float* fold = nullptr;
+  int n_fold = 0;
   if (n_seg > 1) {
     const int ns = seg_count(sq.nc, seg_len, n_seg);
     if (seg >= ns) return;
     restrict_to_segment(sq, seg, seg_len);
-    st_in = ws.seg_state + (static_cast<int64_t>(pair) * n_seg + seg) * page;
+    if (ns > 1) {
+      if (st_in) st_in = ws.seg_state + static_cast<int64_t>(pair) * page;  // null: a zero start
+      fold = ws.seg_sum + static_cast<int64_t>(pair) * (n_seg - 1) * (V + K) * K;
+      n_fold = seg;
+    }
     if (seg != ns - 1) st_out = nullptr;
   }
 
@@ -1101,30 +1189,50 @@ __global__ __launch_bounds__(scan_threads<NCH>()) __attribute__((amdgpu_waves_pe
     const int64_t rows = static_cast<int64_t>(cs.slice) * 16 * K;
     const float* s_in = st_in ? st_in + rows : nullptr;
     float* s_out = st_out ? st_out + rows : nullptr;
+    const float* fc = fold ? fold + rows : nullptr;
+    const float* fm = fold ? fold + static_cast<int64_t>(V) * K : nullptr;
+    const int64_t fstride = static_cast<int64_t>(V + K) * K;
     if (wv == 0)
-      scan_chain<K, V, Tin, NCH>(sms[0], cs, s_in, s_out, -1);
+      scan_chain<K, V, Tin, NCH>(sms[0], cs, s_in, s_out, -1, false, fc, fm, n_fold, fstride);
     else
-      scan_chain<K, V, Tin, NCH>(sms[NCH - 1], cs, s_in, s_out, -1);
+      scan_chain<K, V, Tin, NCH>(sms[NCH - 1], cs, s_in, s_out, -1, false, fc, fm, n_fold, fstride);
   } else if (wv == kProducer) {
     scan_producer<K, V, Tin, NCH>(sms, sq, q, k, v, H, ws);
-  } else if (wv == 2) {
-    scan_output<0, K, V, Tin, Tout, NCH>(sms, sq, q, o, H, scale, ws);
   } else {
-    scan_output<1, K, V, Tin, Tout, NCH>(sms, sq, q, o, H, scale, ws);
+    if (n_fold > 0) {
+      // The maps come from another kernel and are not in this XCD's L2 yet:
+      // the output waves, idle until the chains' first step, touch every
+      // 128-byte line of the pages the chains fold through (each of the NG
+      // workgroups of this (pair, segment) a share), so the chains' loads hit L2.
+      constexpr int kLines = (V + K) * K * 4 / 128;  // lines per page
+      const int lane = threadIdx.x & 63, ow = wv - 2;
+      uint32_t sink = 0;
+      for (int j = 0; j < n_fold; ++j)
+        for (int m = 64 * ow + lane; m * NG + grp < kLines; m += 128)
+          sink += __builtin_bit_cast(uint32_t, fold[j * static_cast<int64_t>(V + K) * K + 32 * (m * NG + grp)]);
+      asm volatile("" ::"v"(sink));
+    }
+    if (wv == 2)
+      scan_output<0, K, V, Tin, Tout, NCH>(sms, sq, q, o, H, scale, ws);
+    else
+      scan_output<1, K, V, Tin, Tout, NCH>(sms, sq, q, o, H, scale, ws);
   }
 }
 
-// Chunk-parallel form, step 1. Over segment j the state map is affine,
+// Chunk-parallel form. Over segment j the state map is affine,
 // h_out = M_j h_in + c_j (the chunk step is linear in h). Workgroup (pair,
 // segment j < n_seg - 1, 4 slices) runs the segment's chain with four chain
 // waves (one per SIMD) and a producer: slices of c_j start from zero with the
-// chunks' V, slices of M_j start from identity columns with V = 0. Both land
-// in the workspace in the state layout: page (pair, j) holds rows [v][key] of
-// c_j^T, then rows [m][key] of M_j^T (row m = column m of M_j).
+// chunks' V, slices of M_j start from identity columns with V = 0. Page
+// (pair, j) of the workspace holds c_j^T as rows [v][key], then M_j as rows
+// [key][m]. The c-slice workgroups of segment 0 also copy the pair's initial
+// state into the workspace, where every segment's scan starts from it.
 template <int K, int V>
 __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(2, 2))) void summary_kernel(
     const __bf16* __restrict__ k, const __bf16* __restrict__ v, int H, int n_seqs, int T_eq, int ncs_eq,
-    int total_tokens, int n_chunks, const int32_t* __restrict__ cu, int seg_len, int n_seg, ChunkWs ws) {
+    int total_tokens, int n_chunks, const int32_t* __restrict__ cu, const float* __restrict__ h0,
+    const float* __restrict__ pool, int64_t pool_slots, const int32_t* __restrict__ slots, int seg_len, int n_seg,
+    ChunkWs ws) {
   constexpr int NCH = 4;
   using S = ScanSmem<K, __bf16, NCH>;
   constexpr int NSL = V / 16, NKS = K / 16;
@@ -1155,138 +1263,33 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (wv < NCH) {
     ScanSeq cs = sq;
     cs.slice = sq.slice + wv;
-    float* s_out = page + static_cast<int64_t>(cs.slice) * 16 * K;  // c rows, then M rows
+    const int lane = threadIdx.x & 63;
+    const int64_t st_page = static_cast<int64_t>(V) * K;
+    if (seg == 0 && is_c) {
+      const float* s0 = nullptr;
+      if (pool) {
+        const int s = slots[sq.seq];
+        if (s > 0 && s < pool_slots) s0 = pool + (static_cast<int64_t>(s) * H + sq.h) * st_page;
+      } else if (h0) {
+        s0 = h0 + (static_cast<int64_t>(sq.seq) * H + sq.h) * st_page;
+      }
+      const int64_t rows = static_cast<int64_t>(cs.slice) * 16 * K;
+      f32x4* dst = reinterpret_cast<f32x4*>(ws.seg_state + static_cast<int64_t>(pair) * st_page + rows);
+      for (int i = lane; i < 16 * K / 4; i += 64) dst[i] = s0 ? reinterpret_cast<const f32x4*>(s0 + rows)[i] : zero4();
+    }
+    // c rows [v][key]; M rows [key][m]: column m0 .. m0 + 15 of M_j stored transposed
     const int ident = is_c ? -1 : (cs.slice - NSL) * 16;
+    float* s_out = is_c ? page + static_cast<int64_t>(cs.slice) * 16 * K : page + static_cast<int64_t>(V) * K + ident;
     if (wv == 0)
-      scan_chain<K, V, __bf16, NCH, false>(sms[0], cs, nullptr, s_out, ident);
+      scan_chain<K, V, __bf16, NCH, false>(sms[0], cs, nullptr, s_out, ident, !is_c);
     else if (wv == 1)
-      scan_chain<K, V, __bf16, NCH, false>(sms[1], cs, nullptr, s_out, ident);
+      scan_chain<K, V, __bf16, NCH, false>(sms[1], cs, nullptr, s_out, ident, !is_c);
     else if (wv == 2)
-      scan_chain<K, V, __bf16, NCH, false>(sms[2], cs, nullptr, s_out, ident);
+      scan_chain<K, V, __bf16, NCH, false>(sms[2], cs, nullptr, s_out, ident, !is_c);
     else
-      scan_chain<K, V, __bf16, NCH, false>(sms[3], cs, nullptr, s_out, ident);
+      scan_chain<K, V, __bf16, NCH, false>(sms[3], cs, nullptr, s_out, ident, !is_c);
   } else {
     scan_producer<K, V, __bf16, NCH, true>(sms, sq, nullptr, k, v, H, ws, is_c);
-  }
-}
-
-// Chunk-parallel form, step 2: the initial state of every segment,
-// S_0 = the sequence's initial state, S_{j+1} = S_j M_j^T + c_j^T (state
-// layout [v][key]), in fp32. Rows are independent: workgroup (pair, 8 rows),
-// thread (p, l) computes rows 2 p, 2 p + 1 at keys 2 l, 2 l + 1. M_j^T is
-// copied into LDS (direct copies, double buffered: the next map lands while
-// the current one is applied); a row's values reach all its threads from LDS.
-template <int K, int V>
-__global__ __launch_bounds__(256) void combine_kernel(int H, int n_seqs, int T_eq, int ncs_eq, int total_tokens,
-                                                     int n_chunks, const int32_t* __restrict__ cu,
-                                                     const float* __restrict__ h0, const float* __restrict__ pool,
-                                                     int64_t pool_slots, const int32_t* __restrict__ slots,
-                                                     int seg_len, int n_seg, ChunkWs ws) {
-  constexpr int RB = V / 8;
-  constexpr int kCopies = K * K * 4 / 1024 / 4;  // 1 KiB copies of one map per wave
-  __shared__ __attribute__((aligned(1024))) float mt_lds[2][K * K];
-  __shared__ __attribute__((aligned(16))) float srow[2][8][K];
-  // a pair's workgroups share an XCD (blockIdx % 8), the one its summaries
-  // were written from, so its maps come into that XCD's L2 once
-  const int xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
-  const int rb = rest % RB, pair = (rest / RB) * 8 + xcd;
-  if (pair >= n_seqs * H) return;
-  const ScanSeq sq = seq_of(pair, H, T_eq, ncs_eq, total_tokens, n_chunks, cu, ws);
-  const int ns = seg_count(sq.nc, seg_len, n_seg);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r0 = 2 * w, key = 2 * lane;
-  const bool on = key < K;
-  const int64_t page = static_cast<int64_t>(V) * K;
-  const int64_t sum_page = static_cast<int64_t>(V + K) * K;
-  const float* sums = ws.seg_sum + static_cast<int64_t>(pair) * (n_seg - 1) * sum_page;
-
-  auto copy_map = [&](int j) {  // M_j^T rows into mt_lds[j & 1]
-    const Buf md(sums + j * sum_page + static_cast<int64_t>(V) * K, K * K * 4);
-#pragma unroll
-    for (int i = 0; i < kCopies; ++i) {
-      const int blk = w * kCopies + i;
-      md.to_lds16(reinterpret_cast<char*>(mt_lds[j & 1]) + 1024 * blk, 16 * lane, 1024 * blk);
-    }
-  };
-
-  const float* s0 = nullptr;
-  if (pool) {
-    const int s = slots[sq.seq];
-    if (s > 0 && s < pool_slots) s0 = pool + (static_cast<int64_t>(s) * H + sq.h) * page;
-  } else if (h0) {
-    s0 = h0 + (static_cast<int64_t>(sq.seq) * H + sq.h) * page;
-  }
-  // c_j rows for every step, loaded up front; every state is stored at the end
-  // (so each step waits only for its map's copies)
-  float c[kMaxSegments - 1][2][2], x[kMaxSegments][2][2];
-#pragma unroll
-  for (int j = 0; j + 1 < kMaxSegments; ++j)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float* crow = sums + j * sum_page + static_cast<int64_t>(8 * rb + r0 + i) * K + key;
-      const bool ld = on && j + 1 < ns;
-      c[j][i][0] = ld ? crow[0] : 0.f;
-      c[j][i][1] = ld ? crow[1] : 0.f;
-    }
-  if (ns > 1) copy_map(0);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t row = 8 * rb + r0 + i;
-    x[0][i][0] = on && s0 ? s0[row * K + key] : 0.f;
-    x[0][i][1] = on && s0 ? s0[row * K + key + 1] : 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j + 1 < kMaxSegments; ++j) {
-    if (j + 1 >= ns) break;
-    const int b = j & 1;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (on) *reinterpret_cast<float2*>(&srow[b][r0 + i][key]) = float2{x[j][i][0], x[j][i][1]};
-    wait_vmem();  // this wave's copies of M_j^T
-    __syncthreads();
-    if (j + 2 < ns) copy_map(j + 1);
-    const float* m = mt_lds[b];
-    float acc[2][2] = {{c[j][0][0], c[j][0][1]}, {c[j][1][0], c[j][1][1]}};
-    if (on) {
-      // two partial sums per output (even and odd m) for independent FMA chains
-      float part[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-#pragma unroll 8
-      for (int mm = 0; mm < K; mm += 4) {
-        const f32x4 s_a = *reinterpret_cast<const f32x4*>(&srow[b][r0][mm]);
-        const f32x4 s_b = *reinterpret_cast<const f32x4*>(&srow[b][r0 + 1][mm]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float2 mv = *reinterpret_cast<const float2*>(&m[(mm + e) * K + key]);
-          float(&pa)[2] = (e & 1) ? part[0] : acc[0];
-          float(&pb)[2] = (e & 1) ? part[1] : acc[1];
-          pa[0] += s_a[e] * mv.x;
-          pa[1] += s_a[e] * mv.y;
-          pb[0] += s_b[e] * mv.x;
-          pb[1] += s_b[e] * mv.y;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        acc[i][0] += part[i][0];
-        acc[i][1] += part[i][1];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      x[j + 1][i][0] = acc[i][0];
-      x[j + 1][i][1] = acc[i][1];
-    }
-  }
-  if (on) {
-    float* st = ws.seg_state + static_cast<int64_t>(pair) * n_seg * page;
-#pragma unroll
-    for (int j = 0; j < kMaxSegments; ++j) {
-      if (j >= ns) break;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        *reinterpret_cast<float2*>(&st[j * page + static_cast<int64_t>(8 * rb + r0 + i) * K + key]) =
-            float2{x[j][i][0], x[j][i][1]};
-    }
   }
 }
 
@@ -1326,7 +1329,7 @@ WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, b
   l.seg_sum = off;
   if (sm > 1) off = align256(off + static_cast<size_t>(pairs) * (sm - 1) * (V + K) * K * 4);
   l.seg_state = off;
-  if (sm > 1) off = align256(off + static_cast<size_t>(pairs) * sm * V * K * 4);
+  if (sm > 1) off = align256(off + static_cast<size_t>(pairs) * V * K * 4);
   l.total = off;
   return l;
 }
@@ -1365,8 +1368,9 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
   const int64_t pairs = static_cast<int64_t>(a.n_seqs) * a.H;
   const unsigned pair8 = static_cast<unsigned>((pairs + 7) / 8);
   // Chunk-parallel form where the scan would leave most compute units idle:
-  // n_seg segments per sequence, their maps (summary), the segments' initial
-  // states (combine), then every segment's scan at once.
+  // n_seg segments per sequence, their maps (summary), then every segment's
+  // scan at once, each chain first carrying the initial state through the maps
+  // of the segments before its own.
   int n_seg = 1, seg_len = 0;
   const int cap = segment_cap(pairs, V, !std::is_same<Tin, __bf16>::value);
   if (cap > 1) {
@@ -1382,12 +1386,8 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
       constexpr int NGA = (NSL + K / 16) / 4;
       hipLaunchKernelGGL((summary_kernel<K, V>), dim3(8 * NGA * (n_seg - 1) * pair8), dim3(320), 0, a.stream,
                          static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v), a.H, a.n_seqs, a.T_eq,
-                         ncs_eq, static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens,
-                         seg_len, n_seg, a.ws);
-      hipLaunchKernelGGL((combine_kernel<K, V>), dim3(8 * (V / 8) * pair8), dim3(256), 0,
-                         a.stream, a.H, a.n_seqs, a.T_eq, ncs_eq, static_cast<int>(a.total_tokens),
-                         static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0, a.pool, a.pool_slots, a.slots, seg_len,
-                         n_seg, a.ws);
+                         ncs_eq, static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0,
+                         a.pool, a.pool_slots, a.slots, seg_len, n_seg, a.ws);
     }
   }
   // Two chains per workgroup (sharing K, A' and the gates, on two SIMDs of a

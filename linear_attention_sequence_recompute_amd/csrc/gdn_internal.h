@@ -33,8 +33,9 @@ struct DecodeArgs {
 //   info [chunk] int4 {seq, first token, rows, 0} and seq_chunk0 [n_seqs + 1]:
 //        the chunk schedule of a packed (varlen) call
 //   seg_sum [pair][n_seg - 1][V + K][K] f32   chunk-parallel form: per segment,
-//        the affine map of the state, c^T rows then M^T rows
-//   seg_state [pair][n_seg][V][K] f32          the initial state of each segment
+//        the affine map of the state h -> M h + c: c^T rows [v][key], then M
+//        rows [key][m]
+//   seg_state [pair][V][K] f32                 a copy of the pair's initial state
 struct ChunkWs {
   uint8_t* af;
   uint8_t* pf;

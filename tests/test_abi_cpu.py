@@ -56,8 +56,8 @@ def test_workspace_bytes():
     per = b2 / ((4096 // 64 + 1) * 16)
     assert 24 * 1024 + 768 <= per < 26 * 1024
     # bf16 with 16 (sequence, head) pairs: room for the chunk-parallel form with 4
-    # segments: 3 segment maps ([V + K][K] f32) and 4 initial states ([V][K] f32) per pair
-    assert b1 - b2 == 16 * (3 * 256 * 128 + 4 * 128 * 128) * 4
+    # segments: 3 segment maps ([V + K][K] f32) and a copy of the initial state ([V][K] f32) per pair
+    assert b1 - b2 == 16 * (3 * 256 * 128 + 128 * 128) * 4
     # 256 pairs fill the GPU without segments: no such room
     per3 = b3 / ((60217 // 64 + 16) * 16)
     assert 24 * 1024 + 768 <= per3 < 26 * 1024
