@@ -3,7 +3,7 @@
 
 A step is one chunked forward pass (gdn_chunk_fwd: the prep kernel for
 recompute_w_u, then chunk_fwd_h fused with chunk_fwd_o, which at this shape runs
-in the chunk-parallel form: summary kernel, combine kernel, scan kernel) over
+in the chunk-parallel form: summary kernel, then scan kernel) over
 one batch of B=1, H=16, T=4096, K=V=128 bf16 inputs, already resident in device
 memory. The decode step (gdn_recurrent_step, N=256 requests,
 H=32, K=V=128, a 512-slot float32 state pool) is timed beside it in the same run
@@ -14,8 +14,8 @@ steps are plain calls. Per-kernel durations come from K further calls of
 gdn_chunk_fwd_profiled, which records HIP events on the library's stream around
 each launch (recording them inside the timed steps would add about 10 us per
 call); the roofline of the dominant part, chunk_fwd_h + chunk_fwd_o (the span of
-the summary, combine and scan kernels), is its algorithmic FLOPs per call over
-that duration.
+the summary and scan kernels), is its algorithmic FLOPs per call over that
+duration.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --only chunk|decode|copy --steps K   (profiling runs)
@@ -342,11 +342,11 @@ def main():
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": K, "chunk": C,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma",
-                     "kernel": "chunk_fwd_h fused with chunk_fwd_o: summary_kernel + combine_kernel + scan_kernel "
+                     "kernel": "chunk_fwd_h fused with chunk_fwd_o: summary_kernel + scan_kernel "
                                "(chunk-parallel form, 4 segments of 16 chunks)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic_for("summary_kernel", "combine_kernel", "scan_kernel"),
+                     "traffic": traffic_for("summary_kernel", "scan_kernel"),
                      "flops_per_launch": flops_ho, "avg_launch_us": scan_s * 1e6},
         "kernels_us": {"prep": res_c["prep_ms"]["mean"] * 1e3, "h_o": res_c["scan_ms"]["mean"] * 1e3,
                        "call": res_c["call_ms"]["mean"] * 1e3,

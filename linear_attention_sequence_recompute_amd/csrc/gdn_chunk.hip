@@ -540,8 +540,9 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, cons
   // permuted key order), split hi + lo; B operand = the state split. The map
   // rows come in batches of two tiles of one key block, kD batches in flight
   // (a ring of register sets); c_j is added last. From a zero initial state the
-  // first map is not needed: the state after segment 0 is c_0.
-  if (n_fold > 0) {
+  // first map is not needed: the state after segment 0 is c_0. (The
+  // chunk-parallel form runs for bf16 inputs only.)
+  if (std::is_same<Tin, __bf16>::value && n_fold > 0) {
     constexpr int NB = NKB * NKB;  // batches per map: NKB key blocks x (2 NKB tiles / 2)
     constexpr int kD = 4;
     static_assert(NB % kD == 0, "whole rings per map");
