@@ -1200,19 +1200,6 @@ __global__ __launch_bounds__(scan_threads<NCH>()) __attribute__((amdgpu_waves_pe
   } else if (wv == kProducer) {
     scan_producer<K, V, Tin, NCH>(sms, sq, q, k, v, H, ws);
   } else {
-    if (n_fold > 0) {
-      // The maps come from another kernel and are not in this XCD's L2 yet:
-      // the output waves, idle until the chains' first step, touch every
-      // 128-byte line of the pages the chains fold through (each of the NG
-      // workgroups of this (pair, segment) a share), so the chains' loads hit L2.
-      constexpr int kLines = (V + K) * K * 4 / 128;  // lines per page
-      const int lane = threadIdx.x & 63, ow = wv - 2;
-      uint32_t sink = 0;
-      for (int j = 0; j < n_fold; ++j)
-        for (int m = 64 * ow + lane; m * NG + grp < kLines; m += 128)
-          sink += __builtin_bit_cast(uint32_t, fold[j * static_cast<int64_t>(V + K) * K + 32 * (m * NG + grp)]);
-      asm volatile("" ::"v"(sink));
-    }
     if (wv == 2)
       scan_output<0, K, V, Tin, Tout, NCH>(sms, sq, q, o, H, scale, ws);
     else
