@@ -200,3 +200,61 @@ def decode_inputs(
     slots[mask] = active
     slots[pad_pos] = rng.choice(np.array([0, -1]), len(pad_pos))
     return DecodeInputs(q, k, v, a, beta, pool, slots, dtype)
+
+
+@dataclass
+class VerifyInputs:
+    q: np.ndarray          # [N, T, H, K]
+    k: np.ndarray
+    v: np.ndarray          # [N, T, H, V]
+    a: np.ndarray          # [N, T, H]
+    beta: np.ndarray
+    pool: np.ndarray       # [P, H, V, K]
+    slots: np.ndarray      # [N, C] int32
+    accepted: np.ndarray   # [N] int32
+    dtype: str
+
+
+def verify_inputs(
+    N: int,
+    T: int,
+    H: int,
+    K: int,
+    V: int,
+    pool_slots: int,
+    dtype: str = "bf16",
+    seed: int = 0,
+    cols: int = 0,
+    n_padding: int = 0,
+    n_nowrite: int = 0,
+    gate_shift: float = 2.0,
+) -> VerifyInputs:
+    """Draw one speculative-verify decode call: N requests of T tokens, a slot
+    table [N, C] (C = cols or T) whose positive entries are distinct slots drawn
+    from 1..pool_slots-1, and accepted counts uniform in [1, C]. ``n_padding``
+    requests get a source slot (column accepted - 1) of 0 or -1; ``n_nowrite``
+    other table entries of active requests (never their source) get 0 or -1."""
+    rng = np.random.default_rng(seed)
+    C = cols or T
+    if C < T:
+        raise ValueError("the slot table needs at least T columns")
+    q = _round(_unit_rows(rng, (N, T, H, K)), dtype)
+    k = _round(_unit_rows(rng, (N, T, H, K)), dtype)
+    v = _round(rng.standard_normal((N, T, H, V)), dtype)
+    beta = round_to_f32(_sigmoid(rng.standard_normal((N, T, H))))
+    a = round_to_f32(-_softplus(rng.standard_normal((N, T, H)) + gate_shift))
+    pool = round_to_f32(rng.normal(0.0, 0.1, (pool_slots, H, V, K)))
+    if N * C > pool_slots - 1:
+        raise ValueError("more table entries than usable pool slots")
+    slots = rng.choice(np.arange(1, pool_slots), N * C, replace=False).astype(np.int32).reshape(N, C)
+    accepted = rng.integers(1, C + 1, N).astype(np.int32)
+    pad = rng.choice(N, n_padding, replace=False) if n_padding else np.zeros(0, np.int64)
+    for b in pad:
+        slots[b, accepted[b] - 1] = rng.choice([0, -1])
+    active = np.setdiff1d(np.arange(N), pad)
+    cand = [(b, c) for b in active for c in range(C) if c != accepted[b] - 1]
+    if n_nowrite:
+        for i in rng.choice(len(cand), n_nowrite, replace=False):
+            b, c = cand[i]
+            slots[b, c] = rng.choice([0, -1])
+    return VerifyInputs(q, k, v, a, beta, pool, slots, accepted, dtype)

@@ -14,6 +14,8 @@ Functions (all float64 numpy):
   chunk_fwd_o with chunk size 64), exposing its intermediates.
 * ``*_varlen``       - the same over a packed token stream with sequence offsets.
 * ``decode_step``    - one recurrent step over a slot-indexed state pool.
+* ``decode_verify``  - T tokens per request (speculative verify) over that pool,
+  with per-token state writes.
 
 Every function is pinned by tests in ``tests/test_oracle_pins.py`` against closed
 forms, invariants and a hand-derived golden example; no function is "parity
@@ -26,5 +28,6 @@ from .gdn import (  # noqa: F401
     recurrent_fwd_varlen,
     chunked_fwd_varlen,
     decode_step,
+    decode_verify,
     unit_lower_inverse,
 )

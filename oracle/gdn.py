@@ -188,3 +188,40 @@ def decode_step(q, k, v, a, beta, pool, slots, scale=1.0):
         o[b] = ob[0]
         pool[slot] = S
     return o, pool
+
+
+def decode_verify(q, k, v, a, beta, pool, slots, accepted, scale=1.0):
+    """Speculative-verify decode: T tokens per request over a slot-indexed pool.
+
+    vLLM KdaSplit page, class docstring (``tokens`` q > 1): request b's T tokens
+    (rows b * T + t) run in order; its state comes from pool[slots[b, accepted[b]
+    - 1]], and the state after token t goes to pool[slots[b, t]] when that slot is
+    > 0. A request whose source slot is <= 0 (or whose accepted count is outside
+    [1, slot columns], a reading where the page is silent) is padding: its outputs
+    are zero and nothing is written. Each token is one step of ``recurrent_fwd``.
+
+    q, k: [N, T, H, K]; v: [N, T, H, V]; a, beta: [N, T, H]; pool: [P, H, V, K];
+    slots: [N, C] with C >= T; accepted: [N]. Returns (o [N, T, H, V], new_pool);
+    the input pool is not modified.
+    """
+    q, k, v, a, beta = map(_as64, (q, k, v, a, beta))
+    pool = _as64(pool).copy()
+    N, T, H, _ = q.shape
+    o = np.zeros((N, T, H, v.shape[-1]))
+    cols = slots.shape[1]
+    for b in range(N):
+        acc = int(accepted[b])
+        if not 1 <= acc <= cols:
+            continue
+        src = int(slots[b, acc - 1])
+        if src <= 0:
+            continue
+        S = pool[src].copy()
+        for t in range(T):
+            ot, S = recurrent_fwd(q[b, t:t + 1], k[b, t:t + 1], v[b, t:t + 1], a[b, t:t + 1],
+                                  beta[b, t:t + 1], scale=scale, S0=S)
+            o[b, t] = ot[0]
+            dst = int(slots[b, t])
+            if dst > 0:
+                pool[dst] = S
+    return o, pool

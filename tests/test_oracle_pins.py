@@ -14,9 +14,9 @@ import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
 
-from oracle import (chunked_fwd, chunked_fwd_varlen, decode_step, recurrent_fwd,
+from oracle import (chunked_fwd, chunked_fwd_varlen, decode_step, decode_verify, recurrent_fwd,
                     recurrent_fwd_varlen, unit_lower_inverse)
-from linear_attention_sequence_recompute_amd.workloads import chunk_inputs, decode_inputs
+from linear_attention_sequence_recompute_amd.workloads import chunk_inputs, decode_inputs, verify_inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_derived.json")
 
@@ -383,3 +383,79 @@ def test_pins_catch_chunk_mistakes(mutation):
     if rel(o2, o1) > 1e-8 or rel(S2, S1) > 1e-8:
         caught.append("recurrent_equals_chunked")
     assert caught, f"no pin caught the planted mistake {mutation!r}"
+
+
+# ------------------------------------------------ speculative-verify decode
+
+def _verify_pins(fn):
+    """Pins of a verify-decode implementation ``fn`` (the oracle's signature).
+    Each request's outputs and per-token written states are checked against the
+    chunked WY form (an independent algorithm) run over the request's first t + 1
+    tokens from the source slot; padding, unwritten slots and untouched pool
+    entries are checked exactly."""
+    vi = verify_inputs(N=6, T=5, H=2, K=8, V=6, pool_slots=64, dtype="f32", seed=9, cols=7,
+                       n_padding=2, n_nowrite=4, gate_shift=-4.0)
+    o, pool = fn(vi.q, vi.k, vi.v, vi.a, vi.beta, vi.pool, vi.slots, vi.accepted, scale=0.7)
+    written = set()
+    for b in range(6):
+        src = int(vi.slots[b, vi.accepted[b] - 1])
+        if src <= 0:
+            assert np.all(o[b] == 0), "padding request has nonzero output"
+            continue
+        for t in range(5):
+            ot, St = chunked_fwd(vi.q[b, :t + 1], vi.k[b, :t + 1], vi.v[b, :t + 1], vi.a[b, :t + 1],
+                                 vi.beta[b, :t + 1], scale=0.7, S0=vi.pool[src])
+            assert rel(o[b, t], ot[t]) < 1e-12, f"request {b} token {t}: output"
+            dst = int(vi.slots[b, t])
+            if dst > 0:
+                assert rel(pool[dst], St) < 1e-12, f"request {b} token {t}: written state"
+                written.add(dst)
+    for s in range(64):
+        if s not in written:
+            np.testing.assert_array_equal(pool[s], vi.pool[s])  # untouched, bit for bit
+
+
+def test_verify_decode_pins():
+    _verify_pins(decode_verify)
+
+
+def test_verify_decode_one_token_is_a_decode_step():
+    """T = 1, accepted = 1: the source and destination are slots[b, 0], one step."""
+    vi = verify_inputs(N=5, T=1, H=2, K=8, V=8, pool_slots=12, dtype="f32", seed=3, n_padding=1)
+    o, pool = decode_verify(vi.q, vi.k, vi.v, vi.a, vi.beta, vi.pool, vi.slots, vi.accepted, scale=0.5)
+    o1, pool1 = decode_step(vi.q[:, 0], vi.k[:, 0], vi.v[:, 0], vi.a[:, 0], vi.beta[:, 0], vi.pool,
+                            vi.slots[:, 0], scale=0.5)
+    np.testing.assert_array_equal(o[:, 0], o1)
+    np.testing.assert_array_equal(pool, pool1)
+
+
+def _verify_mutant(q, k, v, a, beta, pool, slots, accepted, scale=1.0, mutation=None):
+    pool = pool.astype(np.float64).copy()
+    N, T, H, _ = q.shape
+    o = np.zeros((N, T, H, v.shape[-1]))
+    for b in range(N):
+        acc = int(accepted[b])
+        src = int(slots[b, acc if mutation == "source_off_by_one" and acc < slots.shape[1] else acc - 1])
+        if src <= 0:
+            continue
+        S = pool[src].copy()
+        for t in range(T):
+            before = S.copy()
+            ot, S = recurrent_fwd(q[b, t:t + 1], k[b, t:t + 1], v[b, t:t + 1], a[b, t:t + 1],
+                                  beta[b, t:t + 1], scale=scale, S0=S)
+            o[b, t] = ot[0]
+            dst = int(slots[b, t])
+            if mutation == "write_before_update" and dst > 0:
+                pool[dst] = before
+            elif mutation == "write_ignores_padding_slot":
+                pool[abs(dst)] = S
+            elif dst > 0:
+                pool[dst] = S
+    return o, pool
+
+
+@pytest.mark.parametrize("mutation", ["source_off_by_one", "write_before_update", "write_ignores_padding_slot"])
+def test_verify_pins_catch_mistakes(mutation):
+    _verify_pins(lambda *a_, **k_: _verify_mutant(*a_, **k_, mutation=None))  # the clean copy passes
+    with pytest.raises(AssertionError):
+        _verify_pins(lambda *a_, **k_: _verify_mutant(*a_, **k_, mutation=mutation))
