@@ -44,6 +44,8 @@ CSRC = os.path.join(ROOT, "linear_attention_sequence_recompute_amd", "csrc")
 B, H, T, K, V, C = 1, 16, 4096, 128, 128, 64
 # decode workload: N=256 requests, H=32, K=V=128, pool of 512 slots
 DN, DH, DK, DV, DSLOTS = 256, 32, 128, 128, 512
+# speculative-verify decode: 96 requests x 4 tokens over the same pool shape
+VN, VT = 96, 4
 
 
 def log(*a):
@@ -235,6 +237,47 @@ def bench_decode(torch, api, hev, steps, warmup):
     return dict(wall_s=wall, kernel_ms=stats(ms), n_active=int((di.slots > 0).sum()))
 
 
+def verify_bytes(n_active: int, T: int) -> int:
+    """Algorithmic HBM bytes of one verify call: per active (request, head) the
+    source state is read once and T states are written; q, k, v, o in bf16 and
+    g, beta in fp32 for each token."""
+    per = (1 + T) * DV * DK * 4 + T * ((2 * DK + DV) * 2 + 2 * 4 + DV * 2)
+    return n_active * DH * per
+
+
+def bench_verify(torch, api, hev, steps, warmup):
+    """Speculative-verify decode: VN requests x VT tokens over the decode pool."""
+    from linear_attention_sequence_recompute_amd.workloads import verify_inputs
+
+    vi = verify_inputs(VN, VT, DH, DK, DV, DSLOTS, dtype="bf16", seed=8)
+    dev = torch.device("cuda")
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (vi.q, vi.k, vi.v))
+    g, b = (torch.from_numpy(x).float().to(dev) for x in (vi.a, vi.beta))
+    pool = torch.from_numpy(vi.pool).float().to(dev)
+    slots = torch.from_numpy(vi.slots).int().to(dev)
+    accepted = torch.from_numpy(vi.accepted).int().to(dev)
+    o = torch.empty(VN, VT, DH, DV, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        api.recurrent_verify(q, k, v, g, b, pool, slots, accepted, scale=DK ** -0.5, out=o, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [hev.create(2) for _ in range(steps)]
+    s = stream.cuda_stream
+    for i in range(steps):
+        hev.record(evs[i][0], s)
+        step()
+        hev.record(evs[i][1], s)
+    torch.cuda.synchronize()
+    ms = [hev.ms(e[0], e[1]) for e in evs]
+    for e in evs:
+        hev.destroy(e)
+    return dict(kernel_ms=stats(ms), n_active=VN)
+
+
 def bench_copy(torch, steps, nbytes=1 << 30):
     """A plain device copy of known size: the calibration kernel for PMC byte
     counters (FETCH_SIZE and WRITE_SIZE of this launch should read nbytes each)."""
@@ -281,7 +324,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "copy"], default="all")
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "verify", "copy"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -313,6 +356,11 @@ def main():
         log("decode: N=256 H=32 K=V=128 pool=512 ...")
         res_d = bench_decode(torch, api, hev, args.steps, args.warmup)
         log(json.dumps(res_d))
+    res_v = None
+    if args.only in ("all", "verify"):
+        log(f"verify decode: N={VN} T={VT} H=32 K=V=128 pool=512 ...")
+        res_v = bench_verify(torch, api, hev, args.steps, args.warmup)
+        log(json.dumps(res_v))
     if args.only != "all":
         return
 
@@ -360,6 +408,16 @@ def main():
                                 "frac": dec_gbs / PEAK_HBM_GBS, "traffic": traffic_for("recurrent_step_kernel"),
                                 "bytes_per_launch": dec_b}},
     }
+    ver_s = res_v["kernel_ms"]["mean"] / 1e3
+    ver_b = verify_bytes(res_v["n_active"], VT)
+    out["decode_verify"] = {
+        "workload": f"speculative-verify decode, {VN} requests x {VT} tokens, H=32, K=V=128, pool [512, 32, 128, 128] "
+                    "fp32 (source read once, a state written per token), bf16 q/k/v/o",
+        "value": ver_b / ver_s / 1e9, "unit": "GB/s", "avg_launch_us": ver_s * 1e6,
+        "tokens_per_s": VN * VT / ver_s,
+        "roofline": {"bound": "hbm", "achieved": ver_b / ver_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ver_b / ver_s / 1e9 / PEAK_HBM_GBS, "traffic": traffic_for("recurrent_verify_kernel"),
+                     "bytes_per_launch": ver_b}}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

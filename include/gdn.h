@@ -158,6 +158,39 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const
                               const int32_t* slots, void* o, int N, int H, int K, int V,
                               float scale, gdn_dtype in_dtype, gdn_dtype out_dtype, void* stream);
 
+/*
+ * Speculative-verify decode: T tokens per request (the vLLM KdaSplit page, class
+ * docstring, ``tokens`` q > 1, with its spec-cache semantics).
+ *
+ *  q, k        [N * T, H, K] in_dtype, rows b * T + t;  v [N * T, H, V] in_dtype
+ *  g, beta     [N * T, H] float32 raw log-gate a (<= 0) and write strength
+ *  state_pool  float32 [pool_slots, H, V, K]
+ *  slots       device int32 [N, slot_cols] (row-major), slot_cols >= T
+ *  accepted    device int32 [N]
+ *  o           [N * T, H, V] out_dtype
+ *
+ * Request b starts from pool[slots[b, accepted[b] - 1]] and runs its T tokens in
+ * order, each one step of gdn_recurrent_step (decay, delta-rule write, output from
+ * the updated state); the state after token t is stored to pool[slots[b, t]] if
+ * that slot is in [1, pool_slots). A request whose source slot is outside
+ * [1, pool_slots), or whose accepted count is outside [1, slot_cols], is padding:
+ * its T output rows are +0 and nothing is written. The source is read before any
+ * write of the request (so slots[b, accepted - 1] may be rewritten by it);
+ * positive slots written by different requests, and their sources, must be
+ * distinct.
+ *
+ * Returns GDN_EUNSUPPORTED for K or V outside {64, 128} or an unknown dtype;
+ * GDN_EINVAL for N < 0, T outside [1, 8], slot_cols < T, H outside [1, 65535],
+ * sizes whose grid would not fit, a NULL pointer, pool_slots <= 0 or a
+ * misaligned pointer; GDN_OK without launching for N == 0; GDN_EHIP if the launch
+ * fails.
+ */
+gdn_status gdn_recurrent_verify(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, float* state_pool, int64_t pool_slots,
+                                const int32_t* slots, int slot_cols, const int32_t* accepted, void* o,
+                                int N, int T, int H, int K, int V, float scale, gdn_dtype in_dtype,
+                                gdn_dtype out_dtype, void* stream);
+
 /* Static, human-readable name of a status code. Never NULL. */
 const char* gdn_status_string(gdn_status s);
 

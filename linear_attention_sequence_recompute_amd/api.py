@@ -158,3 +158,37 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     _lib.check(st, "gdn_recurrent_step")
     return out
 
+
+
+def recurrent_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                     state_pool: torch.Tensor, slots: torch.Tensor, accepted: torch.Tensor, *,
+                     scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+                     out: Optional[torch.Tensor] = None, stream=None):
+    """Speculative-verify decode (gdn_recurrent_verify): q, k [N, T, H, K]; v
+    [N, T, H, V]; g, beta [N, T, H] float32; state_pool [P, H, V, K] float32,
+    written in place at the per-token slots; slots [N, C] int32 (C >= T);
+    accepted [N] int32. Returns o [N, T, H, V]."""
+    N, T, H, K = q.shape
+    V = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    for name, t in (("g", g), ("beta", beta), ("state_pool", state_pool)):
+        _need(t, name, torch.float32)
+    _need(slots, "slots", torch.int32)
+    _need(accepted, "accepted", torch.int32)
+    if k.shape != q.shape or v.shape[:3] != (N, T, H) or g.shape != (N, T, H) or beta.shape != (N, T, H):
+        raise ValueError("inconsistent shapes of q, k, v, g, beta")
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, V, K):
+        raise ValueError("state_pool must be [P, H, V, K]")
+    if slots.dim() != 2 or slots.shape[0] != N or accepted.shape != (N,):
+        raise ValueError("slots must be [N, C] and accepted [N]")
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((N, T, H, V), dtype=out_dtype, device=q.device)
+    _need(out, "out", out_dtype)
+    st = _lib.lib().gdn_recurrent_verify(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), state_pool.shape[0], _ptr(slots),
+        slots.shape[1], _ptr(accepted), _ptr(out), N, T, H, K, V, float(K ** -0.5 if scale is None else scale),
+        _dt(q.dtype), _dt(out_dtype), _stream(stream))
+    _lib.check(st, "gdn_recurrent_verify")
+    return out

@@ -219,4 +219,46 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const
   return hip_status(gdn::launch_decode(a));
 }
 
+
+gdn_status gdn_recurrent_verify(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                float* state_pool, int64_t pool_slots, const int32_t* slots, int slot_cols,
+                                const int32_t* accepted, void* o, int N, int T, int H, int K, int V, float scale,
+                                gdn_dtype in_dtype, gdn_dtype out_dtype, void* stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !supported_dim(K) || !supported_dim(V))
+    return GDN_EUNSUPPORTED;
+  if (N < 0 || H <= 0 || H > 65535 || T < 1 || T > 8 || slot_cols < T) return GDN_EINVAL;
+  if (static_cast<int64_t>(N) * H * (V / 16) > INT32_MAX) return GDN_EINVAL;
+  if (static_cast<int64_t>(N) * T * H > INT32_MAX / 128) return GDN_EINVAL;
+  if (N == 0) return GDN_OK;
+  if (!q || !k || !v || !g || !beta || !state_pool || !slots || !accepted || !o || pool_slots <= 0)
+    return GDN_EINVAL;
+  if (!aligned(state_pool, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(slots, 4) || !aligned(accepted, 4))
+    return GDN_EINVAL;
+  const size_t in_b = dtype_bytes(in_dtype), out_b = dtype_bytes(out_dtype);
+  if (!aligned(q, in_b) || !aligned(k, in_b) || !aligned(v, in_b) || !aligned(o, out_b)) return GDN_EINVAL;
+
+  gdn::VerifyArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.pool = state_pool;
+  a.pool_slots = pool_slots;
+  a.slots = slots;
+  a.cols = slot_cols;
+  a.accepted = accepted;
+  a.o = o;
+  a.N = N;
+  a.T = T;
+  a.H = H;
+  a.K = K;
+  a.V = V;
+  a.scale = scale;
+  a.in_f32 = in_dtype == GDN_F32;
+  a.out_f32 = out_dtype == GDN_F32;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_verify(a));
+}
+
 }  // extern "C"

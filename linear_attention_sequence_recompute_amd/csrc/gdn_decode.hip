@@ -102,6 +102,124 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
   }
 }
 
+// Speculative verify (the KdaSplit class docstring, tokens q > 1): request b's T
+// tokens (rows b T + t) run in order from the state in slot[b, accepted[b] - 1];
+// the state after token t is stored to slot[b, t] when that slot is in (0,
+// pool_slots). A request whose source slot is not (or whose accepted count is
+// outside [1, cols]) is padding: zero outputs, no writes. The layout is the decode
+// step's; the state rows stay in registers across the tokens, whose inputs are
+// all loaded before the first update.
+constexpr int kMaxVerifyTokens = 8;
+
+template <int K, int V, typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void recurrent_verify_kernel(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ pool,
+    int64_t pool_slots, const int32_t* __restrict__ slots, int cols, const int32_t* __restrict__ accepted,
+    Tout* __restrict__ o, int T, int H, float scale) {
+  constexpr int LPR = K / 4;
+  constexpr int RPP = 256 / LPR;
+  constexpr int PASSES = kDecodeRows / RPP;
+  constexpr int NP = V / kDecodeRows;
+  const int per_req = H * NP;
+  const int b = blockIdx.x / per_req, h = (blockIdx.x % per_req) / NP, part = blockIdx.x % NP;
+  const int tid = threadIdx.x;
+  const int col = (tid % LPR) * 4;
+  const int rsub = tid / LPR;
+  const int row0 = part * kDecodeRows;
+  const int64_t page = static_cast<int64_t>(V) * K;
+  const int32_t* srow = slots + static_cast<int64_t>(b) * cols;
+  const int acc = accepted[b];
+  const int src = acc >= 1 && acc <= cols ? srow[acc - 1] : 0;
+  if (src <= 0 || src >= pool_slots) {  // padding: zero outputs, nothing written
+    if (tid < kDecodeRows)
+      for (int t = 0; t < T; ++t) store_out(o + ((static_cast<int64_t>(b) * T + t) * H + h) * V + row0 + tid, 0.f);
+    return;
+  }
+  const float* S = pool + (static_cast<int64_t>(src) * H + h) * page + static_cast<int64_t>(row0) * K;
+  f32x4 s[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p)
+    s[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (p * RPP + rsub) * K + col));
+
+  float kk[kMaxVerifyTokens][4], qq[kMaxVerifyTokens][4], vv[kMaxVerifyTokens][PASSES];
+  float decay[kMaxVerifyTokens], bt[kMaxVerifyTokens];
+  int dst[kMaxVerifyTokens];
+#pragma unroll
+  for (int t = 0; t < kMaxVerifyTokens; ++t) {
+    if (t < T) {
+      const int64_t tok = (static_cast<int64_t>(b) * T + t) * H + h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kk[t][e] = ld_in(k + tok * K + col + e);
+        qq[t][e] = scale * ld_in(q + tok * K + col + e);
+      }
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) vv[t][p] = ld_in(v + tok * V + row0 + p * RPP + rsub);
+      decay[t] = expf(g[tok]);
+      bt[t] = beta[tok];
+      dst[t] = srow[t];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kMaxVerifyTokens; ++t) {
+    if (t >= T) break;
+    const int64_t tok = (static_cast<int64_t>(b) * T + t) * H + h;
+    float dk[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      s[p] *= decay[t];
+      dk[p] = s[p][0] * kk[t][0] + s[p][1] * kk[t][1] + s[p][2] * kk[t][2] + s[p][3] * kk[t][3];
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) dk[p] = group_sum<LPR>(dk[p]);
+    float dq[PASSES];
+    float* D = dst[t] > 0 && dst[t] < pool_slots
+                   ? pool + (static_cast<int64_t>(dst[t]) * H + h) * page + static_cast<int64_t>(row0) * K
+                   : nullptr;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const float vn = bt[t] * (vv[t][p] - dk[p]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[p][e] = fmaf(kk[t][e], vn, s[p][e]);
+      dq[p] = s[p][0] * qq[t][0] + s[p][1] * qq[t][1] + s[p][2] * qq[t][2] + s[p][3] * qq[t][3];
+      if (D) __builtin_nontemporal_store(s[p], reinterpret_cast<f32x4*>(D + (p * RPP + rsub) * K + col));
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) dq[p] = group_sum<LPR>(dq[p]);
+    if (tid % LPR == 0) {
+      Tout* orow = o + tok * V + row0;
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) store_out(orow + p * RPP + rsub, dq[p]);
+    }
+  }
+}
+
+template <int K, int V, typename Tin, typename Tout>
+static hipError_t launch_verify_t(const VerifyArgs& a) {
+  const dim3 grid(static_cast<unsigned>(a.N) * a.H * (V / kDecodeRows));  // request slowest
+  hipLaunchKernelGGL((recurrent_verify_kernel<K, V, Tin, Tout>), grid, dim3(256), 0, a.stream,
+                     static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
+                     static_cast<const Tin*>(a.v), a.g, a.beta, a.pool, a.pool_slots, a.slots, a.cols,
+                     a.accepted, static_cast<Tout*>(a.o), a.T, a.H, a.scale);
+  return hipGetLastError();
+}
+
+template <int K, int V>
+static hipError_t launch_verify_kv(const VerifyArgs& a) {
+  if (a.in_f32) {
+    return a.out_f32 ? launch_verify_t<K, V, float, float>(a) : launch_verify_t<K, V, float, __bf16>(a);
+  }
+  return a.out_f32 ? launch_verify_t<K, V, __bf16, float>(a) : launch_verify_t<K, V, __bf16, __bf16>(a);
+}
+
+hipError_t launch_verify(const VerifyArgs& a) {
+  if (a.K == 128 && a.V == 128) return launch_verify_kv<128, 128>(a);
+  if (a.K == 128 && a.V == 64) return launch_verify_kv<128, 64>(a);
+  if (a.K == 64 && a.V == 128) return launch_verify_kv<64, 128>(a);
+  return launch_verify_kv<64, 64>(a);
+}
+
 template <int K, int V, typename Tin, typename Tout>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
   const dim3 grid(static_cast<unsigned>(a.N) * a.H * (V / kDecodeRows));  // request slowest

@@ -21,6 +21,21 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
+struct VerifyArgs {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  float* pool;
+  int64_t pool_slots;
+  const int32_t* slots;  // [N, cols]
+  int cols;
+  const int32_t* accepted;  // [N]
+  void* o;
+  int N, T, H, K, V;
+  float scale;
+  bool in_f32, out_f32;
+  hipStream_t stream;
+};
+
 // Chunk intermediates written by the prep kernel and read by the scan kernel.
 // A fragment is stored as planes of [64 lanes][16 bytes] (see Prec in
 // gdn_common.h: two planes for a computed operand). "ch" = chunk * H + head.
@@ -79,6 +94,7 @@ WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, b
 ChunkWs carve_workspace(const WsLayout& l, void* base);
 
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_verify(const VerifyArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 
 }  // namespace gdn

@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
-                                         "gdn_chunk_fwd_profiled", "gdn_recurrent_step", "gdn_status_string"}
+                                         "gdn_chunk_fwd_profiled", "gdn_recurrent_step",
+                                         "gdn_recurrent_verify", "gdn_status_string"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -146,3 +147,30 @@ def test_recurrent_step_validation():
 def test_recurrent_step_grid_limit():
     # one workgroup per 16 state rows of each (request, head) must fit a 1-D grid
     assert _step(N=1 << 20, H=4096, V=128) == _lib.GDN_EINVAL
+
+
+def _verify(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, pool=FAKE, pool_slots=64, slots=FAKE, cols=4,
+             accepted=FAKE, o=FAKE, N=4, T=4, H=2, K=128, V=128, scale=1.0, in_dt=BF16, out_dt=BF16, stream=None)
+    a.update(kw)
+    return _lib.lib().gdn_recurrent_verify(a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["pool_slots"],
+                                           a["slots"], a["cols"], a["accepted"], a["o"], a["N"], a["T"], a["H"],
+                                           a["K"], a["V"], a["scale"], a["in_dt"], a["out_dt"], a["stream"])
+
+
+def test_recurrent_verify_validation():
+    E = _lib
+    assert _verify(K=32) == E.GDN_EUNSUPPORTED
+    assert _verify(in_dt=4) == E.GDN_EUNSUPPORTED
+    assert _verify(T=0) == E.GDN_EINVAL
+    assert _verify(T=9, cols=9) == E.GDN_EINVAL
+    assert _verify(cols=3) == E.GDN_EINVAL  # fewer slot columns than tokens
+    assert _verify(N=-1) == E.GDN_EINVAL
+    assert _verify(H=0) == E.GDN_EINVAL
+    assert _verify(N=0) == E.GDN_OK
+    assert _verify(accepted=None) == E.GDN_EINVAL
+    assert _verify(slots=None) == E.GDN_EINVAL
+    assert _verify(pool_slots=0) == E.GDN_EINVAL
+    assert _verify(accepted=FAKE + 2) == E.GDN_EINVAL
+    assert _verify(q=FAKE + 1) == E.GDN_EINVAL
+    assert _verify(N=1 << 20, H=4096) == E.GDN_EINVAL  # grid limit

@@ -13,7 +13,8 @@ import torch
 
 import oracle
 from linear_attention_sequence_recompute_amd import api
-from linear_attention_sequence_recompute_amd.workloads import chunk_inputs, decode_inputs, varlen_lengths
+from linear_attention_sequence_recompute_amd.workloads import (chunk_inputs, decode_inputs, varlen_lengths,
+                                                              verify_inputs)
 from tests.gpu_util import TORCH_DT, bf16_rne, dev, host, max_err_over_rms
 
 pytestmark = pytest.mark.gpu
@@ -393,6 +394,71 @@ def test_decode_out_of_range_slot_is_padding():
     assert torch.all(o[3] == 0) and torch.all(o[5] == 0)
     keep = [s for s in range(16) if s not in set(di.slots[[0, 1, 2, 4, 6, 7]].tolist())]
     assert torch.equal(pool[keep], pool0[keep])
+
+
+# ----------------------------------------------------- speculative verify
+
+def run_verify(vi, scale, out_dtype, pool_dev):
+    dt = TORCH_DT[vi.dtype]
+    o = api.recurrent_verify(dev(vi.q, dt), dev(vi.k, dt), dev(vi.v, dt), dev(vi.a), dev(vi.beta), pool_dev,
+                             dev(vi.slots, torch.int32), dev(vi.accepted, torch.int32), scale=scale,
+                             out_dtype=TORCH_DT[out_dtype])
+    torch.cuda.synchronize()
+    return o
+
+
+def check_verify(vi, scale, label):
+    """f32 outputs and written states vs the oracle; padding requests +0; slots
+    not written bit-identical; bf16 outputs == RNE(f32 outputs)."""
+    tol = TOL[vi.dtype]
+    pool0 = dev(vi.pool)
+    p32 = pool0.clone()
+    o32 = run_verify(vi, scale, "f32", p32)
+    p16 = pool0.clone()
+    o16 = run_verify(vi, scale, "bf16", p16)
+    assert torch.equal(o16, bf16_rne(o32)), f"{label}: bf16 output is not RNE of the f32 output"
+    assert torch.equal(p16, p32), f"{label}: written states depend on the output dtype"
+    o_ref, pool_ref = oracle.decode_verify(vi.q, vi.k, vi.v, vi.a, vi.beta, vi.pool, vi.slots, vi.accepted,
+                                           scale=scale)
+    N, T = vi.q.shape[:2]
+    cols = vi.slots.shape[1]
+    o_h = host(o32)
+    active, written = [], set()
+    for b in range(N):
+        acc = int(vi.accepted[b])
+        src = int(vi.slots[b, acc - 1]) if 1 <= acc <= cols else 0
+        if src <= 0:
+            assert bool((o32[b].view(torch.int32) == 0).all()), f"{label}: padding request {b} output is not +0"
+            continue
+        active.append(b)
+        written.update(int(x) for x in vi.slots[b, :T] if x > 0)
+    eo = max_err_over_rms(o_h[active], o_ref[active])
+    pool_h = host(p32)
+    es = max(max_err_over_rms(pool_h[s], pool_ref[s]) for s in written) if written else 0.0
+    for s in range(vi.pool.shape[0]):
+        if s not in written:
+            assert torch.equal(p32[s], pool0[s]), f"{label}: slot {s} was written"
+    _print(f"[verify {label}] max|do|/rms={eo:.3e} max|dS|/rms={es:.3e} tol={tol}")
+    assert eo <= tol and es <= tol
+
+
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_verify_small(K, V, dtype, T):
+    """Speculative verify: 6 requests (one padding), T tokens each, a slot table
+    wider than T with some non-positive entries (not written), long-memory gates."""
+    vi = verify_inputs(N=6, T=T, H=2, K=K, V=V, pool_slots=64, dtype=dtype, seed=70 + T + K + V, cols=T + 2,
+                       n_padding=1, n_nowrite=2, gate_shift=-4.0)
+    check_verify(vi, K ** -0.5, f"K={K} V={V} {dtype} T={T}")
+
+
+def test_verify_config_full():
+    """96 requests x 4 tokens, H=32, K=V=128, 512-slot pool (the timed shape), 8
+    padding requests and 16 unwritten table entries; every output and state."""
+    vi = verify_inputs(N=96, T=4, H=32, K=128, V=128, pool_slots=512, dtype="bf16", seed=7, n_padding=8,
+                       n_nowrite=16)
+    check_verify(vi, 128 ** -0.5, "N96 T4 H32")
 
 
 def test_graph_capture_replays_match_eager():
