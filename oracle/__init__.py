@@ -16,6 +16,8 @@ Functions (all float64 numpy):
 * ``decode_step``    - one recurrent step over a slot-indexed state pool.
 * ``decode_verify``  - T tokens per request (speculative verify) over that pool,
   with per-token state writes.
+* ``fp8_quant``      - group quantisation to FP8 E4M3 (``oracle/fp8.py``), with
+  ``e4m3_encode`` / ``e4m3_decode``.
 
 Every function is pinned by tests in ``tests/test_oracle_pins.py`` against closed
 forms, invariants and a hand-derived golden example; no function is "parity
@@ -31,3 +33,4 @@ from .gdn import (  # noqa: F401
     decode_verify,
     unit_lower_inverse,
 )
+from .fp8 import e4m3_decode, e4m3_encode, fp8_quant  # noqa: F401
