@@ -46,6 +46,8 @@ B, H, T, K, V, C = 1, 16, 4096, 128, 128, 64
 DN, DH, DK, DV, DSLOTS = 256, 32, 128, 128, 512
 # speculative-verify decode: 96 requests x 4 tokens over the same pool shape
 VN, VT = 96, 4
+# fp8 group quantisation: a [16384, 4096] float32 activation matrix, groups of 128
+QR, QC, QG = 16384, 4096, 128
 
 
 def log(*a):
@@ -278,6 +280,34 @@ def bench_verify(torch, api, hev, steps, warmup):
     return dict(kernel_ms=stats(ms), n_active=VN)
 
 
+def bench_fp8(torch, api, hev, steps, warmup):
+    """fp8 group quantisation of a [QR, QC] float32 activation matrix, groups of QG."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev).manual_seed(9)
+    x = torch.randn(QR, QC, device=dev, generator=g)
+    codes = torch.empty(QR, QC, dtype=torch.uint8, device=dev)
+    scales = torch.empty(QR, QC // QG, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        api.fp8_quant(x, QG, codes=codes, scales=scales, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [hev.create(2) for _ in range(steps)]
+    s = stream.cuda_stream
+    for i in range(steps):
+        hev.record(evs[i][0], s)
+        step()
+        hev.record(evs[i][1], s)
+    torch.cuda.synchronize()
+    ms = [hev.ms(e[0], e[1]) for e in evs]
+    for e in evs:
+        hev.destroy(e)
+    return dict(kernel_ms=stats(ms))
+
+
 def bench_copy(torch, steps, nbytes=1 << 30):
     """A plain device copy of known size: the calibration kernel for PMC byte
     counters (FETCH_SIZE and WRITE_SIZE of this launch should read nbytes each)."""
@@ -324,7 +354,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "verify", "copy"], default="all")
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "verify", "fp8", "copy"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -361,6 +391,11 @@ def main():
         log(f"verify decode: N={VN} T={VT} H=32 K=V=128 pool=512 ...")
         res_v = bench_verify(torch, api, hev, args.steps, args.warmup)
         log(json.dumps(res_v))
+    res_q = None
+    if args.only in ("all", "fp8"):
+        log(f"fp8 quant: [{QR}, {QC}] float32, groups of {QG} ...")
+        res_q = bench_fp8(torch, api, hev, args.steps, args.warmup)
+        log(json.dumps(res_q))
     if args.only != "all":
         return
 
@@ -418,6 +453,15 @@ def main():
         "roofline": {"bound": "hbm", "achieved": ver_b / ver_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": ver_b / ver_s / 1e9 / PEAK_HBM_GBS, "traffic": traffic_for("recurrent_verify_kernel"),
                      "bytes_per_launch": ver_b}}
+    q_s = res_q["kernel_ms"]["mean"] / 1e3
+    q_b = QR * QC * (4 + 1) + QR * (QC // QG) * 4
+    out["fp8_quant"] = {
+        "workload": f"fp8 group quantisation, [{QR}, {QC}] float32 activations, groups of {QG}, E4M3 codes + "
+                    "float32 scales",
+        "value": q_b / q_s / 1e9, "unit": "GB/s", "avg_launch_us": q_s * 1e6,
+        "roofline": {"bound": "hbm", "achieved": q_b / q_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": q_b / q_s / 1e9 / PEAK_HBM_GBS, "traffic": traffic_for("fp8_quant_kernel"),
+                     "bytes_per_launch": q_b}}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

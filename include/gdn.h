@@ -191,6 +191,28 @@ gdn_status gdn_recurrent_verify(const void* q, const void* k, const void* v, con
                                 int N, int T, int H, int K, int V, float scale, gdn_dtype in_dtype,
                                 gdn_dtype out_dtype, void* stream);
 
+/*
+ * FP8 group quantisation (the WarpDrive page, kernel 1, fp8_quant).
+ *
+ *  x       float32 [rows, cols], row-major, 16-byte aligned; finite values
+ *  codes   uint8 [rows, cols] (E4M3 "fn": sign, 4 exponent bits with bias 7,
+ *          3 mantissa bits, largest finite 448), 4-byte aligned
+ *  scales  float32 [rows, cols / group]
+ *  group   64 or 128 consecutive elements of a row
+ *
+ * Per group: scale = absmax / 448 (float32); each element is divided by scale
+ * (float32), clamped to [-448, 448] and rounded to the nearest E4M3 value, ties to
+ * even. A group whose absmax is 0 gets scale 0 and codes 0. x * scale of the
+ * decoded codes approximates x to half an E4M3 unit in the last place.
+ *
+ * Returns GDN_EUNSUPPORTED for a group other than 64 or 128; GDN_EINVAL for
+ * negative sizes, cols not a multiple of group, sizes whose grid would not fit,
+ * a NULL or misaligned pointer; GDN_OK without launching when there is nothing
+ * to do; GDN_EHIP if the launch fails.
+ */
+gdn_status gdn_fp8_quant(const float* x, void* codes, float* scales, int64_t rows, int64_t cols,
+                         int group, void* stream);
+
 /* Static, human-readable name of a status code. Never NULL. */
 const char* gdn_status_string(gdn_status s);
 

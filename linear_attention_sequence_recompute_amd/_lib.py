@@ -30,6 +30,7 @@ SIGNATURES = {
     "gdn_recurrent_step": (_I, [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "gdn_recurrent_verify": (_I, [_P, _P, _P, _P, _P, _P, _I64, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
                                   _P]),
+    "gdn_fp8_quant": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
     "gdn_status_string": (ctypes.c_char_p, [_I]),
 }
 

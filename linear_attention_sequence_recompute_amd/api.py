@@ -192,3 +192,22 @@ def recurrent_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
         _dt(q.dtype), _dt(out_dtype), _stream(stream))
     _lib.check(st, "gdn_recurrent_verify")
     return out
+
+
+def fp8_quant(x: torch.Tensor, group: int = 128, *, codes: Optional[torch.Tensor] = None,
+              scales: Optional[torch.Tensor] = None, stream=None):
+    """FP8 group quantisation (gdn_fp8_quant): x float32 [..., C] with C a multiple
+    of ``group`` (64 or 128). Returns (codes uint8 [..., C] holding E4M3 values,
+    scales float32 [..., C / group])."""
+    _need(x, "x", torch.float32)
+    C = x.shape[-1]
+    rows = x.numel() // C if C else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((*x.shape[:-1], C // group), dtype=torch.float32, device=x.device)
+    _need(codes, "codes", torch.uint8)
+    _need(scales, "scales", torch.float32)
+    st = _lib.lib().gdn_fp8_quant(_ptr(x), _ptr(codes), _ptr(scales), rows, C, group, _stream(stream))
+    _lib.check(st, "gdn_fp8_quant")
+    return codes, scales

@@ -2,6 +2,7 @@
 // workspace carving and the launch sequence. Declarations and contracts are in
 // include/gdn.h.
 #include <limits.h>
+#include <stdint.h>
 
 #include "gdn.h"
 #include "gdn_internal.h"
@@ -259,6 +260,28 @@ gdn_status gdn_recurrent_verify(const void* q, const void* k, const void* v, con
   a.out_f32 = out_dtype == GDN_F32;
   a.stream = static_cast<hipStream_t>(stream);
   return hip_status(gdn::launch_verify(a));
+}
+
+
+gdn_status gdn_fp8_quant(const float* x, void* codes, float* scales, int64_t rows, int64_t cols, int group,
+                         void* stream) {
+  if (group != 64 && group != 128) return GDN_EUNSUPPORTED;
+  if (rows < 0 || cols < 0 || cols % group != 0) return GDN_EINVAL;
+  if (cols > 0 && rows > INT64_MAX / cols) return GDN_EINVAL;
+  const int64_t n_groups = rows * (cols / group);
+  // one workgroup per 32 (group 128) or 64 (group 64) groups in a 1-D grid
+  if (n_groups / (group == 128 ? 32 : 64) >= INT32_MAX) return GDN_EINVAL;
+  if (n_groups == 0) return GDN_OK;
+  if (!x || !codes || !scales) return GDN_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(scales, 4)) return GDN_EINVAL;
+  gdn::Fp8Args a{};
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  a.n_groups = n_groups;
+  a.group = group;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_fp8_quant(a));
 }
 
 }  // extern "C"

@@ -36,6 +36,15 @@ struct VerifyArgs {
   hipStream_t stream;
 };
 
+struct Fp8Args {
+  const float* x;     // [n_groups * group] float32
+  void* codes;        // [n_groups * group] uint8 (E4M3)
+  float* scales;      // [n_groups]
+  int64_t n_groups;
+  int group;          // 64 or 128
+  hipStream_t stream;
+};
+
 // Chunk intermediates written by the prep kernel and read by the scan kernel.
 // A fragment is stored as planes of [64 lanes][16 bytes] (see Prec in
 // gdn_common.h: two planes for a computed operand). "ch" = chunk * H + head.
@@ -95,6 +104,7 @@ ChunkWs carve_workspace(const WsLayout& l, void* base);
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_verify(const VerifyArgs& a);
+hipError_t launch_fp8_quant(const Fp8Args& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 
 }  // namespace gdn

@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
                                          "gdn_chunk_fwd_profiled", "gdn_recurrent_step",
-                                         "gdn_recurrent_verify", "gdn_status_string"}
+                                         "gdn_recurrent_verify", "gdn_fp8_quant", "gdn_status_string"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -174,3 +174,21 @@ def test_recurrent_verify_validation():
     assert _verify(accepted=FAKE + 2) == E.GDN_EINVAL
     assert _verify(q=FAKE + 1) == E.GDN_EINVAL
     assert _verify(N=1 << 20, H=4096) == E.GDN_EINVAL  # grid limit
+
+
+def _fp8(**kw):
+    a = dict(x=FAKE, codes=FAKE, scales=FAKE, rows=4, cols=256, group=128, stream=None)
+    a.update(kw)
+    return _lib.lib().gdn_fp8_quant(a["x"], a["codes"], a["scales"], a["rows"], a["cols"], a["group"], a["stream"])
+
+
+def test_fp8_quant_validation():
+    E = _lib
+    assert _fp8(group=32) == E.GDN_EUNSUPPORTED
+    assert _fp8(cols=200) == E.GDN_EINVAL       # not a multiple of the group
+    assert _fp8(rows=-1) == E.GDN_EINVAL
+    assert _fp8(rows=0) == E.GDN_OK
+    assert _fp8(x=None) == E.GDN_EINVAL
+    assert _fp8(x=FAKE + 4) == E.GDN_EINVAL     # x must be 16-byte aligned
+    assert _fp8(codes=FAKE + 2) == E.GDN_EINVAL
+    assert _fp8(rows=1 << 40, cols=1 << 20) == E.GDN_EINVAL  # grid limit

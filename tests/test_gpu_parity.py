@@ -461,6 +461,65 @@ def test_verify_config_full():
     check_verify(vi, 128 ** -0.5, "N96 T4 H32")
 
 
+# ------------------------------------------------------- fp8 quantisation
+
+def _fp8_input(rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-20, 20, (rows, 1)))).astype(np.float32)
+    x[::7, : cols // 2] = 0.0                       # all-zero groups
+    x[1::5, 3] = -0.0                               # negative zeros
+    x[rows // 2, 5] = np.float32(1e-40)             # a float32 subnormal
+    return x
+
+
+@pytest.mark.parametrize("group", [64, 128])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (37, 384), (300, 1024)])
+def test_fp8_quant_bit_exact(group, rows, cols):
+    """Codes and scales equal the oracle's bit for bit (several workgroups and a
+    ragged last one, zero groups, signed zeros, subnormal inputs)."""
+    x = _fp8_input(rows, cols, seed=rows + cols + group)
+    codes, scales = api.fp8_quant(dev(x), group)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.fp8_quant(x, group)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+    np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_fp8_quant_every_code_and_tie():
+    """Groups whose absmax is 448 have scale 1, so the quotients are the inputs:
+    every finite E4M3 value and every midpoint between neighbours (ties, which
+    round to the even code) goes through the conversion and must give the
+    oracle's code."""
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    vals = np.sort(oracle.e4m3_decode(finite)).astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2
+    body = np.concatenate([vals, mids]).astype(np.float32)
+    groups = -(-len(body) // 127)
+    x = np.zeros((groups, 128), np.float32)
+    x[:, 0] = 448.0
+    x[:, 1:].flat[:len(body)] = body
+    codes, scales = api.fp8_quant(dev(x.reshape(1, -1)), 128)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.fp8_quant(x.reshape(1, -1), 128)
+    assert np.all(s_ref == 1.0)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+
+
+def test_fp8_quant_config_sampled():
+    """The timed shape, [16384, 4096] float32 with groups of 128: 512 sampled rows
+    bit-exact against the oracle."""
+    rows, cols = 16384, 4096
+    xd = torch.randn(rows, cols, device="cuda") * torch.exp2(torch.randint(-8, 8, (rows, 1), device="cuda").float())
+    codes, scales = api.fp8_quant(xd, 128)
+    torch.cuda.synchronize()
+    pick = np.random.default_rng(5).choice(rows, 512, replace=False)
+    x = xd[torch.from_numpy(pick).cuda()].cpu().numpy()
+    c_ref, s_ref = oracle.fp8_quant(x, 128)
+    np.testing.assert_array_equal(codes[torch.from_numpy(pick).cuda()].cpu().numpy(), c_ref)
+    np.testing.assert_array_equal(scales[torch.from_numpy(pick).cuda()].cpu().numpy().view(np.uint32),
+                                  s_ref.view(np.uint32))
+
+
 def test_graph_capture_replays_match_eager():
     """A chunked call and a decode step captured in one HIP graph: three replays,
     with eager work between them, give the eager results bit for bit (the chunked
