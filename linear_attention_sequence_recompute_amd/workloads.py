@@ -258,3 +258,10 @@ def verify_inputs(
             b, c = cand[i]
             slots[b, c] = rng.choice([0, -1])
     return VerifyInputs(q, k, v, a, beta, pool, slots, accepted, dtype)
+
+
+def channel_log_decay(shape, seed, shift=2.0):
+    """Per-key-channel log-decays -softplus(N(0, 1) + shift), float32 (the scalar
+    gate's distribution, drawn independently for every channel)."""
+    rng = np.random.default_rng(seed)
+    return round_to_f32(-_softplus(rng.standard_normal(shape) + shift))

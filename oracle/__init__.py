@@ -16,6 +16,8 @@ Functions (all float64 numpy):
 * ``decode_step``    - one recurrent step over a slot-indexed state pool.
 * ``decode_verify``  - T tokens per request (speculative verify) over that pool,
   with per-token state writes.
+* ``recurrent_fwd_kda`` / ``decode_step_kda`` - the rule with a decay per key
+  channel (KdaSplit), per token and as a decode step over the pool.
 * ``fp8_quant``      - group quantisation to FP8 E4M3 (``oracle/fp8.py``), with
   ``e4m3_encode`` / ``e4m3_decode``.
 
@@ -31,6 +33,8 @@ from .gdn import (  # noqa: F401
     chunked_fwd_varlen,
     decode_step,
     decode_verify,
+    decode_step_kda,
+    recurrent_fwd_kda,
     unit_lower_inverse,
 )
 from .fp8 import e4m3_decode, e4m3_encode, fp8_quant  # noqa: F401

@@ -225,3 +225,47 @@ def decode_verify(q, k, v, a, beta, pool, slots, accepted, scale=1.0):
             if dst > 0:
                 pool[dst] = S
     return o, pool
+
+
+def recurrent_fwd_kda(q, k, v, g, beta, scale=1.0, S0=None):
+    """Delta rule with a decay per key channel (the vLLM KdaSplit page, method
+    ``update``: every state element of key column e is multiplied by that column's
+    decay, then the same delta-rule write and query dot as ``recurrent_fwd``):
+
+        S <- S diag(exp(g_t))          (g_t in R^K, the per-channel log-decay)
+        delta = beta_t (v_t - S k_t);  S <- S + delta k_t^T;  o_t = S (s q_t)
+
+    q, k, g: [T, H, K]; v: [T, H, V]; beta: [T, H]; S0: [H, V, K] or None.
+    Returns (o [T, H, V], S_T [H, V, K]).
+    """
+    q, k, v, g, beta = map(_as64, (q, k, v, g, beta))
+    T, H, K = q.shape
+    V = v.shape[-1]
+    S = np.zeros((H, V, K)) if S0 is None else _as64(S0).copy()
+    o = np.zeros((T, H, V))
+    for t in range(T):
+        S *= np.exp(g[t])[:, None, :]
+        dot = np.einsum("hvk,hk->hv", S, k[t])
+        delta = beta[t][:, None] * (v[t] - dot)
+        S += delta[:, :, None] * k[t][:, None, :]
+        o[t] = np.einsum("hvk,hk->hv", S, scale * q[t])
+    return o, S
+
+
+def decode_step_kda(q, k, v, g, beta, pool, slots, scale=1.0):
+    """``decode_step`` with a per-key-channel log-decay g [N, H, K]: one step of
+    ``recurrent_fwd_kda`` per active row over the slot-indexed pool (slot <= 0 is
+    padding: zero output, nothing written)."""
+    q, k, v, g, beta = map(_as64, (q, k, v, g, beta))
+    pool = _as64(pool).copy()
+    N, H, _ = q.shape
+    o = np.zeros((N, H, v.shape[-1]))
+    for b in range(N):
+        slot = int(slots[b])
+        if slot <= 0:
+            continue
+        ob, S = recurrent_fwd_kda(q[b:b + 1], k[b:b + 1], v[b:b + 1], g[b:b + 1], beta[b:b + 1],
+                                  scale=scale, S0=pool[slot])
+        o[b] = ob[0]
+        pool[slot] = S
+    return o, pool

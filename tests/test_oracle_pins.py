@@ -14,9 +14,10 @@ import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
 
-from oracle import (chunked_fwd, chunked_fwd_varlen, decode_step, decode_verify, recurrent_fwd,
-                    recurrent_fwd_varlen, unit_lower_inverse)
-from linear_attention_sequence_recompute_amd.workloads import chunk_inputs, decode_inputs, verify_inputs
+from oracle import (chunked_fwd, chunked_fwd_varlen, decode_step, decode_step_kda, decode_verify, recurrent_fwd,
+                    recurrent_fwd_kda, recurrent_fwd_varlen, unit_lower_inverse)
+from linear_attention_sequence_recompute_amd.workloads import (channel_log_decay, chunk_inputs, decode_inputs,
+                                                              verify_inputs)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_derived.json")
 
@@ -459,3 +460,97 @@ def test_verify_pins_catch_mistakes(mutation):
     _verify_pins(lambda *a_, **k_: _verify_mutant(*a_, **k_, mutation=None))  # the clean copy passes
     with pytest.raises(AssertionError):
         _verify_pins(lambda *a_, **k_: _verify_mutant(*a_, **k_, mutation=mutation))
+
+
+# -------------------------------------------- per-key-channel decay (KDA)
+
+def test_kda_uniform_channels_is_the_scalar_rule():
+    q, k, v, a, b, S0 = _inputs(40, K=16, V=12, seed=11, shift=-4.0)
+    g = np.repeat(a[:, :, None], 16, axis=2)
+    o1, S1 = recurrent_fwd(q, k, v, a, b, scale=0.5, S0=S0)
+    o2, S2 = recurrent_fwd_kda(q, k, v, g, b, scale=0.5, S0=S0)
+    assert rel(o2, o1) < 1e-14 and rel(S2, S1) < 1e-14
+
+
+def _kda_closed_form_checks(fn):
+    """beta = 0: each key column decays by its own cumulative gate; basis keys:
+    each column is an exponential moving average written only under its own key."""
+    T, H, K, V = 30, 2, 8, 5
+    rng = np.random.default_rng(12)
+    g = channel_log_decay((T, H, K), seed=13, shift=-3.0)
+    q = rng.standard_normal((T, H, K))
+    v = rng.standard_normal((T, H, V))
+    S0 = rng.standard_normal((H, V, K))
+    # beta = 0
+    kk = rng.standard_normal((T, H, K))
+    o, S = fn(q, kk, v, g, np.zeros((T, H)), scale=0.7, S0=S0)
+    G = np.cumsum(g, axis=0)
+    assert rel(S, S0 * np.exp(G[-1])[:, None, :]) < 1e-12
+    for t in range(T):
+        St = S0 * np.exp(G[t])[:, None, :]
+        assert rel(o[t], np.einsum("hvk,hk->hv", St, 0.7 * q[t])) < 1e-12
+    # basis keys: column i_t gets (1 - beta) col + beta v after every column decays
+    idx = rng.integers(0, K, (T, H))
+    kb = np.zeros((T, H, K))
+    for t in range(T):
+        kb[t, np.arange(H), idx[t]] = 1.0
+    beta = rng.uniform(0.1, 0.9, (T, H))
+    o, S = fn(q, kb, v, g, beta, scale=1.0, S0=S0)
+    M = S0.copy()
+    for t in range(T):
+        M = M * np.exp(g[t])[:, None, :]
+        for h in range(H):
+            i = idx[t, h]
+            M[h, :, i] = (1 - beta[t, h]) * M[h, :, i] + beta[t, h] * v[t, h]
+        assert rel(o[t], np.einsum("hvk,hk->hv", M, q[t])) < 1e-12
+    assert rel(S, M) < 1e-12
+
+
+def test_kda_closed_forms():
+    _kda_closed_form_checks(recurrent_fwd_kda)
+
+
+def test_kda_decode_step_is_one_token_and_padding():
+    di = decode_inputs(N=10, H=2, K=8, V=8, pool_slots=16, dtype="f32", seed=14, n_padding=3)
+    g = channel_log_decay((10, 2, 8), seed=15)
+    o, pool = decode_step_kda(di.q, di.k, di.v, g, di.beta, di.pool, di.slots, scale=0.4)
+    used = set()
+    for b in range(10):
+        s = int(di.slots[b])
+        if s <= 0:
+            assert np.all(o[b] == 0)
+            continue
+        used.add(s)
+        ob, S = recurrent_fwd_kda(di.q[b:b + 1], di.k[b:b + 1], di.v[b:b + 1], g[b:b + 1], di.beta[b:b + 1],
+                                  scale=0.4, S0=di.pool[s])
+        np.testing.assert_array_equal(o[b], ob[0])
+        np.testing.assert_array_equal(pool[s], S)
+    for s in range(16):
+        if s not in used:
+            np.testing.assert_array_equal(pool[s], di.pool[s])
+
+
+def _kda_mutant(mutation):
+    def fn(q, k, v, g, beta, scale=1.0, S0=None):
+        T, H, K = q.shape
+        S = S0.astype(np.float64).copy()
+        o = np.zeros((T, H, v.shape[-1]))
+        for t in range(T):
+            if mutation == "decay_rows":
+                S *= np.exp(g[t][:, :S.shape[1]])[:, :, None]
+            elif mutation != "decay_after_update":
+                S *= np.exp(g[t])[:, None, :]
+            dot = np.einsum("hvk,hk->hv", S, k[t])
+            S += (beta[t][:, None] * (v[t] - dot))[:, :, None] * k[t][:, None, :]
+            if mutation == "decay_after_update":
+                S *= np.exp(g[t])[:, None, :]
+            o[t] = np.einsum("hvk,hk->hv", S, scale * q[t])
+        return o, S
+    return fn
+
+
+@pytest.mark.parametrize("mutation", ["decay_rows", "decay_after_update"])
+def test_kda_pins_catch_mistakes(mutation):
+    _kda_closed_form_checks(_kda_mutant(None))
+    with pytest.raises(AssertionError):
+        _kda_closed_form_checks(_kda_mutant(mutation))
