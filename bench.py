@@ -239,6 +239,39 @@ def bench_decode(torch, api, hev, steps, warmup):
     return dict(wall_s=wall, kernel_ms=stats(ms), n_active=int((di.slots > 0).sum()))
 
 
+def bench_decode_kda(torch, api, hev, steps, warmup):
+    """The decode workload with a log-decay per key channel (g [N, H, K])."""
+    from linear_attention_sequence_recompute_amd.workloads import channel_log_decay, decode_inputs
+
+    di = decode_inputs(DN, DH, DK, DV, DSLOTS, dtype="bf16", seed=5, n_padding=0)
+    dev = torch.device("cuda")
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (di.q, di.k, di.v))
+    g = torch.from_numpy(channel_log_decay((DN, DH, DK), seed=6)).float().to(dev)
+    b = torch.from_numpy(di.beta).float().to(dev)
+    pool = torch.from_numpy(di.pool).float().to(dev)
+    slots = torch.from_numpy(di.slots).int().to(dev)
+    o = torch.empty(DN, DH, DV, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        api.recurrent_step_kda(q, k, v, g, b, pool, slots, scale=DK ** -0.5, out=o, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [hev.create(2) for _ in range(steps)]
+    s = stream.cuda_stream
+    for i in range(steps):
+        hev.record(evs[i][0], s)
+        step()
+        hev.record(evs[i][1], s)
+    torch.cuda.synchronize()
+    ms = [hev.ms(e[0], e[1]) for e in evs]
+    for e in evs:
+        hev.destroy(e)
+    return dict(kernel_ms=stats(ms), n_active=int((di.slots > 0).sum()))
+
+
 def verify_bytes(n_active: int, T: int) -> int:
     """Algorithmic HBM bytes of one verify call: per active (request, head) the
     source state is read once and T states are written; q, k, v, o in bf16 and
@@ -354,7 +387,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "verify", "fp8", "copy"], default="all")
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "kda", "verify", "fp8", "copy"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -386,6 +419,11 @@ def main():
         log("decode: N=256 H=32 K=V=128 pool=512 ...")
         res_d = bench_decode(torch, api, hev, args.steps, args.warmup)
         log(json.dumps(res_d))
+    res_k = None
+    if args.only in ("all", "kda"):
+        log("decode with per-key-channel decay: N=256 H=32 K=V=128 pool=512 ...")
+        res_k = bench_decode_kda(torch, api, hev, args.steps, args.warmup)
+        log(json.dumps(res_k))
     res_v = None
     if args.only in ("all", "verify"):
         log(f"verify decode: N={VN} T={VT} H=32 K=V=128 pool=512 ...")
@@ -443,6 +481,14 @@ def main():
                                 "frac": dec_gbs / PEAK_HBM_GBS, "traffic": traffic_for("recurrent_step_kernel"),
                                 "bytes_per_launch": dec_b}},
     }
+    kda_s = res_k["kernel_ms"]["mean"] / 1e3
+    kda_b = decode_bytes(res_k["n_active"]) + res_k["n_active"] * DH * (DK - 1) * 4  # g per key channel
+    out["decode_kda"] = {
+        "workload": "recurrent decode step with a log-decay per key channel, N=256 requests (all active), H=32, "
+                    "K=V=128, pool [512, 32, 128, 128] fp32, bf16 q/k/v/o",
+        "value": kda_b / kda_s / 1e9, "unit": "GB/s", "avg_launch_us": kda_s * 1e6,
+        "roofline": {"bound": "hbm", "achieved": kda_b / kda_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": kda_b / kda_s / 1e9 / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": kda_b}}
     ver_s = res_v["kernel_ms"]["mean"] / 1e3
     ver_b = verify_bytes(res_v["n_active"], VT)
     out["decode_verify"] = {

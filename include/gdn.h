@@ -159,6 +159,24 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const
                               float scale, gdn_dtype in_dtype, gdn_dtype out_dtype, void* stream);
 
 /*
+ * gdn_recurrent_step with a decay per key channel (the vLLM KdaSplit page, method
+ * update: every state element of key column e is multiplied by that column's
+ * decay before the delta-rule write).
+ *
+ *  g           float32 [N, H, K], 16-byte aligned: the per-channel log-decay
+ *              (<= 0); every other argument as in gdn_recurrent_step
+ *
+ * Per active row b and head h: S = pool[slots[b], h]; S <- S diag(exp(g[b, h]));
+ * S <- S + beta (v - S k) k^T; o = S (scale q); the updated S is stored back.
+ * Status codes as gdn_recurrent_step (g must be 16-byte aligned).
+ */
+gdn_status gdn_recurrent_step_kda(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, float* state_pool, int64_t pool_slots,
+                                  const int32_t* slots, void* o, int N, int H, int K, int V,
+                                  float scale, gdn_dtype in_dtype, gdn_dtype out_dtype,
+                                  void* stream);
+
+/*
  * Speculative-verify decode: T tokens per request (the vLLM KdaSplit page, class
  * docstring, ``tokens`` q > 1, with its spec-cache semantics).
  *

@@ -28,6 +28,7 @@ SIGNATURES = {
     "gdn_chunk_fwd_profiled": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I,
                                     _P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P, _P]),
     "gdn_recurrent_step": (_I, [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "gdn_recurrent_step_kda": (_I, [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "gdn_recurrent_verify": (_I, [_P, _P, _P, _P, _P, _P, _I64, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
                                   _P]),
     "gdn_fp8_quant": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),

@@ -211,3 +211,31 @@ def fp8_quant(x: torch.Tensor, group: int = 128, *, codes: Optional[torch.Tensor
     st = _lib.lib().gdn_fp8_quant(_ptr(x), _ptr(codes), _ptr(scales), rows, C, group, _stream(stream))
     _lib.check(st, "gdn_fp8_quant")
     return codes, scales
+
+
+def recurrent_step_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                       state_pool: torch.Tensor, slots: torch.Tensor, *, scale: Optional[float] = None,
+                       out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None, stream=None):
+    """One decode step with a decay per key channel (gdn_recurrent_step_kda): as
+    ``recurrent_step`` but g is [N, H, K] float32 (per-channel log-decays)."""
+    N, H, K = q.shape
+    V = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    for name, t in (("g", g), ("beta", beta), ("state_pool", state_pool)):
+        _need(t, name, torch.float32)
+    _need(slots, "slots", torch.int32)
+    if k.shape != q.shape or v.shape[:2] != (N, H) or g.shape != (N, H, K) or beta.shape != (N, H):
+        raise ValueError("inconsistent shapes of q, k, v, g, beta")
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, V, K) or slots.shape != (N,):
+        raise ValueError("state_pool must be [P, H, V, K] and slots [N]")
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((N, H, V), dtype=out_dtype, device=q.device)
+    _need(out, "out", out_dtype)
+    st = _lib.lib().gdn_recurrent_step_kda(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), state_pool.shape[0], _ptr(slots),
+        _ptr(out), N, H, K, V, float(K ** -0.5 if scale is None else scale), _dt(q.dtype), _dt(out_dtype),
+        _stream(stream))
+    _lib.check(st, "gdn_recurrent_step_kda")
+    return out

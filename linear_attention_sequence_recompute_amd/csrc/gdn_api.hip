@@ -185,9 +185,14 @@ gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const void* v, c
                         workspace_bytes, stream, events);
 }
 
-gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                              float* state_pool, int64_t pool_slots, const int32_t* slots, void* o, int N, int H,
-                              int K, int V, float scale, gdn_dtype in_dtype, gdn_dtype out_dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+gdn_status recurrent_step_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               float* state_pool, int64_t pool_slots, const int32_t* slots, void* o, int N, int H,
+                               int K, int V, float scale, gdn_dtype in_dtype, gdn_dtype out_dtype, void* stream,
+                               bool kda) {
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !supported_dim(K) || !supported_dim(V))
     return GDN_EUNSUPPORTED;
   if (N < 0 || H <= 0 || H > 65535) return GDN_EINVAL;
@@ -195,11 +200,13 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const
   if (static_cast<int64_t>(N) * H * (V / 16) > INT32_MAX) return GDN_EINVAL;
   if (N == 0) return GDN_OK;
   if (!q || !k || !v || !g || !beta || !state_pool || !slots || !o || pool_slots <= 0) return GDN_EINVAL;
-  if (!aligned(state_pool, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(slots, 4)) return GDN_EINVAL;
+  if (!aligned(state_pool, 16) || !aligned(g, kda ? 16 : 4) || !aligned(beta, 4) || !aligned(slots, 4))
+    return GDN_EINVAL;
   const size_t in_b = dtype_bytes(in_dtype), out_b = dtype_bytes(out_dtype);
   if (!aligned(q, in_b) || !aligned(k, in_b) || !aligned(v, in_b) || !aligned(o, out_b)) return GDN_EINVAL;
 
   gdn::DecodeArgs a{};
+  a.kda = kda;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -218,6 +225,24 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const
   a.out_f32 = out_dtype == GDN_F32;
   a.stream = static_cast<hipStream_t>(stream);
   return hip_status(gdn::launch_decode(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                              float* state_pool, int64_t pool_slots, const int32_t* slots, void* o, int N, int H,
+                              int K, int V, float scale, gdn_dtype in_dtype, gdn_dtype out_dtype, void* stream) {
+  return recurrent_step_impl(q, k, v, g, beta, state_pool, pool_slots, slots, o, N, H, K, V, scale, in_dtype,
+                             out_dtype, stream, false);
+}
+
+gdn_status gdn_recurrent_step_kda(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                  float* state_pool, int64_t pool_slots, const int32_t* slots, void* o, int N, int H,
+                                  int K, int V, float scale, gdn_dtype in_dtype, gdn_dtype out_dtype, void* stream) {
+  return recurrent_step_impl(q, k, v, g, beta, state_pool, pool_slots, slots, o, N, H, K, V, scale, in_dtype,
+                             out_dtype, stream, true);
 }
 
 

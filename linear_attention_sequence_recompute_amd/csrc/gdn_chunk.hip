@@ -10,12 +10,17 @@
 //  * prep_kernel, one workgroup per (chunk, head), fully parallel: the
 //    chunk-local gate cumsum, K K^T -> L, the triangular solve A = (I + L)^-1 in
 //    LDS, and A' stored in the MFMA operand order the scan kernel reads;
-//  * scan_kernel, one workgroup per (sequence, head, 16-column slice of V): the
-//    sequential chunk loop of chunk_fwd_h with chunk_fwd_o fused into it. Each
-//    chunk's K is staged once in LDS and serves K h, K^T (read transposed) and the
-//    score matrix P = s (Q K^T) * E * M; v_new = A' (V - e^g (K h)); the state
-//    lives in MFMA accumulators, the decay e^{g_last} folded into the accumulator
-//    before K^T v_gated is added. Per-chunk states and v_new never leave the chip.
+//  * scan_kernel, one workgroup per (sequence, head, one or two 16-column slices
+//    of V): the sequential chunk loop of chunk_fwd_h with chunk_fwd_o fused into
+//    it. Each chunk's K is staged once in LDS and serves K h, K^T (read
+//    transposed) and the score matrix P = s (Q K^T) * E * M; v_new =
+//    A' (V - e^g (K h)); the state lives in MFMA accumulators, the decay
+//    e^{g_last} folded into the accumulator before K^T v_gated is added.
+//    Per-chunk states and v_new never leave the chip;
+//  * with few (sequence, head) pairs, the chunk-parallel form: summary_kernel
+//    forms the affine state map of each segment of chunks (h -> M h + c), and
+//    scan_kernel then runs every segment at once, each chain first carrying the
+//    initial state through the maps of the segments before its own.
 //
 // Precision: q, k, v are exact in bf16 and enter the MFMA as one operand; every
 // computed operand (A', K h residuals, h, v_new, P) enters as a bf16 hi + lo pair

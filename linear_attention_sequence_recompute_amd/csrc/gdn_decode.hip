@@ -34,7 +34,9 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-template <int K, int V, typename Tin, typename Tout>
+// KDA: g holds a log-decay per key channel ([N, H, K], the KdaSplit page's
+// per-column decays); each lane scales its 4 key columns by their own factors.
+template <int K, int V, typename Tin, typename Tout, bool KDA = false>
 __global__ __launch_bounds__(256) void recurrent_step_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ pool,
@@ -74,7 +76,14 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
   float vv[PASSES];
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) vv[p] = ld_in(v + tok * V + row0 + p * RPP + rsub);
-  const float decay = expf(g[tok]);
+  f32x4 decay;
+  if constexpr (KDA) {
+    const f32x4 lg = *reinterpret_cast<const f32x4*>(g + tok * K + col);
+    decay = f32x4{expf(lg[0]), expf(lg[1]), expf(lg[2]), expf(lg[3])};
+  } else {
+    const float d = expf(g[tok]);
+    decay = f32x4{d, d, d, d};
+  }
   const float bt = beta[tok];
 
   float dk[PASSES];
@@ -223,10 +232,15 @@ hipError_t launch_verify(const VerifyArgs& a) {
 template <int K, int V, typename Tin, typename Tout>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
   const dim3 grid(static_cast<unsigned>(a.N) * a.H * (V / kDecodeRows));  // request slowest
-  hipLaunchKernelGGL((recurrent_step_kernel<K, V, Tin, Tout>), grid, dim3(256), 0, a.stream,
-                     static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
-                     static_cast<const Tin*>(a.v), a.g, a.beta, a.pool, a.pool_slots, a.slots,
-                     static_cast<Tout*>(a.o), a.H, a.scale);
+  auto launch = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, a.stream, static_cast<const Tin*>(a.q),
+                       static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v), a.g, a.beta, a.pool,
+                       a.pool_slots, a.slots, static_cast<Tout*>(a.o), a.H, a.scale);
+  };
+  if (a.kda)
+    launch(recurrent_step_kernel<K, V, Tin, Tout, true>);
+  else
+    launch(recurrent_step_kernel<K, V, Tin, Tout, false>);
   return hipGetLastError();
 }
 

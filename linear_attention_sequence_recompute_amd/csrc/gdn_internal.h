@@ -10,7 +10,8 @@ namespace gdn {
 
 struct DecodeArgs {
   const void *q, *k, *v;
-  const float *g, *beta;
+  const float *g, *beta;  // g: [N, H] scalar log-gate, or [N, H, K] per key channel (kda)
+  bool kda;
   float* pool;
   int64_t pool_slots;
   const int32_t* slots;

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
-                                         "gdn_chunk_fwd_profiled", "gdn_recurrent_step",
+                                         "gdn_chunk_fwd_profiled", "gdn_recurrent_step", "gdn_recurrent_step_kda",
                                          "gdn_recurrent_verify", "gdn_fp8_quant", "gdn_status_string"}
 
 
@@ -192,3 +192,20 @@ def test_fp8_quant_validation():
     assert _fp8(x=FAKE + 4) == E.GDN_EINVAL     # x must be 16-byte aligned
     assert _fp8(codes=FAKE + 2) == E.GDN_EINVAL
     assert _fp8(rows=1 << 40, cols=1 << 20) == E.GDN_EINVAL  # grid limit
+
+
+def test_recurrent_step_kda_validation():
+    E = _lib
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, pool=FAKE, pool_slots=8, slots=FAKE, o=FAKE, N=4, H=2,
+                K=128, V=128, scale=1.0, in_dt=BF16, out_dt=BF16, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return _lib.lib().gdn_recurrent_step_kda(a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"],
+                                                 a["pool_slots"], a["slots"], a["o"], a["N"], a["H"], a["K"],
+                                                 a["V"], a["scale"], a["in_dt"], a["out_dt"], a["stream"])
+    assert call(K=96) == E.GDN_EUNSUPPORTED
+    assert call(N=0) == E.GDN_OK
+    assert call(g=None) == E.GDN_EINVAL
+    assert call(g=FAKE + 4) == E.GDN_EINVAL   # the per-channel decays are read as float4
+    assert call(pool=FAKE + 4) == E.GDN_EINVAL

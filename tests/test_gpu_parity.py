@@ -13,8 +13,8 @@ import torch
 
 import oracle
 from linear_attention_sequence_recompute_amd import api
-from linear_attention_sequence_recompute_amd.workloads import (chunk_inputs, decode_inputs, varlen_lengths,
-                                                              verify_inputs)
+from linear_attention_sequence_recompute_amd.workloads import (channel_log_decay, chunk_inputs, decode_inputs,
+                                                              varlen_lengths, verify_inputs)
 from tests.gpu_util import TORCH_DT, bf16_rne, dev, host, max_err_over_rms
 
 pytestmark = pytest.mark.gpu
@@ -394,6 +394,66 @@ def test_decode_out_of_range_slot_is_padding():
     assert torch.all(o[3] == 0) and torch.all(o[5] == 0)
     keep = [s for s in range(16) if s not in set(di.slots[[0, 1, 2, 4, 6, 7]].tolist())]
     assert torch.equal(pool[keep], pool0[keep])
+
+
+# --------------------------------------------- per-key-channel decay (KDA)
+
+def check_decode_kda(di, g, scale, label):
+    tol = TOL[di.dtype]
+    dt = TORCH_DT[di.dtype]
+    pool0 = dev(di.pool)
+    outs = {}
+    for od in ("f32", "bf16"):
+        pool = pool0.clone()
+        o = api.recurrent_step_kda(dev(di.q, dt), dev(di.k, dt), dev(di.v, dt), dev(g), dev(di.beta), pool,
+                                   dev(di.slots, torch.int32), scale=scale, out_dtype=TORCH_DT[od])
+        torch.cuda.synchronize()
+        outs[od] = (o, pool)
+    (o32, p32), (o16, p16) = outs["f32"], outs["bf16"]
+    assert torch.equal(o16, bf16_rne(o32)) and torch.equal(p16, p32)
+    o_ref, pool_ref = oracle.decode_step_kda(di.q, di.k, di.v, g, di.beta, di.pool, di.slots, scale=scale)
+    act = [b for b in range(len(di.slots)) if di.slots[b] > 0]
+    pad = [b for b in range(len(di.slots)) if di.slots[b] <= 0]
+    eo = max_err_over_rms(host(o32)[act], o_ref[act])
+    used = {int(di.slots[b]) for b in act}
+    es = max(max_err_over_rms(host(p32[s]), pool_ref[s]) for s in used)
+    for b in pad:
+        assert bool((o32[b].view(torch.int32) == 0).all()), f"{label}: padding row {b} output is not +0"
+    for s in range(di.pool.shape[0]):
+        if s not in used:
+            assert torch.equal(p32[s], pool0[s]), f"{label}: slot {s} was written"
+    _print(f"[decode kda {label}] max|do|/rms={eo:.3e} max|dS|/rms={es:.3e} tol={tol}")
+    assert eo <= tol and es <= tol
+
+
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_kda_small(K, V, dtype):
+    di = decode_inputs(N=24, H=3, K=K, V=V, pool_slots=40, dtype=dtype, seed=80 + K + V, n_padding=4)
+    g = channel_log_decay((24, 3, K), seed=81 + K, shift=-2.0)
+    check_decode_kda(di, g, K ** -0.5, f"K={K} V={V} {dtype}")
+
+
+def test_decode_kda_config_full():
+    """N=256 requests, H=32, K=V=128, 512-slot pool, 32 padding rows."""
+    di = decode_inputs(N=256, H=32, K=128, V=128, pool_slots=512, dtype="bf16", seed=5, n_padding=32)
+    g = channel_log_decay((256, 32, 128), seed=82)
+    check_decode_kda(di, g, 128 ** -0.5, "N256 H32")
+
+
+def test_decode_kda_uniform_channels_equal_the_scalar_step():
+    """A decay vector with every channel equal to the scalar gate gives the scalar
+    kernel's results bit for bit (the same multiply per state element)."""
+    di = decode_inputs(N=40, H=4, K=128, V=128, pool_slots=64, dtype="bf16", seed=83, n_padding=5)
+    g = np.repeat(di.a[:, :, None], 128, axis=2).astype(np.float32)
+    dt = torch.bfloat16
+    p1, p2 = dev(di.pool), dev(di.pool)
+    o1 = api.recurrent_step(dev(di.q, dt), dev(di.k, dt), dev(di.v, dt), dev(di.a), dev(di.beta), p1,
+                            dev(di.slots, torch.int32), out_dtype=torch.float32)
+    o2 = api.recurrent_step_kda(dev(di.q, dt), dev(di.k, dt), dev(di.v, dt), dev(g), dev(di.beta), p2,
+                                dev(di.slots, torch.int32), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(p1, p2)
 
 
 # ----------------------------------------------------- speculative verify
