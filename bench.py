@@ -488,7 +488,8 @@ def main():
                     "K=V=128, pool [512, 32, 128, 128] fp32, bf16 q/k/v/o",
         "value": kda_b / kda_s / 1e9, "unit": "GB/s", "avg_launch_us": kda_s * 1e6,
         "roofline": {"bound": "hbm", "achieved": kda_b / kda_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": kda_b / kda_s / 1e9 / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": kda_b}}
+                     "frac": kda_b / kda_s / 1e9 / PEAK_HBM_GBS, "traffic": traffic_for("recurrent_step_kernel_kda"),
+                     "bytes_per_launch": kda_b}}
     ver_s = res_v["kernel_ms"]["mean"] / 1e3
     ver_b = verify_bytes(res_v["n_active"], VT)
     out["decode_verify"] = {
