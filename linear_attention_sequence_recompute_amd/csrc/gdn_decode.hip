@@ -116,8 +116,8 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
 // the state after token t is stored to slot[b, t] when that slot is in (0,
 // pool_slots). A request whose source slot is not (or whose accepted count is
 // outside [1, cols]) is padding: zero outputs, no writes. The layout is the decode
-// step's; the state rows stay in registers across the tokens, whose inputs are
-// all loaded before the first update.
+// step's; the state rows stay in registers across the tokens, each token's inputs
+// loaded while the previous token is applied.
 constexpr int kMaxVerifyTokens = 8;
 
 template <int K, int V, typename Tin, typename Tout>
@@ -151,47 +151,52 @@ __global__ __launch_bounds__(256) void recurrent_verify_kernel(
   for (int p = 0; p < PASSES; ++p)
     s[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (p * RPP + rsub) * K + col));
 
-  float kk[kMaxVerifyTokens][4], qq[kMaxVerifyTokens][4], vv[kMaxVerifyTokens][PASSES];
-  float decay[kMaxVerifyTokens], bt[kMaxVerifyTokens];
-  int dst[kMaxVerifyTokens];
+  // inputs of one token, loaded one token ahead of their use (two sets live)
+  struct TokIn {
+    float kk[4], qq[4], vv[PASSES], decay, bt;
+    int dst;
+  };
+  auto load_tok = [&](int t) {
+    TokIn r;
+    const int64_t tok = (static_cast<int64_t>(b) * T + t) * H + h;
 #pragma unroll
-  for (int t = 0; t < kMaxVerifyTokens; ++t) {
-    if (t < T) {
-      const int64_t tok = (static_cast<int64_t>(b) * T + t) * H + h;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kk[t][e] = ld_in(k + tok * K + col + e);
-        qq[t][e] = scale * ld_in(q + tok * K + col + e);
-      }
-#pragma unroll
-      for (int p = 0; p < PASSES; ++p) vv[t][p] = ld_in(v + tok * V + row0 + p * RPP + rsub);
-      decay[t] = expf(g[tok]);
-      bt[t] = beta[tok];
-      dst[t] = srow[t];
+    for (int e = 0; e < 4; ++e) {
+      r.kk[e] = ld_in(k + tok * K + col + e);
+      r.qq[e] = scale * ld_in(q + tok * K + col + e);
     }
-  }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) r.vv[p] = ld_in(v + tok * V + row0 + p * RPP + rsub);
+    r.decay = expf(g[tok]);
+    r.bt = beta[tok];
+    r.dst = srow[t];
+    return r;
+  };
+  TokIn cur = load_tok(0);
 #pragma unroll
   for (int t = 0; t < kMaxVerifyTokens; ++t) {
     if (t >= T) break;
+    TokIn nxt = cur;
+    if (t + 1 < T) nxt = load_tok(t + 1);
+    __builtin_amdgcn_sched_barrier(0);  // the next token's loads go out before this token's work
     const int64_t tok = (static_cast<int64_t>(b) * T + t) * H + h;
     float dk[PASSES];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      s[p] *= decay[t];
-      dk[p] = s[p][0] * kk[t][0] + s[p][1] * kk[t][1] + s[p][2] * kk[t][2] + s[p][3] * kk[t][3];
+      s[p] *= cur.decay;
+      dk[p] = s[p][0] * cur.kk[0] + s[p][1] * cur.kk[1] + s[p][2] * cur.kk[2] + s[p][3] * cur.kk[3];
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) dk[p] = group_sum<LPR>(dk[p]);
     float dq[PASSES];
-    float* D = dst[t] > 0 && dst[t] < pool_slots
-                   ? pool + (static_cast<int64_t>(dst[t]) * H + h) * page + static_cast<int64_t>(row0) * K
+    float* D = cur.dst > 0 && cur.dst < pool_slots
+                   ? pool + (static_cast<int64_t>(cur.dst) * H + h) * page + static_cast<int64_t>(row0) * K
                    : nullptr;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      const float vn = bt[t] * (vv[t][p] - dk[p]);
+      const float vn = cur.bt * (cur.vv[p] - dk[p]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[p][e] = fmaf(kk[t][e], vn, s[p][e]);
-      dq[p] = s[p][0] * qq[t][0] + s[p][1] * qq[t][1] + s[p][2] * qq[t][2] + s[p][3] * qq[t][3];
+      for (int e = 0; e < 4; ++e) s[p][e] = fmaf(cur.kk[e], vn, s[p][e]);
+      dq[p] = s[p][0] * cur.qq[0] + s[p][1] * cur.qq[1] + s[p][2] * cur.qq[2] + s[p][3] * cur.qq[3];
       if (D) __builtin_nontemporal_store(s[p], reinterpret_cast<f32x4*>(D + (p * RPP + rsub) * K + col));
     }
 #pragma unroll
@@ -201,6 +206,7 @@ __global__ __launch_bounds__(256) void recurrent_verify_kernel(
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) store_out(orow + p * RPP + rsub, dq[p]);
     }
+    cur = nxt;
   }
 }
 
