@@ -18,6 +18,9 @@ Functions (all float64 numpy):
   with per-token state writes.
 * ``recurrent_fwd_kda`` / ``decode_step_kda`` - the rule with a decay per key
   channel (KdaSplit), per token and as a decode step over the pool.
+* ``decode_prologue`` / ``gated_rmsnorm`` - the decode layer's front (conv1d
+  over a conv-state pool, SiLU, q/k L2 norm, sigmoid beta) and back (gated
+  RMSNorm) operations (``oracle/layer.py``).
 * ``fp8_quant``      - group quantisation to FP8 E4M3 (``oracle/fp8.py``), with
   ``e4m3_encode`` / ``e4m3_decode``.
 
@@ -38,3 +41,4 @@ from .gdn import (  # noqa: F401
     unit_lower_inverse,
 )
 from .fp8 import e4m3_decode, e4m3_encode, fp8_quant  # noqa: F401
+from .layer import conv_silu_step, decode_prologue, gated_rmsnorm  # noqa: F401

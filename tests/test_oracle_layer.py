@@ -1,0 +1,117 @@
+"""Pins of the decode layer's front and back operations (KdaSplit kernel body).
+
+The convolution is checked against numpy's convolve over a token sequence (a
+library routine), the state shift against the inputs it must hold, the norms
+against closed forms; planted mistakes each fail a pin.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import conv_silu_step, decode_prologue, gated_rmsnorm
+from oracle import layer as layer_mod
+
+
+def _silu(y):
+    return y / (1.0 + np.exp(-y))
+
+
+def check_conv(fn):
+    rng = np.random.default_rng(0)
+    H, D, T = 2, 4, 9
+    C = 3 * H * D
+    w = rng.standard_normal((3, 4, H * D))
+    bias = rng.standard_normal(C)
+    xs = rng.standard_normal((T, C))
+    st = np.zeros((3, C, 3))
+    ys = []
+    for t in range(T):
+        y, st = fn(xs[t:t + 1], w, bias, st, np.array([2]))
+        ys.append(y[0])
+    ys = np.array(ys)
+    wc = np.concatenate([w[s].T for s in range(3)], axis=0)  # [C, 4], tap 3 multiplies the newest input
+    for c in range(C):
+        ref = np.convolve(xs[:, c], wc[c, ::-1])[:T] + bias[c]  # causal, zero history
+        np.testing.assert_allclose(ys[:, c], _silu(ref), rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(st[2], xs[-3:].T)   # the slot holds the last three inputs, oldest first
+    np.testing.assert_array_equal(st[1], 0.0)         # other slots untouched
+    # padding row: zero output, state untouched
+    y, st2 = fn(xs[:1], w, bias, st, np.array([0]))
+    assert np.all(y == 0) and np.array_equal(st2, st)
+
+
+def test_conv_matches_numpy_convolve():
+    check_conv(conv_silu_step)
+
+
+def test_prologue_norms():
+    rng = np.random.default_rng(1)
+    H, D, N = 3, 8, 5
+    C = 3 * H * D
+    x = rng.standard_normal((N, C)) * 3
+    w = rng.standard_normal((3, 4, H * D))
+    st = rng.standard_normal((7, C, 3))
+    slots = np.array([1, 0, 3, 6, -1])
+    q, k, v, beta, _ = decode_prologue(x, w, None, st, slots, rng.standard_normal((N, H)), H, D)
+    for b in (0, 2, 3):
+        nq, nk = np.sum(q[b] ** 2, -1), np.sum(k[b] ** 2, -1)
+        assert np.all(np.abs(nq - 1) < 1e-3) and np.all(np.abs(nk - 1) < 1e-3)
+        assert np.all((beta[b] > 0) & (beta[b] < 1))
+    for b in (1, 4):
+        assert np.all(q[b] == 0) and np.all(k[b] == 0) and np.all(v[b] == 0) and np.all(beta[b] == 0)
+    # identity convolution (only the newest tap, weight 1): v = silu(x) exactly
+    wid = np.zeros((3, 4, H * D))
+    wid[:, 3, :] = 1.0
+    _, _, v2, _, _ = decode_prologue(x, wid, None, st, slots, np.zeros((N, H)), H, D)
+    np.testing.assert_allclose(v2[0].ravel(), _silu(x[0, 2 * H * D:]), rtol=1e-14)
+
+
+def check_rmsnorm(fn):
+    rng = np.random.default_rng(2)
+    o = rng.standard_normal((4, 2, 16))
+    out = fn(o, np.full((4, 32), 40.0), np.ones(16), 1e-6)   # sigmoid(40) = 1 - 4e-18
+    np.testing.assert_allclose(np.sqrt(np.mean(out ** 2, -1)), 1.0, rtol=1e-5)
+    c = np.full((1, 1, 16), 3.0)                               # constant vector: 3 / sqrt(9 + eps)
+    w = rng.uniform(0.5, 2, 16)
+    g = rng.standard_normal((1, 16))
+    ref = 3.0 / np.sqrt(9.0 + 1e-2) * w / (1 + np.exp(-g[0]))
+    np.testing.assert_allclose(fn(c, g, w, 1e-2)[0, 0], ref, rtol=1e-12)
+
+
+def test_gated_rmsnorm_closed_forms():
+    check_rmsnorm(gated_rmsnorm)
+
+
+def _conv_mutant(mutation):
+    def fn(x, w, bias, conv_state, slots):
+        st = np.asarray(conv_state, np.float64).copy()
+        N, C = x.shape
+        wc = np.concatenate([np.asarray(w)[s].T for s in range(3)], axis=0)
+        if mutation == "taps_reversed":
+            wc = wc[:, ::-1]
+        y = np.zeros((N, C))
+        for b in range(N):
+            slot = int(slots[b])
+            if slot <= 0:
+                continue
+            window = np.concatenate([st[slot], x[b][:, None]], axis=1)
+            acc = np.sum(window * wc, axis=1) + (bias if bias is not None else 0)
+            y[b] = _silu(acc)
+            st[slot] = window[:, :3] if mutation == "shift_keeps_oldest" else window[:, 1:]
+        return y, st
+    return fn
+
+
+@pytest.mark.parametrize("mutation", ["taps_reversed", "shift_keeps_oldest"])
+def test_conv_pins_catch_mistakes(mutation):
+    check_conv(_conv_mutant(None))
+    with pytest.raises(AssertionError):
+        check_conv(_conv_mutant(mutation))
+
+
+def test_rmsnorm_pins_catch_missing_eps_and_gate():
+    with pytest.raises(AssertionError):
+        check_rmsnorm(lambda o, g, w, eps: layer_mod.gated_rmsnorm(o, g, w, 0.0))
+    with pytest.raises(AssertionError):
+        check_rmsnorm(lambda o, g, w, eps: layer_mod.gated_rmsnorm(o, np.full_like(np.asarray(g, float), 40.0), w,
+                                                                   eps))
