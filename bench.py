@@ -341,6 +341,63 @@ def bench_fp8(torch, api, hev, steps, warmup):
     return dict(kernel_ms=stats(ms))
 
 
+def layer_bytes():
+    """Algorithmic bytes of the decode layer's front and back operations at
+    N=DN requests, H=DH heads of DK channels (all active): each input and output
+    element moved once, the conv state read and written once."""
+    dim = DH * DK
+    pro = (DN * 3 * dim * 2 + 2 * DN * 3 * dim * 3 * 2 + (3 * 4 * dim + 3 * dim) * 4 + DN * DH * 4
+           + DN * 3 * dim * 4 + DN * DH * 4)
+    rms = DN * dim * 4 + DN * dim * 2 + DK * 4 + DN * dim * 2
+    return pro, rms
+
+
+def bench_layer(torch, api, hev, steps, warmup):
+    """Decode layer front (conv + SiLU + norms + beta) and back (gated RMSNorm)
+    operations for N=DN requests, H=DH heads of DK channels, a conv-state pool of
+    DSLOTS slots."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev).manual_seed(13)
+    dim = DH * DK
+    x = torch.randn(DN, 3 * dim, device=dev, generator=g).to(torch.bfloat16)
+    w = torch.rand(3, 4, dim, device=dev, generator=g) - 0.5
+    bias = torch.rand(3 * dim, device=dev, generator=g) - 0.5
+    conv = torch.randn(DSLOTS, 3 * dim, 3, device=dev, generator=g).to(torch.bfloat16)
+    slots = (torch.randperm(DSLOTS - 1, device=dev, generator=g)[:DN] + 1).to(torch.int32)
+    braw = torch.randn(DN, DH, device=dev, generator=g)
+    o = torch.randn(DN, DH, DK, device=dev, generator=g)
+    gate = torch.randn(DN, dim, device=dev, generator=g).to(torch.bfloat16)
+    nw = torch.ones(DK, device=dev)
+    out = torch.empty(DN, DH, DK, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def pro():
+        api.decode_prologue(x, w, bias, conv, slots, braw, DH, stream=stream)
+
+    def rms():
+        api.gated_rmsnorm(o, gate, nw, 1e-6, out=out, stream=stream)
+
+    for _ in range(warmup):
+        pro()
+        rms()
+    torch.cuda.synchronize()
+    evs = [hev.create(4) for _ in range(steps)]
+    s = stream.cuda_stream
+    for i in range(steps):
+        hev.record(evs[i][0], s)
+        pro()
+        hev.record(evs[i][1], s)
+        hev.record(evs[i][2], s)
+        rms()
+        hev.record(evs[i][3], s)
+    torch.cuda.synchronize()
+    ms_p = [hev.ms(e[0], e[1]) for e in evs]
+    ms_r = [hev.ms(e[2], e[3]) for e in evs]
+    for e in evs:
+        hev.destroy(e)
+    return dict(prologue_ms=stats(ms_p), rmsnorm_ms=stats(ms_r))
+
+
 def bench_copy(torch, steps, nbytes=1 << 30):
     """A plain device copy of known size: the calibration kernel for PMC byte
     counters (FETCH_SIZE and WRITE_SIZE of this launch should read nbytes each)."""
@@ -387,7 +444,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "kda", "verify", "fp8", "copy"], default="all")
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "kda", "verify", "fp8", "layer", "copy"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -434,6 +491,11 @@ def main():
         log(f"fp8 quant: [{QR}, {QC}] float32, groups of {QG} ...")
         res_q = bench_fp8(torch, api, hev, args.steps, args.warmup)
         log(json.dumps(res_q))
+    res_l = None
+    if args.only in ("all", "layer"):
+        log(f"decode layer front/back: N={DN} H={DH} D={DK} conv pool={DSLOTS} ...")
+        res_l = bench_layer(torch, api, hev, args.steps, args.warmup)
+        log(json.dumps(res_l))
     if args.only != "all":
         return
 
@@ -509,6 +571,19 @@ def main():
         "roofline": {"bound": "hbm", "achieved": q_b / q_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": q_b / q_s / 1e9 / PEAK_HBM_GBS, "traffic": traffic_for("fp8_quant_kernel"),
                      "bytes_per_launch": q_b}}
+    lp_b, lr_b = layer_bytes()
+    lp_s, lr_s = res_l["prologue_ms"]["mean"] / 1e3, res_l["rmsnorm_ms"]["mean"] / 1e3
+    out["decode_layer"] = {
+        "workload": f"decode layer front (4-tap conv over a bf16 conv-state pool of {DSLOTS} slots, SiLU, q/k L2 "
+                    f"norm, sigmoid beta) and back (gated RMSNorm, bf16 out), N={DN} requests, H={DH}, D={DK}",
+        "prologue": {"avg_launch_us": lp_s * 1e6, "bytes_per_launch": lp_b,
+                     "roofline": {"bound": "hbm", "achieved": lp_b / lp_s / 1e9, "peak": PEAK_HBM_GBS,
+                                  "unit": "GB/s", "frac": lp_b / lp_s / 1e9 / PEAK_HBM_GBS,
+                                  "traffic": traffic_for("decode_prologue_kernel")}},
+        "gated_rmsnorm": {"avg_launch_us": lr_s * 1e6, "bytes_per_launch": lr_b,
+                          "roofline": {"bound": "hbm", "achieved": lr_b / lr_s / 1e9, "peak": PEAK_HBM_GBS,
+                                       "unit": "GB/s", "frac": lr_b / lr_s / 1e9 / PEAK_HBM_GBS,
+                                       "traffic": traffic_for("gated_rmsnorm_kernel")}}}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -231,6 +231,60 @@ gdn_status gdn_recurrent_verify(const void* q, const void* k, const void* v, con
 gdn_status gdn_fp8_quant(const float* x, void* codes, float* scales, int64_t rows, int64_t cols,
                          int group, void* stream);
 
+/*
+ * Front operations of a decode layer (vLLM KdaSplit page, kernel body: the
+ * convolution, activation and normalisation steps before the recurrent update),
+ * one token per request, for heads of D = K = V channels.
+ *
+ *  x           bf16 [N, 3 H D]: the token's projected q, k, v sections, each
+ *              [H, D] (channel h D + c of a section)
+ *  conv_w      float32 [3, 4, H D]: per section, tap (oldest first) and channel
+ *  conv_bias   float32 [3 H D], or NULL for none
+ *  conv_state  bf16 [pool_slots, 3 H D, 3]: the slot's previous three inputs per
+ *              channel, oldest first; updated in place for active rows to its
+ *              last two entries followed by x
+ *  slots       device int32 [N]; slot <= 0 or >= pool_slots marks padding: its
+ *              q, k, v rows and beta are +0 and conv_state is not touched.
+ *              Active slots must be distinct.
+ *  beta_raw    float32 [N, H]
+ *  q, k, v     float32 [N, H, D] (outputs; the layout the decode step reads)
+ *  beta        float32 [N, H] (output)
+ *
+ * Per channel: y = SiLU(bias + sum over the 4 taps of w * input), with the
+ * window (conv_state[slot, ch, 0..2], x); then each head's q and k are divided by
+ * sqrt(sum of squares + 1e-6) and beta = sigmoid(beta_raw). The query scale is
+ * not applied here (the decode step takes it).
+ *
+ * Returns GDN_EUNSUPPORTED for D outside {64, 128}; GDN_EINVAL for N < 0, H
+ * outside [1, 65535], N H above 2^31 - 1, a NULL pointer (other than conv_bias),
+ * pool_slots <= 0 or a misaligned pointer; GDN_OK without launching for N == 0;
+ * GDN_EHIP if the launch fails.
+ */
+gdn_status gdn_decode_prologue(const void* x, const float* conv_w, const float* conv_bias,
+                               void* conv_state, int64_t pool_slots, const int32_t* slots,
+                               const float* beta_raw, float* q, float* k, float* v, float* beta,
+                               int N, int H, int D, void* stream);
+
+/*
+ * Gated RMSNorm of each head's decode output (vLLM KdaSplit page, kernel body:
+ * the output normalisation after the recurrent update).
+ *
+ *  o       float32 [N, H, D] (the decode step's output in float32)
+ *  gate    bf16 [N, H D] (raw gate; sigmoid is applied here)
+ *  norm_w  float32 [D], shared by the heads
+ *  out     [N, H, D] in out_dtype (bf16 or float32); may not alias o
+ *
+ * out = o * rsqrt(mean over the head's D channels of o^2 + eps) * norm_w[c] *
+ * sigmoid(gate), in float32.
+ *
+ * Returns GDN_EUNSUPPORTED for D outside {64, 128} or an unknown dtype;
+ * GDN_EINVAL for N < 0, H outside [1, 65535], N H above 2^31 - 1, eps < 0 or
+ * NaN, a NULL or misaligned pointer; GDN_OK without launching for N == 0;
+ * GDN_EHIP if the launch fails.
+ */
+gdn_status gdn_gated_rmsnorm(const float* o, const void* gate, const float* norm_w, float eps,
+                             void* out, int N, int H, int D, gdn_dtype out_dtype, void* stream);
+
 /* Static, human-readable name of a status code. Never NULL. */
 const char* gdn_status_string(gdn_status s);
 

@@ -32,6 +32,8 @@ SIGNATURES = {
     "gdn_recurrent_verify": (_I, [_P, _P, _P, _P, _P, _P, _I64, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
                                   _P]),
     "gdn_fp8_quant": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
+    "gdn_decode_prologue": (_I, [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "gdn_gated_rmsnorm": (_I, [_P, _P, _P, _F, _P, _I, _I, _I, _I, _P]),
     "gdn_status_string": (ctypes.c_char_p, [_I]),
 }
 

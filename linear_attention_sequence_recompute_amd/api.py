@@ -239,3 +239,55 @@ def recurrent_step_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: tor
         _stream(stream))
     _lib.check(st, "gdn_recurrent_step_kda")
     return out
+
+
+def decode_prologue(x: torch.Tensor, conv_w: torch.Tensor, conv_bias: Optional[torch.Tensor],
+                    conv_state: torch.Tensor, slots: torch.Tensor, beta_raw: torch.Tensor, H: int, *,
+                    stream=None):
+    """Front operations of a decode layer (gdn_decode_prologue): x bf16 [N, 3 H D],
+    conv_w float32 [3, 4, H D], conv_bias float32 [3 H D] or None, conv_state bf16
+    [P, 3 H D, 3] (updated in place), slots int32 [N], beta_raw float32 [N, H].
+    Returns (q, k, v float32 [N, H, D], beta float32 [N, H])."""
+    _need(x, "x", torch.bfloat16)
+    _need(conv_w, "conv_w", torch.float32)
+    _need(conv_state, "conv_state", torch.bfloat16)
+    _need(slots, "slots", torch.int32)
+    _need(beta_raw, "beta_raw", torch.float32)
+    N, C = x.shape
+    if C % (3 * H):
+        raise ValueError("x must be [N, 3 H D]")
+    D = C // (3 * H)
+    if conv_w.shape != (3, 4, H * D) or conv_state.dim() != 3 or tuple(conv_state.shape[1:]) != (C, 3):
+        raise ValueError("conv_w must be [3, 4, H D] and conv_state [P, 3 H D, 3]")
+    if slots.shape != (N,) or beta_raw.shape != (N, H):
+        raise ValueError("slots must be [N] and beta_raw [N, H]")
+    if conv_bias is not None:
+        _need(conv_bias, "conv_bias", torch.float32)
+        if conv_bias.shape != (C,):
+            raise ValueError("conv_bias must be [3 H D]")
+    q, k, v = (torch.empty((N, H, D), dtype=torch.float32, device=x.device) for _ in range(3))
+    beta = torch.empty((N, H), dtype=torch.float32, device=x.device)
+    st = _lib.lib().gdn_decode_prologue(
+        _ptr(x), _ptr(conv_w), _ptr(conv_bias), _ptr(conv_state), conv_state.shape[0], _ptr(slots),
+        _ptr(beta_raw), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), N, H, D, _stream(stream))
+    _lib.check(st, "gdn_decode_prologue")
+    return q, k, v, beta
+
+
+def gated_rmsnorm(o: torch.Tensor, gate: torch.Tensor, norm_w: torch.Tensor, eps: float = 1e-6, *,
+                  out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None, stream=None):
+    """Gated RMSNorm of decode outputs (gdn_gated_rmsnorm): o float32 [N, H, D],
+    gate bf16 [N, H D], norm_w float32 [D]. Returns [N, H, D] in out_dtype."""
+    _need(o, "o", torch.float32)
+    _need(gate, "gate", torch.bfloat16)
+    _need(norm_w, "norm_w", torch.float32)
+    N, H, D = o.shape
+    if gate.shape != (N, H * D) or norm_w.shape != (D,):
+        raise ValueError("gate must be [N, H D] and norm_w [D]")
+    if out is None:
+        out = torch.empty((N, H, D), dtype=out_dtype, device=o.device)
+    _need(out, "out", out_dtype)
+    st = _lib.lib().gdn_gated_rmsnorm(_ptr(o), _ptr(gate), _ptr(norm_w), float(eps), _ptr(out), N, H, D,
+                                      _dt(out_dtype), _stream(stream))
+    _lib.check(st, "gdn_gated_rmsnorm")
+    return out

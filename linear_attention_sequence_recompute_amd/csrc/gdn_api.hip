@@ -309,4 +309,59 @@ gdn_status gdn_fp8_quant(const float* x, void* codes, float* scales, int64_t row
   return hip_status(gdn::launch_fp8_quant(a));
 }
 
+
+gdn_status gdn_decode_prologue(const void* x, const float* conv_w, const float* conv_bias, void* conv_state,
+                               int64_t pool_slots, const int32_t* slots, const float* beta_raw, float* q, float* k,
+                               float* v, float* beta, int N, int H, int D, void* stream) {
+  if (D != 64 && D != 128) return GDN_EUNSUPPORTED;
+  if (N < 0 || H <= 0 || H > 65535 || static_cast<int64_t>(N) * H > INT32_MAX) return GDN_EINVAL;
+  if (N == 0) return GDN_OK;
+  if (!x || !conv_w || !conv_state || !slots || !beta_raw || !q || !k || !v || !beta || pool_slots <= 0)
+    return GDN_EINVAL;
+  if (!aligned(x, 2) || !aligned(conv_state, 2) || !aligned(conv_w, 4) || !aligned(slots, 4) ||
+      !aligned(beta_raw, 4) || !aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(beta, 4) ||
+      (conv_bias && !aligned(conv_bias, 4)))
+    return GDN_EINVAL;
+  gdn::PrologueArgs a{};
+  a.x = x;
+  a.conv_w = conv_w;
+  a.conv_bias = conv_bias;
+  a.conv_state = conv_state;
+  a.pool_slots = pool_slots;
+  a.slots = slots;
+  a.beta_raw = beta_raw;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.N = N;
+  a.H = H;
+  a.D = D;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_decode_prologue(a));
+}
+
+gdn_status gdn_gated_rmsnorm(const float* o, const void* gate, const float* norm_w, float eps, void* out, int N, int H,
+                             int D, gdn_dtype out_dtype, void* stream) {
+  if (D != 64 && D != 128) return GDN_EUNSUPPORTED;
+  if (!valid_dtype(out_dtype)) return GDN_EUNSUPPORTED;
+  if (N < 0 || H <= 0 || H > 65535 || static_cast<int64_t>(N) * H > INT32_MAX || !(eps >= 0.f)) return GDN_EINVAL;
+  if (N == 0) return GDN_OK;
+  if (!o || !gate || !norm_w || !out) return GDN_EINVAL;
+  if (!aligned(o, 4) || !aligned(gate, 2) || !aligned(norm_w, 4) || !aligned(out, dtype_bytes(out_dtype)))
+    return GDN_EINVAL;
+  gdn::RmsNormArgs a{};
+  a.o = o;
+  a.gate = gate;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.out = out;
+  a.out_f32 = out_dtype == GDN_F32;
+  a.N = N;
+  a.H = H;
+  a.D = D;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_gated_rmsnorm(a));
+}
+
 }  // extern "C"

@@ -37,6 +37,30 @@ struct VerifyArgs {
   hipStream_t stream;
 };
 
+struct PrologueArgs {
+  const void* x;            // [N, 3 H D] bf16
+  const float* conv_w;      // [3, 4, H D]
+  const float* conv_bias;   // [3 H D] or null
+  void* conv_state;         // [pool_slots, 3 H D, 3] bf16
+  int64_t pool_slots;
+  const int32_t* slots;     // [N]
+  const float* beta_raw;    // [N, H]
+  float *q, *k, *v, *beta;  // [N, H, D] x 3, [N, H]
+  int N, H, D;
+  hipStream_t stream;
+};
+
+struct RmsNormArgs {
+  const float* o;       // [N, H, D]
+  const void* gate;     // [N, H D] bf16
+  const float* norm_w;  // [D]
+  float eps;
+  void* out;            // [N, H, D]
+  bool out_f32;
+  int N, H, D;
+  hipStream_t stream;
+};
+
 struct Fp8Args {
   const float* x;     // [n_groups * group] float32
   void* codes;        // [n_groups * group] uint8 (E4M3)
@@ -106,6 +130,8 @@ ChunkWs carve_workspace(const WsLayout& l, void* base);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_verify(const VerifyArgs& a);
 hipError_t launch_fp8_quant(const Fp8Args& a);
+hipError_t launch_decode_prologue(const PrologueArgs& a);
+hipError_t launch_gated_rmsnorm(const RmsNormArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 
 }  // namespace gdn

@@ -14,7 +14,11 @@ vLLM KdaSplit page describe; neither page measures on a public dataset):
 * raw per-token log-gate a = -softplus(N(0, 1) + shift), float32, shift = 2 for the
   standard "short memory" gate (mean per-token decay about 0.16) and -4 for the
   "long memory" gate that stresses the carry across chunks;
-* initial states and pools ~ N(0, 0.1^2), float32, in [.., H, V, K] layout.
+* initial states and pools ~ N(0, 0.1^2), float32, in [.., H, V, K] layout;
+* decode layer front and back (``layer_inputs``): projected inputs x, raw gates
+  and conv states ~ N(0, 1) rounded to bf16; conv weights ~ U(-1/2, 1/2) (the
+  usual 1/sqrt(taps) bound for 4 taps) and biases ~ U(-1/2, 1/2) in float32; raw
+  beta ~ N(0, 1); norm weights 1 + N(0, 0.1^2).
 
 All values are returned as float64 numpy arrays that are exactly representable in
 the stated storage dtype, plus the storage dtype itself, so the oracle consumes
@@ -35,6 +39,8 @@ __all__ = [
     "chunk_inputs",
     "varlen_lengths",
     "decode_inputs",
+    "LayerInputs",
+    "layer_inputs",
 ]
 
 
@@ -265,3 +271,42 @@ def channel_log_decay(shape, seed, shift=2.0):
     gate's distribution, drawn independently for every channel)."""
     rng = np.random.default_rng(seed)
     return round_to_f32(-_softplus(rng.standard_normal(shape) + shift))
+
+
+@dataclass
+class LayerInputs:
+    x: np.ndarray           # [N, 3 H D] bf16 values
+    conv_w: np.ndarray      # [3, 4, H D] float32
+    conv_bias: np.ndarray   # [3 H D] float32
+    conv_state: np.ndarray  # [pool_slots, 3 H D, 3] bf16 values
+    slots: np.ndarray       # [N] int32; <= 0 padding
+    beta_raw: np.ndarray    # [N, H] float32
+    gate: np.ndarray        # [N, H D] bf16 values
+    norm_w: np.ndarray      # [D] float32
+    H: int
+    D: int
+
+
+def layer_inputs(N: int, H: int, D: int, pool_slots: int, seed: int = 0, n_padding: int = 0) -> LayerInputs:
+    """Draw one decode token per request for the layer's front and back operations.
+    Slots are drawn as in ``decode_inputs``: distinct active slots in
+    1..pool_slots-1, ``n_padding`` rows at random positions with slot 0 or -1."""
+    rng = np.random.default_rng(seed)
+    dim = H * D
+    x = round_to_bf16(rng.standard_normal((N, 3 * dim)))
+    conv_w = round_to_f32(rng.uniform(-0.5, 0.5, (3, 4, dim)))
+    conv_bias = round_to_f32(rng.uniform(-0.5, 0.5, 3 * dim))
+    conv_state = round_to_bf16(rng.standard_normal((pool_slots, 3 * dim, 3)))
+    beta_raw = round_to_f32(rng.standard_normal((N, H)))
+    gate = round_to_bf16(rng.standard_normal((N, dim)))
+    norm_w = round_to_f32(1.0 + 0.1 * rng.standard_normal(D))
+    n_active = N - n_padding
+    if n_active > pool_slots - 1:
+        raise ValueError("more active rows than usable pool slots")
+    slots = np.zeros(N, dtype=np.int32)
+    pad_pos = rng.choice(N, n_padding, replace=False) if n_padding else np.zeros(0, np.int64)
+    mask = np.ones(N, bool)
+    mask[pad_pos] = False
+    slots[mask] = rng.choice(np.arange(1, pool_slots), n_active, replace=False)
+    slots[pad_pos] = rng.choice(np.array([0, -1]), len(pad_pos))
+    return LayerInputs(x, conv_w, conv_bias, conv_state, slots, beta_raw, gate, norm_w, H, D)

@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
                                          "gdn_chunk_fwd_profiled", "gdn_recurrent_step", "gdn_recurrent_step_kda",
-                                         "gdn_recurrent_verify", "gdn_fp8_quant", "gdn_status_string"}
+                                         "gdn_recurrent_verify", "gdn_fp8_quant", "gdn_decode_prologue",
+                                         "gdn_gated_rmsnorm", "gdn_status_string"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -209,3 +210,44 @@ def test_recurrent_step_kda_validation():
     assert call(g=None) == E.GDN_EINVAL
     assert call(g=FAKE + 4) == E.GDN_EINVAL   # the per-channel decays are read as float4
     assert call(pool=FAKE + 4) == E.GDN_EINVAL
+
+
+def test_decode_prologue_validation():
+    E = _lib
+    args = dict(x=FAKE, w=FAKE, bias=None, state=FAKE, pool_slots=8, slots=FAKE, beta_raw=FAKE, q=FAKE, k=FAKE,
+                v=FAKE, beta=FAKE, N=4, H=2, D=128, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return _lib.lib().gdn_decode_prologue(a["x"], a["w"], a["bias"], a["state"], a["pool_slots"], a["slots"],
+                                              a["beta_raw"], a["q"], a["k"], a["v"], a["beta"], a["N"], a["H"],
+                                              a["D"], a["stream"])
+    assert call(D=96) == E.GDN_EUNSUPPORTED
+    assert call(N=0) == E.GDN_OK
+    assert call(N=-1) == E.GDN_EINVAL
+    assert call(H=0) == E.GDN_EINVAL
+    assert call(state=None) == E.GDN_EINVAL
+    assert call(beta=None) == E.GDN_EINVAL
+    assert call(pool_slots=0) == E.GDN_EINVAL
+    assert call(x=FAKE + 1) == E.GDN_EINVAL
+    assert call(bias=FAKE + 2) == E.GDN_EINVAL
+    assert call(N=1 << 20, H=4096) == E.GDN_EINVAL  # grid limit
+
+
+def test_gated_rmsnorm_validation():
+    E = _lib
+    args = dict(o=FAKE, gate=FAKE, w=FAKE, eps=1e-6, out=FAKE, N=4, H=2, D=64, out_dt=BF16, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return _lib.lib().gdn_gated_rmsnorm(a["o"], a["gate"], a["w"], a["eps"], a["out"], a["N"], a["H"], a["D"],
+                                            a["out_dt"], a["stream"])
+    assert call(D=32) == E.GDN_EUNSUPPORTED
+    assert call(out_dt=4) == E.GDN_EUNSUPPORTED
+    assert call(N=0) == E.GDN_OK
+    assert call(eps=-1.0) == E.GDN_EINVAL
+    assert call(eps=float("nan")) == E.GDN_EINVAL
+    assert call(gate=None) == E.GDN_EINVAL
+    assert call(o=FAKE + 2) == E.GDN_EINVAL
+    assert call(out=FAKE + 1) == E.GDN_EINVAL
+    assert call(N=1 << 20, H=4096) == E.GDN_EINVAL

@@ -14,7 +14,8 @@ import torch
 import oracle
 from linear_attention_sequence_recompute_amd import api
 from linear_attention_sequence_recompute_amd.workloads import (channel_log_decay, chunk_inputs, decode_inputs,
-                                                              varlen_lengths, verify_inputs)
+                                                              layer_inputs, round_to_f32, varlen_lengths,
+                                                              verify_inputs)
 from tests.gpu_util import TORCH_DT, bf16_rne, dev, host, max_err_over_rms
 
 pytestmark = pytest.mark.gpu
@@ -578,6 +579,114 @@ def test_fp8_quant_config_sampled():
     np.testing.assert_array_equal(codes[torch.from_numpy(pick).cuda()].cpu().numpy(), c_ref)
     np.testing.assert_array_equal(scales[torch.from_numpy(pick).cuda()].cpu().numpy().view(np.uint32),
                                   s_ref.view(np.uint32))
+
+
+# ------------------------------------------ decode layer front and back operations
+#
+# Tolerances: q, k, v, beta and the normalised output are float32 results of a
+# few float32 operations on exactly representable inputs, so they are held to
+# max|err| <= 1e-5 * RMS(reference); the conv state is bf16 values moved, so it is
+# compared bit for bit; a bf16 output equals RNE of the float32 output of the
+# same call.
+
+LAYER_TOL = 1e-5
+
+
+def run_prologue(li, state_dev, bias=True):
+    return api.decode_prologue(dev(li.x, torch.bfloat16), dev(li.conv_w), dev(li.conv_bias) if bias else None,
+                               state_dev, dev(li.slots, torch.int32), dev(li.beta_raw), li.H)
+
+
+def check_prologue(li, label, bias=True):
+    state0 = dev(li.conv_state, torch.bfloat16)
+    state = state0.clone()
+    q, k, v, beta = run_prologue(li, state, bias)
+    torch.cuda.synchronize()
+    rq, rk, rv, rb, rst = oracle.decode_prologue(li.x, li.conv_w, li.conv_bias if bias else None, li.conv_state,
+                                                 li.slots, li.beta_raw, li.H, li.D)
+    act = li.slots > 0
+    errs = [max_err_over_rms(host(t)[act], r[act]) for t, r in ((q, rq), (k, rk), (v, rv), (beta, rb))]
+    for t in (q, k, v, beta):
+        assert bool((t[torch.from_numpy(~act).cuda()].view(torch.int32) == 0).all()), f"{label}: padding not +0"
+    assert np.array_equal(host(state), rst), f"{label}: conv state differs"
+    _print(f"[prologue {label}] max err/rms q,k,v,beta = " + " ".join(f"{e:.2e}" for e in errs))
+    assert max(errs) <= LAYER_TOL
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bias", [True, False])
+def test_decode_prologue_small(D, bias):
+    li = layer_inputs(N=37, H=3, D=D, pool_slots=48, seed=D + bias, n_padding=5)
+    check_prologue(li, f"D={D} bias={bias}", bias)
+
+
+def test_decode_prologue_config_full():
+    """N=256 requests, H=32 heads of 128 channels, a pool of 512 conv states, 32 padding rows."""
+    li = layer_inputs(N=256, H=32, D=128, pool_slots=512, seed=9, n_padding=32)
+    check_prologue(li, "N256 H32 D128")
+
+
+def test_decode_prologue_consecutive_tokens_shift_the_state():
+    """Four tokens in a row through one slot: the state after them holds the last
+    three inputs, and every token's outputs match the oracle's running state."""
+    li = layer_inputs(N=4, H=2, D=64, pool_slots=8, seed=77)
+    state = dev(li.conv_state, torch.bfloat16)
+    st_ref = li.conv_state
+    for t in range(4):
+        x_t, b_t, slot = li.x[t:t + 1], li.beta_raw[t:t + 1], np.array([3], np.int32)
+        q, k, v, beta = api.decode_prologue(dev(x_t, torch.bfloat16), dev(li.conv_w), dev(li.conv_bias), state,
+                                            dev(slot, torch.int32), dev(b_t), li.H)
+        torch.cuda.synchronize()
+        rq, rk, rv, rb, st_ref = oracle.decode_prologue(x_t, li.conv_w, li.conv_bias, st_ref, slot, b_t, li.H,
+                                                        li.D)
+        for t_, r in ((q, rq), (k, rk), (v, rv), (beta, rb)):
+            assert max_err_over_rms(host(t_), r) <= LAYER_TOL
+    assert np.array_equal(host(state), st_ref)
+    assert np.array_equal(host(state)[3], li.x[1:4].T)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_gated_rmsnorm(D):
+    N, H = 29, 5
+    rng = np.random.default_rng(D)
+    o = rng.standard_normal((N, H, D)).astype(np.float32).astype(np.float64)
+    o[3] *= 1e-3  # a small-norm row
+    li = layer_inputs(N=N, H=H, D=D, pool_slots=N + 1, seed=D)
+    o_d = dev(o)
+    outs = {od: api.gated_rmsnorm(o_d, dev(li.gate, torch.bfloat16), dev(li.norm_w), 1e-6,
+                                  out_dtype=TORCH_DT[od]) for od in ("f32", "bf16")}
+    torch.cuda.synchronize()
+    ref = oracle.gated_rmsnorm(o, li.gate, li.norm_w, 1e-6)
+    err = max_err_over_rms(host(outs["f32"]), ref)
+    _print(f"[gated rmsnorm D={D}] max err/rms={err:.2e}")
+    assert err <= LAYER_TOL
+    assert torch.equal(outs["bf16"], bf16_rne(outs["f32"]))
+
+
+def test_decode_layer_composition():
+    """Front operations, the recurrent decode step and the gated RMSNorm in a row,
+    against the oracle's three steps: N=64 requests, H=4 heads of 128 channels."""
+    N, H, D, P = 64, 4, 128, 80
+    li = layer_inputs(N=N, H=H, D=D, pool_slots=P, seed=123, n_padding=6)
+    rng = np.random.default_rng(124)
+    a = round_to_f32(-np.log1p(np.exp(rng.standard_normal((N, H)) + 2.0)))
+    pool0 = round_to_f32(rng.normal(0.0, 0.1, (P, H, D, D)))
+    conv = dev(li.conv_state, torch.bfloat16)
+    pool = dev(pool0)
+    slots = dev(li.slots, torch.int32)
+    q, k, v, beta = run_prologue(li, conv)
+    o = api.recurrent_step(q, k, v, dev(a), beta, pool, slots, scale=D ** -0.5, out_dtype=torch.float32)
+    out = api.gated_rmsnorm(o, dev(li.gate, torch.bfloat16), dev(li.norm_w), 1e-6, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rq, rk, rv, rb, _ = oracle.decode_prologue(li.x, li.conv_w, li.conv_bias, li.conv_state, li.slots,
+                                               li.beta_raw, H, D)
+    ro, rpool = oracle.decode_step(rq, rk, rv, a, rb, pool0, li.slots, scale=D ** -0.5)
+    ref = oracle.gated_rmsnorm(ro, li.gate, li.norm_w, 1e-6)
+    act = li.slots > 0
+    e_out = max_err_over_rms(host(out)[act], ref[act])
+    e_st = max_err_over_rms(host(pool)[li.slots[act]], rpool[li.slots[act]])
+    _print(f"[decode layer] max err/rms out={e_out:.2e} state={e_st:.2e}")
+    assert e_out <= TOL["f32"] and e_st <= TOL["f32"]
 
 
 def test_graph_capture_replays_match_eager():
