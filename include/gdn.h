@@ -255,6 +255,9 @@ gdn_status gdn_fp8_quant(const float* x, void* codes, float* scales, int64_t row
  * sqrt(sum of squares + 1e-6) and beta = sigmoid(beta_raw). The query scale is
  * not applied here (the decode step takes it).
  *
+ * Alignment: x, conv_state, beta_raw, beta and slots 4 bytes; conv_w, conv_bias,
+ * q, k and v 8 bytes (each lane moves two adjacent channels).
+ *
  * Returns GDN_EUNSUPPORTED for D outside {64, 128}; GDN_EINVAL for N < 0, H
  * outside [1, 65535], N H above 2^31 - 1, a NULL pointer (other than conv_bias),
  * pool_slots <= 0 or a misaligned pointer; GDN_OK without launching for N == 0;
@@ -276,6 +279,9 @@ gdn_status gdn_decode_prologue(const void* x, const float* conv_w, const float* 
  *
  * out = o * rsqrt(mean over the head's D channels of o^2 + eps) * norm_w[c] *
  * sigmoid(gate), in float32.
+ *
+ * Alignment: o and norm_w 8 bytes; gate 4 bytes; out 4 bytes (bf16) or 8 bytes
+ * (float32).
  *
  * Returns GDN_EUNSUPPORTED for D outside {64, 128} or an unknown dtype;
  * GDN_EINVAL for N < 0, H outside [1, 65535], N H above 2^31 - 1, eps < 0 or

@@ -318,9 +318,9 @@ gdn_status gdn_decode_prologue(const void* x, const float* conv_w, const float* 
   if (N == 0) return GDN_OK;
   if (!x || !conv_w || !conv_state || !slots || !beta_raw || !q || !k || !v || !beta || pool_slots <= 0)
     return GDN_EINVAL;
-  if (!aligned(x, 2) || !aligned(conv_state, 2) || !aligned(conv_w, 4) || !aligned(slots, 4) ||
-      !aligned(beta_raw, 4) || !aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(beta, 4) ||
-      (conv_bias && !aligned(conv_bias, 4)))
+  if (!aligned(x, 4) || !aligned(conv_state, 4) || !aligned(conv_w, 8) || !aligned(slots, 4) ||
+      !aligned(beta_raw, 4) || !aligned(q, 8) || !aligned(k, 8) || !aligned(v, 8) || !aligned(beta, 4) ||
+      (conv_bias && !aligned(conv_bias, 8)))
     return GDN_EINVAL;
   gdn::PrologueArgs a{};
   a.x = x;
@@ -348,7 +348,7 @@ gdn_status gdn_gated_rmsnorm(const float* o, const void* gate, const float* norm
   if (N < 0 || H <= 0 || H > 65535 || static_cast<int64_t>(N) * H > INT32_MAX || !(eps >= 0.f)) return GDN_EINVAL;
   if (N == 0) return GDN_OK;
   if (!o || !gate || !norm_w || !out) return GDN_EINVAL;
-  if (!aligned(o, 4) || !aligned(gate, 2) || !aligned(norm_w, 4) || !aligned(out, dtype_bytes(out_dtype)))
+  if (!aligned(o, 8) || !aligned(gate, 4) || !aligned(norm_w, 8) || !aligned(out, 2 * dtype_bytes(out_dtype)))
     return GDN_EINVAL;
   gdn::RmsNormArgs a{};
   a.o = o;

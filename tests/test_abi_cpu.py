@@ -229,8 +229,10 @@ def test_decode_prologue_validation():
     assert call(state=None) == E.GDN_EINVAL
     assert call(beta=None) == E.GDN_EINVAL
     assert call(pool_slots=0) == E.GDN_EINVAL
-    assert call(x=FAKE + 1) == E.GDN_EINVAL
-    assert call(bias=FAKE + 2) == E.GDN_EINVAL
+    assert call(x=FAKE + 2) == E.GDN_EINVAL      # pairs of bf16 channels: 4-byte aligned
+    assert call(state=FAKE + 2) == E.GDN_EINVAL
+    assert call(q=FAKE + 4) == E.GDN_EINVAL      # float2 pairs: 8-byte aligned
+    assert call(bias=FAKE + 4) == E.GDN_EINVAL
     assert call(N=1 << 20, H=4096) == E.GDN_EINVAL  # grid limit
 
 
@@ -248,6 +250,8 @@ def test_gated_rmsnorm_validation():
     assert call(eps=-1.0) == E.GDN_EINVAL
     assert call(eps=float("nan")) == E.GDN_EINVAL
     assert call(gate=None) == E.GDN_EINVAL
-    assert call(o=FAKE + 2) == E.GDN_EINVAL
-    assert call(out=FAKE + 1) == E.GDN_EINVAL
+    assert call(o=FAKE + 4) == E.GDN_EINVAL
+    assert call(gate=FAKE + 2) == E.GDN_EINVAL
+    assert call(out=FAKE + 2) == E.GDN_EINVAL
+    assert call(out=FAKE + 4, out_dt=_lib.GDN_F32) == E.GDN_EINVAL
     assert call(N=1 << 20, H=4096) == E.GDN_EINVAL
