@@ -44,7 +44,7 @@ def test_conv_matches_numpy_convolve():
     check_conv(conv_silu_step)
 
 
-def test_prologue_norms():
+def check_prologue(fn):
     rng = np.random.default_rng(1)
     H, D, N = 3, 8, 5
     C = 3 * H * D
@@ -52,18 +52,54 @@ def test_prologue_norms():
     w = rng.standard_normal((3, 4, H * D))
     st = rng.standard_normal((7, C, 3))
     slots = np.array([1, 0, 3, 6, -1])
-    q, k, v, beta, _ = decode_prologue(x, w, None, st, slots, rng.standard_normal((N, H)), H, D)
+    q, k, v, beta, _ = fn(x, w, None, st, slots, rng.standard_normal((N, H)), H, D)
     for b in (0, 2, 3):
-        nq, nk = np.sum(q[b] ** 2, -1), np.sum(k[b] ** 2, -1)
+        nq, nk = np.sum(q[b] ** 2, -1), np.sum(k[b] ** 2, -1)   # per head
         assert np.all(np.abs(nq - 1) < 1e-3) and np.all(np.abs(nk - 1) < 1e-3)
         assert np.all((beta[b] > 0) & (beta[b] < 1))
     for b in (1, 4):
         assert np.all(q[b] == 0) and np.all(k[b] == 0) and np.all(v[b] == 0) and np.all(beta[b] == 0)
-    # identity convolution (only the newest tap, weight 1): v = silu(x) exactly
+    # identity convolution (only the newest tap, weight 1): v = silu(x) exactly; beta = 1/2 at raw 0
     wid = np.zeros((3, 4, H * D))
     wid[:, 3, :] = 1.0
-    _, _, v2, _, _ = decode_prologue(x, wid, None, st, slots, np.zeros((N, H)), H, D)
+    q2, _, v2, b2, _ = fn(x, wid, None, st, slots, np.zeros((N, H)), H, D)
     np.testing.assert_allclose(v2[0].ravel(), _silu(x[0, 2 * H * D:]), rtol=1e-14)
+    assert np.all(b2[[0, 2, 3]] == 0.5)
+    # a tiny q head: the 1e-6 under the root sets its norm, sum / (sum + 1e-6)
+    xs = x.copy()
+    xs[0, :D] = 1e-4
+    q3, _, _, _, _ = fn(xs, wid, None, st, slots, np.zeros((N, H)), H, D)
+    y = _silu(1e-4)
+    np.testing.assert_allclose(np.sum(q3[0, 0] ** 2), D * y * y / (D * y * y + 1e-6), rtol=1e-9)
+
+
+def test_prologue_norms():
+    check_prologue(decode_prologue)
+
+
+def _prologue_mutant(mutation):
+    def fn(x, w, bias, conv_state, slots, beta_raw, H, D):
+        y, st = conv_silu_step(x, w, bias, conv_state, slots)
+        N = y.shape[0]
+        q = y[:, :H * D].reshape(N, H, D)
+        k = y[:, H * D:2 * H * D].reshape(N, H, D)
+        v = y[:, 2 * H * D:].reshape(N, H, D)
+        if mutation == "norm_over_all_heads":
+            q = q / np.sqrt(np.sum(q * q, axis=(1, 2), keepdims=True) + 1e-6)
+            k = k / np.sqrt(np.sum(k * k, axis=(1, 2), keepdims=True) + 1e-6)
+        else:  # eps_outside_root
+            q = q / (np.sqrt(np.sum(q * q, axis=-1, keepdims=True)) + 1e-6)
+            k = k / (np.sqrt(np.sum(k * k, axis=-1, keepdims=True)) + 1e-6)
+        beta = 1.0 / (1.0 + np.exp(-np.asarray(beta_raw, np.float64)))
+        beta[np.asarray(slots) <= 0] = 0.0
+        return q, k, v, beta, st
+    return fn
+
+
+@pytest.mark.parametrize("mutation", ["norm_over_all_heads", "eps_outside_root"])
+def test_prologue_pins_catch_mistakes(mutation):
+    with pytest.raises(AssertionError):
+        check_prologue(_prologue_mutant(mutation))
 
 
 def check_rmsnorm(fn):
