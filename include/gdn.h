@@ -291,6 +291,47 @@ gdn_status gdn_decode_prologue(const void* x, const float* conv_w, const float* 
 gdn_status gdn_gated_rmsnorm(const float* o, const void* gate, const float* norm_w, float eps,
                              void* out, int N, int H, int D, gdn_dtype out_dtype, void* stream);
 
+/*
+ * Workspace bytes gdn_chunk_fwd_kda needs for B sequences of T tokens: per
+ * (sequence, chunk of 64 tokens, head) (2 * 64 * 64 + 3 * 64 * K + K) float32.
+ * Returns 0 for negative sizes, H outside [1, 65535] or K outside {64, 128}.
+ */
+size_t gdn_chunk_fwd_kda_workspace_bytes(int B, int64_t T, int H, int K);
+
+/*
+ * Chunked forward pass of the delta rule with a decay per key channel (vLLM
+ * KdaSplit page, method `update`: each key column of the state is multiplied by
+ * its own decay before the delta-rule write; here in the chunk form, chunks of 64
+ * tokens) over B sequences of T tokens each.
+ *
+ *  q, k      [B, T, H, K] in_dtype
+ *  v         [B, T, H, V] in_dtype
+ *  g         [B, T, H, K] float32   per-token, per-key-channel log-decays (<= 0),
+ *                                   raw (the library sums them within each chunk)
+ *  beta      [B, T, H] float32
+ *  o         [B, T, H, V] out_dtype
+ *  scale     multiplies q
+ *  h0, ht    float32 [B, H, V, K] or NULL (zero start; no final state). ht may
+ *            be h0 (updated in place).
+ *  workspace device scratch of at least gdn_chunk_fwd_kda_workspace_bytes(B, T,
+ *            H, K) bytes, 256-byte aligned; contents on entry are ignored.
+ *
+ * Per token: S <- S diag(exp(g_t)); delta = beta_t (v_t - S k_t);
+ * S <- S + delta k_t^T; o_t = S (scale q_t). Results in float32; o in bfloat16 is
+ * round-to-nearest-even of the float32 result. T == 0 passes h0 to ht.
+ *
+ * Returns GDN_EUNSUPPORTED for K outside {64, 128}, V not a multiple of 16 in
+ * [16, 256] or an unknown dtype; GDN_EINVAL for B outside [0, 65535], T < 0, H
+ * outside [1, 65535], a non-finite scale, a NULL input or output when T > 0, a
+ * misaligned pointer, or sizes whose grid would not fit; GDN_EWORKSPACE for a
+ * missing, small or misaligned workspace; GDN_OK without launching for B == 0;
+ * GDN_EHIP if a launch fails.
+ */
+gdn_status gdn_chunk_fwd_kda(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, void* o, int B, int64_t T, int H, int K, int V,
+                             float scale, gdn_dtype in_dtype, gdn_dtype out_dtype, const float* h0,
+                             float* ht, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code. Never NULL. */
 const char* gdn_status_string(gdn_status s);
 

@@ -291,3 +291,47 @@ def gated_rmsnorm(o: torch.Tensor, gate: torch.Tensor, norm_w: torch.Tensor, eps
                                       _dt(out_dtype), _stream(stream))
     _lib.check(st, "gdn_gated_rmsnorm")
     return out
+
+
+def chunk_fwd_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
+                  scale: Optional[float] = None, h0: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                  ht: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Chunked forward with a decay per key channel (gdn_chunk_fwd_kda) over B
+    equal-length sequences: q, k [B, T, H, K] (or [T, H, K]); v [.., V]; g float32
+    [B, T, H, K] per-channel log-decays; beta float32 [B, T, H]; h0 float32
+    [B, H, V, K] or None. Returns (o [B, T, H, V], ht or None)."""
+    squeeze = q.dim() == 3
+    if squeeze:
+        q, k, v, g, beta = (x.unsqueeze(0) for x in (q, k, v, g, beta))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32)
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError("inconsistent shapes of q, k, v, g, beta")
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=out_dtype, device=q.device)
+    _need(out, "out", out_dtype)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+        if h0.shape != (B, H, V, K):
+            raise ValueError("h0 must be [B, H, V, K]")
+    if output_final_state and ht is None:
+        ht = torch.empty((B, H, V, K), dtype=torch.float32, device=q.device)
+    if ht is not None:
+        _need(ht, "ht", torch.float32)
+    need = int(_lib.lib().gdn_chunk_fwd_kda_workspace_bytes(B, T, H, K))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = _lib.lib().gdn_chunk_fwd_kda(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(out), B, T, H, K, V,
+        float(K ** -0.5 if scale is None else scale), _dt(q.dtype), _dt(out_dtype), _ptr(h0), _ptr(ht),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check(st, "gdn_chunk_fwd_kda")
+    if squeeze:
+        out = out.squeeze(0)
+    return out, ht

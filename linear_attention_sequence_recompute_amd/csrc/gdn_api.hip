@@ -6,6 +6,7 @@
 
 #include "gdn.h"
 #include "gdn_internal.h"
+#include <cmath>
 
 namespace {
 
@@ -362,6 +363,52 @@ gdn_status gdn_gated_rmsnorm(const float* o, const void* gate, const float* norm
   a.D = D;
   a.stream = static_cast<hipStream_t>(stream);
   return hip_status(gdn::launch_gated_rmsnorm(a));
+}
+
+
+size_t gdn_chunk_fwd_kda_workspace_bytes(int B, int64_t T, int H, int K) {
+  if (B < 0 || T < 0 || H <= 0 || H > 65535 || (K != 64 && K != 128)) return 0;
+  return static_cast<size_t>(gdn::kda_workspace_floats(B, T, H, K)) * sizeof(float);
+}
+
+gdn_status gdn_chunk_fwd_kda(const void* q, const void* k, const void* v, const float* g, const float* beta, void* o,
+                             int B, int64_t T, int H, int K, int V, float scale, gdn_dtype in_dtype,
+                             gdn_dtype out_dtype, const float* h0, float* ht, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || (K != 64 && K != 128) || V % 16 != 0 || V < 16 ||
+      V > 256)
+    return GDN_EUNSUPPORTED;
+  if (B < 0 || B > 65535 || T < 0 || H <= 0 || H > 65535 || !std::isfinite(scale)) return GDN_EINVAL;
+  const int64_t NC = (T + 63) / 64;
+  if (static_cast<int64_t>(B) * NC > INT32_MAX || T > INT32_MAX) return GDN_EINVAL;
+  if (B == 0) return GDN_OK;
+  if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_EINVAL;
+  const size_t in_b = dtype_bytes(in_dtype), out_b = dtype_bytes(out_dtype);
+  if (!aligned(q, in_b) || !aligned(k, in_b) || !aligned(v, in_b) || !aligned(g, 4) || !aligned(beta, 4) ||
+      !aligned(o, out_b) || !aligned(h0, 4) || !aligned(ht, 4))
+    return GDN_EINVAL;
+  const size_t need = gdn_chunk_fwd_kda_workspace_bytes(B, T, H, K);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return GDN_EWORKSPACE;
+  gdn::KdaChunkArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.o = o;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.K = K;
+  a.V = V;
+  a.scale = scale;
+  a.in_f32 = in_dtype == GDN_F32;
+  a.out_f32 = out_dtype == GDN_F32;
+  a.h0 = h0;
+  a.ht = ht;
+  a.ws = static_cast<float*>(workspace);
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_chunk_fwd_kda(a));
 }
 
 }  // extern "C"

@@ -61,6 +61,24 @@ struct RmsNormArgs {
   hipStream_t stream;
 };
 
+struct KdaChunkArgs {
+  const void *q, *k, *v;  // [B, T, H, K] / [B, T, H, V]
+  const float* g;         // [B, T, H, K] per-channel log-decays
+  const float* beta;      // [B, T, H]
+  void* o;                // [B, T, H, V]
+  int B;
+  int64_t T;
+  int H, K, V;
+  float scale;
+  bool in_f32, out_f32;
+  const float* h0;  // [B, H, V, K] or null
+  float* ht;        // [B, H, V, K] or null
+  float* ws;        // kda_workspace_floats(B, T, H, K) floats
+  hipStream_t stream;
+  hipEvent_t events[3];  // optional: before prep, after prep, after the scan
+};
+int64_t kda_workspace_floats(int B, int64_t T, int H, int K);
+
 struct Fp8Args {
   const float* x;     // [n_groups * group] float32
   void* codes;        // [n_groups * group] uint8 (E4M3)
@@ -132,6 +150,7 @@ hipError_t launch_verify(const VerifyArgs& a);
 hipError_t launch_fp8_quant(const Fp8Args& a);
 hipError_t launch_decode_prologue(const PrologueArgs& a);
 hipError_t launch_gated_rmsnorm(const RmsNormArgs& a);
+hipError_t launch_chunk_fwd_kda(const KdaChunkArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 
 }  // namespace gdn

@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
                                          "gdn_chunk_fwd_profiled", "gdn_recurrent_step", "gdn_recurrent_step_kda",
                                          "gdn_recurrent_verify", "gdn_fp8_quant", "gdn_decode_prologue",
-                                         "gdn_gated_rmsnorm", "gdn_status_string"}
+                                         "gdn_gated_rmsnorm", "gdn_chunk_fwd_kda_workspace_bytes",
+                                         "gdn_chunk_fwd_kda", "gdn_status_string"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -255,3 +256,33 @@ def test_gated_rmsnorm_validation():
     assert call(out=FAKE + 2) == E.GDN_EINVAL
     assert call(out=FAKE + 4, out_dt=_lib.GDN_F32) == E.GDN_EINVAL
     assert call(N=1 << 20, H=4096) == E.GDN_EINVAL
+
+
+def test_chunk_fwd_kda_validation():
+    E = _lib
+    L = _lib.lib()
+    assert L.gdn_chunk_fwd_kda_workspace_bytes(1, 4096, 16, 128) == 64 * 16 * (2 * 4096 + 3 * 64 * 128 + 128) * 4
+    assert L.gdn_chunk_fwd_kda_workspace_bytes(2, 65, 3, 64) == 2 * 2 * 3 * (2 * 4096 + 3 * 64 * 64 + 64) * 4
+    assert L.gdn_chunk_fwd_kda_workspace_bytes(1, 100, 2, 96) == 0
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE, B=2, T=100, H=2, K=128, V=128, scale=1.0,
+                in_dt=BF16, out_dt=BF16, h0=None, ht=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.gdn_chunk_fwd_kda(a["q"], a["k"], a["v"], a["g"], a["beta"], a["o"], a["B"], a["T"], a["H"],
+                                   a["K"], a["V"], a["scale"], a["in_dt"], a["out_dt"], a["h0"], a["ht"], a["ws"],
+                                   a["ws_bytes"], a["stream"])
+    assert call(K=96) == E.GDN_EUNSUPPORTED
+    assert call(V=40) == E.GDN_EUNSUPPORTED
+    assert call(V=512) == E.GDN_EUNSUPPORTED
+    assert call(in_dt=4) == E.GDN_EUNSUPPORTED
+    assert call(B=0) == E.GDN_OK
+    assert call(B=-1) == E.GDN_EINVAL
+    assert call(H=0) == E.GDN_EINVAL
+    assert call(scale=float("inf")) == E.GDN_EINVAL
+    assert call(q=None) == E.GDN_EINVAL
+    assert call(q=FAKE + 1) == E.GDN_EINVAL
+    assert call(h0=FAKE + 2) == E.GDN_EINVAL
+    assert call(ws=None) == E.GDN_EWORKSPACE
+    assert call(ws_bytes=1024) == E.GDN_EWORKSPACE
+    assert call(ws=FAKE + 16) == E.GDN_EWORKSPACE

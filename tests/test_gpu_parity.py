@@ -581,6 +581,76 @@ def test_fp8_quant_config_sampled():
                                   s_ref.view(np.uint32))
 
 
+# ------------------------------------- chunk form with a decay per key channel
+
+def run_chunk_kda(ci, g, B, T, scale, out_dtype, h0=None, ht=None):
+    dt = TORCH_DT[ci.dtype]
+    H, K = ci.q.shape[1:]
+    V = ci.v.shape[-1]
+    q, k = dev(ci.q, dt).view(B, T, H, K), dev(ci.k, dt).view(B, T, H, K)
+    v = dev(ci.v, dt).view(B, T, H, V)
+    o, ht = api.chunk_fwd_kda(q, k, v, dev(g).view(B, T, H, K), dev(ci.beta).view(B, T, H), scale=scale, h0=h0,
+                              ht=ht, out_dtype=TORCH_DT[out_dtype])
+    torch.cuda.synchronize()
+    return o, ht
+
+
+def check_chunk_kda(B, T, H, K, V, dtype, seed, shift, label, heads=None):
+    ci = chunk_inputs([T] * B, H, K, V, dtype=dtype, seed=seed, h0_std=0.1)
+    g = channel_log_decay((B * T, H, K), seed + 1, shift)
+    scale = K ** -0.5
+    h0 = dev(ci.h0)
+    o32, ht32 = run_chunk_kda(ci, g, B, T, scale, "f32", h0)
+    o16, ht16 = run_chunk_kda(ci, g, B, T, scale, "bf16", h0)
+    assert torch.equal(o16, bf16_rne(o32)), f"{label}: bf16 output is not RNE of the f32 output"
+    assert torch.equal(ht16, ht32)
+    heads = list(range(H)) if heads is None else heads
+    eo = es = 0.0
+    for b in range(B):
+        sl = slice(b * T, (b + 1) * T)
+        o_ref, s_ref = oracle.recurrent_fwd_kda(ci.q[sl][:, heads], ci.k[sl][:, heads], ci.v[sl][:, heads],
+                                                g[sl][:, heads], ci.beta[sl][:, heads], scale=scale,
+                                                S0=ci.h0[b][heads])
+        eo = max(eo, max_err_over_rms(host(o32[b])[:, heads], o_ref))
+        es = max(es, max_err_over_rms(host(ht32[b])[heads], s_ref))
+    tol = TOL[dtype]
+    _print(f"[chunk kda {label}] max|do|/rms={eo:.3e} max|dS|/rms={es:.3e} tol={tol}")
+    assert eo <= tol and es <= tol
+
+
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chunk_kda_small(K, V, dtype):
+    """Two sequences of 150 tokens (two full chunks and a ragged one), three heads."""
+    check_chunk_kda(2, 150, 3, K, V, dtype, seed=90 + K + V, shift=2.0, label=f"K={K} V={V} {dtype}")
+
+
+def test_chunk_kda_long_memory():
+    """Slow per-channel decays (shift -4): the carry across chunks dominates."""
+    check_chunk_kda(1, 300, 2, 128, 128, "bf16", seed=97, shift=-4.0, label="long memory")
+
+
+def test_chunk_kda_config_sampled():
+    """B=1, H=16, T=4096, K=V=128 (the chunk workload's shape), heads 0, 7, 15 against the oracle."""
+    check_chunk_kda(1, 4096, 16, 128, 128, "bf16", seed=98, shift=2.0, label="H16 T4096", heads=[0, 7, 15])
+
+
+def test_chunk_kda_empty_and_in_place():
+    ci = chunk_inputs([1, 1], 2, 64, 64, dtype="bf16", seed=99, h0_std=0.1)
+    h0 = dev(ci.h0)
+    g = channel_log_decay((2, 2, 64), 100)
+    empty = ci.q[:0]
+    o, ht = api.chunk_fwd_kda(dev(empty, torch.bfloat16).view(2, 0, 2, 64), dev(empty, torch.bfloat16).view(2, 0, 2, 64),
+                              dev(ci.v[:0], torch.bfloat16).view(2, 0, 2, 64), dev(g[:0]).view(2, 0, 2, 64),
+                              dev(ci.beta[:0]).view(2, 0, 2), h0=h0)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(ht, h0)  # T == 0 passes the initial state through
+    o1, ht1 = run_chunk_kda(ci, g, 2, 1, 0.5, "f32", h0)
+    state = h0.clone()
+    o2, ht2 = run_chunk_kda(ci, g, 2, 1, 0.5, "f32", state, ht=state)  # in place
+    assert torch.equal(o1, o2) and torch.equal(ht1, state)
+
+
 # ------------------------------------------ decode layer front and back operations
 #
 # Tolerances: q, k, v, beta and the normalised output are float32 results of a
