@@ -18,7 +18,7 @@ the summary and scan kernels), is its algorithmic FLOPs per call over that
 duration.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-       python bench.py --only chunk|decode|copy --steps K   (profiling runs)
+       python bench.py --only chunk|decode|kda|verify|fp8|layer|chunk_kda|copy --steps K   (profiling runs)
 """
 
 from __future__ import annotations
@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 CSRC = os.path.join(ROOT, "linear_attention_sequence_recompute_amd", "csrc")
 
@@ -203,6 +204,61 @@ def bench_chunk(torch, api, hev, steps, warmup, flush_bytes=512 << 20):
     del flush
     return dict(wall_s=wall, prep_ms=stats(prep), scan_ms=stats(scan), call_ms=stats(whole),
                 cold_prep_ms=stats(cold_prep), cold_scan_ms=stats(cold_scan))
+
+
+def kda_chunk_flops():
+    """Algorithmic flops per call of the chunk form with per-channel decays at the
+    chunk workload's shape. Scan, per (chunk, head, value column): (K o e^G) h,
+    (s q o e^G) h and (K o e^{G_last - G})^T D, 64 K multiply-adds each, and
+    A' R and P D, 64 * 64 each. Prep, per (chunk, head): 2080 token pairs x K
+    channels (one exponent, three multiply-adds), the substitution 64 * 2016
+    multiply-adds, and the three scaled operands (64 K, two exponents)."""
+    nch = B * (T // C) * H
+    scan = nch * V * 2 * (3 * C * K + 2 * C * C)
+    prep = nch * (2080 * K * 7 + 2 * C * 2016 + C * K * 5)
+    return scan, prep
+
+
+def bench_chunk_kda(torch, api, hev, steps, warmup):
+    """The chunk form with a decay per key channel at the chunk workload's shape:
+    B=1, H=16, T=4096, K=V=128, bf16 in and out, per-channel log-decays."""
+    from linear_attention_sequence_recompute_amd.workloads import channel_log_decay, chunk_inputs
+
+    ci = chunk_inputs([T] * B, H, K, V, dtype="bf16", seed=2)
+    dev = torch.device("cuda")
+
+    def t(x, dt):
+        return torch.from_numpy(x).to(dt).to(dev).view(B, T, *x.shape[1:])
+
+    q, k, v = (t(x, torch.bfloat16) for x in (ci.q, ci.k, ci.v))
+    g = t(channel_log_decay((B * T, H, K), 3), torch.float32)
+    b = t(ci.beta, torch.float32)
+    o = torch.empty(B, T, H, V, dtype=torch.bfloat16, device=dev)
+    ht = torch.empty(B, H, V, K, dtype=torch.float32, device=dev)
+    ws = torch.empty(int(api._lib.lib().gdn_chunk_fwd_kda_workspace_bytes(B, T, H, K)), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        api.chunk_fwd_kda(q, k, v, g, b, scale=K ** -0.5, out=o, ht=ht, workspace=ws, stream=stream, events=evs)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [hev.create(3) for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    prep = [hev.ms(e[0], e[1]) for e in evs]
+    scan = [hev.ms(e[1], e[2]) for e in evs]
+    for e in evs:
+        hev.destroy(e)
+    return dict(wall_s=wall, prep_ms=stats(prep), scan_ms=stats(scan))
 
 
 def bench_decode(torch, api, hev, steps, warmup):
@@ -444,7 +500,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "kda", "verify", "fp8", "layer", "copy"], default="all")
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "kda", "verify", "fp8", "layer", "chunk_kda", "copy"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -496,6 +552,11 @@ def main():
         log(f"decode layer front/back: N={DN} H={DH} D={DK} conv pool={DSLOTS} ...")
         res_l = bench_layer(torch, api, hev, args.steps, args.warmup)
         log(json.dumps(res_l))
+    res_ck = None
+    if args.only in ("all", "chunk_kda"):
+        log("chunk form with per-channel decays: B=1 H=16 T=4096 K=V=128 bf16 ...")
+        res_ck = bench_chunk_kda(torch, api, hev, args.steps, args.warmup)
+        log(json.dumps(res_ck))
     if args.only != "all":
         return
 
@@ -584,6 +645,22 @@ def main():
                           "roofline": {"bound": "hbm", "achieved": lr_b / lr_s / 1e9, "peak": PEAK_HBM_GBS,
                                        "unit": "GB/s", "frac": lr_b / lr_s / 1e9 / PEAK_HBM_GBS,
                                        "traffic": traffic_for("gated_rmsnorm_kernel")}}}
+    ck_scan_f, ck_prep_f = kda_chunk_flops()
+    ck_scan_s, ck_prep_s = res_ck["scan_ms"]["mean"] / 1e3, res_ck["prep_ms"]["mean"] / 1e3
+    ck_ms = 1e3 * res_ck["wall_s"] / args.steps
+    out["chunk_kda"] = {
+        "workload": "chunk form of the delta rule with a log-decay per key channel, B=1 H=16 T=4096 K=V=128 C=64, "
+                    "bf16 q/k/v/o, fp32 g [T, H, K] and beta, fp32 final state",
+        "value": B * T / (ck_ms / 1e3), "unit": "tokens/s", "ms_per_call": ck_ms,
+        "kernels_us": {"prep": ck_prep_s * 1e6, "scan": ck_scan_s * 1e6},
+        "roofline": {"bound": "alu", "kernel": "kda_scan_kernel (fp32 VALU)", "achieved": ck_scan_f / ck_scan_s / 1e12,
+                     "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ck_scan_f / ck_scan_s / 1e12 / PEAK_FP32_TFLOPS,
+                     "traffic": traffic_for("kda_scan_kernel"), "flops_per_launch": ck_scan_f,
+                     "avg_launch_us": ck_scan_s * 1e6},
+        "prep_roofline": {"bound": "alu", "achieved": ck_prep_f / ck_prep_s / 1e12, "peak": PEAK_FP32_TFLOPS,
+                          "unit": "TFLOP/s", "frac": ck_prep_f / ck_prep_s / 1e12 / PEAK_FP32_TFLOPS,
+                          "traffic": traffic_for("kda_prep_kernel"), "flops_per_launch": ck_prep_f}}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -332,6 +332,18 @@ gdn_status gdn_chunk_fwd_kda(const void* q, const void* k, const void* v, const 
                              float scale, gdn_dtype in_dtype, gdn_dtype out_dtype, const float* h0,
                              float* ht, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Diagnostic variant of gdn_chunk_fwd_kda for measurement: same arguments and
+ * results; in addition it records three caller-created HIP events (hipEvent_t,
+ * passed as void*) on `stream`: events[0] before the prep kernel, events[1]
+ * after it, events[2] after the scan. GDN_EINVAL if events or one of them is NULL.
+ */
+gdn_status gdn_chunk_fwd_kda_profiled(const void* q, const void* k, const void* v, const float* g,
+                                      const float* beta, void* o, int B, int64_t T, int H, int K,
+                                      int V, float scale, gdn_dtype in_dtype, gdn_dtype out_dtype,
+                                      const float* h0, float* ht, void* workspace,
+                                      size_t workspace_bytes, void* stream, void* const* events);
+
 /* Static, human-readable name of a status code. Never NULL. */
 const char* gdn_status_string(gdn_status s);
 

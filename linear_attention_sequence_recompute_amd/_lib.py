@@ -37,6 +37,8 @@ SIGNATURES = {
     "gdn_chunk_fwd_kda_workspace_bytes": (ctypes.c_size_t, [_I, _I64, _I, _I]),
     "gdn_chunk_fwd_kda": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I, _P, _P, _P, ctypes.c_size_t,
                                _P]),
+    "gdn_chunk_fwd_kda_profiled": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I, _P, _P, _P,
+                                        ctypes.c_size_t, _P, _P]),
     "gdn_status_string": (ctypes.c_char_p, [_I]),
 }
 

@@ -296,7 +296,8 @@ def gated_rmsnorm(o: torch.Tensor, gate: torch.Tensor, norm_w: torch.Tensor, eps
 def chunk_fwd_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
                   scale: Optional[float] = None, h0: Optional[torch.Tensor] = None, output_final_state: bool = True,
                   ht: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
-                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+                  events: Optional[Sequence[int]] = None):
     """Chunked forward with a decay per key channel (gdn_chunk_fwd_kda) over B
     equal-length sequences: q, k [B, T, H, K] (or [T, H, K]); v [.., V]; g float32
     [B, T, H, K] per-channel log-decays; beta float32 [B, T, H]; h0 float32
@@ -327,10 +328,13 @@ def chunk_fwd_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     need = int(_lib.lib().gdn_chunk_fwd_kda_workspace_bytes(B, T, H, K))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    st = _lib.lib().gdn_chunk_fwd_kda(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(out), B, T, H, K, V,
-        float(K ** -0.5 if scale is None else scale), _dt(q.dtype), _dt(out_dtype), _ptr(h0), _ptr(ht),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(out), B, T, H, K, V,
+            float(K ** -0.5 if scale is None else scale), _dt(q.dtype), _dt(out_dtype), _ptr(h0), _ptr(ht),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if events is None:
+        st = _lib.lib().gdn_chunk_fwd_kda(*args)
+    else:
+        st = _lib.lib().gdn_chunk_fwd_kda_profiled(*args, (ctypes.c_void_p * 3)(*events))
     _lib.check(st, "gdn_chunk_fwd_kda")
     if squeeze:
         out = out.squeeze(0)

@@ -371,10 +371,10 @@ size_t gdn_chunk_fwd_kda_workspace_bytes(int B, int64_t T, int H, int K) {
   return static_cast<size_t>(gdn::kda_workspace_floats(B, T, H, K)) * sizeof(float);
 }
 
-gdn_status gdn_chunk_fwd_kda(const void* q, const void* k, const void* v, const float* g, const float* beta, void* o,
-                             int B, int64_t T, int H, int K, int V, float scale, gdn_dtype in_dtype,
-                             gdn_dtype out_dtype, const float* h0, float* ht, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+static gdn_status chunk_fwd_kda_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                     void* o, int B, int64_t T, int H, int K, int V, float scale, gdn_dtype in_dtype,
+                                     gdn_dtype out_dtype, const float* h0, float* ht, void* workspace,
+                                     size_t workspace_bytes, void* stream, void* const* events) {
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || (K != 64 && K != 128) || V % 16 != 0 || V < 16 ||
       V > 256)
     return GDN_EUNSUPPORTED;
@@ -408,7 +408,25 @@ gdn_status gdn_chunk_fwd_kda(const void* q, const void* k, const void* v, const 
   a.ht = ht;
   a.ws = static_cast<float*>(workspace);
   a.stream = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < 3; ++i) a.events[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
   return hip_status(gdn::launch_chunk_fwd_kda(a));
+}
+
+gdn_status gdn_chunk_fwd_kda(const void* q, const void* k, const void* v, const float* g, const float* beta, void* o,
+                             int B, int64_t T, int H, int K, int V, float scale, gdn_dtype in_dtype,
+                             gdn_dtype out_dtype, const float* h0, float* ht, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return chunk_fwd_kda_impl(q, k, v, g, beta, o, B, T, H, K, V, scale, in_dtype, out_dtype, h0, ht, workspace,
+                            workspace_bytes, stream, nullptr);
+}
+
+gdn_status gdn_chunk_fwd_kda_profiled(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                      void* o, int B, int64_t T, int H, int K, int V, float scale,
+                                      gdn_dtype in_dtype, gdn_dtype out_dtype, const float* h0, float* ht,
+                                      void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  if (!events || !events[0] || !events[1] || !events[2]) return GDN_EINVAL;
+  return chunk_fwd_kda_impl(q, k, v, g, beta, o, B, T, H, K, V, scale, in_dtype, out_dtype, h0, ht, workspace,
+                            workspace_bytes, stream, events);
 }
 
 }  // extern "C"

@@ -12,9 +12,12 @@
 //   h' = diag(e^{G_last}) h + (K o e^{G_last - G})^T D
 // Every exponent above is <= 0, so nothing overflows. prep forms, per (chunk,
 // head), A' = (I + L)^{-1} diag(beta), P and the three scaled K / q operands;
-// the scan carries a 16-column slice of h through the chunks of a sequence.
+// the scan carries a 16-column slice of h through the chunks of a sequence, its
+// products on the fp32 MFMA.
 #include "gdn_common.h"
 #include "gdn_internal.h"
+
+#include <utility>
 
 namespace gdn {
 
@@ -123,127 +126,182 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
   }
 }
 
-// One workgroup per (value slice of 16 columns, head, sequence); the slice of the
-// state [K][16] stays in LDS across the sequence's chunks.
+// Scan operands of one (chunk, head) in LDS: rows padded by 4 floats so that
+// the 16 rows one MFMA operand read touches spread over the banks.
+template <int K>
+struct KdaScanLds {
+  static constexpr int LDX = K + 4, LDA = 68;
+  static constexpr int kRowF4 = K / 4;            // float4 per [64][K] row
+  static constexpr int kMK = 64 * kRowF4 / 256;   // prefetch steps per [64][K] operand
+  static constexpr int kSteps = 8 + 3 * kMK + 1;  // A', P (4 steps each), three [64][K], e^{G_last}
+  float Kg[64 * LDX], Qg[64 * LDX], Kd[64 * LDX];
+  float Ap[64 * LDA], P[64 * LDA];
+  float gL[K];
+  float h[K * 16];   // the state slice [key][16 value columns]
+  float R[64 * 16];  // V - (K o e^G) h
+  float D[64 * 16];  // the chunk's deltas
+};
+
+// The chunk's workspace block, float4 f = tid + 256 m, loaded into registers:
+// steps [0, kHalf) in one array and the rest in another (two arrays of this size
+// stay in registers where one of the whole size is placed in scratch memory).
+template <int K>
+struct KdaPf {
+  static constexpr int kHalf = KdaScanLds<K>::kSteps / 2;
+  float4 a[kHalf];
+  float4 b[KdaScanLds<K>::kSteps - kHalf];
+};
+
+template <int K, int M>
+__device__ __forceinline__ float4 kda_ld(const float4* s4, int tid) {
+  using L = KdaScanLds<K>;
+  return M < L::kSteps - 1 ? s4[tid + 256 * M] : s4[min(tid, K / 4 - 1) + 256 * M];  // last: e^{G_last}, no branch
+}
+
+template <int K, int M>
+__device__ __forceinline__ void kda_st(const float4& x, KdaScanLds<K>& sm, int tid) {
+  using L = KdaScanLds<K>;
+  if constexpr (M == L::kSteps - 1) {
+    if (tid < K / 4) *reinterpret_cast<float4*>(&sm.gL[4 * tid]) = x;
+  } else {
+    float* dst;
+    if constexpr (M < 8) {
+      const int f = tid + 256 * (M & 3);
+      dst = (M < 4 ? sm.Ap : sm.P) + (f >> 4) * L::LDA + 4 * (f & 15);
+    } else {
+      constexpr int op = (M - 8) / L::kMK;
+      const int f = tid + 256 * ((M - 8) % L::kMK);
+      dst = (op == 0 ? sm.Kg : op == 1 ? sm.Qg : sm.Kd) + (f / L::kRowF4) * L::LDX + 4 * (f % L::kRowF4);
+    }
+    *reinterpret_cast<float4*>(dst) = x;
+  }
+}
+
+template <int K, int... Ms>
+__device__ __forceinline__ void kda_prefetch_seq(KdaPf<K>& pf, const float4* s4, int tid,
+                                                 std::integer_sequence<int, Ms...>) {
+  constexpr int h = KdaPf<K>::kHalf;
+  ((Ms < h ? (void)(pf.a[Ms < h ? Ms : 0] = kda_ld<K, Ms>(s4, tid))
+           : (void)(pf.b[Ms < h ? 0 : Ms - h] = kda_ld<K, Ms>(s4, tid))), ...);
+}
+template <int K, int... Ms>
+__device__ __forceinline__ void kda_stage_seq(const KdaPf<K>& pf, KdaScanLds<K>& sm, int tid,
+                                              std::integer_sequence<int, Ms...>) {
+  constexpr int h = KdaPf<K>::kHalf;
+  ((Ms < h ? kda_st<K, Ms>(pf.a[Ms < h ? Ms : 0], sm, tid) : kda_st<K, Ms>(pf.b[Ms < h ? 0 : Ms - h], sm, tid)),
+   ...);
+}
+template <int K>
+__device__ __forceinline__ void kda_prefetch(KdaPf<K>& pf, const float* src, int tid) {
+  kda_prefetch_seq<K>(pf, reinterpret_cast<const float4*>(src), tid,
+                      std::make_integer_sequence<int, KdaScanLds<K>::kSteps>{});
+}
+template <int K>
+__device__ __forceinline__ void kda_stage(const KdaPf<K>& pf, KdaScanLds<K>& sm, int tid) {
+  kda_stage_seq<K>(pf, sm, tid, std::make_integer_sequence<int, KdaScanLds<K>::kSteps>{});
+}
+
+// One workgroup (4 waves) per (value slice of 16 columns, head, sequence); the
+// slice of the state [K][16] stays in LDS across the sequence's chunks. All four
+// products of a chunk run on v_mfma_f32_16x16x4f32 (fp32 in, fp32 out): lane
+// (g, c) supplies a = X[c][k] and b = Y[k][c] for k = 4 kk + g and holds rows
+// 4 g .. 4 g + 3, column c of the 16 x 16 result. Wave w owns token rows
+// 16 w .. 16 w + 15 of R, D and o, and K / 64 of the state's 16-row tiles. The
+// next chunk's operands are loaded into registers while this one is computed.
 template <int K, typename Tin, typename Tout>
 __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __restrict__ v, const float* __restrict__ ws,
                                                                const float* h0, float* ht, Tout* __restrict__ o,
                                                                int T, int H, int V, int NC) {
-  __shared__ __attribute__((aligned(16))) float sh[K][kKdaSlice];
-  __shared__ __attribute__((aligned(16))) float sR[64][kKdaSlice];
-  __shared__ __attribute__((aligned(16))) float sVn[64][kKdaSlice];
+  using L = KdaScanLds<K>;
+  __shared__ __attribute__((aligned(16))) L sm;
   const int h = blockIdx.y, b = blockIdx.z;
   const int v_base = blockIdx.x * kKdaSlice;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int64_t st_base = (static_cast<int64_t>(b) * H + h) * V + v_base;  // state [.., V, K] rows of this slice
   for (int e = tid; e < K * kKdaSlice; e += kKdaThreads) {
     const int cc = e % K, vv = e / K;
-    sh[cc][vv] = h0 ? h0[(st_base + vv) * K + cc] : 0.f;
+    sm.h[cc * 16 + vv] = h0 ? h0[(st_base + vv) * K + cc] : 0.f;
   }
-  __syncthreads();
-  const int i = tid >> 2, v0 = (tid & 3) * 4;  // token row, 4 value columns
-  constexpr int TPR = kKdaThreads / K, CPT = kKdaSlice / TPR;
-  const int hr = tid / TPR, hc0 = (tid % TPR) * CPT;  // state row (key channel), CPT columns
   const int64_t per = kda_floats_per_chunk(K);
-  for (int c = 0; c < NC; ++c) {
-    const float* base = ws + ((static_cast<int64_t>(b) * NC + c) * H + h) * per;
-    const float *Ap = base, *P = base + 4096, *Kg = base + 8192, *Qg = Kg + 64 * K, *Kd = Qg + 64 * K,
-                *gL = Kd + 64 * K;
-    const int t0 = c * 64, n = min(64, T - t0);
-    const int64_t row = (static_cast<int64_t>(b) * T + t0 + i) * H + h;
-    // R = V - (K o e^G) h
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i < n) {
-      const Tin* vp = v + row * V + v_base + v0;
-      acc = make_float4(ld_in(vp), ld_in(vp + 1), ld_in(vp + 2), ld_in(vp + 3));
-    }
-#pragma unroll 4
-    for (int cc = 0; cc < K; cc += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(Kg + i * K + cc);
-      const float av[4] = {a.x, a.y, a.z, a.w};
+  const float* ws_bh = ws + (static_cast<int64_t>(b) * NC * H + h) * per;  // chunk c at + c * H * per
+  // The next chunk's operands, loaded while this one is computed.
+  KdaPf<K> pf;
+  Tin vr[4];
+  auto load_v = [&](int ch) __attribute__((always_inline)) {  // lane's V values: rows 16 w + 4 g + r, column c
+    const int t0 = ch * 64, n = min(64, T - t0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float4 hv = *reinterpret_cast<const float4*>(&sh[cc + e][v0]);
-        acc.x = fmaf(-av[e], hv.x, acc.x);
-        acc.y = fmaf(-av[e], hv.y, acc.y);
-        acc.z = fmaf(-av[e], hv.z, acc.z);
-        acc.w = fmaf(-av[e], hv.w, acc.w);
-      }
+    for (int r = 0; r < 4; ++r) {
+      // Rows past the end read the last row and are zeroed where used: a load
+      // under a branch would be waited for at once, and with it the prefetch.
+      const int ic = min(16 * w + 4 * g + r, n - 1);
+      vr[r] = v[((static_cast<int64_t>(b) * T + t0 + ic) * H + h) * V + v_base + c];
     }
-    *reinterpret_cast<float4*>(&sR[i][v0]) = acc;
+  };
+  const int n_jj = 4 * w + 4;  // A' and P vanish above the diagonal: k < 16 (w + 1)
+  if (NC > 0) {
+    kda_prefetch<K>(pf, ws_bh, tid);
+    load_v(0);
+  }
+  for (int ch = 0; ch < NC; ++ch) {
+    const int t0 = ch * 64, n = min(64, T - t0);
+    __syncthreads();  // the previous chunk is done with the operands and the state
+    kda_stage<K>(pf, sm, tid);
+    float vcur[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vcur[r] = 16 * w + 4 * g + r < n ? ld_in(&vr[r]) : 0.f;
+    {  // the last chunk reloads itself (unused): an unconditional load keeps pf in registers
+      const int nx = min(ch + 1, NC - 1);
+      kda_prefetch<K>(pf, ws_bh + static_cast<int64_t>(nx) * H * per, tid);
+      load_v(nx);
+    }
+    __syncthreads();
+    // R = V - (K o e^G) h
+    f32x4 acc = zero4();
+#pragma unroll 8
+    for (int kk = 0; kk < K / 4; ++kk)
+      acc = mfma_f32(sm.Kg[(16 * w + c) * L::LDX + 4 * kk + g], sm.h[(4 * kk + g) * 16 + c], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.R[(16 * w + 4 * g + r) * 16 + c] = vcur[r] - acc[r];
     __syncthreads();
     // D = A' R
-    float4 dn = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-    for (int j = 0; j < 64; j += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(Ap + i * 64 + j);
-      const float av[4] = {a.x, a.y, a.z, a.w};
+    acc = zero4();
+    for (int jj = 0; jj < n_jj; ++jj)
+      acc = mfma_f32(sm.Ap[(16 * w + c) * L::LDA + 4 * jj + g], sm.R[(4 * jj + g) * 16 + c], acc);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float4 r = *reinterpret_cast<const float4*>(&sR[j + e][v0]);
-        dn.x = fmaf(av[e], r.x, dn.x);
-        dn.y = fmaf(av[e], r.y, dn.y);
-        dn.z = fmaf(av[e], r.z, dn.z);
-        dn.w = fmaf(av[e], r.w, dn.w);
-      }
-    }
-    *reinterpret_cast<float4*>(&sVn[i][v0]) = dn;
+    for (int r = 0; r < 4; ++r) sm.D[(16 * w + 4 * g + r) * 16 + c] = acc[r];
     __syncthreads();
     // o = (s q o e^G) h + P D
-    float4 ov = make_float4(0.f, 0.f, 0.f, 0.f);
+    acc = zero4();
+#pragma unroll 8
+    for (int kk = 0; kk < K / 4; ++kk)
+      acc = mfma_f32(sm.Qg[(16 * w + c) * L::LDX + 4 * kk + g], sm.h[(4 * kk + g) * 16 + c], acc);
+    for (int jj = 0; jj < n_jj; ++jj)
+      acc = mfma_f32(sm.P[(16 * w + c) * L::LDA + 4 * jj + g], sm.D[(4 * jj + g) * 16 + c], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * w + 4 * g + r;
+      if (i < n) store_out(o + ((static_cast<int64_t>(b) * T + t0 + i) * H + h) * V + v_base + c, acc[r]);
+    }
+    __syncthreads();  // every wave has read the state
+    // h' = diag(e^{G_last}) h + (K o e^{G_last - G})^T D, 16 state rows at a time
+#pragma unroll
+    for (int u = 0; u < K / 64; ++u) {
+      const int t = w * (K / 64) + u;
+      f32x4 hs;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hs[r] = sm.gL[16 * t + 4 * g + r] * sm.h[(16 * t + 4 * g + r) * 16 + c];
 #pragma unroll 4
-    for (int cc = 0; cc < K; cc += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(Qg + i * K + cc);
-      const float av[4] = {a.x, a.y, a.z, a.w};
+      for (int ii = 0; ii < 16; ++ii)
+        hs = mfma_f32(sm.Kd[(4 * ii + g) * L::LDX + 16 * t + c], sm.D[(4 * ii + g) * 16 + c], hs);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float4 hv = *reinterpret_cast<const float4*>(&sh[cc + e][v0]);
-        ov.x = fmaf(av[e], hv.x, ov.x);
-        ov.y = fmaf(av[e], hv.y, ov.y);
-        ov.z = fmaf(av[e], hv.z, ov.z);
-        ov.w = fmaf(av[e], hv.w, ov.w);
-      }
+      for (int r = 0; r < 4; ++r) sm.h[(16 * t + 4 * g + r) * 16 + c] = hs[r];
     }
-#pragma unroll 4
-    for (int j = 0; j < 64; j += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(P + i * 64 + j);
-      const float av[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float4 r = *reinterpret_cast<const float4*>(&sVn[j + e][v0]);
-        ov.x = fmaf(av[e], r.x, ov.x);
-        ov.y = fmaf(av[e], r.y, ov.y);
-        ov.z = fmaf(av[e], r.z, ov.z);
-        ov.w = fmaf(av[e], r.w, ov.w);
-      }
-    }
-    if (i < n) {
-      Tout* op = o + row * V + v_base + v0;
-      store_out(op, ov.x);
-      store_out(op + 1, ov.y);
-      store_out(op + 2, ov.z);
-      store_out(op + 3, ov.w);
-    }
-    __syncthreads();  // the state is read above and rewritten below
-    // h' = diag(e^{G_last}) h + (K o e^{G_last - G})^T D
-    float hn[CPT];
-    const float gl = gL[hr];
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) hn[r] = gl * sh[hr][hc0 + r];
-#pragma unroll 4
-    for (int ii = 0; ii < 64; ++ii) {
-      const float kd = Kd[ii * K + hr];
-#pragma unroll
-      for (int r = 0; r < CPT; ++r) hn[r] = fmaf(kd, sVn[ii][hc0 + r], hn[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) sh[hr][hc0 + r] = hn[r];
-    __syncthreads();
   }
+  __syncthreads();
   if (ht)
     for (int e = tid; e < K * kKdaSlice; e += kKdaThreads) {
       const int cc = e % K, vv = e / K;
-      ht[(st_base + vv) * K + cc] = sh[cc][vv];
+      ht[(st_base + vv) * K + cc] = sm.h[cc * 16 + vv];
     }
 }
 

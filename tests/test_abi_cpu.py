@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
                                          "gdn_chunk_fwd_profiled", "gdn_recurrent_step", "gdn_recurrent_step_kda",
                                          "gdn_recurrent_verify", "gdn_fp8_quant", "gdn_decode_prologue",
                                          "gdn_gated_rmsnorm", "gdn_chunk_fwd_kda_workspace_bytes",
-                                         "gdn_chunk_fwd_kda", "gdn_status_string"}
+                                         "gdn_chunk_fwd_kda", "gdn_chunk_fwd_kda_profiled", "gdn_status_string"}
 
 
 def test_library_exports_every_declared_symbol():
