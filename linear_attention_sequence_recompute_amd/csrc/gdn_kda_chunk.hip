@@ -22,6 +22,12 @@
 namespace gdn {
 
 constexpr int kKdaThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^x by the hardware's v_exp_f32 (about 1 ulp); every argument here is <= 0, and
+// results below the normal range become 0, as the exponentials they stand for
+// are then negligible against the other terms of their sums.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int kKdaSlice = 16;  // value columns of the state per scan workgroup
 
 // Floats per (chunk, head) in the workspace: A' [64][64], P [64][64], then
@@ -59,7 +65,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
     }
     sQ[i * LD + cc] = qv;
     sK[i * LD + cc] = kv;
-    sG[i * LD + cc] = gv;
+    sG[i * LD + cc] = gv * kLog2e;  // base-2 exponents: e^x = 2^(x log2 e)
   }
   if (tid < 64) sB[tid] = tid < n ? beta[(static_cast<int64_t>(b) * T + t0 + tid) * H + h] : 0.f;
   __syncthreads();
@@ -86,7 +92,8 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
       const float4 kj = *reinterpret_cast<const float4*>(&sK[j * LD + cc]);
       const float4 gi = *reinterpret_cast<const float4*>(&sG[i * LD + cc]);
       const float4 gj = *reinterpret_cast<const float4*>(&sG[j * LD + cc]);
-      const float e0 = expf(gi.x - gj.x), e1 = expf(gi.y - gj.y), e2 = expf(gi.z - gj.z), e3 = expf(gi.w - gj.w);
+      const float e0 = exp2_hw(gi.x - gj.x), e1 = exp2_hw(gi.y - gj.y), e2 = exp2_hw(gi.z - gj.z),
+                  e3 = exp2_hw(gi.w - gj.w);
       const float w0 = kj.x * e0, w1 = kj.y * e1, w2 = kj.z * e2, w3 = kj.w * e3;
       accP = fmaf(qi.x, w0, fmaf(qi.y, w1, fmaf(qi.z, w2, fmaf(qi.w, w3, accP))));
       accL = fmaf(ki.x, w0, fmaf(ki.y, w1, fmaf(ki.z, w2, fmaf(ki.w, w3, accL))));
@@ -102,8 +109,16 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
     const int j = tid;
     sA[0][j] = j == 0 ? 1.f : 0.f;
     for (int i = 1; i < 64; ++i) {
-      float acc = 0.f;
-      for (int m = 0; m < i; ++m) acc = fmaf(sL[i][m], sA[m][j], acc);
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;  // four chains hide the FMA latency
+      int m = 0;
+      for (; m + 3 < i; m += 4) {
+        a0 = fmaf(sL[i][m], sA[m][j], a0);
+        a1 = fmaf(sL[i][m + 1], sA[m + 1][j], a1);
+        a2 = fmaf(sL[i][m + 2], sA[m + 2][j], a2);
+        a3 = fmaf(sL[i][m + 3], sA[m + 3][j], a3);
+      }
+      for (; m < i; ++m) a0 = fmaf(sL[i][m], sA[m][j], a0);
+      const float acc = (a0 + a1) + (a2 + a3);
       sA[i][j] = i == j ? 1.f : (i > j ? -acc : 0.f);
     }
   } else {
@@ -111,12 +126,12 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
     for (int e = tid - 64; e < 64 * K; e += kKdaThreads - 64) {
       const int i = e / K, cc = e % K;
       const float G = sG[i * LD + cc], GL = sG[63 * LD + cc];
-      const float eg = expf(G);
+      const float eg = exp2_hw(G);
       Kg[e] = sK[i * LD + cc] * eg;
       Qg[e] = scale * sQ[i * LD + cc] * eg;
-      Kd[e] = sK[i * LD + cc] * expf(GL - G);
+      Kd[e] = sK[i * LD + cc] * exp2_hw(GL - G);
     }
-    for (int cc = tid - 64; cc < K; cc += kKdaThreads - 64) gL[cc] = expf(sG[63 * LD + cc]);
+    for (int cc = tid - 64; cc < K; cc += kKdaThreads - 64) gL[cc] = exp2_hw(sG[63 * LD + cc]);
   }
   __syncthreads();
   for (int e = tid; e < 4096; e += kKdaThreads) {
