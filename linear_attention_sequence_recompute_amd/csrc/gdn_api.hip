@@ -380,7 +380,9 @@ static gdn_status chunk_fwd_kda_impl(const void* q, const void* k, const void* v
     return GDN_EUNSUPPORTED;
   if (B < 0 || B > 65535 || T < 0 || H <= 0 || H > 65535 || !std::isfinite(scale)) return GDN_EINVAL;
   const int64_t NC = (T + 63) / 64;
-  if (static_cast<int64_t>(B) * NC > INT32_MAX || T > INT32_MAX) return GDN_EINVAL;
+  if (static_cast<int64_t>(B) * NC > INT32_MAX || T > INT32_MAX ||
+      (static_cast<int64_t>(B) * H + 7) / 8 * 8 * (V / 16) > INT32_MAX)
+    return GDN_EINVAL;
   if (B == 0) return GDN_OK;
   if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_EINVAL;
   const size_t in_b = dtype_bytes(in_dtype), out_b = dtype_bytes(out_dtype);

@@ -145,17 +145,30 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
 // the 16 rows one MFMA operand read touches spread over the banks.
 template <int K>
 struct KdaScanLds {
-  static constexpr int LDX = K + 4, LDA = 68;
+  static constexpr int LDX = K + 4, LDA = 68, LDT = 68;
   static constexpr int kRowF4 = K / 4;            // float4 per [64][K] row
   static constexpr int kMK = 64 * kRowF4 / 256;   // prefetch steps per [64][K] operand
   static constexpr int kSteps = 8 + 3 * kMK + 1;  // A', P (4 steps each), three [64][K], e^{G_last}
-  float Kg[64 * LDX], Qg[64 * LDX], Kd[64 * LDX];
+  float Kg[64 * LDX], Qg[64 * LDX];
+  float KdT[K * LDT];  // K o e^{G_last - G}, transposed: [key][token]
   float Ap[64 * LDA], P[64 * LDA];
   float gL[K];
-  float h[K * 16];   // the state slice [key][16 value columns]
-  float R[64 * 16];  // V - (K o e^G) h
-  float D[64 * 16];  // the chunk's deltas
+  float hT[16 * LDX];  // the state slice, transposed: [value column][key]
+  float RT[16 * LDT];  // (V - (K o e^G) h)^T
+  float DT[16 * LDT];  // the chunk's deltas, transposed
 };
+
+// 16-deep fp32 product on v_mfma_f32_16x16x4f32 with k = 16 kb + 4 g + e in
+// instruction e: lane (g, c) supplies a = X[c][16 kb + 4 g + e] and
+// b = Y[16 kb + 4 g + e][c], so both come from one 16-byte LDS read each when X
+// is stored by rows and Y by columns.
+__device__ __forceinline__ f32x4 kda_mma16(const float4& a, const float4& b, f32x4 acc) {
+  acc = mfma_f32(a.x, b.x, acc);
+  acc = mfma_f32(a.y, b.y, acc);
+  acc = mfma_f32(a.z, b.z, acc);
+  return mfma_f32(a.w, b.w, acc);
+}
+__device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
 // The chunk's workspace block, float4 f = tid + 256 m, loaded into registers:
 // steps [0, kHalf) in one array and the rest in another (two arrays of this size
@@ -186,7 +199,15 @@ __device__ __forceinline__ void kda_st(const float4& x, KdaScanLds<K>& sm, int t
     } else {
       constexpr int op = (M - 8) / L::kMK;
       const int f = tid + 256 * ((M - 8) % L::kMK);
-      dst = (op == 0 ? sm.Kg : op == 1 ? sm.Qg : sm.Kd) + (f / L::kRowF4) * L::LDX + 4 * (f % L::kRowF4);
+      const int row = f / L::kRowF4, col = 4 * (f % L::kRowF4);
+      if constexpr (op == 2) {  // stored transposed: the state update reads it by key
+        sm.KdT[(col + 0) * L::LDT + row] = x.x;
+        sm.KdT[(col + 1) * L::LDT + row] = x.y;
+        sm.KdT[(col + 2) * L::LDT + row] = x.z;
+        sm.KdT[(col + 3) * L::LDT + row] = x.w;
+        return;
+      }
+      dst = (op == 0 ? sm.Kg : sm.Qg) + row * L::LDX + col;
     }
     *reinterpret_cast<float4*>(dst) = x;
   }
@@ -226,16 +247,22 @@ __device__ __forceinline__ void kda_stage(const KdaPf<K>& pf, KdaScanLds<K>& sm,
 template <int K, typename Tin, typename Tout>
 __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __restrict__ v, const float* __restrict__ ws,
                                                                const float* h0, float* ht, Tout* __restrict__ o,
-                                                               int T, int H, int V, int NC) {
+                                                               int T, int H, int V, int NC, int n_pairs) {
   using L = KdaScanLds<K>;
   __shared__ __attribute__((aligned(16))) L sm;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int v_base = blockIdx.x * kKdaSlice;
+  // Workgroups are dealt to the 8 XCDs round-robin by id: the slices of one
+  // (sequence, head) pair get ids of one residue mod 8, so they share an XCD and
+  // its L2, which then serves their common reads of the chunk operands.
+  const int n_slices = V / kKdaSlice, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int pair = (idx / n_slices) * 8 + xcd;
+  if (pair >= n_pairs) return;  // padding of the grid to whole rounds of 8
+  const int h = pair % H, b = pair / H;
+  const int v_base = (idx % n_slices) * kKdaSlice;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int64_t st_base = (static_cast<int64_t>(b) * H + h) * V + v_base;  // state [.., V, K] rows of this slice
   for (int e = tid; e < K * kKdaSlice; e += kKdaThreads) {
     const int cc = e % K, vv = e / K;
-    sm.h[cc * 16 + vv] = h0 ? h0[(st_base + vv) * K + cc] : 0.f;
+    sm.hT[vv * L::LDX + cc] = h0 ? h0[(st_base + vv) * K + cc] : 0.f;
   }
   const int64_t per = kda_floats_per_chunk(K);
   const float* ws_bh = ws + (static_cast<int64_t>(b) * NC * H + h) * per;  // chunk c at + c * H * per
@@ -252,7 +279,6 @@ __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __rest
       vr[r] = v[((static_cast<int64_t>(b) * T + t0 + ic) * H + h) * V + v_base + c];
     }
   };
-  const int n_jj = 4 * w + 4;  // A' and P vanish above the diagonal: k < 16 (w + 1)
   if (NC > 0) {
     kda_prefetch<K>(pf, ws_bh, tid);
     load_v(0);
@@ -272,51 +298,55 @@ __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __rest
     __syncthreads();
     // R = V - (K o e^G) h
     f32x4 acc = zero4();
-#pragma unroll 8
-    for (int kk = 0; kk < K / 4; ++kk)
-      acc = mfma_f32(sm.Kg[(16 * w + c) * L::LDX + 4 * kk + g], sm.h[(4 * kk + g) * 16 + c], acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.R[(16 * w + 4 * g + r) * 16 + c] = vcur[r] - acc[r];
+    for (int kb = 0; kb < K / 16; ++kb)
+      acc = kda_mma16(lds4(&sm.Kg[(16 * w + c) * L::LDX + 16 * kb + 4 * g]), lds4(&sm.hT[c * L::LDX + 16 * kb + 4 * g]),
+                      acc);
+    *reinterpret_cast<float4*>(&sm.RT[c * L::LDT + 16 * w + 4 * g]) =
+        make_float4(vcur[0] - acc[0], vcur[1] - acc[1], vcur[2] - acc[2], vcur[3] - acc[3]);
     __syncthreads();
-    // D = A' R
+    // D = A' R (A' vanishes above the diagonal: k < 16 (w + 1))
     acc = zero4();
-    for (int jj = 0; jj < n_jj; ++jj)
-      acc = mfma_f32(sm.Ap[(16 * w + c) * L::LDA + 4 * jj + g], sm.R[(4 * jj + g) * 16 + c], acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm.D[(16 * w + 4 * g + r) * 16 + c] = acc[r];
+    for (int kb = 0; kb <= w; ++kb)
+      acc = kda_mma16(lds4(&sm.Ap[(16 * w + c) * L::LDA + 16 * kb + 4 * g]), lds4(&sm.RT[c * L::LDT + 16 * kb + 4 * g]),
+                      acc);
+    *reinterpret_cast<float4*>(&sm.DT[c * L::LDT + 16 * w + 4 * g]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     __syncthreads();
     // o = (s q o e^G) h + P D
     acc = zero4();
-#pragma unroll 8
-    for (int kk = 0; kk < K / 4; ++kk)
-      acc = mfma_f32(sm.Qg[(16 * w + c) * L::LDX + 4 * kk + g], sm.h[(4 * kk + g) * 16 + c], acc);
-    for (int jj = 0; jj < n_jj; ++jj)
-      acc = mfma_f32(sm.P[(16 * w + c) * L::LDA + 4 * jj + g], sm.D[(4 * jj + g) * 16 + c], acc);
+#pragma unroll
+    for (int kb = 0; kb < K / 16; ++kb)
+      acc = kda_mma16(lds4(&sm.Qg[(16 * w + c) * L::LDX + 16 * kb + 4 * g]), lds4(&sm.hT[c * L::LDX + 16 * kb + 4 * g]),
+                      acc);
+    for (int kb = 0; kb <= w; ++kb)
+      acc = kda_mma16(lds4(&sm.P[(16 * w + c) * L::LDA + 16 * kb + 4 * g]), lds4(&sm.DT[c * L::LDT + 16 * kb + 4 * g]),
+                      acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * w + 4 * g + r;
       if (i < n) store_out(o + ((static_cast<int64_t>(b) * T + t0 + i) * H + h) * V + v_base + c, acc[r]);
     }
     __syncthreads();  // every wave has read the state
-    // h' = diag(e^{G_last}) h + (K o e^{G_last - G})^T D, 16 state rows at a time
+    // h' = diag(e^{G_last}) h + (K o e^{G_last - G})^T D, 16 keys at a time:
+    // lane (g, c) holds keys 16 t + 4 g + r of value column c
 #pragma unroll
     for (int u = 0; u < K / 64; ++u) {
       const int t = w * (K / 64) + u;
-      f32x4 hs;
+      float* hp = &sm.hT[c * L::LDX + 16 * t + 4 * g];
+      const float4 h4 = lds4(hp), g4 = lds4(&sm.gL[16 * t + 4 * g]);
+      f32x4 hs = f32x4{g4.x * h4.x, g4.y * h4.y, g4.z * h4.z, g4.w * h4.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hs[r] = sm.gL[16 * t + 4 * g + r] * sm.h[(16 * t + 4 * g + r) * 16 + c];
-#pragma unroll 4
-      for (int ii = 0; ii < 16; ++ii)
-        hs = mfma_f32(sm.Kd[(4 * ii + g) * L::LDX + 16 * t + c], sm.D[(4 * ii + g) * 16 + c], hs);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.h[(16 * t + 4 * g + r) * 16 + c] = hs[r];
+      for (int kb = 0; kb < 4; ++kb)
+        hs = kda_mma16(lds4(&sm.KdT[(16 * t + c) * L::LDT + 16 * kb + 4 * g]), lds4(&sm.DT[c * L::LDT + 16 * kb + 4 * g]),
+                       hs);
+      *reinterpret_cast<float4*>(hp) = make_float4(hs[0], hs[1], hs[2], hs[3]);
     }
   }
   __syncthreads();
   if (ht)
     for (int e = tid; e < K * kKdaSlice; e += kKdaThreads) {
       const int cc = e % K, vv = e / K;
-      ht[(st_base + vv) * K + cc] = sm.h[cc * 16 + vv];
+      ht[(st_base + vv) * K + cc] = sm.hT[vv * L::LDX + cc];
     }
 }
 
@@ -333,15 +363,16 @@ static void launch_kda_typed(const KdaChunkArgs& a) {
                        static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), a.g, a.beta, a.ws,
                        static_cast<int>(a.T), a.H, NC, a.scale);
   if (a.events[1]) (void)hipEventRecord(a.events[1], a.stream);
-  const dim3 grid(a.V / kKdaSlice, a.H, a.B);
+  const int n_pairs = a.B * a.H;
+  const dim3 grid(static_cast<unsigned>((n_pairs + 7) / 8) * 8 * (a.V / kKdaSlice));
   if (a.out_f32)
     hipLaunchKernelGGL((kda_scan_kernel<K, Tin, float>), grid, dim3(kKdaThreads), 0, a.stream,
                        static_cast<const Tin*>(a.v), a.ws, a.h0, a.ht, static_cast<float*>(a.o),
-                       static_cast<int>(a.T), a.H, a.V, NC);
+                       static_cast<int>(a.T), a.H, a.V, NC, n_pairs);
   else
     hipLaunchKernelGGL((kda_scan_kernel<K, Tin, __bf16>), grid, dim3(kKdaThreads), 0, a.stream,
                        static_cast<const Tin*>(a.v), a.ws, a.h0, a.ht, static_cast<__bf16*>(a.o),
-                       static_cast<int>(a.T), a.H, a.V, NC);
+                       static_cast<int>(a.T), a.H, a.V, NC, n_pairs);
 }
 
 hipError_t launch_chunk_fwd_kda(const KdaChunkArgs& a) {
