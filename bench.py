@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
-PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector, published
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32, vector and dense MFMA alike, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 CSRC = os.path.join(ROOT, "linear_attention_sequence_recompute_amd", "csrc")
 
@@ -653,7 +653,7 @@ def main():
                     "bf16 q/k/v/o, fp32 g [T, H, K] and beta, fp32 final state",
         "value": B * T / (ck_ms / 1e3), "unit": "tokens/s", "ms_per_call": ck_ms,
         "kernels_us": {"prep": ck_prep_s * 1e6, "scan": ck_scan_s * 1e6},
-        "roofline": {"bound": "alu", "kernel": "kda_scan_kernel (fp32 VALU)", "achieved": ck_scan_f / ck_scan_s / 1e12,
+        "roofline": {"bound": "mfma", "kernel": "kda_scan_kernel (fp32 MFMA)", "achieved": ck_scan_f / ck_scan_s / 1e12,
                      "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                      "frac": ck_scan_f / ck_scan_s / 1e12 / PEAK_FP32_TFLOPS,
                      "traffic": traffic_for("kda_scan_kernel"), "flops_per_launch": ck_scan_f,
