@@ -635,6 +635,29 @@ def test_chunk_kda_config_sampled():
     check_chunk_kda(1, 4096, 16, 128, 128, "bf16", seed=98, shift=2.0, label="H16 T4096", heads=[0, 7, 15])
 
 
+def test_chunk_kda_uniform_channels_equal_the_scalar_gate():
+    """Every key channel given the token's scalar log-gate: the per-channel chunk
+    form computes the scalar rule, checked against the scalar oracle and against
+    the scalar chunk path on the same inputs."""
+    B, T, H, K, V = 2, 200, 2, 128, 128
+    ci = chunk_inputs([T] * B, H, K, V, dtype="bf16", seed=101, h0_std=0.1)
+    g = np.repeat(ci.a[:, :, None], K, axis=2)
+    h0 = dev(ci.h0)
+    o_k, ht_k = run_chunk_kda(ci, g, B, T, K ** -0.5, "f32", h0)
+    o_s, ht_s = run_chunk(ci, K ** -0.5, "f32")
+    eo = es = 0.0
+    for b in range(B):
+        sl = slice(b * T, (b + 1) * T)
+        o_ref, s_ref = oracle.recurrent_fwd(ci.q[sl], ci.k[sl], ci.v[sl], ci.a[sl], ci.beta[sl], scale=K ** -0.5,
+                                            S0=ci.h0[b])
+        eo = max(eo, max_err_over_rms(host(o_k[b]), o_ref))
+        es = max(es, max_err_over_rms(host(ht_k[b]), s_ref))
+    e_cross = max_err_over_rms(host(o_k).reshape(B * T, H, V), host(o_s))
+    _print(f"[chunk kda uniform] vs scalar oracle o={eo:.2e} S={es:.2e}; vs scalar chunk path {e_cross:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"] and e_cross <= TOL["bf16"]
+    assert max_err_over_rms(host(ht_k), host(ht_s)) <= TOL["bf16"]
+
+
 def test_chunk_kda_empty_and_in_place():
     ci = chunk_inputs([1, 1], 2, 64, 64, dtype="bf16", seed=99, h0_std=0.1)
     h0 = dev(ci.h0)
