@@ -319,6 +319,8 @@ size_t gdn_chunk_fwd_kda_workspace_bytes(int B, int64_t T, int H, int K);
  * Per token: S <- S diag(exp(g_t)); delta = beta_t (v_t - S k_t);
  * S <- S + delta k_t^T; o_t = S (scale q_t). Results in float32; o in bfloat16 is
  * round-to-nearest-even of the float32 result. T == 0 passes h0 to ht.
+ * Alignment: q, k and g 16 bytes (read four channels at a time); v, o by their
+ * element size; beta, h0 and ht 4 bytes.
  *
  * Returns GDN_EUNSUPPORTED for K outside {64, 128}, V not a multiple of 16 in
  * [16, 256] or an unknown dtype; GDN_EINVAL for B outside [0, 65535], T < 0, H

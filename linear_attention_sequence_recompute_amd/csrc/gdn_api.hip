@@ -386,7 +386,7 @@ static gdn_status chunk_fwd_kda_impl(const void* q, const void* k, const void* v
   if (B == 0) return GDN_OK;
   if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_EINVAL;
   const size_t in_b = dtype_bytes(in_dtype), out_b = dtype_bytes(out_dtype);
-  if (!aligned(q, in_b) || !aligned(k, in_b) || !aligned(v, in_b) || !aligned(g, 4) || !aligned(beta, 4) ||
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, in_b) || !aligned(g, 16) || !aligned(beta, 4) ||
       !aligned(o, out_b) || !aligned(h0, 4) || !aligned(ht, 4))
     return GDN_EINVAL;
   const size_t need = gdn_chunk_fwd_kda_workspace_bytes(B, T, H, K);

@@ -22,6 +22,14 @@
 namespace gdn {
 
 constexpr int kKdaThreads = 256;
+
+// Four consecutive inputs as float (8-byte loads for bf16, 16-byte for float).
+__device__ __forceinline__ float4 ld_in4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 ld_in4(const __bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
 constexpr float kLog2e = 1.4426950408889634f;
 
 // 2^x by the hardware's v_exp_f32 (about 1 ulp); every argument here is <= 0, and
@@ -53,21 +61,31 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
   float* base = ws + (static_cast<int64_t>(blockIdx.x) * H + h) * kda_floats_per_chunk(K);
   float *Ap = base, *P = base + 4096, *Kg = base + 8192, *Qg = Kg + 64 * K, *Kd = Qg + 64 * K, *gL = Kd + 64 * K;
 
-  // Rows past the sequence end: q = k = 0, g = 0, beta = 0.
-  for (int e = tid; e < 64 * K; e += kKdaThreads) {
-    const int i = e / K, cc = e % K;
-    float qv = 0.f, kv = 0.f, gv = 0.f;
-    if (i < n) {
-      const int64_t idx = ((static_cast<int64_t>(b) * T + t0 + i) * H + h) * K + cc;
-      qv = ld_in(q + idx);
-      kv = ld_in(k + idx);
-      gv = g[idx];
-    }
-    sQ[i * LD + cc] = qv;
-    sK[i * LD + cc] = kv;
-    sG[i * LD + cc] = gv * kLog2e;  // base-2 exponents: e^x = 2^(x log2 e)
+  // Rows past the sequence end: q = k = 0, g = 0, beta = 0. Every load is issued
+  // before the first LDS write, four channels at a time, rows past the end
+  // reading the last row (a load under a branch would be waited for at once).
+  constexpr int G4 = 64 * K / 4 / kKdaThreads;  // 4-channel groups per lane and operand
+  float4 lq[G4], lk[G4], lg[G4];
+#pragma unroll
+  for (int m = 0; m < G4; ++m) {
+    const int e = tid + kKdaThreads * m, i = e / (K / 4), c4 = 4 * (e % (K / 4));
+    const int64_t idx = ((static_cast<int64_t>(b) * T + t0 + min(i, n - 1)) * H + h) * K + c4;
+    lq[m] = ld_in4(q + idx);
+    lk[m] = ld_in4(k + idx);
+    lg[m] = *reinterpret_cast<const float4*>(g + idx);
   }
-  if (tid < 64) sB[tid] = tid < n ? beta[(static_cast<int64_t>(b) * T + t0 + tid) * H + h] : 0.f;
+  const float bt = beta[(static_cast<int64_t>(b) * T + t0 + min(tid & 63, n - 1)) * H + h];
+#pragma unroll
+  for (int m = 0; m < G4; ++m) {
+    const int e = tid + kKdaThreads * m, i = e / (K / 4), c4 = 4 * (e % (K / 4));
+    const float f = i < n ? 1.f : 0.f;  // values, not references, are selected: the arrays stay in registers
+    const float fg = f * kLog2e;        // base-2 exponents: e^x = 2^(x log2 e)
+    const float4 x = lq[m], y = lk[m], z = lg[m];
+    *reinterpret_cast<float4*>(&sQ[i * LD + c4]) = make_float4(f * x.x, f * x.y, f * x.z, f * x.w);
+    *reinterpret_cast<float4*>(&sK[i * LD + c4]) = make_float4(f * y.x, f * y.y, f * y.z, f * y.w);
+    *reinterpret_cast<float4*>(&sG[i * LD + c4]) = make_float4(fg * z.x, fg * z.y, fg * z.z, fg * z.w);
+  }
+  if (tid < 64) sB[tid] = tid < n ? bt : 0.f;
   __syncthreads();
   for (int cc = tid; cc < K; cc += kKdaThreads) {  // inclusive cumulative sum over the chunk's tokens
     float s = 0.f;
@@ -78,12 +96,14 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
   }
   __syncthreads();
 
-  // The lower triangle (j <= i) of the pair matrices, 2080 pairs spread evenly.
-  for (int p = tid; p < 64 * 65 / 2; p += kKdaThreads) {
-    int i = static_cast<int>((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-    while ((i + 1) * (i + 2) / 2 <= p) ++i;
-    while (i * (i + 1) / 2 > p) --i;
-    const int j = p - i * (i + 1) / 2;
+  // Diagonal 16 x 16 blocks of the pair matrices (j <= i within a block of 16
+  // tokens): 4 x 136 pairs spread evenly, one exponent per pair and channel.
+  for (int p = tid; p < 4 * 136; p += kKdaThreads) {
+    const int blk = p / 136, pp = p % 136;
+    int a = static_cast<int>((sqrtf(8.f * pp + 1.f) - 1.f) * 0.5f);
+    while ((a + 1) * (a + 2) / 2 <= pp) ++a;
+    while (a * (a + 1) / 2 > pp) --a;
+    const int i = 16 * blk + a, j = 16 * blk + pp - a * (a + 1) / 2;
     float accP = 0.f, accL = 0.f;
 #pragma unroll 4
     for (int cc = 0; cc < K; cc += 4) {
@@ -100,6 +120,46 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
     }
     P[i * 64 + j] = scale * accP;
     if (j < i) sL[i][j] = sB[i] * accL;
+  }
+  // Off-diagonal blocks (I > J) as fp32 MFMA products: with the reference token
+  // r = 16 I between the two blocks, e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j},
+  // both factors <= 1, so the rows of block I (q and k) scaled by the first and
+  // the rows of block J (k) by the second multiply as plain matrices. Wave w
+  // takes blocks w and w + 4 of (1,0) (2,0) (2,1) (3,0) (3,1) (3,2). Lane (g, c)
+  // supplies row c of each operand at channels 16 kb + 4 g .. + 3 and holds rows
+  // 4 g .. 4 g + 3, column c of the 16 x 16 results.
+  {
+    const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+    for (int ob = w; ob < 6; ob += 4) {
+      const int I = ob < 1 ? 1 : ob < 3 ? 2 : 3, J = ob < 1 ? 0 : ob < 3 ? ob - 1 : ob - 3;
+      const int ri = 16 * I + c, rj = 16 * J + c, r0 = 16 * I;
+      f32x4 accP = zero4(), accL = zero4();
+      for (int kb = 0; kb < K / 16; ++kb) {
+        const int cc = 16 * kb + 4 * g;
+        const float4 qi = *reinterpret_cast<const float4*>(&sQ[ri * LD + cc]);
+        const float4 ki = *reinterpret_cast<const float4*>(&sK[ri * LD + cc]);
+        const float4 kj = *reinterpret_cast<const float4*>(&sK[rj * LD + cc]);
+        const float4 gi = *reinterpret_cast<const float4*>(&sG[ri * LD + cc]);
+        const float4 gj = *reinterpret_cast<const float4*>(&sG[rj * LD + cc]);
+        const float4 gr = *reinterpret_cast<const float4*>(&sG[r0 * LD + cc]);
+        const float ea[4] = {exp2_hw(gi.x - gr.x), exp2_hw(gi.y - gr.y), exp2_hw(gi.z - gr.z), exp2_hw(gi.w - gr.w)};
+        const float eb[4] = {exp2_hw(gr.x - gj.x), exp2_hw(gr.y - gj.y), exp2_hw(gr.z - gj.z), exp2_hw(gr.w - gj.w)};
+        const float qa[4] = {qi.x, qi.y, qi.z, qi.w}, ka[4] = {ki.x, ki.y, ki.z, ki.w};
+        const float kb4[4] = {kj.x, kj.y, kj.z, kj.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float bv = kb4[e] * eb[e];
+          accP = mfma_f32(qa[e] * ea[e], bv, accP);
+          accL = mfma_f32(ka[e] * ea[e], bv, accL);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * g + r, j = 16 * J + c;
+        P[i * 64 + j] = scale * accP[r];
+        sL[i][j] = sB[i] * accL[r];
+      }
+    }
   }
   __syncthreads();
 

@@ -282,6 +282,8 @@ def test_chunk_fwd_kda_validation():
     assert call(scale=float("inf")) == E.GDN_EINVAL
     assert call(q=None) == E.GDN_EINVAL
     assert call(q=FAKE + 1) == E.GDN_EINVAL
+    assert call(k=FAKE + 8) == E.GDN_EINVAL      # q, k, g read four channels at a time: 16-byte aligned
+    assert call(g=FAKE + 4) == E.GDN_EINVAL
     assert call(h0=FAKE + 2) == E.GDN_EINVAL
     assert call(ws=None) == E.GDN_EWORKSPACE
     assert call(ws_bytes=1024) == E.GDN_EWORKSPACE
