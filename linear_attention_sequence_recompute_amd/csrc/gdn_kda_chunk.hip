@@ -38,6 +38,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int kKdaSlice = 16;  // value columns of the state per scan workgroup
 
+// 16-deep fp32 product on v_mfma_f32_16x16x4f32 with k = 16 kb + 4 g + e in
+// instruction e: lane (g, c) supplies a = X[c][16 kb + 4 g + e] and
+// b = Y[16 kb + 4 g + e][c], so both come from one 16-byte LDS read each when X
+// is stored by rows and Y by columns.
+__device__ __forceinline__ f32x4 kda_mma16(const float4& a, const float4& b, f32x4 acc) {
+  acc = mfma_f32(a.x, b.x, acc);
+  acc = mfma_f32(a.y, b.y, acc);
+  acc = mfma_f32(a.z, b.z, acc);
+  return mfma_f32(a.w, b.w, acc);
+}
+__device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
 // Floats per (chunk, head) in the workspace: A' [64][64], P [64][64], then
 // K o e^G, s q o e^G, K o e^{G_last - G} (each [64][K]) and e^{G_last} [K].
 __host__ __device__ constexpr int64_t kda_floats_per_chunk(int K) { return 2 * 64 * 64 + 3 * 64 * K + K; }
@@ -54,6 +66,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
   __shared__ __attribute__((aligned(16))) float sG[64 * LD];
   __shared__ float sL[64][65];
   __shared__ float sA[64][65];
+  __shared__ float sX[16][65];  // the earlier blocks' part of a block row of A
   __shared__ float sB[64];
   const int b = blockIdx.x / NC, c = blockIdx.x % NC, h = blockIdx.y;
   const int t0 = c * 64, n = min(64, T - t0);
@@ -164,22 +177,39 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
   __syncthreads();
 
   if (tid < 64) {
-    // A = (I + L)^{-1} by forward substitution, one column per lane:
-    // A_ij = delta_ij - sum_{m < i} L_im A_mj (A is unit lower triangular).
-    const int j = tid;
-    sA[0][j] = j == 0 ? 1.f : 0.f;
-    for (int i = 1; i < 64; ++i) {
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;  // four chains hide the FMA latency
-      int m = 0;
-      for (; m + 3 < i; m += 4) {
-        a0 = fmaf(sL[i][m], sA[m][j], a0);
-        a1 = fmaf(sL[i][m + 1], sA[m + 1][j], a1);
-        a2 = fmaf(sL[i][m + 2], sA[m + 2][j], a2);
-        a3 = fmaf(sL[i][m + 3], sA[m + 3][j], a3);
+    // A = (I + L)^{-1}, A_ij = delta_ij - sum_{m < i} L_im A_mj (A is unit lower
+    // triangular), by blocks of 16 rows on this wave: the part of the sum over
+    // the earlier blocks (m < 16 R) is one fp32 MFMA product into sX, the rest
+    // a forward substitution within the block, one column per lane. LDS written
+    // and read by this one wave needs no barrier: its LDS accesses run in order.
+    const int j = tid, g = tid >> 4, c = tid & 15;
+    for (int R = 0; R < 4; ++R) {
+      if (R > 0) {
+        for (int ct = 0; ct < 4; ++ct) {
+          f32x4 acc = zero4();
+          for (int kb = 0; kb < R; ++kb) {
+            const int k0 = 16 * kb + 4 * g, row = 16 * R + c, col = 16 * ct + c;
+            acc = kda_mma16(make_float4(sL[row][k0], sL[row][k0 + 1], sL[row][k0 + 2], sL[row][k0 + 3]),
+                            make_float4(sA[k0][col], sA[k0 + 1][col], sA[k0 + 2][col], sA[k0 + 3][col]), acc);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sX[4 * g + r][16 * ct + c] = acc[r];
+        }
+        __builtin_amdgcn_wave_barrier();
       }
-      for (; m < i; ++m) a0 = fmaf(sL[i][m], sA[m][j], a0);
-      const float acc = (a0 + a1) + (a2 + a3);
-      sA[i][j] = i == j ? 1.f : (i > j ? -acc : 0.f);
+      for (int ii = 0; ii < 16; ++ii) {
+        const int i = 16 * R + ii;
+        float a0 = R > 0 ? sX[ii][j] : 0.f, a1 = 0.f;
+        int m = 16 * R;
+        for (; m + 1 < i; m += 2) {
+          a0 = fmaf(sL[i][m], sA[m][j], a0);
+          a1 = fmaf(sL[i][m + 1], sA[m + 1][j], a1);
+        }
+        if (m < i) a0 = fmaf(sL[i][m], sA[m][j], a0);
+        const float acc = a0 + a1;
+        sA[i][j] = i == j ? 1.f : (i > j ? -acc : 0.f);
+      }
+      __builtin_amdgcn_wave_barrier();
     }
   } else {
     // Meanwhile the other waves write the state-side operands.
@@ -218,17 +248,6 @@ struct KdaScanLds {
   float DT[16 * LDT];  // the chunk's deltas, transposed
 };
 
-// 16-deep fp32 product on v_mfma_f32_16x16x4f32 with k = 16 kb + 4 g + e in
-// instruction e: lane (g, c) supplies a = X[c][16 kb + 4 g + e] and
-// b = Y[16 kb + 4 g + e][c], so both come from one 16-byte LDS read each when X
-// is stored by rows and Y by columns.
-__device__ __forceinline__ f32x4 kda_mma16(const float4& a, const float4& b, f32x4 acc) {
-  acc = mfma_f32(a.x, b.x, acc);
-  acc = mfma_f32(a.y, b.y, acc);
-  acc = mfma_f32(a.z, b.z, acc);
-  return mfma_f32(a.w, b.w, acc);
-}
-__device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
 // The chunk's workspace block, float4 f = tid + 256 m, loaded into registers:
 // steps [0, kHalf) in one array and the rest in another (two arrays of this size
