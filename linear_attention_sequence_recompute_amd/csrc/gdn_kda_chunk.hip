@@ -259,10 +259,19 @@ struct KdaPf {
   float4 b[KdaScanLds<K>::kSteps - kHalf];
 };
 
+// The K-decay operand is stored transposed in LDS; for it consecutive lanes take
+// consecutive token rows (f = tid + 256 m: row f % 64, four channels at
+// 4 (f / 64)), so that the transposed LDS writes fall in different banks.
 template <int K, int M>
 __device__ __forceinline__ float4 kda_ld(const float4* s4, int tid) {
   using L = KdaScanLds<K>;
-  return M < L::kSteps - 1 ? s4[tid + 256 * M] : s4[min(tid, K / 4 - 1) + 256 * M];  // last: e^{G_last}, no branch
+  constexpr int kd0 = 8 + 2 * L::kMK, kd_base = 2048 + 2 * 64 * L::kRowF4;  // first step, first float4 of it
+  if constexpr (M >= kd0 && M < kd0 + L::kMK) {
+    const int f = tid + 256 * (M - kd0);
+    return s4[kd_base + (f % 64) * L::kRowF4 + f / 64];
+  } else {
+    return M < L::kSteps - 1 ? s4[tid + 256 * M] : s4[min(tid, K / 4 - 1) + 256 * M];  // last: e^{G_last}, no branch
+  }
 }
 
 template <int K, int M>
@@ -278,14 +287,15 @@ __device__ __forceinline__ void kda_st(const float4& x, KdaScanLds<K>& sm, int t
     } else {
       constexpr int op = (M - 8) / L::kMK;
       const int f = tid + 256 * ((M - 8) % L::kMK);
-      const int row = f / L::kRowF4, col = 4 * (f % L::kRowF4);
       if constexpr (op == 2) {  // stored transposed: the state update reads it by key
+        const int row = f % 64, col = 4 * (f / 64);
         sm.KdT[(col + 0) * L::LDT + row] = x.x;
         sm.KdT[(col + 1) * L::LDT + row] = x.y;
         sm.KdT[(col + 2) * L::LDT + row] = x.z;
         sm.KdT[(col + 3) * L::LDT + row] = x.w;
         return;
       }
+      const int row = f / L::kRowF4, col = 4 * (f % L::kRowF4);
       dst = (op == 0 ? sm.Kg : sm.Qg) + row * L::LDX + col;
     }
     *reinterpret_cast<float4*>(dst) = x;
