@@ -240,7 +240,7 @@ struct KdaScanLds {
   static constexpr int kMK = 64 * kRowF4 / 256;   // prefetch steps per [64][K] operand
   static constexpr int kSteps = 8 + 3 * kMK + 1;  // A', P (4 steps each), three [64][K], e^{G_last}
   float Kg[64 * LDX], Qg[64 * LDX];
-  float KdT[K * LDT];  // K o e^{G_last - G}, transposed: [key][token]
+  float Kd[64 * LDX];  // K o e^{G_last - G}
   float Ap[64 * LDA], P[64 * LDA];
   float gL[K];
   float hT[16 * LDX];  // the state slice, transposed: [value column][key]
@@ -259,19 +259,10 @@ struct KdaPf {
   float4 b[KdaScanLds<K>::kSteps - kHalf];
 };
 
-// The K-decay operand is stored transposed in LDS; for it consecutive lanes take
-// consecutive token rows (f = tid + 256 m: row f % 64, four channels at
-// 4 (f / 64)), so that the transposed LDS writes fall in different banks.
 template <int K, int M>
 __device__ __forceinline__ float4 kda_ld(const float4* s4, int tid) {
   using L = KdaScanLds<K>;
-  constexpr int kd0 = 8 + 2 * L::kMK, kd_base = 2048 + 2 * 64 * L::kRowF4;  // first step, first float4 of it
-  if constexpr (M >= kd0 && M < kd0 + L::kMK) {
-    const int f = tid + 256 * (M - kd0);
-    return s4[kd_base + (f % 64) * L::kRowF4 + f / 64];
-  } else {
-    return M < L::kSteps - 1 ? s4[tid + 256 * M] : s4[min(tid, K / 4 - 1) + 256 * M];  // last: e^{G_last}, no branch
-  }
+  return M < L::kSteps - 1 ? s4[tid + 256 * M] : s4[min(tid, K / 4 - 1) + 256 * M];  // last: e^{G_last}, no branch
 }
 
 template <int K, int M>
@@ -287,16 +278,8 @@ __device__ __forceinline__ void kda_st(const float4& x, KdaScanLds<K>& sm, int t
     } else {
       constexpr int op = (M - 8) / L::kMK;
       const int f = tid + 256 * ((M - 8) % L::kMK);
-      if constexpr (op == 2) {  // stored transposed: the state update reads it by key
-        const int row = f % 64, col = 4 * (f / 64);
-        sm.KdT[(col + 0) * L::LDT + row] = x.x;
-        sm.KdT[(col + 1) * L::LDT + row] = x.y;
-        sm.KdT[(col + 2) * L::LDT + row] = x.z;
-        sm.KdT[(col + 3) * L::LDT + row] = x.w;
-        return;
-      }
       const int row = f / L::kRowF4, col = 4 * (f % L::kRowF4);
-      dst = (op == 0 ? sm.Kg : sm.Qg) + row * L::LDX + col;
+      dst = (op == 0 ? sm.Kg : op == 1 ? sm.Qg : sm.Kd) + row * L::LDX + col;
     }
     *reinterpret_cast<float4*>(dst) = x;
   }
@@ -425,9 +408,13 @@ __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __rest
       const float4 h4 = lds4(hp), g4 = lds4(&sm.gL[16 * t + 4 * g]);
       f32x4 hs = f32x4{g4.x * h4.x, g4.y * h4.y, g4.z * h4.z, g4.w * h4.w};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        hs = kda_mma16(lds4(&sm.KdT[(16 * t + c) * L::LDT + 16 * kb + 4 * g]), lds4(&sm.DT[c * L::LDT + 16 * kb + 4 * g]),
-                       hs);
+      for (int kb = 0; kb < 4; ++kb) {
+        // a = (K o e^{G_last - G})^T: a column of the row-major tile, four
+        // reads that fall in 64 different banks (row stride K + 4)
+        const float* kd = &sm.Kd[(16 * kb + 4 * g) * L::LDX + 16 * t + c];
+        hs = kda_mma16(make_float4(kd[0], kd[L::LDX], kd[2 * L::LDX], kd[3 * L::LDX]),
+                       lds4(&sm.DT[c * L::LDT + 16 * kb + 4 * g]), hs);
+      }
       *reinterpret_cast<float4*>(hp) = make_float4(hs[0], hs[1], hs[2], hs[3]);
     }
   }
