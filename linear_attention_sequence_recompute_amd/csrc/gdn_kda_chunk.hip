@@ -304,6 +304,16 @@ __device__ __forceinline__ void kda_prefetch(KdaPf<K>& pf, const float* src, int
   kda_prefetch_seq<K>(pf, reinterpret_cast<const float4*>(src), tid,
                       std::make_integer_sequence<int, KdaScanLds<K>::kSteps>{});
 }
+// Steps [M0, M0 + N) only.
+template <int K, int M0, int... Ns>
+__device__ __forceinline__ void kda_prefetch_part_seq(KdaPf<K>& pf, const float4* s4, int tid,
+                                                      std::integer_sequence<int, Ns...>) {
+  kda_prefetch_seq<K>(pf, s4, tid, std::integer_sequence<int, (M0 + Ns)...>{});
+}
+template <int K, int M0, int N>
+__device__ __forceinline__ void kda_prefetch_part(KdaPf<K>& pf, const float* src, int tid) {
+  kda_prefetch_part_seq<K, M0>(pf, reinterpret_cast<const float4*>(src), tid, std::make_integer_sequence<int, N>{});
+}
 template <int K>
 __device__ __forceinline__ void kda_stage(const KdaPf<K>& pf, KdaScanLds<K>& sm, int tid) {
   kda_stage_seq<K>(pf, sm, tid, std::make_integer_sequence<int, KdaScanLds<K>::kSteps>{});
@@ -362,12 +372,15 @@ __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __rest
     float vcur[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) vcur[r] = 16 * w + 4 * g + r < n ? ld_in(&vr[r]) : 0.f;
-    {  // the last chunk reloads itself (unused): an unconditional load keeps pf in registers
-      const int nx = min(ch + 1, NC - 1);
-      kda_prefetch<K>(pf, ws_bh + static_cast<int64_t>(nx) * H * per, tid);
-      load_v(nx);
-    }
+    // The next chunk's operands are loaded in four groups spread over this
+    // chunk's steps, each after its registers have been staged above (the last
+    // chunk reloads itself, unused: unconditional loads keep pf in registers).
+    const float* nxt = ws_bh + static_cast<int64_t>(min(ch + 1, NC - 1)) * H * per;
+    constexpr int kKd0 = 8 + 2 * L::kMK;
+    kda_prefetch_part<K, kKd0, L::kMK + 1>(pf, nxt, tid);  // K-decay and e^{G_last}
+    load_v(min(ch + 1, NC - 1));
     __syncthreads();
+    kda_prefetch_part<K, 0, 8>(pf, nxt, tid);  // A', P
     // R = V - (K o e^G) h
     f32x4 acc = zero4();
 #pragma unroll
@@ -377,6 +390,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __rest
     *reinterpret_cast<float4*>(&sm.RT[c * L::LDT + 16 * w + 4 * g]) =
         make_float4(vcur[0] - acc[0], vcur[1] - acc[1], vcur[2] - acc[2], vcur[3] - acc[3]);
     __syncthreads();
+    kda_prefetch_part<K, 8, L::kMK>(pf, nxt, tid);  // K o e^G
     // D = A' R (A' vanishes above the diagonal: k < 16 (w + 1))
     acc = zero4();
     for (int kb = 0; kb <= w; ++kb)
@@ -384,6 +398,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __rest
                       acc);
     *reinterpret_cast<float4*>(&sm.DT[c * L::LDT + 16 * w + 4 * g]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     __syncthreads();
+    kda_prefetch_part<K, 8 + L::kMK, L::kMK>(pf, nxt, tid);  // s q o e^G
     // o = (s q o e^G) h + P D
     acc = zero4();
 #pragma unroll
