@@ -320,12 +320,13 @@ __device__ __forceinline__ void kda_stage(const KdaPf<K>& pf, KdaScanLds<K>& sm,
 }
 
 // One workgroup (4 waves) per (value slice of 16 columns, head, sequence); the
-// slice of the state [K][16] stays in LDS across the sequence's chunks. All four
-// products of a chunk run on v_mfma_f32_16x16x4f32 (fp32 in, fp32 out): lane
-// (g, c) supplies a = X[c][k] and b = Y[k][c] for k = 4 kk + g and holds rows
-// 4 g .. 4 g + 3, column c of the 16 x 16 result. Wave w owns token rows
-// 16 w .. 16 w + 15 of R, D and o, and K / 64 of the state's 16-row tiles. The
-// next chunk's operands are loaded into registers while this one is computed.
+// slice of the state (K keys x 16 columns, stored by column) stays in LDS across
+// the sequence's chunks. All four products of a chunk run on
+// v_mfma_f32_16x16x4f32 (fp32 in, fp32 out) in 16-deep blocks (kda_mma16); each
+// lane holds rows 4 g .. 4 g + 3, column c of a 16 x 16 result. Wave w owns
+// token rows 16 w .. 16 w + 15 of R, D and o, and K / 64 of the state's 16-key
+// tiles. The next chunk's operands are loaded into registers while this one is
+// computed.
 template <int K, typename Tin, typename Tout>
 __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __restrict__ v, const float* __restrict__ ws,
                                                                const float* h0, float* ht, Tout* __restrict__ o,
