@@ -21,7 +21,8 @@
 
 namespace gdn {
 
-constexpr int kKdaThreads = 256;
+constexpr int kKdaThreads = 256;  // scan
+constexpr int kPrepThreads = 512;  // prep: one workgroup per CU (its LDS), so eight waves
 
 // Four consecutive inputs as float (8-byte loads for bf16, 16-byte for float).
 __device__ __forceinline__ float4 ld_in4(const float* p) { return *reinterpret_cast<const float4*>(p); }
@@ -55,7 +56,7 @@ __device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cas
 __host__ __device__ constexpr int64_t kda_floats_per_chunk(int K) { return 2 * 64 * 64 + 3 * 64 * K + K; }
 
 template <int K, typename Tin>
-__global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
+__global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                                                                const float* __restrict__ g,
                                                                const float* __restrict__ beta,
                                                                float* __restrict__ ws, int T, int H, int NC,
@@ -77,11 +78,11 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
   // Rows past the sequence end: q = k = 0, g = 0, beta = 0. Every load is issued
   // before the first LDS write, four channels at a time, rows past the end
   // reading the last row (a load under a branch would be waited for at once).
-  constexpr int G4 = 64 * K / 4 / kKdaThreads;  // 4-channel groups per lane and operand
+  constexpr int G4 = 64 * K / 4 / kPrepThreads;  // 4-channel groups per lane and operand
   float4 lq[G4], lk[G4], lg[G4];
 #pragma unroll
   for (int m = 0; m < G4; ++m) {
-    const int e = tid + kKdaThreads * m, i = e / (K / 4), c4 = 4 * (e % (K / 4));
+    const int e = tid + kPrepThreads * m, i = e / (K / 4), c4 = 4 * (e % (K / 4));
     const int64_t idx = ((static_cast<int64_t>(b) * T + t0 + min(i, n - 1)) * H + h) * K + c4;
     lq[m] = ld_in4(q + idx);
     lk[m] = ld_in4(k + idx);
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
   const float bt = beta[(static_cast<int64_t>(b) * T + t0 + min(tid & 63, n - 1)) * H + h];
 #pragma unroll
   for (int m = 0; m < G4; ++m) {
-    const int e = tid + kKdaThreads * m, i = e / (K / 4), c4 = 4 * (e % (K / 4));
+    const int e = tid + kPrepThreads * m, i = e / (K / 4), c4 = 4 * (e % (K / 4));
     const float f = i < n ? 1.f : 0.f;  // values, not references, are selected: the arrays stay in registers
     const float fg = f * kLog2e;        // base-2 exponents: e^x = 2^(x log2 e)
     const float4 x = lq[m], y = lk[m], z = lg[m];
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
   }
   if (tid < 64) sB[tid] = tid < n ? bt : 0.f;
   __syncthreads();
-  for (int cc = tid; cc < K; cc += kKdaThreads) {  // inclusive cumulative sum over the chunk's tokens
+  for (int cc = tid; cc < K; cc += kPrepThreads) {  // inclusive cumulative sum over the chunk's tokens
     float s = 0.f;
     for (int i = 0; i < 64; ++i) {
       s += sG[i * LD + cc];
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
 
   // Diagonal 16 x 16 blocks of the pair matrices (j <= i within a block of 16
   // tokens): 4 x 136 pairs spread evenly, one exponent per pair and channel.
-  for (int p = tid; p < 4 * 136; p += kKdaThreads) {
+  for (int p = tid; p < 4 * 136; p += kPrepThreads) {
     const int blk = p / 136, pp = p % 136;
     int a = static_cast<int>((sqrtf(8.f * pp + 1.f) - 1.f) * 0.5f);
     while ((a + 1) * (a + 2) / 2 <= pp) ++a;
@@ -138,12 +139,12 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
   // r = 16 I between the two blocks, e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j},
   // both factors <= 1, so the rows of block I (q and k) scaled by the first and
   // the rows of block J (k) by the second multiply as plain matrices. Wave w
-  // takes blocks w and w + 4 of (1,0) (2,0) (2,1) (3,0) (3,1) (3,2). Lane (g, c)
+  // takes block w of (1,0) (2,0) (2,1) (3,0) (3,1) (3,2). Lane (g, c)
   // supplies row c of each operand at channels 16 kb + 4 g .. + 3 and holds rows
   // 4 g .. 4 g + 3, column c of the 16 x 16 results.
   {
     const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-    for (int ob = w; ob < 6; ob += 4) {
+    for (int ob = w; ob < 6; ob += kPrepThreads / 64) {
       const int I = ob < 1 ? 1 : ob < 3 ? 2 : 3, J = ob < 1 ? 0 : ob < 3 ? ob - 1 : ob - 3;
       const int ri = 16 * I + c, rj = 16 * J + c, r0 = 16 * I;
       f32x4 accP = zero4(), accL = zero4();
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
     }
   } else {
     // Meanwhile the other waves write the state-side operands.
-    for (int e = tid - 64; e < 64 * K; e += kKdaThreads - 64) {
+    for (int e = tid - 64; e < 64 * K; e += kPrepThreads - 64) {
       const int i = e / K, cc = e % K;
       const float G = sG[i * LD + cc], GL = sG[63 * LD + cc];
       const float eg = exp2_hw(G);
@@ -221,10 +222,10 @@ __global__ __launch_bounds__(kKdaThreads) void kda_prep_kernel(const Tin* __rest
       Qg[e] = scale * sQ[i * LD + cc] * eg;
       Kd[e] = sK[i * LD + cc] * exp2_hw(GL - G);
     }
-    for (int cc = tid - 64; cc < K; cc += kKdaThreads - 64) gL[cc] = exp2_hw(sG[63 * LD + cc]);
+    for (int cc = tid - 64; cc < K; cc += kPrepThreads - 64) gL[cc] = exp2_hw(sG[63 * LD + cc]);
   }
   __syncthreads();
-  for (int e = tid; e < 4096; e += kKdaThreads) {
+  for (int e = tid; e < 4096; e += kPrepThreads) {
     const int i = e >> 6, j = e & 63;
     Ap[e] = sA[i][j] * sB[j];  // A' = A diag(beta); zero above the diagonal
     if (j > i) P[e] = 0.f;
@@ -451,7 +452,7 @@ template <int K, typename Tin>
 static void launch_kda_typed(const KdaChunkArgs& a) {
   const int NC = static_cast<int>((a.T + 63) / 64);
   if (NC > 0)
-    hipLaunchKernelGGL((kda_prep_kernel<K, Tin>), dim3(a.B * NC, a.H), dim3(kKdaThreads), 0, a.stream,
+    hipLaunchKernelGGL((kda_prep_kernel<K, Tin>), dim3(a.B * NC, a.H), dim3(kPrepThreads), 0, a.stream,
                        static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), a.g, a.beta, a.ws,
                        static_cast<int>(a.T), a.H, NC, a.scale);
   if (a.events[1]) (void)hipEventRecord(a.events[1], a.stream);
