@@ -3,22 +3,26 @@
 
 A step is one chunked forward pass (gdn_chunk_fwd: the prep kernel for
 recompute_w_u, then chunk_fwd_h fused with chunk_fwd_o, which at this shape runs
-in the chunk-parallel form: summary kernel, then scan kernel) over
-one batch of B=1, H=16, T=4096, K=V=128 bf16 inputs, already resident in device
-memory. The decode step (gdn_recurrent_step, N=256 requests,
-H=32, K=V=128, a 512-slot float32 state pool) is timed beside it in the same run
-and reported under "decode".
+in the chunk-parallel form: summary kernel, then scan kernel) over one batch of
+B=1, H=16, T=4096, K=V=128 bf16 inputs, already resident in device memory.
+`value` is tokens over the wall time of the K timed steps (back to back, between
+device synchronisations). Beside it, per call, HIP events recorded by the
+library on its stream give the prep and h + o durations twice: warm (calls back
+to back) and cold (a 512 MiB fill before each call evicts L2 and the 256 MiB
+infinity cache), each as mean, median, p10 and p90.
 
-Prints one JSON line on stdout (everything else goes to stderr). The K timed
-steps are plain calls. Per-kernel durations come from K further calls of
-gdn_chunk_fwd_profiled, which records HIP events on the library's stream around
-each launch (recording them inside the timed steps would add about 10 us per
-call); the roofline of the dominant part, chunk_fwd_h + chunk_fwd_o (the span of
-the summary and scan kernels), is its algorithmic FLOPs per call over that
-duration.
+The other chunk workloads (tiny float32; B=4 H=32 T=8192 with h0; 16 packed
+sequences with a state pool) are timed the same way under "configs". The decode
+step (gdn_recurrent_step, N=256 requests, H=32, K=V=128, a 512-slot float32
+state pool) and the other kernels of the library are timed beside them, and
+measurement probes give the peaks this GPU reaches (a bf16 MFMA loop, a 2 GiB
+streaming copy and read) next to the published ones.
+
+Prints one JSON line on stdout (everything else goes to stderr).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-       python bench.py --only chunk|decode|kda|verify|fp8|layer|chunk_kda|copy --steps K   (profiling runs)
+       python bench.py --only chunk|chunk1|chunk3|chunk4|decode|kda|verify|fp8|layer|chunk_kda|peaks|copy --steps K
+       (profiling runs)
 """
 
 from __future__ import annotations
@@ -31,6 +35,8 @@ import os
 import re
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -64,14 +70,23 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def chunk_flops():
-    """Algorithmic FLOPs per launch (dense per-chunk tiles, as the WarpDrive page
-    lists the products). Returns (h + o, full forward)."""
-    n_ch = B * H * (T // C)
-    h = 2 * C * K * V + 2 * C * K * V            # w h, k^T v_gated
-    o = 2 * C * K * V + 2 * C * C * K + 2 * C * C * V  # q h, q k^T, P v_new
-    prep = 2 * C * C * K + C ** 3 // 3 + 2 * C * C * V + 2 * C * C * K  # k k^T, solve, u, w
-    return n_ch * (h + o), n_ch * (h + o + prep)
+def chunk_flops(lengths, H, K, V):
+    """Algorithmic FLOPs of one call (the dense per-chunk tiles, as the WarpDrive
+    page lists the products) over sequences of the given lengths. A chunk of n
+    tokens (n = 64 but for a sequence's ragged last chunk) counts, per head,
+    h: 2nKV (w h) + 2nKV (k^T v_gated); o: 2nKV (q h) + 2n^2 K (q k^T) + 2n^2 V
+    (P v_new); prep: 2n^2 K (k k^T) + n^3 / 3 (solve) + 2n^2 V (u) + 2n^2 K (w).
+    Returns (h + o, full forward)."""
+    ho = full = 0
+    for L in lengths:
+        for c0 in range(0, int(L), C):
+            n = min(C, int(L) - c0)
+            h = 4 * n * K * V
+            o = 2 * n * K * V + 2 * n * n * K + 2 * n * n * V
+            prep = 2 * n * n * K + n ** 3 // 3 + 2 * n * n * V + 2 * n * n * K
+            ho += H * (h + o)
+            full += H * (h + o + prep)
+    return ho, full
 
 
 def decode_bytes(n_active: int) -> int:
@@ -147,63 +162,132 @@ def traffic_for(*kernels: str):
     return total
 
 
-def bench_chunk(torch, api, hev, steps, warmup, flush_bytes=512 << 20):
-    from linear_attention_sequence_recompute_amd.workloads import chunk_inputs
+# Chunk workloads: (label, lengths, H, K, V, input dtype, seed, h0 std, pool slots).
+# Equal lengths run as [B, T, ...] tensors; unequal ones packed with cu_seqlens.
+CHUNK_CONFIGS = {
+    "chunk1": ("tiny chunked forward, B=1 H=1 T=256 K=V=64, float32 q/k/v/o, h0 = 0", [256], 1, 64, 64, "f32", 1,
+               None, None),
+    "chunk": ("chunked GatedDeltaNet forward, B=1 H=16 T=4096 K=V=128 C=64, bf16 q/k/v, fp32 beta/g, o bf16 + "
+              "final state fp32", [T] * B, H, K, V, "bf16", 2, None, None),
+    "chunk3": ("long/batched chunked forward, B=4 H=32 T=8192 K=V=128, bf16 q/k/v/o, h0 ~ N(0, 0.1^2) fp32, "
+               "final state fp32", [8192] * 4, 32, 128, 128, "bf16", 3, 0.1, None),
+    "chunk4": ("variable-length packed prefill, 16 sequences of uniform [100, 6000] tokens (60217 in all), H=16 "
+               "K=V=128, bf16 q/k/v/o, states read from and written to a 17-slot fp32 pool", "varlen", 16, 128, 128,
+               "bf16", 4, None, 17),
+}
 
-    ci = chunk_inputs([T] * B, H, K, V, dtype="bf16", seed=2)
+
+def chunk_workload(name):
+    from linear_attention_sequence_recompute_amd.workloads import chunk_inputs, varlen_lengths
+
+    label, lengths, h, k, v, dtype, seed, h0_std, pool = CHUNK_CONFIGS[name]
+    if lengths == "varlen":
+        lengths = [int(x) for x in varlen_lengths(16, 100, 6000, seed=4)]
+    ci = chunk_inputs(lengths, h, k, v, dtype=dtype, seed=seed, h0_std=h0_std, pool_slots=pool)
+    return label, ci
+
+
+def bench_chunk(torch, api, hev, steps, warmup, name="chunk", flush_bytes=512 << 20):
+    """Warm wall time of `steps` back-to-back calls, then per-call events warm and
+    cold (caches flushed before every call)."""
+    label, ci = chunk_workload(name)
     dev = torch.device("cuda")
+    dt = torch.bfloat16 if ci.dtype == "bf16" else torch.float32
+    Hh, Kk = ci.q.shape[1:]
+    Vv = ci.v.shape[-1]
+    lengths = np.diff(ci.cu_seqlens).tolist()
+    n = ci.n_seqs
 
-    def t(x, dt):
-        return torch.from_numpy(x).to(dt).to(dev).view(B, T, *x.shape[1:])
+    def t(x, d):
+        x = torch.from_numpy(np.ascontiguousarray(x)).to(d).to(dev)
+        return x.view(n, -1, *x.shape[1:]) if ci.equal_length else x
 
-    q, k, v = (t(x, torch.bfloat16) for x in (ci.q, ci.k, ci.v))
+    q, k, v = (t(x, dt) for x in (ci.q, ci.k, ci.v))
     g, b = t(ci.a, torch.float32), t(ci.beta, torch.float32)
-    o = torch.empty(B, T, H, V, dtype=torch.bfloat16, device=dev)
-    ht = torch.empty(B, H, V, K, dtype=torch.float32, device=dev)
-    ws = torch.empty(api.workspace_bytes(B, B * T, H, K, V), dtype=torch.uint8, device=dev)
+    o = torch.empty(v.shape, dtype=dt, device=dev)
+    kw = {}
+    if ci.pool is not None:
+        kw["state_pool"] = torch.from_numpy(ci.pool).float().to(dev)
+        kw["state_slots"] = torch.from_numpy(ci.slots).int().to(dev)
+    else:
+        kw["ht"] = torch.empty(n, Hh, Vv, Kk, dtype=torch.float32, device=dev)
+        if ci.h0 is not None:
+            kw["h0"] = torch.from_numpy(ci.h0).float().to(dev)
+    if not ci.equal_length:
+        kw["cu_seqlens"] = ci.cu_seqlens.tolist()
+        kw["cu_seqlens_dev"] = torch.from_numpy(ci.cu_seqlens).int().to(dev)
+    del ci
+    ws = torch.empty(api.workspace_bytes(n, int(sum(lengths)), Hh, Kk, Vv, dt), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    scale = K ** -0.5
+    scale = Kk ** -0.5
 
     def step(evs=None):
-        api.chunk_fwd(q, k, v, g, b, scale=scale, out=o, ht=ht, workspace=ws, stream=stream, events=evs)
+        api.chunk_fwd(q, k, v, g, b, scale=scale, out=o, workspace=ws, stream=stream, events=evs, **kw)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # the timed steps: plain calls (events between the two kernels cost about
-    # 10 us per call, so per-kernel durations come from the next loop)
+    # 10 us per call, so per-kernel durations come from the next loops)
     t0 = time.perf_counter()
     for i in range(steps):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per-kernel durations: as many calls again, with HIP events the library
+    # per-part durations: as many calls again, with HIP events the library
     # records on the launch stream before prep, between the kernels and after scan
     evs = [hev.create(3) for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    prep = [hev.ms(e[0], e[1]) for e in evs]
-    scan = [hev.ms(e[1], e[2]) for e in evs]
-    whole = [hev.ms(e[0], e[2]) for e in evs]
+    warm = dict(prep_us=stats([1e3 * hev.ms(e[0], e[1]) for e in evs]),
+                h_o_us=stats([1e3 * hev.ms(e[1], e[2]) for e in evs]),
+                call_us=stats([1e3 * hev.ms(e[0], e[2]) for e in evs]))
 
-    # the same with L2 and the 256 MiB infinity cache flushed before every step
+    # the same with L2 and the 256 MiB infinity cache flushed before every call
     flush = torch.empty(flush_bytes, dtype=torch.uint8, device=dev)
-    cold_prep, cold_scan = [], []
+    cp, cs, cc = [], [], []
     for i in range(steps):
         flush.fill_(i & 0xFF)
         step(evs[i])
         torch.cuda.synchronize()
-        cold_prep.append(hev.ms(evs[i][0], evs[i][1]))
-        cold_scan.append(hev.ms(evs[i][1], evs[i][2]))
+        cp.append(1e3 * hev.ms(evs[i][0], evs[i][1]))
+        cs.append(1e3 * hev.ms(evs[i][1], evs[i][2]))
+        cc.append(1e3 * hev.ms(evs[i][0], evs[i][2]))
     for e in evs:
         hev.destroy(e)
     del flush
-    return dict(wall_s=wall, prep_ms=stats(prep), scan_ms=stats(scan), call_ms=stats(whole),
-                cold_prep_ms=stats(cold_prep), cold_scan_ms=stats(cold_scan))
+    cold = dict(prep_us=stats(cp), h_o_us=stats(cs), call_us=stats(cc))
+    return dict(label=label, lengths=lengths, H=Hh, K=Kk, V=Vv, dtype=dt, wall_s=wall, warm=warm, cold=cold)
+
+
+def chunk_entry(res, steps, peaks):
+    """JSON entry of a chunk workload: tokens/s (warm wall time, warm and cold
+    events), per-part times and the h + o roofline against the bf16 MFMA peak
+    (float32 inputs run on the fp32 MFMA and are priced against its peak)."""
+    tokens = int(sum(res["lengths"]))
+    f_ho, f_full = chunk_flops(res["lengths"], res["H"], res["K"], res["V"])
+    bf16 = res["dtype"] is not None and str(res["dtype"]).endswith("bfloat16")
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    ho_w, ho_c = res["warm"]["h_o_us"]["mean"], res["cold"]["h_o_us"]["mean"]
+    ach_w, ach_c = f_ho / ho_w / 1e6, f_ho / ho_c / 1e6
+    ms = 1e3 * res["wall_s"] / steps
+    entry = {
+        "workload": res["label"],
+        "value": tokens / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
+        "value_cold": tokens / (res["cold"]["call_us"]["mean"] / 1e6),
+        "timing_us": {"warm": res["warm"], "cold": res["cold"]},
+        "roofline": {"bound": "mfma", "achieved": ach_w, "peak": peak, "unit": "TFLOP/s", "frac": ach_w / peak,
+                     "cold_achieved": ach_c, "cold_frac": ach_c / peak, "flops_per_launch": f_ho,
+                     "avg_launch_us": ho_w},
+        "full_fwd_tflops": f_full / (ms / 1e3) / 1e12,
+    }
+    if bf16 and peaks and peaks.get("mfma_bf16_tflops"):
+        entry["roofline"]["frac_of_measured_peak"] = ach_w / peaks["mfma_bf16_tflops"]
+    return entry
 
 
 def kda_chunk_flops():
@@ -292,7 +376,7 @@ def bench_decode(torch, api, hev, steps, warmup):
     ms = [hev.ms(e[0], e[1]) for e in evs]
     for e in evs:
         hev.destroy(e)
-    return dict(wall_s=wall, kernel_ms=stats(ms), n_active=int((di.slots > 0).sum()))
+    return dict(wall_s=wall, kernel_ms=stats(ms), n_active=int((di.slots > 0).sum()), _inputs=di)
 
 
 def bench_decode_kda(torch, api, hev, steps, warmup):
@@ -466,23 +550,78 @@ def bench_copy(torch, steps, nbytes=1 << 30):
     return nbytes
 
 
-def cpu_baseline(min_seconds=10.0):
-    """The fp64 oracle (chunked WY form) on the host cores, over repeated passes
-    of the same B=1, H=16, T=4096 workload until min_seconds have elapsed."""
-    import numpy as np  # noqa: F401
+def bench_peaks(torch, api, hev, reps=5, nbytes=2 << 30):
+    """The peaks this GPU reaches, from the library's measurement probes: a bf16
+    MFMA loop over every SIMD (2 waves each, 8 independent accumulators per
+    wave), a streaming copy of 2 GiB and a streaming read of 2 GiB."""
+    L = api._lib.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    waves, iters = cus * 4 * 2, 4096
+    sink = torch.empty(max(waves * 64, 8192), dtype=torch.float32, device="cuda")
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
 
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        evs = [hev.create(2) for _ in range(reps)]
+        for e in evs:
+            hev.record(e[0], stream)
+            fn()
+            hev.record(e[1], stream)
+        torch.cuda.synchronize()
+        ms = [hev.ms(e[0], e[1]) for e in evs]
+        for e in evs:
+            hev.destroy(e)
+        return stats(ms)["median"] / 1e3
+
+    def ok(st):
+        assert st == 0, api._lib.status_string(st)
+
+    t_mfma = timed(lambda: ok(L.gdn_probe_mfma_bf16(sink.data_ptr(), waves, iters, stream)))
+    t_copy = timed(lambda: ok(L.gdn_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream)))
+    t_read = timed(lambda: ok(L.gdn_probe_read(src.data_ptr(), sink.data_ptr(), nbytes, stream)))
+    del src, dst
+    flops = waves * iters * 8 * 16384
+    return {"mfma_bf16_tflops": flops / t_mfma / 1e12, "copy_gbs": 2 * nbytes / t_copy / 1e9,
+            "read_gbs": nbytes / t_read / 1e9,
+            "probes": f"bf16 MFMA loop: {waves} waves x {iters} x 8 v_mfma_f32_16x16x32_bf16; copy and read of "
+                      f"{nbytes >> 30} GiB (copy counts bytes read + written); median of {reps}"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(min_seconds=10.0, decode_in=None):
+    """The fp64 oracle on the host cores, each leg on a bounded sample:
+    the chunked WY form (O2) over repeated full passes of the B=1, H=16, T=4096
+    workload until min_seconds have elapsed (the headline value); the naive
+    per-token recurrence (O1) over the tiny workload (repeated for a second) and
+    one full pass of the H=16, T=4096 workload; the decode step (O3) over the
+    N=256, H=32 decode workload once (GB/s of the same algorithmic bytes as the
+    GPU's)."""
     import oracle
     from linear_attention_sequence_recompute_amd.workloads import chunk_inputs
 
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
     ci = chunk_inputs([T], H, K, V, dtype="bf16", seed=2)
-    n_tok = 0
+    n_tok = passes = 0
     t0 = time.perf_counter()
-    passes = 0
     while True:
         oracle.chunked_fwd(ci.q, ci.k, ci.v, ci.a, ci.beta, scale=K ** -0.5)
         n_tok += T
@@ -490,9 +629,28 @@ def cpu_baseline(min_seconds=10.0):
         if time.perf_counter() - t0 >= min_seconds:
             break
     dt = time.perf_counter() - t0
+    extra = {}
+    t1 = time.perf_counter()
+    oracle.recurrent_fwd(ci.q, ci.k, ci.v, ci.a, ci.beta, scale=K ** -0.5)
+    extra["o1_naive_h16_t4096_tokens_per_s"] = T / (time.perf_counter() - t1)
+    tiny = chunk_inputs([256], 1, 64, 64, dtype="f32", seed=1)
+    n1 = 0
+    t1 = time.perf_counter()
+    while time.perf_counter() - t1 < 1.0:
+        oracle.recurrent_fwd(tiny.q, tiny.k, tiny.v, tiny.a, tiny.beta, scale=1.0)
+        n1 += 256
+    extra["o1_naive_tiny_tokens_per_s"] = n1 / (time.perf_counter() - t1)
+    if decode_in is not None:
+        di = decode_in
+        t1 = time.perf_counter()
+        oracle.decode_step(di.q, di.k, di.v, di.a, di.beta, di.pool, di.slots, scale=DK ** -0.5)
+        dt3 = time.perf_counter() - t1
+        extra["o3_decode_gbs"] = decode_bytes(int((di.slots > 0).sum())) / dt3 / 1e9
+        extra["o3_decode_s"] = dt3
     return dict(value=n_tok / dt, unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=f"{passes} full passes of the B=1 H=16 T=4096 K=V=128 workload through the fp64 chunked "
-                       f"oracle (numpy, {threads} BLAS threads) in {dt:.1f} s")
+                       f"oracle (numpy, {threads} BLAS threads) in {dt:.1f} s; O1 and O3 legs as in 'extra'",
+                cpu_model=cpu_model(), affinity_cores=affinity, blas_threads=int(threads), extra=extra)
 
 
 def main():
@@ -500,7 +658,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "kda", "verify", "fp8", "layer", "chunk_kda", "copy"], default="all")
+    ap.add_argument("--only", choices=["all", "chunk", "chunk1", "chunk3", "chunk4", "decode", "kda", "verify", "fp8",
+                                       "layer", "chunk_kda", "peaks", "copy"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -523,96 +682,86 @@ def main():
         n = bench_copy(torch, args.steps)
         log(f"copied {n} bytes x {args.steps}")
         return
-    res_c = res_d = None
-    if args.only in ("all", "chunk"):
-        log("chunk: B=1 H=16 T=4096 K=V=128 bf16 ...")
-        res_c = bench_chunk(torch, api, hev, args.steps, args.warmup)
-        log(json.dumps(res_c))
-    if args.only in ("all", "decode"):
-        log("decode: N=256 H=32 K=V=128 pool=512 ...")
-        res_d = bench_decode(torch, api, hev, args.steps, args.warmup)
-        log(json.dumps(res_d))
-    res_k = None
-    if args.only in ("all", "kda"):
-        log("decode with per-key-channel decay: N=256 H=32 K=V=128 pool=512 ...")
-        res_k = bench_decode_kda(torch, api, hev, args.steps, args.warmup)
-        log(json.dumps(res_k))
-    res_v = None
-    if args.only in ("all", "verify"):
-        log(f"verify decode: N={VN} T={VT} H=32 K=V=128 pool=512 ...")
-        res_v = bench_verify(torch, api, hev, args.steps, args.warmup)
-        log(json.dumps(res_v))
-    res_q = None
-    if args.only in ("all", "fp8"):
-        log(f"fp8 quant: [{QR}, {QC}] float32, groups of {QG} ...")
-        res_q = bench_fp8(torch, api, hev, args.steps, args.warmup)
-        log(json.dumps(res_q))
-    res_l = None
-    if args.only in ("all", "layer"):
-        log(f"decode layer front/back: N={DN} H={DH} D={DK} conv pool={DSLOTS} ...")
-        res_l = bench_layer(torch, api, hev, args.steps, args.warmup)
-        log(json.dumps(res_l))
-    res_ck = None
-    if args.only in ("all", "chunk_kda"):
-        log("chunk form with per-channel decays: B=1 H=16 T=4096 K=V=128 bf16 ...")
-        res_ck = bench_chunk_kda(torch, api, hev, args.steps, args.warmup)
-        log(json.dumps(res_ck))
-    if args.only != "all":
+    only = args.only
+    res = {}
+
+    def run(name, fn, msg):
+        if only in ("all", name):
+            log(msg + " ...")
+            res[name] = fn()
+            log(json.dumps({k: v for k, v in res[name].items() if not k.startswith("_")}, default=str))
+
+    run("peaks", lambda: bench_peaks(torch, api, hev), "measured peaks: bf16 MFMA loop, 2 GiB copy and read")
+    for name in ("chunk", "chunk1", "chunk3", "chunk4"):
+        run(name, lambda name=name: bench_chunk(torch, api, hev, args.steps, args.warmup, name),
+            f"{name}: {CHUNK_CONFIGS[name][0]}")
+    run("decode", lambda: bench_decode(torch, api, hev, args.steps, args.warmup), "decode: N=256 H=32 K=V=128 pool=512")
+    run("kda", lambda: bench_decode_kda(torch, api, hev, args.steps, args.warmup),
+        "decode with per-key-channel decay: N=256 H=32 K=V=128 pool=512")
+    run("verify", lambda: bench_verify(torch, api, hev, args.steps, args.warmup),
+        f"verify decode: N={VN} T={VT} H=32 K=V=128 pool=512")
+    run("fp8", lambda: bench_fp8(torch, api, hev, args.steps, args.warmup), f"fp8 quant: [{QR}, {QC}] float32, "
+        f"groups of {QG}")
+    run("layer", lambda: bench_layer(torch, api, hev, args.steps, args.warmup),
+        f"decode layer front/back: N={DN} H={DH} D={DK} conv pool={DSLOTS}")
+    run("chunk_kda", lambda: bench_chunk_kda(torch, api, hev, args.steps, args.warmup),
+        "chunk form with per-channel decays: B=1 H=16 T=4096 K=V=128 bf16")
+    if only != "all":
         return
 
-    flops_ho, flops_full = chunk_flops()
-    tokens = B * T
-    ms_per_step = 1e3 * res_c["wall_s"] / args.steps
-    scan_s = res_c["scan_ms"]["mean"] / 1e3
-    achieved = flops_ho / scan_s / 1e12
+    peaks = res["peaks"]
+    head = chunk_entry(res["chunk"], args.steps, peaks)
+    head["roofline"]["kernel"] = ("chunk_fwd_h fused with chunk_fwd_o: summary_kernel + scan_kernel "
+                                  "(chunk-parallel form, 4 segments of 16 chunks)")
+    head["roofline"]["traffic"] = traffic_for("summary_kernel", "scan_kernel")
+    res_d = res["decode"]
     dec_s = res_d["kernel_ms"]["mean"] / 1e3
     dec_b = decode_bytes(res_d["n_active"])
     dec_gbs = dec_b / dec_s / 1e9
+
+    def hbm_roofline(achieved_gbs, kernel_traffic, nbytes):
+        return {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved_gbs / PEAK_HBM_GBS, "frac_of_measured_copy": achieved_gbs / peaks["copy_gbs"],
+                "traffic": kernel_traffic, "bytes_per_launch": nbytes}
+
     out = {
         "metric": "GDN fwd tokens/s + % bf16 MFMA peak (H16,K=V=128,T4096); decode GB/s % peak",
-        "value": tokens / (ms_per_step / 1e3),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "chunked GatedDeltaNet forward, B=1 H=16 T=4096 K=V=128 C=64, bf16 q/k/v, "
-                               "fp32 beta/g, o bf16 + final state fp32",
-                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": K, "chunk": C,
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma",
-                     "kernel": "chunk_fwd_h fused with chunk_fwd_o: summary_kernel + scan_kernel "
-                               "(chunk-parallel form, 4 segments of 16 chunks)",
-                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic_for("summary_kernel", "scan_kernel"),
-                     "flops_per_launch": flops_ho, "avg_launch_us": scan_s * 1e6},
-        "kernels_us": {"prep": res_c["prep_ms"]["mean"] * 1e3, "h_o": res_c["scan_ms"]["mean"] * 1e3,
-                       "call": res_c["call_ms"]["mean"] * 1e3,
-                       "cold_prep": res_c["cold_prep_ms"]["mean"] * 1e3,
-                       "cold_h_o": res_c["cold_scan_ms"]["mean"] * 1e3},
-        "full_fwd_tflops": flops_full / (ms_per_step / 1e3) / 1e12,
+        "config": {"workload": head["workload"], "global_batch": B, "seq_len": T, "heads": H, "head_dim": K,
+                   "chunk": C, "parallelism": "single GPU"},
+        "value_cold": head["value_cold"],
+        "timing_us": head["timing_us"],
+        "roofline": head["roofline"],
+        "full_fwd_tflops": head["full_fwd_tflops"],
+        "measured_peaks": peaks,
+        "configs": {"tiny_f32": chunk_entry(res["chunk1"], args.steps, peaks),
+                    "batched_long": chunk_entry(res["chunk3"], args.steps, peaks),
+                    "varlen_pool": chunk_entry(res["chunk4"], args.steps, peaks)},
         "decode": {"workload": "recurrent decode step, N=256 requests (all active), H=32, K=V=128, "
                                "pool [512, 32, 128, 128] fp32, bf16 q/k/v/o",
                    "value": dec_gbs, "unit": "GB/s", "avg_launch_us": dec_s * 1e6,
-                   "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                "frac": dec_gbs / PEAK_HBM_GBS, "traffic": traffic_for("recurrent_step_kernel"),
-                                "bytes_per_launch": dec_b}},
+                   "timing_us": {k: v * 1e3 for k, v in res_d["kernel_ms"].items()},
+                   "roofline": hbm_roofline(dec_gbs, traffic_for("recurrent_step_kernel"), dec_b)},
     }
+    res_k = res["kda"]
     kda_s = res_k["kernel_ms"]["mean"] / 1e3
     kda_b = decode_bytes(res_k["n_active"]) + res_k["n_active"] * DH * (DK - 1) * 4  # g per key channel
     out["decode_kda"] = {
         "workload": "recurrent decode step with a log-decay per key channel, N=256 requests (all active), H=32, "
                     "K=V=128, pool [512, 32, 128, 128] fp32, bf16 q/k/v/o",
         "value": kda_b / kda_s / 1e9, "unit": "GB/s", "avg_launch_us": kda_s * 1e6,
-        "roofline": {"bound": "hbm", "achieved": kda_b / kda_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": kda_b / kda_s / 1e9 / PEAK_HBM_GBS, "traffic": traffic_for("recurrent_step_kernel_kda"),
-                     "bytes_per_launch": kda_b}}
+        "roofline": hbm_roofline(kda_b / kda_s / 1e9, traffic_for("recurrent_step_kernel_kda"), kda_b)}
+    res_v = res["verify"]
     ver_s = res_v["kernel_ms"]["mean"] / 1e3
     ver_b = verify_bytes(res_v["n_active"], VT)
     out["decode_verify"] = {
@@ -620,31 +769,25 @@ def main():
                     "fp32 (source read once, a state written per token), bf16 q/k/v/o",
         "value": ver_b / ver_s / 1e9, "unit": "GB/s", "avg_launch_us": ver_s * 1e6,
         "tokens_per_s": VN * VT / ver_s,
-        "roofline": {"bound": "hbm", "achieved": ver_b / ver_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": ver_b / ver_s / 1e9 / PEAK_HBM_GBS, "traffic": traffic_for("recurrent_verify_kernel"),
-                     "bytes_per_launch": ver_b}}
-    q_s = res_q["kernel_ms"]["mean"] / 1e3
+        "roofline": hbm_roofline(ver_b / ver_s / 1e9, traffic_for("recurrent_verify_kernel"), ver_b)}
+    q_s = res["fp8"]["kernel_ms"]["mean"] / 1e3
     q_b = QR * QC * (4 + 1) + QR * (QC // QG) * 4
     out["fp8_quant"] = {
         "workload": f"fp8 group quantisation, [{QR}, {QC}] float32 activations, groups of {QG}, E4M3 codes + "
                     "float32 scales",
         "value": q_b / q_s / 1e9, "unit": "GB/s", "avg_launch_us": q_s * 1e6,
-        "roofline": {"bound": "hbm", "achieved": q_b / q_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": q_b / q_s / 1e9 / PEAK_HBM_GBS, "traffic": traffic_for("fp8_quant_kernel"),
-                     "bytes_per_launch": q_b}}
+        "roofline": hbm_roofline(q_b / q_s / 1e9, traffic_for("fp8_quant_kernel"), q_b)}
     lp_b, lr_b = layer_bytes()
+    res_l = res["layer"]
     lp_s, lr_s = res_l["prologue_ms"]["mean"] / 1e3, res_l["rmsnorm_ms"]["mean"] / 1e3
     out["decode_layer"] = {
         "workload": f"decode layer front (4-tap conv over a bf16 conv-state pool of {DSLOTS} slots, SiLU, q/k L2 "
                     f"norm, sigmoid beta) and back (gated RMSNorm, bf16 out), N={DN} requests, H={DH}, D={DK}",
         "prologue": {"avg_launch_us": lp_s * 1e6, "bytes_per_launch": lp_b,
-                     "roofline": {"bound": "hbm", "achieved": lp_b / lp_s / 1e9, "peak": PEAK_HBM_GBS,
-                                  "unit": "GB/s", "frac": lp_b / lp_s / 1e9 / PEAK_HBM_GBS,
-                                  "traffic": traffic_for("decode_prologue_kernel")}},
+                     "roofline": hbm_roofline(lp_b / lp_s / 1e9, traffic_for("decode_prologue_kernel"), lp_b)},
         "gated_rmsnorm": {"avg_launch_us": lr_s * 1e6, "bytes_per_launch": lr_b,
-                          "roofline": {"bound": "hbm", "achieved": lr_b / lr_s / 1e9, "peak": PEAK_HBM_GBS,
-                                       "unit": "GB/s", "frac": lr_b / lr_s / 1e9 / PEAK_HBM_GBS,
-                                       "traffic": traffic_for("gated_rmsnorm_kernel")}}}
+                          "roofline": hbm_roofline(lr_b / lr_s / 1e9, traffic_for("gated_rmsnorm_kernel"), lr_b)}}
+    res_ck = res["chunk_kda"]
     ck_scan_f, ck_prep_f = kda_chunk_flops()
     ck_scan_s, ck_prep_s = res_ck["scan_ms"]["mean"] / 1e3, res_ck["prep_ms"]["mean"] / 1e3
     ck_ms = 1e3 * res_ck["wall_s"] / args.steps
@@ -663,7 +806,7 @@ def main():
                           "traffic": traffic_for("kda_prep_kernel"), "flops_per_launch": ck_prep_f}}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds, res_d.get("_inputs"))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

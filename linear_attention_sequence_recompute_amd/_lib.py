@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libgdn.so")
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
 GDN_BF16, GDN_F32 = 0, 1
 
-# (name, restype, argtypes) for every entry point declared in include/gdn.h
+# (name, restype, argtypes) for every entry point declared in include/*.h
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _I64 = ctypes.c_int64
@@ -40,6 +40,10 @@ SIGNATURES = {
     "gdn_chunk_fwd_kda_profiled": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I, _P, _P, _P,
                                         ctypes.c_size_t, _P, _P]),
     "gdn_status_string": (ctypes.c_char_p, [_I]),
+    # measurement probes (include/gdn_probe.h)
+    "gdn_probe_mfma_bf16": (_I, [_P, _I, _I, _P]),
+    "gdn_probe_copy": (_I, [_P, _P, _I64, _P]),
+    "gdn_probe_read": (_I, [_P, _P, _I64, _P]),
 }
 
 

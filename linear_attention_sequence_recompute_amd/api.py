@@ -36,6 +36,13 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
+def _shape(t: Optional[torch.Tensor], shape, name: str):
+    """Rejects a tensor whose shape is not ``shape``: the C ABI takes sizes, not
+    shapes, so a wrong-sized buffer would otherwise be read or written out of bounds."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _need(t: torch.Tensor, name: str, dtype=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -80,12 +87,29 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         n_seqs = 1 if cu_seqlens is None else len(cu_seqlens) - 1
     else:
         raise ValueError("q must be [B, T, H, K] or [Ttot, H, K]")
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or g.shape != q.shape[:-1] or beta.shape != g.shape:
+        raise ValueError("inconsistent shapes of q, k, v, g, beta")
+    if cu_seqlens is not None and n_seqs < 1:
+        raise ValueError("cu_seqlens needs at least two offsets")
+    state = (n_seqs, H, V, K)
+    _shape(out, v.shape, "out")
+    if state_pool is not None:
+        if h0 is not None or ht is not None:
+            raise ValueError("h0 and ht must be None when state_pool is given")
+        if state_slots is None:
+            raise ValueError("state_pool needs state_slots")
+        if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, V, K):
+            raise ValueError(f"state_pool must have shape (P, {H}, {V}, {K}), got {tuple(state_pool.shape)}")
+        _shape(state_slots, (n_seqs,), "state_slots")
+    else:
+        _shape(h0, state, "h0")
+        _shape(ht, state, "ht")
+    if cu_seqlens_dev is not None:
+        _shape(cu_seqlens_dev, (n_seqs + 1,), "cu_seqlens_dev")
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
     for name, t in (("g", g), ("beta", beta)):
         _need(t, name, torch.float32)
-    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or g.shape != q.shape[:-1] or beta.shape != g.shape:
-        raise ValueError("inconsistent shapes of q, k, v, g, beta")
     in_dt = q.dtype
     out_dtype = out_dtype or in_dt
     if out is None:
@@ -307,12 +331,15 @@ def chunk_fwd_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         q, k, v, g, beta = (x.unsqueeze(0) for x in (q, k, v, g, beta))
     B, T, H, K = q.shape
     V = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError("inconsistent shapes of q, k, v, g, beta")
+    _shape(out, (B, T, H, V), "out")
+    _shape(h0, (B, H, V, K), "h0")
+    _shape(ht, (B, H, V, K), "ht")
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
     _need(g, "g", torch.float32)
     _need(beta, "beta", torch.float32)
-    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != (B, T, H) or beta.shape != (B, T, H):
-        raise ValueError("inconsistent shapes of q, k, v, g, beta")
     out_dtype = out_dtype or q.dtype
     if out is None:
         out = torch.empty((B, T, H, V), dtype=out_dtype, device=q.device)

@@ -516,7 +516,7 @@ struct ScanSeq {
 // s_out[key * K + lc]). PUB: publish the state and v_new for output waves.
 template <int K, int V, typename Tin, int NCH, bool PUB = true>
 __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, const ScanSeq& sq,
-                                           const float* __restrict__ s_in, float* __restrict__ s_out, int ident,
+                                           const float* s_in, float* s_out, int ident,  // may alias
                                            bool out_t = false, const float* __restrict__ fc = nullptr,
                                            const float* __restrict__ fm = nullptr, int n_fold = 0,
                                            int64_t fstride = 0) {
@@ -1127,7 +1127,7 @@ template <int K, int V, typename Tin, typename Tout, int NCH>
 __global__ __launch_bounds__(scan_threads<NCH>()) __attribute__((amdgpu_waves_per_eu(NCH, NCH))) void scan_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o, int H,
     float scale, int n_seqs, int T_eq, int ncs_eq, int total_tokens, int n_chunks, const int32_t* __restrict__ cu,
-    const float* __restrict__ h0, float* __restrict__ ht, float* __restrict__ pool, int64_t pool_slots,
+    const float* h0, float* ht, float* pool, int64_t pool_slots,  // h0 and ht may alias (in place)
     const int32_t* __restrict__ slots, int seg_len, int n_seg, ChunkWs ws) {
   using S = ScanSmem<K, Tin, NCH>;
   constexpr int NG = V / 16 / NCH;  // workgroups per (sequence, head, segment)

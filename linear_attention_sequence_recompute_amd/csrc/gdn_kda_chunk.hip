@@ -55,6 +55,8 @@ __device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cas
 // K o e^G, s q o e^G, K o e^{G_last - G} (each [64][K]) and e^{G_last} [K].
 __host__ __device__ constexpr int64_t kda_floats_per_chunk(int K) { return 2 * 64 * 64 + 3 * 64 * K + K; }
 
+constexpr float kMinLogDecay = -100.f;  // per token and channel
+
 template <int K, typename Tin>
 __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                                                                const float* __restrict__ g,
@@ -97,7 +99,12 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(const Tin* __res
     const float4 x = lq[m], y = lk[m], z = lg[m];
     *reinterpret_cast<float4*>(&sQ[i * LD + c4]) = make_float4(f * x.x, f * x.y, f * x.z, f * x.w);
     *reinterpret_cast<float4*>(&sK[i * LD + c4]) = make_float4(f * y.x, f * y.y, f * y.z, f * y.w);
-    *reinterpret_cast<float4*>(&sG[i * LD + c4]) = make_float4(fg * z.x, fg * z.y, fg * z.z, fg * z.w);
+    // a log-decay of -inf (the channel forgets everything) is taken as kMinLogDecay:
+    // its factor e^-100 is 0 to every digit that matters, while the differences
+    // G_i - G_j of cumulative sums stay finite (-inf - -inf would be NaN)
+    *reinterpret_cast<float4*>(&sG[i * LD + c4]) =
+        make_float4(fg * fmaxf(z.x, kMinLogDecay), fg * fmaxf(z.y, kMinLogDecay), fg * fmaxf(z.z, kMinLogDecay),
+                    fg * fmaxf(z.w, kMinLogDecay));
   }
   if (tid < 64) sB[tid] = tid < n ? bt : 0.f;
   __syncthreads();

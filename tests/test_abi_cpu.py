@@ -13,6 +13,8 @@ from linear_attention_sequence_recompute_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libgdn.so not built")
 
@@ -20,13 +22,15 @@ BF16, F32 = _lib.GDN_BF16, _lib.GDN_F32
 FAKE = 1 << 20  # an aligned non-null address; never dereferenced by the failing calls below
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    return re.findall(r"^\S[^()#]*?\b(gdn_\w+)\s*\(", text, re.M)
+def declared_functions(headers=None):
+    names = []
+    for h in headers or HEADERS:
+        names += re.findall(r"^\S[^()#]*?\b(gdn_\w+)\s*\(", open(h).read(), re.M)
+    return names
 
 
 def test_header_declares_the_boundary():
-    assert set(declared_functions()) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
+    assert set(declared_functions([HEADER])) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
                                          "gdn_chunk_fwd_profiled", "gdn_recurrent_step", "gdn_recurrent_step_kda",
                                          "gdn_recurrent_verify", "gdn_fp8_quant", "gdn_decode_prologue",
                                          "gdn_gated_rmsnorm", "gdn_chunk_fwd_kda_workspace_bytes",
@@ -288,3 +292,16 @@ def test_chunk_fwd_kda_validation():
     assert call(ws=None) == E.GDN_EWORKSPACE
     assert call(ws_bytes=1024) == E.GDN_EWORKSPACE
     assert call(ws=FAKE + 16) == E.GDN_EWORKSPACE
+
+
+def test_probe_validation():
+    """The measurement probes reject bad arguments before launching."""
+    L = _lib.lib()
+    EINVAL = _lib.GDN_EINVAL
+    assert L.gdn_probe_mfma_bf16(None, 2048, 10, None) == EINVAL
+    assert L.gdn_probe_mfma_bf16(FAKE, 2046, 10, None) == EINVAL  # not a multiple of 4
+    assert L.gdn_probe_mfma_bf16(FAKE, 2048, 0, None) == EINVAL
+    assert L.gdn_probe_copy(FAKE, None, 1 << 20, None) == EINVAL
+    assert L.gdn_probe_copy(FAKE, FAKE + 8, 1 << 20, None) == EINVAL  # misaligned
+    assert L.gdn_probe_copy(FAKE, FAKE, 1000, None) == EINVAL  # not a multiple of 16
+    assert L.gdn_probe_read(FAKE, FAKE, 0, None) == EINVAL

@@ -243,16 +243,18 @@ def test_config_h16_t4096_full():
     check_chunk(ci, 128 ** -0.5, label="H16 T4096")
 
 
-def test_config_batched_long_sampled():
+def test_config_batched_long_full():
     """B=4, H=32, T=8192, K=V=128, bf16, h0 ~ N(0, 0.1^2): the launch the long
-    configuration times; the oracle checks sampled (sequence, head) pairs."""
+    configuration times; every (sequence, head) pair, every output and every
+    final state against the oracle."""
     ci = chunk_inputs([8192] * 4, 32, 128, 128, dtype="bf16", seed=3, h0_std=0.1)
-    check_chunk(ci, 128 ** -0.5, heads=[0, 17, 31], seqs=[0, 3], label="B4 H32 T8192 sampled")
+    check_chunk(ci, 128 ** -0.5, label="B4 H32 T8192")
 
 
-def test_varlen_pool_sampled():
+def test_varlen_pool_full():
     """16 packed sequences, lengths uniform in [100, 6000] (not chunk-aligned),
-    initial states read from and final states written back to a state pool."""
+    initial states read from and final states written back to a state pool;
+    every (sequence, head) pair checked."""
     lengths = varlen_lengths(16, 100, 6000, seed=4)
     ci = chunk_inputs(lengths, 16, 128, 128, dtype="bf16", seed=4, pool_slots=17)
     pool0 = dev(ci.pool)
@@ -265,17 +267,16 @@ def test_varlen_pool_sampled():
     assert torch.equal(pool16, pool32)
     # slot 0 is reserved and untouched
     assert torch.equal(pool32[0], pool0[0])
-    seqs = [int(np.argmin(lengths)), int(np.argmax(lengths)), 5]
-    heads = [0, 9]
-    ref = oracle_chunk(ci, scale, heads=heads, seqs=seqs)
+    ref = oracle_chunk(ci, scale)
     o_h = host(o32)
-    for s in seqs:
+    worst_o = worst_s = 0.0
+    for s in range(len(lengths)):
         r = slice(int(ci.cu_seqlens[s]), int(ci.cu_seqlens[s + 1]))
         o_ref, S_ref = ref[s]
-        eo = max_err_over_rms(o_h[r][:, heads], o_ref)
-        es = max_err_over_rms(host(pool32[ci.slots[s]])[heads], S_ref)
-        _print(f"[varlen seq {s} len {lengths[s]}] max|do|/rms={eo:.3e} max|dS|/rms={es:.3e}")
-        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+        worst_o = max(worst_o, max_err_over_rms(o_h[r], o_ref))
+        worst_s = max(worst_s, max_err_over_rms(host(pool32[ci.slots[s]]), S_ref))
+    _print(f"[varlen 16 seqs, all pairs] max|do|/rms={worst_o:.3e} max|dS|/rms={worst_s:.3e}")
+    assert worst_o <= TOL["bf16"] and worst_s <= TOL["bf16"]
 
 
 def test_varlen_edge_lengths_dense_states():
@@ -595,9 +596,13 @@ def run_chunk_kda(ci, g, B, T, scale, out_dtype, h0=None, ht=None):
     return o, ht
 
 
-def check_chunk_kda(B, T, H, K, V, dtype, seed, shift, label, heads=None):
+def check_chunk_kda(B, T, H, K, V, dtype, seed, shift, label, heads=None, forget=0):
     ci = chunk_inputs([T] * B, H, K, V, dtype=dtype, seed=seed, h0_std=0.1)
     g = channel_log_decay((B * T, H, K), seed + 1, shift)
+    if forget:  # `forget` random (token, head, channel) entries forget everything: log-decay -inf
+        rng = np.random.default_rng(seed + 2)
+        idx = rng.choice(g.size, forget, replace=False)
+        g.reshape(-1)[idx] = -np.inf
     scale = K ** -0.5
     h0 = dev(ci.h0)
     o32, ht32 = run_chunk_kda(ci, g, B, T, scale, "f32", h0)
@@ -630,9 +635,17 @@ def test_chunk_kda_long_memory():
     check_chunk_kda(1, 300, 2, 128, 128, "bf16", seed=97, shift=-4.0, label="long memory")
 
 
-def test_chunk_kda_config_sampled():
-    """B=1, H=16, T=4096, K=V=128 (the chunk workload's shape), heads 0, 7, 15 against the oracle."""
-    check_chunk_kda(1, 4096, 16, 128, 128, "bf16", seed=98, shift=2.0, label="H16 T4096", heads=[0, 7, 15])
+def test_chunk_kda_config_full():
+    """B=1, H=16, T=4096, K=V=128 (the chunk workload's shape), every head against the oracle."""
+    check_chunk_kda(1, 4096, 16, 128, 128, "bf16", seed=98, shift=2.0, label="H16 T4096")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chunk_kda_fully_forgetting_channels(dtype):
+    """Some (token, head, channel) log-decays are -inf (that channel's memory is
+    wiped): outputs and states stay finite and match the definition, where
+    exp(-inf) = 0; rows past the ragged end read such a value too."""
+    check_chunk_kda(2, 150, 3, 128, 128, dtype, seed=120, shift=-4.0, label=f"-inf decays {dtype}", forget=200)
 
 
 def test_chunk_kda_uniform_channels_equal_the_scalar_gate():
