@@ -22,7 +22,9 @@
  *
  * Conventions shared by every entry point:
  *  - Pointers are device pointers owned by the caller unless stated otherwise.
- *    The library allocates nothing and keeps no state between calls.
+ *    The library allocates nothing and keeps no state between calls (the one
+ *    exception, gdn_chunk_fwd_noalloc's device array, holds no state either:
+ *    its contents on entry are ignored).
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
  *    Calls return without waiting for the GPU.
  *  - Arguments are validated on the host before anything is enqueued; on any
@@ -131,6 +133,39 @@ gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const void* v, c
                                   float* state_pool, int64_t pool_slots,
                                   const int32_t* state_slots, void* workspace,
                                   size_t workspace_bytes, void* stream, void* const* events);
+
+/*
+ * Bytes of the device array that backs gdn_chunk_fwd_noalloc's workspace: the
+ * largest gdn_chunk_fwd_workspace_bytes(...) that entry point accepts (64 MiB;
+ * e.g. B=1, H=16, T=4096, K=V=128 in bfloat16 needs about 33 MB).
+ */
+#define GDN_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/*
+ * gdn_chunk_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. Same
+ * arguments (without workspace and workspace_bytes), same launches, same
+ * results bit for bit; the workspace is a file-scope device array of the
+ * library, GDN_NOALLOC_WORKSPACE_BYTES bytes, of which each GPU the library runs
+ * on holds its own copy until the process ends. Nothing is allocated and the
+ * array's contents on entry are ignored (every call writes what it reads).
+ *
+ * The device is the current HIP device, which must be the stream's. Calls on
+ * one GPU share that GPU's array: two calls whose work overlaps on the GPU (on
+ * different streams, or from different host threads without ordering) race and
+ * give undefined results; calls in one stream are ordered and safe.
+ *
+ * Returns GDN_EWORKSPACE, without launching, when
+ * gdn_chunk_fwd_workspace_bytes(n_seqs, total_tokens, H, K, V, in_dtype) exceeds
+ * GDN_NOALLOC_WORKSPACE_BYTES; GDN_EHIP if the array's device address cannot
+ * be obtained or a launch fails; otherwise every status as gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, void* o, int n_seqs, int64_t total_tokens, int H,
+                                 int K, int V, float scale, gdn_dtype in_dtype, gdn_dtype out_dtype,
+                                 const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                 const float* h0, float* ht, float* state_pool, int64_t pool_slots,
+                                 const int32_t* state_slots, void* stream);
 
 /*
  * One decode step for N requests over a slot-indexed state pool (the vLLM

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libgdn.so")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
 GDN_BF16, GDN_F32 = 0, 1
+GDN_NOALLOC_WORKSPACE_BYTES = 64 << 20  # include/gdn.h
 
 # (name, restype, argtypes) for every entry point declared in include/*.h
 _P = ctypes.c_void_p
@@ -27,6 +28,8 @@ SIGNATURES = {
                            _P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "gdn_chunk_fwd_profiled": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I,
                                     _P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P, _P]),
+    "gdn_chunk_fwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I,
+                                   _P, _P, _P, _P, _P, _I64, _P, _P]),
     "gdn_recurrent_step": (_I, [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "gdn_recurrent_step_kda": (_I, [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "gdn_recurrent_verify": (_I, [_P, _P, _P, _P, _P, _P, _I64, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,

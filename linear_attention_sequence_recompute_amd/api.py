@@ -13,7 +13,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["chunk_fwd", "recurrent_step", "workspace_bytes", "GdnError"]
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "recurrent_step", "workspace_bytes", "GdnError"]
 
 GdnError = _lib.GdnError
 
@@ -76,6 +76,31 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     hipEvent_t handles recorded around the prep and scan kernels
     (gdn_chunk_fwd_profiled).
     """
+    return _chunk_call(q, k, v, g, beta, scale, cu_seqlens, cu_seqlens_dev, h0, output_final_state, ht, state_pool,
+                       state_slots, out_dtype, out, workspace, stream, events, noalloc=False)
+
+
+def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
+                      out: torch.Tensor, scale: Optional[float] = None, cu_seqlens: Optional[Sequence[int]] = None,
+                      cu_seqlens_dev: Optional[torch.Tensor] = None, h0: Optional[torch.Tensor] = None,
+                      ht: Optional[torch.Tensor] = None, state_pool: Optional[torch.Tensor] = None,
+                      state_slots: Optional[torch.Tensor] = None, stream=None):
+    """``chunk_fwd`` through gdn_chunk_fwd_noalloc: no workspace argument and no
+    device allocation, here or in the library (whose workspace is its own device
+    array of GDN_NOALLOC_WORKSPACE_BYTES). ``out`` must be given (its dtype is
+    the output dtype); the final state is stored only into a given ``ht`` (or
+    the pool); packed calls need ``cu_seqlens_dev`` as well as ``cu_seqlens``.
+    Returns (out, ht)."""
+    if out is None:
+        raise ValueError("chunk_fwd_noalloc needs out")
+    if cu_seqlens is not None and cu_seqlens_dev is None:
+        raise ValueError("chunk_fwd_noalloc needs cu_seqlens_dev with cu_seqlens")
+    return _chunk_call(q, k, v, g, beta, scale, cu_seqlens, cu_seqlens_dev, h0, False, ht, state_pool, state_slots,
+                       out.dtype, out, None, stream, None, noalloc=True)
+
+
+def _chunk_call(q, k, v, g, beta, scale, cu_seqlens, cu_seqlens_dev, h0, output_final_state, ht, state_pool,
+                state_slots, out_dtype, out, workspace, stream, events, noalloc):
     H, K = q.shape[-2], q.shape[-1]
     V = v.shape[-1]
     if q.dim() == 4:
@@ -138,14 +163,17 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         if ht is not None:
             _need(ht, "ht", torch.float32)
 
-    need = workspace_bytes(n_seqs, total, H, K, V, in_dt)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(out), n_seqs, total, H, K, V,
             float(K ** -0.5 if scale is None else scale), _dt(in_dt), _dt(out_dtype),
             _ptr(cu_dev), None if cu_host is None else cu_host.data_ptr(),
-            _ptr(h0), _ptr(ht), _ptr(state_pool), pool_slots, _ptr(state_slots),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+            _ptr(h0), _ptr(ht), _ptr(state_pool), pool_slots, _ptr(state_slots))
+    if noalloc:
+        _lib.check(_lib.lib().gdn_chunk_fwd_noalloc(*args, _stream(stream)), "gdn_chunk_fwd_noalloc")
+        return out, ht
+    need = workspace_bytes(n_seqs, total, H, K, V, in_dt)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    args = args + (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if events is None:
         st = _lib.lib().gdn_chunk_fwd(*args)
     else:

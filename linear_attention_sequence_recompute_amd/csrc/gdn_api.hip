@@ -7,6 +7,7 @@
 #include "gdn.h"
 #include "gdn_internal.h"
 #include <cmath>
+#include <mutex>
 
 namespace {
 
@@ -184,6 +185,62 @@ gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const void* v, c
   return chunk_fwd_impl(q, k, v, g, beta, o, n_seqs, total_tokens, H, K, V, scale, in_dtype, out_dtype,
                         cu_seqlens, cu_seqlens_host, h0, ht, state_pool, pool_slots, state_slots, workspace,
                         workspace_bytes, stream, events);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// gdn_chunk_fwd_noalloc: gdn_chunk_fwd with its workspace in a file-scope
+// device array instead of a caller buffer. Each GPU the library runs on holds
+// its own copy of the array (GDN_NOALLOC_WORKSPACE_BYTES) until the process
+// ends. In host code `scratch` names a host-side stand-in, not device memory:
+// the array's device address is asked of the runtime once per device (with
+// that device current) and only that address is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[GDN_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's copy of `scratch` (nullptr on error).
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                 void* o, int n_seqs, int64_t total_tokens, int H, int K, int V, float scale,
+                                 gdn_dtype in_dtype, gdn_dtype out_dtype, const int32_t* cu_seqlens,
+                                 const int32_t* cu_seqlens_host, const float* h0, float* ht, float* state_pool,
+                                 int64_t pool_slots, const int32_t* state_slots, void* stream) {
+  // Validation first, without a workspace: an error other than the missing
+  // workspace (or a call with nothing to do) returns here, before the device is
+  // touched; sizes that need more than the array holds get GDN_EWORKSPACE.
+  const gdn_status st = chunk_fwd_impl(q, k, v, g, beta, o, n_seqs, total_tokens, H, K, V, scale, in_dtype,
+                                       out_dtype, cu_seqlens, cu_seqlens_host, h0, ht, state_pool, pool_slots,
+                                       state_slots, nullptr, 0, stream, nullptr);
+  if (st != GDN_EWORKSPACE) return st;
+  const size_t need = gdn_chunk_fwd_workspace_bytes(n_seqs, total_tokens, H, K, V, in_dtype);
+  if (need == 0 || need > GDN_NOALLOC_WORKSPACE_BYTES) return GDN_EWORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return GDN_EHIP;
+  return chunk_fwd_impl(q, k, v, g, beta, o, n_seqs, total_tokens, H, K, V, scale, in_dtype, out_dtype,
+                        cu_seqlens, cu_seqlens_host, h0, ht, state_pool, pool_slots, state_slots, ws,
+                        GDN_NOALLOC_WORKSPACE_BYTES, stream, nullptr);
 }
 
 }  // extern "C"

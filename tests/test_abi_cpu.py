@@ -31,7 +31,8 @@ def declared_functions(headers=None):
 
 def test_header_declares_the_boundary():
     assert set(declared_functions([HEADER])) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
-                                         "gdn_chunk_fwd_profiled", "gdn_recurrent_step", "gdn_recurrent_step_kda",
+                                         "gdn_chunk_fwd_profiled", "gdn_chunk_fwd_noalloc", "gdn_recurrent_step",
+                                         "gdn_recurrent_step_kda",
                                          "gdn_recurrent_verify", "gdn_fp8_quant", "gdn_decode_prologue",
                                          "gdn_gated_rmsnorm", "gdn_chunk_fwd_kda_workspace_bytes",
                                          "gdn_chunk_fwd_kda", "gdn_chunk_fwd_kda_profiled", "gdn_status_string"}
@@ -305,3 +306,29 @@ def test_probe_validation():
     assert L.gdn_probe_copy(FAKE, FAKE + 8, 1 << 20, None) == EINVAL  # misaligned
     assert L.gdn_probe_copy(FAKE, FAKE, 1000, None) == EINVAL  # not a multiple of 16
     assert L.gdn_probe_read(FAKE, FAKE, 0, None) == EINVAL
+
+
+def _noalloc(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE, n_seqs=1, total=256, H=2, K=64, V=64,
+                scale=1.0, in_dt=BF16, out_dt=BF16, cu=None, cu_host=None, h0=None, ht=None, pool=None,
+                pool_slots=0, slots=None, stream=None)
+    args.update(kw)
+    a = args
+    return _lib.lib().gdn_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["g"], a["beta"], a["o"], a["n_seqs"],
+                                            a["total"], a["H"], a["K"], a["V"], a["scale"], a["in_dt"], a["out_dt"],
+                                            a["cu"], a["cu_host"], a["h0"], a["ht"], a["pool"], a["pool_slots"],
+                                            a["slots"], a["stream"])
+
+
+def test_noalloc_rejects_before_touching_the_device():
+    """Sizes whose workspace exceeds the library's device array are refused with
+    GDN_EWORKSPACE, and invalid arguments with the same status as gdn_chunk_fwd,
+    both before the array's device address is asked for (no GPU here)."""
+    L = _lib.lib()
+    big = dict(n_seqs=4, total=4 * 8192, H=32, K=128, V=128)
+    assert L.gdn_chunk_fwd_workspace_bytes(4, 4 * 8192, 32, 128, 128, BF16) > _lib.GDN_NOALLOC_WORKSPACE_BYTES
+    assert _noalloc(**big) == _lib.GDN_EWORKSPACE
+    assert _noalloc(K=96) == _lib.GDN_EUNSUPPORTED
+    assert _noalloc(H=0) == _lib.GDN_EINVAL
+    assert _noalloc(q=None) == _lib.GDN_EINVAL
+    assert _noalloc(in_dt=7) == _lib.GDN_EUNSUPPORTED
