@@ -501,6 +501,22 @@ struct ScanSmem {
   char (*qt)[kQBytes];               // [2] q tiles (swizzled like K), output waves
   char (*pt)[kPTiles][2 * kPlane];   // [2] P tiles, output waves
   float (*go)[3 * kChunk];           // [2] gate vectors, output waves
+  char* fold[2];                     // map halves being folded (before the first chunk)
+  char* sink;                        // 256 bytes nobody reads (L2 warming copies land there)
+};
+
+// A segment map M_j (K x K) as the A operands of the fold h <- M_j h + c_j:
+// fragment (key block kb, state tile t) of two planes (hi, lo), lane (g, c)
+// holding row krow(t, c) of M_j (the state tile's permuted key order) at
+// columns 32 kb + 8 g .. + 7. Stored [kb][t][plane][64 lanes][16 bytes], so
+// that the key blocks of one half of the contraction are contiguous (they are
+// copied into LDS and folded half a map at a time).
+template <int K>
+struct MapFrag {
+  static constexpr int NKB = K / 32;
+  static constexpr int kBytes = NKB * 2 * NKB * 2 * kPlane;  // = K * K * 4
+  static constexpr int kHalfBytes = kBytes / 2;
+  __host__ __device__ static constexpr int at(int kb, int t) { return (kb * 2 * NKB + t) * 2 * kPlane; }
 };
 
 struct ScanSeq {
@@ -510,16 +526,17 @@ struct ScanSeq {
 // The chain wave. Its state slice starts from rows [lc][key] of s_in (zeros if
 // null; if ident >= 0, the columns ident .. ident + 15 of the identity, which
 // makes the final state those columns of the chunks' linear map), is then
-// carried through n_fold segment maps (h <- M_j h + c_j, M_j rows [key][m] at
-// fm + j fstride, this slice's c_j^T rows [lc][key] at fc + j fstride), and
-// ends in s_out (if not null; rows [lc][key], or with out_t the transpose,
-// s_out[key * K + lc]). PUB: publish the state and v_new for output waves.
+// carried through n_fold segment maps (h <- M_j h + c_j: M_j from the LDS
+// halves sm.fold the producer stages, this slice's c_j^T rows [lc][key] at
+// fc + j fstride), and
+// ends in s_out (if not null; rows [lc][key], or with out_t, for map columns,
+// the split fragments of MapFrag at s_out). PUB: publish the state and v_new
+// for output waves.
 template <int K, int V, typename Tin, int NCH, bool PUB = true>
 __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, const ScanSeq& sq,
                                            const float* s_in, float* s_out, int ident,  // may alias
                                            bool out_t = false, const float* __restrict__ fc = nullptr,
-                                           const float* __restrict__ fm = nullptr, int n_fold = 0,
-                                           int64_t fstride = 0) {
+                                           int n_fold = 0, int64_t fstride = 0) {
   using P = Prec<Tin>;
   using In = typename P::In;
   using Cmp = typename P::Cmp;
@@ -540,42 +557,15 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, cons
         if (key0 + r == ident + lc) hs[t][r] = 1.f;
     }
   }
-  // the maps of the segments before this one, on the MFMA like K h: A operand
-  // lane (g, c) = 8 consecutive m of row key_row(t, c) of M_j (the state tile's
-  // permuted key order), split hi + lo; B operand = the state split. The map
-  // rows come in batches of two tiles of one key block, kD batches in flight
-  // (a ring of register sets); c_j is added last. From a zero initial state the
-  // first map is not needed: the state after segment 0 is c_0. (The
-  // chunk-parallel form runs for bf16 inputs only.)
+  // The maps of the segments before this one, h <- M_j h + c_j, on the MFMA like
+  // K h (A operand: map fragments, split hi + lo by the summary; B operand: the
+  // state split), half a map (half the key blocks) at a time from the LDS
+  // buffers the producer fills, one barrier per half. (The chunk-parallel form
+  // runs for bf16 inputs only.)
   if (std::is_same<Tin, __bf16>::value && n_fold > 0) {
-    constexpr int NB = NKB * NKB;  // batches per map: NKB key blocks x (2 NKB tiles / 2)
-    constexpr int kD = 4;
-    static_assert(NB % kD == 0, "whole rings per map");
-    f32x4 ring[kD][2][2];
-    auto load_batch = [&](int j, int bt, f32x4 (&buf)[2][2]) {
-      const int kb = bt / NKB, t0 = 2 * (bt % NKB);
-      const float* mj = fm + j * fstride + 32 * kb + 8 * lg;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int t = t0 + i;
-        const int krow = 32 * (t >> 1) + 8 * (lc >> 2) + 4 * (t & 1) + (lc & 3);
-        buf[i][0] = *reinterpret_cast<const f32x4*>(mj + krow * K);
-        buf[i][1] = *reinterpret_cast<const f32x4*>(mj + krow * K + 4);
-      }
-    };
-    const int j0 = s_in ? 0 : 1;  // zero start: h after segment 0 = c_0
-    if (j0 == 1) {
-#pragma unroll
-      for (int t = 0; t < 2 * NKB; ++t) {
-        const int key0 = 32 * (t >> 1) + 8 * lg + 4 * (t & 1);
-        hs[t] = *reinterpret_cast<const f32x4*>(fc + lc * K + key0);
-      }
-    }
-    if (j0 < n_fold) {
-#pragma unroll
-      for (int d = 0; d < kD; ++d) load_batch(j0, d, ring[d]);
-    }
-    for (int j = j0; j < n_fold; ++j) {
+    using MF = MapFrag<K>;
+    __syncthreads();  // the first half is staged
+    for (int j = 0; j < n_fold; ++j) {
       const float* cj = fc + j * fstride;
       f32x4 cv[2 * NKB];
 #pragma unroll
@@ -589,20 +579,19 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, cons
 #pragma unroll
       for (int t = 0; t < 2 * NKB; ++t) hs[t] = zero4();
 #pragma unroll
-      for (int bt = 0; bt < NB; ++bt) {
-        f32x4(&buf)[2][2] = ring[bt % kD];
-        const int kb = bt / NKB, t0 = 2 * (bt % NKB);
+      for (int hh = 0; hh < 2; ++hh) {
+        const char* buf = sm.fold[hh];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const Cmp am = P::cmp_tiles(buf[i][0], buf[i][1]);
+        for (int kl = 0; kl < NKB / 2; ++kl) {
+          const int kb = hh * (NKB / 2) + kl;
 #pragma unroll
-          for (int u = 0; u < Terms<Cmp, Cmp>::n; ++u) hs[t0 + i] = term(am, hb[kb], hs[t0 + i], u);
+          for (int t = 0; t < 2 * NKB; ++t) {
+            const Cmp am = P::ld_cmp(buf + MF::at(kl, t), lane);
+#pragma unroll
+            for (int u = 0; u < Terms<Cmp, Cmp>::n; ++u) hs[t] = term(am, hb[kb], hs[t], u);
+          }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (bt + kD < NB)
-          load_batch(j, bt + kD, buf);
-        else if (j + 1 < n_fold)
-          load_batch(j + 1, bt + kD - NB, buf);
+        __syncthreads();  // this half is consumed; the next one is staged
       }
 #pragma unroll
       for (int t = 0; t < 2 * NKB; ++t) hs[t] += cv[t];
@@ -757,16 +746,33 @@ __device__ __forceinline__ void scan_chain(const ScanSmem<K, Tin, NCH>& sm, cons
 #pragma unroll
     for (int i = 0; i < 2 * NKB; ++i) hs[i] = hx[i];
   }
-  if (s_out) {
+  if (s_out && out_t) {
+    // columns ident + lc of M_j as split fragments (MapFrag): element (row, m)
+    // with row = key(t, lg, r) sits in fragment (m >> 5, t), lane
+    // (g' = (m >> 3) & 3, c' = 4 lg + r), element m & 7
+    using MF = MapFrag<K>;
+    const int m = ident + lc;
+    char* base = reinterpret_cast<char*>(s_out);
+    const int lane_off = (((m >> 3) & 3) * 16 + 4 * lg) * 16 + (m & 7) * 2;
+#pragma unroll
+    for (int t = 0; t < 2 * NKB; ++t) {
+      uint32_t h01, l01, h23, l23;
+      split2(hs[t][0], hs[t][1], h01, l01);
+      split2(hs[t][2], hs[t][3], h23, l23);
+      const uint32_t hv[4] = {h01 & 0xffffu, h01 >> 16, h23 & 0xffffu, h23 >> 16};
+      const uint32_t lv[4] = {l01 & 0xffffu, l01 >> 16, l23 & 0xffffu, l23 >> 16};
+      char* f = base + MF::at(m >> 5, t) + lane_off;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<uint16_t*>(f + r * 16) = static_cast<uint16_t>(hv[r]);
+        *reinterpret_cast<uint16_t*>(f + kPlane + r * 16) = static_cast<uint16_t>(lv[r]);
+      }
+    }
+  } else if (s_out) {
 #pragma unroll
     for (int t = 0; t < 2 * NKB; ++t) {
       const int key0 = 32 * (t >> 1) + 8 * lg + 4 * (t & 1);
-      if (out_t) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s_out[(key0 + r) * K + lc] = hs[t][r];
-      } else {
-        *reinterpret_cast<f32x4*>(s_out + lc * K + key0) = hs[t];
-      }
+      *reinterpret_cast<f32x4*>(s_out + lc * K + key0) = hs[t];
     }
   }
 }
@@ -798,11 +804,15 @@ struct ScanIo {
 // landed before the barrier.
 // SUM: for the segment summary kernel (no output waves; the V slices are
 // staged only if has_v, the workgroup's chains being map columns otherwise).
+// Before the first chunk it copies the halves of the n_fold segment maps the
+// chains fold (fragments at maps + j * map_stride bytes) into sm.fold, one
+// half per barrier, a half ahead of the chains.
 template <int K, int V, typename Tin, int NCH, bool SUM = false>
 __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin, NCH> (&sms)[NCH], const ScanSeq& sq,
                                               const Tin* __restrict__ q, const Tin* __restrict__ k,
                                               const Tin* __restrict__ v, int H, const ChunkWs& ws,
-                                              bool has_v = true) {
+                                              bool has_v = true, const char* maps = nullptr, int n_fold = 0,
+                                              int64_t map_stride = 0) {
   using S = ScanSmem<K, Tin, NCH>;
   const S& sm = sms[0];
   const int lane = threadIdx.x & 63;
@@ -894,6 +904,31 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin, NCH> (&sms)
   constexpr int kPrefetchOps = SUM ? 3 : 5;
   const int nc = sq.nc;
   if (nc > 0) stage_chain(0, 0);
+  if (n_fold > 0) {
+    using MF = MapFrag<K>;
+    auto stage_half = [&](int hf) {  // half hf & 1 of map hf >> 1
+      const Buf md(maps + (hf >> 1) * map_stride + (hf & 1) * MF::kHalfBytes, MF::kHalfBytes);
+      char* dst = sm.fold[hf & 1];
+#pragma unroll
+      for (int j = 0; j < MF::kHalfBytes / 1024; ++j) md.to_lds16(dst + 1024 * j, 16 * lane, 1024 * j);
+    };
+    // every line of the maps into L2 first (a 4-byte direct-to-LDS read per
+    // 128-byte line, into a block nobody reads: no registers held), so that
+    // the half copies below, a half ahead of the chains, hit L2
+    for (int j = 0; j < n_fold; ++j) {
+      const Buf md(maps + j * map_stride, MF::kBytes);
+#pragma unroll
+      for (int i = 0; i < MF::kBytes / 128 / 64; ++i) md.to_lds4(sm.sink, 128u * (64 * i + lane), 0);
+    }
+    stage_half(0);
+    wait_vmem();
+    __syncthreads();
+    for (int hf = 0; hf < 2 * n_fold; ++hf) {
+      if (hf + 1 < 2 * n_fold) stage_half(hf + 1);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
   wait_vmem();
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
@@ -916,7 +951,7 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin, NCH> (&sms)
 template <int OW, int K, int V, typename Tin, typename Tout, int NCH>
 __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin, NCH> (&sms)[NCH], const ScanSeq& sq,
                                             const Tin* __restrict__ q, Tout* __restrict__ o, int H, float scale,
-                                            const ChunkWs& ws) {
+                                            const ChunkWs& ws, int n_fold = 0) {
   using S = ScanSmem<K, Tin, NCH>;
   const S& sm0 = sms[0];
   using P = Prec<Tin>;
@@ -1017,6 +1052,8 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin, NCH> (&sms)[N
     }
   };
 
+  // the barriers of the chains' map folds (two halves per map, one more before)
+  for (int hf = 0; n_fold > 0 && hf <= 2 * n_fold; ++hf) __syncthreads();
   const int nc = sq.nc;
   __syncthreads();
   if constexpr (kQ && kP) {
@@ -1094,97 +1131,104 @@ __device__ __forceinline__ ScanSeq seq_of(int pair, int H, int T_eq, int ncs_eq,
   return sq;
 }
 
-// Segments of seg_len chunks (the last one shorter): a sequence of nc chunks
-// has max(1, ceil(nc / seg_len)) of them, segment 0 existing even for an empty
-// sequence so that its initial state passes to its final state. Never more
-// than n_seg (the grid's and the workspace's count), whatever the device copy
-// of the offsets says.
-__device__ __forceinline__ int seg_count(int nc, int seg_len, int n_seg) {
-  return nc <= seg_len ? 1 : min(n_seg, (nc + seg_len - 1) / seg_len);
+// Segments of the chunk-parallel form: segment 0 holds the first L0 chunks of a
+// sequence, each later one L1 chunks, the last one whatever remains. A
+// sequence of nc chunks has max(1, 1 + ceil((nc - L0) / L1)) segments, never
+// more than n_seg (the grid's and the workspace's count, whatever the device
+// copy of the offsets says); segment 0 exists even for an empty sequence, so
+// that its initial state passes to its final state. (Later segments fold more
+// maps before their first chunk; giving each one chunk fewer was measured and
+// changed nothing.)
+struct SegGeom {
+  int n_seg, L0, L1;
+  __device__ int count(int nc) const { return nc <= L0 ? 1 : min(n_seg, 1 + (nc - L0 + L1 - 1) / L1); }
+  // restricts sq to segment `seg` (< count(sq.nc))
+  __device__ void restrict(ScanSeq& sq, int seg) const {
+    const int ns = count(sq.nc);
+    const int c0 = seg == 0 ? 0 : L0 + (seg - 1) * L1;
+    const int c1 = seg == ns - 1 ? sq.nc : min(sq.nc, seg == 0 ? L0 : L0 + seg * L1);
+    sq.start += kChunk * c0;
+    sq.chunk0 += c0;
+    sq.len = max(0, min(sq.len - kChunk * c0, kChunk * (c1 - c0)));
+    sq.nc = (sq.len + kChunk - 1) / kChunk;
+  }
+};
+
+// Arguments every scan-side kernel takes.
+template <typename Tin, typename Tout>
+struct ScanArgs {
+  const Tin* q;
+  const Tin* k;
+  const Tin* v;
+  Tout* o;
+  int H;
+  float scale;
+  int n_seqs, T_eq, ncs_eq, total_tokens, n_chunks;
+  const int32_t* cu;
+  const float* h0;  // h0 and ht may alias (in-place update)
+  float* ht;
+  float* pool;
+  int64_t pool_slots;
+  const int32_t* slots;
+  SegGeom geo;
+  ChunkWs ws;
+};
+
+// The sequence's initial (st_in) and final (st_out) state pages of head sq.h:
+// a pool slot, or h0 / ht (null: zero start / not stored).
+template <int K, int V, typename Tin, typename Tout>
+__device__ __forceinline__ void state_pages(const ScanArgs<Tin, Tout>& a, const ScanSeq& sq, const float*& st_in,
+                                            float*& st_out) {
+  const int64_t page = static_cast<int64_t>(V) * K;
+  st_in = nullptr;
+  st_out = nullptr;
+  if (a.pool) {
+    const int s = a.slots[sq.seq];
+    if (s > 0 && s < a.pool_slots) {
+      st_in = a.pool + (static_cast<int64_t>(s) * a.H + sq.h) * page;
+      st_out = a.pool + (static_cast<int64_t>(s) * a.H + sq.h) * page;
+    }
+  } else {
+    if (a.h0) st_in = a.h0 + (static_cast<int64_t>(sq.seq) * a.H + sq.h) * page;
+    if (a.ht) st_out = a.ht + (static_cast<int64_t>(sq.seq) * a.H + sq.h) * page;
+  }
 }
 
-// Restricts sq to segment `seg` (which must exist).
-__device__ __forceinline__ void restrict_to_segment(ScanSeq& sq, int seg, int seg_len) {
-  const int c0 = seg * seg_len;
-  sq.start += kChunk * c0;
-  sq.chunk0 += c0;
-  sq.len = min(sq.len - kChunk * c0, kChunk * seg_len);
-  if (sq.len < 0) sq.len = 0;
-  sq.nc = (sq.len + kChunk - 1) / kChunk;
-}
-
+// One scan workgroup (pair, slices grp * NCH .., segment seg) over LDS sm:
+// waves 0 .. NCH - 1 run the chains, the producer and two output waves the rest.
 // NCH = 1: waves 0 chain, 1 producer, 2 and 3 output. NCH = 2: waves 0 and 1
 // chains, 2 and 3 output, 4 producer. The waves of a workgroup are spread over
 // the four SIMDs of its CU (waves 0..3 on four different ones, wave 4 beside
 // wave 0), so each chain, which is bound by its own instruction issue, has a
 // SIMD to itself or shares it with the producer, the lightest role.
 //
-// n_seg > 1: the chunk-parallel form. Workgroup (pair, segment j, slices) runs
-// its segment from the sequence's initial state carried through the maps of
-// segments 0 .. j - 1 (summary kernel), and only the last segment stores the
-// final state.
+// Chunk-parallel form (geo.n_seg > 1): segment 0 runs from the sequence's
+// initial state and, when later segments exist, leaves its final state in
+// ws.seg_state (their common starting point); segment j >= 1 starts from that
+// state carried through the maps of segments 1 .. j - 1 (summary part of the
+// first launch); only the sequence's last segment stores its final state.
 template <int K, int V, typename Tin, typename Tout, int NCH>
-__global__ __launch_bounds__(scan_threads<NCH>()) __attribute__((amdgpu_waves_per_eu(NCH, NCH))) void scan_kernel(
-    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o, int H,
-    float scale, int n_seqs, int T_eq, int ncs_eq, int total_tokens, int n_chunks, const int32_t* __restrict__ cu,
-    const float* h0, float* ht, float* pool, int64_t pool_slots,  // h0 and ht may alias (in place)
-    const int32_t* __restrict__ slots, int seg_len, int n_seg, ChunkWs ws) {
-  using S = ScanSmem<K, Tin, NCH>;
-  constexpr int NG = V / 16 / NCH;  // workgroups per (sequence, head, segment)
-  constexpr int NKB = K / 32;
-  static_assert(NCH == 1 || NCH == 2, "one or two chains per workgroup");
-  __shared__ __attribute__((aligned(1024))) char lds_k[2][KTile<K, Tin>::kBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_a[2][6][2 * kPlane];
-  __shared__ __attribute__((aligned(1024))) Tin lds_v[NCH][2][kChunk * 16];
-  __shared__ __attribute__((aligned(16))) float lds_gx[2][3 * kChunk];
-  __shared__ __attribute__((aligned(16))) char lds_h[NCH][2][NKB][2 * kPlane];
-  __shared__ __attribute__((aligned(16))) f32x4 lds_vn[NCH][2][4][64];
-  __shared__ __attribute__((aligned(1024))) char lds_qt[S::kQBufs][S::kQBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_pt[S::kPBufs][S::kPTiles][2 * kPlane];
-  __shared__ __attribute__((aligned(16))) float lds_go[S::kQBufs][3 * kChunk];
-  S sms[NCH];
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) sms[j] = S{lds_k, lds_a, lds_v[j], lds_gx, lds_h[j], lds_vn[j], lds_qt, lds_pt, lds_go};
-
-  // Workgroups of one (sequence, head) share an XCD (blockIdx % 8) and its L2.
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, rest = bid >> 3;
-  const int grp = rest % NG, r2 = rest / NG;
-  const int seg = r2 % n_seg;
-  const int pair = (r2 / n_seg) * 8 + xcd;
-  if (pair >= n_seqs * H) return;
-  ScanSeq sq = seq_of(pair, H, T_eq, ncs_eq, total_tokens, n_chunks, cu, ws);
+__device__ __forceinline__ void scan_wg(const ScanSmem<K, Tin, NCH> (&sms)[NCH], const ScanArgs<Tin, Tout>& a,
+                                        int pair, int grp, int seg) {
+  ScanSeq sq = seq_of(pair, a.H, a.T_eq, a.ncs_eq, a.total_tokens, a.n_chunks, a.cu, a.ws);
   sq.slice = grp * NCH;  // the workgroup's first slice
-
-  // the sequence's initial and final state pages
+  const float* st_in;
+  float* st_out;
+  state_pages<K, V>(a, sq, st_in, st_out);
   const int64_t page = static_cast<int64_t>(V) * K;
-  const float* st_in = nullptr;
-  float* st_out = nullptr;
-  if (pool) {
-    const int s = slots[sq.seq];
-    if (s > 0 && s < pool_slots) {
-      st_in = pool + (static_cast<int64_t>(s) * H + sq.h) * page;
-      st_out = pool + (static_cast<int64_t>(s) * H + sq.h) * page;
-    }
-  } else {
-    if (h0) st_in = h0 + (static_cast<int64_t>(sq.seq) * H + sq.h) * page;
-    if (ht) st_out = ht + (static_cast<int64_t>(sq.seq) * H + sq.h) * page;
-  }
-  // chunk-parallel form: a sequence with several segments starts each from the
-  // copy of its initial state the summary kernel made (its final state may be
-  // written in place meanwhile) carried through the maps of the segments before
   const float* fold = nullptr;
   int n_fold = 0;
-  if (n_seg > 1) {
-    const int ns = seg_count(sq.nc, seg_len, n_seg);
+  if (a.geo.n_seg > 1) {
+    const int ns = a.geo.count(sq.nc);
     if (seg >= ns) return;
-    restrict_to_segment(sq, seg, seg_len);
-    if (ns > 1) {
-      if (st_in) st_in = ws.seg_state + static_cast<int64_t>(pair) * page;  // null: a zero start
-      fold = ws.seg_sum + static_cast<int64_t>(pair) * (n_seg - 1) * (V + K) * K;
-      n_fold = seg;
+    a.geo.restrict(sq, seg);
+    float* mid = a.ws.seg_state + static_cast<int64_t>(pair) * page;
+    if (seg > 0) {
+      st_in = mid;
+      fold = a.ws.seg_sum + static_cast<int64_t>(pair) * (a.geo.n_seg - 2) * (V + K) * K;
+      n_fold = seg - 1;
     }
-    if (seg != ns - 1) st_out = nullptr;
+    if (seg != ns - 1) st_out = seg == 0 ? mid : nullptr;
   }
 
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1196,83 +1240,50 @@ __global__ __launch_bounds__(scan_threads<NCH>()) __attribute__((amdgpu_waves_pe
     const float* s_in = st_in ? st_in + rows : nullptr;
     float* s_out = st_out ? st_out + rows : nullptr;
     const float* fc = fold ? fold + rows : nullptr;
-    const float* fm = fold ? fold + static_cast<int64_t>(V) * K : nullptr;
     const int64_t fstride = static_cast<int64_t>(V + K) * K;
     if (wv == 0)
-      scan_chain<K, V, Tin, NCH>(sms[0], cs, s_in, s_out, -1, false, fc, fm, n_fold, fstride);
+      scan_chain<K, V, Tin, NCH>(sms[0], cs, s_in, s_out, -1, false, fc, n_fold, fstride);
     else
-      scan_chain<K, V, Tin, NCH>(sms[NCH - 1], cs, s_in, s_out, -1, false, fc, fm, n_fold, fstride);
+      scan_chain<K, V, Tin, NCH>(sms[NCH - 1], cs, s_in, s_out, -1, false, fc, n_fold, fstride);
   } else if (wv == kProducer) {
-    scan_producer<K, V, Tin, NCH>(sms, sq, q, k, v, H, ws);
+    const char* maps = fold ? reinterpret_cast<const char*>(fold + static_cast<int64_t>(V) * K) : nullptr;
+    scan_producer<K, V, Tin, NCH>(sms, sq, a.q, a.k, a.v, a.H, a.ws, true, maps, n_fold,
+                                  static_cast<int64_t>(V + K) * K * 4);
   } else {
     if (wv == 2)
-      scan_output<0, K, V, Tin, Tout, NCH>(sms, sq, q, o, H, scale, ws);
+      scan_output<0, K, V, Tin, Tout, NCH>(sms, sq, a.q, a.o, a.H, a.scale, a.ws, n_fold);
     else
-      scan_output<1, K, V, Tin, Tout, NCH>(sms, sq, q, o, H, scale, ws);
+      scan_output<1, K, V, Tin, Tout, NCH>(sms, sq, a.q, a.o, a.H, a.scale, a.ws, n_fold);
   }
 }
 
-// Chunk-parallel form. Over segment j the state map is affine,
-// h_out = M_j h_in + c_j (the chunk step is linear in h). Workgroup (pair,
-// segment j < n_seg - 1, 4 slices) runs the segment's chain with four chain
-// waves (one per SIMD) and a producer: slices of c_j start from zero with the
-// chunks' V, slices of M_j start from identity columns with V = 0. Page
-// (pair, j) of the workspace holds c_j^T as rows [v][key], then M_j as rows
-// [key][m]. The c-slice workgroups of segment 0 also copy the pair's initial
-// state into the workspace, where every segment's scan starts from it.
-template <int K, int V>
-__global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(2, 2))) void summary_kernel(
-    const __bf16* __restrict__ k, const __bf16* __restrict__ v, int H, int n_seqs, int T_eq, int ncs_eq,
-    int total_tokens, int n_chunks, const int32_t* __restrict__ cu, const float* __restrict__ h0,
-    const float* __restrict__ pool, int64_t pool_slots, const int32_t* __restrict__ slots, int seg_len, int n_seg,
-    ChunkWs ws) {
+// A segment's affine state map, h_out = M_j h_in + c_j (the chunk step is
+// linear in h): workgroup (pair, segment j >= 1, 4 slices) runs the segment's
+// chain with four chain waves (one per SIMD) and the producer: slices of c_j
+// start from zero with the chunks' V, slices of M_j start from identity
+// columns with V = 0. Page (pair, j - 1) of the workspace holds c_j^T as rows
+// [v][key] (float32), then M_j as split A-operand fragments (MapFrag). Only
+// maps that a later segment of the sequence folds are formed (not the last
+// segment's).
+template <int K, int V, typename Tout>
+__device__ __forceinline__ void summary_wg(const ScanSmem<K, __bf16, 4> (&sms)[4],
+                                           const ScanArgs<__bf16, Tout>& a, int pair, int grp, int seg) {
   constexpr int NCH = 4;
-  using S = ScanSmem<K, __bf16, NCH>;
-  constexpr int NSL = V / 16, NKS = K / 16;
-  constexpr int NGA = (NSL + NKS) / NCH;
-  static_assert(NSL % NCH == 0 && NKS % NCH == 0, "a workgroup's slices are all of c or all of M");
-  __shared__ __attribute__((aligned(1024))) char lds_k[2][KTile<K, __bf16>::kBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_a[2][6][2 * kPlane];
-  __shared__ __attribute__((aligned(1024))) __bf16 lds_v[NCH][2][kChunk * 16];
-  __shared__ __attribute__((aligned(16))) float lds_gx[2][3 * kChunk];
-  S sms[NCH];
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) sms[j] = S{lds_k, lds_a, lds_v[j], lds_gx, nullptr, nullptr, nullptr, nullptr, nullptr};
-
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, rest = bid >> 3;
-  const int grp = rest % NGA, r2 = rest / NGA;
-  const int seg = r2 % (n_seg - 1);
-  const int pair = (r2 / (n_seg - 1)) * 8 + xcd;
-  if (pair >= n_seqs * H) return;
-  ScanSeq sq = seq_of(pair, H, T_eq, ncs_eq, total_tokens, n_chunks, cu, ws);
-  if (seg >= seg_count(sq.nc, seg_len, n_seg) - 1) return;  // the last segment's map is never used
-  restrict_to_segment(sq, seg, seg_len);
+  constexpr int NSL = V / 16;
+  ScanSeq sq = seq_of(pair, a.H, a.T_eq, a.ncs_eq, a.total_tokens, a.n_chunks, a.cu, a.ws);
+  if (seg >= a.geo.count(sq.nc) - 1) return;  // no later segment folds this map
+  a.geo.restrict(sq, seg);
   sq.slice = grp * NCH;
   const bool is_c = sq.slice < NSL;
-  float* page = ws.seg_sum + (static_cast<int64_t>(pair) * (n_seg - 1) + seg) * (V + K) * K;
+  float* page = a.ws.seg_sum + (static_cast<int64_t>(pair) * (a.geo.n_seg - 2) + seg - 1) * (V + K) * K;
 
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wv < NCH) {
     ScanSeq cs = sq;
     cs.slice = sq.slice + wv;
-    const int lane = threadIdx.x & 63;
-    const int64_t st_page = static_cast<int64_t>(V) * K;
-    if (seg == 0 && is_c) {
-      const float* s0 = nullptr;
-      if (pool) {
-        const int s = slots[sq.seq];
-        if (s > 0 && s < pool_slots) s0 = pool + (static_cast<int64_t>(s) * H + sq.h) * st_page;
-      } else if (h0) {
-        s0 = h0 + (static_cast<int64_t>(sq.seq) * H + sq.h) * st_page;
-      }
-      const int64_t rows = static_cast<int64_t>(cs.slice) * 16 * K;
-      f32x4* dst = reinterpret_cast<f32x4*>(ws.seg_state + static_cast<int64_t>(pair) * st_page + rows);
-      for (int i = lane; i < 16 * K / 4; i += 64) dst[i] = s0 ? reinterpret_cast<const f32x4*>(s0 + rows)[i] : zero4();
-    }
-    // c rows [v][key]; M rows [key][m]: column m0 .. m0 + 15 of M_j stored transposed
+    // c rows [v][key]; columns m0 .. m0 + 15 of M_j into its split fragments
     const int ident = is_c ? -1 : (cs.slice - NSL) * 16;
-    float* s_out = is_c ? page + static_cast<int64_t>(cs.slice) * 16 * K : page + static_cast<int64_t>(V) * K + ident;
+    float* s_out = is_c ? page + static_cast<int64_t>(cs.slice) * 16 * K : page + static_cast<int64_t>(V) * K;
     if (wv == 0)
       scan_chain<K, V, __bf16, NCH, false>(sms[0], cs, nullptr, s_out, ident, !is_c);
     else if (wv == 1)
@@ -1282,31 +1293,120 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     else
       scan_chain<K, V, __bf16, NCH, false>(sms[3], cs, nullptr, s_out, ident, !is_c);
   } else {
-    scan_producer<K, V, __bf16, NCH, true>(sms, sq, nullptr, k, v, H, ws, is_c);
+    scan_producer<K, V, __bf16, NCH, true>(sms, sq, nullptr, a.k, a.v, a.H, a.ws, is_c);
   }
 }
+
+// The LDS of a scan workgroup, as separate __shared__ arrays (so that the
+// compiler can tell the direct-to-LDS copies from the exchange buffers and does
+// not make LDS reads wait for unrelated copies), and its view per chain.
+#define GDN_SCAN_LDS(K, Tin, NCH)                                                         \
+  using S = ScanSmem<K, Tin, NCH>;                                                        \
+  constexpr int NKB = K / 32;                                                             \
+  __shared__ __attribute__((aligned(1024))) char lds_k[2][KTile<K, Tin>::kBytes];         \
+  __shared__ __attribute__((aligned(1024))) char lds_a[2][6][2 * kPlane];                 \
+  __shared__ __attribute__((aligned(1024))) Tin lds_v[NCH][2][kChunk * 16];               \
+  __shared__ __attribute__((aligned(16))) float lds_gx[2][3 * kChunk];                    \
+  __shared__ __attribute__((aligned(16))) char lds_h[NCH][2][NKB][2 * kPlane];            \
+  __shared__ __attribute__((aligned(16))) f32x4 lds_vn[NCH][2][4][64];                    \
+  __shared__ __attribute__((aligned(1024))) char lds_qt[S::kQBufs][S::kQBytes];           \
+  __shared__ __attribute__((aligned(1024))) char lds_pt[S::kPBufs][S::kPTiles][2 * kPlane]; \
+  __shared__ __attribute__((aligned(16))) float lds_go[S::kQBufs][3 * kChunk];            \
+  S sms[NCH];                                                                             \
+  _Pragma("unroll") for (int j = 0; j < NCH; ++j) sms[j] =                                \
+      S{lds_k, lds_a, lds_v[j], lds_gx, lds_h[j], lds_vn[j], lds_qt, lds_pt, lds_go,      \
+        {&lds_qt[0][0], &lds_h[0][0][0][0]}, &lds_pt[S::kPBufs - 1][S::kPTiles - 1][0]};    \
+  static_assert(NCH == 1 || (sizeof(lds_qt) >= MapFrag<K>::kHalfBytes &&                  \
+                             sizeof(lds_h) >= MapFrag<K>::kHalfBytes),                    \
+                "a map half fits each fold buffer");
+
+// The single-pass scan (geo.n_seg == 1) or, in the chunk-parallel form, the
+// segments j >= 1 of every sequence at once (second launch).
+// Workgroups of one (sequence, head) share an XCD (blockIdx % 8) and its L2.
+template <int K, int V, typename Tin, typename Tout, int NCH>
+__global__ __launch_bounds__(scan_threads<NCH>()) __attribute__((amdgpu_waves_per_eu(NCH, NCH))) void scan_kernel(
+    ScanArgs<Tin, Tout> a) {
+  static_assert(NCH == 1 || NCH == 2, "one or two chains per workgroup");
+  GDN_SCAN_LDS(K, Tin, NCH)
+  constexpr int NG = V / 16 / NCH;  // workgroups per (sequence, head, segment)
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, rest = bid >> 3;
+  const int grp = rest % NG, r2 = rest / NG;
+  const int nl = a.geo.n_seg > 1 ? a.geo.n_seg - 1 : 1;  // segments this launch runs
+  const int seg = a.geo.n_seg > 1 ? 1 + r2 % nl : 0;
+  const int pair = (r2 / nl) * 8 + xcd;
+  if (pair >= a.n_seqs * a.H) return;
+  scan_wg<K, V, Tin, Tout, NCH>(sms, a, pair, grp, seg);
+}
+
+// First launch of the chunk-parallel form (bf16 inputs, two slices per scan
+// workgroup): the scan of every sequence's segment 0 (blocks [0, n_scan0))
+// side by side with the maps of segments 1 .. n_seg - 2 (the remaining
+// blocks), which need no state. Both kinds of workgroup have five waves and use
+// one LDS layout (the summary's third and fourth V slices live in the q-tile
+// buffers, which its workgroups do not otherwise use).
+template <int K, int V, typename Tout>
+__global__ __launch_bounds__(scan_threads<2>()) __attribute__((amdgpu_waves_per_eu(2, 2))) void seg0_kernel(
+    ScanArgs<__bf16, Tout> a, int n_scan0) {
+  GDN_SCAN_LDS(K, __bf16, 2)
+  const int bid = blockIdx.x;
+  if (bid < n_scan0) {
+    constexpr int NG = V / 16 / 2;
+    const int xcd = bid & 7, rest = bid >> 3;
+    const int pair = (rest / NG) * 8 + xcd;
+    if (pair >= a.n_seqs * a.H) return;
+    scan_wg<K, V, __bf16, Tout, 2>(sms, a, pair, rest % NG, 0);
+  } else {
+    using S4 = ScanSmem<K, __bf16, 4>;
+    static_assert(sizeof(lds_qt) >= 2 * sizeof(lds_v[0]), "two more V slices fit the q-tile buffers");
+    typedef __bf16 VBuf[kChunk * 16];
+    VBuf* v2 = reinterpret_cast<VBuf*>(&lds_qt[0][0]);
+    S4 s4[4];
+    s4[0] = S4{lds_k, lds_a, lds_v[0], lds_gx, nullptr, nullptr, nullptr, nullptr, nullptr, {nullptr, nullptr}, nullptr};
+    s4[1] = S4{lds_k, lds_a, lds_v[1], lds_gx, nullptr, nullptr, nullptr, nullptr, nullptr, {nullptr, nullptr}, nullptr};
+    s4[2] = S4{lds_k, lds_a, v2, lds_gx, nullptr, nullptr, nullptr, nullptr, nullptr, {nullptr, nullptr}, nullptr};
+    s4[3] = S4{lds_k, lds_a, v2 + 2, lds_gx, nullptr, nullptr, nullptr, nullptr, nullptr, {nullptr, nullptr}, nullptr};
+    constexpr int NGA = (V / 16 + K / 16) / 4;
+    const int b2 = bid - n_scan0;  // n_scan0 is a multiple of 8: b2 keeps the XCD of bid
+    const int xcd = b2 & 7, rest = b2 >> 3;
+    const int grp = rest % NGA, r2 = rest / NGA;
+    const int nm = a.geo.n_seg - 2;  // maps per sequence
+    const int seg = 1 + r2 % nm;
+    const int pair = (r2 / nm) * 8 + xcd;
+    if (pair >= a.n_seqs * a.H) return;
+    summary_wg<K, V, Tout>(s4, a, pair, grp, seg);
+  }
+}
+#undef GDN_SCAN_LDS
 
 // ---------------------------------------------------------------------------
 // Host side: workspace layout and launch sequence.
 // ---------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Segments per sequence for the chunk-parallel form (bf16 inputs): as many as
-// keep two-slice scan workgroups within kSegCUs compute units, at most 8; 1
-// (not used) below 4, where the summaries would cost more than they save.
+// Segments per sequence for the chunk-parallel form (bf16 inputs), 1 where it
+// is not taken. Its first launch runs every sequence's segment 0 (NG two-slice
+// scan workgroups per pair) beside the maps of segments 1 .. n - 2 (NGA
+// summary workgroups per pair and map); the second runs segments 1 .. n - 1
+// (NG per pair and segment). n is the largest count for which both launches
+// fit the compute units at once (at most kMaxSegments), taken if it is at
+// least 3 (with 2, segment 1 would simply wait for segment 0).
 constexpr int kSegCUs = 256;
-static int segment_cap(int64_t pairs, int V, bool in_f32) {
+static int segment_cap(int64_t pairs, int K, int V, bool in_f32, int n_cus = kSegCUs) {
   if (in_f32 || pairs <= 0) return 1;
-  const int64_t wg = pairs * (V / 16) / 2;
-  const int64_t s = std::min<int64_t>(kMaxSegments, kSegCUs / wg);
-  return s >= 4 ? static_cast<int>(s) : 1;
+  const int64_t p8 = (pairs + 7) / 8 * 8;
+  const int64_t ng = V / 16 / 2, nga = (V / 16 + K / 16) / 4;
+  int64_t n = std::min<int64_t>(kMaxSegments, n_cus / (p8 * ng) + 1);
+  if (n_cus / p8 < ng) return 1;
+  n = std::min<int64_t>(n, 2 + (n_cus / p8 - ng) / nga);
+  return n >= 3 ? static_cast<int>(n) : 1;
 }
 
 WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, bool in_f32) {
   const size_t nch = static_cast<size_t>(max_chunks) * H;
   const int64_t pairs = static_cast<int64_t>(n_seqs) * H;
   WsLayout l{};
-  l.max_segments = segment_cap(pairs, V, in_f32);
+  l.max_segments = segment_cap(pairs, K, V, in_f32);
   size_t off = 0;
   l.af = off;
   off = align256(off + nch * kTileSetBytes);
@@ -1320,7 +1420,7 @@ WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, b
   off = align256(off + static_cast<size_t>(n_seqs + 1) * 4);
   const size_t sm = static_cast<size_t>(l.max_segments);
   l.seg_sum = off;
-  if (sm > 1) off = align256(off + static_cast<size_t>(pairs) * (sm - 1) * (V + K) * K * 4);
+  if (sm > 1) off = align256(off + static_cast<size_t>(pairs) * (sm - 2) * (V + K) * K * 4);
   l.seg_state = off;
   if (sm > 1) off = align256(off + static_cast<size_t>(pairs) * V * K * 4);
   l.total = off;
@@ -1360,47 +1460,49 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
   if (a.events[1]) (void)hipEventRecord(a.events[1], a.stream);
   const int64_t pairs = static_cast<int64_t>(a.n_seqs) * a.H;
   const unsigned pair8 = static_cast<unsigned>((pairs + 7) / 8);
+  ScanArgs<Tin, Tout> sa{static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
+                         static_cast<Tout*>(a.o), a.H, a.scale, a.n_seqs, a.T_eq, ncs_eq,
+                         static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0, a.ht,
+                         a.pool, a.pool_slots, a.slots, SegGeom{1, 0, 0}, a.ws};
   // Chunk-parallel form where the scan would leave most compute units idle:
-  // n_seg segments per sequence, their maps (summary), then every segment's
-  // scan at once, each chain first carrying the initial state through the maps
-  // of the segments before its own.
-  int n_seg = 1, seg_len = 0;
-  const int cap = segment_cap(pairs, V, !std::is_same<Tin, __bf16>::value);
-  if (cap > 1) {
-    const int64_t wg = pairs * NSL / 2;
-    const int s = static_cast<int>(std::min<int64_t>({static_cast<int64_t>(cap), a.n_cus / wg, a.max_nc / 4}));
-    if (s >= 4) {
-      seg_len = (a.max_nc + s - 1) / s;
-      n_seg = (a.max_nc + seg_len - 1) / seg_len;
-    }
+  // n segments per sequence, the first of L0 chunks, the others of L1. The
+  // first launch scans every segment 0 and forms the maps of segments 1 ..
+  // n - 2; the second scans segments 1 .. n - 1 at once, each from segment 0's
+  // final state carried through the maps of the segments before its own.
+  const int cap = segment_cap(pairs, K, V, !std::is_same<Tin, __bf16>::value);  // as the workspace was sized
+  if (cap > 1 && a.max_nc >= 4 * 3) {
+    const int n = std::min(cap, a.max_nc / 4);
+    const int L1 = (a.max_nc + n - 1) / n;
+    const int L0 = a.max_nc - (n - 1) * L1;
+    if (n >= 3 && L0 >= 1) sa.geo = SegGeom{n, L0, L1};
   }
   if constexpr (std::is_same<Tin, __bf16>::value) {
-    if (n_seg > 1) {
+    if (sa.geo.n_seg > 1) {
       constexpr int NGA = (NSL + K / 16) / 4;
-      hipLaunchKernelGGL((summary_kernel<K, V>), dim3(8 * NGA * (n_seg - 1) * pair8), dim3(320), 0, a.stream,
-                         static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v), a.H, a.n_seqs, a.T_eq,
-                         ncs_eq, static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0,
-                         a.pool, a.pool_slots, a.slots, seg_len, n_seg, a.ws);
+      const unsigned n_scan0 = 8 * (NSL / 2) * pair8;
+      const unsigned n_sum = 8 * NGA * (sa.geo.n_seg - 2) * pair8;
+      hipLaunchKernelGGL((seg0_kernel<K, V, Tout>), dim3(n_scan0 + n_sum), dim3(scan_threads<2>()), 0, a.stream, sa,
+                         static_cast<int>(n_scan0));
+      hipLaunchKernelGGL((scan_kernel<K, V, Tin, Tout, 2>), dim3(8 * (NSL / 2) * (sa.geo.n_seg - 1) * pair8),
+                         dim3(scan_threads<2>()), 0, a.stream, sa);
+      const hipError_t err = hipGetLastError();
+      if (a.events[2]) (void)hipEventRecord(a.events[2], a.stream);
+      return err;
     }
   }
   // Two chains per workgroup (sharing K, A' and the gates, on two SIMDs of a
-  // CU) once one-chain workgroups would outnumber the compute units, and in
-  // the chunk-parallel form; bf16 inputs only (float32 operands would not
-  // leave room in LDS for the rest).
-  auto launch = [&](auto kern, int nch) {
-    const unsigned blocks = 8 * (NSL / nch) * n_seg * pair8;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * (nch + 3)), 0, a.stream, static_cast<const Tin*>(a.q),
-                       static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v), static_cast<Tout*>(a.o), a.H,
-                       a.scale, a.n_seqs, a.T_eq, ncs_eq, static_cast<int>(a.total_tokens),
-                       static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0, a.ht, a.pool, a.pool_slots, a.slots,
-                       seg_len, n_seg, a.ws);
-  };
+  // CU) once one-chain workgroups would outnumber the compute units; bf16
+  // inputs only (float32 operands would not leave room in LDS for the rest).
   bool two = false;
   if constexpr (std::is_same<Tin, __bf16>::value) {
-    two = pairs * NSL > a.n_cus || n_seg > 1;
-    if (two) launch(scan_kernel<K, V, Tin, Tout, 2>, 2);
+    two = pairs * NSL > a.n_cus;
+    if (two)
+      hipLaunchKernelGGL((scan_kernel<K, V, Tin, Tout, 2>), dim3(8 * (NSL / 2) * pair8), dim3(scan_threads<2>()), 0,
+                         a.stream, sa);
   }
-  if (!two) launch(scan_kernel<K, V, Tin, Tout, 1>, 1);
+  if (!two)
+    hipLaunchKernelGGL((scan_kernel<K, V, Tin, Tout, 1>), dim3(8 * NSL * pair8), dim3(scan_threads<1>()), 0, a.stream,
+                       sa);
   const hipError_t err = hipGetLastError();
   if (a.events[2]) (void)hipEventRecord(a.events[2], a.stream);
   return err;

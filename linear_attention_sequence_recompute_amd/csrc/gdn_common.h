@@ -306,6 +306,12 @@ struct Buf {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(static_cast<uintptr_t>(l)), 16,
                                              voff, soff, 0, 0);
   }
+  // 4 bytes per lane straight into LDS (lane i's at lds_block + 4 i).
+  __device__ __forceinline__ void to_lds4(void* lds_block, uint32_t voff, uint32_t soff) const {
+    const uint32_t l = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_block));  // LDS offset
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(static_cast<uintptr_t>(l)), 4,
+                                             voff, soff, 0, 0);
+  }
   // 4 bytes per lane (0 for lanes with voff >= the descriptor size).
   __device__ __forceinline__ uint32_t load4(uint32_t voff) const {
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
