@@ -553,7 +553,7 @@ def bench_copy(torch, steps, nbytes=1 << 30):
 def bench_peaks(torch, api, hev, reps=5, nbytes=2 << 30):
     """The peaks this GPU reaches, from the library's measurement probes: a bf16
     MFMA loop over every SIMD (2 waves each, 8 independent accumulators per
-    wave), a streaming copy of 2 GiB and a streaming read of 2 GiB."""
+    wave), a streaming copy, read and write of 2 GiB each."""
     L = api._lib.lib()
     stream = torch.cuda.current_stream().cuda_stream
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -583,12 +583,13 @@ def bench_peaks(torch, api, hev, reps=5, nbytes=2 << 30):
     t_mfma = timed(lambda: ok(L.gdn_probe_mfma_bf16(sink.data_ptr(), waves, iters, stream)))
     t_copy = timed(lambda: ok(L.gdn_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream)))
     t_read = timed(lambda: ok(L.gdn_probe_read(src.data_ptr(), sink.data_ptr(), nbytes, stream)))
+    t_write = timed(lambda: ok(L.gdn_probe_write(dst.data_ptr(), nbytes, stream)))
     del src, dst
     flops = waves * iters * 8 * 16384
     return {"mfma_bf16_tflops": flops / t_mfma / 1e12, "copy_gbs": 2 * nbytes / t_copy / 1e9,
-            "read_gbs": nbytes / t_read / 1e9,
-            "probes": f"bf16 MFMA loop: {waves} waves x {iters} x 8 v_mfma_f32_16x16x32_bf16; copy and read of "
-                      f"{nbytes >> 30} GiB (copy counts bytes read + written); median of {reps}"}
+            "read_gbs": nbytes / t_read / 1e9, "write_gbs": nbytes / t_write / 1e9,
+            "probes": f"bf16 MFMA loop: {waves} waves x {iters} x 8 v_mfma_f32_16x16x32_bf16; copy, read and write "
+                      f"of {nbytes >> 30} GiB (copy counts bytes read + written); median of {reps}"}
 
 
 def cpu_model():
@@ -719,10 +720,18 @@ def main():
     dec_b = decode_bytes(res_d["n_active"])
     dec_gbs = dec_b / dec_s / 1e9
 
-    def hbm_roofline(achieved_gbs, kernel_traffic, nbytes):
-        return {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved_gbs / PEAK_HBM_GBS, "frac_of_measured_copy": achieved_gbs / peaks["copy_gbs"],
-                "traffic": kernel_traffic, "bytes_per_launch": nbytes}
+    def hbm_roofline(achieved_gbs, kernel_traffic, nbytes, write_bytes=None):
+        """HBM roofline entry; with the bytes written known, also the ceiling the
+        measured streaming read and write rates give for that read/write mix
+        (read bytes at the read rate, then written bytes at the write rate)."""
+        r = {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": achieved_gbs / PEAK_HBM_GBS, "frac_of_measured_copy": achieved_gbs / peaks["copy_gbs"],
+             "traffic": kernel_traffic, "bytes_per_launch": nbytes}
+        if write_bytes is not None:
+            rd = nbytes - write_bytes
+            mix = nbytes / (rd / peaks["read_gbs"] + write_bytes / peaks["write_gbs"])
+            r.update(write_bytes=write_bytes, measured_mix_ceiling_gbs=mix, frac_of_measured_mix=achieved_gbs / mix)
+        return r
 
     out = {
         "metric": "GDN fwd tokens/s + % bf16 MFMA peak (H16,K=V=128,T4096); decode GB/s % peak",
@@ -751,7 +760,8 @@ def main():
                                "pool [512, 32, 128, 128] fp32, bf16 q/k/v/o",
                    "value": dec_gbs, "unit": "GB/s", "avg_launch_us": dec_s * 1e6,
                    "timing_us": {k: v * 1e3 for k, v in res_d["kernel_ms"].items()},
-                   "roofline": hbm_roofline(dec_gbs, traffic_for("recurrent_step_kernel"), dec_b)},
+                   "roofline": hbm_roofline(dec_gbs, traffic_for("recurrent_step_kernel"), dec_b,
+                                            res_d["n_active"] * DH * (DV * DK * 4 + DV * 2))},
     }
     res_k = res["kda"]
     kda_s = res_k["kernel_ms"]["mean"] / 1e3
@@ -769,7 +779,8 @@ def main():
                     "fp32 (source read once, a state written per token), bf16 q/k/v/o",
         "value": ver_b / ver_s / 1e9, "unit": "GB/s", "avg_launch_us": ver_s * 1e6,
         "tokens_per_s": VN * VT / ver_s,
-        "roofline": hbm_roofline(ver_b / ver_s / 1e9, traffic_for("recurrent_verify_kernel"), ver_b)}
+        "roofline": hbm_roofline(ver_b / ver_s / 1e9, traffic_for("recurrent_verify_kernel"), ver_b,
+                                 res_v["n_active"] * DH * VT * (DV * DK * 4 + DV * 2))}
     q_s = res["fp8"]["kernel_ms"]["mean"] / 1e3
     q_b = QR * QC * (4 + 1) + QR * (QC // QG) * 4
     out["fp8_quant"] = {

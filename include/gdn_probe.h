@@ -16,6 +16,8 @@
  *                       (sink holds waves * 64 floats).
  *  gdn_probe_copy       HBM streaming copy of `bytes` (a multiple of 16) from
  *                       src to dst: bytes read + bytes written per call.
+ *  gdn_probe_write      HBM streaming write of `bytes` (a multiple of 16) to
+ *                       dst (a constant pattern; nothing is read).
  *  gdn_probe_read       HBM streaming read of `bytes` (a multiple of 16) from
  *                       src; each workgroup writes one float of its partial sum
  *                       to sink[workgroup] (sink holds at least 8192 floats).
@@ -39,6 +41,7 @@ extern "C" {
 
 gdn_status gdn_probe_mfma_bf16(float* sink, int waves, int iters, void* stream);
 gdn_status gdn_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+gdn_status gdn_probe_write(void* dst, int64_t bytes, void* stream);
 gdn_status gdn_probe_read(const void* src, float* sink, int64_t bytes, void* stream);
 
 #ifdef __cplusplus

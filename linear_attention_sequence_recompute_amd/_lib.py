@@ -46,6 +46,7 @@ SIGNATURES = {
     # measurement probes (include/gdn_probe.h)
     "gdn_probe_mfma_bf16": (_I, [_P, _I, _I, _P]),
     "gdn_probe_copy": (_I, [_P, _P, _I64, _P]),
+    "gdn_probe_write": (_I, [_P, _I64, _P]),
     "gdn_probe_read": (_I, [_P, _P, _I64, _P]),
 }
 

@@ -119,6 +119,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
 // step's; the state rows stay in registers across the tokens, each token's inputs
 // loaded while the previous token is applied.
 constexpr int kMaxVerifyTokens = 8;
+constexpr int kVerifyRows = 16;  // state rows per workgroup
 
 template <int K, int V, typename Tin, typename Tout>
 __global__ __launch_bounds__(256) void recurrent_verify_kernel(
@@ -128,20 +129,20 @@ __global__ __launch_bounds__(256) void recurrent_verify_kernel(
     Tout* __restrict__ o, int T, int H, float scale) {
   constexpr int LPR = K / 4;
   constexpr int RPP = 256 / LPR;
-  constexpr int PASSES = kDecodeRows / RPP;
-  constexpr int NP = V / kDecodeRows;
+  constexpr int PASSES = kVerifyRows / RPP;
+  constexpr int NP = V / kVerifyRows;
   const int per_req = H * NP;
   const int b = blockIdx.x / per_req, h = (blockIdx.x % per_req) / NP, part = blockIdx.x % NP;
   const int tid = threadIdx.x;
   const int col = (tid % LPR) * 4;
   const int rsub = tid / LPR;
-  const int row0 = part * kDecodeRows;
+  const int row0 = part * kVerifyRows;
   const int64_t page = static_cast<int64_t>(V) * K;
   const int32_t* srow = slots + static_cast<int64_t>(b) * cols;
   const int acc = accepted[b];
   const int src = acc >= 1 && acc <= cols ? srow[acc - 1] : 0;
   if (src <= 0 || src >= pool_slots) {  // padding: zero outputs, nothing written
-    if (tid < kDecodeRows)
+    if (tid < kVerifyRows)
       for (int t = 0; t < T; ++t) store_out(o + ((static_cast<int64_t>(b) * T + t) * H + h) * V + row0 + tid, 0.f);
     return;
   }
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(256) void recurrent_verify_kernel(
 
 template <int K, int V, typename Tin, typename Tout>
 static hipError_t launch_verify_t(const VerifyArgs& a) {
-  const dim3 grid(static_cast<unsigned>(a.N) * a.H * (V / kDecodeRows));  // request slowest
+  const dim3 grid(static_cast<unsigned>(a.N) * a.H * (V / kVerifyRows));  // request slowest
   hipLaunchKernelGGL((recurrent_verify_kernel<K, V, Tin, Tout>), grid, dim3(256), 0, a.stream,
                      static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
                      static_cast<const Tin*>(a.v), a.g, a.beta, a.pool, a.pool_slots, a.slots, a.cols,

@@ -1,5 +1,5 @@
 // Measurement probes: kernels that each drive one hardware limit (the bf16
-// matrix-core rate, HBM streaming copy, HBM streaming read), timed by the
+// matrix-core rate, HBM streaming copy, write and read), timed by the
 // caller to obtain the peaks this GPU reaches. Contracts in include/gdn_probe.h.
 #include <stdint.h>
 
@@ -53,6 +53,14 @@ __global__ __launch_bounds__(256) void copy_probe_kernel(const f32x4* __restrict
   for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Grid-stride streaming store of a constant (no reads).
+__global__ __launch_bounds__(256) void write_probe_kernel(f32x4* __restrict__ dst, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  const f32x4 x = f32x4{1.f, 2.f, 3.f, 4.f};
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride)
+    __builtin_nontemporal_store(x, dst + i);
+}
+
 __global__ __launch_bounds__(256) void read_probe_kernel(const f32x4* __restrict__ src, float* __restrict__ sink,
                                                          int64_t n) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
@@ -92,6 +100,13 @@ gdn_status gdn_probe_copy(const void* src, void* dst, int64_t bytes, void* strea
   if (!src || !dst || !aligned16(src) || !aligned16(dst) || bytes <= 0 || bytes % 16) return GDN_EINVAL;
   hipLaunchKernelGGL(copy_probe_kernel, dim3(kStreamBlocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const gdn::f32x4*>(src), static_cast<gdn::f32x4*>(dst), bytes / 16);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_probe_write(void* dst, int64_t bytes, void* stream) {
+  if (!dst || !aligned16(dst) || bytes <= 0 || bytes % 16) return GDN_EINVAL;
+  hipLaunchKernelGGL(write_probe_kernel, dim3(kStreamBlocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<gdn::f32x4*>(dst), bytes / 16);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 

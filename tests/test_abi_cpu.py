@@ -306,6 +306,8 @@ def test_probe_validation():
     assert L.gdn_probe_copy(FAKE, FAKE + 8, 1 << 20, None) == EINVAL  # misaligned
     assert L.gdn_probe_copy(FAKE, FAKE, 1000, None) == EINVAL  # not a multiple of 16
     assert L.gdn_probe_read(FAKE, FAKE, 0, None) == EINVAL
+    assert L.gdn_probe_write(None, 1 << 20, None) == EINVAL
+    assert L.gdn_probe_write(FAKE, 24, None) == EINVAL
 
 
 def _noalloc(**kw):
