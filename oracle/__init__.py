@@ -21,6 +21,9 @@ Functions (all float64 numpy):
 * ``decode_prologue`` / ``gated_rmsnorm`` - the decode layer's front (conv1d
   over a conv-state pool, SiLU, q/k L2 norm, sigmoid beta) and back (gated
   RMSNorm) operations (``oracle/layer.py``).
+* ``kda_gate``       - the per-key-channel decays of the KDA decode layer from its
+  low-rank gate projection (``oracle/gate.py``), in each of the page's float32
+  reduction orders, exactly.
 * ``fp8_quant``      - group quantisation to FP8 E4M3 (``oracle/fp8.py``), with
   ``e4m3_encode`` / ``e4m3_decode``.
 
@@ -42,3 +45,4 @@ from .gdn import (  # noqa: F401
 )
 from .fp8 import e4m3_decode, e4m3_encode, fp8_quant  # noqa: F401
 from .layer import conv_silu_step, decode_prologue, gated_rmsnorm  # noqa: F401
+from .gate import kda_gate  # noqa: F401
