@@ -245,6 +245,39 @@ gdn_status gdn_recurrent_verify(const void* q, const void* k, const void* v, con
                                 gdn_dtype out_dtype, void* stream);
 
 /*
+ * Per-key-channel decays of the KDA decode layer from its low-rank gate
+ * projection (the vLLM KdaSplit page, method gate_warp and its multicast): for
+ * token t, head h and key channel f,
+ *
+ *   raw  = sum over c < 128 of f_a[t, c] * f_b[h K + f, c]     (float32)
+ *   g    = lower_bound * sigmoid(exp(a_log[h]) * (bf16(raw) + dt_bias[h K + f]))
+ *
+ * with bf16() round to nearest even; the decay is exp(g), so g is the log-decay
+ * gdn_recurrent_step_kda and gdn_chunk_fwd_kda take.
+ *
+ *  f_a       bf16 [N, 128]   the gate's activations (rank 128), 16-byte aligned
+ *  f_b       bf16 [H * K, 128] the projection weight, 16-byte aligned
+ *  a_log     float32 [H];  dt_bias float32 [H * K]
+ *  lower_bound  finite float (the log-decay at gate 1; <= 0 for decays <= 1)
+ *  mode      float32 reduction order of raw, as the page names them:
+ *            0 = one chain over the 128 columns; 1 = four chains of 32 columns,
+ *            summed 0 + (((c0 + c1) + c2) + c3); 2 = sixteen partials of 8
+ *            columns summed in a butterfly (p[i] += p[i + 2^s], s = 3, 2, 1, 0).
+ *            Each is a fixed sequence of IEEE float32 fused multiply-adds (in
+ *            column order) and adds, so bf16(raw) is reproducible bit for bit.
+ *  g         float32 [N, H, K] (output)
+ *  raw_g     bf16 [N, H, K] (output: bf16(raw)), or NULL
+ *
+ * Returns GDN_EUNSUPPORTED for K outside {64, 128}; GDN_EINVAL for a mode
+ * outside {0, 1, 2}, N < 0, H outside [1, 65535], a non-finite lower_bound, a
+ * NULL or misaligned pointer (raw_g may be NULL); GDN_OK without launching for
+ * N == 0; GDN_EHIP if the launch fails.
+ */
+gdn_status gdn_kda_gate(const void* f_a, const void* f_b, const float* a_log, const float* dt_bias,
+                        float lower_bound, int mode, float* g, void* raw_g, int N, int H, int K,
+                        void* stream);
+
+/*
  * FP8 group quantisation (the WarpDrive page, kernel 1, fp8_quant).
  *
  *  x       float32 [rows, cols], row-major, 16-byte aligned; finite values

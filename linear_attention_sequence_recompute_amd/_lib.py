@@ -34,6 +34,7 @@ SIGNATURES = {
     "gdn_recurrent_step_kda": (_I, [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "gdn_recurrent_verify": (_I, [_P, _P, _P, _P, _P, _P, _I64, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
                                   _P]),
+    "gdn_kda_gate": (_I, [_P, _P, _P, _P, _F, _I, _P, _P, _I, _I, _I, _P]),
     "gdn_fp8_quant": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
     "gdn_decode_prologue": (_I, [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "gdn_gated_rmsnorm": (_I, [_P, _P, _P, _F, _P, _I, _I, _I, _I, _P]),

@@ -246,6 +246,36 @@ def recurrent_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     return out
 
 
+def kda_gate(f_a: torch.Tensor, f_b: torch.Tensor, a_log: torch.Tensor, dt_bias: torch.Tensor,
+             lower_bound: float, H: int, *, mode: int = 0, with_raw: bool = False, out: Optional[torch.Tensor] = None,
+             stream=None):
+    """Per-key-channel log-decays of the KDA decode layer (gdn_kda_gate): f_a bf16
+    [N, 128]; f_b bf16 [H * K, 128]; a_log float32 [H]; dt_bias float32 [H * K].
+    Returns g float32 [N, H, K] (and the bf16 projection [N, H, K] with
+    ``with_raw``)."""
+    N = f_a.shape[0]
+    if f_a.dim() != 2 or f_a.shape[1] != 128:
+        raise ValueError("f_a must be [N, 128]")
+    if f_b.dim() != 2 or f_b.shape[1] != 128 or f_b.shape[0] % H:
+        raise ValueError("f_b must be [H * K, 128]")
+    K = f_b.shape[0] // H
+    _shape(a_log, (H,), "a_log")
+    _shape(dt_bias, (H * K,), "dt_bias")
+    _shape(out, (N, H, K), "out")
+    _need(f_a, "f_a", torch.bfloat16)
+    _need(f_b, "f_b", torch.bfloat16)
+    _need(a_log, "a_log", torch.float32)
+    _need(dt_bias, "dt_bias", torch.float32)
+    if out is None:
+        out = torch.empty((N, H, K), dtype=torch.float32, device=f_a.device)
+    _need(out, "out", torch.float32)
+    raw = torch.empty((N, H, K), dtype=torch.bfloat16, device=f_a.device) if with_raw else None
+    st = _lib.lib().gdn_kda_gate(_ptr(f_a), _ptr(f_b), _ptr(a_log), _ptr(dt_bias), float(lower_bound), int(mode),
+                                 _ptr(out), _ptr(raw), N, H, K, _stream(stream))
+    _lib.check(st, "gdn_kda_gate")
+    return (out, raw) if with_raw else out
+
+
 def fp8_quant(x: torch.Tensor, group: int = 128, *, codes: Optional[torch.Tensor] = None,
               scales: Optional[torch.Tensor] = None, stream=None):
     """FP8 group quantisation (gdn_fp8_quant): x float32 [..., C] with C a multiple

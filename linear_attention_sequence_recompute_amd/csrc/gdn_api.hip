@@ -346,6 +346,32 @@ gdn_status gdn_recurrent_verify(const void* q, const void* k, const void* v, con
 }
 
 
+gdn_status gdn_kda_gate(const void* f_a, const void* f_b, const float* a_log, const float* dt_bias,
+                        float lower_bound, int mode, float* g, void* raw_g, int N, int H, int K, void* stream) {
+  if (K != 64 && K != 128) return GDN_EUNSUPPORTED;
+  if (mode < 0 || mode > 2 || N < 0 || H <= 0 || H > 65535 || !std::isfinite(lower_bound)) return GDN_EINVAL;
+  if (static_cast<int64_t>(N) * H * K > INT64_MAX / 4) return GDN_EINVAL;
+  if (N == 0) return GDN_OK;
+  if (!f_a || !f_b || !a_log || !dt_bias || !g) return GDN_EINVAL;
+  if (!aligned(f_a, 16) || !aligned(f_b, 16) || !aligned(a_log, 4) || !aligned(dt_bias, 4) || !aligned(g, 4) ||
+      (raw_g && !aligned(raw_g, 2)))
+    return GDN_EINVAL;
+  gdn::GateArgs a{};
+  a.f_a = f_a;
+  a.f_b = f_b;
+  a.a_log = a_log;
+  a.dt_bias = dt_bias;
+  a.lower_bound = lower_bound;
+  a.mode = mode;
+  a.g = g;
+  a.raw_out = raw_g;
+  a.N = N;
+  a.H = H;
+  a.K = K;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_kda_gate(a));
+}
+
 gdn_status gdn_fp8_quant(const float* x, void* codes, float* scales, int64_t rows, int64_t cols, int group,
                          void* stream) {
   if (group != 64 && group != 128) return GDN_EUNSUPPORTED;

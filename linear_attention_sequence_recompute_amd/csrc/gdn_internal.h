@@ -79,6 +79,19 @@ struct KdaChunkArgs {
 };
 int64_t kda_workspace_floats(int B, int64_t T, int H, int K);
 
+struct GateArgs {
+  const void* f_a;      // [N, 128] bf16
+  const void* f_b;      // [H * K, 128] bf16
+  const float* a_log;   // [H]
+  const float* dt_bias; // [H * K]
+  float lower_bound;
+  int mode;             // reduction order of the projection: 0, 1 or 2
+  float* g;             // [N, H, K] log-decays
+  void* raw_out;        // [N, H, K] bf16 projection, or null
+  int N, H, K;
+  hipStream_t stream;
+};
+
 struct Fp8Args {
   const float* x;     // [n_groups * group] float32
   void* codes;        // [n_groups * group] uint8 (E4M3)
@@ -99,10 +112,11 @@ struct Fp8Args {
 //        the log-gate; rows past the chunk end repeat g_last), e^g, e^{g_last - g}
 //   info [chunk] int4 {seq, first token, rows, 0} and seq_chunk0 [n_seqs + 1]:
 //        the chunk schedule of a packed (varlen) call
-//   seg_sum [pair][n_seg - 1][V + K][K] f32   chunk-parallel form: per segment,
-//        the affine map of the state h -> M h + c: c^T rows [v][key], then M
-//        rows [key][m]
-//   seg_state [pair][V][K] f32                 a copy of the pair's initial state
+//   seg_sum [pair][n_seg - 2][(V + K) K] f32  chunk-parallel form: for segments
+//        1 .. n_seg - 2, the affine map of the state h -> M h + c: c^T rows
+//        [v][key] (float32), then M as split bf16 A-operand fragments (MapFrag)
+//   seg_state [pair][V][K] f32                 segment 0's final state, where
+//        every later segment of the pair starts
 struct ChunkWs {
   uint8_t* af;
   uint8_t* pf;
@@ -152,5 +166,6 @@ hipError_t launch_decode_prologue(const PrologueArgs& a);
 hipError_t launch_gated_rmsnorm(const RmsNormArgs& a);
 hipError_t launch_chunk_fwd_kda(const KdaChunkArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
+hipError_t launch_kda_gate(const GateArgs& a);
 
 }  // namespace gdn

@@ -41,6 +41,8 @@ __all__ = [
     "decode_inputs",
     "LayerInputs",
     "layer_inputs",
+    "GateInputs",
+    "gate_inputs",
 ]
 
 
@@ -310,3 +312,24 @@ def layer_inputs(N: int, H: int, D: int, pool_slots: int, seed: int = 0, n_paddi
     slots[mask] = rng.choice(np.arange(1, pool_slots), n_active, replace=False)
     slots[pad_pos] = rng.choice(np.array([0, -1]), len(pad_pos))
     return LayerInputs(x, conv_w, conv_bias, conv_state, slots, beta_raw, gate, norm_w, H, D)
+
+
+@dataclass
+class GateInputs:
+    f_a: np.ndarray      # [N, 128] bf16 values
+    f_b: np.ndarray      # [H * K, 128] bf16 values
+    a_log: np.ndarray    # [H] float32
+    dt_bias: np.ndarray  # [H * K] float32
+    lower_bound: float
+
+
+def gate_inputs(N: int, H: int, K: int, seed: int = 0, lower_bound: float = -5.0) -> GateInputs:
+    """Inputs of the KDA gate stage: activations f_a ~ N(0, 1) and projection
+    weights F_B ~ N(0, 1 / 128) (unit-variance projections), both rounded to bf16;
+    a_log ~ U(-2, 1/2) and dt_bias ~ N(0, 1) in float32."""
+    rng = np.random.default_rng(seed)
+    f_a = round_to_bf16(rng.standard_normal((N, 128)))
+    f_b = round_to_bf16(rng.standard_normal((H * K, 128)) / np.sqrt(128.0))
+    a_log = round_to_f32(rng.uniform(-2.0, 0.5, H))
+    dt = round_to_f32(rng.standard_normal(H * K))
+    return GateInputs(f_a, f_b, a_log, dt, float(np.float32(lower_bound)))

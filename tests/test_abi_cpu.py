@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     assert set(declared_functions([HEADER])) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
                                          "gdn_chunk_fwd_profiled", "gdn_chunk_fwd_noalloc", "gdn_recurrent_step",
                                          "gdn_recurrent_step_kda",
-                                         "gdn_recurrent_verify", "gdn_fp8_quant", "gdn_decode_prologue",
+                                         "gdn_recurrent_verify", "gdn_kda_gate", "gdn_fp8_quant", "gdn_decode_prologue",
                                          "gdn_gated_rmsnorm", "gdn_chunk_fwd_kda_workspace_bytes",
                                          "gdn_chunk_fwd_kda", "gdn_chunk_fwd_kda_profiled", "gdn_status_string"}
 
@@ -334,3 +334,18 @@ def test_noalloc_rejects_before_touching_the_device():
     assert _noalloc(H=0) == _lib.GDN_EINVAL
     assert _noalloc(q=None) == _lib.GDN_EINVAL
     assert _noalloc(in_dt=7) == _lib.GDN_EUNSUPPORTED
+
+
+def test_kda_gate_validation():
+    L = _lib.lib()
+    EINVAL, EUNS = _lib.GDN_EINVAL, _lib.GDN_EUNSUPPORTED
+    call = lambda **kw: L.gdn_kda_gate(kw.get("fa", FAKE), kw.get("fb", FAKE), kw.get("al", FAKE), kw.get("dt", FAKE),
+                                       kw.get("lb", -5.0), kw.get("mode", 0), kw.get("g", FAKE), kw.get("raw", None),
+                                       kw.get("N", 4), kw.get("H", 2), kw.get("K", 128), None)
+    assert call(K=96) == EUNS
+    assert call(mode=3) == EINVAL and call(mode=-1) == EINVAL
+    assert call(H=0) == EINVAL and call(N=-1) == EINVAL
+    assert call(lb=float("inf")) == EINVAL and call(lb=float("nan")) == EINVAL
+    assert call(fa=None) == EINVAL and call(g=None) == EINVAL
+    assert call(fa=FAKE + 8) == EINVAL and call(raw=FAKE + 1) == EINVAL
+    assert call(N=0) == _lib.GDN_OK

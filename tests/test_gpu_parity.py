@@ -7,6 +7,8 @@ output of the same call, bit for bit. Integer work (schedules, slots, padding,
 untouched pool pages) is checked exactly.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -852,3 +854,66 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(o, o_ref) and torch.equal(ht, ht_ref), f"replay {rep}: chunked call differs"
         assert torch.equal(do, do_ref[rep]) and torch.equal(pool_g, pool_ref[rep]), f"replay {rep}: decode differs"
     _print("[graph] 3 replays equal to eager")
+
+
+# ------------------------------------------ gate stage of the KDA decode layer
+#
+# The bf16 projection is a rounding decision taken in float32 in the order the
+# gate mode fixes, on both sides: bit-exact. The log-decays go through
+# transcendentals (float32 on the GPU, float64 in the oracle): within
+# 2e-6 * |lower_bound|.
+
+def _gate_dev(gi):
+    return (dev(gi.f_a, torch.bfloat16), dev(gi.f_b, torch.bfloat16), dev(gi.a_log), dev(gi.dt_bias))
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("N,H,K", [(1, 3, 128), (13, 2, 64), (300, 5, 128)])
+def test_kda_gate(mode, N, H, K):
+    from linear_attention_sequence_recompute_amd.workloads import gate_inputs
+    gi = gate_inputs(N, H, K, seed=200 + N + H + K + mode)
+    g, raw = api.kda_gate(*_gate_dev(gi), gi.lower_bound, H, mode=mode, with_raw=True)
+    torch.cuda.synchronize()
+    raw_ref, g_ref = oracle.kda_gate(gi.f_a, gi.f_b, gi.a_log, gi.dt_bias, gi.lower_bound, H, K, mode)
+    np.testing.assert_array_equal(host(raw), raw_ref)
+    err = float(np.max(np.abs(host(g) - g_ref)))
+    _print(f"[kda gate mode={mode} N={N} H={H} K={K}] max|dg|={err:.2e}")
+    assert err <= 2e-6 * abs(gi.lower_bound)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_kda_gate_orders_golden(mode):
+    """The hand-derived fixture where the three orders round differently."""
+    import json
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "gate_orders.json")))
+    f_a = np.zeros((1, 128))
+    for c, x in gold["f_a"].items():
+        f_a[0, int(c)] = x
+    K = 64
+    f_b = np.zeros((K, 128))  # features 2.. are zero rows
+    for f, row in enumerate(gold["f_b"]):
+        for c, x in row.items():
+            f_b[f, int(c)] = x
+    g, raw = api.kda_gate(dev(f_a, torch.bfloat16), dev(f_b, torch.bfloat16), dev(np.zeros(1)), dev(np.zeros(K)),
+                          -1.0, 1, mode=mode, with_raw=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(raw)[0, 0, :2], gold["raw_g"][str(mode)])
+
+
+def test_kda_gate_then_decode_step():
+    """gate -> decode step with per-channel decays, against the oracle's chain."""
+    from linear_attention_sequence_recompute_amd.workloads import gate_inputs
+    N, H, K = 64, 4, 128
+    gi = gate_inputs(N, H, K, seed=210)
+    di = decode_inputs(N, H, K, K, 80, dtype="bf16", seed=211, n_padding=5)
+    g = api.kda_gate(*_gate_dev(gi), gi.lower_bound, H, mode=1)
+    pool = dev(di.pool)
+    o = api.recurrent_step_kda(dev(di.q, torch.bfloat16), dev(di.k, torch.bfloat16), dev(di.v, torch.bfloat16), g,
+                               dev(di.beta), pool, dev(di.slots, torch.int32), scale=K ** -0.5,
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _, g_ref = oracle.kda_gate(gi.f_a, gi.f_b, gi.a_log, gi.dt_bias, gi.lower_bound, H, K, 1)
+    o_ref, pool_ref = oracle.decode_step_kda(di.q, di.k, di.v, g_ref, di.beta, di.pool, di.slots, scale=K ** -0.5)
+    eo, ep = max_err_over_rms(host(o), o_ref), max_err_over_rms(host(pool), pool_ref)
+    _print(f"[gate -> decode kda] o {eo:.2e} pool {ep:.2e}")
+    assert eo <= 1e-4 and ep <= 1e-4
