@@ -21,7 +21,8 @@ streaming copy and read) next to the published ones.
 Prints one JSON line on stdout (everything else goes to stderr).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-       python bench.py --only chunk|chunk1|chunk3|chunk4|decode|kda|verify|fp8|layer|chunk_kda|peaks|copy --steps K
+       python bench.py --only chunk|chunk1|chunk3|chunk4|decode|kda|verify|fp8|layer|gate|chunk_kda|peaks|copy
+                       --steps K
        (profiling runs)
 """
 
@@ -481,6 +482,37 @@ def bench_fp8(torch, api, hev, steps, warmup):
     return dict(kernel_ms=stats(ms))
 
 
+def bench_gate(torch, api, hev, steps, warmup):
+    """The KDA gate stage for N=DN tokens, H=DH heads, K=DK channels, each mode."""
+    from linear_attention_sequence_recompute_amd.workloads import gate_inputs
+
+    gi = gate_inputs(DN, DH, DK, seed=14)
+    dev = torch.device("cuda")
+    t = lambda x, d: torch.from_numpy(x).to(d).to(dev)
+    f_a, f_b, a_log, dt = t(gi.f_a, torch.bfloat16), t(gi.f_b, torch.bfloat16), t(gi.a_log, torch.float32), \
+        t(gi.dt_bias, torch.float32)
+    g = torch.empty(DN, DH, DK, device=dev)
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    out = {}
+    for mode in (0, 1, 2):
+        def step():
+            api.kda_gate(f_a, f_b, a_log, dt, gi.lower_bound, DH, mode=mode, out=g, stream=stream)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [hev.create(2) for _ in range(steps)]
+        for i in range(steps):
+            hev.record(evs[i][0], s)
+            step()
+            hev.record(evs[i][1], s)
+        torch.cuda.synchronize()
+        out[f"mode{mode}_ms"] = stats([hev.ms(e[0], e[1]) for e in evs])
+        for e in evs:
+            hev.destroy(e)
+    return out
+
+
 def layer_bytes():
     """Algorithmic bytes of the decode layer's front and back operations at
     N=DN requests, H=DH heads of DK channels (all active): each input and output
@@ -660,7 +692,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["all", "chunk", "chunk1", "chunk3", "chunk4", "decode", "kda", "verify", "fp8",
-                                       "layer", "chunk_kda", "peaks", "copy"], default="all")
+                                       "layer", "gate", "chunk_kda", "peaks", "copy"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -705,6 +737,8 @@ def main():
         f"groups of {QG}")
     run("layer", lambda: bench_layer(torch, api, hev, args.steps, args.warmup),
         f"decode layer front/back: N={DN} H={DH} D={DK} conv pool={DSLOTS}")
+    run("gate", lambda: bench_gate(torch, api, hev, args.steps, args.warmup),
+        f"KDA gate stage: N={DN} H={DH} K={DK}, rank 128, modes 0-2")
     run("chunk_kda", lambda: bench_chunk_kda(torch, api, hev, args.steps, args.warmup),
         "chunk form with per-channel decays: B=1 H=16 T=4096 K=V=128 bf16")
     if only != "all":
@@ -798,6 +832,16 @@ def main():
                      "roofline": hbm_roofline(lp_b / lp_s / 1e9, traffic_for("decode_prologue_kernel"), lp_b)},
         "gated_rmsnorm": {"avg_launch_us": lr_s * 1e6, "bytes_per_launch": lr_b,
                           "roofline": hbm_roofline(lr_b / lr_s / 1e9, traffic_for("gated_rmsnorm_kernel"), lr_b)}}
+    gate_flops = 2 * DN * DH * DK * 128
+    out["kda_gate"] = {
+        "workload": f"KDA gate stage (low-rank projection f_a . F_B, bf16 rounding, decays), N={DN} tokens, H={DH}, "
+                    f"K={DK}, rank 128; the projection as exact IEEE float32 FMA chains",
+        "modes_us": {m: res["gate"][f"mode{m}_ms"]["mean"] * 1e3 for m in (0, 1, 2)},
+        "roofline": {"bound": "alu", "achieved": gate_flops / (res["gate"]["mode0_ms"]["mean"] / 1e3) / 1e12,
+                     "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gate_flops / (res["gate"]["mode0_ms"]["mean"] / 1e3) / 1e12 / PEAK_FP32_TFLOPS,
+                     "flops_per_launch": gate_flops, "note": "mode 0; the fp32 vector peak counts packed FMAs, "
+                                                             "which IEEE-ordered scalar chains cannot use"}}
     res_ck = res["chunk_kda"]
     ck_scan_f, ck_prep_f = kda_chunk_flops()
     ck_scan_s, ck_prep_s = res_ck["scan_ms"]["mean"] / 1e3, res_ck["prep_ms"]["mean"] / 1e3

@@ -20,7 +20,8 @@ Functions (all float64 numpy):
   channel (KdaSplit), per token and as a decode step over the pool.
 * ``decode_prologue`` / ``gated_rmsnorm`` - the decode layer's front (conv1d
   over a conv-state pool, SiLU, q/k L2 norm, sigmoid beta) and back (gated
-  RMSNorm) operations (``oracle/layer.py``).
+  RMSNorm) operations (``oracle/layer.py``); ``decode_prologue_verify`` the front
+  for T tokens per request with the speculative-verify conv page.
 * ``kda_gate``       - the per-key-channel decays of the KDA decode layer from its
   low-rank gate projection (``oracle/gate.py``), in each of the page's float32
   reduction orders, exactly.
@@ -44,5 +45,5 @@ from .gdn import (  # noqa: F401
     unit_lower_inverse,
 )
 from .fp8 import e4m3_decode, e4m3_encode, fp8_quant  # noqa: F401
-from .layer import conv_silu_step, decode_prologue, gated_rmsnorm  # noqa: F401
+from .layer import conv_silu_step, decode_prologue, decode_prologue_verify, gated_rmsnorm  # noqa: F401
 from .gate import kda_gate  # noqa: F401

@@ -151,3 +151,103 @@ def test_rmsnorm_pins_catch_missing_eps_and_gate():
     with pytest.raises(AssertionError):
         check_rmsnorm(lambda o, g, w, eps: layer_mod.gated_rmsnorm(o, np.full_like(np.asarray(g, float), 40.0), w,
                                                                    eps))
+
+
+# ------------------------------------------------ multi-token (verify) conv front
+
+from oracle import decode_prologue_verify  # noqa: E402
+from oracle import layer as _layer  # noqa: E402
+
+
+def test_verify_front_one_token_is_the_decode_front():
+    rng = np.random.default_rng(5)
+    H, D, N, P = 2, 4, 5, 7
+    C = 3 * H * D
+    x = rng.standard_normal((N, C))
+    w = rng.standard_normal((3, 4, H * D))
+    bias = rng.standard_normal(C)
+    st = rng.standard_normal((P, C, 3))
+    slots = np.array([3, 0, 5, 1, 6])
+    braw = rng.standard_normal((N, H))
+    ref = decode_prologue(x, w, bias, st, slots, braw, H, D)
+    got = decode_prologue_verify(x, w, bias, st, slots[:, None], np.ones(N, int), braw, H, D, 1)
+    for a, b in zip(got, ref):
+        np.testing.assert_allclose(a, b, rtol=1e-14, atol=1e-14)
+
+
+def _spec_stream(fn, seed=11):
+    """Calls of T = 4 drafts with random accepted counts on one conv slot: every
+    call's outputs equal the causal convolution (numpy's convolve) over the
+    stream of accepted inputs followed by the call's drafts; the page after a call
+    is (column a, column a + 1, drafts)."""
+    rng = np.random.default_rng(seed)
+    H, D, T, P = 1, 2, 4, 3
+    C = 3 * H * D
+    w = rng.standard_normal((3, 4, H * D))
+    wc = np.concatenate([w[s].T for s in range(3)], axis=0)
+    hist = rng.standard_normal((3, C))  # the accepted stream so far (oldest first)
+    st = np.zeros((P, C, T + 2))
+    st[2, :, :3] = hist.T
+    stream = list(hist)
+    acc = 1
+    for call in range(6):
+        x = rng.standard_normal((T, C))
+        slots = np.array([[2, 1, 2, 1]])
+        q, k, v, beta, st2 = fn(x, w, None, st, slots, np.array([acc]), np.zeros((T, H)), H, D, T)
+        y = np.concatenate([q, k, v], axis=0)  # normalised: compare v (raw SiLU) and q, k directions
+        seq = np.array(stream + list(x))  # accepted stream, then the drafts
+        for c in range(C):
+            ref = np.convolve(seq[:, c], wc[c, ::-1])[:len(seq)]
+            conv = ref[len(stream):]
+            silu = conv / (1 + np.exp(-conv))
+            if c >= 2 * H * D:  # v section: raw
+                np.testing.assert_allclose(v[:, 0, c - 2 * H * D], silu, rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(st2[2][:, :2], st[2][:, acc:acc + 2])
+        np.testing.assert_array_equal(st2[2][:, 2:], x.T)
+        np.testing.assert_array_equal(st2[1], st[1])
+        m = int(rng.integers(1, T + 1))  # drafts accepted
+        stream += list(x[:m])
+        acc, st = m, st2
+
+
+def test_verify_front_follows_the_accepted_stream():
+    _spec_stream(decode_prologue_verify)
+
+
+def test_verify_front_padding():
+    rng = np.random.default_rng(6)
+    H, D, T, P = 1, 2, 3, 4
+    C = 3 * H * D
+    st = rng.standard_normal((P, C, T + 2))
+    x = rng.standard_normal((4 * T, C))
+    slots = np.array([[1, 2, 3], [0, 2, 3], [2, 0, 3], [3, 1, 2]])
+    accepted = np.array([0, 1, 2, 4])  # 0 and T + 1 out of range; row 1's conv slot 0; row 2's source slot 0
+    q, k, v, beta, st2 = decode_prologue_verify(x, rng.standard_normal((3, 4, H * D)), None, st, slots, accepted,
+                                                np.ones((4 * T, H)), H, D, T)
+    assert np.all(q == 0) and np.all(v == 0) and np.all(beta == 0)
+    np.testing.assert_array_equal(st2, st)
+
+
+@pytest.mark.parametrize("mutation", ["taps_from_a", "rewrite_keeps_a_minus_1", "conv_slot_from_source"])
+def test_verify_front_pins_catch_mistakes(mutation):
+    def mutant(x, w, bias, conv_state, slots, accepted, beta_raw, H, D, T):
+        x = np.asarray(x, np.float64)
+        st = np.asarray(conv_state, np.float64).copy()
+        N, C = x.shape[0] // T, st.shape[1]
+        wc = np.concatenate([np.asarray(w, np.float64)[s].T for s in range(3)], axis=0)
+        y = np.zeros((N * T, C))
+        for b in range(N):
+            a = int(accepted[b])
+            cs = int(slots[b, a - 1]) if mutation == "conv_slot_from_source" else int(slots[b, 0])
+            page = st[cs]
+            o = a if mutation == "taps_from_a" else a - 1
+            seq = np.concatenate([page[:, o:o + 3], x[b * T:(b + 1) * T].T], axis=1)
+            for t in range(T):
+                z = np.sum(seq[:, t:t + 4] * wc, axis=1)
+                y[b * T + t] = z * _layer._sig(z)
+            r = a - 1 if mutation == "rewrite_keeps_a_minus_1" else a
+            st[cs] = np.concatenate([page[:, r:r + 2], x[b * T:(b + 1) * T].T], axis=1)
+        q, k, v = _layer._sections(y, H, D)
+        return q, k, v, np.zeros((N * T, H)), st
+    with pytest.raises(AssertionError):
+        _spec_stream(mutant)
