@@ -337,6 +337,48 @@ gdn_status gdn_decode_prologue(const void* x, const float* conv_w, const float* 
                                int N, int H, int D, void* stream);
 
 /*
+ * Front operations of a decode layer for T tokens per request (speculative
+ * verify: the vLLM KdaSplit page, class docstring, ``tokens`` q > 1, and the
+ * kernel body's multi-token conv window and rewrite), heads of D = K = V
+ * channels. Rows of x, beta_raw and the outputs are b * T + t.
+ *
+ *  x           bf16 [N * T, 3 H D]: the tokens' projected q, k, v sections
+ *  conv_w      float32 [3, 4, H D];  conv_bias float32 [3 H D] or NULL
+ *  conv_state  bf16 [pool_slots, 3 H D, T + 2]: request b's conv page is
+ *              slot[b, 0]; its columns a - 1, a, a + 1 (a = accepted[b]) are
+ *              the three inputs before the request's first token. Updated in
+ *              place for active requests to (column a, column a + 1, x_0, ...,
+ *              x_{T-1}).
+ *  slots       device int32 [N, slot_cols] (row-major), slot_cols >= T; the
+ *              recurrent state's source is slot[b, a - 1] (as in
+ *              gdn_recurrent_verify)
+ *  accepted    device int32 [N]
+ *  beta_raw    float32 [N * T, H]
+ *  q, k, v     float32 [N * T, H, D] (outputs);  beta float32 [N * T, H]
+ *
+ * Token t's channel takes y = SiLU(bias + sum over the 4 taps of w * window)
+ * with the window (page column a - 1 + t .. , then the inputs) at positions
+ * t .. t + 3 of (three page columns, x_0 .. x_{T-1}); then each head's q and k
+ * are divided by sqrt(sum of squares + 1e-6) and beta = sigmoid(beta_raw).
+ * A request whose accepted count is outside [1, T], whose source slot is <= 0,
+ * or whose conv slot is outside [1, pool_slots) is padding: its rows are +0 and
+ * its conv page is not touched. Active conv slots must be distinct.
+ *
+ * Alignment: x, slots, accepted, beta_raw and beta 4 bytes; conv_state 2 bytes;
+ * conv_w, conv_bias, q, k and v 8 bytes.
+ *
+ * Returns GDN_EUNSUPPORTED for D outside {64, 128}; GDN_EINVAL for N < 0, T
+ * outside [1, 8], slot_cols < T, H outside [1, 65535], sizes whose grid would not
+ * fit, a NULL pointer (other than conv_bias), pool_slots <= 0 or a misaligned
+ * pointer; GDN_OK without launching for N == 0; GDN_EHIP if the launch fails.
+ */
+gdn_status gdn_decode_prologue_verify(const void* x, const float* conv_w, const float* conv_bias,
+                                      void* conv_state, int64_t pool_slots, const int32_t* slots,
+                                      int slot_cols, const int32_t* accepted, const float* beta_raw,
+                                      float* q, float* k, float* v, float* beta, int N, int T, int H,
+                                      int D, void* stream);
+
+/*
  * Gated RMSNorm of each head's decode output (vLLM KdaSplit page, kernel body:
  * the output normalisation after the recurrent update).
  *

@@ -356,6 +356,39 @@ def decode_prologue(x: torch.Tensor, conv_w: torch.Tensor, conv_bias: Optional[t
     return q, k, v, beta
 
 
+def decode_prologue_verify(x: torch.Tensor, conv_w: torch.Tensor, conv_bias: Optional[torch.Tensor],
+                           conv_state: torch.Tensor, slots: torch.Tensor, accepted: torch.Tensor,
+                           beta_raw: torch.Tensor, H: int, T: int, *, stream=None):
+    """Front operations for T tokens per request (gdn_decode_prologue_verify): x
+    bf16 [N T, 3 H D]; conv_state bf16 [P, 3 H D, T + 2] (updated in place);
+    slots int32 [N, C >= T]; accepted int32 [N]; beta_raw float32 [N T, H].
+    Returns (q, k, v float32 [N T, H, D], beta float32 [N T, H])."""
+    if x.dim() != 2 or x.shape[0] % T or x.shape[1] % (3 * H):
+        raise ValueError("x must be [N T, 3 H D]")
+    NT, C = x.shape
+    N, D = NT // T, C // (3 * H)
+    if conv_w.shape != (3, 4, H * D) or conv_state.dim() != 3 or tuple(conv_state.shape[1:]) != (C, T + 2):
+        raise ValueError("conv_w must be [3, 4, H D] and conv_state [P, 3 H D, T + 2]")
+    if slots.dim() != 2 or slots.shape[0] != N or accepted.shape != (N,) or beta_raw.shape != (NT, H):
+        raise ValueError("slots must be [N, C], accepted [N] and beta_raw [N T, H]")
+    _need(x, "x", torch.bfloat16)
+    _need(conv_w, "conv_w", torch.float32)
+    _need(conv_state, "conv_state", torch.bfloat16)
+    _need(slots, "slots", torch.int32)
+    _need(accepted, "accepted", torch.int32)
+    _need(beta_raw, "beta_raw", torch.float32)
+    if conv_bias is not None:
+        _need(conv_bias, "conv_bias", torch.float32)
+        _shape(conv_bias, (C,), "conv_bias")
+    q, k, v = (torch.empty((NT, H, D), dtype=torch.float32, device=x.device) for _ in range(3))
+    beta = torch.empty((NT, H), dtype=torch.float32, device=x.device)
+    st = _lib.lib().gdn_decode_prologue_verify(
+        _ptr(x), _ptr(conv_w), _ptr(conv_bias), _ptr(conv_state), conv_state.shape[0], _ptr(slots), slots.shape[1],
+        _ptr(accepted), _ptr(beta_raw), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), N, T, H, D, _stream(stream))
+    _lib.check(st, "gdn_decode_prologue_verify")
+    return q, k, v, beta
+
+
 def gated_rmsnorm(o: torch.Tensor, gate: torch.Tensor, norm_w: torch.Tensor, eps: float = 1e-6, *,
                   out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None, stream=None):
     """Gated RMSNorm of decode outputs (gdn_gated_rmsnorm): o float32 [N, H, D],

@@ -425,6 +425,44 @@ gdn_status gdn_decode_prologue(const void* x, const float* conv_w, const float* 
   return hip_status(gdn::launch_decode_prologue(a));
 }
 
+gdn_status gdn_decode_prologue_verify(const void* x, const float* conv_w, const float* conv_bias, void* conv_state,
+                                      int64_t pool_slots, const int32_t* slots, int slot_cols,
+                                      const int32_t* accepted, const float* beta_raw, float* q, float* k, float* v,
+                                      float* beta, int N, int T, int H, int D, void* stream) {
+  if (D != 64 && D != 128) return GDN_EUNSUPPORTED;
+  if (N < 0 || T < 1 || T > 8 || slot_cols < T || H <= 0 || H > 65535) return GDN_EINVAL;
+  if (static_cast<int64_t>(N) * H * (D / 2) > INT32_MAX || static_cast<int64_t>(N) * T * H > INT32_MAX)
+    return GDN_EINVAL;
+  if (N == 0) return GDN_OK;
+  if (!x || !conv_w || !conv_state || !slots || !accepted || !beta_raw || !q || !k || !v || !beta ||
+      pool_slots <= 0)
+    return GDN_EINVAL;
+  if (!aligned(x, 4) || !aligned(conv_state, 2) || !aligned(conv_w, 8) || !aligned(slots, 4) ||
+      !aligned(accepted, 4) || !aligned(beta_raw, 4) || !aligned(q, 8) || !aligned(k, 8) || !aligned(v, 8) ||
+      !aligned(beta, 4) || (conv_bias && !aligned(conv_bias, 8)))
+    return GDN_EINVAL;
+  gdn::PrologueArgs a{};
+  a.x = x;
+  a.conv_w = conv_w;
+  a.conv_bias = conv_bias;
+  a.conv_state = conv_state;
+  a.pool_slots = pool_slots;
+  a.slots = slots;
+  a.cols = slot_cols;
+  a.accepted = accepted;
+  a.beta_raw = beta_raw;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.N = N;
+  a.T = T;
+  a.H = H;
+  a.D = D;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_decode_prologue_verify(a));
+}
+
 gdn_status gdn_gated_rmsnorm(const float* o, const void* gate, const float* norm_w, float eps, void* out, int N, int H,
                              int D, gdn_dtype out_dtype, void* stream) {
   if (D != 64 && D != 128) return GDN_EUNSUPPORTED;

@@ -43,10 +43,12 @@ struct PrologueArgs {
   const float* conv_bias;   // [3 H D] or null
   void* conv_state;         // [pool_slots, 3 H D, 3] bf16
   int64_t pool_slots;
-  const int32_t* slots;     // [N]
-  const float* beta_raw;    // [N, H]
-  float *q, *k, *v, *beta;  // [N, H, D] x 3, [N, H]
-  int N, H, D;
+  const int32_t* slots;     // [N], or [N, cols] (verify: T tokens per request)
+  int cols;                 // verify: slot columns
+  const int32_t* accepted;  // verify: [N]
+  const float* beta_raw;    // [N T, H]
+  float *q, *k, *v, *beta;  // [N T, H, D] x 3, [N T, H]
+  int N, T, H, D;
   hipStream_t stream;
 };
 
@@ -163,6 +165,7 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_verify(const VerifyArgs& a);
 hipError_t launch_fp8_quant(const Fp8Args& a);
 hipError_t launch_decode_prologue(const PrologueArgs& a);
+hipError_t launch_decode_prologue_verify(const PrologueArgs& a);
 hipError_t launch_gated_rmsnorm(const RmsNormArgs& a);
 hipError_t launch_chunk_fwd_kda(const KdaChunkArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);

@@ -134,6 +134,111 @@ __global__ __launch_bounds__(kLayerThreads) void decode_prologue_kernel(
   }
 }
 
+// The front for T tokens per request (speculative verify, the KdaSplit class
+// docstring and the kernel body's tokens branch): the conv page of slot[b, 0]
+// holds T + 2 inputs per channel; token t convolves (page columns a - 1, a, a + 1,
+// then x_0 .. x_{T-1}) at positions t .. t + 3 (a = accepted[b]), and the page
+// becomes (column a, column a + 1, x_0 .. x_{T-1}). A group of D / 2 lanes takes
+// one (request, head), two adjacent channels per lane, and runs the T tokens in
+// a sliding window held in registers; every tap is read before the page is
+// rewritten (each lane reads and writes only its own channels).
+template <int D, bool BIAS>
+__global__ __launch_bounds__(kLayerThreads) void decode_prologue_verify_kernel(
+    const __bf16* __restrict__ x, const float* __restrict__ conv_w, const float* __restrict__ conv_bias,
+    __bf16* __restrict__ conv_state, int64_t pool_slots, const int32_t* __restrict__ slots, int cols,
+    const int32_t* __restrict__ accepted, const float* __restrict__ beta_raw, float* __restrict__ q,
+    float* __restrict__ k, float* __restrict__ v, float* __restrict__ beta, int N, int T, int H) {
+  constexpr int LPH = D / 2;
+  constexpr int kMaxT = 8;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kLayerThreads + threadIdx.x;
+  const int64_t grp = gid / LPH;  // (request, head)
+  if (grp >= static_cast<int64_t>(N) * H) return;  // whole groups leave together
+  const int c = 2 * static_cast<int>(gid % LPH);
+  const int h = static_cast<int>(grp % H);
+  const int64_t b = grp / H;
+  const int64_t dim = static_cast<int64_t>(H) * D, C = 3 * dim;
+  const int W = T + 2;  // page columns
+  const int acc = accepted[b];
+  int cslot = 0, src = 0;
+  if (acc >= 1 && acc <= T) {
+    src = slots[b * cols + acc - 1];
+    cslot = slots[b * cols];
+  }
+  const bool live = src > 0 && cslot > 0 && cslot < pool_slots;
+  if (!live) {  // padding: zero outputs, conv state untouched
+    const float2 z = make_float2(0.f, 0.f);
+    for (int t = 0; t < T; ++t) {
+      const int64_t row = (b * T + t) * H + h, out = row * D + c;
+      *reinterpret_cast<float2*>(q + out) = z;
+      *reinterpret_cast<float2*>(k + out) = z;
+      *reinterpret_cast<float2*>(v + out) = z;
+      if (c == 0) beta[row] = 0.f;
+    }
+    return;
+  }
+  float2 y[3][kMaxT];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const int64_t ch = s * dim + static_cast<int64_t>(h) * D + c;
+    const float* wc = conv_w + (s * 4) * dim + static_cast<int64_t>(h) * D + c;  // weights [3][4][dim]
+    float2 w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = *reinterpret_cast<const float2*>(wc + i * dim);
+    const float2 bias = BIAS ? *reinterpret_cast<const float2*>(conv_bias + ch) : make_float2(0.f, 0.f);
+    __bf16* page0 = conv_state + (static_cast<int64_t>(cslot) * C + ch) * W;  // channel c; c + 1 at + W
+    // the window: three taps, then the tokens' inputs
+    float s0[kMaxT + 3], s1[kMaxT + 3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      s0[j] = static_cast<float>(page0[acc - 1 + j]);
+      s1[j] = static_cast<float>(page0[W + acc - 1 + j]);
+    }
+    uint32_t xw[kMaxT];
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) {
+      if (t >= T) break;
+      xw[t] = *reinterpret_cast<const uint32_t*>(x + (b * T + t) * C + ch);
+      s0[3 + t] = bf_lo(xw[t]);
+      s1[3 + t] = bf_hi(xw[t]);
+    }
+    const __bf16 k0a = page0[acc], k0b = page0[acc + 1], k1a = page0[W + acc], k1b = page0[W + acc + 1];
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) {
+      if (t >= T) break;
+      float2 a = bias;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a.x = fmaf(w[i].x, s0[t + i], a.x);
+        a.y = fmaf(w[i].y, s1[t + i], a.y);
+      }
+      y[s][t] = make_float2(a.x / (1.f + expf(-a.x)), a.y / (1.f + expf(-a.y)));  // SiLU
+    }
+    // the page becomes (column a, column a + 1, x_0 .. x_{T-1})
+    page0[0] = k0a;
+    page0[1] = k0b;
+    page0[W] = k1a;
+    page0[W + 1] = k1b;
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) {
+      if (t >= T) break;
+      page0[2 + t] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(xw[t] & 0xffffu));
+      page0[W + 2 + t] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(xw[t] >> 16));
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kMaxT; ++t) {
+    if (t >= T) break;
+    const int64_t row = (b * T + t) * H + h, out = row * D + c;
+    const float nq = row_sum<D>(y[0][t].x * y[0][t].x + y[0][t].y * y[0][t].y);
+    const float nk = row_sum<D>(y[1][t].x * y[1][t].x + y[1][t].y * y[1][t].y);
+    const float rq = rsqrtf(nq + 1e-6f), rk = rsqrtf(nk + 1e-6f);
+    *reinterpret_cast<float2*>(q + out) = make_float2(y[0][t].x * rq, y[0][t].y * rq);
+    *reinterpret_cast<float2*>(k + out) = make_float2(y[1][t].x * rk, y[1][t].y * rk);
+    *reinterpret_cast<float2*>(v + out) = y[2][t];
+    if (c == 0) beta[row] = 1.f / (1.f + expf(-beta_raw[row]));
+  }
+}
+
 __device__ __forceinline__ void store_pair(float* p, float a, float b) {
   *reinterpret_cast<float2*>(p) = make_float2(a, b);
 }
@@ -172,6 +277,19 @@ hipError_t launch_decode_prologue(const PrologueArgs& a) {
   hipLaunchKernelGGL(kern, grid, dim3(kLayerThreads), 0, a.stream, static_cast<const __bf16*>(a.x), a.conv_w,
                      a.conv_bias, static_cast<__bf16*>(a.conv_state), a.pool_slots, a.slots, a.beta_raw, a.q, a.k,
                      a.v, a.beta, a.N, a.H, groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_prologue_verify(const PrologueArgs& a) {
+  const int64_t groups = static_cast<int64_t>(a.N) * a.H;
+  const dim3 grid(layer_blocks(groups, a.D));
+  auto kern = a.D == 128 ? (a.conv_bias ? decode_prologue_verify_kernel<128, true>
+                                        : decode_prologue_verify_kernel<128, false>)
+                         : (a.conv_bias ? decode_prologue_verify_kernel<64, true>
+                                        : decode_prologue_verify_kernel<64, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(kLayerThreads), 0, a.stream, static_cast<const __bf16*>(a.x), a.conv_w,
+                     a.conv_bias, static_cast<__bf16*>(a.conv_state), a.pool_slots, a.slots, a.cols, a.accepted,
+                     a.beta_raw, a.q, a.k, a.v, a.beta, a.N, a.T, a.H);
   return hipGetLastError();
 }
 

@@ -43,6 +43,8 @@ __all__ = [
     "layer_inputs",
     "GateInputs",
     "gate_inputs",
+    "LayerVerifyInputs",
+    "layer_verify_inputs",
 ]
 
 
@@ -333,3 +335,52 @@ def gate_inputs(N: int, H: int, K: int, seed: int = 0, lower_bound: float = -5.0
     a_log = round_to_f32(rng.uniform(-2.0, 0.5, H))
     dt = round_to_f32(rng.standard_normal(H * K))
     return GateInputs(f_a, f_b, a_log, dt, float(np.float32(lower_bound)))
+
+
+@dataclass
+class LayerVerifyInputs:
+    x: np.ndarray           # [N * T, 3 H D] bf16 values
+    conv_w: np.ndarray      # [3, 4, H D] float32
+    conv_bias: np.ndarray   # [3 H D] float32
+    conv_state: np.ndarray  # [P, 3 H D, T + 2] bf16 values
+    slots: np.ndarray       # [N, T] int32: conv page slot[b, 0], state source slot[b, accepted - 1]
+    accepted: np.ndarray    # [N] int32
+    beta_raw: np.ndarray    # [N * T, H] float32
+    gate: np.ndarray        # [N * T, H D] bf16 values
+    norm_w: np.ndarray      # [D] float32
+    a: np.ndarray           # [N * T, H] float32 raw log-gates of the recurrent step
+    pool: np.ndarray        # [P, H, D, D] float32 recurrent states
+    H: int
+    D: int
+    T: int
+
+
+def layer_verify_inputs(N: int, T: int, H: int, D: int, pool_slots: int, seed: int = 0,
+                        n_padding: int = 0) -> LayerVerifyInputs:
+    """One speculative-verify call of a decode layer: T tokens per request, the
+    distributions of ``layer_inputs`` for the front and back operations and of
+    ``verify_inputs`` for the recurrent step; one slot table [N, T] of distinct
+    positive slots serves the conv pages (column 0) and the recurrent states;
+    accepted counts uniform in [1, T]; ``n_padding`` requests get a source slot
+    (column accepted - 1) of 0 or -1."""
+    rng = np.random.default_rng(seed)
+    dim = H * D
+    x = round_to_bf16(rng.standard_normal((N * T, 3 * dim)))
+    conv_w = round_to_f32(rng.uniform(-0.5, 0.5, (3, 4, dim)))
+    conv_bias = round_to_f32(rng.uniform(-0.5, 0.5, 3 * dim))
+    conv_state = round_to_bf16(rng.standard_normal((pool_slots, 3 * dim, T + 2)))
+    beta_raw = round_to_f32(rng.standard_normal((N * T, H)))
+    gate = round_to_bf16(rng.standard_normal((N * T, dim)))
+    norm_w = round_to_f32(1.0 + 0.1 * rng.standard_normal(D))
+    a = round_to_f32(-_softplus(rng.standard_normal((N * T, H)) + 2.0))
+    pool = round_to_f32(rng.normal(0.0, 0.1, (pool_slots, H, D, D)))
+    if N * T > pool_slots - 1:
+        raise ValueError("more table entries than usable pool slots")
+    slots = rng.choice(np.arange(1, pool_slots), N * T, replace=False).astype(np.int32).reshape(N, T)
+    accepted = rng.integers(1, T + 1, N).astype(np.int32)
+    for b in (rng.choice(N, n_padding, replace=False) if n_padding else []):
+        if accepted[b] == 1:  # keep the conv slot (column 0) positive where it is not the source
+            accepted[b] = min(2, T)
+        slots[b, accepted[b] - 1] = rng.choice([0, -1])
+    return LayerVerifyInputs(x, conv_w, conv_bias, conv_state, slots, accepted, beta_raw, gate, norm_w, a, pool,
+                             H, D, T)

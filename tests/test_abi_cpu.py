@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     assert set(declared_functions([HEADER])) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
                                          "gdn_chunk_fwd_profiled", "gdn_chunk_fwd_noalloc", "gdn_recurrent_step",
                                          "gdn_recurrent_step_kda",
-                                         "gdn_recurrent_verify", "gdn_kda_gate", "gdn_fp8_quant", "gdn_decode_prologue",
+                                         "gdn_recurrent_verify", "gdn_kda_gate", "gdn_fp8_quant", "gdn_decode_prologue", "gdn_decode_prologue_verify",
                                          "gdn_gated_rmsnorm", "gdn_chunk_fwd_kda_workspace_bytes",
                                          "gdn_chunk_fwd_kda", "gdn_chunk_fwd_kda_profiled", "gdn_status_string"}
 
@@ -348,4 +348,22 @@ def test_kda_gate_validation():
     assert call(lb=float("inf")) == EINVAL and call(lb=float("nan")) == EINVAL
     assert call(fa=None) == EINVAL and call(g=None) == EINVAL
     assert call(fa=FAKE + 8) == EINVAL and call(raw=FAKE + 1) == EINVAL
+    assert call(N=0) == _lib.GDN_OK
+
+
+def test_decode_prologue_verify_validation():
+    L = _lib.lib()
+    EINVAL, EUNS = _lib.GDN_EINVAL, _lib.GDN_EUNSUPPORTED
+
+    def call(**kw):
+        a = dict(x=FAKE, w=FAKE, bias=None, st=FAKE, pool=8, slots=FAKE, cols=4, acc=FAKE, braw=FAKE, q=FAKE, k=FAKE,
+                 v=FAKE, beta=FAKE, N=2, T=4, H=2, D=128)
+        a.update(kw)
+        return L.gdn_decode_prologue_verify(a["x"], a["w"], a["bias"], a["st"], a["pool"], a["slots"], a["cols"],
+                                            a["acc"], a["braw"], a["q"], a["k"], a["v"], a["beta"], a["N"], a["T"],
+                                            a["H"], a["D"], None)
+    assert call(D=96) == EUNS
+    assert call(T=0) == EINVAL and call(T=9) == EINVAL and call(cols=3) == EINVAL
+    assert call(acc=None) == EINVAL and call(pool=0) == EINVAL
+    assert call(q=FAKE + 4) == EINVAL and call(st=FAKE + 1) == EINVAL
     assert call(N=0) == _lib.GDN_OK

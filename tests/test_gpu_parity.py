@@ -917,3 +917,61 @@ def test_kda_gate_then_decode_step():
     eo, ep = max_err_over_rms(host(o), o_ref), max_err_over_rms(host(pool), pool_ref)
     _print(f"[gate -> decode kda] o {eo:.2e} pool {ep:.2e}")
     assert eo <= 1e-4 and ep <= 1e-4
+
+
+# -------------------------------------- decode layer front for speculative verify
+
+def check_prologue_verify(li, label):
+    state = dev(li.conv_state, torch.bfloat16)
+    q, k, v, beta = api.decode_prologue_verify(dev(li.x, torch.bfloat16), dev(li.conv_w), dev(li.conv_bias), state,
+                                               dev(li.slots, torch.int32), dev(li.accepted, torch.int32),
+                                               dev(li.beta_raw), li.H, li.T)
+    torch.cuda.synchronize()
+    rq, rk, rv, rb, rst = oracle.decode_prologue_verify(li.x, li.conv_w, li.conv_bias, li.conv_state, li.slots,
+                                                        li.accepted, li.beta_raw, li.H, li.D, li.T)
+    act = rb[:, 0] != 0
+    errs = [max_err_over_rms(host(t)[act], r[act]) for t, r in ((q, rq), (k, rk), (v, rv), (beta, rb))]
+    for t in (q, k, v, beta):
+        assert bool((t[torch.from_numpy(~act).cuda()].view(torch.int32) == 0).all()), f"{label}: padding not +0"
+    assert np.array_equal(host(state), rst), f"{label}: conv state differs"
+    _print(f"[prologue verify {label}] max err/rms q,k,v,beta = " + " ".join(f"{e:.2e}" for e in errs))
+    assert max(errs) <= LAYER_TOL
+
+
+@pytest.mark.parametrize("D,T", [(64, 2), (128, 4), (128, 8), (64, 1)])
+def test_decode_prologue_verify(D, T):
+    from linear_attention_sequence_recompute_amd.workloads import layer_verify_inputs
+    li = layer_verify_inputs(N=13, T=T, H=3, D=D, pool_slots=13 * T + 9, seed=300 + D + T, n_padding=3)
+    check_prologue_verify(li, f"D={D} T={T}")
+
+
+def test_decode_layer_verify_composition():
+    """Verify-mode front (T = 4), the speculative-verify decode and the gated
+    RMSNorm in a row, against the oracle's three steps: N=24 requests, H=4 heads
+    of 128 channels, 3 padding requests."""
+    from linear_attention_sequence_recompute_amd.workloads import layer_verify_inputs
+    N, T, H, D = 24, 4, 4, 128
+    P = N * T + 5
+    li = layer_verify_inputs(N=N, T=T, H=H, D=D, pool_slots=P, seed=321, n_padding=3)
+    conv = dev(li.conv_state, torch.bfloat16)
+    pool = dev(li.pool)
+    slots, acc = dev(li.slots, torch.int32), dev(li.accepted, torch.int32)
+    q, k, v, beta = api.decode_prologue_verify(dev(li.x, torch.bfloat16), dev(li.conv_w), dev(li.conv_bias), conv,
+                                               slots, acc, dev(li.beta_raw), H, T)
+    o = api.recurrent_verify(q.view(N, T, H, D), k.view(N, T, H, D), v.view(N, T, H, D), dev(li.a).view(N, T, H),
+                             beta.view(N, T, H), pool, slots, acc, scale=D ** -0.5, out_dtype=torch.float32)
+    out = api.gated_rmsnorm(o.view(N * T, H, D), dev(li.gate, torch.bfloat16), dev(li.norm_w), 1e-6,
+                            out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rq, rk, rv, rb, _ = oracle.decode_prologue_verify(li.x, li.conv_w, li.conv_bias, li.conv_state, li.slots,
+                                                      li.accepted, li.beta_raw, H, D, T)
+    ro, rpool = oracle.decode_verify(rq.reshape(N, T, H, D), rk.reshape(N, T, H, D), rv.reshape(N, T, H, D),
+                                     li.a.reshape(N, T, H), rb.reshape(N, T, H), li.pool, li.slots, li.accepted,
+                                     scale=D ** -0.5)
+    ref = oracle.gated_rmsnorm(ro.reshape(N * T, H, D), li.gate, li.norm_w, 1e-6)
+    act = rb[:, 0] != 0
+    e_out = max_err_over_rms(host(out)[act], ref[act])
+    e_st = max_err_over_rms(host(pool), rpool)
+    _print(f"[decode layer verify] max err/rms out={e_out:.2e} pool={e_st:.2e}")
+    assert e_out <= TOL["f32"] and e_st <= TOL["f32"]
+    assert bool((out[torch.from_numpy(~act).cuda()] == 0).all())
