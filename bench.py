@@ -567,7 +567,36 @@ def bench_layer(torch, api, hev, steps, warmup):
     ms_r = [hev.ms(e[2], e[3]) for e in evs]
     for e in evs:
         hev.destroy(e)
-    return dict(prologue_ms=stats(ms_p), rmsnorm_ms=stats(ms_r))
+    # the whole layer: separate launches (front, decode step, RMSNorm) against
+    # the fused one, on the same inputs and a pool of DSLOTS states
+    pool = torch.randn(DSLOTS, DH, DK, DK, device=dev, generator=g) * 0.1
+    lg = -torch.nn.functional.softplus(torch.randn(DN, DH, device=dev, generator=g) + 2.0)
+    out32 = torch.empty(DN, DH, DK, dtype=torch.float32, device=dev)
+
+    def separate():
+        q, k, v, beta = api.decode_prologue(x, w, bias, conv, slots, braw, DH, stream=stream)
+        api.recurrent_step(q, k, v, lg, beta, pool, slots, scale=DK ** -0.5, out=out32, stream=stream)
+        api.gated_rmsnorm(out32, gate, nw, 1e-6, out=out, stream=stream)
+
+    def fused():
+        api.decode_layer(x, w, bias, conv, slots, braw, lg, pool, DH, gate=gate, norm_w=nw, out=out, stream=stream)
+
+    res = {}
+    for name, fn in (("separate", separate), ("fused", fused)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [hev.create(2) for _ in range(steps)]
+        for i in range(steps):
+            hev.record(evs[i][0], s)
+            fn()
+            hev.record(evs[i][1], s)
+        torch.cuda.synchronize()
+        res[name] = stats([hev.ms(e[0], e[1]) for e in evs])
+        for e in evs:
+            hev.destroy(e)
+    return dict(prologue_ms=stats(ms_p), rmsnorm_ms=stats(ms_r), layer_separate_ms=res["separate"],
+                layer_fused_ms=res["fused"])
 
 
 def bench_copy(torch, steps, nbytes=1 << 30):
@@ -832,6 +861,17 @@ def main():
                      "roofline": hbm_roofline(lp_b / lp_s / 1e9, traffic_for("decode_prologue_kernel"), lp_b)},
         "gated_rmsnorm": {"avg_launch_us": lr_s * 1e6, "bytes_per_launch": lr_b,
                           "roofline": hbm_roofline(lr_b / lr_s / 1e9, traffic_for("gated_rmsnorm_kernel"), lr_b)}}
+    lf_s = res_l["layer_fused_ms"]["mean"] / 1e3
+    # the fused layer's algorithmic bytes: the decode step's (q, k, v not read) plus the front's x, conv state read and
+    # written, weights, beta_raw and the RMSNorm's gate and weights
+    lf_b = dec_b - DN * DH * (2 * DK + DV) * 2 + DN * 3 * DH * DK * 2 + 2 * DN * 3 * DH * DK * 3 * 2 \
+        + (3 * 4 * DH * DK + 3 * DH * DK) * 4 + DN * DH * 4 + DN * DH * DK * 2 + DK * 4
+    out["decode_layer"]["layer"] = {
+        "workload": f"the whole decode layer (front, decode step with a scalar gate, gated RMSNorm), N={DN} H={DH} "
+                    f"D={DK}, state pool {DSLOTS} slots",
+        "separate_launches_us": res_l["layer_separate_ms"]["mean"] * 1e3,
+        "fused_us": lf_s * 1e6, "bytes_per_launch": lf_b,
+        "roofline": hbm_roofline(lf_b / lf_s / 1e9, traffic_for("decode_layer_kernel"), lf_b)}
     gate_flops = 2 * DN * DH * DK * 128
     out["kda_gate"] = {
         "workload": f"KDA gate stage (low-rank projection f_a . F_B, bf16 rounding, decays), N={DN} tokens, H={DH}, "

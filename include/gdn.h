@@ -402,6 +402,38 @@ gdn_status gdn_gated_rmsnorm(const float* o, const void* gate, const float* norm
                              void* out, int N, int H, int D, gdn_dtype out_dtype, void* stream);
 
 /*
+ * The decode layer in one launch, one token per request (the vLLM KdaSplit page,
+ * kernel body: convolution, activation and normalisation steps, the recurrent
+ * update, the output norm), for heads of D = K = V channels: the steps of
+ * gdn_decode_prologue, then gdn_recurrent_step (g_per_channel = 0: g [N, H]) or
+ * gdn_recurrent_step_kda (g_per_channel != 0: g [N, H, D], 16-byte aligned) on
+ * its q, k, v and beta, then gdn_gated_rmsnorm (when norm_w is not NULL; else
+ * out is the raw update output). Every argument as in those entry points;
+ * the conv-state pool has conv_slots slots and the state pool pool_slots, both
+ * indexed by slots[b]; a slot <= 0 or outside either pool is padding (out row
+ * +0, neither pool touched). Active slots must be distinct.
+ *
+ *  x           bf16 [N, 3 H D];  conv_w float32 [3, 4, H D];  conv_bias [3 H D] or NULL
+ *  conv_state  bf16 [conv_slots, 3 H D, 3] (in place)
+ *  beta_raw    float32 [N, H]
+ *  state_pool  float32 [pool_slots, H, D, D] (in place)
+ *  gate        bf16 [N, H D] (with norm_w);  norm_w float32 [D] or NULL;  eps >= 0
+ *  out         [N, H, D] out_dtype
+ *  scale       multiplies the normalised q
+ *
+ * Returns GDN_EUNSUPPORTED for D outside {64, 128} or an unknown dtype;
+ * GDN_EINVAL for N < 0, H outside [1, 65535], N H above 2^31 - 1, a negative or
+ * NaN eps with norm_w, a NULL pointer (other than conv_bias, norm_w and then
+ * gate), a pool size <= 0 or a misaligned pointer; GDN_OK without launching for
+ * N == 0; GDN_EHIP if the launch fails.
+ */
+gdn_status gdn_decode_layer(const void* x, const float* conv_w, const float* conv_bias, void* conv_state,
+                            int64_t conv_slots, const int32_t* slots, const float* beta_raw,
+                            const float* g, int g_per_channel, float* state_pool, int64_t pool_slots,
+                            const void* gate, const float* norm_w, float eps, void* out,
+                            gdn_dtype out_dtype, int N, int H, int D, float scale, void* stream);
+
+/*
  * Workspace bytes gdn_chunk_fwd_kda needs for B sequences of T tokens: per
  * (sequence, chunk of 64 tokens, head) (2 * 64 * 64 + 3 * 64 * K + K) float32.
  * Returns 0 for negative sizes, H outside [1, 65535] or K outside {64, 128}.

@@ -39,6 +39,8 @@ SIGNATURES = {
     "gdn_decode_prologue": (_I, [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "gdn_decode_prologue_verify": (_I, [_P, _P, _P, _P, _I64, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                         _P]),
+    "gdn_decode_layer": (_I, [_P, _P, _P, _P, _I64, _P, _P, _P, _I, _P, _I64, _P, _P, _F, _P, _I, _I, _I, _I, _F,
+                              _P]),
     "gdn_gated_rmsnorm": (_I, [_P, _P, _P, _F, _P, _I, _I, _I, _I, _P]),
     "gdn_chunk_fwd_kda_workspace_bytes": (ctypes.c_size_t, [_I, _I64, _I, _I]),
     "gdn_chunk_fwd_kda": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I, _P, _P, _P, ctypes.c_size_t,

@@ -389,6 +389,54 @@ def decode_prologue_verify(x: torch.Tensor, conv_w: torch.Tensor, conv_bias: Opt
     return q, k, v, beta
 
 
+def decode_layer(x: torch.Tensor, conv_w: torch.Tensor, conv_bias: Optional[torch.Tensor], conv_state: torch.Tensor,
+                 slots: torch.Tensor, beta_raw: torch.Tensor, g: torch.Tensor, state_pool: torch.Tensor, H: int, *,
+                 gate: Optional[torch.Tensor] = None, norm_w: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                 scale: Optional[float] = None, out_dtype: torch.dtype = torch.bfloat16,
+                 out: Optional[torch.Tensor] = None, stream=None):
+    """The decode layer in one launch (gdn_decode_layer): front operations, the
+    delta-rule update (g [N, H] scalar or [N, H, D] per-channel log-decays) and,
+    with norm_w, the gated RMSNorm. Returns out [N, H, D]."""
+    if x.dim() != 2 or x.shape[1] % (3 * H):
+        raise ValueError("x must be [N, 3 H D]")
+    N, C = x.shape
+    D = C // (3 * H)
+    if conv_w.shape != (3, 4, H * D) or conv_state.dim() != 3 or tuple(conv_state.shape[1:]) != (C, 3):
+        raise ValueError("conv_w must be [3, 4, H D] and conv_state [P, 3 H D, 3]")
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, D, D):
+        raise ValueError("state_pool must be [P, H, D, D]")
+    kda = g.dim() == 3
+    _shape(g, (N, H, D) if kda else (N, H), "g")
+    _shape(slots, (N,), "slots")
+    _shape(beta_raw, (N, H), "beta_raw")
+    _shape(out, (N, H, D), "out")
+    if norm_w is not None:
+        _shape(norm_w, (D,), "norm_w")
+        _shape(gate, (N, H * D), "gate")
+    _need(x, "x", torch.bfloat16)
+    _need(conv_w, "conv_w", torch.float32)
+    _need(conv_state, "conv_state", torch.bfloat16)
+    _need(slots, "slots", torch.int32)
+    _need(beta_raw, "beta_raw", torch.float32)
+    _need(g, "g", torch.float32)
+    _need(state_pool, "state_pool", torch.float32)
+    if conv_bias is not None:
+        _need(conv_bias, "conv_bias", torch.float32)
+        _shape(conv_bias, (C,), "conv_bias")
+    if norm_w is not None:
+        _need(norm_w, "norm_w", torch.float32)
+        _need(gate, "gate", torch.bfloat16)
+    if out is None:
+        out = torch.empty((N, H, D), dtype=out_dtype, device=x.device)
+    _need(out, "out", out_dtype)
+    st = _lib.lib().gdn_decode_layer(
+        _ptr(x), _ptr(conv_w), _ptr(conv_bias), _ptr(conv_state), conv_state.shape[0], _ptr(slots), _ptr(beta_raw),
+        _ptr(g), int(kda), _ptr(state_pool), state_pool.shape[0], _ptr(gate), _ptr(norm_w), float(eps), _ptr(out),
+        _dt(out.dtype), N, H, D, float(D ** -0.5 if scale is None else scale), _stream(stream))
+    _lib.check(st, "gdn_decode_layer")
+    return out
+
+
 def gated_rmsnorm(o: torch.Tensor, gate: torch.Tensor, norm_w: torch.Tensor, eps: float = 1e-6, *,
                   out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None, stream=None):
     """Gated RMSNorm of decode outputs (gdn_gated_rmsnorm): o float32 [N, H, D],

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgdn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["gdn_api.hip", "gdn_chunk.hip", "gdn_decode.hip", "gdn_fp8.hip", "gdn_layer.hip", "gdn_kda_chunk.hip", "gdn_probe.hip", "gdn_gate.hip"]
+SOURCES = ["gdn_api.hip", "gdn_chunk.hip", "gdn_decode.hip", "gdn_fp8.hip", "gdn_layer.hip", "gdn_kda_chunk.hip", "gdn_probe.hip", "gdn_gate.hip", "gdn_decode_layer.hip"]
 ARCH = "gfx950"
 
 

@@ -463,6 +463,49 @@ gdn_status gdn_decode_prologue_verify(const void* x, const float* conv_w, const 
   return hip_status(gdn::launch_decode_prologue_verify(a));
 }
 
+gdn_status gdn_decode_layer(const void* x, const float* conv_w, const float* conv_bias, void* conv_state,
+                            int64_t conv_slots, const int32_t* slots, const float* beta_raw, const float* g,
+                            int g_per_channel, float* state_pool, int64_t pool_slots, const void* gate,
+                            const float* norm_w, float eps, void* out, gdn_dtype out_dtype, int N, int H, int D,
+                            float scale, void* stream) {
+  if (D != 64 && D != 128) return GDN_EUNSUPPORTED;
+  if (!valid_dtype(out_dtype)) return GDN_EUNSUPPORTED;
+  if (N < 0 || H <= 0 || H > 65535 || static_cast<int64_t>(N) * H > INT32_MAX) return GDN_EINVAL;
+  if (norm_w && !(eps >= 0.f)) return GDN_EINVAL;
+  if (N == 0) return GDN_OK;
+  if (!x || !conv_w || !conv_state || !slots || !beta_raw || !g || !state_pool || !out || conv_slots <= 0 ||
+      pool_slots <= 0 || (norm_w && !gate))
+    return GDN_EINVAL;
+  if (!aligned(x, 2) || !aligned(conv_state, 2) || !aligned(conv_w, 4) || !aligned(slots, 4) ||
+      !aligned(beta_raw, 4) || !aligned(g, g_per_channel ? 16 : 4) || !aligned(state_pool, 16) ||
+      !aligned(out, dtype_bytes(out_dtype)) || (conv_bias && !aligned(conv_bias, 4)) ||
+      (norm_w && (!aligned(norm_w, 4) || !aligned(gate, 2))))
+    return GDN_EINVAL;
+  gdn::LayerArgs a{};
+  a.x = x;
+  a.conv_w = conv_w;
+  a.conv_bias = conv_bias;
+  a.conv_state = conv_state;
+  a.conv_slots = conv_slots;
+  a.slots = slots;
+  a.beta_raw = beta_raw;
+  a.g = g;
+  a.kda = g_per_channel != 0;
+  a.pool = state_pool;
+  a.pool_slots = pool_slots;
+  a.gate = gate;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.out = out;
+  a.out_f32 = out_dtype == GDN_F32;
+  a.N = N;
+  a.H = H;
+  a.D = D;
+  a.scale = scale;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(gdn::launch_decode_layer(a));
+}
+
 gdn_status gdn_gated_rmsnorm(const float* o, const void* gate, const float* norm_w, float eps, void* out, int N, int H,
                              int D, gdn_dtype out_dtype, void* stream) {
   if (D != 64 && D != 128) return GDN_EUNSUPPORTED;

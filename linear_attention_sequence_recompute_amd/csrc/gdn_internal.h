@@ -52,6 +52,28 @@ struct PrologueArgs {
   hipStream_t stream;
 };
 
+struct LayerArgs {
+  const void* x;            // [N, 3 H D] bf16
+  const float* conv_w;      // [3, 4, H D]
+  const float* conv_bias;   // [3 H D] or null
+  void* conv_state;         // [conv_slots, 3 H D, 3] bf16
+  int64_t conv_slots;
+  const int32_t* slots;     // [N]
+  const float* beta_raw;    // [N, H]
+  const float* g;           // [N, H] or, kda, [N, H, D] log-decays
+  bool kda;
+  float* pool;              // [pool_slots, H, D, D]
+  int64_t pool_slots;
+  const void* gate;         // [N, H D] bf16 (with norm_w)
+  const float* norm_w;      // [D], or null: the raw output
+  float eps;
+  void* out;                // [N, H, D]
+  bool out_f32;
+  int N, H, D;
+  float scale;
+  hipStream_t stream;
+};
+
 struct RmsNormArgs {
   const float* o;       // [N, H, D]
   const void* gate;     // [N, H D] bf16
@@ -167,6 +189,7 @@ hipError_t launch_fp8_quant(const Fp8Args& a);
 hipError_t launch_decode_prologue(const PrologueArgs& a);
 hipError_t launch_decode_prologue_verify(const PrologueArgs& a);
 hipError_t launch_gated_rmsnorm(const RmsNormArgs& a);
+hipError_t launch_decode_layer(const LayerArgs& a);
 hipError_t launch_chunk_fwd_kda(const KdaChunkArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 hipError_t launch_kda_gate(const GateArgs& a);

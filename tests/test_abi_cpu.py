@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     assert set(declared_functions([HEADER])) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
                                          "gdn_chunk_fwd_profiled", "gdn_chunk_fwd_noalloc", "gdn_recurrent_step",
                                          "gdn_recurrent_step_kda",
-                                         "gdn_recurrent_verify", "gdn_kda_gate", "gdn_fp8_quant", "gdn_decode_prologue", "gdn_decode_prologue_verify",
+                                         "gdn_recurrent_verify", "gdn_kda_gate", "gdn_fp8_quant", "gdn_decode_prologue", "gdn_decode_prologue_verify", "gdn_decode_layer",
                                          "gdn_gated_rmsnorm", "gdn_chunk_fwd_kda_workspace_bytes",
                                          "gdn_chunk_fwd_kda", "gdn_chunk_fwd_kda_profiled", "gdn_status_string"}
 
@@ -366,4 +366,22 @@ def test_decode_prologue_verify_validation():
     assert call(T=0) == EINVAL and call(T=9) == EINVAL and call(cols=3) == EINVAL
     assert call(acc=None) == EINVAL and call(pool=0) == EINVAL
     assert call(q=FAKE + 4) == EINVAL and call(st=FAKE + 1) == EINVAL
+    assert call(N=0) == _lib.GDN_OK
+
+
+def test_decode_layer_validation():
+    L = _lib.lib()
+    EINVAL, EUNS = _lib.GDN_EINVAL, _lib.GDN_EUNSUPPORTED
+
+    def call(**kw):
+        a = dict(x=FAKE, w=FAKE, bias=None, st=FAKE, cs=8, slots=FAKE, braw=FAKE, g=FAKE, kda=0, pool=FAKE, ps=8,
+                 gate=FAKE, nw=FAKE, eps=1e-6, out=FAKE, od=BF16, N=2, H=2, D=128)
+        a.update(kw)
+        return L.gdn_decode_layer(a["x"], a["w"], a["bias"], a["st"], a["cs"], a["slots"], a["braw"], a["g"], a["kda"],
+                                  a["pool"], a["ps"], a["gate"], a["nw"], a["eps"], a["out"], a["od"], a["N"], a["H"],
+                                  a["D"], 1.0, None)
+    assert call(D=96) == EUNS and call(od=7) == EUNS
+    assert call(H=0) == EINVAL and call(eps=-1.0) == EINVAL and call(eps=float("nan")) == EINVAL
+    assert call(gate=None) == EINVAL and call(pool=None) == EINVAL and call(cs=0) == EINVAL
+    assert call(kda=1, g=FAKE + 4) == EINVAL and call(pool=FAKE + 4) == EINVAL
     assert call(N=0) == _lib.GDN_OK

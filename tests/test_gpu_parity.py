@@ -975,3 +975,54 @@ def test_decode_layer_verify_composition():
     _print(f"[decode layer verify] max err/rms out={e_out:.2e} pool={e_st:.2e}")
     assert e_out <= TOL["f32"] and e_st <= TOL["f32"]
     assert bool((out[torch.from_numpy(~act).cuda()] == 0).all())
+
+
+# ---------------------------------------------------- the decode layer in one launch
+
+def _layer_fused_case(N, H, D, P, seed, kda, norm, n_padding, out_dtype="f32"):
+    li = layer_inputs(N=N, H=H, D=D, pool_slots=P, seed=seed, n_padding=n_padding)
+    rng = np.random.default_rng(seed + 1)
+    if kda:
+        g = channel_log_decay((N, H, D), seed + 2)
+    else:
+        g = round_to_f32(-np.log1p(np.exp(rng.standard_normal((N, H)) + 2.0)))
+    pool0 = round_to_f32(rng.normal(0.0, 0.1, (P, H, D, D)))
+    conv = dev(li.conv_state, torch.bfloat16)
+    pool = dev(pool0)
+    out = api.decode_layer(dev(li.x, torch.bfloat16), dev(li.conv_w), dev(li.conv_bias), conv,
+                           dev(li.slots, torch.int32), dev(li.beta_raw), dev(g), pool, H,
+                           gate=dev(li.gate, torch.bfloat16) if norm else None, norm_w=dev(li.norm_w) if norm else None,
+                           out_dtype=TORCH_DT[out_dtype])
+    torch.cuda.synchronize()
+    rq, rk, rv, rb, rst = oracle.decode_prologue(li.x, li.conv_w, li.conv_bias, li.conv_state, li.slots,
+                                                 li.beta_raw, H, D)
+    step = oracle.decode_step_kda if kda else oracle.decode_step
+    ro, rpool = step(rq, rk, rv, g, rb, pool0, li.slots, scale=D ** -0.5)
+    ref = oracle.gated_rmsnorm(ro, li.gate, li.norm_w, 1e-6) if norm else ro
+    act = li.slots > 0
+    e_out = max_err_over_rms(host(out)[act], ref[act])
+    e_st = max_err_over_rms(host(pool)[li.slots[act]], rpool[li.slots[act]])
+    return li, out, conv, pool, pool0, rst, e_out, e_st, act
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("norm", [False, True])
+def test_decode_layer_fused(D, kda, norm):
+    li, out, conv, pool, pool0, rst, e_out, e_st, act = _layer_fused_case(40, 3, D, 52, 400 + D + 2 * kda + norm, kda,
+                                                                          norm, n_padding=5)
+    _print(f"[decode layer fused D={D} kda={kda} norm={norm}] out {e_out:.2e} state {e_st:.2e}")
+    assert e_out <= TOL["f32"] and e_st <= TOL["f32"]
+    assert np.array_equal(host(conv), rst), "conv state differs"
+    assert bool((out[torch.from_numpy(~act).cuda()].view(torch.int32) == 0).all()), "padding rows not +0"
+    unused = np.setdiff1d(np.arange(pool.shape[0]), li.slots[act])
+    assert torch.equal(pool[torch.from_numpy(unused).cuda()], dev(pool0)[torch.from_numpy(unused).cuda()])
+
+
+def test_decode_layer_fused_config_full():
+    """N=256 requests, H=32 heads of 128, pool of 512 slots, 32 padding rows, per-channel
+    decays, gated RMSNorm, bf16 output (= RNE of the float32 output of the same call)."""
+    li, out, conv, pool, pool0, rst, e_out, e_st, act = _layer_fused_case(256, 32, 128, 512, 450, True, True, 32)
+    _print(f"[decode layer fused N256 H32] out {e_out:.2e} state {e_st:.2e}")
+    assert e_out <= TOL["f32"] and e_st <= TOL["f32"]
+    assert np.array_equal(host(conv), rst)
