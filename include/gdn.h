@@ -434,58 +434,70 @@ gdn_status gdn_decode_layer(const void* x, const float* conv_w, const float* con
                             gdn_dtype out_dtype, int N, int H, int D, float scale, void* stream);
 
 /*
- * Workspace bytes gdn_chunk_fwd_kda needs for B sequences of T tokens: per
- * (sequence, chunk of 64 tokens, head) (2 * 64 * 64 + 3 * 64 * K + K) float32.
- * Returns 0 for negative sizes, H outside [1, 65535] or K outside {64, 128}.
+ * Bytes of device workspace gdn_chunk_fwd_kda needs (an upper bound valid for
+ * every split of total_tokens into n_seqs sequences): per (chunk of 64 tokens,
+ * head) (2 * 64 * 64 + 3 * 64 * K + K) float32 of chunk operands, then the chunk
+ * schedule of a packed call. Returns 0 for invalid sizes.
  */
-size_t gdn_chunk_fwd_kda_workspace_bytes(int B, int64_t T, int H, int K);
+size_t gdn_chunk_fwd_kda_workspace_bytes(int n_seqs, int64_t total_tokens, int H, int K);
 
 /*
  * Chunked forward pass of the delta rule with a decay per key channel (vLLM
  * KdaSplit page, method `update`: each key column of the state is multiplied by
  * its own decay before the delta-rule write; here in the chunk form, chunks of 64
- * tokens) over B sequences of T tokens each.
+ * tokens) over n_seqs sequences packed into one token stream. Arguments as in
+ * gdn_chunk_fwd, except:
  *
- *  q, k      [B, T, H, K] in_dtype
- *  v         [B, T, H, V] in_dtype
- *  g         [B, T, H, K] float32   per-token, per-key-channel log-decays (<= 0),
- *                                   raw (the library sums them within each chunk)
- *  beta      [B, T, H] float32
- *  o         [B, T, H, V] out_dtype
- *  scale     multiplies q
- *  h0, ht    float32 [B, H, V, K] or NULL (zero start; no final state). ht may
- *            be h0 (updated in place).
- *  workspace device scratch of at least gdn_chunk_fwd_kda_workspace_bytes(B, T,
- *            H, K) bytes, 256-byte aligned; contents on entry are ignored.
+ *  g         float32 [total_tokens, H, K], 16-byte aligned: per-token,
+ *            per-key-channel log-decays (<= 0; -inf, a channel that forgets
+ *            everything, is accepted), raw (the library sums them within each
+ *            chunk)
+ *  q, k      16-byte aligned (read four channels at a time); v, o by their
+ *            element size; beta, states, pool and slots 4 bytes
+ *  workspace at least gdn_chunk_fwd_kda_workspace_bytes(n_seqs, total_tokens,
+ *            H, K) bytes, 256-byte aligned
+ *  V         a multiple of 16 in [16, 256]
  *
  * Per token: S <- S diag(exp(g_t)); delta = beta_t (v_t - S k_t);
- * S <- S + delta k_t^T; o_t = S (scale q_t). Results in float32; o in bfloat16 is
- * round-to-nearest-even of the float32 result. T == 0 passes h0 to ht.
- * Alignment: q, k and g 16 bytes (read four channels at a time); v, o by their
- * element size; beta, h0 and ht 4 bytes.
+ * S <- S + delta k_t^T; o_t = S (scale q_t). cu_seqlens (device) and
+ * cu_seqlens_host (host) give the sequence offsets, or are both NULL for
+ * n_seqs sequences of total_tokens / n_seqs tokens. States: h0 / ht float32
+ * [n_seqs, H, V, K] (NULL = zeros / not stored; ht may be h0), or a pool
+ * [pool_slots, H, V, K] with device int32 state_slots [n_seqs] (slot <= 0 or
+ * >= pool_slots: zero start, no write; active slots distinct), updated in place.
+ * Results in float32; o in bfloat16 is round-to-nearest-even of the float32
+ * result. An empty sequence passes its initial state to its final state.
  *
  * Returns GDN_EUNSUPPORTED for K outside {64, 128}, V not a multiple of 16 in
- * [16, 256] or an unknown dtype; GDN_EINVAL for B outside [0, 65535], T < 0, H
- * outside [1, 65535], a non-finite scale, a NULL input or output when T > 0, a
- * misaligned pointer, or sizes whose grid would not fit; GDN_EWORKSPACE for a
- * missing, small or misaligned workspace; GDN_OK without launching for B == 0;
- * GDN_EHIP if a launch fails.
+ * [16, 256] or an unknown dtype; GDN_EINVAL for n_seqs < 0, total_tokens < 0, H
+ * outside [1, 65535], a non-finite scale, inconsistent offsets or lengths, a
+ * NULL input or output when total_tokens > 0, a pool with h0 or ht, a misaligned
+ * pointer, or sizes whose grid would not fit; GDN_EWORKSPACE for a missing,
+ * small or misaligned workspace; GDN_OK without launching for n_seqs == 0 and
+ * total_tokens == 0; GDN_EHIP if a launch fails.
  */
 gdn_status gdn_chunk_fwd_kda(const void* q, const void* k, const void* v, const float* g,
-                             const float* beta, void* o, int B, int64_t T, int H, int K, int V,
-                             float scale, gdn_dtype in_dtype, gdn_dtype out_dtype, const float* h0,
-                             float* ht, void* workspace, size_t workspace_bytes, void* stream);
+                             const float* beta, void* o, int n_seqs, int64_t total_tokens, int H,
+                             int K, int V, float scale, gdn_dtype in_dtype, gdn_dtype out_dtype,
+                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                             const float* h0, float* ht, float* state_pool, int64_t pool_slots,
+                             const int32_t* state_slots, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /*
  * Diagnostic variant of gdn_chunk_fwd_kda for measurement: same arguments and
  * results; in addition it records three caller-created HIP events (hipEvent_t,
- * passed as void*) on `stream`: events[0] before the prep kernel, events[1]
- * after it, events[2] after the scan. GDN_EINVAL if events or one of them is NULL.
+ * passed as void*) on `stream`: events[0] before the first kernel, events[1]
+ * after the prep kernel, events[2] after the scan. GDN_EINVAL if events or one
+ * of them is NULL.
  */
 gdn_status gdn_chunk_fwd_kda_profiled(const void* q, const void* k, const void* v, const float* g,
-                                      const float* beta, void* o, int B, int64_t T, int H, int K,
-                                      int V, float scale, gdn_dtype in_dtype, gdn_dtype out_dtype,
-                                      const float* h0, float* ht, void* workspace,
+                                      const float* beta, void* o, int n_seqs, int64_t total_tokens,
+                                      int H, int K, int V, float scale, gdn_dtype in_dtype,
+                                      gdn_dtype out_dtype, const int32_t* cu_seqlens,
+                                      const int32_t* cu_seqlens_host, const float* h0, float* ht,
+                                      float* state_pool, int64_t pool_slots,
+                                      const int32_t* state_slots, void* workspace,
                                       size_t workspace_bytes, void* stream, void* const* events);
 
 /* Static, human-readable name of a status code. Never NULL. */

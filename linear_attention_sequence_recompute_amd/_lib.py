@@ -42,11 +42,11 @@ SIGNATURES = {
     "gdn_decode_layer": (_I, [_P, _P, _P, _P, _I64, _P, _P, _P, _I, _P, _I64, _P, _P, _F, _P, _I, _I, _I, _I, _F,
                               _P]),
     "gdn_gated_rmsnorm": (_I, [_P, _P, _P, _F, _P, _I, _I, _I, _I, _P]),
-    "gdn_chunk_fwd_kda_workspace_bytes": (ctypes.c_size_t, [_I, _I64, _I, _I]),
-    "gdn_chunk_fwd_kda": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I, _P, _P, _P, ctypes.c_size_t,
-                               _P]),
-    "gdn_chunk_fwd_kda_profiled": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I, _P, _P, _P,
-                                        ctypes.c_size_t, _P, _P]),
+    "gdn_chunk_fwd_kda_workspace_bytes": (_SZ, [_I, _I64, _I, _I]),
+    "gdn_chunk_fwd_kda": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I,
+                               _P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "gdn_chunk_fwd_kda_profiled": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I,
+                                        _P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P, _P]),
     "gdn_status_string": (ctypes.c_char_p, [_I]),
     # measurement probes (include/gdn_probe.h)
     "gdn_probe_mfma_bf16": (_I, [_P, _I, _I, _P]),

@@ -77,7 +77,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     (gdn_chunk_fwd_profiled).
     """
     return _chunk_call(q, k, v, g, beta, scale, cu_seqlens, cu_seqlens_dev, h0, output_final_state, ht, state_pool,
-                       state_slots, out_dtype, out, workspace, stream, events, noalloc=False)
+                       state_slots, out_dtype, out, workspace, stream, events, noalloc=False, kda=False)
 
 
 def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
@@ -96,11 +96,11 @@ def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
     if cu_seqlens is not None and cu_seqlens_dev is None:
         raise ValueError("chunk_fwd_noalloc needs cu_seqlens_dev with cu_seqlens")
     return _chunk_call(q, k, v, g, beta, scale, cu_seqlens, cu_seqlens_dev, h0, False, ht, state_pool, state_slots,
-                       out.dtype, out, None, stream, None, noalloc=True)
+                       out.dtype, out, None, stream, None, noalloc=True, kda=False)
 
 
 def _chunk_call(q, k, v, g, beta, scale, cu_seqlens, cu_seqlens_dev, h0, output_final_state, ht, state_pool,
-                state_slots, out_dtype, out, workspace, stream, events, noalloc):
+                state_slots, out_dtype, out, workspace, stream, events, noalloc, kda):
     H, K = q.shape[-2], q.shape[-1]
     V = v.shape[-1]
     if q.dim() == 4:
@@ -112,7 +112,8 @@ def _chunk_call(q, k, v, g, beta, scale, cu_seqlens, cu_seqlens_dev, h0, output_
         n_seqs = 1 if cu_seqlens is None else len(cu_seqlens) - 1
     else:
         raise ValueError("q must be [B, T, H, K] or [Ttot, H, K]")
-    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or g.shape != q.shape[:-1] or beta.shape != g.shape:
+    g_shape = q.shape if kda else q.shape[:-1]
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or g.shape != g_shape or beta.shape != q.shape[:-1]:
         raise ValueError("inconsistent shapes of q, k, v, g, beta")
     if cu_seqlens is not None and n_seqs < 1:
         raise ValueError("cu_seqlens needs at least two offsets")
@@ -167,18 +168,21 @@ def _chunk_call(q, k, v, g, beta, scale, cu_seqlens, cu_seqlens_dev, h0, output_
             float(K ** -0.5 if scale is None else scale), _dt(in_dt), _dt(out_dtype),
             _ptr(cu_dev), None if cu_host is None else cu_host.data_ptr(),
             _ptr(h0), _ptr(ht), _ptr(state_pool), pool_slots, _ptr(state_slots))
+    L = _lib.lib()
     if noalloc:
-        _lib.check(_lib.lib().gdn_chunk_fwd_noalloc(*args, _stream(stream)), "gdn_chunk_fwd_noalloc")
+        _lib.check(L.gdn_chunk_fwd_noalloc(*args, _stream(stream)), "gdn_chunk_fwd_noalloc")
         return out, ht
-    need = workspace_bytes(n_seqs, total, H, K, V, in_dt)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    args = args + (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
-    if events is None:
-        st = _lib.lib().gdn_chunk_fwd(*args)
+    if kda:
+        need, fn, fn_prof, name = (int(L.gdn_chunk_fwd_kda_workspace_bytes(n_seqs, total, H, K)), L.gdn_chunk_fwd_kda,
+                                   L.gdn_chunk_fwd_kda_profiled, "gdn_chunk_fwd_kda")
     else:
-        st = _lib.lib().gdn_chunk_fwd_profiled(*args, (ctypes.c_void_p * 3)(*events))
-    _lib.check(st, "gdn_chunk_fwd")
+        need, fn, fn_prof, name = (workspace_bytes(n_seqs, total, H, K, V, in_dt), L.gdn_chunk_fwd,
+                                   L.gdn_chunk_fwd_profiled, "gdn_chunk_fwd")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    args = args + (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    st = fn(*args) if events is None else fn_prof(*args, (ctypes.c_void_p * 3)(*events))
+    _lib.check(st, name)
     return out, ht
 
 
@@ -457,51 +461,15 @@ def gated_rmsnorm(o: torch.Tensor, gate: torch.Tensor, norm_w: torch.Tensor, eps
 
 
 def chunk_fwd_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
-                  scale: Optional[float] = None, h0: Optional[torch.Tensor] = None, output_final_state: bool = True,
-                  ht: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
-                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
-                  events: Optional[Sequence[int]] = None):
-    """Chunked forward with a decay per key channel (gdn_chunk_fwd_kda) over B
-    equal-length sequences: q, k [B, T, H, K] (or [T, H, K]); v [.., V]; g float32
-    [B, T, H, K] per-channel log-decays; beta float32 [B, T, H]; h0 float32
-    [B, H, V, K] or None. Returns (o [B, T, H, V], ht or None)."""
-    squeeze = q.dim() == 3
-    if squeeze:
-        q, k, v, g, beta = (x.unsqueeze(0) for x in (q, k, v, g, beta))
-    B, T, H, K = q.shape
-    V = v.shape[-1]
-    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != (B, T, H) or beta.shape != (B, T, H):
-        raise ValueError("inconsistent shapes of q, k, v, g, beta")
-    _shape(out, (B, T, H, V), "out")
-    _shape(h0, (B, H, V, K), "h0")
-    _shape(ht, (B, H, V, K), "ht")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _need(t, name, q.dtype)
-    _need(g, "g", torch.float32)
-    _need(beta, "beta", torch.float32)
-    out_dtype = out_dtype or q.dtype
-    if out is None:
-        out = torch.empty((B, T, H, V), dtype=out_dtype, device=q.device)
-    _need(out, "out", out_dtype)
-    if h0 is not None:
-        _need(h0, "h0", torch.float32)
-        if h0.shape != (B, H, V, K):
-            raise ValueError("h0 must be [B, H, V, K]")
-    if output_final_state and ht is None:
-        ht = torch.empty((B, H, V, K), dtype=torch.float32, device=q.device)
-    if ht is not None:
-        _need(ht, "ht", torch.float32)
-    need = int(_lib.lib().gdn_chunk_fwd_kda_workspace_bytes(B, T, H, K))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(out), B, T, H, K, V,
-            float(K ** -0.5 if scale is None else scale), _dt(q.dtype), _dt(out_dtype), _ptr(h0), _ptr(ht),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
-    if events is None:
-        st = _lib.lib().gdn_chunk_fwd_kda(*args)
-    else:
-        st = _lib.lib().gdn_chunk_fwd_kda_profiled(*args, (ctypes.c_void_p * 3)(*events))
-    _lib.check(st, "gdn_chunk_fwd_kda")
-    if squeeze:
-        out = out.squeeze(0)
-    return out, ht
+                  scale: Optional[float] = None, cu_seqlens: Optional[Sequence[int]] = None,
+                  cu_seqlens_dev: Optional[torch.Tensor] = None, h0: Optional[torch.Tensor] = None,
+                  output_final_state: bool = True, ht: Optional[torch.Tensor] = None,
+                  state_pool: Optional[torch.Tensor] = None, state_slots: Optional[torch.Tensor] = None,
+                  out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None, events: Optional[Sequence[int]] = None):
+    """Chunked forward with a decay per key channel (gdn_chunk_fwd_kda): as
+    ``chunk_fwd`` (B equal-length sequences [B, T, ...] or a packed stream with
+    ``cu_seqlens``; h0 / ht or a state pool) but g is float32 [..., H, K], the
+    per-token, per-channel log-decays. Returns (o, ht)."""
+    return _chunk_call(q, k, v, g, beta, scale, cu_seqlens, cu_seqlens_dev, h0, output_final_state, ht, state_pool,
+                       state_slots, out_dtype, out, workspace, stream, events, noalloc=False, kda=True)

@@ -530,31 +530,53 @@ gdn_status gdn_gated_rmsnorm(const float* o, const void* gate, const float* norm
 }
 
 
-size_t gdn_chunk_fwd_kda_workspace_bytes(int B, int64_t T, int H, int K) {
-  if (B < 0 || T < 0 || H <= 0 || H > 65535 || (K != 64 && K != 128)) return 0;
-  return static_cast<size_t>(gdn::kda_workspace_floats(B, T, H, K)) * sizeof(float);
+size_t gdn_chunk_fwd_kda_workspace_bytes(int n_seqs, int64_t total_tokens, int H, int K) {
+  if (n_seqs < 0 || total_tokens < 0 || H <= 0 || H > 65535 || (K != 64 && K != 128)) return 0;
+  return gdn::kda_workspace_bytes(max_chunks(n_seqs, total_tokens), n_seqs, H, K);
 }
 
 static gdn_status chunk_fwd_kda_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                                     void* o, int B, int64_t T, int H, int K, int V, float scale, gdn_dtype in_dtype,
-                                     gdn_dtype out_dtype, const float* h0, float* ht, void* workspace,
+                                     void* o, int n_seqs, int64_t total_tokens, int H, int K, int V, float scale,
+                                     gdn_dtype in_dtype, gdn_dtype out_dtype, const int32_t* cu_seqlens,
+                                     const int32_t* cu_seqlens_host, const float* h0, float* ht, float* state_pool,
+                                     int64_t pool_slots, const int32_t* state_slots, void* workspace,
                                      size_t workspace_bytes, void* stream, void* const* events) {
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || (K != 64 && K != 128) || V % 16 != 0 || V < 16 ||
       V > 256)
     return GDN_EUNSUPPORTED;
-  if (B < 0 || B > 65535 || T < 0 || H <= 0 || H > 65535 || !std::isfinite(scale)) return GDN_EINVAL;
-  const int64_t NC = (T + 63) / 64;
-  if (static_cast<int64_t>(B) * NC > INT32_MAX || T > INT32_MAX ||
-      (static_cast<int64_t>(B) * H + 7) / 8 * 8 * (V / 16) > INT32_MAX)
-    return GDN_EINVAL;
-  if (B == 0) return GDN_OK;
-  if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_EINVAL;
+  if (n_seqs < 0 || total_tokens < 0 || H <= 0 || H > 65535 || !std::isfinite(scale)) return GDN_EINVAL;
+  if (total_tokens > INT_MAX - 2 * kChunkTokens) return GDN_EINVAL;
+  if (n_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_EINVAL;
+  if ((cu_seqlens == nullptr) != (cu_seqlens_host == nullptr)) return GDN_EINVAL;
+  if ((static_cast<int64_t>(n_seqs) * H + 7) / 8 * 8 * (V / 16) > INT32_MAX) return GDN_EINVAL;
+  int64_t n_chunks = 0;
+  int T_eq = 0;
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] != 0 || cu_seqlens_host[n_seqs] != total_tokens) return GDN_EINVAL;
+    for (int s = 0; s < n_seqs; ++s) {
+      const int64_t len = static_cast<int64_t>(cu_seqlens_host[s + 1]) - cu_seqlens_host[s];
+      if (len < 0) return GDN_EINVAL;
+      n_chunks += (len + kChunkTokens - 1) / kChunkTokens;
+    }
+  } else {
+    if (total_tokens % n_seqs != 0) return GDN_EINVAL;
+    T_eq = static_cast<int>(total_tokens / n_seqs);
+    n_chunks = static_cast<int64_t>(n_seqs) * ((T_eq + kChunkTokens - 1) / kChunkTokens);
+  }
+  if (n_chunks > INT_MAX) return GDN_EINVAL;
+  if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_EINVAL;
   const size_t in_b = dtype_bytes(in_dtype), out_b = dtype_bytes(out_dtype);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, in_b) || !aligned(g, 16) || !aligned(beta, 4) ||
-      !aligned(o, out_b) || !aligned(h0, 4) || !aligned(ht, 4))
+      !aligned(o, out_b))
     return GDN_EINVAL;
-  const size_t need = gdn_chunk_fwd_kda_workspace_bytes(B, T, H, K);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return GDN_EWORKSPACE;
+  if (state_pool) {
+    if (h0 || ht || !state_slots || pool_slots <= 0 || !aligned(state_pool, 4) || !aligned(state_slots, 4))
+      return GDN_EINVAL;
+  } else {
+    if (state_slots || !aligned(h0, 4) || !aligned(ht, 4)) return GDN_EINVAL;
+  }
+  const size_t need = gdn_chunk_fwd_kda_workspace_bytes(n_seqs, total_tokens, H, K);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return GDN_EWORKSPACE;
   gdn::KdaChunkArgs a{};
   a.q = q;
   a.k = k;
@@ -562,36 +584,47 @@ static gdn_status chunk_fwd_kda_impl(const void* q, const void* k, const void* v
   a.g = g;
   a.beta = beta;
   a.o = o;
-  a.B = B;
-  a.T = T;
+  a.n_seqs = n_seqs;
+  a.total_tokens = total_tokens;
   a.H = H;
   a.K = K;
   a.V = V;
   a.scale = scale;
   a.in_f32 = in_dtype == GDN_F32;
   a.out_f32 = out_dtype == GDN_F32;
+  a.cu_seqlens = cu_seqlens;
+  a.n_chunks = n_chunks;
+  a.T_eq = T_eq;
   a.h0 = h0;
   a.ht = ht;
-  a.ws = static_cast<float*>(workspace);
+  a.pool = state_pool;
+  a.pool_slots = pool_slots;
+  a.slots = state_slots;
+  a.ws = workspace;
   a.stream = static_cast<hipStream_t>(stream);
   for (int i = 0; i < 3; ++i) a.events[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
   return hip_status(gdn::launch_chunk_fwd_kda(a));
 }
 
 gdn_status gdn_chunk_fwd_kda(const void* q, const void* k, const void* v, const float* g, const float* beta, void* o,
-                             int B, int64_t T, int H, int K, int V, float scale, gdn_dtype in_dtype,
-                             gdn_dtype out_dtype, const float* h0, float* ht, void* workspace,
-                             size_t workspace_bytes, void* stream) {
-  return chunk_fwd_kda_impl(q, k, v, g, beta, o, B, T, H, K, V, scale, in_dtype, out_dtype, h0, ht, workspace,
+                             int n_seqs, int64_t total_tokens, int H, int K, int V, float scale, gdn_dtype in_dtype,
+                             gdn_dtype out_dtype, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                             const float* h0, float* ht, float* state_pool, int64_t pool_slots,
+                             const int32_t* state_slots, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_fwd_kda_impl(q, k, v, g, beta, o, n_seqs, total_tokens, H, K, V, scale, in_dtype, out_dtype,
+                            cu_seqlens, cu_seqlens_host, h0, ht, state_pool, pool_slots, state_slots, workspace,
                             workspace_bytes, stream, nullptr);
 }
 
 gdn_status gdn_chunk_fwd_kda_profiled(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                                      void* o, int B, int64_t T, int H, int K, int V, float scale,
-                                      gdn_dtype in_dtype, gdn_dtype out_dtype, const float* h0, float* ht,
+                                      void* o, int n_seqs, int64_t total_tokens, int H, int K, int V, float scale,
+                                      gdn_dtype in_dtype, gdn_dtype out_dtype, const int32_t* cu_seqlens,
+                                      const int32_t* cu_seqlens_host, const float* h0, float* ht,
+                                      float* state_pool, int64_t pool_slots, const int32_t* state_slots,
                                       void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
   if (!events || !events[0] || !events[1] || !events[2]) return GDN_EINVAL;
-  return chunk_fwd_kda_impl(q, k, v, g, beta, o, B, T, H, K, V, scale, in_dtype, out_dtype, h0, ht, workspace,
+  return chunk_fwd_kda_impl(q, k, v, g, beta, o, n_seqs, total_tokens, H, K, V, scale, in_dtype, out_dtype,
+                            cu_seqlens, cu_seqlens_host, h0, ht, state_pool, pool_slots, state_slots, workspace,
                             workspace_bytes, stream, events);
 }
 

@@ -86,6 +86,12 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict
   if (tid == 0) seq_chunk0[n_seqs] = carry;
 }
 
+hipError_t launch_chunk_schedule(const int32_t* cu, int n_seqs, int total_tokens, int cap, int* seq_chunk0,
+                                 int4* info, hipStream_t stream) {
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(256), 0, stream, cu, n_seqs, total_tokens, cap, seq_chunk0, info);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // chunk_fwd_h with chunk_fwd_o fused: sequential over the chunks of one
 // sequence, for one head and one slice of 16 value columns. Three waves:

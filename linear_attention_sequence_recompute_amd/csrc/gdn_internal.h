@@ -86,22 +86,30 @@ struct RmsNormArgs {
 };
 
 struct KdaChunkArgs {
-  const void *q, *k, *v;  // [B, T, H, K] / [B, T, H, V]
-  const float* g;         // [B, T, H, K] per-channel log-decays
-  const float* beta;      // [B, T, H]
-  void* o;                // [B, T, H, V]
-  int B;
-  int64_t T;
+  const void *q, *k, *v;  // [Ttot, H, K] / [Ttot, H, V]
+  const float* g;         // [Ttot, H, K] per-channel log-decays
+  const float* beta;      // [Ttot, H]
+  void* o;                // [Ttot, H, V]
+  int n_seqs;
+  int64_t total_tokens;
   int H, K, V;
   float scale;
   bool in_f32, out_f32;
-  const float* h0;  // [B, H, V, K] or null
-  float* ht;        // [B, H, V, K] or null
-  float* ws;        // kda_workspace_floats(B, T, H, K) floats
+  const int32_t* cu_seqlens;  // device, or null for equal lengths
+  int64_t n_chunks;           // total chunks over all sequences
+  int T_eq;                   // equal-length mode: tokens per sequence
+  const float* h0;  // [n_seqs, H, V, K] or null
+  float* ht;        // [n_seqs, H, V, K] or null
+  float* pool;      // [pool_slots, H, V, K] or null (then h0 / ht)
+  int64_t pool_slots;
+  const int32_t* slots;  // [n_seqs]
+  void* ws;              // kda_workspace_bytes(...) bytes
   hipStream_t stream;
   hipEvent_t events[3];  // optional: before prep, after prep, after the scan
 };
-int64_t kda_workspace_floats(int B, int64_t T, int H, int K);
+size_t kda_workspace_bytes(int64_t max_chunks, int n_seqs, int H, int K);
+hipError_t launch_chunk_schedule(const int32_t* cu, int n_seqs, int total_tokens, int cap, int* seq_chunk0,
+                                 int4* info, hipStream_t stream);
 
 struct GateArgs {
   const void* f_a;      // [N, 128] bf16

@@ -57,11 +57,31 @@ __host__ __device__ constexpr int64_t kda_floats_per_chunk(int K) { return 2 * 6
 
 constexpr float kMinLogDecay = -100.f;  // per token and channel
 
+// Chunk c (global index over the packed sequences) of head h: first token t0 and
+// n rows. Packed calls read the schedule (info); an entry that does not fit the
+// token stream marks an empty chunk, whose workspace no scan reads.
+struct KdaChunkGeo {
+  const int4* info;
+  int T_eq, ncs_eq, total_tokens;
+  __device__ bool at(int c, int& t0, int& n) const {
+    if (info) {
+      const int4 ci = info[c];
+      t0 = ci.y;
+      n = ci.z;
+      return ci.x >= 0 && n > 0 && n <= 64 && t0 >= 0 && t0 <= total_tokens - n;
+    }
+    const int s = c / ncs_eq, j = c % ncs_eq;
+    t0 = s * T_eq + 64 * j;
+    n = min(64, T_eq - 64 * j);
+    return n > 0;
+  }
+};
+
 template <int K, typename Tin>
 __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                                                                const float* __restrict__ g,
                                                                const float* __restrict__ beta,
-                                                               float* __restrict__ ws, int T, int H, int NC,
+                                                               float* __restrict__ ws, KdaChunkGeo geo, int H,
                                                                float scale) {
   constexpr int LD = K + 4;  // row stride: rows read at the same column fall in different banks
   __shared__ __attribute__((aligned(16))) float sQ[64 * LD];
@@ -71,8 +91,9 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(const Tin* __res
   __shared__ float sA[64][65];
   __shared__ float sX[16][65];  // the earlier blocks' part of a block row of A
   __shared__ float sB[64];
-  const int b = blockIdx.x / NC, c = blockIdx.x % NC, h = blockIdx.y;
-  const int t0 = c * 64, n = min(64, T - t0);
+  const int h = blockIdx.y;
+  int t0, n;
+  if (!geo.at(blockIdx.x, t0, n)) return;
   const int tid = threadIdx.x;
   float* base = ws + (static_cast<int64_t>(blockIdx.x) * H + h) * kda_floats_per_chunk(K);
   float *Ap = base, *P = base + 4096, *Kg = base + 8192, *Qg = Kg + 64 * K, *Kd = Qg + 64 * K, *gL = Kd + 64 * K;
@@ -85,12 +106,12 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(const Tin* __res
 #pragma unroll
   for (int m = 0; m < G4; ++m) {
     const int e = tid + kPrepThreads * m, i = e / (K / 4), c4 = 4 * (e % (K / 4));
-    const int64_t idx = ((static_cast<int64_t>(b) * T + t0 + min(i, n - 1)) * H + h) * K + c4;
+    const int64_t idx = ((static_cast<int64_t>(t0) + min(i, n - 1)) * H + h) * K + c4;
     lq[m] = ld_in4(q + idx);
     lk[m] = ld_in4(k + idx);
     lg[m] = *reinterpret_cast<const float4*>(g + idx);
   }
-  const float bt = beta[(static_cast<int64_t>(b) * T + t0 + min(tid & 63, n - 1)) * H + h];
+  const float bt = beta[(static_cast<int64_t>(t0) + min(tid & 63, n - 1)) * H + h];
 #pragma unroll
   for (int m = 0; m < G4; ++m) {
     const int e = tid + kPrepThreads * m, i = e / (K / 4), c4 = 4 * (e % (K / 4));
@@ -335,39 +356,82 @@ __device__ __forceinline__ void kda_stage(const KdaPf<K>& pf, KdaScanLds<K>& sm,
 // token rows 16 w .. 16 w + 15 of R, D and o, and K / 64 of the state's 16-key
 // tiles. The next chunk's operands are loaded into registers while this one is
 // computed.
+// Arguments of the scan: the sequences (packed with cu_seqlens and the chunk
+// schedule, or of equal length T_eq) and where their states live.
+struct KdaScanArgs {
+  const float* h0;  // may alias ht (in place)
+  float* ht;
+  float* pool;
+  int64_t pool_slots;
+  const int32_t* slots;
+  int H, V, n_seqs, T_eq, ncs_eq, total_tokens, n_chunks;
+  const int32_t* cu;
+  const int* seq_chunk0;
+};
+
 template <int K, typename Tin, typename Tout>
 __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __restrict__ v, const float* __restrict__ ws,
-                                                               const float* h0, float* ht, Tout* __restrict__ o,
-                                                               int T, int H, int V, int NC, int n_pairs) {
+                                                               Tout* __restrict__ o, KdaScanArgs a) {
   using L = KdaScanLds<K>;
   __shared__ __attribute__((aligned(16))) L sm;
+  const int H = a.H, V = a.V;
   // Workgroups are dealt to the 8 XCDs round-robin by id: the slices of one
   // (sequence, head) pair get ids of one residue mod 8, so they share an XCD and
   // its L2, which then serves their common reads of the chunk operands.
   const int n_slices = V / kKdaSlice, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
   const int pair = (idx / n_slices) * 8 + xcd;
-  if (pair >= n_pairs) return;  // padding of the grid to whole rounds of 8
-  const int h = pair % H, b = pair / H;
+  if (pair >= a.n_seqs * H) return;  // padding of the grid to whole rounds of 8
+  const int h = pair % H, seq = pair / H;
+  // the sequence's tokens and chunks (a packed call whose offsets do not fit the
+  // token stream or the chunk count gets an empty sequence)
+  int start, len, chunk0;
+  if (a.cu) {
+    start = a.cu[seq];
+    len = a.cu[seq + 1] - start;
+    chunk0 = a.seq_chunk0[seq];
+    if (start < 0 || len < 0 || start > a.total_tokens - len || chunk0 < 0 ||
+        chunk0 > a.n_chunks - (len + 63) / 64)
+      len = 0;
+  } else {
+    start = seq * a.T_eq;
+    len = a.T_eq;
+    chunk0 = seq * a.ncs_eq;
+  }
+  const int NC = (len + 63) / 64;
   const int v_base = (idx % n_slices) * kKdaSlice;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-  const int64_t st_base = (static_cast<int64_t>(b) * H + h) * V + v_base;  // state [.., V, K] rows of this slice
+  // the state pages: a pool slot (<= 0 or past the pool: zero start, no write) or h0 / ht
+  const int64_t page = static_cast<int64_t>(V) * K;
+  const float* st_in = nullptr;
+  float* st_out = nullptr;
+  if (a.pool) {
+    const int sl = a.slots[seq];
+    if (sl > 0 && sl < a.pool_slots) {
+      st_in = a.pool + (static_cast<int64_t>(sl) * H + h) * page;
+      st_out = a.pool + (static_cast<int64_t>(sl) * H + h) * page;
+    }
+  } else {
+    if (a.h0) st_in = a.h0 + (static_cast<int64_t>(seq) * H + h) * page;
+    if (a.ht) st_out = a.ht + (static_cast<int64_t>(seq) * H + h) * page;
+  }
+  const int64_t st_row = static_cast<int64_t>(v_base) * K;  // this slice's rows [.., V, K]
   for (int e = tid; e < K * kKdaSlice; e += kKdaThreads) {
     const int cc = e % K, vv = e / K;
-    sm.hT[vv * L::LDX + cc] = h0 ? h0[(st_base + vv) * K + cc] : 0.f;
+    sm.hT[vv * L::LDX + cc] = st_in ? st_in[st_row + vv * K + cc] : 0.f;
   }
   const int64_t per = kda_floats_per_chunk(K);
-  const float* ws_bh = ws + (static_cast<int64_t>(b) * NC * H + h) * per;  // chunk c at + c * H * per
+  const float* ws_bh = ws + (static_cast<int64_t>(chunk0) * H + h) * per;  // chunk c at + c * H * per
   // The next chunk's operands, loaded while this one is computed.
   KdaPf<K> pf;
   Tin vr[4];
   auto load_v = [&](int ch) __attribute__((always_inline)) {  // lane's V values: rows 16 w + 4 g + r, column c
-    const int t0 = ch * 64, n = min(64, T - t0);
+    const int t0 = ch * 64, n = min(64, len - t0);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       // Rows past the end read the last row and are zeroed where used: a load
       // under a branch would be waited for at once, and with it the prefetch.
       const int ic = min(16 * w + 4 * g + r, n - 1);
-      vr[r] = v[((static_cast<int64_t>(b) * T + t0 + ic) * H + h) * V + v_base + c];
+      vr[r] = v[((static_cast<int64_t>(start) + t0 + ic) * H + h) * V + v_base + c];
     }
   };
   if (NC > 0) {
@@ -375,7 +439,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __rest
     load_v(0);
   }
   for (int ch = 0; ch < NC; ++ch) {
-    const int t0 = ch * 64, n = min(64, T - t0);
+    const int t0 = ch * 64, n = min(64, len - t0);
     __syncthreads();  // the previous chunk is done with the operands and the state
     kda_stage<K>(pf, sm, tid);
     float vcur[4];
@@ -420,7 +484,7 @@ __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __rest
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * w + 4 * g + r;
-      if (i < n) store_out(o + ((static_cast<int64_t>(b) * T + t0 + i) * H + h) * V + v_base + c, acc[r]);
+      if (i < n) store_out(o + ((static_cast<int64_t>(start) + t0 + i) * H + h) * V + v_base + c, acc[r]);
     }
     __syncthreads();  // every wave has read the state
     // h' = diag(e^{G_last}) h + (K o e^{G_last - G})^T D, 16 keys at a time:
@@ -443,36 +507,50 @@ __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __rest
     }
   }
   __syncthreads();
-  if (ht)
+  if (st_out)
     for (int e = tid; e < K * kKdaSlice; e += kKdaThreads) {
       const int cc = e % K, vv = e / K;
-      ht[(st_base + vv) * K + cc] = sm.hT[vv * L::LDX + cc];
+      st_out[st_row + vv * K + cc] = sm.hT[vv * L::LDX + cc];
     }
 }
 
-int64_t kda_workspace_floats(int B, int64_t T, int H, int K) {
-  const int64_t NC = (T + 63) / 64;
-  return static_cast<int64_t>(B) * NC * H * kda_floats_per_chunk(K);
+// Workspace: the chunk operands per (chunk, head), then the chunk schedule of
+// a packed call (16 bytes per chunk, 4 per sequence and one more).
+static size_t kda_ops_bytes(int64_t max_chunks, int H, int K) {
+  return (static_cast<size_t>(max_chunks) * H * kda_floats_per_chunk(K) * 4 + 255) & ~static_cast<size_t>(255);
+}
+size_t kda_workspace_bytes(int64_t max_chunks, int n_seqs, int H, int K) {
+  return kda_ops_bytes(max_chunks, H, K) + static_cast<size_t>(max_chunks) * 16 +
+         static_cast<size_t>(n_seqs + 1) * 4;
 }
 
 template <int K, typename Tin>
 static void launch_kda_typed(const KdaChunkArgs& a) {
-  const int NC = static_cast<int>((a.T + 63) / 64);
-  if (NC > 0)
-    hipLaunchKernelGGL((kda_prep_kernel<K, Tin>), dim3(a.B * NC, a.H), dim3(kPrepThreads), 0, a.stream,
-                       static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), a.g, a.beta, a.ws,
-                       static_cast<int>(a.T), a.H, NC, a.scale);
+  const bool varlen = a.cu_seqlens != nullptr;
+  const int ncs_eq = varlen ? 0 : (a.T_eq + 63) / 64;
+  float* ops = static_cast<float*>(a.ws);
+  char* sched = static_cast<char*>(a.ws) + kda_ops_bytes(a.n_chunks, a.H, K);
+  int4* info = reinterpret_cast<int4*>(sched);
+  int* seq_chunk0 = reinterpret_cast<int*>(sched + a.n_chunks * 16);
+  if (varlen)
+    (void)launch_chunk_schedule(a.cu_seqlens, a.n_seqs, static_cast<int>(a.total_tokens),
+                                static_cast<int>(a.n_chunks), seq_chunk0, info, a.stream);
+  if (a.n_chunks > 0)
+    hipLaunchKernelGGL((kda_prep_kernel<K, Tin>), dim3(static_cast<unsigned>(a.n_chunks), a.H), dim3(kPrepThreads), 0,
+                       a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), a.g, a.beta, ops,
+                       KdaChunkGeo{varlen ? info : nullptr, a.T_eq, ncs_eq, static_cast<int>(a.total_tokens)}, a.H,
+                       a.scale);
   if (a.events[1]) (void)hipEventRecord(a.events[1], a.stream);
-  const int n_pairs = a.B * a.H;
+  KdaScanArgs sa{a.h0, a.ht, a.pool, a.pool_slots, a.slots, a.H, a.V, a.n_seqs, a.T_eq, ncs_eq,
+                 static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens, seq_chunk0};
+  const int64_t n_pairs = static_cast<int64_t>(a.n_seqs) * a.H;
   const dim3 grid(static_cast<unsigned>((n_pairs + 7) / 8) * 8 * (a.V / kKdaSlice));
   if (a.out_f32)
     hipLaunchKernelGGL((kda_scan_kernel<K, Tin, float>), grid, dim3(kKdaThreads), 0, a.stream,
-                       static_cast<const Tin*>(a.v), a.ws, a.h0, a.ht, static_cast<float*>(a.o),
-                       static_cast<int>(a.T), a.H, a.V, NC, n_pairs);
+                       static_cast<const Tin*>(a.v), ops, static_cast<float*>(a.o), sa);
   else
     hipLaunchKernelGGL((kda_scan_kernel<K, Tin, __bf16>), grid, dim3(kKdaThreads), 0, a.stream,
-                       static_cast<const Tin*>(a.v), a.ws, a.h0, a.ht, static_cast<__bf16*>(a.o),
-                       static_cast<int>(a.T), a.H, a.V, NC, n_pairs);
+                       static_cast<const Tin*>(a.v), ops, static_cast<__bf16*>(a.o), sa);
 }
 
 hipError_t launch_chunk_fwd_kda(const KdaChunkArgs& a) {

@@ -266,23 +266,28 @@ def test_gated_rmsnorm_validation():
 def test_chunk_fwd_kda_validation():
     E = _lib
     L = _lib.lib()
-    assert L.gdn_chunk_fwd_kda_workspace_bytes(1, 4096, 16, 128) == 64 * 16 * (2 * 4096 + 3 * 64 * 128 + 128) * 4
-    assert L.gdn_chunk_fwd_kda_workspace_bytes(2, 65, 3, 64) == 2 * 2 * 3 * (2 * 4096 + 3 * 64 * 64 + 64) * 4
+    # chunk operands for floor(T / 64) + n_seqs chunks, then the packed schedule (16 B per chunk, 4 B per offset)
+    ops = (64 + 1) * 16 * (2 * 4096 + 3 * 64 * 128 + 128) * 4
+    assert L.gdn_chunk_fwd_kda_workspace_bytes(1, 4096, 16, 128) == (ops + 255) // 256 * 256 + 65 * 16 + 2 * 4
     assert L.gdn_chunk_fwd_kda_workspace_bytes(1, 100, 2, 96) == 0
-    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE, B=2, T=100, H=2, K=128, V=128, scale=1.0,
-                in_dt=BF16, out_dt=BF16, h0=None, ht=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    assert L.gdn_chunk_fwd_kda_workspace_bytes(-1, 100, 2, 64) == 0
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE, n=2, total=200, H=2, K=128, V=128, scale=1.0,
+                in_dt=BF16, out_dt=BF16, cu=None, cu_host=None, h0=None, ht=None, pool=None, pool_slots=0,
+                slots=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
 
     def call(**kw):
         a = dict(args, **kw)
-        return L.gdn_chunk_fwd_kda(a["q"], a["k"], a["v"], a["g"], a["beta"], a["o"], a["B"], a["T"], a["H"],
-                                   a["K"], a["V"], a["scale"], a["in_dt"], a["out_dt"], a["h0"], a["ht"], a["ws"],
-                                   a["ws_bytes"], a["stream"])
+        return L.gdn_chunk_fwd_kda(a["q"], a["k"], a["v"], a["g"], a["beta"], a["o"], a["n"], a["total"], a["H"],
+                                   a["K"], a["V"], a["scale"], a["in_dt"], a["out_dt"], a["cu"], a["cu_host"], a["h0"],
+                                   a["ht"], a["pool"], a["pool_slots"], a["slots"], a["ws"], a["ws_bytes"],
+                                   a["stream"])
     assert call(K=96) == E.GDN_EUNSUPPORTED
     assert call(V=40) == E.GDN_EUNSUPPORTED
     assert call(V=512) == E.GDN_EUNSUPPORTED
     assert call(in_dt=4) == E.GDN_EUNSUPPORTED
-    assert call(B=0) == E.GDN_OK
-    assert call(B=-1) == E.GDN_EINVAL
+    assert call(n=0, total=0) == E.GDN_OK
+    assert call(n=-1) == E.GDN_EINVAL
+    assert call(total=201) == E.GDN_EINVAL         # not a multiple of n_seqs without offsets
     assert call(H=0) == E.GDN_EINVAL
     assert call(scale=float("inf")) == E.GDN_EINVAL
     assert call(q=None) == E.GDN_EINVAL
@@ -290,6 +295,12 @@ def test_chunk_fwd_kda_validation():
     assert call(k=FAKE + 8) == E.GDN_EINVAL      # q, k, g read four channels at a time: 16-byte aligned
     assert call(g=FAKE + 4) == E.GDN_EINVAL
     assert call(h0=FAKE + 2) == E.GDN_EINVAL
+    assert call(pool=FAKE, pool_slots=4, slots=FAKE, h0=FAKE) == E.GDN_EINVAL  # a pool excludes h0 / ht
+    assert call(pool=FAKE, pool_slots=4, slots=None) == E.GDN_EINVAL
+    assert call(slots=FAKE) == E.GDN_EINVAL                                    # slots without a pool
+    bad = (ctypes.c_int32 * 3)(0, 120, 100)
+    assert call(cu=FAKE, cu_host=ctypes.addressof(bad)) == E.GDN_EINVAL        # decreasing offsets
+    assert call(cu=FAKE, cu_host=None) == E.GDN_EINVAL
     assert call(ws=None) == E.GDN_EWORKSPACE
     assert call(ws_bytes=1024) == E.GDN_EWORKSPACE
     assert call(ws=FAKE + 16) == E.GDN_EWORKSPACE

@@ -1026,3 +1026,64 @@ def test_decode_layer_fused_config_full():
     _print(f"[decode layer fused N256 H32] out {e_out:.2e} state {e_st:.2e}")
     assert e_out <= TOL["f32"] and e_st <= TOL["f32"]
     assert np.array_equal(host(conv), rst)
+
+
+def test_chunk_kda_varlen_pool():
+    """Packed sequences of very different lengths (empty, one token, chunk
+    multiples, ragged tails) with per-channel decays and states in a pool (one
+    padding slot): every sequence against the per-token definition; unused and
+    padding slots untouched; bf16 output = RNE of the float32 output."""
+    lengths = [300, 0, 1, 64, 65, 130, 7]
+    H, K, V = 3, 128, 64
+    ci = chunk_inputs(lengths, H, K, V, dtype="bf16", seed=130, pool_slots=10, slot_ids=[4, 2, 0, 7, 1, 9, 5])
+    g = channel_log_decay((ci.total_tokens, H, K), 131, -1.0)
+    dt = torch.bfloat16
+    q, k, v = dev(ci.q, dt), dev(ci.k, dt), dev(ci.v, dt)
+    cu = ci.cu_seqlens.tolist()
+    pool0 = dev(ci.pool)
+    outs = {}
+    for od in ("f32", "bf16"):
+        pool = pool0.clone()
+        o, ht = api.chunk_fwd_kda(q, k, v, dev(g), dev(ci.beta), scale=K ** -0.5, cu_seqlens=cu, state_pool=pool,
+                                  state_slots=dev(ci.slots, torch.int32), out_dtype=TORCH_DT[od])
+        torch.cuda.synchronize()
+        assert ht is None
+        outs[od] = (o, pool)
+    assert torch.equal(outs["bf16"][0], bf16_rne(outs["f32"][0]))
+    assert torch.equal(outs["bf16"][1], outs["f32"][1])
+    o, pool = outs["f32"]
+    for sl in (0, 3, 6, 8):  # unused and the padding sequence's: untouched
+        assert torch.equal(pool[sl], pool0[sl]), f"slot {sl} was written"
+    oh = host(o)
+    eo = es = 0.0
+    for s in range(len(lengths)):
+        r = slice(cu[s], cu[s + 1])
+        S0 = ci.pool[ci.slots[s]] if ci.slots[s] > 0 else None
+        o_ref, S_ref = oracle.recurrent_fwd_kda(ci.q[r], ci.k[r], ci.v[r], g[r], ci.beta[r], scale=K ** -0.5, S0=S0)
+        if lengths[s]:
+            eo = max(eo, max_err_over_rms(oh[r], o_ref))
+        if ci.slots[s] > 0:
+            es = max(es, max_err_over_rms(host(pool[ci.slots[s]]), S_ref))
+    _print(f"[chunk kda varlen pool] max|do|/rms={eo:.3e} max|dS|/rms={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_chunk_kda_varlen_dense_states_f32():
+    """Packed float32 inputs with dense h0 / ht updated in place (ht = h0)."""
+    lengths = [150, 64, 1, 200]
+    H, K, V = 2, 64, 128
+    ci = chunk_inputs(lengths, H, K, V, dtype="f32", seed=140, h0_std=0.1)
+    g = channel_log_decay((ci.total_tokens, H, K), 141, -2.0)
+    cu = ci.cu_seqlens.tolist()
+    state = dev(ci.h0)
+    o, ht = api.chunk_fwd_kda(dev(ci.q), dev(ci.k), dev(ci.v), dev(g), dev(ci.beta), scale=0.3, cu_seqlens=cu,
+                              h0=state, ht=state, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    eo = es = 0.0
+    for s in range(len(lengths)):
+        r = slice(cu[s], cu[s + 1])
+        o_ref, S_ref = oracle.recurrent_fwd_kda(ci.q[r], ci.k[r], ci.v[r], g[r], ci.beta[r], scale=0.3, S0=ci.h0[s])
+        eo = max(eo, max_err_over_rms(host(o)[r], o_ref))
+        es = max(es, max_err_over_rms(host(state[s]), S_ref))
+    _print(f"[chunk kda varlen f32 in place] max|do|/rms={eo:.3e} max|dS|/rms={es:.3e}")
+    assert eo <= TOL["f32"] and es <= TOL["f32"]
