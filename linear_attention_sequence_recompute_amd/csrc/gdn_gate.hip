@@ -12,16 +12,15 @@
 // is read here as column order.
 //
 // One workgroup per (block of kGateTok tokens, head), one thread per key
-// channel: the thread's F_B row lives in registers as float32, the block's
-// activations in LDS as float32 (read by all threads at the same address), and
-// four tokens run at once as independent chains.
+// channel: the thread's F_B row lives in registers as float32; each token's
+// activations are read once per wave into scalar registers.
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
 constexpr int kGateRank = 128;
-constexpr int kGateTok = 16;  // tokens per workgroup
+constexpr int kGateTok = 8;  // tokens per workgroup
 
 __device__ __forceinline__ void unpack8(const u32x4& u, float* dst) {
 #pragma unroll
@@ -38,98 +37,79 @@ __global__ __launch_bounds__(K) void kda_gate_kernel(const __bf16* __restrict__ 
                                                      float* __restrict__ g, __bf16* __restrict__ raw_out, int N,
                                                      int H) {
   constexpr int R = kGateRank;
-  __shared__ __attribute__((aligned(16))) float xs[kGateTok][R];
   const int f = threadIdx.x, h = blockIdx.y;
   const int t0 = blockIdx.x * kGateTok;
   const int nt = min(kGateTok, N - t0);
-  for (int i = f; i < kGateTok * R / 8; i += K) {
-    const int tok = i / (R / 8), c8 = 8 * (i % (R / 8));
-    u32x4 u = u32x4{0u, 0u, 0u, 0u};
-    if (tok < nt) u = *reinterpret_cast<const u32x4*>(f_a + static_cast<int64_t>(t0 + tok) * R + c8);
-    unpack8(u, &xs[tok][c8]);
-  }
   float w[R];
   const __bf16* wr = f_b + (static_cast<int64_t>(h) * K + f) * R;
 #pragma unroll
   for (int c8 = 0; c8 < R / 8; ++c8) unpack8(*reinterpret_cast<const u32x4*>(wr + 8 * c8), &w[8 * c8]);
   const float ea = expf(a_log[h]);
   const float dt = dt_bias[h * K + f];
-  __syncthreads();
 
-  for (int tb = 0; tb < nt; tb += 4) {
-    float raw[4];
+  // one token at a time (a wave issues dependent VALU operations back to back);
+  // the token's activations are the same for every lane: uniform loads, which
+  // the compiler places in scalar registers
+  for (int t = 0; t < nt; ++t) {
+    const uint32_t* xr = reinterpret_cast<const uint32_t*>(f_a) + static_cast<int64_t>(t0 + t) * (R / 2);
+    // column c of the token as float32 (bf16 pairs, low half first)
+    auto x = [&](int c) {
+      const uint32_t u = xr[c >> 1];
+      return __uint_as_float((c & 1) ? (u & 0xffff0000u) : (u << 16));
+    };
+    // keeps one 32-column chunk of unpacked activations live at a time
+    auto chunk_end = [](int c4) {
+      if (c4 % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+    };
+    float raw;
     if constexpr (MODE == 0) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      float acc = 0.f;
 #pragma unroll
       for (int c4 = 0; c4 < R / 4; ++c4) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float4 x = *reinterpret_cast<const float4*>(&xs[(tb + t) & (kGateTok - 1)][4 * c4]);
-          acc[t] = fmaf(x.x, w[4 * c4], acc[t]);
-          acc[t] = fmaf(x.y, w[4 * c4 + 1], acc[t]);
-          acc[t] = fmaf(x.z, w[4 * c4 + 2], acc[t]);
-          acc[t] = fmaf(x.w, w[4 * c4 + 3], acc[t]);
-        }
+        acc = fmaf(x(4 * c4), w[4 * c4], acc);
+        acc = fmaf(x(4 * c4 + 1), w[4 * c4 + 1], acc);
+        acc = fmaf(x(4 * c4 + 2), w[4 * c4 + 2], acc);
+        acc = fmaf(x(4 * c4 + 3), w[4 * c4 + 3], acc);
+        chunk_end(c4);
       }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) raw[t] = acc[t];
+      raw = acc;
     } else if constexpr (MODE == 1) {
-      float p[4][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[t][j] = 0.f;
+      float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c4 = 0; c4 < R / 4; ++c4) {
         const int j = c4 / 8;  // 32 columns per chain
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float4 x = *reinterpret_cast<const float4*>(&xs[(tb + t) & (kGateTok - 1)][4 * c4]);
-          p[t][j] = fmaf(x.x, w[4 * c4], p[t][j]);
-          p[t][j] = fmaf(x.y, w[4 * c4 + 1], p[t][j]);
-          p[t][j] = fmaf(x.z, w[4 * c4 + 2], p[t][j]);
-          p[t][j] = fmaf(x.w, w[4 * c4 + 3], p[t][j]);
-        }
+        p[j] = fmaf(x(4 * c4), w[4 * c4], p[j]);
+        p[j] = fmaf(x(4 * c4 + 1), w[4 * c4 + 1], p[j]);
+        p[j] = fmaf(x(4 * c4 + 2), w[4 * c4 + 2], p[j]);
+        p[j] = fmaf(x(4 * c4 + 3), w[4 * c4 + 3], p[j]);
+        chunk_end(c4);
       }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) raw[t] = 0.f + (((p[t][0] + p[t][1]) + p[t][2]) + p[t][3]);
+      raw = 0.f + (((p[0] + p[1]) + p[2]) + p[3]);
     } else {
-      float p[4][16];
+      float p[16];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) p[t][i] = 0.f;
+      for (int i = 0; i < 16; ++i) p[i] = 0.f;
 #pragma unroll
       for (int c4 = 0; c4 < R / 4; ++c4) {
         const int i = c4 / 2;  // 8 columns per partial
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float4 x = *reinterpret_cast<const float4*>(&xs[(tb + t) & (kGateTok - 1)][4 * c4]);
-          p[t][i] = fmaf(x.x, w[4 * c4], p[t][i]);
-          p[t][i] = fmaf(x.y, w[4 * c4 + 1], p[t][i]);
-          p[t][i] = fmaf(x.z, w[4 * c4 + 2], p[t][i]);
-          p[t][i] = fmaf(x.w, w[4 * c4 + 3], p[t][i]);
-        }
+        p[i] = fmaf(x(4 * c4), w[4 * c4], p[i]);
+        p[i] = fmaf(x(4 * c4 + 1), w[4 * c4 + 1], p[i]);
+        p[i] = fmaf(x(4 * c4 + 2), w[4 * c4 + 2], p[i]);
+        p[i] = fmaf(x(4 * c4 + 3), w[4 * c4 + 3], p[i]);
+        chunk_end(c4);
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int sh = 3; sh >= 0; --sh)
 #pragma unroll
-        for (int s = 3; s >= 0; --s)
-#pragma unroll
-          for (int i = 0; i < (1 << s); ++i) p[t][i] = p[t][i] + p[t][i | (1 << s)];
-        raw[t] = p[t][0];
-      }
+        for (int i = 0; i < (1 << sh); ++i) p[i] = p[i] + p[i | (1 << sh)];
+      raw = p[0];
     }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (tb + t >= nt) break;
-      const __bf16 rg = static_cast<__bf16>(raw[t]);  // round to nearest even
-      const float pre = ea * (static_cast<float>(rg) + dt);
-      const float gate = 1.f / (1.f + expf(-pre));
-      const int64_t o = (static_cast<int64_t>(t0 + tb + t) * H + h) * K + f;
-      g[o] = lower_bound * gate;
-      if (raw_out) raw_out[o] = rg;
-    }
+    const __bf16 rg = static_cast<__bf16>(raw);  // round to nearest even
+    const float pre = ea * (static_cast<float>(rg) + dt);
+    const float gate = 1.f / (1.f + expf(-pre));
+    const int64_t o = (static_cast<int64_t>(t0 + t) * H + h) * K + f;
+    g[o] = lower_bound * gate;
+    if (raw_out) raw_out[o] = rg;
   }
 }
 
