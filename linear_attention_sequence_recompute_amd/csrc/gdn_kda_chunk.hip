@@ -17,6 +17,7 @@
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
+#include <type_traits>
 #include <utility>
 
 namespace gdn {
@@ -369,51 +370,68 @@ struct KdaScanArgs {
   const int* seq_chunk0;
 };
 
+// The (sequence, head, value slice) a scan workgroup serves, and its sequence's
+// tokens and chunks. Workgroups are dealt to the 8 XCDs round-robin by id: the
+// slices of one (sequence, head) pair get ids of one residue mod 8, so they
+// share an XCD and its L2, which serves their common reads of the chunk operands.
+struct KdaSeq {
+  int seq, h, start, len, chunk0, v_base;
+};
+__device__ __forceinline__ bool kda_seq_of(const KdaScanArgs& a, KdaSeq& s) {
+  const int n_slices = a.V / kKdaSlice, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int pair = (idx / n_slices) * 8 + xcd;
+  if (pair >= a.n_seqs * a.H) return false;  // padding of the grid to whole rounds of 8
+  s.h = pair % a.H;
+  s.seq = pair / a.H;
+  s.v_base = (idx % n_slices) * kKdaSlice;
+  // a packed call whose offsets do not fit the token stream or the chunk count
+  // gets an empty sequence
+  if (a.cu) {
+    s.start = a.cu[s.seq];
+    s.len = a.cu[s.seq + 1] - s.start;
+    s.chunk0 = a.seq_chunk0[s.seq];
+    if (s.start < 0 || s.len < 0 || s.start > a.total_tokens - s.len || s.chunk0 < 0 ||
+        s.chunk0 > a.n_chunks - (s.len + 63) / 64)
+      s.len = 0;
+  } else {
+    s.start = s.seq * a.T_eq;
+    s.len = a.T_eq;
+    s.chunk0 = s.seq * a.ncs_eq;
+  }
+  return true;
+}
+// The state pages: a pool slot (<= 0 or past the pool: zero start, no write) or h0 / ht.
+template <int K>
+__device__ __forceinline__ void kda_pages(const KdaScanArgs& a, const KdaSeq& s, const float*& st_in, float*& st_out) {
+  const int64_t page = static_cast<int64_t>(a.V) * K;
+  st_in = nullptr;
+  st_out = nullptr;
+  if (a.pool) {
+    const int sl = a.slots[s.seq];
+    if (sl > 0 && sl < a.pool_slots) {
+      st_in = a.pool + (static_cast<int64_t>(sl) * a.H + s.h) * page;
+      st_out = a.pool + (static_cast<int64_t>(sl) * a.H + s.h) * page;
+    }
+  } else {
+    if (a.h0) st_in = a.h0 + (static_cast<int64_t>(s.seq) * a.H + s.h) * page;
+    if (a.ht) st_out = a.ht + (static_cast<int64_t>(s.seq) * a.H + s.h) * page;
+  }
+}
+
+
 template <int K, typename Tin, typename Tout>
 __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __restrict__ v, const float* __restrict__ ws,
                                                                Tout* __restrict__ o, KdaScanArgs a) {
   using L = KdaScanLds<K>;
   __shared__ __attribute__((aligned(16))) L sm;
-  const int H = a.H, V = a.V;
-  // Workgroups are dealt to the 8 XCDs round-robin by id: the slices of one
-  // (sequence, head) pair get ids of one residue mod 8, so they share an XCD and
-  // its L2, which then serves their common reads of the chunk operands.
-  const int n_slices = V / kKdaSlice, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
-  const int pair = (idx / n_slices) * 8 + xcd;
-  if (pair >= a.n_seqs * H) return;  // padding of the grid to whole rounds of 8
-  const int h = pair % H, seq = pair / H;
-  // the sequence's tokens and chunks (a packed call whose offsets do not fit the
-  // token stream or the chunk count gets an empty sequence)
-  int start, len, chunk0;
-  if (a.cu) {
-    start = a.cu[seq];
-    len = a.cu[seq + 1] - start;
-    chunk0 = a.seq_chunk0[seq];
-    if (start < 0 || len < 0 || start > a.total_tokens - len || chunk0 < 0 ||
-        chunk0 > a.n_chunks - (len + 63) / 64)
-      len = 0;
-  } else {
-    start = seq * a.T_eq;
-    len = a.T_eq;
-    chunk0 = seq * a.ncs_eq;
-  }
+  KdaSeq sq;
+  if (!kda_seq_of(a, sq)) return;
+  const int H = a.H, V = a.V, h = sq.h, start = sq.start, len = sq.len, chunk0 = sq.chunk0, v_base = sq.v_base;
   const int NC = (len + 63) / 64;
-  const int v_base = (idx % n_slices) * kKdaSlice;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-  // the state pages: a pool slot (<= 0 or past the pool: zero start, no write) or h0 / ht
-  const int64_t page = static_cast<int64_t>(V) * K;
-  const float* st_in = nullptr;
-  float* st_out = nullptr;
-  if (a.pool) {
-    const int sl = a.slots[seq];
-    if (sl > 0 && sl < a.pool_slots) {
-      st_in = a.pool + (static_cast<int64_t>(sl) * H + h) * page;
-      st_out = a.pool + (static_cast<int64_t>(sl) * H + h) * page;
-    }
-  } else {
-    if (a.h0) st_in = a.h0 + (static_cast<int64_t>(seq) * H + h) * page;
-    if (a.ht) st_out = a.ht + (static_cast<int64_t>(seq) * H + h) * page;
-  }
+  const float* st_in;
+  float* st_out;
+  kda_pages<K>(a, sq, st_in, st_out);
   const int64_t st_row = static_cast<int64_t>(v_base) * K;  // this slice's rows [.., V, K]
   for (int e = tid; e < K * kKdaSlice; e += kKdaThreads) {
     const int cc = e % K, vv = e / K;
@@ -514,6 +532,524 @@ __global__ __launch_bounds__(kKdaThreads) void kda_scan_kernel(const Tin* __rest
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs: the chunk step on the bf16 MFMA (v_mfma_f32_16x16x32_bf16).
+// Every operand of the scan is a computed fp32 matrix (the decays differ per key
+// channel, so no product has an exact bf16 side as in the scalar-decay path);
+// each is carried as a split bf16 pair hi + lo and each product takes the three
+// MFMA terms of two split operands, about 16 significant bits (the same as
+// every computed operand of the scalar-decay path).
+//
+// prep writes, per (chunk, head), the scan's operands as fragments in the
+// layout of gdn_common.h (planes of 64 lanes x 16 bytes, hi then lo):
+//   kg  [4 row tiles][K/32 key blocks]  K o e^G            (A operand: token rows)
+//   qg  [4][K/32]                       s q o e^G
+//   kdt [K/16 key tiles][2 token blocks] (K o e^{G_last - G})^T (A operand: key rows)
+//   af  [6]                             A' = (I + L)^{-1} diag(beta), nonzero tiles
+//   pf  [6]                             P, the same tiles
+//   gl  [K] f32                         e^{G_last}
+// ---------------------------------------------------------------------------
+template <int K>
+struct KdaOps {
+  static constexpr int NKB = K / 32, NT = K / 16;
+  static constexpr int kFrag = 2 * 1024;  // one split fragment: hi plane, lo plane
+  static constexpr int kg = 0;
+  static constexpr int qg = kg + 4 * NKB * kFrag;
+  static constexpr int kdt = qg + 4 * NKB * kFrag;
+  static constexpr int af = kdt + NT * 2 * kFrag;
+  static constexpr int pf = af + 6 * kFrag;
+  static constexpr int gl = pf + 6 * kFrag;
+  static constexpr int bytes = (gl + 4 * K + 255) & ~255;
+};
+static_assert(KdaOps<128>::bytes <= kda_floats_per_chunk(128) * 4, "split operands fit the fp32 layout's space");
+static_assert(KdaOps<64>::bytes <= kda_floats_per_chunk(64) * 4, "split operands fit the fp32 layout's space");
+
+// Nonzero A' / P tiles (row tile rt, token block ks): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
+__device__ __forceinline__ constexpr int kda_a_tile(int rt, int ks) { return rt < 2 ? rt : 2 * rt - 2 + ks; }
+
+// The 8 values at channels c0 + kappa(g, e) of a row, as floats.
+__device__ __forceinline__ void kda_row8(const __bf16* row, int c0, int g, float (&x)[8]) {
+  const u32x2 a = *reinterpret_cast<const u32x2*>(row + c0 + 4 * g);
+  const u32x2 b = *reinterpret_cast<const u32x2*>(row + c0 + 16 + 4 * g);
+  const uint32_t u[4] = {a[0], a[1], b[0], b[1]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(u[e] << 16);
+    x[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void kda_row8(const float* row, int c0, int g, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(row + c0 + 4 * g);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(row + c0 + 16 + 4 * g);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = a[e];
+    x[4 + e] = b[e];
+  }
+}
+
+// 16-deep fp32 product of two LDS-resident 16 x 16 blocks (v_mfma_f32_16x16x4f32):
+// lane (g, c) supplies a = X[c][4 g + e], b = Y[4 g + e][c] to instruction e.
+__device__ __forceinline__ f32x4 kda_mma16v(const f32x4& a, const f32x4& b, f32x4 acc) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], b[e], acc);
+  return acc;
+}
+
+// A diagonal 16 x 16 block of L and P is factored about its middle token m,
+// e^{G_i - G_j} = e^{G_i - G_m} e^{G_m - G_j}, when no channel's G moves by more
+// than kDiagSpan (log2 units) from G_m within the block, so that neither factor
+// leaves the float range; otherwise it is summed pair by pair.
+constexpr float kDiagSpan = 64.f;
+
+template <int K>
+__global__ __launch_bounds__(256) void kda_prep_split_kernel(const __bf16* __restrict__ q,
+                                                             const __bf16* __restrict__ k,
+                                                             const float* __restrict__ g,
+                                                             const float* __restrict__ beta, char* __restrict__ ws,
+                                                             KdaChunkGeo geo, int H, float scale) {
+  using P = Prec<__bf16>;
+  using Ops = KdaOps<K>;
+  constexpr int NKB = K / 32, TPW = K / 64;
+  constexpr int LDK = K + 8, LDG = K + 4, LDA = 68;
+  constexpr int CQ = K / 4, RG = 256 / CQ, RPG = 64 / RG;  // cumsum: channel quads x row groups
+  __shared__ __attribute__((aligned(16))) __bf16 sK[64 * LDK];
+  __shared__ __attribute__((aligned(16))) float sG[64 * LDG];  // G log2(e), chunk-local inclusive cumsum
+  __shared__ __attribute__((aligned(16))) float sLA[64][LDA];  // L; diagonal blocks become their inverses
+  __shared__ float sOff[6][16][17];                             // A_ij below the diagonal
+  __shared__ float sB[64];
+  const int h = blockIdx.y;
+  int t0, n;
+  if (!geo.at(blockIdx.x, t0, n)) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lg = lane >> 4, lc = lane & 15;
+  char* ops = ws + (static_cast<int64_t>(blockIdx.x) * H + h) * Ops::bytes;
+  const int64_t rs = static_cast<int64_t>(H) * K;
+  const int64_t base = (static_cast<int64_t>(t0) * H + h) * K;
+  auto q_row = [&](int i) { return q + base + min(i, n - 1) * rs; };  // rows past the end: masked by the caller
+  auto off_block = [](int i, int j) { return i * (i - 1) / 2 + j; };  // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+
+  // (0) K into LDS (rows past the end zero), the chunk-local inclusive cumsum of
+  // the log-decays into sG by row groups (group totals through sLA), beta
+  {
+    const int cq = tid % CQ, rg = tid / CQ;
+    u32x2 kk[RPG];
+    f32x4 gv[RPG];
+#pragma unroll
+    for (int ii = 0; ii < RPG; ++ii) {
+      const int64_t idx = base + min(rg * RPG + ii, n - 1) * rs + 4 * cq;
+      kk[ii] = *reinterpret_cast<const u32x2*>(k + idx);
+      gv[ii] = *reinterpret_cast<const f32x4*>(g + idx);
+    }
+    const float bt = tid < 64 ? beta[(static_cast<int64_t>(t0) + min(tid, n - 1)) * H + h] : 0.f;
+    f32x4 s = zero4();
+#pragma unroll
+    for (int ii = 0; ii < RPG; ++ii) {
+      const int i = rg * RPG + ii;
+      const bool in = i < n;
+      const float f = in ? kLog2e : 0.f;
+      // a log-decay of -inf is taken as kMinLogDecay (see the fp32 prep)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] += f * fmaxf(gv[ii][e], kMinLogDecay);
+      gv[ii] = s;
+      *reinterpret_cast<u32x2*>(&sK[i * LDK + 4 * cq]) = in ? kk[ii] : u32x2{0u, 0u};
+    }
+    float* tot = &sLA[0][0];  // [RG][K]
+    *reinterpret_cast<f32x4*>(&tot[rg * K + 4 * cq]) = s;
+    if (tid < 64) sB[tid] = tid < n ? bt : 0.f;
+    __syncthreads();
+    f32x4 off = zero4();
+    for (int r2 = 0; r2 < rg; ++r2) off += *reinterpret_cast<const f32x4*>(&tot[r2 * K + 4 * cq]);
+#pragma unroll
+    for (int ii = 0; ii < RPG; ++ii) *reinterpret_cast<f32x4*>(&sG[(rg * RPG + ii) * LDG + 4 * cq]) = gv[ii] + off;
+    __syncthreads();
+  }
+
+  // (1) L = StrictLower(diag(beta) ((K o e^G)(K o e^-G)^T)) and P = s (Q o e^G)(K o
+  // e^-G)^T masked to j <= i, by 16 x 16 blocks (I, J <= I), grouped into the P
+  // fragments (row tile I, token block ks) as in the scalar-decay prep: three,
+  // three, two and two blocks per wave. A block below the diagonal is factored
+  // about the first token r = 16 I of row block I (both factors <= 1). Each block
+  // is computed transposed, (rows j) x (columns i), so that lane (g, c) ends with
+  // row i = 16 I + c at the four columns j = 16 J + 4 g + r: a pair of such tiles
+  // is one A-operand fragment of P, and L goes to LDS row by row.
+  constexpr int kGrp[4][2] = {{0, 6}, {2, 5}, {4, -1}, {7, -1}};
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int grp = kGrp[w][gi];
+    if (grp < 0) continue;
+    const int I = grp >> 1, ks = grp & 1;
+    const int i = 16 * I + lc;
+    const float bi = sB[i];
+    const float qm = i < n ? scale : 0.f;
+    const __bf16* qi_row = q_row(i);
+    f32x4 pt[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int J = 2 * ks + half;
+      if (J > I) continue;
+      const int jr = 16 * J + lc;  // the row this lane supplies to the A operand
+      bool exact = false;
+      int ref = 16 * I;
+      if (J == I) {
+        ref = 16 * I + 8;
+        bool bad = false;
+        for (int ch = lane; ch < K; ch += 64) {
+          const float gm = sG[ref * LDG + ch];
+          bad |= sG[16 * I * LDG + ch] - gm > kDiagSpan || gm - sG[(16 * I + 15) * LDG + ch] > kDiagSpan;
+        }
+        exact = __ballot(bad) != 0ull;
+      }
+      f32x4 lacc = zero4(), pacc = zero4();
+      if (!exact) {
+        f32x4 la[3] = {zero4(), zero4(), zero4()}, pa[3] = {zero4(), zero4(), zero4()};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          float gr[8], kj[8], gj[8], ki[8], gi8[8], qi[8];
+          kda_row8(sG + ref * LDG, 32 * kb, lg, gr);
+          kda_row8(sK + jr * LDK, 32 * kb, lg, kj);
+          kda_row8(sG + jr * LDG, 32 * kb, lg, gj);
+          kda_row8(sK + i * LDK, 32 * kb, lg, ki);
+          kda_row8(sG + i * LDG, 32 * kb, lg, gi8);
+          kda_row8(qi_row, 32 * kb, lg, qi);
+          float xa[8], xk[8], xq[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            xa[e] = kj[e] * exp2_hw(gr[e] - gj[e]);
+            const float ei = exp2_hw(gi8[e] - gr[e]);
+            xk[e] = ki[e] * ei;
+            xq[e] = qm * qi[e] * ei;
+          }
+          const FragS fa = P::cmp8(xa), fk = P::cmp8(xk), fq = P::cmp8(xq);
+#pragma unroll
+          for (int t = 0; t < 3; ++t) {
+            la[t] = term(fa, fk, la[t], t);
+            pa[t] = term(fa, fq, pa[t], t);
+          }
+        }
+        lacc = la[0] + la[1] + la[2];
+        pacc = pa[0] + pa[1] + pa[2];
+      } else {
+        // pair by pair: element (i, j = 16 I + 4 g + r), channels four at a time
+        for (int c4 = 0; c4 < K; c4 += 4) {
+          const u32x2 qu = *reinterpret_cast<const u32x2*>(qi_row + c4);
+          const f32x4 qv = {__uint_as_float(qu[0] << 16), __uint_as_float(qu[0] & 0xffff0000u),
+                            __uint_as_float(qu[1] << 16), __uint_as_float(qu[1] & 0xffff0000u)};
+          const u32x2 ku = *reinterpret_cast<const u32x2*>(&sK[i * LDK + c4]);
+          const f32x4 kv = {__uint_as_float(ku[0] << 16), __uint_as_float(ku[0] & 0xffff0000u),
+                            __uint_as_float(ku[1] << 16), __uint_as_float(ku[1] & 0xffff0000u)};
+          const f32x4 gv = *reinterpret_cast<const f32x4*>(&sG[i * LDG + c4]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * I + 4 * lg + r;
+            const u32x2 ju = *reinterpret_cast<const u32x2*>(&sK[j * LDK + c4]);
+            const f32x4 kjv = {__uint_as_float(ju[0] << 16), __uint_as_float(ju[0] & 0xffff0000u),
+                               __uint_as_float(ju[1] << 16), __uint_as_float(ju[1] & 0xffff0000u)};
+            const f32x4 gjv = *reinterpret_cast<const f32x4*>(&sG[j * LDG + c4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              // exponents of the pairs above the diagonal (discarded) are kept <= 0
+              const float wgt = kjv[e] * exp2_hw(fminf(gv[e] - gjv[e], 0.f));
+              lacc[r] = fmaf(kv[e], wgt, lacc[r]);
+              pacc[r] = fmaf(qv[e], wgt, pacc[r]);
+            }
+          }
+        }
+        pacc *= qm;
+      }
+      f32x4 lv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * J + 4 * lg + r;
+        lv[r] = j < i ? bi * lacc[r] : 0.f;
+        pt[half][r] = j <= i ? pacc[r] : 0.f;
+      }
+      *reinterpret_cast<f32x4*>(&sLA[i][16 * J + 4 * lg]) = lv;
+    }
+    P::st_cmp(ops + Ops::pf + kda_a_tile(I, ks) * Ops::kFrag, lane, P::cmp_tiles(pt[0], pt[1]));
+  }
+  __syncthreads();
+
+  // (2) D_w = (I + L_ww)^-1 by forward substitution (lane (j, part) keeps rows
+  // [4 part, 4 part + 4) of column j; the parts are added by quad permutations),
+  // then this wave's share of the state-side operands
+  {
+    const int j = lane >> 2, part = lane & 3;
+    f32x4 lrow[15];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) lrow[i - 1] = *reinterpret_cast<const f32x4*>(&sLA[16 * w + i][16 * w + 4 * part]);
+    f32x4 av;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) av[r] = (4 * part + r == j) ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      float s = (lrow[i - 1][0] * av[0] + lrow[i - 1][1] * av[1]) + (lrow[i - 1][2] * av[2] + lrow[i - 1][3] * av[3]);
+      s += quad_xor1(s);
+      s += quad_xor2(s);
+      if (part == (i >> 2) && i > j) av[i & 3] = -s;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sLA[16 * w + 4 * part + r][16 * w + j] = av[r];
+  }
+  {
+    // K o e^G and s q o e^G, row tile w
+    const int i = 16 * w + lc;
+    const float qm = i < n ? scale : 0.f;
+    const __bf16* qi_row = q_row(i);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float ki[8], gi8[8], qi[8], xk[8], xq[8];
+      kda_row8(sK + i * LDK, 32 * kb, lg, ki);
+      kda_row8(sG + i * LDG, 32 * kb, lg, gi8);
+      kda_row8(qi_row, 32 * kb, lg, qi);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float eg = exp2_hw(gi8[e]);
+        xk[e] = ki[e] * eg;
+        xq[e] = qm * qi[e] * eg;
+      }
+      P::st_cmp(ops + Ops::kg + (w * NKB + kb) * Ops::kFrag, lane, P::cmp8(xk));
+      P::st_cmp(ops + Ops::qg + (w * NKB + kb) * Ops::kFrag, lane, P::cmp8(xq));
+    }
+    // (K o e^{G_last - G})^T, key tiles TPW w .. TPW w + TPW - 1
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = TPW * w + u, key = 16 * t + lc;
+      const float gL = sG[63 * LDG + key];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int jt = 32 * tb + kappa(lg, e);
+          x[e] = static_cast<float>(sK[jt * LDK + key]) * exp2_hw(gL - sG[jt * LDG + key]);
+        }
+        P::st_cmp(ops + Ops::kdt + (2 * t + tb) * Ops::kFrag, lane, P::cmp8(x));
+      }
+    }
+    if (tid < K) reinterpret_cast<float*>(ops + Ops::gl)[tid] = exp2_hw(sG[63 * LDG + tid]);
+  }
+  __syncthreads();
+
+  // (3) the blocks below the diagonal by distance d from it,
+  // A_ij = -D_i sum_{j <= m < i} L_im A_mj (waves 0 .. 3 - d)
+#pragma unroll
+  for (int d = 1; d < 4; ++d) {
+    if (w < 4 - d) {
+      const int jb = w, ib = w + d;
+      f32x4 x = zero4();
+#pragma unroll
+      for (int kb = jb; kb < ib; ++kb) {
+        const f32x4 lik = *reinterpret_cast<const f32x4*>(&sLA[16 * ib + lc][16 * kb + 4 * lg]);
+        f32x4 akj;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          akj[e] = kb == jb ? sLA[16 * jb + 4 * lg + e][16 * jb + lc] : sOff[off_block(kb, jb)][4 * lg + e][lc];
+        x = kda_mma16v(lik, akj, x);
+      }
+      const f32x4 di = *reinterpret_cast<const f32x4*>(&sLA[16 * ib + lc][16 * ib + 4 * lg]);
+      const f32x4 y = kda_mma16v(di, x, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sOff[off_block(ib, jb)][4 * lg + r][lc] = -y[r];
+    }
+    __syncthreads();
+  }
+
+  // (4) A' = A diag(beta): wave w writes row tile w, token blocks 0 and (row
+  // tiles 2, 3) 1
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if (ks > 0 && w < 2) continue;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int m = 32 * ks + kappa(lg, e);
+      const int mb = m >> 4;
+      const float av = mb == w ? sLA[16 * w + lc][m] : mb < w ? sOff[off_block(w, mb)][lc][m & 15] : 0.f;
+      x[e] = av * sB[m];
+    }
+    P::st_cmp(ops + Ops::af + kda_a_tile(w, ks) * Ops::kFrag, lane, P::cmp8(x));
+  }
+}
+
+// One workgroup (4 waves) per (value slice of 16 columns, head, sequence). Wave
+// w owns token rows 16 w .. 16 w + 15 of R, D and o, and the state's key tiles
+// TPW w .. TPW w + TPW - 1 (16 keys x 16 columns each, lane (g, c) holding keys
+// 16 t + 4 g + r of column c) in MFMA accumulators. Per chunk:
+//   (1) R = V - (K o e^G) h, its row tile into LDS as half a B operand;
+//   (2) D = A' R (row tile w), into LDS the same way;
+//   (3) h <- diag(e^{G_last}) h + (K o e^{G_last - G})^T D on the wave's key
+//       tiles, published as B operands for the next chunk (double buffered);
+//   (4) o = (s q o e^G) h + P D from the state the chunk started with.
+// Three barriers per chunk; each operand fragment is loaded from the workspace
+// into registers for the next chunk right after its last use in this one.
+template <int K, typename Tout>
+__global__ __launch_bounds__(256) void kda_scan_split_kernel(const __bf16* __restrict__ v,
+                                                             const char* __restrict__ ws, Tout* __restrict__ o,
+                                                             KdaScanArgs a) {
+  using P = Prec<__bf16>;
+  using Ops = KdaOps<K>;
+  constexpr int NKB = K / 32, TPW = K / 64, F = Ops::kFrag;
+  __shared__ __attribute__((aligned(16))) char hB[2][NKB][F];  // the state as B operands (key blocks)
+  __shared__ __attribute__((aligned(16))) char rB[2][F];       // R as B operands (token blocks)
+  __shared__ __attribute__((aligned(16))) char dB[2][F];       // D as B operands (token blocks)
+  KdaSeq s;
+  if (!kda_seq_of(a, s)) return;
+  const int H = a.H, V = a.V, h = s.h;
+  const int NC = (s.len + 63) / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lg = lane >> 4, lc = lane & 15;
+  const float* st_in;
+  float* st_out;
+  kda_pages<K>(a, s, st_in, st_out);
+  const int64_t st_row = static_cast<int64_t>(s.v_base) * K;  // this slice's rows of the [V, K] page
+
+  f32x4 hs[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = TPW * w + u;
+    hs[u] = st_in ? *reinterpret_cast<const f32x4*>(st_in + st_row + lc * K + 16 * t + 4 * lg) : zero4();
+    P::st_tile(hB[0][t >> 1], lane, t & 1, hs[u]);
+  }
+  const char* ops0 = ws + (static_cast<int64_t>(s.chunk0) * H + h) * Ops::bytes;
+  const int64_t cstride = static_cast<int64_t>(H) * Ops::bytes;
+
+  FragS kg[NKB], qg[NKB], af[2], pf[2], kd[TPW][2];
+  f32x4 gl[TPW];
+  __bf16 vr[4];
+  auto ld_kg = [&](const char* c) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) kg[kb] = P::ld_cmp(c + Ops::kg + (w * NKB + kb) * F, lane);
+  };
+  auto ld_qg = [&](const char* c) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) qg[kb] = P::ld_cmp(c + Ops::qg + (w * NKB + kb) * F, lane);
+  };
+  auto ld_af = [&](const char* c) {
+    af[0] = P::ld_cmp(c + Ops::af + kda_a_tile(w, 0) * F, lane);
+    if (w >= 2) af[1] = P::ld_cmp(c + Ops::af + kda_a_tile(w, 1) * F, lane);
+  };
+  auto ld_pf = [&](const char* c) {
+    pf[0] = P::ld_cmp(c + Ops::pf + kda_a_tile(w, 0) * F, lane);
+    if (w >= 2) pf[1] = P::ld_cmp(c + Ops::pf + kda_a_tile(w, 1) * F, lane);
+  };
+  auto ld_kd = [&](const char* c) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = TPW * w + u;
+      kd[u][0] = P::ld_cmp(c + Ops::kdt + (2 * t) * F, lane);
+      kd[u][1] = P::ld_cmp(c + Ops::kdt + (2 * t + 1) * F, lane);
+      gl[u] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(c + Ops::gl) + 16 * t + 4 * lg);
+    }
+  };
+  auto ld_v = [&](int ch) {  // rows 16 w + 4 g + r of chunk ch, column v_base + c
+    const int n = min(64, s.len - 64 * ch);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // rows past the end read the last row and are zeroed where used
+      const int ic = min(16 * w + 4 * lg + r, n - 1);
+      vr[r] = v[((static_cast<int64_t>(s.start) + 64 * ch + ic) * H + h) * V + s.v_base + lc];
+    }
+  };
+  if (NC > 0) {
+    ld_kg(ops0);
+    ld_qg(ops0);
+    ld_af(ops0);
+    ld_pf(ops0);
+    ld_kd(ops0);
+    ld_v(0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) af[i] = pf[i] = FragS{zero_bf16x8(), zero_bf16x8()};
+  }
+  __syncthreads();  // the initial state is published
+
+  int cur = 0;
+  for (int ch = 0; ch < NC; ++ch) {
+    const int t0 = 64 * ch, n = min(64, s.len - t0);
+    const char* nx = ops0 + static_cast<int64_t>(min(ch + 1, NC - 1)) * cstride;
+    float vc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vc[r] = 16 * w + 4 * lg + r < n ? static_cast<float>(vr[r]) : 0.f;
+
+    // (1) R = V - (K o e^G) h
+    FragS hb[NKB];
+    f32x4 z[3] = {zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      hb[kb] = P::ld_cmp(hB[cur][kb], lane);
+#pragma unroll
+      for (int t = 0; t < 3; ++t) z[t] = term(kg[kb], hb[kb], z[t], t);
+    }
+    const f32x4 zz = z[0] + z[1] + z[2];
+    P::st_tile(rB[w >> 1], lane, w & 1, f32x4{vc[0] - zz[0], vc[1] - zz[1], vc[2] - zz[2], vc[3] - zz[3]});
+    ld_kg(nx);
+    ld_v(min(ch + 1, NC - 1));
+    __syncthreads();
+
+    // (2) D = A' R (A' vanishes above the diagonal: token block 1 only for row tiles 2, 3)
+    f32x4 d[3] = {zero4(), zero4(), zero4()};
+    {
+      const FragS r0 = P::ld_cmp(rB[0], lane);
+#pragma unroll
+      for (int t = 0; t < 3; ++t) d[t] = term(af[0], r0, d[t], t);
+    }
+    if (w >= 2) {
+      const FragS r1 = P::ld_cmp(rB[1], lane);
+#pragma unroll
+      for (int t = 0; t < 3; ++t) d[t] = term(af[1], r1, d[t], t);
+    }
+    P::st_tile(dB[w >> 1], lane, w & 1, d[0] + d[1] + d[2]);
+    ld_af(nx);
+    __syncthreads();
+
+    // (3) h <- diag(e^{G_last}) h + (K o e^{G_last - G})^T D
+    const FragS db[2] = {P::ld_cmp(dB[0], lane), P::ld_cmp(dB[1], lane)};
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = TPW * w + u;
+      f32x4 acc[3] = {gl[u] * hs[u], zero4(), zero4()};
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int tt = 0; tt < 3; ++tt) acc[tt] = term(kd[u][tb], db[tb], acc[tt], tt);
+      hs[u] = acc[0] + acc[1] + acc[2];
+      P::st_tile(hB[cur ^ 1][t >> 1], lane, t & 1, hs[u]);
+    }
+    ld_kd(nx);
+
+    // (4) o = (s q o e^G) h + P D, h the state the chunk started with
+    f32x4 oc[3] = {zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) oc[t] = term(qg[kb], hb[kb], oc[t], t);
+#pragma unroll
+    for (int t = 0; t < 3; ++t) oc[t] = term(pf[0], db[0], oc[t], t);
+    if (w >= 2) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t) oc[t] = term(pf[1], db[1], oc[t], t);
+    }
+    const f32x4 ov = oc[0] + oc[1] + oc[2];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * w + 4 * lg + r;
+      if (i < n) store_out(o + ((static_cast<int64_t>(s.start) + t0 + i) * H + h) * V + s.v_base + lc, ov[r]);
+    }
+    ld_qg(nx);
+    ld_pf(nx);
+    cur ^= 1;
+    __syncthreads();  // the new state is published; every wave is done with R, D and the old state
+  }
+  if (st_out) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = TPW * w + u;
+      *reinterpret_cast<f32x4*>(st_out + st_row + lc * K + 16 * t + 4 * lg) = hs[u];
+    }
+  }
+}
+
 // Workspace: the chunk operands per (chunk, head), then the chunk schedule of
 // a packed call (16 bytes per chunk, 4 per sequence and one more).
 static size_t kda_ops_bytes(int64_t max_chunks, int H, int K) {
@@ -535,16 +1071,33 @@ static void launch_kda_typed(const KdaChunkArgs& a) {
   if (varlen)
     (void)launch_chunk_schedule(a.cu_seqlens, a.n_seqs, static_cast<int>(a.total_tokens),
                                 static_cast<int>(a.n_chunks), seq_chunk0, info, a.stream);
-  if (a.n_chunks > 0)
-    hipLaunchKernelGGL((kda_prep_kernel<K, Tin>), dim3(static_cast<unsigned>(a.n_chunks), a.H), dim3(kPrepThreads), 0,
-                       a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), a.g, a.beta, ops,
-                       KdaChunkGeo{varlen ? info : nullptr, a.T_eq, ncs_eq, static_cast<int>(a.total_tokens)}, a.H,
-                       a.scale);
+  const KdaChunkGeo geo{varlen ? info : nullptr, a.T_eq, ncs_eq, static_cast<int>(a.total_tokens)};
+  constexpr bool kSplit = std::is_same<Tin, __bf16>::value;
+  if (a.n_chunks > 0) {
+    if constexpr (kSplit)
+      hipLaunchKernelGGL((kda_prep_split_kernel<K>), dim3(static_cast<unsigned>(a.n_chunks), a.H), dim3(256), 0,
+                         a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k), a.g, a.beta,
+                         static_cast<char*>(a.ws), geo, a.H, a.scale);
+    else
+      hipLaunchKernelGGL((kda_prep_kernel<K, Tin>), dim3(static_cast<unsigned>(a.n_chunks), a.H), dim3(kPrepThreads),
+                         0, a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), a.g, a.beta, ops, geo,
+                         a.H, a.scale);
+  }
   if (a.events[1]) (void)hipEventRecord(a.events[1], a.stream);
   KdaScanArgs sa{a.h0, a.ht, a.pool, a.pool_slots, a.slots, a.H, a.V, a.n_seqs, a.T_eq, ncs_eq,
                  static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens, seq_chunk0};
   const int64_t n_pairs = static_cast<int64_t>(a.n_seqs) * a.H;
   const dim3 grid(static_cast<unsigned>((n_pairs + 7) / 8) * 8 * (a.V / kKdaSlice));
+  if constexpr (kSplit) {
+    if (a.out_f32)
+      hipLaunchKernelGGL((kda_scan_split_kernel<K, float>), grid, dim3(256), 0, a.stream,
+                         static_cast<const __bf16*>(a.v), static_cast<const char*>(a.ws), static_cast<float*>(a.o), sa);
+    else
+      hipLaunchKernelGGL((kda_scan_split_kernel<K, __bf16>), grid, dim3(256), 0, a.stream,
+                         static_cast<const __bf16*>(a.v), static_cast<const char*>(a.ws), static_cast<__bf16*>(a.o),
+                         sa);
+    return;
+  }
   if (a.out_f32)
     hipLaunchKernelGGL((kda_scan_kernel<K, Tin, float>), grid, dim3(kKdaThreads), 0, a.stream,
                        static_cast<const Tin*>(a.v), ops, static_cast<float*>(a.o), sa);
