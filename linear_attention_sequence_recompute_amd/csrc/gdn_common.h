@@ -316,6 +316,10 @@ struct Buf {
   __device__ __forceinline__ uint32_t load4(uint32_t voff) const {
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
   }
+  // 2 bytes per lane (0 past the descriptor size).
+  __device__ __forceinline__ uint16_t load2(uint32_t voff, uint32_t soff) const {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  }
   __device__ __forceinline__ void store(float x, uint32_t voff, uint32_t soff) const {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, soff, 0);
   }

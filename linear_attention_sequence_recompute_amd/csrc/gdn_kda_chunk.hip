@@ -881,8 +881,10 @@ __global__ __launch_bounds__(256) void kda_prep_split_kernel(const __bf16* __res
 //   (3) h <- diag(e^{G_last}) h + (K o e^{G_last - G})^T D on the wave's key
 //       tiles, published as B operands for the next chunk (double buffered);
 //   (4) o = (s q o e^G) h + P D from the state the chunk started with.
-// Three barriers per chunk; each operand fragment is loaded from the workspace
-// into registers for the next chunk right after its last use in this one.
+// The chunk's operands (about 130 KB per workgroup) are what bounds a step:
+// their loads are spread over the step, each issued right after the last use
+// of the registers it refills.
+// Three barriers per chunk.
 template <int K, typename Tout>
 __global__ __launch_bounds__(256) void kda_scan_split_kernel(const __bf16* __restrict__ v,
                                                              const char* __restrict__ ws, Tout* __restrict__ o,
@@ -913,51 +915,69 @@ __global__ __launch_bounds__(256) void kda_scan_split_kernel(const __bf16* __res
   }
   const char* ops0 = ws + (static_cast<int64_t>(s.chunk0) * H + h) * Ops::bytes;
   const int64_t cstride = static_cast<int64_t>(H) * Ops::bytes;
+  // Global accesses go through buffer descriptors: a chunk's fragment block
+  // (uniform offsets in scalar registers, lane * 16 the only per-lane offset),
+  // and the chunk's V and o rows of this head and slice, the descriptor ending
+  // at the chunk's last row (rows past it read as zeros, their stores are
+  // dropped).
+  const uint32_t HV = static_cast<uint32_t>(H) * V;
+  uint32_t row_el[4];  // element offsets of rows 16 w + 4 g + r, column c, within a chunk
+#pragma unroll
+  for (int r = 0; r < 4; ++r) row_el[r] = static_cast<uint32_t>(16 * w + 4 * lg + r) * HV + lc;
+  auto rows_buf = [&](const void* base_el, int ch, int esize) {
+    const int n = min(64, s.len - 64 * ch);
+    const int64_t first = (static_cast<int64_t>(s.start) + 64 * ch) * H + h;
+    return Buf(static_cast<const char*>(base_el) + (first * V + s.v_base) * esize,
+               static_cast<uint32_t>(((n - 1) * HV + 16) * esize));
+  };
+  const uint32_t lo16 = lane * 16;
 
   FragS kg[NKB], qg[NKB], af[2], pf[2], kd[TPW][2];
   f32x4 gl[TPW];
-  __bf16 vr[4];
-  auto ld_kg = [&](const char* c) {
+  uint16_t vr[4];
+  auto frag = [&](const Buf& b, int off) {
+    return FragS{as_bf16x8(b.load16(lo16, off)), as_bf16x8(b.load16(lo16, off + 1024))};
+  };
+  auto ld_kg = [&](const Buf& b) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) kg[kb] = P::ld_cmp(c + Ops::kg + (w * NKB + kb) * F, lane);
+    for (int kb = 0; kb < NKB; ++kb) kg[kb] = frag(b, Ops::kg + (w * NKB + kb) * F);
   };
-  auto ld_qg = [&](const char* c) {
+  auto ld_qg = [&](const Buf& b) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) qg[kb] = P::ld_cmp(c + Ops::qg + (w * NKB + kb) * F, lane);
+    for (int kb = 0; kb < NKB; ++kb) qg[kb] = frag(b, Ops::qg + (w * NKB + kb) * F);
   };
-  auto ld_af = [&](const char* c) {
-    af[0] = P::ld_cmp(c + Ops::af + kda_a_tile(w, 0) * F, lane);
-    if (w >= 2) af[1] = P::ld_cmp(c + Ops::af + kda_a_tile(w, 1) * F, lane);
+  auto ld_af = [&](const Buf& b) {
+    af[0] = frag(b, Ops::af + kda_a_tile(w, 0) * F);
+    if (w >= 2) af[1] = frag(b, Ops::af + kda_a_tile(w, 1) * F);
   };
-  auto ld_pf = [&](const char* c) {
-    pf[0] = P::ld_cmp(c + Ops::pf + kda_a_tile(w, 0) * F, lane);
-    if (w >= 2) pf[1] = P::ld_cmp(c + Ops::pf + kda_a_tile(w, 1) * F, lane);
+  auto ld_pf = [&](const Buf& b) {
+    pf[0] = frag(b, Ops::pf + kda_a_tile(w, 0) * F);
+    if (w >= 2) pf[1] = frag(b, Ops::pf + kda_a_tile(w, 1) * F);
   };
-  auto ld_kd = [&](const char* c) {
+  auto ld_kd = [&](const Buf& b) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int t = TPW * w + u;
-      kd[u][0] = P::ld_cmp(c + Ops::kdt + (2 * t) * F, lane);
-      kd[u][1] = P::ld_cmp(c + Ops::kdt + (2 * t + 1) * F, lane);
-      gl[u] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(c + Ops::gl) + 16 * t + 4 * lg);
+      kd[u][0] = frag(b, Ops::kdt + (2 * t) * F);
+      kd[u][1] = frag(b, Ops::kdt + (2 * t + 1) * F);
+      gl[u] = __builtin_bit_cast(f32x4, b.load16(static_cast<uint32_t>(16 * t + 4 * lg) * 4, Ops::gl));
     }
   };
-  auto ld_v = [&](int ch) {  // rows 16 w + 4 g + r of chunk ch, column v_base + c
-    const int n = min(64, s.len - 64 * ch);
+  auto ld_v = [&](int ch) {  // rows 16 w + 4 g + r of chunk ch, column v_base + c (0 past the end)
+    const Buf vb = rows_buf(v, ch, 2);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      // rows past the end read the last row and are zeroed where used
-      const int ic = min(16 * w + 4 * lg + r, n - 1);
-      vr[r] = v[((static_cast<int64_t>(s.start) + 64 * ch + ic) * H + h) * V + s.v_base + lc];
-    }
+    for (int r = 0; r < 4; ++r) vr[r] = vb.load2(row_el[r] * 2, 0);
   };
   if (NC > 0) {
-    ld_kg(ops0);
-    ld_qg(ops0);
-    ld_af(ops0);
-    ld_pf(ops0);
-    ld_kd(ops0);
+    // in the order the loop issues them: the memory counter is waited on by
+    // position, and the wait at the loop head serves both ways into it
+    const Buf b0(ops0, Ops::bytes);
+    ld_kg(b0);
     ld_v(0);
+    ld_af(b0);
+    ld_kd(b0);
+    ld_qg(b0);
+    ld_pf(b0);
   } else {
 #pragma unroll
     for (int i = 0; i < 2; ++i) af[i] = pf[i] = FragS{zero_bf16x8(), zero_bf16x8()};
@@ -966,11 +986,10 @@ __global__ __launch_bounds__(256) void kda_scan_split_kernel(const __bf16* __res
 
   int cur = 0;
   for (int ch = 0; ch < NC; ++ch) {
-    const int t0 = 64 * ch, n = min(64, s.len - t0);
-    const char* nx = ops0 + static_cast<int64_t>(min(ch + 1, NC - 1)) * cstride;
+    const Buf nx(ops0 + static_cast<int64_t>(min(ch + 1, NC - 1)) * cstride, Ops::bytes);
     float vc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vc[r] = 16 * w + 4 * lg + r < n ? static_cast<float>(vr[r]) : 0.f;
+    for (int r = 0; r < 4; ++r) vc[r] = __uint_as_float(static_cast<uint32_t>(vr[r]) << 16);
 
     // (1) R = V - (K o e^G) h
     FragS hb[NKB];
@@ -1031,10 +1050,10 @@ __global__ __launch_bounds__(256) void kda_scan_split_kernel(const __bf16* __res
       for (int t = 0; t < 3; ++t) oc[t] = term(pf[1], db[1], oc[t], t);
     }
     const f32x4 ov = oc[0] + oc[1] + oc[2];
+    {
+      const Buf ob = rows_buf(o, ch, sizeof(Tout));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * w + 4 * lg + r;
-      if (i < n) store_out(o + ((static_cast<int64_t>(s.start) + t0 + i) * H + h) * V + s.v_base + lc, ov[r]);
+      for (int r = 0; r < 4; ++r) ob.store(static_cast<Tout>(ov[r]), row_el[r] * sizeof(Tout), 0);
     }
     ld_qg(nx);
     ld_pf(nx);
