@@ -581,8 +581,21 @@ def bench_layer(torch, api, hev, steps, warmup):
     def fused():
         api.decode_layer(x, w, bias, conv, slots, braw, lg, pool, DH, gate=gate, norm_w=nw, out=out, stream=stream)
 
+    # the layer with per-key-channel decays from the gate's projection: the gate
+    # stage, then the fused layer on its decays
+    f_a = torch.randn(DN, 128, device=dev, generator=g).to(torch.bfloat16)
+    f_b = (torch.randn(DH * DK, 128, device=dev, generator=g) * 128 ** -0.5).to(torch.bfloat16)
+    a_log = torch.rand(DH, device=dev, generator=g) * 2.5 - 2.0
+    dt = torch.randn(DH * DK, device=dev, generator=g)
+    g_kda = torch.empty(DN, DH, DK, device=dev)
+
+    def gate_then_fused():
+        api.kda_gate(f_a, f_b, a_log, dt, -5.0, DH, mode=1, out=g_kda, stream=stream)
+        api.decode_layer(x, w, bias, conv, slots, braw, g_kda, pool, DH, gate=gate, norm_w=nw, out=out, stream=stream)
+
+
     res = {}
-    for name, fn in (("separate", separate), ("fused", fused)):
+    for name, fn in (("separate", separate), ("fused", fused), ("kda_gate_then_fused", gate_then_fused)):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -596,7 +609,7 @@ def bench_layer(torch, api, hev, steps, warmup):
         for e in evs:
             hev.destroy(e)
     return dict(prologue_ms=stats(ms_p), rmsnorm_ms=stats(ms_r), layer_separate_ms=res["separate"],
-                layer_fused_ms=res["fused"])
+                layer_fused_ms=res["fused"], layer_kda_gate_then_fused_ms=res["kda_gate_then_fused"])
 
 
 def bench_copy(torch, steps, nbytes=1 << 30):
@@ -872,6 +885,11 @@ def main():
         "separate_launches_us": res_l["layer_separate_ms"]["mean"] * 1e3,
         "fused_us": lf_s * 1e6, "bytes_per_launch": lf_b,
         "roofline": hbm_roofline(lf_b / lf_s / 1e9, traffic_for("decode_layer_kernel"), lf_b)}
+    out["decode_layer"]["layer_kda_gate"] = {
+        "workload": f"the decode layer with per-key-channel decays from the gate's rank-128 projection (mode 1): "
+                    f"the gate stage, then the fused layer on its decays, N={DN} H={DH} D={DK}, state pool {DSLOTS} "
+                    f"slots",
+        "gate_stage_then_fused_us": res_l["layer_kda_gate_then_fused_ms"]["mean"] * 1e3}
     gate_flops = 2 * DN * DH * DK * 128
     out["kda_gate"] = {
         "workload": f"KDA gate stage (low-rank projection f_a . F_B, bf16 rounding, decays), N={DN} tokens, H={DH}, "
