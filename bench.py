@@ -788,9 +788,10 @@ def main():
 
     peaks = res["peaks"]
     head = chunk_entry(res["chunk"], args.steps, peaks)
-    head["roofline"]["kernel"] = ("chunk_fwd_h fused with chunk_fwd_o: summary_kernel + scan_kernel "
-                                  "(chunk-parallel form, 4 segments of 16 chunks)")
-    head["roofline"]["traffic"] = traffic_for("summary_kernel", "scan_kernel")
+    head["roofline"]["kernel"] = ("chunk_fwd_h fused with chunk_fwd_o: seg0_kernel (segment 0's scan beside the "
+                                  "maps of segments 1-3) + scan_kernel (segments 1-4); the chunk-parallel form at "
+                                  "this shape, 5 segments of 12 + 4 x 13 chunks")
+    head["roofline"]["traffic"] = traffic_for("seg0_kernel", "scan_kernel")
     res_d = res["decode"]
     dec_s = res_d["kernel_ms"]["mean"] / 1e3
     dec_b = decode_bytes(res_d["n_active"])
@@ -909,14 +910,16 @@ def main():
                     "bf16 q/k/v/o, fp32 g [T, H, K] and beta, fp32 final state",
         "value": B * T / (ck_ms / 1e3), "unit": "tokens/s", "ms_per_call": ck_ms,
         "kernels_us": {"prep": ck_prep_s * 1e6, "scan": ck_scan_s * 1e6},
-        "roofline": {"bound": "mfma", "kernel": "kda_scan_kernel (fp32 MFMA)", "achieved": ck_scan_f / ck_scan_s / 1e12,
-                     "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ck_scan_f / ck_scan_s / 1e12 / PEAK_FP32_TFLOPS,
-                     "traffic": traffic_for("kda_scan_kernel"), "flops_per_launch": ck_scan_f,
-                     "avg_launch_us": ck_scan_s * 1e6},
+        "roofline": {"bound": "mfma", "kernel": "kda_scan_split_kernel (split-bf16 MFMA)",
+                     "achieved": ck_scan_f / ck_scan_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ck_scan_f / ck_scan_s / 1e12 / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_for("kda_scan_split_kernel"), "flops_per_launch": ck_scan_f,
+                     "avg_launch_us": ck_scan_s * 1e6,
+                     "note": "128 workgroups of 64 dependent chunk steps; a step is bound by delivering its "
+                             "~130 KB of operand fragments per workgroup through the CU's vector memory path"},
         "prep_roofline": {"bound": "alu", "achieved": ck_prep_f / ck_prep_s / 1e12, "peak": PEAK_FP32_TFLOPS,
                           "unit": "TFLOP/s", "frac": ck_prep_f / ck_prep_s / 1e12 / PEAK_FP32_TFLOPS,
-                          "traffic": traffic_for("kda_prep_kernel"), "flops_per_launch": ck_prep_f}}
+                          "traffic": traffic_for("kda_prep_split_kernel"), "flops_per_launch": ck_prep_f}}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds, res_d.get("_inputs"))
