@@ -269,9 +269,10 @@ gdn_status gdn_recurrent_verify(const void* q, const void* k, const void* v, con
  *  raw_g     bf16 [N, H, K] (output: bf16(raw)), or NULL
  *
  * Returns GDN_EUNSUPPORTED for K outside {64, 128}; GDN_EINVAL for a mode
- * outside {0, 1, 2}, N < 0, H outside [1, 65535], a non-finite lower_bound, a
- * NULL or misaligned pointer (raw_g may be NULL); GDN_OK without launching for
- * N == 0; GDN_EHIP if the launch fails.
+ * outside {0, 1, 2}, N < 0, H outside [1, 65535], ceil(N / 8) * 8 ceil(H / 8)
+ * above 2^31 - 1, a non-finite lower_bound, a NULL or misaligned pointer (raw_g
+ * may be NULL); GDN_OK without launching for N == 0; GDN_EHIP if the launch
+ * fails.
  */
 gdn_status gdn_kda_gate(const void* f_a, const void* f_b, const float* a_log, const float* dt_bias,
                         float lower_bound, int mode, float* g, void* raw_g, int N, int H, int K,

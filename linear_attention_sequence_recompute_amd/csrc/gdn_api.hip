@@ -351,6 +351,8 @@ gdn_status gdn_kda_gate(const void* f_a, const void* f_b, const float* a_log, co
   if (K != 64 && K != 128) return GDN_EUNSUPPORTED;
   if (mode < 0 || mode > 2 || N < 0 || H <= 0 || H > 65535 || !std::isfinite(lower_bound)) return GDN_EINVAL;
   if (static_cast<int64_t>(N) * H * K > INT64_MAX / 4) return GDN_EINVAL;
+  // one workgroup per (8 tokens, head), heads padded to multiples of 8: a 1-D grid
+  if ((static_cast<int64_t>(N) + 7) / 8 * ((H + 7) / 8) * 8 > INT32_MAX) return GDN_EINVAL;
   if (N == 0) return GDN_OK;
   if (!f_a || !f_b || !a_log || !dt_bias || !g) return GDN_EINVAL;
   if (!aligned(f_a, 16) || !aligned(f_b, 16) || !aligned(a_log, 4) || !aligned(dt_bias, 4) || !aligned(g, 4) ||

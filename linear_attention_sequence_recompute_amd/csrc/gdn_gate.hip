@@ -4,7 +4,8 @@
 //
 // One workgroup per (block of kGateTok tokens, head), one thread per key
 // channel: the thread's F_B row lives in registers as float32; each token's
-// activations are read once per wave into scalar registers.
+// activations are read once per wave into scalar registers. The blocks of a head
+// share an XCD.
 #include "gdn_common.h"
 #include "gdn_gate.h"
 #include "gdn_internal.h"
@@ -28,8 +29,15 @@ __global__ __launch_bounds__(K) void kda_gate_kernel(const __bf16* __restrict__ 
                                                      float* __restrict__ g, __bf16* __restrict__ raw_out, int N,
                                                      int H) {
   constexpr int R = kGateRank;
-  const int f = threadIdx.x, h = blockIdx.y;
-  const int t0 = blockIdx.x * kGateTok;
+  // Workgroups are dealt to the 8 XCDs round-robin by id: the token blocks of
+  // one head get ids of one residue mod 8, so they share an XCD and its L2,
+  // which then serves their common F_B rows (the grid is padded to whole
+  // rounds of 8 heads)
+  const int n_tb = (N + kGateTok - 1) / kGateTok, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int h = (idx / n_tb) * 8 + xcd, tb = idx % n_tb;
+  if (h >= H) return;
+  const int f = threadIdx.x;
+  const int t0 = tb * kGateTok;
   const int nt = min(kGateTok, N - t0);
   float w[R];
   const __bf16* wr = f_b + (static_cast<int64_t>(h) * K + f) * R;
@@ -53,7 +61,8 @@ __global__ __launch_bounds__(K) void kda_gate_kernel(const __bf16* __restrict__ 
 
 template <int K>
 static void launch_gate_k(const GateArgs& a) {
-  const dim3 grid(static_cast<unsigned>((a.N + kGateTok - 1) / kGateTok), static_cast<unsigned>(a.H));
+  const int64_t n_tb = (a.N + kGateTok - 1) / kGateTok;
+  const dim3 grid(static_cast<unsigned>(n_tb * ((a.H + 7) / 8) * 8));
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(K), 0, a.stream, static_cast<const __bf16*>(a.f_a),
                        static_cast<const __bf16*>(a.f_b), a.a_log, a.dt_bias, a.lower_bound, a.g,

@@ -359,6 +359,7 @@ def test_kda_gate_validation():
     assert call(lb=float("inf")) == EINVAL and call(lb=float("nan")) == EINVAL
     assert call(fa=None) == EINVAL and call(g=None) == EINVAL
     assert call(fa=FAKE + 8) == EINVAL and call(raw=FAKE + 1) == EINVAL
+    assert call(N=2 ** 31 - 1, H=65535) == EINVAL  # the 1-D grid would exceed 2^31 - 1 workgroups
     assert call(N=0) == _lib.GDN_OK
 
 
