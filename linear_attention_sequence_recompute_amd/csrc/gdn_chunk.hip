@@ -914,18 +914,12 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin, NCH> (&sms)
     using MF = MapFrag<K>;
     auto stage_half = [&](int hf) {  // half hf & 1 of map hf >> 1
       const Buf md(maps + (hf >> 1) * map_stride + (hf & 1) * MF::kHalfBytes, MF::kHalfBytes);
-      char* dst = sm.fold[hf & 1];
+      char* dst = (hf & 1) ? sm.fold[1] : sm.fold[0];  // a select: an indexed member array would live in scratch
 #pragma unroll
       for (int j = 0; j < MF::kHalfBytes / 1024; ++j) md.to_lds16(dst + 1024 * j, 16 * lane, 1024 * j);
     };
-    // every line of the maps into L2 first (a 4-byte direct-to-LDS read per
-    // 128-byte line, into a block nobody reads: no registers held), so that
-    // the half copies below, a half ahead of the chains, hit L2
-    for (int j = 0; j < n_fold; ++j) {
-      const Buf md(maps + j * map_stride, MF::kBytes);
-#pragma unroll
-      for (int i = 0; i < MF::kBytes / 128 / 64; ++i) md.to_lds4(sm.sink, 128u * (64 * i + lane), 0);
-    }
+    // (the maps' lines are brought into L2 by output wave 1 meanwhile, so that
+    // this wave's first wait covers the first chunk and the first half only)
     stage_half(0);
     wait_vmem();
     __syncthreads();
@@ -957,7 +951,8 @@ __device__ __forceinline__ void scan_producer(const ScanSmem<K, Tin, NCH> (&sms)
 template <int OW, int K, int V, typename Tin, typename Tout, int NCH>
 __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin, NCH> (&sms)[NCH], const ScanSeq& sq,
                                             const Tin* __restrict__ q, Tout* __restrict__ o, int H, float scale,
-                                            const ChunkWs& ws, int n_fold = 0) {
+                                            const ChunkWs& ws, int n_fold = 0, const char* maps = nullptr,
+                                            int64_t map_stride = 0) {
   using S = ScanSmem<K, Tin, NCH>;
   const S& sm0 = sms[0];
   using P = Prec<Tin>;
@@ -1058,7 +1053,18 @@ __device__ __forceinline__ void scan_output(const ScanSmem<K, Tin, NCH> (&sms)[N
     }
   };
 
-  // the barriers of the chains' map folds (two halves per map, one more before)
+  // every line of the maps the chains fold into L2 (a 4-byte direct-to-LDS
+  // read per 128-byte line, into a block nobody reads: no registers held), so
+  // that the producer's half copies, a half ahead of the chains, hit L2; then
+  // the barriers of the folds (two halves per map, one more before)
+  if (OW == 1 && n_fold > 0) {
+    using MF = MapFrag<K>;
+    for (int j = 0; j < n_fold; ++j) {
+      const Buf md(maps + j * map_stride, MF::kBytes);
+#pragma unroll
+      for (int i = 0; i < MF::kBytes / 128 / 64; ++i) md.to_lds4(sm0.sink, 128u * (64 * i + lane), 0);
+    }
+  }
   for (int hf = 0; n_fold > 0 && hf <= 2 * n_fold; ++hf) __syncthreads();
   const int nc = sq.nc;
   __syncthreads();
@@ -1256,10 +1262,12 @@ __device__ __forceinline__ void scan_wg(const ScanSmem<K, Tin, NCH> (&sms)[NCH],
     scan_producer<K, V, Tin, NCH>(sms, sq, a.q, a.k, a.v, a.H, a.ws, true, maps, n_fold,
                                   static_cast<int64_t>(V + K) * K * 4);
   } else {
+    const char* maps = fold ? reinterpret_cast<const char*>(fold + static_cast<int64_t>(V) * K) : nullptr;
     if (wv == 2)
       scan_output<0, K, V, Tin, Tout, NCH>(sms, sq, a.q, a.o, a.H, a.scale, a.ws, n_fold);
     else
-      scan_output<1, K, V, Tin, Tout, NCH>(sms, sq, a.q, a.o, a.H, a.scale, a.ws, n_fold);
+      scan_output<1, K, V, Tin, Tout, NCH>(sms, sq, a.q, a.o, a.H, a.scale, a.ws, n_fold, maps,
+                                           static_cast<int64_t>(V + K) * K * 4);
   }
 }
 
