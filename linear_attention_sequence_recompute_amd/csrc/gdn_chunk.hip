@@ -1148,9 +1148,8 @@ __device__ __forceinline__ ScanSeq seq_of(int pair, int H, int T_eq, int ncs_eq,
 // sequence of nc chunks has max(1, 1 + ceil((nc - L0) / L1)) segments, never
 // more than n_seg (the grid's and the workspace's count, whatever the device
 // copy of the offsets says); segment 0 exists even for an empty sequence, so
-// that its initial state passes to its final state. (Later segments fold more
-// maps before their first chunk; giving each one chunk fewer was measured and
-// changed nothing.)
+// that its initial state passes to its final state. The host picks L0 and L1
+// (segment_lengths).
 struct SegGeom {
   int n_seg, L0, L1;
   __device__ int count(int nc) const { return nc <= L0 ? 1 : min(n_seg, 1 + (nc - L0 + L1 - 1) / L1); }
@@ -1416,6 +1415,46 @@ static int segment_cap(int64_t pairs, int K, int V, bool in_f32, int n_cus = kSe
   return n >= 3 ? static_cast<int>(n) : 1;
 }
 
+// Lengths of the chunk-parallel form's segments for the longest sequence (nc
+// chunks, n segments), from a cost model of the two launches in chain steps
+// (measured on MI355X at B = 1, H = 16, K = V = 128: a step of segment 0 takes
+// 1.57 us and its first step comes 0.75 us after a map's (it loads the initial
+// state first), a step of a map 1.66, a step of a later segment 1.48, and a
+// map fold 2.45 before the first step): the first launch lasts as long as the
+// longer of segment 0 and a map, the second as long as its slowest segment,
+// segment j (>= 1) folding j - 1 maps first. The last segment takes what
+// remains, so shortening it (it folds the most maps) lengthens segment 0
+// while the maps outlast it. For each L1 the cost is piecewise linear in L0;
+// its breaks are the candidates.
+static void segment_lengths(int nc, int n, int& L0_out, int& L1_out) {
+  constexpr double ts = 1.57, t0 = 0.75, tm = 1.66, t1 = 1.48, F = 2.45;
+  auto cost = [&](int L0, int L1) {
+    const int last = nc - L0 - (n - 2) * L1;
+    if (L0 < 1 || L1 < 1 || last < 1) return 1e300;
+    const double first = std::max(t0 + L0 * ts, L1 * tm);
+    const double later = std::max((n - 3) * F + L1 * t1, (n - 2) * F + last * t1);
+    return first + later;
+  };
+  double best = 1e300;
+  L1_out = (nc + n - 1) / n;
+  L0_out = nc - (n - 1) * L1_out;
+  for (int L1 = 1; (n - 2) * L1 + 2 <= nc; ++L1) {
+    const int rest = nc - (n - 2) * L1;  // L0 + last
+    const double a = (L1 * tm - t0) / ts;  // L0 where segment 0 starts to outlast the maps
+    const double b = rest - ((n - 3) * F + L1 * t1 - (n - 2) * F) / t1;  // L0 where the last segment stops binding
+    const int cand[6] = {static_cast<int>(a), static_cast<int>(a) + 1, static_cast<int>(b), static_cast<int>(b) + 1, 1,
+                         rest - 1};
+    for (int L0 : cand) {
+      const double c = cost(L0, L1);
+      if (c < best) {
+        best = c;
+        L0_out = L0;
+        L1_out = L1;
+      }
+    }
+  }
+}
+
 WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, bool in_f32) {
   const size_t nch = static_cast<size_t>(max_chunks) * H;
   const int64_t pairs = static_cast<int64_t>(n_seqs) * H;
@@ -1479,15 +1518,16 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
                          static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks), a.cu_seqlens, a.h0, a.ht,
                          a.pool, a.pool_slots, a.slots, SegGeom{1, 0, 0}, a.ws};
   // Chunk-parallel form where the scan would leave most compute units idle:
-  // n segments per sequence, the first of L0 chunks, the others of L1. The
-  // first launch scans every segment 0 and forms the maps of segments 1 ..
-  // n - 2; the second scans segments 1 .. n - 1 at once, each from segment 0's
-  // final state carried through the maps of the segments before its own.
+  // n segments per sequence, the first of L0 chunks, the others of L1, the
+  // last of what remains. The first launch scans every segment 0 and forms the
+  // maps of segments 1 .. n - 2; the second scans segments 1 .. n - 1 at once,
+  // each from segment 0's final state carried through the maps of the
+  // segments before its own.
   const int cap = segment_cap(pairs, K, V, !std::is_same<Tin, __bf16>::value);  // as the workspace was sized
   if (cap > 1 && a.max_nc >= 4 * 3) {
     const int n = std::min(cap, a.max_nc / 4);
-    const int L1 = (a.max_nc + n - 1) / n;
-    const int L0 = a.max_nc - (n - 1) * L1;
+    int L0 = 0, L1 = 0;
+    segment_lengths(a.max_nc, n, L0, L1);
     if (n >= 3 && L0 >= 1) sa.geo = SegGeom{n, L0, L1};
   }
   if constexpr (std::is_same<Tin, __bf16>::value) {
