@@ -790,7 +790,7 @@ def main():
     head = chunk_entry(res["chunk"], args.steps, peaks)
     head["roofline"]["kernel"] = ("chunk_fwd_h fused with chunk_fwd_o: seg0_kernel (segment 0's scan beside the "
                                   "maps of segments 1-3) + scan_kernel (segments 1-4); the chunk-parallel form at "
-                                  "this shape, 5 segments of 12 + 4 x 13 chunks")
+                                  "this shape, 5 segments of 4 x 13 + 12 chunks")
     head["roofline"]["traffic"] = traffic_for("seg0_kernel", "scan_kernel")
     res_d = res["decode"]
     dec_s = res_d["kernel_ms"]["mean"] / 1e3
