@@ -73,6 +73,41 @@ size_t gdn_chunk_fwd_workspace_bytes(int n_seqs, int64_t total_tokens, int H, in
                                      gdn_dtype in_dtype);
 
 /*
+ * Where gdn_chunk_fwd leaves its intermediates in the workspace for a call
+ * with these sizes (max_len: tokens of the longest sequence), so that they can
+ * be inspected after the call returns and before the workspace is reused:
+ * recompute_w_u's outputs and, in the chunk-parallel form, the segment states
+ * and maps of chunk_fwd_h (WarpDrive page, kernels 5 and 3, "Pipeline").
+ * Host only, no device access; GDN_EINVAL for invalid sizes or null outputs,
+ * GDN_EUNSUPPORTED for head sizes or dtypes gdn_chunk_fwd does not take.
+ *  plan[3]     segments per sequence n (1: every sequence scanned in one pass),
+ *              chunks of segment 0, chunks of each of segments 1 .. n - 2 (the
+ *              last segment has what remains)
+ *  offsets[5]  byte offsets from the workspace base of:
+ *   [0] A' = A diag(beta): per (chunk, head), ch = chunk * H + head (chunks
+ *       numbered sequence by sequence), 6 tiles (row tile rt, token block ks) =
+ *       (0,0) (1,0) (2,0) (2,1) (3,0) (3,1), each two planes of 64 lanes x 16
+ *       bytes; lane l = 16 g + c holds row 16 rt + c at the token columns
+ *       32 ks + kappa(g, e), e = 0..7, kappa(g, e) = 4 g + e for e < 4 and
+ *       16 + 4 g + (e - 4) otherwise; bfloat16 inputs: plane 0 the bfloat16
+ *       high parts, plane 1 the low parts (value = high + low); float32 inputs:
+ *       plane 0 values e = 0..3, plane 1 values e = 4..7, as float32
+ *   [1] P = s (Q K^T) * E * M, the same way
+ *   [2] the gate vectors, per ch 3 x 64 float32: g (chunk-local inclusive sum;
+ *       rows past a chunk's end repeat its last), e^g, e^{g_last - g}
+ *   [3] the maps of segments 1 .. n - 2 (n >= 3), per pair = sequence * H +
+ *       head and segment, (V + K) K float32 words: c^T as rows [v][key], then
+ *       M (h_out = M h_in + c for the [K, V] state) as K / 32 x K / 16
+ *       fragments (key block kb, state tile t) of two bfloat16 planes (high,
+ *       low) of 64 lanes x 16 bytes, lane 16 g + c holding row
+ *       32 (t / 2) + 8 (c / 4) + 4 (t % 2) + c % 4 of M at columns
+ *       32 kb + 8 g + e, e = 0..7
+ *   [4] segment 0's final state per pair, [V][K] float32 (n >= 3)
+ */
+gdn_status gdn_chunk_fwd_plan(int n_seqs, int64_t total_tokens, int64_t max_len, int H, int K, int V,
+                              gdn_dtype in_dtype, int32_t* plan, int64_t* offsets);
+
+/*
  * Chunked forward pass over n_seqs sequences packed into one token stream.
  *
  *  q, k        [total_tokens, H, K] in_dtype   queries, keys (the library does

@@ -24,6 +24,7 @@ _F = ctypes.c_float
 _SZ = ctypes.c_size_t
 SIGNATURES = {
     "gdn_chunk_fwd_workspace_bytes": (_SZ, [_I, _I64, _I, _I, _I, _I]),
+    "gdn_chunk_fwd_plan": (_I, [_I, _I64, _I64, _I, _I, _I, _I, _P, _P]),
     "gdn_chunk_fwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I,
                            _P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "gdn_chunk_fwd_profiled": (_I, [_P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _I, _I,

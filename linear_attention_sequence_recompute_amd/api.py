@@ -13,7 +13,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "recurrent_step", "workspace_bytes", "GdnError"]
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_plan", "recurrent_step", "workspace_bytes", "GdnError"]
 
 GdnError = _lib.GdnError
 
@@ -55,6 +55,17 @@ def _need(t: torch.Tensor, name: str, dtype=None):
 def workspace_bytes(n_seqs: int, total_tokens: int, H: int, K: int, V: int, in_dtype=torch.bfloat16) -> int:
     """Device workspace bytes ``chunk_fwd`` needs (see gdn_chunk_fwd_workspace_bytes)."""
     return int(_lib.lib().gdn_chunk_fwd_workspace_bytes(n_seqs, total_tokens, H, K, V, _dt(in_dtype)))
+
+
+def chunk_fwd_plan(n_seqs: int, total_tokens: int, max_len: int, H: int, K: int, V: int, in_dtype=torch.bfloat16):
+    """Segment plan and workspace offsets of ``chunk_fwd`` for these sizes (see
+    gdn_chunk_fwd_plan): ((segments, chunks of segment 0, chunks of segments
+    1 .. n - 2), {name: byte offset} for "af", "pf", "gx", "seg_sum", "seg_state")."""
+    plan = (ctypes.c_int32 * 3)()
+    offs = (ctypes.c_int64 * 5)()
+    _lib.check(_lib.lib().gdn_chunk_fwd_plan(n_seqs, total_tokens, max_len, H, K, V, _dt(in_dtype), plan, offs),
+               "gdn_chunk_fwd_plan")
+    return tuple(plan), dict(zip(("af", "pf", "gx", "seg_sum", "seg_state"), tuple(offs)))
 
 
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,

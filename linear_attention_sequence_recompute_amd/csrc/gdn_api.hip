@@ -71,6 +71,29 @@ size_t gdn_chunk_fwd_workspace_bytes(int n_seqs, int64_t total_tokens, int H, in
       .total;
 }
 
+gdn_status gdn_chunk_fwd_plan(int n_seqs, int64_t total_tokens, int64_t max_len, int H, int K, int V,
+                              gdn_dtype in_dtype, int32_t* plan, int64_t* offsets) {
+  if (!plan || !offsets || n_seqs < 0 || total_tokens < 0 || max_len < 0 || max_len > total_tokens || H <= 0 ||
+      (n_seqs == 0 && total_tokens > 0))
+    return GDN_EINVAL;
+  if (!supported_dim(K) || !supported_dim(V) || !valid_dtype(in_dtype)) return GDN_EUNSUPPORTED;
+  const int64_t max_nc = (max_len + kChunkTokens - 1) / kChunkTokens;
+  if (max_nc > INT32_MAX) return GDN_EINVAL;
+  const gdn::SegPlan sp = gdn::segment_plan(static_cast<int64_t>(n_seqs) * H, K, V, in_dtype == GDN_F32,
+                                            static_cast<int>(max_nc));
+  const gdn::WsLayout l =
+      gdn::workspace_layout(max_chunks(n_seqs, total_tokens), n_seqs, H, K, V, in_dtype == GDN_F32);
+  plan[0] = sp.n_seg;
+  plan[1] = sp.L0;
+  plan[2] = sp.L1;
+  offsets[0] = static_cast<int64_t>(l.af);
+  offsets[1] = static_cast<int64_t>(l.pf);
+  offsets[2] = static_cast<int64_t>(l.gx);
+  offsets[3] = static_cast<int64_t>(l.seg_sum);
+  offsets[4] = static_cast<int64_t>(l.seg_state);
+  return GDN_OK;
+}
+
 }  // extern "C"
 
 namespace {

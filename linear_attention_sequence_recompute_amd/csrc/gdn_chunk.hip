@@ -1455,6 +1455,19 @@ static void segment_lengths(int nc, int n, int& L0_out, int& L1_out) {
   }
 }
 
+// The chunk-parallel form's segments for a call whose longest sequence has
+// max_nc chunks ({1, 0, 0}: the single-pass scan).
+SegPlan segment_plan(int64_t pairs, int K, int V, bool in_f32, int max_nc) {
+  const int cap = segment_cap(pairs, K, V, in_f32);  // as the workspace was sized
+  if (cap > 1 && max_nc >= 4 * 3) {
+    const int n = std::min(cap, max_nc / 4);
+    int L0 = 0, L1 = 0;
+    segment_lengths(max_nc, n, L0, L1);
+    if (n >= 3 && L0 >= 1) return SegPlan{n, L0, L1};
+  }
+  return SegPlan{1, 0, 0};
+}
+
 WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, bool in_f32) {
   const size_t nch = static_cast<size_t>(max_chunks) * H;
   const int64_t pairs = static_cast<int64_t>(n_seqs) * H;
@@ -1523,13 +1536,8 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
   // maps of segments 1 .. n - 2; the second scans segments 1 .. n - 1 at once,
   // each from segment 0's final state carried through the maps of the
   // segments before its own.
-  const int cap = segment_cap(pairs, K, V, !std::is_same<Tin, __bf16>::value);  // as the workspace was sized
-  if (cap > 1 && a.max_nc >= 4 * 3) {
-    const int n = std::min(cap, a.max_nc / 4);
-    int L0 = 0, L1 = 0;
-    segment_lengths(a.max_nc, n, L0, L1);
-    if (n >= 3 && L0 >= 1) sa.geo = SegGeom{n, L0, L1};
-  }
+  const SegPlan plan = segment_plan(pairs, K, V, !std::is_same<Tin, __bf16>::value, a.max_nc);
+  if (plan.n_seg > 1) sa.geo = SegGeom{plan.n_seg, plan.L0, plan.L1};
   if constexpr (std::is_same<Tin, __bf16>::value) {
     if (sa.geo.n_seg > 1) {
       constexpr int NGA = (NSL + K / 16) / 4;

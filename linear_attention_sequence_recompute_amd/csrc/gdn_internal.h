@@ -189,6 +189,12 @@ struct WsLayout {
   int max_segments;  // segments per sequence the chunk-parallel form may use (1: not used)
 };
 WsLayout workspace_layout(int64_t max_chunks, int n_seqs, int H, int K, int V, bool in_f32);
+// Segments of the chunk-parallel form: n_seg per sequence (1: single pass),
+// segment 0 of L0 chunks, segments 1 .. n_seg - 2 of L1, the last the rest.
+struct SegPlan {
+  int n_seg, L0, L1;
+};
+SegPlan segment_plan(int64_t pairs, int K, int V, bool in_f32, int max_nc);
 ChunkWs carve_workspace(const WsLayout& l, void* base);
 
 hipError_t launch_decode(const DecodeArgs& a);

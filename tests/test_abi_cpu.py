@@ -30,7 +30,7 @@ def declared_functions(headers=None):
 
 
 def test_header_declares_the_boundary():
-    assert set(declared_functions([HEADER])) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
+    assert set(declared_functions([HEADER])) == {"gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_plan", "gdn_chunk_fwd",
                                          "gdn_chunk_fwd_profiled", "gdn_chunk_fwd_noalloc", "gdn_recurrent_step",
                                          "gdn_recurrent_step_kda",
                                          "gdn_recurrent_verify", "gdn_kda_gate", "gdn_fp8_quant", "gdn_decode_prologue", "gdn_decode_prologue_verify", "gdn_decode_layer",
@@ -397,3 +397,33 @@ def test_decode_layer_validation():
     assert call(gate=None) == EINVAL and call(pool=None) == EINVAL and call(cs=0) == EINVAL
     assert call(kda=1, g=FAKE + 4) == EINVAL and call(pool=FAKE + 4) == EINVAL
     assert call(N=0) == _lib.GDN_OK
+
+
+def test_chunk_fwd_plan():
+    """gdn_chunk_fwd_plan: the segment plan the host takes (64 chunks for 16 pairs in five
+    segments, 13 + 13 x 3 + 12; one pass for many pairs and for float32 inputs) and
+    workspace offsets consistent with gdn_chunk_fwd_workspace_bytes; invalid sizes and
+    null outputs rejected. Host only."""
+    plan = (ctypes.c_int32 * 3)()
+    offs = (ctypes.c_int64 * 5)()
+    L = _lib.lib()
+
+    def call(n_seqs=1, total=4096, max_len=4096, H=16, K=128, V=128, dt=_lib.GDN_BF16, p=plan, o=offs):
+        return L.gdn_chunk_fwd_plan(n_seqs, total, max_len, H, K, V, dt, p, o)
+
+    assert call() == _lib.GDN_OK
+    assert tuple(plan) == (5, 13, 13)
+    nch = (4096 // 64 + 1) * 16  # chunk slots: total / 64 + n_seqs, per head
+    af, pf, gx, seg_sum, seg_state = tuple(offs)
+    assert af == 0 and pf == nch * 12288 and gx == 2 * nch * 12288 and seg_sum > gx + nch * 768
+    assert seg_state - seg_sum == 16 * 3 * (128 + 128) * 128 * 4  # 16 pairs x 3 maps
+    assert seg_state + 16 * 128 * 128 * 4 <= L.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 128, 128, _lib.GDN_BF16)
+    assert call(n_seqs=4, total=4 * 8192, max_len=8192, H=32) == _lib.GDN_OK and tuple(plan) == (1, 0, 0)
+    assert call(dt=_lib.GDN_F32) == _lib.GDN_OK and tuple(plan) == (1, 0, 0)
+    assert call(total=64 * 11, max_len=64 * 11) == _lib.GDN_OK and tuple(plan) == (1, 0, 0)  # too short to split
+    EINVAL = _lib.GDN_EINVAL
+    assert call(max_len=4097) == EINVAL
+    assert call(n_seqs=-1) == EINVAL
+    assert call(H=0) == EINVAL
+    assert call(p=None) == EINVAL and call(o=None) == EINVAL
+    assert call(K=96) == _lib.GDN_EUNSUPPORTED

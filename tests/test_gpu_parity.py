@@ -239,6 +239,141 @@ def test_segmented_in_place_state():
         assert max_err_over_rms(host(ht1[s]), ref[s][1]) <= TOL["bf16"]
 
 
+# Intermediates: prep's workspace outputs and the chunk-parallel form's segment
+# states and maps, read back through gdn_chunk_fwd_plan's offsets, against the
+# oracle's stages, so that a regression shows in the stage that caused it.
+
+_TILES = ((0, 0), (1, 0), (2, 0), (2, 1), (3, 0), (3, 1))
+
+
+def _kappa(g, e):
+    return 4 * g + e if e < 4 else 12 + 4 * g + e
+
+
+def _bf16_planes(raw, shape):
+    """hi + lo of bfloat16 plane pairs: raw bytes -> float64 [..., 2 planes, 64 lanes, 8]."""
+    x = np.frombuffer(raw.tobytes(), dtype=np.uint16).reshape(*shape, 2, 64, 8)
+    f = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return f[..., 0, :, :] + f[..., 1, :, :]
+
+
+def _tile_set(raw, n_ch):
+    """A' or P of each (chunk, head) from its six A-operand tiles, [n_ch, 64, 64]."""
+    val = _bf16_planes(raw[:n_ch * 12288], (n_ch, 6))
+    out = np.zeros((n_ch, 64, 64))
+    for t, (rt, ks) in enumerate(_TILES):
+        for g in range(4):
+            for e in range(8):
+                out[:, 16 * rt:16 * rt + 16, 32 * ks + _kappa(g, e)] = val[:, t, 16 * g:16 * g + 16, e]
+    return out
+
+
+def test_prep_intermediates_match_oracle_stages():
+    """recompute_w_u's outputs in the workspace (WarpDrive page, kernel 5):
+    A' = A diag(beta) and P = s (Q K^T) * E * M as the high + low planes of their
+    A-operand tiles, and the gate vectors g, e^g, e^{g_last - g}, against the
+    oracle's per-chunk stages; two sequences of 300 tokens (a ragged chunk of 44
+    rows: its rows and columns past the end are zero, its gate rows repeat the
+    last), 4 heads, every (chunk, head)."""
+    B, T, H, K, V = 2, 300, 4, 128, 128
+    ci = chunk_inputs([T] * B, H, K, V, dtype="bf16", seed=71, gate_shift=-2.0, h0_std=0.1)
+    dt = torch.bfloat16
+    q, k, v = (dev(x, dt).view(B, T, H, -1) for x in (ci.q, ci.k, ci.v))
+    g, b = dev(ci.a).view(B, T, H), dev(ci.beta).view(B, T, H)
+    ws = torch.zeros(api.workspace_bytes(B, B * T, H, K, V), dtype=torch.uint8, device="cuda")
+    api.chunk_fwd(q, k, v, g, b, scale=0.2, h0=dev(ci.h0), out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    (n_seg, _, _), off = api.chunk_fwd_plan(B, B * T, T, H, K, V)
+    raw = ws.cpu().numpy()
+    ncs = (T + 63) // 64
+    n_ch = B * ncs * H
+    ap = _tile_set(raw[off["af"]:], n_ch)
+    pp = _tile_set(raw[off["pf"]:], n_ch)
+    gx = np.frombuffer(raw[off["gx"]:off["gx"] + n_ch * 768].tobytes(), dtype=np.float32).reshape(n_ch, 3, 64)
+    worst = {"A'": 0.0, "P": 0.0, "g": 0.0, "e^g": 0.0, "e^{gL-g}": 0.0}
+    for s in range(B):
+        r = slice(s * T, (s + 1) * T)
+        _, _, stages = oracle.chunked_fwd(ci.q[r], ci.k[r], ci.v[r], ci.a[r], ci.beta[r], scale=0.2,
+                                          S0=ci.h0[s], return_stages=True)
+        for j, st in enumerate(stages):
+            n = st["g"].shape[1]
+            bta = ci.beta[r][64 * j:64 * j + n].T  # [H, n]
+            for h in range(H):
+                ch = (s * ncs + j) * H + h
+                a_ref = st["A"][h] * bta[h][None, :]
+                p_ref = st["P"][h]
+                for name, got, ref in (("A'", ap[ch], a_ref), ("P", pp[ch], p_ref)):
+                    full = np.zeros((64, 64))
+                    full[:n, :n] = ref
+                    worst[name] = max(worst[name], float(np.max(np.abs(got - full)) / np.max(np.abs(ref))))
+                gv = st["g"][h]
+                g_full = np.concatenate([gv, np.full(64 - n, gv[-1])])
+                worst["g"] = max(worst["g"], float(np.max(np.abs(gx[ch, 0] - g_full) / (1 + np.abs(g_full)))))
+                for name, row, ref in (("e^g", 1, np.exp(g_full)), ("e^{gL-g}", 2, np.exp(g_full[-1] - g_full))):
+                    worst[name] = max(worst[name], float(np.max(np.abs(gx[ch, row] - ref) / ref)))
+    _print("[prep intermediates] " + " ".join(f"{k} {v:.2e}" for k, v in worst.items()), f"(plan {n_seg} segments)")
+    assert worst["A'"] <= 2e-4 and worst["P"] <= 2e-4, worst
+    # g: 64 float32 additions (|error| <= 64 * 2^-24 |g|); the exponentials add that
+    # absolute error of their argument as relative error
+    assert worst["g"] <= 1e-5 and worst["e^g"] <= 1e-4 and worst["e^{gL-g}"] <= 1e-4, worst
+
+
+def test_segment_states_and_maps_match_oracle():
+    """The chunk-parallel form's intermediates in the workspace: segment 0's final
+    state, and for each segment j = 1 .. n - 2 its affine map h -> M_j h + c_j:
+    c_j is the segment's final state from zero, M_j its final state from the
+    identity with V = 0 (the map's linear part), both from the oracle run on the
+    segment's chunks. B = 1, T = 1600 (25 chunks), H = 4: six segments of
+    4 + 5 x 4 + 1 chunks, four maps; long-memory gates."""
+    B, T, H, K, V = 1, 1600, 4, 128, 128
+    (n_seg, L0, L1), off = api.chunk_fwd_plan(B, T, T, H, K, V)
+    assert n_seg >= 3, "this shape is meant to take the chunk-parallel form"
+    ci = chunk_inputs([T], H, K, V, dtype="bf16", seed=72, gate_shift=-4.0, h0_std=0.1)
+    dt = torch.bfloat16
+    q, k, v = (dev(x, dt).view(B, T, H, -1) for x in (ci.q, ci.k, ci.v))
+    g, b = dev(ci.a).view(B, T, H), dev(ci.beta).view(B, T, H)
+    ws = torch.zeros(api.workspace_bytes(B, T, H, K, V), dtype=torch.uint8, device="cuda")
+    api.chunk_fwd(q, k, v, g, b, scale=K ** -0.5, h0=dev(ci.h0), out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    page = (V + K) * K * 4
+    st0 = np.frombuffer(raw[off["seg_state"]:off["seg_state"] + H * V * K * 4].tobytes(), dtype=np.float32)
+    st0 = st0.reshape(H, V, K)
+
+    def oracle_state(c0, c1, S0, zero_v=False):
+        r = slice(64 * c0, 64 * c1)
+        vv = np.zeros_like(ci.v[r]) if zero_v else ci.v[r]
+        _, S = oracle.chunked_fwd(ci.q[r], ci.k[r], vv, ci.a[r], ci.beta[r], scale=K ** -0.5, S0=S0)
+        return S  # [H, V, K]
+
+    e0 = max_err_over_rms(st0, oracle_state(0, L0, ci.h0[0]))
+    worst_c = worst_m = worst_mt = 0.0
+    eye = np.broadcast_to(np.eye(K), (H, V, K)).copy()
+    nkb = K // 32
+    for j in range(1, n_seg - 1):
+        c0, c1 = L0 + (j - 1) * L1, L0 + j * L1
+        c_ref = oracle_state(c0, c1, None)
+        m_ref = oracle_state(c0, c1, eye, zero_v=True).transpose(0, 2, 1)  # M_j = (final state)^T
+        for h in range(H):
+            base = off["seg_sum"] + (h * (n_seg - 2) + j - 1) * page
+            c_got = np.frombuffer(raw[base:base + V * K * 4].tobytes(), dtype=np.float32).reshape(V, K)
+            worst_c = max(worst_c, max_err_over_rms(c_got, c_ref[h]))
+            frag = _bf16_planes(raw[base + V * K * 4:base + page], (nkb, 2 * nkb))  # [kb, t, lane, e]
+            m_got = np.zeros((K, K))
+            for kb in range(nkb):
+                for t in range(2 * nkb):
+                    for lane in range(64):
+                        gg, c = lane >> 4, lane & 15
+                        row = 32 * (t // 2) + 8 * (c // 4) + 4 * (t % 2) + c % 4
+                        m_got[row, 32 * kb + 8 * gg:32 * kb + 8 * gg + 8] = frag[kb, t, lane]
+            worst_m = max(worst_m, max_err_over_rms(m_got, m_ref[h]))
+            worst_mt = max(worst_mt, max_err_over_rms(m_got, m_ref[h].T))  # printed: tells a transposed map
+    _print(f"[segment intermediates: {n_seg} segments of {L0} + {L1} x {n_seg - 2} + rest] "
+           f"state 0 {e0:.3e} c {worst_c:.3e} M {worst_m:.3e} (against M^T {worst_mt:.3e})")
+    tol = TOL["bf16"]
+    assert e0 <= tol and worst_c <= tol and worst_m <= tol
+
+
 def test_config_h16_t4096_full():
     """B=1, H=16, T=4096, K=V=128, bf16: every output and the final state."""
     ci = chunk_inputs([4096], 16, 128, 128, dtype="bf16", seed=2)
