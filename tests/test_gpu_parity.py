@@ -251,15 +251,22 @@ def _kappa(g, e):
 
 
 def _bf16_planes(raw, shape):
-    """hi + lo of bfloat16 plane pairs: raw bytes -> float64 [..., 2 planes, 64 lanes, 8]."""
+    """hi + lo of bfloat16 plane pairs: raw bytes -> float64 [..., 64 lanes, 8]."""
     x = np.frombuffer(raw.tobytes(), dtype=np.uint16).reshape(*shape, 2, 64, 8)
     f = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return f[..., 0, :, :] + f[..., 1, :, :]
 
 
-def _tile_set(raw, n_ch):
+def _f32_planes(raw, shape):
+    """float32 fragments stored as two planes (elements 0-3, then 4-7) -> [..., 64 lanes, 8]."""
+    x = np.frombuffer(raw.tobytes(), dtype=np.float32).reshape(*shape, 2, 64, 4).astype(np.float64)
+    return np.concatenate([x[..., 0, :, :], x[..., 1, :, :]], axis=-1)
+
+
+def _tile_set(raw, n_ch, dtype):
     """A' or P of each (chunk, head) from its six A-operand tiles, [n_ch, 64, 64]."""
-    val = _bf16_planes(raw[:n_ch * 12288], (n_ch, 6))
+    planes = _bf16_planes if dtype == "bf16" else _f32_planes
+    val = planes(raw[:n_ch * 12288], (n_ch, 6))
     out = np.zeros((n_ch, 64, 64))
     for t, (rt, ks) in enumerate(_TILES):
         for g in range(4):
@@ -268,27 +275,28 @@ def _tile_set(raw, n_ch):
     return out
 
 
-def test_prep_intermediates_match_oracle_stages():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prep_intermediates_match_oracle_stages(dtype):
     """recompute_w_u's outputs in the workspace (WarpDrive page, kernel 5):
-    A' = A diag(beta) and P = s (Q K^T) * E * M as the high + low planes of their
-    A-operand tiles, and the gate vectors g, e^g, e^{g_last - g}, against the
-    oracle's per-chunk stages; two sequences of 300 tokens (a ragged chunk of 44
-    rows: its rows and columns past the end are zero, its gate rows repeat the
-    last), 4 heads, every (chunk, head)."""
+    A' = A diag(beta) and P = s (Q K^T) * E * M as A-operand tiles (bf16 inputs:
+    high + low bfloat16 planes; fp32 inputs: float32), and the gate vectors g,
+    e^g, e^{g_last - g}, against the oracle's per-chunk stages; two sequences of
+    300 tokens (a ragged chunk of 44 rows: its rows and columns past the end are
+    zero, its gate rows repeat the last), 4 heads, every (chunk, head)."""
     B, T, H, K, V = 2, 300, 4, 128, 128
-    ci = chunk_inputs([T] * B, H, K, V, dtype="bf16", seed=71, gate_shift=-2.0, h0_std=0.1)
-    dt = torch.bfloat16
+    ci = chunk_inputs([T] * B, H, K, V, dtype=dtype, seed=71, gate_shift=-2.0, h0_std=0.1)
+    dt = TORCH_DT[dtype]
     q, k, v = (dev(x, dt).view(B, T, H, -1) for x in (ci.q, ci.k, ci.v))
     g, b = dev(ci.a).view(B, T, H), dev(ci.beta).view(B, T, H)
-    ws = torch.zeros(api.workspace_bytes(B, B * T, H, K, V), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(api.workspace_bytes(B, B * T, H, K, V, in_dtype=dt), dtype=torch.uint8, device="cuda")
     api.chunk_fwd(q, k, v, g, b, scale=0.2, h0=dev(ci.h0), out_dtype=torch.float32, workspace=ws)
     torch.cuda.synchronize()
-    (n_seg, _, _), off = api.chunk_fwd_plan(B, B * T, T, H, K, V)
+    (n_seg, _, _), off = api.chunk_fwd_plan(B, B * T, T, H, K, V, in_dtype=dt)
     raw = ws.cpu().numpy()
     ncs = (T + 63) // 64
     n_ch = B * ncs * H
-    ap = _tile_set(raw[off["af"]:], n_ch)
-    pp = _tile_set(raw[off["pf"]:], n_ch)
+    ap = _tile_set(raw[off["af"]:], n_ch, dtype)
+    pp = _tile_set(raw[off["pf"]:], n_ch, dtype)
     gx = np.frombuffer(raw[off["gx"]:off["gx"] + n_ch * 768].tobytes(), dtype=np.float32).reshape(n_ch, 3, 64)
     worst = {"A'": 0.0, "P": 0.0, "g": 0.0, "e^g": 0.0, "e^{gL-g}": 0.0}
     for s in range(B):
@@ -311,7 +319,8 @@ def test_prep_intermediates_match_oracle_stages():
                 worst["g"] = max(worst["g"], float(np.max(np.abs(gx[ch, 0] - g_full) / (1 + np.abs(g_full)))))
                 for name, row, ref in (("e^g", 1, np.exp(g_full)), ("e^{gL-g}", 2, np.exp(g_full[-1] - g_full))):
                     worst[name] = max(worst[name], float(np.max(np.abs(gx[ch, row] - ref) / ref)))
-    _print("[prep intermediates] " + " ".join(f"{k} {v:.2e}" for k, v in worst.items()), f"(plan {n_seg} segments)")
+    _print(f"[prep intermediates {dtype}] " + " ".join(f"{k} {v:.2e}" for k, v in worst.items()),
+           f"(plan {n_seg} segments)")
     assert worst["A'"] <= 2e-4 and worst["P"] <= 2e-4, worst
     # g: 64 float32 additions (|error| <= 64 * 2^-24 |g|); the exponentials add that
     # absolute error of their argument as relative error
