@@ -73,8 +73,10 @@ size_t gdn_chunk_fwd_workspace_bytes(int n_seqs, int64_t total_tokens, int H, in
 
 gdn_status gdn_chunk_fwd_plan(int n_seqs, int64_t total_tokens, int64_t max_len, int H, int K, int V,
                               gdn_dtype in_dtype, int32_t* plan, int64_t* offsets) {
+  // (the size limits of gdn_chunk_fwd, so that a plan exists only for a call that can be made)
   if (!plan || !offsets || n_seqs < 0 || total_tokens < 0 || max_len < 0 || max_len > total_tokens || H <= 0 ||
-      (n_seqs == 0 && total_tokens > 0))
+      H > 65535 || (n_seqs == 0 && total_tokens > 0) || total_tokens > INT_MAX - 2 * kChunkTokens ||
+      static_cast<int64_t>(n_seqs) * H > INT_MAX / 8)
     return GDN_EINVAL;
   if (!supported_dim(K) || !supported_dim(V) || !valid_dtype(in_dtype)) return GDN_EUNSUPPORTED;
   const int64_t max_nc = (max_len + kChunkTokens - 1) / kChunkTokens;
