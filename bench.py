@@ -745,8 +745,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: the chunked forward and the decode step need no "
-              f"communication, and this build runs on a single MI355X (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE={world}).", file=sys.stderr)
+              f"communication, and the library runs each call on a single MI355X (asked for --gpus "
+              f"{args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
 
     import torch
