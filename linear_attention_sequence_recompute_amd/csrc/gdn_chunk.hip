@@ -353,8 +353,13 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   if (w == 0) {
     const int64_t gi = static_cast<int64_t>(t0 + lane) * H + h;
     const float a = lane < n ? g[gi] : 0.f;
-    const float gl = wave_inclusive_scan(a);
-    const float glast = __shfl(gl, 63, 64);
+    const float gs = wave_inclusive_scan(a);
+    // g_last is the sum at the chunk's last row, and rows past the end repeat it
+    // exactly: the scan reaches lane 63 by another order of additions than lane
+    // n - 1, and e^{g_last - g} of the last rows, which dominate the state when
+    // the gates forget fast, must come out as 1 where it is 1.
+    const float glast = __shfl(gs, n - 1, 64);
+    const float gl = lane < n ? gs : glast;
     sg[lane] = gl;
     sb[lane] = lane < n ? beta[gi] : 0.f;
     ws.gx[ch * 192 + lane] = gl;

@@ -383,6 +383,58 @@ def test_segment_states_and_maps_match_oracle():
     assert e0 <= tol and worst_c <= tol and worst_m <= tol
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shift", [4.0, 8.0])
+def test_fast_gates_ragged_chunks(dtype, shift):
+    """Gates that forget within a few tokens (mean log-gate about -4 and -8) with
+    sequence lengths that end mid-chunk (498 = 7 x 64 + 50, and 50): the final
+    state is then made almost entirely of the last rows' writes, scaled by
+    e^{g_last - g}, which is exactly 1 at the last row, so the chunk's g_last and
+    the sums of the rows past its end must equal the last row's sum exactly."""
+    for lengths in ([498, 498], [50]):
+        ci = chunk_inputs(lengths, 3, 128, 128, dtype=dtype, seed=7000, h0_std=0.1, gate_shift=shift)
+        check_chunk(ci, 128 ** -0.5, label=f"fast gates {dtype} shift={shift} lengths={lengths}")
+
+
+def _random_chunk_case(seed):
+    """Sizes of one seeded random chunk-path case: 1-4 sequences of equal or mixed
+    lengths (empty and one-token sequences among them), 1-5 heads, every head-size
+    pair, bf16 or fp32, with or without an initial state, three gate regimes."""
+    rng = np.random.default_rng(5000 + seed)
+    n = int(rng.integers(1, 5))
+    K, V = [(128, 128), (64, 64), (128, 64), (64, 128)][int(rng.integers(4))]
+    H = int(rng.integers(1, 6))
+    dtype = "bf16" if rng.random() < 0.75 else "f32"
+    if rng.random() < 0.3:
+        lengths = [int(rng.integers(1, 1400))] * n
+    else:
+        lengths = [int(x) for x in rng.integers(0, 1700, n)]
+        if n > 1 and rng.random() < 0.3:
+            lengths[int(rng.integers(n))] = int(rng.choice([0, 1, 64, 65]))
+    h0 = 0.1 if rng.random() < 0.5 else None
+    shift = float(rng.choice([2.0, -2.0, -4.0]))
+    return lengths, H, K, V, dtype, h0, shift
+
+
+def test_chunk_random_shapes():
+    """Sixteen seeded random cases of the chunk path against the oracle (every
+    (sequence, head) pair, outputs and final states), so that shapes no fixed test
+    names are covered too; the cases that have few pairs and long sequences take
+    the chunk-parallel form, and at least some do."""
+    took_segments = 0
+    for seed in range(16):
+        lengths, H, K, V, dtype, h0, shift = _random_chunk_case(seed)
+        ci = chunk_inputs(lengths, H, K, V, dtype=dtype, seed=7000 + seed, h0_std=h0, gate_shift=shift)
+        (n_seg, _, _), _ = api.chunk_fwd_plan(len(lengths), sum(lengths), max(lengths), H, K, V,
+                                              in_dtype=TORCH_DT[dtype])
+        took_segments += n_seg > 1
+        label = f"random {seed}: lengths {lengths} H={H} K={K} V={V} {dtype} h0={h0 is not None} " \
+                f"shift={shift} segments={n_seg}"
+        _print(label)
+        check_chunk(ci, K ** -0.5, label=label)
+    assert took_segments >= 2, "the sweep should reach the chunk-parallel form"
+
+
 def test_config_h16_t4096_full():
     """B=1, H=16, T=4096, K=V=128, bf16: every output and the final state."""
     ci = chunk_inputs([4096], 16, 128, 128, dtype="bf16", seed=2)
