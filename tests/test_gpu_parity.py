@@ -596,6 +596,29 @@ def test_decode_out_of_range_slot_is_padding():
     assert torch.equal(pool[keep], pool0[keep])
 
 
+def test_decode_random_shapes():
+    """Twelve seeded random decode steps against the oracle (scalar gates; with
+    per-channel decays for every other case): 1-300 requests with some padding
+    rows, 1-6 heads, every head-size pair, bf16 and fp32, pools a little or much
+    larger than the batch, gates from long memory to forgetting within a token."""
+    for seed in range(12):
+        rng = np.random.default_rng(9000 + seed)
+        N = int(rng.integers(1, 301))
+        H = int(rng.integers(1, 7))
+        K, V = [(128, 128), (64, 64), (128, 64), (64, 128)][int(rng.integers(4))]
+        dtype = "bf16" if rng.random() < 0.7 else "f32"
+        n_pad = int(rng.integers(0, N // 4 + 1))
+        pool = N - n_pad + 1 + int(rng.integers(0, 2 * N + 2))
+        shift = float(rng.choice([-4.0, 2.0, 8.0]))
+        di = decode_inputs(N=N, H=H, K=K, V=V, pool_slots=pool, dtype=dtype, seed=9100 + seed, n_padding=n_pad,
+                           gate_shift=shift)
+        label = f"random {seed}: N={N} H={H} K={K} V={V} {dtype} pad={n_pad} pool={pool} shift={shift}"
+        check_decode(di, K ** -0.5, label)
+        if seed % 2:
+            g = channel_log_decay((N, H, K), 9200 + seed, shift)
+            check_decode_kda(di, g, K ** -0.5, label)
+
+
 # --------------------------------------------- per-key-channel decay (KDA)
 
 def check_decode_kda(di, g, scale, label):
@@ -713,6 +736,28 @@ def test_verify_small(K, V, dtype, T):
     check_verify(vi, K ** -0.5, f"K={K} V={V} {dtype} T={T}")
 
 
+def test_verify_random_shapes():
+    """Ten seeded random speculative-verify calls against the oracle: 1-40
+    requests of 1-8 tokens, slot tables up to three columns wider than T with
+    padding requests and entries that are not written, 1-4 heads, every
+    head-size pair, bf16 and fp32, three gate regimes."""
+    for seed in range(10):
+        rng = np.random.default_rng(9300 + seed)
+        N = int(rng.integers(1, 41))
+        T = int(rng.integers(1, 9))
+        C = T + int(rng.integers(0, 4))
+        H = int(rng.integers(1, 5))
+        K, V = [(128, 128), (64, 64), (128, 64), (64, 128)][int(rng.integers(4))]
+        dtype = "bf16" if rng.random() < 0.7 else "f32"
+        n_pad = int(rng.integers(0, N // 3 + 1))
+        n_nowrite = int(rng.integers(0, 4)) if (N - n_pad) * (C - 1) >= 3 else 0
+        shift = float(rng.choice([-4.0, 2.0, 8.0]))
+        vi = verify_inputs(N=N, T=T, H=H, K=K, V=V, pool_slots=N * C + 1 + int(rng.integers(0, 20)), dtype=dtype,
+                           seed=9400 + seed, cols=C, n_padding=n_pad, n_nowrite=n_nowrite, gate_shift=shift)
+        check_verify(vi, K ** -0.5, f"random {seed}: N={N} T={T} C={C} H={H} K={K} V={V} {dtype} pad={n_pad} "
+                                    f"nowrite={n_nowrite} shift={shift}")
+
+
 def test_verify_config_full():
     """96 requests x 4 tokens, H=32, K=V=128, 512-slot pool (the timed shape), 8
     padding requests and 16 unwritten table entries; every output and state."""
@@ -826,6 +871,51 @@ def check_chunk_kda(B, T, H, K, V, dtype, seed, shift, label, heads=None, forget
 def test_chunk_kda_small(K, V, dtype):
     """Two sequences of 150 tokens (two full chunks and a ragged one), three heads."""
     check_chunk_kda(2, 150, 3, K, V, dtype, seed=90 + K + V, shift=2.0, label=f"K={K} V={V} {dtype}")
+
+
+def test_chunk_kda_random_packed():
+    """Eight seeded random packed calls of the per-channel chunk form against the
+    oracle: 1-4 sequences of mixed lengths (empty and one-token ones among them)
+    with dense initial states, 1-4 heads, every head-size pair, bf16 and fp32,
+    decays from long memory to forgetting within a token."""
+    for seed in range(8):
+        rng = np.random.default_rng(9500 + seed)
+        n = int(rng.integers(1, 5))
+        lengths = [int(x) for x in rng.integers(0, 600, n)]
+        if n > 1:
+            lengths[int(rng.integers(n))] = int(rng.choice([0, 1, 64, 65]))
+        H = int(rng.integers(1, 5))
+        K, V = [(128, 128), (64, 64), (128, 64), (64, 128)][int(rng.integers(4))]
+        dtype = "bf16" if rng.random() < 0.6 else "f32"
+        shift = float(rng.choice([-4.0, 2.0, 8.0]))
+        ci = chunk_inputs(lengths, H, K, V, dtype=dtype, seed=9600 + seed, h0_std=0.1)
+        T = sum(lengths)
+        g = channel_log_decay((T, H, K), 9700 + seed, shift)
+        dt = TORCH_DT[dtype]
+        q, k, v = (dev(x, dt) for x in (ci.q, ci.k, ci.v))
+        outs = {}
+        for od in ("f32", "bf16"):
+            o, ht = api.chunk_fwd_kda(q, k, v, dev(g), dev(ci.beta), scale=K ** -0.5, cu_seqlens=ci.cu_seqlens.tolist(),
+                                      h0=dev(ci.h0), out_dtype=TORCH_DT[od])
+            torch.cuda.synchronize()
+            outs[od] = (o, ht)
+        (o32, ht32), (o16, ht16) = outs["f32"], outs["bf16"]
+        assert torch.equal(o16, bf16_rne(o32)) and torch.equal(ht16, ht32)
+        o_h, ht_h = host(o32), host(ht32)
+        eo = es = 0.0
+        for si in range(n):
+            r = slice(int(ci.cu_seqlens[si]), int(ci.cu_seqlens[si + 1]))
+            if r.stop == r.start:
+                assert np.array_equal(ht_h[si], ci.h0[si]), "an empty sequence passes its state through"
+                continue
+            o_ref, s_ref = oracle.recurrent_fwd_kda(ci.q[r], ci.k[r], ci.v[r], g[r], ci.beta[r], scale=K ** -0.5,
+                                                    S0=ci.h0[si])
+            eo = max(eo, max_err_over_rms(o_h[r], o_ref))
+            es = max(es, max_err_over_rms(ht_h[si], s_ref))
+        tol = TOL[dtype]
+        _print(f"[chunk kda random {seed}: lengths {lengths} H={H} K={K} V={V} {dtype} shift={shift}] "
+               f"max|do|/rms={eo:.3e} max|dS|/rms={es:.3e} tol={tol}")
+        assert eo <= tol and es <= tol
 
 
 def test_chunk_kda_long_memory():
