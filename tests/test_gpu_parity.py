@@ -1305,6 +1305,28 @@ def test_decode_layer_fused(D, kda, norm):
     assert torch.equal(pool[torch.from_numpy(unused).cuda()], dev(pool0)[torch.from_numpy(unused).cuda()])
 
 
+def test_decode_layer_fused_random():
+    """Eight seeded random calls of the fused decode layer against the oracle's
+    front, step and gated RMSNorm: 1-200 requests with padding rows, 1-6 heads of
+    64 or 128, pools a little or much larger than the batch, scalar gates or
+    per-channel decays, with and without the norm; the conv state bit for bit."""
+    for seed in range(8):
+        rng = np.random.default_rng(9800 + seed)
+        N = int(rng.integers(1, 201))
+        H = int(rng.integers(1, 7))
+        D = int(rng.choice([64, 128]))
+        n_pad = int(rng.integers(0, N // 4 + 1))
+        P = N + 1 + int(rng.integers(0, N + 8))
+        kda, norm = bool(rng.random() < 0.5), bool(rng.random() < 0.5)
+        li, out, conv, pool, pool0, rst, e_out, e_st, act = _layer_fused_case(N, H, D, P, 9900 + seed, kda, norm,
+                                                                              n_padding=n_pad)
+        _print(f"[decode layer fused random {seed}: N={N} H={H} D={D} P={P} pad={n_pad} kda={kda} norm={norm}] "
+               f"out {e_out:.2e} state {e_st:.2e}")
+        assert e_out <= TOL["f32"] and e_st <= TOL["f32"]
+        assert np.array_equal(host(conv), rst), "conv state differs"
+        assert bool((out[torch.from_numpy(~act).cuda()].view(torch.int32) == 0).all()), "padding rows not +0"
+
+
 def test_decode_layer_fused_config_full():
     """N=256 requests, H=32 heads of 128, pool of 512 slots, 32 padding rows, per-channel
     decays, gated RMSNorm, bf16 output (= RNE of the float32 output of the same call)."""
