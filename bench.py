@@ -3,7 +3,8 @@
 
 A step is one chunked forward pass (gdn_chunk_fwd: the prep kernel for
 recompute_w_u, then chunk_fwd_h fused with chunk_fwd_o, which at this shape runs
-in the chunk-parallel form: summary kernel, then scan kernel) over one batch of
+in the chunk-parallel form: segment 0's scan beside the later segments' state
+maps, then the scan of the later segments) over one batch of
 B=1, H=16, T=4096, K=V=128 bf16 inputs, already resident in device memory.
 `value` is tokens over the wall time of the K timed steps (back to back, between
 device synchronisations). Beside it, per call, HIP events recorded by the
