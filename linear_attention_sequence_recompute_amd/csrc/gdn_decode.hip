@@ -19,7 +19,9 @@
 // the pool) instead of hopping between the scattered slots of consecutive
 // requests (measured on the 512-slot pool with random slots: 5.39 TB/s with the
 // request fastest, 5.82 TB/s this way; 32 or 64 rows per workgroup and
-// temporal loads or stores are slower).
+// temporal loads or stores are slower). The decode step also gives each XCD a
+// contiguous range of pages (xcd_page_part: 6.1 TB/s); for the verify step,
+// whose writes go to other slots than its reads, that made no difference.
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
@@ -46,8 +48,9 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
   constexpr int RPP = 256 / LPR;                 // rows per pass of the workgroup
   constexpr int PASSES = kDecodeRows / RPP;      // passes per workgroup
   constexpr int NP = V / kDecodeRows;  // row groups per head
-  const int per_req = H * NP;
-  const int b = blockIdx.x / per_req, h = (blockIdx.x % per_req) / NP, part = blockIdx.x % NP;
+  int page, part;
+  xcd_page_part<NP>(blockIdx.x, gridDim.x / NP, page, part);
+  const int b = page / H, h = page % H;
   const int tid = threadIdx.x;
   const int col = (tid % LPR) * 4;
   const int rsub = tid / LPR;

@@ -51,7 +51,9 @@ __global__ __launch_bounds__(kLayerWG) void decode_layer_kernel(
   static_assert(PASSES >= 1 && D % RPP == 0, "whole passes");
   __shared__ float yq[D], yk[D], yv[D], yo[D];
   __shared__ float red[16];
-  const int b = blockIdx.x / H, h = blockIdx.x % H;
+  int page, part;
+  xcd_page_part<1>(blockIdx.x, gridDim.x, page, part);
+  const int b = page / H, h = page % H;
   const int tid = threadIdx.x;
   const int col = (tid % LPR) * 4, rsub = tid / LPR;
   const int64_t tok = static_cast<int64_t>(b) * H + h;
