@@ -16,6 +16,9 @@
  *                       (sink holds waves * 64 floats).
  *  gdn_probe_copy       HBM streaming copy of `bytes` (a multiple of 16) from
  *                       src to dst: bytes read + bytes written per call.
+ *                       (copy, write and read: each of 8192 workgroups sweeps
+ *                       one contiguous 1/8192 of the buffer, four 16-byte
+ *                       accesses in flight per lane)
  *  gdn_probe_write      HBM streaming write of `bytes` (a multiple of 16) to
  *                       dst (a constant pattern; nothing is read).
  *  gdn_probe_read       HBM streaming read of `bytes` (a multiple of 16) from

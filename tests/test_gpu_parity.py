@@ -1395,3 +1395,26 @@ def test_chunk_kda_varlen_dense_states_f32():
         es = max(es, max_err_over_rms(host(state[s]), S_ref))
     _print(f"[chunk kda varlen f32 in place] max|do|/rms={eo:.3e} max|dS|/rms={es:.3e}")
     assert eo <= TOL["f32"] and es <= TOL["f32"]
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 8191, 16 * 8192 * 3 + 16 * 77, 1 << 24])
+def test_probes_move_every_byte(nbytes):
+    """The streaming probes cover the whole buffer with their per-workgroup
+    regions (sizes below, at and past one region per workgroup, ragged): the
+    copy reproduces the source, the write fills every element with its pattern,
+    the read's partial sums add up to the source's sum."""
+    lib = api._lib.lib()
+    n = nbytes // 16
+    src = torch.arange(4 * n, dtype=torch.float32, device="cuda").remainder_(97.0)
+    dst = torch.full_like(src, -1.0)
+    sink = torch.zeros(8192, dtype=torch.float32, device="cuda")
+    assert lib.gdn_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, None) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    assert lib.gdn_probe_write(dst.data_ptr(), nbytes, None) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dst.view(n, 4), torch.tensor([1.0, 2.0, 3.0, 4.0], device="cuda").expand(n, 4))
+    assert lib.gdn_probe_read(src.data_ptr(), sink.data_ptr(), nbytes, None) == 0
+    torch.cuda.synchronize()
+    assert float(sink.double().sum()) == pytest.approx(float(src.double().sum()), rel=1e-6)
+
