@@ -136,6 +136,10 @@ gdn_status gdn_chunk_fwd_plan(int n_seqs, int64_t total_tokens, int64_t max_len,
  *  workspace   device scratch of at least gdn_chunk_fwd_workspace_bytes(...)
  *              bytes, 256-byte aligned; contents on entry are ignored.
  *
+ * Size limits (GDN_EINVAL beyond them): H in [1, 65535], total_tokens below
+ * 2^31 - 128, n_seqs H at most 2^28, and (total_tokens / 64 + n_seqs) H, the
+ * (chunk, head) count the call is sized for, below 2^31 - 8 H.
+ *
  * Chunks of 64 tokens start at every sequence start; a sequence's last chunk
  * may be shorter. An empty sequence passes its initial state to ht unchanged.
  * The result is deterministic: identical calls give identical bits, and o in

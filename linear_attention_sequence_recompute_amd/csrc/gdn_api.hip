@@ -76,7 +76,8 @@ gdn_status gdn_chunk_fwd_plan(int n_seqs, int64_t total_tokens, int64_t max_len,
   // (the size limits of gdn_chunk_fwd, so that a plan exists only for a call that can be made)
   if (!plan || !offsets || n_seqs < 0 || total_tokens < 0 || max_len < 0 || max_len > total_tokens || H <= 0 ||
       H > 65535 || (n_seqs == 0 && total_tokens > 0) || total_tokens > INT_MAX - 2 * kChunkTokens ||
-      static_cast<int64_t>(n_seqs) * H > INT_MAX / 8)
+      static_cast<int64_t>(n_seqs) * H > INT_MAX / 8 ||
+      (max_chunks(n_seqs, total_tokens) + 7) / 8 * 8 * H > INT_MAX)
     return GDN_EINVAL;
   if (!supported_dim(K) || !supported_dim(V) || !valid_dtype(in_dtype)) return GDN_EUNSUPPORTED;
   const int64_t max_nc = (max_len + kChunkTokens - 1) / kChunkTokens;
@@ -113,6 +114,7 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
   if (n_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_EINVAL;
   if ((cu_seqlens == nullptr) != (cu_seqlens_host == nullptr)) return GDN_EINVAL;
   if (static_cast<int64_t>(n_seqs) * H > INT_MAX / 8) return GDN_EINVAL;
+  if ((max_chunks(n_seqs, total_tokens) + 7) / 8 * 8 * H > INT_MAX) return GDN_EINVAL;  // prep's grid
 
   // Chunk count and sequence lengths.
   int64_t n_chunks = 0, max_nc = 0;

@@ -294,7 +294,7 @@ template <int K, typename Tin>
 __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k,
                                                    const float* __restrict__ g, const float* __restrict__ beta,
                                                    int H, float scale, int T_eq, int ncs_eq, int total_tokens,
-                                                   const int4* __restrict__ info, ChunkWs ws) {
+                                                   int n_chunks, const int4* __restrict__ info, ChunkWs ws) {
   using P = Prec<Tin>;
   using In = typename P::In;
   using KF = KFrag<K, Tin>;
@@ -306,7 +306,15 @@ __global__ __launch_bounds__(256) void prep_kernel(const Tin* __restrict__ q, co
   __shared__ float sOff[6][16][17];                                 // A_ij below the diagonal
   __shared__ float sg[64], sb[64];
 
-  const int c = blockIdx.x, h = blockIdx.y;
+  // Workgroup -> (chunk, head): the 8 XCDs take workgroups round-robin; XCD x
+  // takes chunk x of every group of 8 chunks and runs its heads back to back, so
+  // that the workgroups in flight together read whole token rows of q and k and
+  // each chunk's rows are read through one L2 (prep 18.1 rather than 18.4 us at
+  // B = 1 H = 16 T = 4096, 184 rather than 193 at B = 4 H = 32 T = 8192). The
+  // grid is padded to whole groups; the padding exits at once.
+  const int r8 = static_cast<int>(blockIdx.x >> 3);
+  const int c = (r8 / H) * 8 + static_cast<int>(blockIdx.x & 7), h = r8 % H;
+  if (c >= n_chunks) return;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lc = lane & 15;
   int t0, n;
@@ -1523,10 +1531,11 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
                        a.ws.info);
   }
   if (a.n_chunks > 0) {
-    hipLaunchKernelGGL((prep_kernel<K, Tin>), dim3(static_cast<unsigned>(a.n_chunks), a.H), dim3(256), 0,
-                       a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), a.g, a.beta, a.H,
-                       a.scale, a.T_eq, ncs_eq, static_cast<int>(a.total_tokens), varlen ? a.ws.info : nullptr,
-                       a.ws);
+    const int64_t prep_wgs = (a.n_chunks + 7) / 8 * 8 * a.H;  // at most INT32_MAX (checked by the caller)
+    hipLaunchKernelGGL((prep_kernel<K, Tin>), dim3(static_cast<unsigned>(prep_wgs)), dim3(256), 0, a.stream,
+                       static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), a.g, a.beta, a.H, a.scale,
+                       a.T_eq, ncs_eq, static_cast<int>(a.total_tokens), static_cast<int>(a.n_chunks),
+                       varlen ? a.ws.info : nullptr, a.ws);
   }
   if (a.events[1]) (void)hipEventRecord(a.events[1], a.stream);
   const int64_t pairs = static_cast<int64_t>(a.n_seqs) * a.H;

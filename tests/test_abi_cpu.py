@@ -428,5 +428,6 @@ def test_chunk_fwd_plan():
     assert call(H=65536) == EINVAL  # the limits of gdn_chunk_fwd
     assert call(total=2**31 - 1, max_len=4096) == EINVAL
     assert call(n_seqs=2**23, total=2**24, max_len=16, H=64) == EINVAL
+    assert call(n_seqs=1, total=2**30, max_len=2**30, H=256) == EINVAL  # (chunk, head) count beyond prep's grid
     assert call(p=None) == EINVAL and call(o=None) == EINVAL
     assert call(K=96) == _lib.GDN_EUNSUPPORTED
