@@ -396,6 +396,18 @@ def test_fast_gates_ragged_chunks(dtype, shift):
         check_chunk(ci, 128 ** -0.5, label=f"fast gates {dtype} shift={shift} lengths={lengths}")
 
 
+@pytest.mark.parametrize("B,T,H", [(1, 32768, 1), (1, 16384, 2)])
+def test_chunk_parallel_at_the_segment_limit(B, T, H):
+    """Very long sequences with few pairs take the most segments the form allows
+    (eight: segment 0, six maps, the last segment folding all six), each of
+    tens of chunks; long-memory gates, so that the state the folds carry
+    matters to the end; outputs and final states in full against the oracle."""
+    (n_seg, L0, L1), _ = api.chunk_fwd_plan(B, B * T, T, H, 128, 128)
+    assert n_seg == 8, (n_seg, L0, L1)
+    ci = chunk_inputs([T] * B, H, 128, 128, dtype="bf16", seed=7700 + T + H, h0_std=0.1, gate_shift=-4.0)
+    check_chunk(ci, 128 ** -0.5, label=f"B={B} T={T} H={H}, {n_seg} segments of {L0} + {L1} x {n_seg - 2} + rest")
+
+
 def _random_chunk_case(seed):
     """Sizes of one seeded random chunk-path case: 1-4 sequences of equal or mixed
     lengths (empty and one-token sequences among them), 1-5 heads, every head-size
