@@ -497,6 +497,15 @@ def test_varlen_edge_lengths_dense_states():
     check_chunk(ci, 0.2, label="varlen edges")
 
 
+def test_many_short_sequences():
+    """700 packed sequences of 0-90 tokens (the chunk schedule walks the sequences
+    256 at a time, carrying the chunk count across its passes), 2 heads, dense
+    h0/ht; every sequence checked."""
+    lengths = [int(x) for x in np.random.default_rng(23).integers(0, 91, 700)]
+    ci = chunk_inputs(lengths, 2, 64, 64, dtype="bf16", seed=24, h0_std=0.1)
+    check_chunk(ci, 0.2, label="700 short sequences")
+
+
 def test_pool_padding_slots():
     """Sequences whose slot is <= 0 start from zero and write nothing back."""
     lengths = [100, 70, 200]
