@@ -2,17 +2,19 @@
 // projection and the log-decay of gdn_gate.h for every (token, head, key
 // channel).
 //
-// One workgroup per (block of kGateTok tokens, head), one thread per key
-// channel: the thread's F_B row lives in registers as float32; each token's
-// activations are read once per wave into scalar registers. The blocks of a head
-// share an XCD.
+// One workgroup per (block of kGateGroups x kGateTok tokens, head): the head's
+// F_B rows are copied into LDS once and shared by kGateGroups groups of
+// threads, one thread per key channel in each; a thread keeps its F_B row in
+// registers as float32 and runs kGateTok tokens, whose activations are read once
+// per wave into scalar registers. The blocks of a head share an XCD.
 #include "gdn_common.h"
 #include "gdn_gate.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
-constexpr int kGateTok = 8;  // tokens per workgroup
+constexpr int kGateTok = 8;     // tokens per thread
+constexpr int kGateGroups = 4;  // thread groups per workgroup, sharing the head's F_B rows
 
 __device__ __forceinline__ void unpack8(const u32x4& u, float* dst) {
 #pragma unroll
@@ -23,32 +25,45 @@ __device__ __forceinline__ void unpack8(const u32x4& u, float* dst) {
 }
 
 template <int K, int MODE>
-__global__ __launch_bounds__(K) void kda_gate_kernel(const __bf16* __restrict__ f_a, const __bf16* __restrict__ f_b,
-                                                     const float* __restrict__ a_log,
-                                                     const float* __restrict__ dt_bias, float lower_bound,
-                                                     float* __restrict__ g, __bf16* __restrict__ raw_out, int N,
-                                                     int H) {
+__global__ __launch_bounds__(K * kGateGroups) void kda_gate_kernel(
+    const __bf16* __restrict__ f_a, const __bf16* __restrict__ f_b, const float* __restrict__ a_log,
+    const float* __restrict__ dt_bias, float lower_bound, float* __restrict__ g, __bf16* __restrict__ raw_out, int N,
+    int H) {
   constexpr int R = kGateRank;
+  static_assert(K % 64 == 0, "a wave's lanes share one token group");
+  constexpr int TPB = kGateTok * kGateGroups;  // tokens per workgroup
+  constexpr int SEG = R / 8;                     // 16-byte segments of an F_B row
+  __shared__ u32x4 sw[K * SEG];
   // Workgroups are dealt to the 8 XCDs round-robin by id: the token blocks of
   // one head get ids of one residue mod 8, so they share an XCD and its L2,
   // which then serves their common F_B rows (the grid is padded to whole
   // rounds of 8 heads)
-  const int n_tb = (N + kGateTok - 1) / kGateTok, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int n_tb = (N + TPB - 1) / TPB, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
   const int h = (idx / n_tb) * 8 + xcd, tb = idx % n_tb;
-  if (h >= H) return;
-  const int f = threadIdx.x;
-  const int t0 = tb * kGateTok;
-  const int nt = min(kGateTok, N - t0);
+  if (h >= H) return;  // whole workgroup
+  // K is a multiple of 64, so a wave's lanes share one group: its token rows
+  // are uniform and their activations stay scalar loads
+  const int tid = threadIdx.x, f = tid % K, grp = __builtin_amdgcn_readfirstlane(tid / K);
+  // The head's F_B rows into LDS, segment s of row r at s ^ (r % SEG): the 16
+  // rows a quarter-wave reads together then hit distinct banks.
+  const u32x4* src = reinterpret_cast<const u32x4*>(f_b + static_cast<int64_t>(h) * K * R);
+  for (int i = tid; i < K * SEG; i += K * kGateGroups) {
+    const int r = i / SEG, sg = i % SEG;
+    sw[r * SEG + (sg ^ (r % SEG))] = src[i];
+  }
+  __syncthreads();
   float w[R];
-  const __bf16* wr = f_b + (static_cast<int64_t>(h) * K + f) * R;
 #pragma unroll
-  for (int c8 = 0; c8 < R / 8; ++c8) unpack8(*reinterpret_cast<const u32x4*>(wr + 8 * c8), &w[8 * c8]);
+  for (int c8 = 0; c8 < SEG; ++c8) unpack8(sw[f * SEG + (c8 ^ (f % SEG))], &w[8 * c8]);
+  const int t0 = tb * TPB + grp * kGateTok;
+  const int nt = min(kGateTok, N - t0);  // <= 0 for the groups past the last token
   const float ea = expf(a_log[h]);
   const float dt = dt_bias[h * K + f];
 
-  // one token at a time (a wave issues dependent VALU operations back to back);
-  // the token's activations are the same for every lane: uniform loads, which
-  // the compiler places in scalar registers
+  // one token at a time (a wave issues dependent VALU operations back to back;
+  // two tokens' chains side by side were slower); the token's activations are
+  // the same for every lane: uniform loads, which the compiler places in scalar
+  // registers
   for (int t = 0; t < nt; ++t) {
     const uint32_t* xr = reinterpret_cast<const uint32_t*>(f_a) + static_cast<int64_t>(t0 + t) * (R / 2);
     const float raw = gate_raw<MODE>([&](int c) { return bf16_pair_col(xr, c); }, [&](int c) { return w[c]; });
@@ -61,10 +76,10 @@ __global__ __launch_bounds__(K) void kda_gate_kernel(const __bf16* __restrict__ 
 
 template <int K>
 static void launch_gate_k(const GateArgs& a) {
-  const int64_t n_tb = (a.N + kGateTok - 1) / kGateTok;
+  const int64_t n_tb = (a.N + kGateTok * kGateGroups - 1) / (kGateTok * kGateGroups);
   const dim3 grid(static_cast<unsigned>(n_tb * ((a.H + 7) / 8) * 8));
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(K), 0, a.stream, static_cast<const __bf16*>(a.f_a),
+    hipLaunchKernelGGL(kern, grid, dim3(K * kGateGroups), 0, a.stream, static_cast<const __bf16*>(a.f_a),
                        static_cast<const __bf16*>(a.f_b), a.a_log, a.dt_bias, a.lower_bound, a.g,
                        static_cast<__bf16*>(a.raw_out), a.N, a.H);
   };
