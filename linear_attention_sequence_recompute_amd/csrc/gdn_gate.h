@@ -35,6 +35,10 @@ __device__ __forceinline__ float gate_raw(X x, W w) {
     for (int c4 = 0; c4 < R / 4; ++c4) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc = fmaf(x(4 * c4 + e), w(4 * c4 + e), acc);
+      // the chain pinned at each chunk end, so that a chunk's FMAs stay ahead of
+      // the next chunk's activation loads (issued all at once, the loads held the
+      // whole row in scalar registers, which then spilled into vector lanes)
+      if (c4 % 8 == 7) asm volatile("" : "+v"(acc));
       chunk_end(c4);
     }
     return acc;
